@@ -1,0 +1,180 @@
+"""q4f16_1 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously correct C implementation (``q4_oracle.c``) of what the
+decode GEMV path computes, loaded through ctypes. Only ``tests/``, the smoke
+check in ``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may use
+it; the HIP library never does, and the two share no code.
+
+Definitions (Zero TVM documentation, section "Q4F16 quantization format"):
+eight 4-bit codes per uint32 word, nibble ``i`` = ``(word >> 4i) & 0xF``, one
+fp16 scale per 32 weights, weight = ``(code - 7) * scale``; y = W x.
+
+Parity pins for every function here live in ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "liborc.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", "-fvisibility=hidden", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or \
+                    os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = C.CDLL(_LIB_PATH)
+            p = C.c_void_p
+            i64 = C.c_int64
+            lib.orc_half_to_f64.argtypes = [C.c_uint16]
+            lib.orc_half_to_f64.restype = C.c_double
+            lib.orc_f64_to_half.argtypes = [C.c_double]
+            lib.orc_f64_to_half.restype = C.c_uint16
+            lib.orc_unpack.argtypes = [p, p, i64, i64]
+            lib.orc_unpack.restype = None
+            lib.orc_pack.argtypes = [p, p, i64, i64]
+            lib.orc_pack.restype = None
+            lib.orc_roundtrip_mismatches.argtypes = [C.c_uint64, C.c_uint64]
+            lib.orc_roundtrip_mismatches.restype = i64
+            lib.orc_gemv_f64.argtypes = [p, p, p, i64, i64, i64, p, i64, p]
+            lib.orc_gemv_f64.restype = C.c_int
+            lib.orc_gemv_exact.argtypes = [p, p, p, i64, i64, i64, p, i64, p, p]
+            lib.orc_gemv_exact.restype = C.c_int
+            lib.orc_row_norms.argtypes = [p, p, i64, i64, p, i64, p]
+            lib.orc_row_norms.restype = C.c_int
+            lib.orc_vec_norm.argtypes = [p, i64]
+            lib.orc_vec_norm.restype = C.c_double
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return C.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def half_to_f64(h: int) -> float:
+    return _load().orc_half_to_f64(int(h))
+
+
+def f64_to_half(v: float) -> int:
+    return _load().orc_f64_to_half(float(v))
+
+
+def unpack(words: np.ndarray, K: int | None = None) -> np.ndarray:
+    """uint32 [N][K/8] -> uint8 codes [N][K]."""
+    w = _c(words, np.uint32)
+    w2 = w.reshape(w.shape[0], -1) if w.ndim > 1 else w.reshape(1, -1)
+    N, K8 = w2.shape
+    out = np.empty((N, 8 * K8), np.uint8)
+    _load().orc_unpack(_ptr(w2), _ptr(out), N, 8 * K8)
+    return out if w.ndim > 1 else out.reshape(-1)
+
+
+def pack(codes: np.ndarray) -> np.ndarray:
+    """uint8 codes [N][K] (K % 8 == 0) -> uint32 [N][K/8]."""
+    c = _c(codes, np.uint8)
+    c2 = c.reshape(c.shape[0], -1) if c.ndim > 1 else c.reshape(1, -1)
+    N, K = c2.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    out = np.empty((N, K // 8), np.uint32)
+    _load().orc_pack(_ptr(c2), _ptr(out), N, K)
+    return out if c.ndim > 1 else out.reshape(-1)
+
+
+def roundtrip_mismatches(w0: int, w1: int) -> int:
+    return int(_load().orc_roundtrip_mismatches(w0, w1))
+
+
+def _rows_arg(rows, N):
+    if rows is None:
+        return None, N
+    r = _c(rows, np.int64).reshape(-1)
+    return r, len(r)
+
+
+def gemv_f64(words, scales, X, rows=None) -> np.ndarray:
+    """fp64 y = W x (X may be [K] or [M][K]); returns [n_rows] or [M][n_rows]."""
+    w = _c(words, np.uint32)
+    s = _c(scales, np.uint16)
+    x = _c(X, np.uint16)
+    N = w.shape[0]
+    K = 8 * w.shape[1]
+    xs = x.reshape(-1, K)
+    M = xs.shape[0]
+    r, nr = _rows_arg(rows, N)
+    Y = np.empty((M, nr), np.float64)
+    rc = _load().orc_gemv_f64(_ptr(w), _ptr(s), _ptr(xs), M, N, K, _ptr(r), nr, _ptr(Y))
+    if rc:
+        raise ValueError(f"orc_gemv_f64 failed ({rc})")
+    return Y[0] if x.ndim == 1 else Y
+
+
+def gemv_exact(words, scales, X, rows=None):
+    """Exact y = W x rounded once: returns (fp64 values, fp16 bit patterns)."""
+    w = _c(words, np.uint32)
+    s = _c(scales, np.uint16)
+    x = _c(X, np.uint16)
+    N = w.shape[0]
+    K = 8 * w.shape[1]
+    xs = x.reshape(-1, K)
+    M = xs.shape[0]
+    r, nr = _rows_arg(rows, N)
+    Y64 = np.empty((M, nr), np.float64)
+    Y16 = np.empty((M, nr), np.uint16)
+    rc = _load().orc_gemv_exact(_ptr(w), _ptr(s), _ptr(xs), M, N, K, _ptr(r), nr,
+                                _ptr(Y64), _ptr(Y16))
+    if rc:
+        raise ValueError(f"orc_gemv_exact failed ({rc})")
+    if x.ndim == 1:
+        return Y64[0], Y16[0]
+    return Y64, Y16
+
+
+def row_norms(words, scales, rows=None) -> np.ndarray:
+    w = _c(words, np.uint32)
+    s = _c(scales, np.uint16)
+    N = w.shape[0]
+    K = 8 * w.shape[1]
+    r, nr = _rows_arg(rows, N)
+    out = np.empty(nr, np.float64)
+    if _load().orc_row_norms(_ptr(w), _ptr(s), N, K, _ptr(r), nr, _ptr(out)):
+        raise ValueError("orc_row_norms failed")
+    return out
+
+
+def vec_norm(x) -> float:
+    xs = _c(x, np.uint16).reshape(-1)
+    return float(_load().orc_vec_norm(_ptr(xs), len(xs)))
+
+
+def tolerance(x_row, row_norms_max: float, rel: float = 2e-3) -> float:
+    """Allowed max |y_gpu - y_ref| for one input row: rel * ||x||_2 * max_n ||W_n||_2."""
+    return rel * vec_norm(x_row) * row_norms_max

@@ -1,0 +1,248 @@
+/*
+ * q4f16_1 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this file's library. The product path (the HIP library) never does, and
+ * the two share no code, header, table or helper.
+ *
+ * What is computed (the plain definitions, written out; slow on purpose):
+ *
+ *   q4f16_1 format -- Zero TVM documentation, section "Q4F16 quantization
+ *   format": eight 4-bit codes per uint32; nibble i of a word is
+ *   (word >> 4i) & 0xF; one fp16 scale per group of 32 weights; a weight is
+ *   (code - 7) * scale.  Layout (the plainest reading of an [out][in] weight
+ *   packed along the input axis): words[n][k/8] holds element k of row n in
+ *   bits [4*(k%8), 4*(k%8)+3]; scales[n][k/32].
+ *
+ *   GEMV -- for every input row m and output row n:
+ *       y[m][n] = sum_k (q[n][k] - 7) * s[n][k/32] * x[m][k].
+ *
+ * Two independent evaluations of that sum are provided:
+ *   orc_gemv_f64   -- fp64 accumulation in ascending k; every product is exact
+ *                     in fp64 (at most 4 + 11 + 11 significant bits), only the
+ *                     additions round.
+ *   orc_gemv_exact -- every finite fp16 value is an integer multiple of 2^-24,
+ *                     so every term is an integer multiple of 2^-48 below 2^84
+ *                     in magnitude; the sum is formed exactly in __int128 and
+ *                     rounded once, to fp64 and to fp16 (round to nearest even).
+ *
+ * fp16 <-> fp64 conversions are written from the IEEE 754 binary16 definition
+ * (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits; exponent 0 is
+ * zero/subnormal, exponent 31 is inf/NaN).  Codes above 15 given to orc_pack
+ * are reduced to their low nibble.
+ *
+ * parity pins: see the CPU tests (closed forms, exact brute force, numpy
+ * float16 conversions, byte-view nibble decoding, hand-worked fixtures).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_EXPORT __attribute__((visibility("default")))
+
+/* ---------------------------------------------------------------- binary16 */
+
+ORC_EXPORT double orc_half_to_f64(uint16_t h) {
+  int sign = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);                /* subnormal: f * 2^-24      */
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);    /* (1 + f/1024) * 2^(e - 15) */
+  return sign ? -v : v;
+}
+
+static int bitlen_u128(unsigned __int128 v) {
+  int n = 0;
+  while (v) { v >>= 1; ++n; }
+  return n;
+}
+
+/* Round mag * 2^e2 to an integer multiple of 2^qe, ties to even; returns the
+ * multiple (exact when e2 >= qe). */
+static unsigned __int128 round_to_quantum(unsigned __int128 mag, int e2, int qe) {
+  if (e2 >= qe) return mag << (e2 - qe);
+  int shift = qe - e2;
+  if (shift > 128) return 0;                       /* below half a quantum */
+  unsigned __int128 r, rem, half;
+  if (shift == 128) {
+    r = 0; rem = mag; half = (unsigned __int128)1 << 127;
+  } else {
+    r = mag >> shift;
+    rem = mag - (r << shift);
+    half = (unsigned __int128)1 << (shift - 1);
+  }
+  if (rem > half || (rem == half && (r & 1))) ++r;
+  return r;
+}
+
+/* Exactly rounded binary16 of (-1)^neg * mag * 2^e2 (overflow gives +-inf). */
+static uint16_t exact_to_half(int neg, unsigned __int128 mag, int e2) {
+  uint16_t sbit = neg ? 0x8000 : 0;
+  if (mag == 0) return sbit;
+  int E = bitlen_u128(mag) - 1 + e2;               /* value in [2^E, 2^(E+1)) */
+  int qe = E - 10 < -24 ? -24 : E - 10;            /* ulp of the result       */
+  unsigned __int128 r = round_to_quantum(mag, e2, qe);
+  if (r == 0) return sbit;
+  if (r >= 2048) { r >>= 1; ++qe; }                /* rounding carried out    */
+  if (r < 1024) return sbit | (uint16_t)r;         /* subnormal (qe == -24)   */
+  int field = qe + 25;                             /* biased exponent         */
+  if (field >= 31) return sbit | 0x7C00;
+  return sbit | (uint16_t)(field << 10) | (uint16_t)(r - 1024);
+}
+
+/* Exactly rounded fp64 of (-1)^neg * mag * 2^e2. */
+static double exact_to_f64(int neg, unsigned __int128 mag, int e2) {
+  if (mag == 0) return neg ? -0.0 : 0.0;
+  int E = bitlen_u128(mag) - 1 + e2;
+  int qe = E - 52 < -1074 ? -1074 : E - 52;
+  unsigned __int128 r = round_to_quantum(mag, e2, qe);
+  double v = ldexp((double)(uint64_t)r, qe);       /* r <= 2^53: exact */
+  return neg ? -v : v;
+}
+
+ORC_EXPORT uint16_t orc_f64_to_half(double v) {
+  if (isnan(v)) return 0x7E00;
+  int neg = signbit(v) ? 1 : 0;
+  if (isinf(v)) return neg ? 0xFC00 : 0x7C00;
+  double a = fabs(v);
+  if (a == 0.0) return neg ? 0x8000 : 0;
+  int ex;
+  double fr = frexp(a, &ex);                       /* a = fr * 2^ex, fr in [0.5, 1) */
+  uint64_t m = (uint64_t)ldexp(fr, 53);            /* exact 53-bit integer          */
+  return exact_to_half(neg, (unsigned __int128)m, ex - 53);
+}
+
+/* fp16 value as an integer multiple of 2^-24; returns 0 for inf / NaN. */
+static int half_to_fixed24(uint16_t h, int64_t* out) {
+  int sign = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+  if (e == 31) return 0;
+  int64_t v = e == 0 ? (int64_t)f : (int64_t)(1024 + f) << (e - 1);
+  *out = sign ? -v : v;
+  return 1;
+}
+
+/* ------------------------------------------------------------------- codec */
+
+static inline unsigned code_at(const uint32_t* words, int64_t K, int64_t n, int64_t k) {
+  uint32_t w = words[n * (K / 8) + k / 8];
+  return (w >> (4 * (k % 8))) & 0xFu;
+}
+
+ORC_EXPORT void orc_unpack(const uint32_t* words, uint8_t* codes, int64_t N, int64_t K) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k)
+      codes[n * K + k] = (uint8_t)code_at(words, K, n, k);
+}
+
+ORC_EXPORT void orc_pack(const uint8_t* codes, uint32_t* words, int64_t N, int64_t K) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t j = 0; j < K / 8; ++j) {
+      uint32_t w = 0;
+      for (int i = 0; i < 8; ++i)
+        w |= (uint32_t)(codes[n * K + 8 * j + i] & 0xFu) << (4 * i);
+      words[n * (K / 8) + j] = w;
+    }
+}
+
+/* Counts words w in [w0, w1) (w1 <= 2^32) for which pack(unpack(w)) != w. */
+ORC_EXPORT int64_t orc_roundtrip_mismatches(uint64_t w0, uint64_t w1) {
+  int64_t bad = 0;
+  for (uint64_t v = w0; v < w1; ++v) {
+    uint32_t w = (uint32_t)v, back;
+    uint8_t c[8];
+    orc_unpack(&w, c, 1, 8);
+    orc_pack(c, &back, 1, 8);
+    bad += back != w;
+  }
+  return bad;
+}
+
+/* -------------------------------------------------------------------- GEMV */
+
+/* Y[m][i] = sum_k (q[n][k] - 7) * s[n][k/32] * X[m][k], n = rows[i] (or i when
+ * rows is NULL), accumulated in fp64 in ascending k.  X is [M][K], Y is
+ * [M][n_rows].  Returns 0, or -1 on a bad shape. */
+ORC_EXPORT int orc_gemv_f64(const uint32_t* words, const uint16_t* scales, const uint16_t* X,
+                            int64_t M, int64_t N, int64_t K, const int64_t* rows,
+                            int64_t n_rows, double* Y) {
+  if (M < 1 || N < 1 || K < 32 || K % 32) return -1;
+  double* x = (double*)malloc(sizeof(double) * (size_t)K);
+  double* s = (double*)malloc(sizeof(double) * (size_t)(K / 32));
+  if (!x || !s) { free(x); free(s); return -1; }
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t k = 0; k < K; ++k) x[k] = orc_half_to_f64(X[m * K + k]);
+    for (int64_t i = 0; i < n_rows; ++i) {
+      int64_t n = rows ? rows[i] : i;
+      if (n < 0 || n >= N) { free(x); free(s); return -1; }
+      for (int64_t g = 0; g < K / 32; ++g) s[g] = orc_half_to_f64(scales[n * (K / 32) + g]);
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        int q = (int)code_at(words, K, n, k);
+        acc += ((double)(q - 7) * s[k / 32]) * x[k];
+      }
+      Y[m * n_rows + i] = acc;
+    }
+  }
+  free(x);
+  free(s);
+  return 0;
+}
+
+/* Exact evaluation of the same sum in __int128 (units of 2^-48), rounded once
+ * to fp64 (Y64) and to fp16 (Y16; either may be NULL).  Returns 0, -1 on a bad
+ * shape, -2 if an input is inf or NaN. */
+ORC_EXPORT int orc_gemv_exact(const uint32_t* words, const uint16_t* scales, const uint16_t* X,
+                              int64_t M, int64_t N, int64_t K, const int64_t* rows,
+                              int64_t n_rows, double* Y64, uint16_t* Y16) {
+  if (M < 1 || N < 1 || K < 32 || K % 32 || K > (1 << 20)) return -1;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t i = 0; i < n_rows; ++i) {
+      int64_t n = rows ? rows[i] : i;
+      if (n < 0 || n >= N) return -1;
+      __int128 acc = 0;
+      for (int64_t k = 0; k < K; ++k) {
+        int64_t sv, xv;
+        if (!half_to_fixed24(scales[n * (K / 32) + k / 32], &sv)) return -2;
+        if (!half_to_fixed24(X[m * K + k], &xv)) return -2;
+        int q = (int)code_at(words, K, n, k);
+        acc += (__int128)(q - 7) * (__int128)sv * (__int128)xv;
+      }
+      int neg = acc < 0;
+      unsigned __int128 mag = neg ? (unsigned __int128)(-acc) : (unsigned __int128)acc;
+      if (Y64) Y64[m * n_rows + i] = exact_to_f64(neg, mag, -48);
+      if (Y16) Y16[m * n_rows + i] = exact_to_half(neg, mag, -48);
+    }
+  return 0;
+}
+
+/* ||W_n||_2 with W_n[k] = (q[n][k] - 7) * s[n][k/32], for n = rows[i]. */
+ORC_EXPORT int orc_row_norms(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
+                             const int64_t* rows, int64_t n_rows, double* out) {
+  if (N < 1 || K < 32 || K % 32) return -1;
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int64_t n = rows ? rows[i] : i;
+    if (n < 0 || n >= N) return -1;
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double w = (double)((int)code_at(words, K, n, k) - 7) *
+                 orc_half_to_f64(scales[n * (K / 32) + k / 32]);
+      acc += w * w;
+    }
+    out[i] = sqrt(acc);
+  }
+  return 0;
+}
+
+/* ||x||_2 of an fp16 vector. */
+ORC_EXPORT double orc_vec_norm(const uint16_t* x, int64_t K) {
+  double acc = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    double v = orc_half_to_f64(x[k]);
+    acc += v * v;
+  }
+  return sqrt(acc);
+}

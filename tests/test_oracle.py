@@ -1,0 +1,334 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Every check compares the oracle with something it does not share code with:
+numpy's IEEE binary16 conversions, numpy's float64 matrix product over an
+independently decoded weight, hand-worked fixtures (tests/golden), closed forms
+and invariants of the definition, and figures the pages print.
+"""
+import ctypes as C
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import ROOT, load_golden_cases, load_page_figures
+
+
+# ----------------------------------------------------------------- binary16
+
+def test_half_decode_exhaustive_vs_numpy():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float64)
+    lib = oracle._load()
+    got = np.array([lib.orc_half_to_f64(int(v)) for v in h])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_half_encode_vs_numpy():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        # every fp16 value and every midpoint between neighbours (ties)
+        np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64),
+        (np.arange(0, 0x7BFF, dtype=np.uint16).view(np.float16).astype(np.float64) +
+         np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)) / 2,
+        [65504.0, 65519.99, 65520.0, 1e9, 2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -26,
+         5.960464477539063e-08, -0.0, 0.0],
+    ])
+    vals = np.concatenate([vals, -vals])
+    ref = vals.astype(np.float16).view(np.uint16)
+    lib = oracle._load()
+    got = np.array([lib.orc_f64_to_half(float(v)) for v in vals], dtype=np.uint16)
+    bad = np.nonzero(got != ref)[0]
+    assert len(bad) == 0, [(vals[i], hex(got[i]), hex(ref[i])) for i in bad[:5]]
+
+
+# -------------------------------------------------------------------- codec
+
+def test_codec_closed_forms():
+    # nibble i of a word is (word >> 4i) & 0xF (Zero TVM, "Q4F16 quantization format")
+    w = np.array([[0x76543210, 0xFEDCBA98, 0x77777777]], np.uint32)
+    c = oracle.unpack(w)
+    assert c.tolist() == [list(range(16)) + [7] * 8]
+    assert np.array_equal(oracle.pack(c), w)
+
+
+def test_codec_vs_little_endian_byte_view():
+    # Independent decoding: a little-endian uint32 is four bytes, low byte first;
+    # byte b of word j holds elements 8j+2b (low nibble) and 8j+2b+1 (high nibble).
+    rng = np.random.default_rng(2)
+    w = rng.integers(0, 2 ** 32, size=(37, 24), dtype=np.uint64).astype(np.uint32)
+    b = w.astype("<u4").view(np.uint8).reshape(37, 24 * 4)
+    ref = np.empty((37, 24 * 8), np.uint8)
+    ref[:, 0::2] = b & 0xF
+    ref[:, 1::2] = b >> 4
+    assert np.array_equal(oracle.unpack(w), ref)
+    assert np.array_equal(oracle.pack(ref), w)
+
+
+def test_codec_masks_high_bits_of_codes():
+    c = np.array([[0x1F, 0xF0, 0x27, 3, 4, 5, 6, 0xFF]], np.uint8)
+    assert oracle.pack(c)[0, 0] == oracle.pack(c & 0xF)[0, 0]
+
+
+def test_codec_roundtrip_random_and_words():
+    c = synth.codes("t/codes", 3, 64 * 96).reshape(64, 96)
+    assert np.array_equal(oracle.unpack(oracle.pack(c)), c)
+    # every word with a single non-zero nibble, and a 2^22 sub-range
+    single = [v << (4 * i) for i in range(8) for v in range(16)]
+    w = np.array(single, np.uint32).reshape(-1, 1)
+    assert np.array_equal(oracle.pack(oracle.unpack(w)), w)
+    assert oracle.roundtrip_mismatches(0xDEAD0000 - (1 << 21), 0xDEAD0000 + (1 << 21)) == 0
+
+
+@pytest.mark.slow
+@pytest.mark.skipif(os.environ.get("Q4_SLOW") != "1", reason="about a minute; set Q4_SLOW=1")
+def test_codec_roundtrip_all_words():
+    assert oracle.roundtrip_mismatches(0, 1 << 32) == 0
+
+
+# --------------------------------------------------------------------- GEMV
+
+def _dequant_numpy(words, scales):
+    """Independent fp64 dequantisation via the byte view and numpy float16."""
+    N, K8 = words.shape
+    b = words.astype("<u4").view(np.uint8).reshape(N, K8 * 4)
+    q = np.empty((N, K8 * 8), np.int64)
+    q[:, 0::2] = b & 0xF
+    q[:, 1::2] = b >> 4
+    s = scales.view(np.float16).astype(np.float64)
+    return (q - 7).astype(np.float64) * np.repeat(s, 32, axis=1)
+
+
+def _rand_case(seed, N, K, M=1, neg_scales=False):
+    rng = np.random.default_rng(seed)
+    w = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    s = np.abs(rng.standard_normal((N, K // 32)) * 0.01) + 1e-3
+    if neg_scales:
+        s *= rng.choice([-1.0, 1.0], size=s.shape)
+    s = s.astype(np.float16).view(np.uint16)
+    x = rng.standard_normal((M, K)).astype(np.float16).view(np.uint16)
+    return w, s, x
+
+
+@pytest.mark.parametrize("N,K,M", [(1, 32, 1), (7, 64, 1), (33, 160, 3), (64, 256, 8), (5, 1024, 2)])
+def test_f64_and_exact_vs_numpy_matmul(N, K, M):
+    w, s, x = _rand_case(N * 1000 + K + M, N, K, M, neg_scales=True)
+    ref = x.view(np.float16).astype(np.float64) @ _dequant_numpy(w, s).T   # [M][N]
+    y64 = oracle.gemv_f64(w, s, x)
+    ye, y16 = oracle.gemv_exact(w, s, x)
+    scale = np.abs(x.view(np.float16).astype(np.float64)) @ np.abs(_dequant_numpy(w, s)).T
+    assert np.all(np.abs(y64 - ref) <= 1e-13 * scale + 1e-300)
+    assert np.all(np.abs(ye - ref) <= 1e-13 * scale + 1e-300)
+    # the exact result rounded once equals numpy's rounding of the exact fp64 value
+    # whenever that fp64 value is itself exact (always true here: |terms| < 2^53 ulps)
+    assert np.array_equal(y16, ye.astype(np.float16).view(np.uint16))
+
+
+def test_small_config_exact_vs_f64_all_rows():
+    c, s, x = synth.small_config(0)
+    w = oracle.pack(c)
+    y64 = oracle.gemv_f64(w, s, x)
+    ye, y16 = oracle.gemv_exact(w, s, x)
+    assert np.max(np.abs(y64 - ye)) <= 1e-12 * np.max(np.abs(ye))
+    ref = x.view(np.float16).astype(np.float64) @ _dequant_numpy(w, s).T
+    assert np.allclose(ye, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", load_golden_cases("hand_worked_gemv.txt"), ids=lambda c: c["name"])
+def test_hand_worked_fixtures(case):
+    y64 = oracle.gemv_f64(case["words"], case["scales"], case["x"])
+    ye, y16 = oracle.gemv_exact(case["words"], case["scales"], case["x"])
+    assert np.array_equal(y16, case["y16"]), (y16, case["y16"])
+    # the fixtures' decimal values are the exact sums before rounding except for
+    # the tie cases, whose fp16 results are listed; compare the fp16 decoding
+    assert np.array_equal(y16.view(np.float16).astype(np.float64), case["y"])
+    assert np.array_equal(np.array([oracle.f64_to_half(v) for v in y64], np.uint16), case["y16"])
+
+
+def test_closed_form_all_sevens_is_zero():
+    N, K = 9, 96
+    w = np.full((N, K // 8), 0x77777777, np.uint32)
+    _, s, x = _rand_case(5, N, K, 1, neg_scales=True)
+    assert np.all(oracle.gemv_f64(w, s, x[0]) == 0.0)
+    assert np.all(oracle.gemv_exact(w, s, x[0])[1] == 0)
+
+
+def test_closed_form_unit_scale_ones_gives_code_sum():
+    c = synth.codes("t/cs", 4, 12 * 320).reshape(12, 320)
+    w = oracle.pack(c)
+    s = np.full((12, 10), 0x3C00, np.uint16)          # 1.0
+    x = np.full(320, 0x3C00, np.uint16)               # ones
+    expect = (c.astype(np.int64) - 7).sum(axis=1)
+    assert np.array_equal(oracle.gemv_f64(w, s, x), expect.astype(np.float64))
+    assert np.array_equal(oracle.gemv_exact(w, s, x)[1],
+                          expect.astype(np.float16).view(np.uint16))
+
+
+def test_one_hot_input_selects_one_weight():
+    # non-square (N=5, K=96): pins nibble, word and group indexing and orientation
+    N, K = 5, 96
+    c = synth.codes("t/oh", 6, N * K).reshape(N, K)
+    w = oracle.pack(c)
+    s = synth.scales_uniform("t/ohs", 6, N * K // 32, 0.005, 0.02).reshape(N, K // 32)
+    sv = s.view(np.float16).astype(np.float64)
+    for k in range(K):
+        x = np.zeros(K, np.uint16)
+        x[k] = 0x3C00
+        expect = (c[:, k].astype(np.float64) - 7) * sv[:, k // 32]
+        assert np.array_equal(oracle.gemv_f64(w, s, x), expect), k
+        assert np.array_equal(oracle.gemv_exact(w, s, x)[1],
+                              expect.astype(np.float16).view(np.uint16)), k
+
+
+def test_scale_group_isolation():
+    N, K = 4, 128
+    c = synth.codes("t/g", 7, N * K).reshape(N, K)
+    w = oracle.pack(c)
+    x = synth.activations("t/gx", 7, K)
+    xv = x.view(np.float16).astype(np.float64)
+    for g in range(K // 32):
+        s = np.zeros((N, K // 32), np.uint16)
+        s[:, g] = 0x3C00
+        expect = ((c[:, 32 * g:32 * g + 32].astype(np.float64) - 7) * xv[32 * g:32 * g + 32]).sum(1)
+        assert np.allclose(oracle.gemv_exact(w, s, x)[0], expect, rtol=0, atol=1e-12)
+
+
+def test_invariants_scaling_and_row_permutation():
+    w, s, x = _rand_case(8, 40, 256, 1, neg_scales=True)
+    y = oracle.gemv_exact(w, s, x[0])[0]
+    s2 = (s.view(np.float16).astype(np.float64) * 2).astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.gemv_exact(w, s2, x[0])[0], 2 * y)
+    perm = np.random.default_rng(9).permutation(40)
+    assert np.array_equal(oracle.gemv_exact(w[perm], s[perm], x[0])[0], y[perm])
+    rows = np.array([39, 0, 17, 17])
+    assert np.array_equal(oracle.gemv_f64(w, s, x[0], rows=rows), oracle.gemv_f64(w, s, x[0])[rows])
+
+
+def test_exact_rejects_inf_and_nan():
+    w, s, x = _rand_case(10, 2, 32)
+    x = x.copy()
+    x[0, 3] = 0x7C00
+    with pytest.raises(ValueError):
+        oracle.gemv_exact(w, s, x[0])
+    assert np.isnan(oracle.gemv_f64(w, s, x[0])).any() or \
+        np.isinf(oracle.gemv_f64(w, s, x[0])).any()
+
+
+def test_tolerance_helpers():
+    w, s, x = _rand_case(11, 6, 64)
+    ref = _dequant_numpy(w, s)
+    assert np.allclose(oracle.row_norms(w, s), np.linalg.norm(ref, axis=1), rtol=1e-14)
+    assert np.isclose(oracle.vec_norm(x[0]),
+                      np.linalg.norm(x[0].view(np.float16).astype(np.float64)), rtol=1e-14)
+    # fp16 output rounding alone stays far inside the tolerance (Cauchy-Schwarz)
+    ye, y16 = oracle.gemv_exact(w, s, x[0])
+    err = np.abs(y16.view(np.float16).astype(np.float64) - ye).max()
+    assert err <= 2e-3 * oracle.vec_norm(x[0]) * oracle.row_norms(w, s).max()
+
+
+# ------------------------------------------------------- figures of the pages
+
+def test_page_figures_bytes_and_shapes():
+    f = load_page_figures()
+    assert synth.PHI3["D"] == f["phi3_D"][0][0]
+    assert synth.PHI3["LAYERS"] == f["phi3_layers"][0][0]
+    assert synth.PHI3["FFN"] == f["phi3_ffn"][0][0]
+    assert synth.PHI3["VOCAB"] == f["phi3_vocab"][0][0]
+    assert synth.TWO_B["D"] == f["twob_hidden"][0][0]
+    assert synth.TWO_B["FFN"] == f["twob_intermediate"][0][0]
+    m = synth.Matrix("x", 1, 32)
+    assert m.weight_bytes == f["q4f16_1_bytes_per_32"][0][0]
+    total = sum(synth.Matrix(l, N, K).weight_bytes for l, N, K in synth.sweep_shapes("phi3"))
+    assert total == 2_093_838_336
+    assert round(total / 1e9, 2) == f["phi3_token_weight_gb"][0][0]
+    for K, iters in f["lane_iters"]:
+        assert K / 8 / 64 == iters     # 64 lanes, one uint32 (8 weights) per iteration
+
+
+def test_sweep_descriptor_lists():
+    phi = synth.sweep_shapes("phi3")
+    assert len(phi) == 129 and phi[-1][1:] == (32064, 3072)
+    assert phi[0][1:] == (9216, 3072) and phi[3][1:] == (3072, 8192)
+    two = synth.sweep_shapes("2b")
+    assert len(two) == 113 and two[-1][1:] == (151936, 2048)
+    w2 = sum(synth.Matrix(l, N, K).weight_bytes for l, N, K in two)
+    assert w2 == 967_753_728
+
+
+# ------------------------------------- planted mistakes must break the pins
+
+MUTATIONS = {
+    "sign": ("acc += ((double)(q - 7) * s[k / 32]) * x[k];",
+             "acc += ((double)(7 - q) * s[k / 32]) * x[k];"),
+    "scale_index": ("acc += ((double)(q - 7) * s[k / 32]) * x[k];",
+                    "acc += ((double)(q - 7) * s[k / 8 % (K / 32)]) * x[k];"),
+    "dropped_term": ("for (int64_t k = 0; k < K; ++k) {\n        int q = (int)code_at(words, K, n, k);\n        acc +=",
+                     "for (int64_t k = 0; k < K - 1; ++k) {\n        int q = (int)code_at(words, K, n, k);\n        acc +="),
+    "nibble_order": ("return (w >> (4 * (k % 8))) & 0xFu;", "return (w >> (4 * (7 - k % 8))) & 0xFu;"),
+    "transposed": ("uint32_t w = words[n * (K / 8) + k / 8];", "uint32_t w = words[(k / 8) * (K / 8) + n % (K / 8)];"),
+    "zero_point_8": ("acc += ((double)(q - 7) * s[k / 32]) * x[k];",
+                     "acc += ((double)(q - 8) * s[k / 32]) * x[k];"),
+}
+
+
+def _build_mutant(tmp, name):
+    src = open(os.path.join(ROOT, "oracle", "q4_oracle.c")).read()
+    a, b = MUTATIONS[name]
+    assert a in src, name
+    path = os.path.join(tmp, f"m_{name}.c")
+    open(path, "w").write(src.replace(a, b))
+    so = os.path.join(tmp, f"m_{name}.so")
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-o", so, path, "-lm"])
+    lib = C.CDLL(so)
+    lib.orc_gemv_f64.argtypes = [C.c_void_p] * 3 + [C.c_int64] * 3 + [C.c_void_p, C.c_int64, C.c_void_p]
+    return lib
+
+
+def _mutant_gemv(lib, w, s, x):
+    w = np.ascontiguousarray(w)
+    s = np.ascontiguousarray(s)
+    x = np.ascontiguousarray(x)
+    N, K = w.shape[0], w.shape[1] * 8
+    y = np.empty(N)
+    lib.orc_gemv_f64(w.ctypes.data, s.ctypes.data, x.ctypes.data, 1, N, K, None, N, y.ctypes.data)
+    return y
+
+
+def _pins_pass(gemv):
+    """A subset of the pins above, run against a given gemv(w, s, x) -> fp64 y."""
+    ok = True
+    for case in load_golden_cases("hand_worked_gemv.txt"):
+        y = gemv(case["words"], case["scales"], case["x"])
+        ok &= np.array_equal(y.astype(np.float16).view(np.uint16), case["y16"])
+    N, K = 5, 96
+    c = synth.codes("t/oh", 6, N * K).reshape(N, K)
+    w = oracle.pack(c)
+    s = synth.scales_uniform("t/ohs", 6, N * K // 32, 0.005, 0.02).reshape(N, K // 32)
+    sv = s.view(np.float16).astype(np.float64)
+    for k in range(K):
+        x = np.zeros(K, np.uint16)
+        x[k] = 0x3C00
+        ok &= np.array_equal(gemv(w, s, x), (c[:, k].astype(np.float64) - 7) * sv[:, k // 32])
+    return bool(ok)
+
+
+def test_pins_pass_on_the_oracle():
+    assert _pins_pass(lambda w, s, x: oracle.gemv_f64(w, s, x))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = _build_mutant(tmp, name)
+        assert not _pins_pass(lambda w, s, x: _mutant_gemv(lib, w, s, x)), name
