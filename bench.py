@@ -1,0 +1,183 @@
+#!/usr/bin/env python3
+"""Benchmark: achieved HBM GB/s of the q4f16_1 decode-step weight sweep on one GPU.
+
+Workload (one "step"): the full Phi-3-mini-shaped decode step at M = 1 --
+32 layers x {qkv 3072->9216, o 3072->3072, gate_up 3072->16384, down 8192->3072}
+plus lm_head 3072->32064, 129 GEMVs over 2,093,838,336 bytes of q4f16_1 words and
+scales (Zero TVM documentation, "The memory-bandwidth ceiling": ~2.09 GB per
+token), seeded synthetic codes and scales, x reused by every layer.  One step is
+one q4_decode_step call over the 129 descriptors, inputs resident in HBM.
+
+Prints ONE JSON line (rank 0):
+  value = algorithmic bytes per step / time per step, in GB/s;
+  roofline = the dominant kernel's algorithmic bytes per launch / its average
+             launch duration (HIP events on the stream it runs on) vs 8 TB/s;
+  cpu_baseline = the CPU oracle on this host over one full step (single thread).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "achieved HBM GB/s (% of peak) and projected decode tok/s, q4 GEMV sweep"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mode", choices=["auto", "launch_each"], default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time only the decode step (for profiler runs)")
+    return ap.parse_args()
+
+
+def build_sweep(torch, q4, synth, np, model="phi3", M=1):
+    shapes = synth.sweep_shapes(model)
+    xs = {}
+    for K in sorted({K for _, _, K in shapes}):
+        h = synth.activations(f"{model}/x{K}", 0, M * K)
+        xs[K] = torch.from_numpy(h.view(np.int16)).cuda().view(torch.float16)
+    descs, meta = [], []
+    for label, N, K in shapes:
+        m = synth.Matrix(label, N, K)
+        W = m.words_torch("cuda")
+        S = torch.from_numpy(m.scales().view(np.int16)).cuda().view(torch.float16)
+        Y = torch.empty(N * M, dtype=torch.float16, device="cuda")
+        descs.append((W, S, xs[K], Y))
+        meta.append((label, N, K))
+    return descs, meta
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import bit_weight_streaming_q4f16_amd as q4
+
+    torch.cuda.set_device(0)
+    q4.load()
+    stream = torch.cuda.Stream()          # default priority
+    t0 = time.time()
+    descs, meta = build_sweep(torch, q4, synth, np)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    layers = q4.make_layers(descs)
+    flags = q4.STEP_LAUNCH_EACH if args.mode == "launch_each" else 0
+    ws_bytes = q4.q4_decode_step_workspace_bytes(layers, 1, flags)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    step_bytes = sum(synth.algorithmic_bytes(1, N, K) for _, N, K in meta)
+    weight_bytes = sum(synth.Matrix(l, N, K).weight_bytes for l, N, K in meta)
+
+    def step():
+        q4.q4_decode_step(layers, 1, flags, ws=ws, ws_bytes=ws_bytes, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        h1 = time.perf_counter()
+    ms = e0.elapsed_time(e1) / args.steps
+    host_ms = (h1 - h0) * 1e3 / args.steps
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    if gbs > PEAK_GBS * 1.02:
+        raise SystemExit(f"measured {gbs:.0f} GB/s is above the HBM peak: measurement error")
+
+    result = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "q4f16/f32acc",
+        "data": "synthetic (seeded SplitMix64 codes/scales, N(0,1) x)",
+        "config": {"workload": "phi3-mini decode-step weight sweep, M=1: 32 x {qkv 3072->9216, "
+                               "o 3072->3072, gate_up 3072->16384, down 8192->3072} + lm_head "
+                               "3072->32064, q4f16_1 group 32",
+                   "gemvs_per_step": len(meta), "algorithmic_bytes_per_step": step_bytes,
+                   "weight_bytes_per_step": weight_bytes, "mode": args.mode},
+        "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
+        "projected_tok_s": round(1e3 / ms, 1),
+        "host_ms_per_step": round(host_ms, 5),
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.only_step:
+        # dominant kernel: one whole step when the step is one launch; otherwise the
+        # step's launches taken together (bytes per step / summed launch time)
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
+                              "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None,
+                              "kernel": "q4_decode_step"}
+        if not args.no_probe:
+            result["probe_read_gbs"] = probe_read(torch, q4, stream)
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(np, torch, descs, meta)
+    print(json.dumps(result), flush=True)
+
+
+def probe_read(torch, q4, stream, nbytes=4 << 30, reps=10):
+    """Streaming-read ceiling: best over grid sizes of reading a 4 GiB buffer."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = {}
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    with torch.cuda.stream(stream):
+        for mult in (2, 4, 8, 16, 32):
+            blocks = cus * mult
+            q4.q4_probe_read(buf, sink, blocks, stream=stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                q4.q4_probe_read(buf, sink, blocks, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best[blocks] = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    b = max(best, key=best.get)
+    return {"best_gbs": round(best[b], 1), "blocks": b,
+            "sweep": {str(k): round(v, 1) for k, v in best.items()}}
+
+
+def cpu_baseline(np, torch, descs, meta):
+    """The CPU oracle (plain C, fp64, one thread) over one full step."""
+    import oracle
+    import synth
+    x_host = {}
+    total_bytes, t = 0, 0.0
+    for (W, S, X, Y), (label, N, K) in zip(descs, meta):
+        w = W.cpu().numpy().view(np.uint32)
+        s = S.view(torch.int16).cpu().numpy().view(np.uint16)
+        if K not in x_host:
+            x_host[K] = X.view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.gemv_f64(w, s, x_host[K])
+        t += time.perf_counter() - t0
+        total_bytes += synth.algorithmic_bytes(1, N, K)
+    return {"value": round(total_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(t, 2),
+            "sample": f"one full step ({len(meta)} GEMVs, all rows), fp64 plain C oracle"}
+
+
+if __name__ == "__main__":
+    main()

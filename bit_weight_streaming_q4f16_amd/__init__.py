@@ -1,0 +1,260 @@
+"""Python binding of the q4f16_1 decode library (include/q4f16.h).
+
+Argument marshalling only: every function takes torch tensors on the GPU,
+checks dtype / device / contiguity / shape, and calls the C ABI entry point of
+the same name on the current HIP stream.  Every step of the computation runs in
+the HIP kernels of libq4f16.so; there is no fallback.  If the library is not
+built, loading fails with an error that says how to build it.
+
+Tensor conventions: packed words are int32 tensors holding uint32 bit patterns
+([N][K/8]); scales, activations and outputs are float16 tensors ([N][K/32],
+[K] or [M][K], [N] or [M][N]); codes are uint8 ([N][K]).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+__all__ = [
+    "Q4Error", "load", "lib_path", "q4_version", "q4_pack", "q4_unpack", "q4_gemv",
+    "q4_gemv_splitk", "q4_gemv_batched", "q4_workspace_bytes", "q4_splitk_workspace_bytes",
+    "q4_decode_step", "q4_decode_step_workspace_bytes", "q4_probe_read", "q4_probe_copy",
+    "Layer", "STEP_LAUNCH_EACH",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "_lib", "libq4f16.so")
+_lock = threading.Lock()
+_lib = None
+
+STEP_LAUNCH_EACH = 0x1
+
+STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
+          4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED"}
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        self.code = code
+        self.name = STATUS.get(code, f"Q4_ERR_{code}")
+        self.detail = detail
+        super().__init__(f"{self.name}: {detail}")
+
+
+class Layer(C.Structure):
+    """q4_layer: one GEMV of a decode step (device pointers and sizes)."""
+    _fields_ = [("words", C.c_void_p), ("scales", C.c_void_p), ("x", C.c_void_p),
+                ("y", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64)]
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def load():
+    """Load libq4f16.so (built by __graft_entry__.build() or
+    ``python -m bit_weight_streaming_q4f16_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB):
+            raise RuntimeError(f"{_LIB} is missing: build it with "
+                               "`python -m bit_weight_streaming_q4f16_amd.build`")
+        lib = C.CDLL(_LIB)
+        p, i64, sz, i32 = C.c_void_p, C.c_int64, C.c_size_t, C.c_int
+        sigs = {
+            "q4_status_str": ([i32], C.c_char_p),
+            "q4_last_error": ([], C.c_char_p),
+            "q4_version": ([], i32),
+            "q4_pack": ([p, p, i64, i64, p], i32),
+            "q4_unpack": ([p, p, i64, i64, p], i32),
+            "q4_gemv": ([p, p, p, p, i64, i64, p, sz, p], i32),
+            "q4_gemv_splitk": ([p, p, p, p, i64, i64, i64, p, sz, p], i32),
+            "q4_gemv_batched": ([p, p, p, p, i64, i64, i64, p, sz, p], i32),
+            "q4_workspace_bytes": ([i64, i64, i64], sz),
+            "q4_splitk_workspace_bytes": ([i64, i64, i64], sz),
+            "q4_decode_step": ([p, i64, i64, C.c_uint32, p, sz, p], i32),
+            "q4_decode_step_workspace_bytes": ([p, i64, i64, C.c_uint32], sz),
+            "q4_probe_read": ([p, sz, p, i64, p], i32),
+            "q4_probe_copy": ([p, p, sz, p], i32),
+        }
+        for name, (args, res) in sigs.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = lib
+        return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise Q4Error(rc, load().q4_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dev(t, name, dtype):
+    if t is None:
+        raise Q4Error(1, f"{name} is None")
+    if not t.is_cuda:
+        raise Q4Error(5, f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise Q4Error(2, f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise Q4Error(2, f"{name} must be contiguous")
+    return t
+
+
+def _ws(nbytes, ws, device):
+    torch = _torch()
+    if nbytes == 0:
+        return ws, (ws.numel() * ws.element_size() if ws is not None else 0)
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def q4_version() -> int:
+    return load().q4_version()
+
+
+def q4_pack(codes, words=None, stream=None):
+    """codes uint8 [N][K] -> words int32 [N][K/8] (uint32 bit patterns)."""
+    torch = _torch()
+    _dev(codes, "codes", torch.uint8)
+    N, K = codes.shape
+    if words is None:
+        words = torch.empty((N, K // 8), dtype=torch.int32, device=codes.device)
+    _dev(words, "words", torch.int32)
+    _check(load().q4_pack(_ptr(codes), _ptr(words), N, K, _stream(stream)))
+    return words
+
+
+def q4_unpack(words, codes=None, stream=None):
+    """words int32 [N][K/8] -> codes uint8 [N][K]."""
+    torch = _torch()
+    _dev(words, "words", torch.int32)
+    N, K8 = words.shape
+    if codes is None:
+        codes = torch.empty((N, 8 * K8), dtype=torch.uint8, device=words.device)
+    _dev(codes, "codes", torch.uint8)
+    _check(load().q4_unpack(_ptr(words), _ptr(codes), N, 8 * K8, _stream(stream)))
+    return codes
+
+
+def q4_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().q4_workspace_bytes(M, N, K))
+
+
+def q4_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
+    return int(load().q4_splitk_workspace_bytes(M, N, splits))
+
+
+def _gemv_shapes(words, scales):
+    torch = _torch()
+    _dev(words, "words", torch.int32)
+    _dev(scales, "scales", torch.float16)
+    N, K8 = words.shape
+    K = 8 * K8
+    if tuple(scales.shape) != (N, K // 32):
+        raise Q4Error(2, f"scales shape {tuple(scales.shape)} != {(N, K // 32)}")
+    return N, K
+
+
+def q4_gemv(words, scales, x, y=None, ws=None, stream=None):
+    """y[N] = dequant(words, scales) @ x[K] (fp16 out, fp32 accumulation)."""
+    torch = _torch()
+    N, K = _gemv_shapes(words, scales)
+    _dev(x, "x", torch.float16)
+    if x.numel() != K:
+        raise Q4Error(2, f"x has {x.numel()} elements, K = {K}")
+    if y is None:
+        y = torch.empty(N, dtype=torch.float16, device=words.device)
+    _dev(y, "y", torch.float16)
+    ws, wsb = _ws(q4_workspace_bytes(1, N, K), ws, words.device)
+    _check(load().q4_gemv(_ptr(words), _ptr(scales), _ptr(x), _ptr(y), N, K, _ptr(ws), wsb,
+                          _stream(stream)))
+    return y
+
+
+def q4_gemv_splitk(words, scales, x, splits: int, y=None, ws=None, stream=None):
+    torch = _torch()
+    N, K = _gemv_shapes(words, scales)
+    _dev(x, "x", torch.float16)
+    if y is None:
+        y = torch.empty(N, dtype=torch.float16, device=words.device)
+    _dev(y, "y", torch.float16)
+    ws, wsb = _ws(q4_splitk_workspace_bytes(1, N, splits), ws, words.device)
+    _check(load().q4_gemv_splitk(_ptr(words), _ptr(scales), _ptr(x), _ptr(y), N, K, splits,
+                                 _ptr(ws), wsb, _stream(stream)))
+    return y
+
+
+def q4_gemv_batched(words, scales, X, Y=None, ws=None, stream=None):
+    """Y[M][N] = X[M][K] @ dequant(words, scales)^T for M <= 8."""
+    torch = _torch()
+    N, K = _gemv_shapes(words, scales)
+    _dev(X, "X", torch.float16)
+    if X.dim() != 2 or X.shape[1] != K:
+        raise Q4Error(2, f"X shape {tuple(X.shape)} must be [M][{K}]")
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=words.device)
+    _dev(Y, "Y", torch.float16)
+    ws, wsb = _ws(q4_workspace_bytes(M, N, K), ws, words.device)
+    _check(load().q4_gemv_batched(_ptr(words), _ptr(scales), _ptr(X), _ptr(Y), M, N, K,
+                                  _ptr(ws), wsb, _stream(stream)))
+    return Y
+
+
+def make_layers(descs):
+    """descs: iterable of (words, scales, x, y) tensors -> ctypes array of Layer."""
+    descs = list(descs)
+    arr = (Layer * len(descs))()
+    for i, (w, s, x, y) in enumerate(descs):
+        N, K8 = w.shape
+        arr[i] = Layer(w.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), N, 8 * K8)
+    return arr
+
+
+def q4_decode_step_workspace_bytes(layers, M: int = 1, flags: int = 0) -> int:
+    return int(load().q4_decode_step_workspace_bytes(layers, len(layers), M, flags))
+
+
+def q4_decode_step(layers, M: int = 1, flags: int = 0, ws=None, ws_bytes=None, stream=None):
+    """Run the GEMVs of a Layer array (see make_layers) in order."""
+    torch = _torch()
+    need = q4_decode_step_workspace_bytes(layers, M, flags)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    wsb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
+    _check(load().q4_decode_step(layers, len(layers), M, flags, _ptr(ws), wsb, _stream(stream)))
+    return ws
+
+
+def q4_probe_read(buf, sink, blocks: int = 0, stream=None):
+    _check(load().q4_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), blocks,
+                                _stream(stream)))
+
+
+def q4_probe_copy(src, dst, stream=None):
+    _check(load().q4_probe_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
+                                _stream(stream)))

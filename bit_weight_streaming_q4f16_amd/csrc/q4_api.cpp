@@ -1,0 +1,288 @@
+// C-ABI entry points of include/q4f16.h: argument validation, plan choice and
+// launches.  Validation runs on the host before any HIP call, so argument errors
+// never enqueue work (and can be checked on a machine without a GPU).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/q4f16.h"
+#include "q4_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int ok() {
+  g_error.clear();
+  return Q4_OK;
+}
+
+__attribute__((format(printf, 2, 3))) int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int device_error(hipError_t e, const char* what) {
+  return fail(Q4_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int64_t N, int64_t K) {
+  if (N < 1) return fail(Q4_ERR_SHAPE, "N = %lld: must be >= 1", (long long)N);
+  if (K < 32 || K % 32) return fail(Q4_ERR_SHAPE, "K = %lld: must be a positive multiple of 32",
+                                    (long long)K);
+  if (N > (int64_t)INT32_MAX || K / 32 > (int64_t)INT32_MAX / 8)
+    return fail(Q4_ERR_UNSUPPORTED, "N = %lld, K = %lld: too large", (long long)N, (long long)K);
+  if (N * (K / 32) > ((int64_t)1 << 40))
+    return fail(Q4_ERR_UNSUPPORTED, "N * K / 32 = %lld: too large", (long long)(N * (K / 32)));
+  return Q4_OK;
+}
+
+// Validate one GEMV's tensors.  `what` names the call for the error text.
+int check_gemv(const char* what, const uint32_t* words, const uint16_t* scales,
+               const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K) {
+  if (!words) return fail(Q4_ERR_NULL, "%s: words is NULL", what);
+  if (!scales) return fail(Q4_ERR_NULL, "%s: scales is NULL", what);
+  if (!x) return fail(Q4_ERR_NULL, "%s: x is NULL", what);
+  if (!y) return fail(Q4_ERR_NULL, "%s: y is NULL", what);
+  if (M < 1 || M > q4::kMaxM)
+    return fail(Q4_ERR_SHAPE, "%s: M = %lld: must be in [1, %d]", what, (long long)M, q4::kMaxM);
+  int rc = check_shape(N, K);
+  if (rc) return fail(rc, "%s: %s", what, g_error.c_str());
+  if (!aligned(words, 16)) return fail(Q4_ERR_ALIGN, "%s: words %p not 16-byte aligned", what,
+                                       (const void*)words);
+  if (!aligned(x, 16)) return fail(Q4_ERR_ALIGN, "%s: x %p not 16-byte aligned", what,
+                                   (const void*)x);
+  if (!aligned(scales, 2)) return fail(Q4_ERR_ALIGN, "%s: scales %p not 2-byte aligned", what,
+                                       (const void*)scales);
+  if (!aligned(y, 2)) return fail(Q4_ERR_ALIGN, "%s: y %p not 2-byte aligned", what,
+                                  (const void*)y);
+  // the output must not overlap an input
+  const uintptr_t y0 = reinterpret_cast<uintptr_t>(y), y1 = y0 + (uintptr_t)(2 * M * N);
+  auto overlaps = [&](const void* p, int64_t bytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + (uintptr_t)bytes;
+    return a0 < y1 && y0 < a1;
+  };
+  if (overlaps(words, N * K / 2) || overlaps(scales, N * K / 16) || overlaps(x, 2 * M * K))
+    return fail(Q4_ERR_SHAPE, "%s: y overlaps an input", what);
+  return Q4_OK;
+}
+
+int check_ws(const char* what, void* ws, size_t have, size_t need) {
+  if (need == 0) return Q4_OK;
+  if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: needs %zu workspace bytes, ws is NULL", what, need);
+  if (have < need)
+    return fail(Q4_ERR_WORKSPACE, "%s: needs %zu workspace bytes, got %zu", what, need, have);
+  if (!aligned(ws, 16)) return fail(Q4_ERR_ALIGN, "%s: ws %p not 16-byte aligned", what, ws);
+  return Q4_OK;
+}
+
+std::mutex g_dev_mutex;
+q4::DeviceInfo g_dev[64];
+
+}  // namespace
+
+namespace q4 {
+
+const DeviceInfo* device_info() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceInfo& d = g_dev[dev];
+  if (d.id < 0) {
+    int cus = 0, lds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    d.cus = cus;
+    d.lds_per_block = (size_t)lds;
+    d.id = dev;
+  }
+  return &d;
+}
+
+}  // namespace q4
+
+extern "C" {
+
+const char* q4_status_str(int status) {
+  switch (status) {
+    case Q4_OK: return "Q4_OK";
+    case Q4_ERR_NULL: return "Q4_ERR_NULL";
+    case Q4_ERR_SHAPE: return "Q4_ERR_SHAPE";
+    case Q4_ERR_ALIGN: return "Q4_ERR_ALIGN";
+    case Q4_ERR_WORKSPACE: return "Q4_ERR_WORKSPACE";
+    case Q4_ERR_DEVICE: return "Q4_ERR_DEVICE";
+    case Q4_ERR_UNSUPPORTED: return "Q4_ERR_UNSUPPORTED";
+    default: return "Q4_ERR_UNKNOWN";
+  }
+}
+
+const char* q4_last_error(void) { return g_error.c_str(); }
+
+int q4_version(void) { return 100; }
+
+int q4_pack(const uint8_t* codes, uint32_t* words, int64_t N, int64_t K, q4_stream_t stream) {
+  if (!codes) return fail(Q4_ERR_NULL, "q4_pack: codes is NULL");
+  if (!words) return fail(Q4_ERR_NULL, "q4_pack: words is NULL");
+  if (int rc = check_shape(N, K)) return fail(rc, "q4_pack: %s", g_error.c_str());
+  if (!aligned(words, 16)) return fail(Q4_ERR_ALIGN, "q4_pack: words not 16-byte aligned");
+  hipError_t e = q4::launch_pack(codes, words, N, K, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_pack");
+}
+
+int q4_unpack(const uint32_t* words, uint8_t* codes, int64_t N, int64_t K, q4_stream_t stream) {
+  if (!words) return fail(Q4_ERR_NULL, "q4_unpack: words is NULL");
+  if (!codes) return fail(Q4_ERR_NULL, "q4_unpack: codes is NULL");
+  if (int rc = check_shape(N, K)) return fail(rc, "q4_unpack: %s", g_error.c_str());
+  if (!aligned(words, 16)) return fail(Q4_ERR_ALIGN, "q4_unpack: words not 16-byte aligned");
+  hipError_t e = q4::launch_unpack(words, codes, N, K, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_unpack");
+}
+
+size_t q4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > q4::kMaxM || N < 1 || K < 32 || K % 32) return 0;
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return 0;
+  return q4::plan_auto(*d, M, N, K).ws_bytes;
+}
+
+size_t q4_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
+  if (M < 1 || M > q4::kMaxM || N < 1 || splits < 2) return 0;
+  return (size_t)4 * (size_t)splits * (size_t)M * (size_t)N;
+}
+
+static int gemv_common(const char* what, const uint32_t* words, const uint16_t* scales,
+                       const uint16_t* x, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                       int64_t splits, void* ws, size_t ws_bytes, q4_stream_t stream) {
+  if (int rc = check_gemv(what, words, scales, x, y, M, N, K)) return rc;
+  if (splits != 0 && (splits < 1 || splits > q4::kMaxSplits || splits > K / 32))
+    return fail(Q4_ERR_SHAPE, "%s: splits = %lld: must be in [1, min(64, K/32 = %lld)]", what,
+                (long long)splits, (long long)(K / 32));
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return fail(Q4_ERR_DEVICE, "%s: no HIP device", what);
+  q4::GemvPlan p = splits == 0 ? q4::plan_auto(*d, M, N, K)
+                               : q4::plan_splits(*d, M, N, K, (int)splits);
+  const int64_t gmax = (K / 32 + p.splits - 1) / p.splits;
+  if (gmax > q4::max_groups_per_slice(*d, M))
+    return fail(Q4_ERR_UNSUPPORTED, "%s: a K slice of %lld groups does not fit in LDS; use more "
+                "splits", what, (long long)gmax);
+  if (int rc = check_ws(what, ws, ws_bytes, p.ws_bytes)) return rc;
+  q4::GemvArgs a{words, scales, x, y, M, N, K};
+  hipError_t e = q4::launch_gemv(*d, a, p, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, what);
+}
+
+int q4_gemv(const uint32_t* words, const uint16_t* scales, const uint16_t* x, uint16_t* y,
+            int64_t N, int64_t K, void* ws, size_t ws_bytes, q4_stream_t stream) {
+  return gemv_common("q4_gemv", words, scales, x, y, 1, N, K, 0, ws, ws_bytes, stream);
+}
+
+int q4_gemv_splitk(const uint32_t* words, const uint16_t* scales, const uint16_t* x,
+                   uint16_t* y, int64_t N, int64_t K, int64_t splits, void* ws,
+                   size_t ws_bytes, q4_stream_t stream) {
+  if (splits < 1) return fail(Q4_ERR_SHAPE, "q4_gemv_splitk: splits = %lld: must be >= 1",
+                              (long long)splits);
+  return gemv_common("q4_gemv_splitk", words, scales, x, y, 1, N, K, splits, ws, ws_bytes,
+                     stream);
+}
+
+int q4_gemv_batched(const uint32_t* words, const uint16_t* scales, const uint16_t* X,
+                    uint16_t* Y, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                    q4_stream_t stream) {
+  return gemv_common("q4_gemv_batched", words, scales, X, Y, M, N, K, 0, ws, ws_bytes, stream);
+}
+
+size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, int64_t M,
+                                      uint32_t flags) {
+  (void)flags;
+  if (!layers || n_layers < 1 || M < 1 || M > q4::kMaxM) return 0;
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return 0;
+  size_t need = 0;
+  for (int64_t i = 0; i < n_layers; ++i) {
+    const q4_layer& L = layers[i];
+    if (L.N < 1 || L.K < 32 || L.K % 32) return 0;
+    const size_t b = q4::plan_auto(*d, M, L.N, L.K).ws_bytes;
+    if (b > need) need = b;
+  }
+  return need;
+}
+
+int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t flags,
+                   void* ws, size_t ws_bytes, q4_stream_t stream) {
+  if (!layers) return fail(Q4_ERR_NULL, "q4_decode_step: layers is NULL");
+  if (n_layers < 1) return fail(Q4_ERR_SHAPE, "q4_decode_step: n_layers = %lld: must be >= 1",
+                                (long long)n_layers);
+  if (flags & ~Q4_STEP_LAUNCH_EACH)
+    return fail(Q4_ERR_SHAPE, "q4_decode_step: unknown flags 0x%x", flags);
+  char what[64];
+  for (int64_t i = 0; i < n_layers; ++i) {
+    const q4_layer& L = layers[i];
+    snprintf(what, sizeof what, "q4_decode_step: layers[%lld]", (long long)i);
+    if (int rc = check_gemv(what, L.words, L.scales, L.x, L.y, M, L.N, L.K)) return rc;
+  }
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return fail(Q4_ERR_DEVICE, "q4_decode_step: no HIP device");
+  std::vector<q4::GemvPlan> plans((size_t)n_layers);
+  size_t need = 0;
+  for (int64_t i = 0; i < n_layers; ++i) {
+    plans[(size_t)i] = q4::plan_auto(*d, M, layers[i].N, layers[i].K);
+    if (plans[(size_t)i].ws_bytes > need) need = plans[(size_t)i].ws_bytes;
+  }
+  if (int rc = check_ws("q4_decode_step", ws, ws_bytes, need)) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t i = 0; i < n_layers; ++i) {
+    const q4_layer& L = layers[i];
+    q4::GemvArgs a{L.words, L.scales, L.x, L.y, M, L.N, L.K};
+    hipError_t e = q4::launch_gemv(*d, a, plans[(size_t)i], ws, s);
+    if (e != hipSuccess) {
+      snprintf(what, sizeof what, "q4_decode_step: layers[%lld]", (long long)i);
+      return device_error(e, what);
+    }
+  }
+  return ok();
+}
+
+int q4_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t blocks,
+                  q4_stream_t stream) {
+  if (!buf || !sink) return fail(Q4_ERR_NULL, "q4_probe_read: NULL pointer");
+  if (bytes == 0 || bytes % 16) return fail(Q4_ERR_SHAPE, "q4_probe_read: bytes %% 16 != 0");
+  if (!aligned(buf, 16)) return fail(Q4_ERR_ALIGN, "q4_probe_read: buf not 16-byte aligned");
+  if (blocks < 0 || blocks > INT32_MAX) return fail(Q4_ERR_SHAPE, "q4_probe_read: bad blocks");
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return fail(Q4_ERR_DEVICE, "q4_probe_read: no HIP device");
+  hipError_t e = q4::launch_probe_read(*d, buf, bytes, sink, blocks,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_probe_read");
+}
+
+int q4_probe_copy(const void* src, void* dst, size_t bytes, q4_stream_t stream) {
+  if (!src || !dst) return fail(Q4_ERR_NULL, "q4_probe_copy: NULL pointer");
+  if (bytes == 0 || bytes % 16) return fail(Q4_ERR_SHAPE, "q4_probe_copy: bytes %% 16 != 0");
+  if (!aligned(src, 16) || !aligned(dst, 16))
+    return fail(Q4_ERR_ALIGN, "q4_probe_copy: pointers not 16-byte aligned");
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(src), b0 = reinterpret_cast<uintptr_t>(dst);
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(Q4_ERR_SHAPE, "q4_probe_copy: overlap");
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return fail(Q4_ERR_DEVICE, "q4_probe_copy: no HIP device");
+  hipError_t e = q4::launch_probe_copy(*d, src, dst, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_probe_copy");
+}
+
+}  // extern "C"

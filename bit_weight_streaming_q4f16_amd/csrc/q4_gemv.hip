@@ -1,0 +1,393 @@
+// q4f16_1 GEMV kernels for gfx950 (CDNA4, wave64).
+//
+// y[n] = sum_k (q[n][k] - 7) * s[n][k/32] * x[k]   (Zero TVM documentation,
+// "Q4F16 quantization format"; fp32 accumulation as its correctness fixes ask).
+//
+// Decode is bandwidth-bound (everything-webgpu AI.md: time per token scales with
+// weight bytes; the generated GEMV lost most of its speed to a barrier-heavy
+// reduction over too little work per thread).  The design here follows that:
+//  * weights stream with 128-bit non-temporal loads; one dwordx4 is four words,
+//    i.e. exactly one 32-weight group, and its scale is one fp16;
+//  * x is staged once per workgroup in LDS, already permuted to the order in
+//    which the dequantised nibble pairs come out, in four planes so that lanes
+//    reading consecutive groups hit consecutive LDS banks;
+//  * dequantisation is exact and cheap: OR-ing a nibble pair into the mantissa
+//    of two fp16 values with exponent 2^10 (nibbles at bits 0-3 and 16-19) or
+//    2^6 (bits 4-7 and 20-23, whose place value 16 matches that exponent's ulp
+//    of 1/16) gives 1024 + q or 64 + q exactly; one packed fp16 subtraction
+//    gives q - 7 exactly; v_dot2_f32_f16 multiplies a pair by the matching x
+//    pair and accumulates in fp32; the scale is applied once per group;
+//  * each row's lanes reduce with DPP and lane-swap instructions, no LDS and no
+//    barrier (the page's fix: reduce across lanes without workgroup barriers);
+//  * a split-K variant writes fp32 partials per K slice; a second pass adds
+//    them in ascending slice order, so results are deterministic;
+//  * small M (2..8) uses MFMA: v_mfma_f32_16x16x32_f16 covers 16 rows by one
+//    32-weight group, so the per-group scale is applied exactly to its result.
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+template <typename T, typename F>
+__device__ __forceinline__ T bits(F v) {
+  return __builtin_bit_cast(T, v);
+}
+
+__device__ __forceinline__ float half_to_float(uint16_t h) {
+  return (float)bits<_Float16>(h);
+}
+
+__device__ __forceinline__ uint16_t float_to_half_rne(float v) {
+  return bits<uint16_t>((_Float16)v);
+}
+
+// A block of 8 consecutive x values (one word's worth) reordered into the pairs
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7) that dequant_word produces.
+__device__ __forceinline__ uint4 pair_order(uint4 v) {
+  uint4 o;
+  o.x = (v.x & 0xFFFFu) | (v.z << 16);
+  o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+  o.z = (v.y & 0xFFFFu) | (v.w << 16);
+  o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+  return o;
+}
+
+// One word -> four fp16 pairs (q0-7, q4-7) (q1-7, q5-7) (q2-7, q6-7) (q3-7, q7-7),
+// all exact.
+__device__ __forceinline__ void dequant_word(uint32_t w, h2_t (&q)[4]) {
+  const uint32_t w8 = w >> 8;
+  const h2_t c1031 = {(_Float16)-1031.0f, (_Float16)-1031.0f};
+  const h2_t c71 = {(_Float16)-71.0f, (_Float16)-71.0f};
+  q[0] = bits<h2_t>((w & 0x000F000Fu) | 0x64006400u) + c1031;
+  q[1] = bits<h2_t>((w & 0x00F000F0u) | 0x54005400u) + c71;
+  q[2] = bits<h2_t>((w8 & 0x000F000Fu) | 0x64006400u) + c1031;
+  q[3] = bits<h2_t>((w8 & 0x00F000F0u) | 0x54005400u) + c71;
+}
+
+// sum over one 32-weight group of (q - 7) * x, fp32.  xs holds four planes of
+// gc pair-ordered blocks: plane j, entry g = x of word j of group g.
+__device__ __forceinline__ float group_dot(uint4 w, const uint4* xs, int gc, int g) {
+  const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 xv = xs[j * gc + g];
+    h2_t q[4];
+    dequant_word(wj[j], q);
+    a = __builtin_amdgcn_fdot2(q[0], bits<h2_t>(xv.x), a, false);
+    b = __builtin_amdgcn_fdot2(q[1], bits<h2_t>(xv.y), b, false);
+    a = __builtin_amdgcn_fdot2(q[2], bits<h2_t>(xv.z), a, false);
+    b = __builtin_amdgcn_fdot2(q[3], bits<h2_t>(xv.w), b, false);
+  }
+  return a + b;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return bits<float>(__builtin_amdgcn_update_dpp(0, bits<int>(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned teams of LPR lanes; every lane of a team gets the total.
+template <int LPR>
+__device__ __forceinline__ float team_sum(float v) {
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "team size");
+  v += dpp<0xB1>(v);                         // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp<0x4E>(v);                         // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (LPR >= 8) v += dpp<0x141>(v);  // row_half_mirror: the other quad
+  if constexpr (LPR >= 16) v += dpp<0x140>(v); // row_mirror: the other half-row
+  if constexpr (LPR >= 32) {                   // rows 0<->1 and 2<->3
+    const auto r = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(v), bits<uint32_t>(v),
+                                                    false, false);
+    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
+  }
+  if constexpr (LPR >= 64) {                   // lanes 0-31 <-> 32-63
+    const auto r = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(v), bits<uint32_t>(v),
+                                                    false, false);
+    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
+  }
+  return v;
+}
+
+// K slice s of G groups split `splits` ways: [G*s/splits, G*(s+1)/splits).
+__device__ __forceinline__ int slice_begin(int G, int splits, int s) {
+  return (int)((int64_t)G * s / splits);
+}
+
+// ---------------------------------------------------------------- M == 1 ---
+// Grid: x = workgroups striding over rows, y = K slice.  A team of LPR lanes owns
+// a row at a time; lane i of the team takes groups i, i + LPR, ... of the slice,
+// UNR of them per trip (loads first, then arithmetic).  Out-of-range groups load
+// the slice's last group again and are discarded by a select.
+template <int LPR, int UNR>
+__global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
+                                                    const uint16_t* __restrict__ S,
+                                                    const uint4* __restrict__ X,
+                                                    uint16_t* __restrict__ Y,
+                                                    float* __restrict__ P, int N, int G,
+                                                    int splits) {
+  extern __shared__ uint4 xs[];
+  const int split = blockIdx.y;
+  const int g0 = slice_begin(G, splits, split);
+  const int gc = slice_begin(G, splits, split + 1) - g0;
+  for (int i = threadIdx.x; i < 4 * gc; i += kBlock) {
+    const int g = i >> 2, j = i & 3;
+    xs[j * gc + g] = pair_order(X[(int64_t)(g0 + g) * 4 + j]);
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & (LPR - 1);
+  const int team = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) / LPR);
+  const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
+  for (int n = team; n < N; n += nteams) {
+    const uint4* wr = W + (int64_t)n * G + g0;
+    const uint16_t* sr = S + (int64_t)n * G + g0;
+    float acc = 0.f;
+    for (int t0 = 0; t0 < gc; t0 += LPR * UNR) {
+      uint4 wv[UNR];
+      uint16_t sv[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        int g = t0 + u * LPR + lane;
+        g = g < gc ? g : gc - 1;
+        wv[u] = load_nt(wr + g);
+        sv[u] = sr[g];
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int graw = t0 + u * LPR + lane;
+        const int g = graw < gc ? graw : gc - 1;
+        const float p = group_dot(wv[u], xs, gc, g);
+        const float t = __builtin_fmaf(p, half_to_float(sv[u]), acc);
+        acc = graw < gc ? t : acc;
+      }
+    }
+    acc = team_sum<LPR>(acc);
+    if (lane == 0) {
+      if (splits == 1)
+        Y[n] = float_to_half_rne(acc);
+      else
+        P[(int64_t)split * N + n] = acc;
+    }
+  }
+}
+
+// ------------------------------------------------------------- M in 2..8 ---
+// One workgroup = 16 rows x one K slice; its four waves take interleaved chunks
+// of four groups.  In a chunk, lane (c = lane/16, r = lane%16) loads group c of
+// row r with one dwordx4; a 4x4 exchange among lanes r, r+16, r+32, r+48
+// (permlane32/permlane16 swaps) leaves word c of every group of the chunk in lane
+// (c, r), which is the B-operand layout of v_mfma_f32_16x16x32_f16 (column = row
+// n, k block = c).  A = X rows (row m = r < M, zero above M), from LDS in the same
+// pair order.  One MFMA per group into a fresh accumulator, then acc += s * D.
+__device__ __forceinline__ void transpose4(uint32_t (&v)[4]) {
+  // rows {0,1} <-> {2,3} for registers (0,2) and (1,3); then rows 0<->1, 2<->3
+  // for (0,1) and (2,3): afterwards row R register t = original row t register R.
+  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  v[0] = a[0]; v[2] = a[1]; v[1] = b[0]; v[3] = b[1];
+  auto c = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
+  v[0] = c[0]; v[1] = c[1]; v[2] = d[0]; v[3] = d[1];
+}
+
+__global__ __launch_bounds__(kBlock) void k_gemv_mfma(const uint4* __restrict__ W,
+                                                      const uint16_t* __restrict__ S,
+                                                      const uint4* __restrict__ X,
+                                                      uint16_t* __restrict__ Y,
+                                                      float* __restrict__ P, int M, int N,
+                                                      int G, int splits) {
+  extern __shared__ uint4 xs[];   // [M][4*gc + 1]: row m, group g, word j at m*(4gc+1) + 4g + j
+  __shared__ f4_t red[3][64];
+  const int split = blockIdx.y;
+  const int g0 = slice_begin(G, splits, split);
+  const int gc = slice_begin(G, splits, split + 1) - g0;
+  const int pitch = 4 * gc + 1;
+  for (int i = threadIdx.x; i < M * 4 * gc; i += kBlock) {
+    const int m = i / (4 * gc), r = i - m * 4 * gc;
+    xs[m * pitch + r] = pair_order(X[(int64_t)m * G * 4 + (int64_t)g0 * 4 + r]);
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, c = l >> 4, r = l & 15;
+  const int n0 = blockIdx.x * 16;
+  const int n = n0 + r < N ? n0 + r : N - 1;
+  const uint4* wr = W + (int64_t)n * G + g0;
+  const uint16_t* sr = S + (int64_t)n * G + g0;
+  const bool has_x = r < M;
+  f4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+  for (int gb = 4 * wave; gb < gc; gb += 16) {
+    const int gl = gb + c < gc ? gb + c : gc - 1;
+    const uint4 wv = load_nt(wr + gl);
+    float s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s[t] = half_to_float(sr[gb + t < gc ? gb + t : gc - 1]);
+    uint32_t v[4] = {wv.x, wv.y, wv.z, wv.w};
+    transpose4(v);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int gt = gb + t < gc ? gb + t : gc - 1;
+      h2_t q[4];
+      dequant_word(v[t], q);
+      const h8_t B = {q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+      h8_t A = {};
+      if (has_x) A = bits<h8_t>(xs[r * pitch + 4 * gt + c]);
+      const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, zero, 0, 0, 0);
+      if (gb + t < gc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(s[t], d[e], acc[e]);
+      }
+    }
+  }
+  // add the four waves' partials in a fixed order
+  if (wave > 0) red[wave - 1][l] = acc;
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) acc += red[w][l];
+    if (n0 + r < N) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * c + e;
+        if (m < M) {
+          if (splits == 1)
+            Y[(int64_t)m * N + n0 + r] = float_to_half_rne(acc[e]);
+          else
+            P[((int64_t)split * M + m) * N + n0 + r] = acc[e];
+        }
+      }
+    }
+  }
+}
+
+// Second pass of split-K: out[i] = fp16(sum over s ascending of P[s*count + i]).
+__global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ P,
+                                                    uint16_t* __restrict__ Y, int64_t count,
+                                                    int splits) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < count; i += stride) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) acc += P[(int64_t)s * count + i];
+    Y[i] = float_to_half_rne(acc);
+  }
+}
+
+// Dynamic LDS above 64 KB must be allowed per kernel (gfx950 has 160 KB per CU).
+template <typename F>
+hipError_t allow_lds(F* kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+int pow2_floor(int64_t v) {
+  int p = 1;
+  while ((int64_t)p * 2 <= v) p *= 2;
+  return p;
+}
+
+int choose_lpr(int64_t G) {
+  int l = pow2_floor(G / 3 > 0 ? G / 3 : 1);
+  return l < 4 ? 4 : (l > 64 ? 64 : l);
+}
+
+template <int LPR>
+hipError_t launch_m1(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
+                     hipStream_t s) {
+  const int64_t G = a.K / 32;
+  const int64_t teams_per_block = kBlock / LPR;
+  int64_t blocks = (a.N + teams_per_block - 1) / teams_per_block;
+  const int64_t cap = (int64_t)d.cus * 64;
+  if (blocks > cap) blocks = cap;
+  const int64_t gmax = (G + p.splits - 1) / p.splits;
+  const size_t lds = (size_t)gmax * 64;
+  const dim3 grid((unsigned)blocks, (unsigned)p.splits);
+  if (hipError_t e = allow_lds(k_gemv_m1<LPR, 2>, lds)) return e;
+  hipLaunchKernelGGL((k_gemv_m1<LPR, 2>), grid, dim3(kBlock), lds, s,
+                     reinterpret_cast<const uint4*>(a.words), a.scales,
+                     reinterpret_cast<const uint4*>(a.x), a.y, part, (int)a.N, (int)G, p.splits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t max_groups_per_slice(const DeviceInfo& d, int64_t M) {
+  // M == 1: 64 bytes of LDS per group.  M > 1: M rows of (4 g + 1) uint4 plus 3 KB
+  // of cross-wave partials.
+  const int64_t lds = (int64_t)d.lds_per_block;
+  if (M <= 1) return lds / 64;
+  return ((lds - 3 * 64 * 16) / (16 * M) - 1) / 4;
+}
+
+GemvPlan plan_splits(const DeviceInfo& d, int64_t M, int64_t N, int64_t K, int splits) {
+  GemvPlan p;
+  p.splits = splits;
+  p.lanes_per_row = M == 1 ? choose_lpr(K / 32) : 64;
+  p.ws_bytes = splits > 1 ? (size_t)4 * splits * M * N : 0;
+  (void)d;
+  return p;
+}
+
+GemvPlan plan_auto(const DeviceInfo& d, int64_t M, int64_t N, int64_t K) {
+  const int64_t G = K / 32;
+  const int64_t gmax = max_groups_per_slice(d, M);
+  int64_t splits = (G + gmax - 1) / gmax;       // fit the slice of x in LDS
+  int64_t blocks;
+  if (M == 1) {
+    const int lpr = choose_lpr(G);
+    blocks = (N + kBlock / lpr - 1) / (kBlock / lpr);
+  } else {
+    blocks = (N + 15) / 16;
+  }
+  // too few workgroups to cover every compute unit twice: split K as well
+  const int64_t want = 2 * (int64_t)d.cus;
+  if (blocks * splits < want) {
+    int64_t s2 = (want + blocks - 1) / blocks;
+    const int64_t smax = M == 1 ? G / 8 : G / 16;
+    if (s2 > smax) s2 = smax;
+    if (s2 > splits) splits = s2;
+  }
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits < 1) splits = 1;
+  return plan_splits(d, M, N, K, (int)splits);
+}
+
+hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p, void* ws,
+                       hipStream_t s) {
+  float* part = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
+  uint16_t* out = a.y;
+  hipError_t e;
+  if (a.M == 1) {
+    switch (p.lanes_per_row) {
+      case 4: e = launch_m1<4>(a, p, part, d, s); break;
+      case 8: e = launch_m1<8>(a, p, part, d, s); break;
+      case 16: e = launch_m1<16>(a, p, part, d, s); break;
+      case 32: e = launch_m1<32>(a, p, part, d, s); break;
+      default: e = launch_m1<64>(a, p, part, d, s); break;
+    }
+  } else {
+    const int64_t G = a.K / 32;
+    const int64_t gmax = (G + p.splits - 1) / p.splits;
+    const size_t lds = (size_t)a.M * (4 * gmax + 1) * 16;
+    const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)p.splits);
+    if (hipError_t e2 = allow_lds(k_gemv_mfma, lds)) return e2;
+    hipLaunchKernelGGL(k_gemv_mfma, grid, dim3(kBlock), lds, s,
+                       reinterpret_cast<const uint4*>(a.words), a.scales,
+                       reinterpret_cast<const uint4*>(a.x), out, part, (int)a.M, (int)a.N,
+                       (int)G, p.splits);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int64_t count = a.M * a.N;
+  int64_t blocks = (count + kBlock - 1) / kBlock;
+  if (blocks > (int64_t)d.cus * 8) blocks = (int64_t)d.cus * 8;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)blocks), dim3(kBlock), 0, s, part, out, count,
+                     p.splits);
+  return hipGetLastError();
+}
+
+}  // namespace q4

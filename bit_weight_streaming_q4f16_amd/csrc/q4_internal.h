@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI layer (q4_api.cpp) and the HIP kernels.
+// Not installed; the public interface is include/q4f16.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 128-bit load with the non-temporal hint (streamed data that is read once).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+constexpr int kBlock = 256;          // threads per workgroup (four wave64s)
+constexpr int kMaxSplits = 64;       // split-K slices accepted by q4_gemv_splitk
+constexpr int kMaxM = 8;             // rows of the batched (small-M) GEMV
+
+struct DeviceInfo {
+  int id = -1;
+  int cus = 0;                       // compute units
+  size_t lds_per_block = 0;          // bytes of LDS one workgroup may allocate
+};
+
+// Properties of the current device (cached per device); nullptr if no device.
+const DeviceInfo* device_info();
+
+// One GEMV as the kernels see it.
+struct GemvArgs {
+  const uint32_t* words;             // [N][K/8]
+  const uint16_t* scales;            // [N][K/32]
+  const uint16_t* x;                 // [M][K]
+  uint16_t* y;                       // [M][N]
+  int64_t M, N, K;
+};
+
+// Launch plan of one GEMV: how many K slices and which kernel shape.
+struct GemvPlan {
+  int splits = 1;                    // K slices (1 = single pass, no workspace)
+  int lanes_per_row = 32;            // M == 1 kernel: lanes cooperating on a row
+  size_t ws_bytes = 0;               // fp32 partials when splits > 1
+};
+
+// Largest number of groups one workgroup stages in LDS for M input rows.
+int64_t max_groups_per_slice(const DeviceInfo& d, int64_t M);
+
+// Automatic plan for a shape (used by q4_gemv, q4_gemv_batched, q4_decode_step).
+GemvPlan plan_auto(const DeviceInfo& d, int64_t M, int64_t N, int64_t K);
+// Plan with an explicit number of slices (q4_gemv_splitk).
+GemvPlan plan_splits(const DeviceInfo& d, int64_t M, int64_t N, int64_t K, int splits);
+
+// Enqueue one GEMV with a plan.  ws must hold plan.ws_bytes.  Returns a hipError_t.
+hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p, void* ws,
+                       hipStream_t s);
+
+hipError_t launch_pack(const uint8_t* codes, uint32_t* words, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_unpack(const uint32_t* words, uint8_t* codes, int64_t N, int64_t K,
+                         hipStream_t s);
+
+hipError_t launch_probe_read(const DeviceInfo& d, const void* buf, size_t bytes, uint32_t* sink,
+                             int64_t blocks, hipStream_t s);
+hipError_t launch_probe_copy(const DeviceInfo& d, const void* src, void* dst, size_t bytes,
+                             hipStream_t s);
+
+}  // namespace q4

@@ -1,0 +1,168 @@
+/*
+ * q4f16.h -- C ABI of the q4f16_1 weight-streaming decode library (MI355X, gfx950).
+ *
+ * The q4f16_1 format (Zero TVM documentation, section "Q4F16 quantization
+ * format"): a weight matrix of logical shape [N][K] (N outputs, K inputs) is
+ * stored as
+ *   words  : uint32 [N][K/8]  -- eight 4-bit codes per word; element k of row n
+ *                                is nibble (k % 8) of words[n][k/8], i.e.
+ *                                (words[n][k/8] >> 4*(k%8)) & 0xF;
+ *   scales : fp16   [N][K/32] -- one scale per group of 32 consecutive weights;
+ * and W[n][k] = (code - 7) * scales[n][k/32].  K must be a multiple of 32, so a
+ * group is exactly four consecutive words (16 bytes).  The everything-webgpu
+ * AI.md format table gives the cost: 16 + 2 = 18 bytes per 32 weights.
+ *
+ * Conventions for every entry point:
+ *  - fp16 values are passed as uint16_t bit patterns (IEEE binary16).
+ *  - Every data pointer is DEVICE memory owned by the caller; the library never
+ *    frees it and keeps no pointer after the call returns, except where a
+ *    function says otherwise.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *    enqueued on it; results are valid once the caller synchronises that stream.
+ *    No entry point synchronises the host with the device.
+ *  - Return value: a q4_status.  Argument errors are detected on the host before
+ *    anything is enqueued (no partial execution).  Q4_ERR_DEVICE reports a HIP
+ *    error at launch time; faults during execution surface at the caller's
+ *    synchronisation.  q4_last_error() gives a text naming the argument and value
+ *    (thread-local, valid until the next call on the same thread).
+ *  - Outputs are fp16, rounded to nearest even from an fp32 accumulation.  Any
+ *    fp32 summation order is a correct result; every variant is deterministic
+ *    (the same inputs give bitwise the same outputs, run to run).
+ */
+#ifndef Q4F16_H
+#define Q4F16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef Q4_API
+#define Q4_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* q4_stream_t;
+
+typedef enum q4_status {
+  Q4_OK = 0,
+  Q4_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  Q4_ERR_SHAPE = 2,       /* N < 1, K < 32, K % 32 != 0, M outside [1, 8], ...  */
+  Q4_ERR_ALIGN = 3,       /* a pointer is not aligned as documented             */
+  Q4_ERR_WORKSPACE = 4,   /* ws NULL or smaller than the size the call needs    */
+  Q4_ERR_DEVICE = 5,      /* a HIP call failed (no device, launch failure, ...) */
+  Q4_ERR_UNSUPPORTED = 6  /* a size beyond what the kernels handle              */
+} q4_status;
+
+/* Name of a status code ("Q4_OK", ...).  Never NULL. */
+Q4_API const char* q4_status_str(int status);
+
+/* Detail of the last error on this thread ("" after a successful call). */
+Q4_API const char* q4_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+Q4_API int q4_version(void);
+
+/* ------------------------------------------------------------------ codec -- */
+
+/* q4_pack: codes uint8 [N][K] (device) -> words uint32 [N][K/8] (device).
+ * Word j of row n = OR over i < 8 of (codes[n][8j+i] & 0xF) << 4i (Zero TVM
+ * documentation, "Q4F16 quantization format": nibble i is (w >> 4i) & 0xF).
+ * Codes above 15 are reduced to their low nibble.  Requires N >= 1, K >= 32,
+ * K % 32 == 0; words 16-byte aligned; codes any alignment.  Bit-exact. */
+Q4_API int q4_pack(const uint8_t* codes, uint32_t* words, int64_t N, int64_t K, q4_stream_t stream);
+
+/* q4_unpack: the inverse of q4_pack, words [N][K/8] -> codes [N][K] (each 0..15).
+ * Same shape and alignment rules. */
+Q4_API int q4_unpack(const uint32_t* words, uint8_t* codes, int64_t N, int64_t K, q4_stream_t stream);
+
+/* ------------------------------------------------------------------- GEMV -- */
+
+/* q4_gemv: y[n] = fp16( sum_k (q[n][k] - 7) * scales[n][k/32] * x[k] ), n < N,
+ * with fp32 accumulation (Zero TVM documentation, "Decode loop": the int4 matmul
+ * of every projection and the LM head; "Q4F16 quantization format" for the
+ * weights).  x: fp16 [K]; y: fp16 [N].  Chooses single-pass or split-K from the
+ * shape and the device; the split-K variant needs a workspace of
+ * q4_workspace_bytes(1, N, K) bytes (0 means none: ws may be NULL).
+ * Alignment: words, x and ws 16 bytes; scales and y 2 bytes.  y must not
+ * overlap any input. */
+Q4_API int q4_gemv(const uint32_t* words, const uint16_t* scales, const uint16_t* x, uint16_t* y,
+            int64_t N, int64_t K, void* ws, size_t ws_bytes, q4_stream_t stream);
+
+/* q4_gemv_splitk: the same product with an explicit number of K slices.
+ * splits == 1 is the single-pass kernel (ws unused).  splits > 1 runs a first
+ * pass writing fp32 partials part[s][n] over slice s of the K groups (groups are
+ * divided as evenly as possible, each slice non-empty) into ws, then a second
+ * pass y[n] = fp16(sum over s ascending of part[s][n]).  1 <= splits <= K/32
+ * and splits <= 64; ws needs q4_splitk_workspace_bytes(1, N, splits) bytes. */
+Q4_API int q4_gemv_splitk(const uint32_t* words, const uint16_t* scales, const uint16_t* x,
+                   uint16_t* y, int64_t N, int64_t K, int64_t splits, void* ws,
+                   size_t ws_bytes, q4_stream_t stream);
+
+/* q4_gemv_batched: Y[m][n] = fp16( sum_k W[n][k] * X[m][k] ) for m < M <= 8,
+ * the weights read once for all M rows (small-M decode: several tokens or
+ * sequences share one pass over the weights, as the Splash page's draft cycles
+ * of eight rows do).  X: fp16 [M][K] row-major; Y: fp16 [M][N] row-major.
+ * Workspace: q4_workspace_bytes(M, N, K).  M == 1 is q4_gemv. */
+Q4_API int q4_gemv_batched(const uint32_t* words, const uint16_t* scales, const uint16_t* X,
+                    uint16_t* Y, int64_t M, int64_t N, int64_t K, void* ws,
+                    size_t ws_bytes, q4_stream_t stream);
+
+/* Workspace bytes q4_gemv (M == 1) or q4_gemv_batched (M > 1) needs for this
+ * shape on the current device (0 = none).  Returns 0 for an invalid shape. */
+Q4_API size_t q4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Workspace bytes of q4_gemv_splitk (M == 1) with `splits` slices. */
+Q4_API size_t q4_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
+
+/* ------------------------------------------------------------ decode step -- */
+
+/* One GEMV of a decode step: y = W x (or Y = W X for M rows).  x/X: fp16 [M][K];
+ * y/Y: fp16 [M][N]. */
+typedef struct q4_layer {
+  const uint32_t* words;   /* [N][K/8]  */
+  const uint16_t* scales;  /* [N][K/32] */
+  const uint16_t* x;       /* [M][K]    */
+  uint16_t* y;             /* [M][N]    */
+  int64_t N;
+  int64_t K;
+} q4_layer;
+
+/* Launch one kernel per descriptor on the stream (stream-ordered). */
+#define Q4_STEP_LAUNCH_EACH 0x1u
+
+/* q4_decode_step: run the GEMVs of layers[0 .. n_layers) in list order, as the
+ * Zero TVM decode loop walks the projections of every layer and then the LM
+ * head ("Decode loop").  The results are those of calling q4_gemv (M == 1) or
+ * q4_gemv_batched (M > 1) on each descriptor in turn; a descriptor's x may be an
+ * earlier descriptor's y.  Every descriptor is validated before anything is
+ * enqueued.  `layers` is host memory, read during the call only.
+ * ws: q4_decode_step_workspace_bytes(...) bytes. */
+Q4_API int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t flags,
+                   void* ws, size_t ws_bytes, q4_stream_t stream);
+
+Q4_API size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, int64_t M,
+                                      uint32_t flags);
+
+/* ------------------------------------------------------ measurement aids -- */
+
+/* Streaming-read ceiling probe (the everything-webgpu page measures the same
+ * ceiling with a kernel that only streams a large buffer, swept over workgroup
+ * counts): every byte of buf[0 .. bytes) is read once with 128-bit loads by
+ * `blocks` workgroups of 256 threads (0 = one per compute unit times 8); a
+ * value depending on all of them is written to sink[0].  bytes % 16 == 0,
+ * buf 16-byte aligned. */
+Q4_API int q4_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t blocks,
+                  q4_stream_t stream);
+
+/* Plain device copy dst[0 .. bytes) = src[0 .. bytes) with 128-bit loads and
+ * stores (the reference kernel for counter calibration).  bytes % 16 == 0,
+ * both 16-byte aligned, no overlap. */
+Q4_API int q4_probe_copy(const void* src, void* dst, size_t bytes, q4_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4F16_H */

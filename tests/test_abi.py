@@ -1,0 +1,142 @@
+"""The C-ABI library: it loads, exports every symbol include/q4f16.h declares,
+and rejects bad arguments on the host before touching a device (no GPU needed,
+no compute call)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+import bit_weight_streaming_q4f16_amd as q4
+
+HEADER = os.path.join(ROOT, "include", "q4f16.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"Q4_API\s+[\w\s\*]*?\b(q4_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q4.lib_path()):
+        from bit_weight_streaming_q4f16_amd import build
+        build.build()
+    return q4.load()
+
+
+def test_header_declares_the_path():
+    syms = declared_symbols()
+    for name in ["q4_pack", "q4_unpack", "q4_gemv", "q4_gemv_splitk", "q4_gemv_batched",
+                 "q4_decode_step", "q4_workspace_bytes", "q4_status_str", "q4_last_error"]:
+        assert name in syms
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", q4.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = [s for s in declared_symbols() if s not in exported]
+    assert not missing, missing
+    for s in declared_symbols():
+        assert hasattr(lib, s)
+    # nothing but the C ABI leaks out under a q4_ prefix
+    extra = [s for s in exported if s.startswith("q4_") and s not in declared_symbols()]
+    assert not extra, extra
+
+
+def test_layer_struct_matches_header():
+    # six 8-byte fields: four pointers and two int64
+    assert C.sizeof(q4.Layer) == 48
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct q4_layer \{(.*?)\} q4_layer;", text, re.S).group(1)
+    fields = re.findall(r"\b(words|scales|x|y|N|K)\s*;", body)
+    assert fields == [f[0] for f in q4.Layer._fields_]
+
+
+def test_status_strings(lib):
+    for code, name in q4.STATUS.items():
+        assert lib.q4_status_str(code).decode() == name
+    assert lib.q4_status_str(99).decode() == "Q4_ERR_UNKNOWN"
+    assert lib.q4_version() >= 100
+
+
+P = C.c_void_p
+A = P(0x10000)      # aligned fake device addresses: never dereferenced by these calls
+B = P(0x20000)
+X = P(0x30000)
+Y = P(0x40000)
+
+
+def _err(lib):
+    return lib.q4_last_error().decode()
+
+
+def test_gemv_argument_errors(lib):
+    f = lib.q4_gemv
+    assert f(None, B, X, Y, 16, 64, None, 0, None) == 1 and "words" in _err(lib)
+    assert f(A, None, X, Y, 16, 64, None, 0, None) == 1 and "scales" in _err(lib)
+    assert f(A, B, None, Y, 16, 64, None, 0, None) == 1 and "x" in _err(lib)
+    assert f(A, B, X, None, 16, 64, None, 0, None) == 1 and "y" in _err(lib)
+    assert f(A, B, X, Y, 0, 64, None, 0, None) == 2 and "N = 0" in _err(lib)
+    assert f(A, B, X, Y, 16, 48, None, 0, None) == 2 and "K = 48" in _err(lib)
+    assert f(A, B, X, Y, 16, 0, None, 0, None) == 2
+    assert f(A, B, X, Y, 16, -32, None, 0, None) == 2
+    assert f(P(0x10004), B, X, Y, 16, 64, None, 0, None) == 3 and "words" in _err(lib)
+    assert f(A, B, P(0x30008), Y, 16, 64, None, 0, None) == 3 and "x" in _err(lib)
+    assert f(A, P(0x20001), X, Y, 16, 64, None, 0, None) == 3 and "scales" in _err(lib)
+    assert f(A, B, X, P(0x40001), 16, 64, None, 0, None) == 3 and "y" in _err(lib)
+    # output overlapping an input
+    assert f(A, B, X, P(0x10000 + 64), 16, 64, None, 0, None) == 2 and "overlap" in _err(lib)
+    assert f(A, B, X, Y, 1 << 40, 64, None, 0, None) == 6
+
+
+def test_batched_and_splitk_argument_errors(lib):
+    assert lib.q4_gemv_batched(A, B, X, Y, 0, 16, 64, None, 0, None) == 2 and "M = 0" in _err(lib)
+    assert lib.q4_gemv_batched(A, B, X, Y, 9, 16, 64, None, 0, None) == 2
+    assert lib.q4_gemv_splitk(A, B, X, Y, 16, 64, 0, None, 0, None) == 2
+    assert lib.q4_gemv_splitk(A, B, X, Y, 16, 64, 3, None, 0, None) == 2   # 3 > K/32
+    assert lib.q4_gemv_splitk(A, B, X, Y, 16, 8192, 65, None, 0, None) == 2
+    assert lib.q4_splitk_workspace_bytes(1, 100, 4) == 1600
+    assert lib.q4_splitk_workspace_bytes(8, 100, 4) == 12800
+    assert lib.q4_splitk_workspace_bytes(1, 100, 1) == 0
+    assert lib.q4_workspace_bytes(1, 16, 48) == 0
+
+
+def test_codec_argument_errors(lib):
+    assert lib.q4_pack(None, A, 4, 64, None) == 1
+    assert lib.q4_pack(X, None, 4, 64, None) == 1
+    assert lib.q4_pack(X, A, 4, 40, None) == 2
+    assert lib.q4_pack(X, P(0x10004), 4, 64, None) == 3
+    assert lib.q4_unpack(A, None, 4, 64, None) == 1
+    assert lib.q4_unpack(P(0x10008), X, 4, 64, None) == 3
+
+
+def test_decode_step_validates_every_descriptor_first(lib):
+    layers = (q4.Layer * 3)()
+    layers[0] = q4.Layer(0x10000, 0x20000, 0x30000, 0x40000, 16, 64)
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x40000, 0x70000, 16, 64)
+    layers[2] = q4.Layer(0x80000, 0x90000, 0x70000, 0xA0000, 16, 40)   # bad K
+    assert lib.q4_decode_step(layers, 3, 1, 0, None, 0, None) == 2
+    assert "layers[2]" in _err(lib)
+    assert lib.q4_decode_step(None, 3, 1, 0, None, 0, None) == 1
+    assert lib.q4_decode_step(layers, 0, 1, 0, None, 0, None) == 2
+    assert lib.q4_decode_step(layers, 2, 9, 0, None, 0, None) == 2
+    assert lib.q4_decode_step(layers, 2, 1, 0x80, None, 0, None) == 2 and "flags" in _err(lib)
+
+
+def test_probe_argument_errors(lib):
+    assert lib.q4_probe_read(None, 16, A, 0, None) == 1
+    assert lib.q4_probe_read(A, 20, X, 0, None) == 2
+    assert lib.q4_probe_copy(A, P(0x10010), 64, None) == 2       # overlap
+    assert lib.q4_probe_copy(A, P(0x20008), 64, None) == 3
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(q4, "_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(q4, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        q4.load()

@@ -41,3 +41,13 @@ def test_distributions():
     sv = synth.half_bits_to_f64(sc)
     assert sc.shape == (256, 16) and x.shape == (512,)
     assert sv.min() >= 0.005 * (1 - 2 ** -11) and sv.max() <= 0.02 * (1 + 2 ** -11)
+
+
+def test_torch_words_match_numpy():
+    import torch
+    for count in (1, 2, 7, 1000, 33_333):
+        a = synth.words("tw", 5, count)
+        b = synth.words_torch("tw", 5, count, device="cpu").numpy().view(np.uint32)
+        assert np.array_equal(a, b), count
+    m = synth.Matrix("tw/m", 9, 96, seed=2)
+    assert np.array_equal(m.words(), m.words_torch("cpu").numpy().view(np.uint32))
