@@ -27,12 +27,18 @@ PEAK_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "achieved HBM GB/s (% of peak) and projected decode tok/s, q4 GEMV sweep"
 
 
+MODES = {"ordered": 0x2, "hazards": 0x0, "launch_each": 0x1}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--mode", choices=["auto", "launch_each"], default="auto")
+    ap.add_argument("--mode", choices=["ordered", "hazards", "launch_each"], default="hazards",
+                    help="ordered: every GEMV waits for its predecessor (a decode step's "
+                         "dependency chain); hazards: waits only on shared memory; "
+                         "launch_each: one kernel per GEMV")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--only-step", action="store_true",
@@ -77,30 +83,33 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     layers = q4.make_layers(descs)
-    flags = q4.STEP_LAUNCH_EACH if args.mode == "launch_each" else 0
-    ws_bytes = q4.q4_decode_step_workspace_bytes(layers, 1, flags)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     step_bytes = sum(synth.algorithmic_bytes(1, N, K) for _, N, K in meta)
     weight_bytes = sum(synth.Matrix(l, N, K).weight_bytes for l, N, K in meta)
 
-    def step():
-        q4.q4_decode_step(layers, 1, flags, ws=ws, ws_bytes=ws_bytes, stream=stream)
+    def time_mode(mode, steps, warmup):
+        flags = MODES[mode]
+        ws_bytes = q4.q4_decode_step_workspace_bytes(layers, 1, flags)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        h0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(args.steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        h1 = time.perf_counter()
-    ms = e0.elapsed_time(e1) / args.steps
-    host_ms = (h1 - h0) * 1e3 / args.steps
+        def step():
+            q4.q4_decode_step(layers, 1, flags, ws=ws, ws_bytes=ws_bytes, stream=stream)
+
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            h0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(steps):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            h1 = time.perf_counter()
+        return e0.elapsed_time(e1) / steps, (h1 - h0) * 1e3 / steps
+
+    ms, host_ms = time_mode(args.mode, args.steps, args.warmup)
     gbs = step_bytes / (ms * 1e-3) / 1e9
     if gbs > PEAK_GBS * 1.02:
         raise SystemExit(f"measured {gbs:.0f} GB/s is above the HBM peak: measurement error")
@@ -120,12 +129,21 @@ def main():
         "host_ms_per_step": round(host_ms, 5),
         "setup_s": round(setup_s, 1),
     }
+    # dominant kernel: the persistent step kernel, one launch per step; its
+    # algorithmic bytes per launch are the step's, its duration the event time per
+    # step (which also holds the counter-clearing kernel launched before it)
+    result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
+                          "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None,
+                          "kernel": "k_step" if args.mode != "launch_each" else "k_gemv_m1 (all)"}
     if not args.only_step:
-        # dominant kernel: one whole step when the step is one launch; otherwise the
-        # step's launches taken together (bytes per step / summed launch time)
-        result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
-                              "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None,
-                              "kernel": "q4_decode_step"}
+        other = {}
+        for mode in MODES:
+            if mode == args.mode:
+                continue
+            m_ms, _ = time_mode(mode, max(5, args.steps // 2), 3)
+            other[mode] = {"ms_per_step": round(m_ms, 5),
+                           "gbs": round(step_bytes / (m_ms * 1e-3) / 1e9, 1)}
+        result["other_modes"] = other
         if not args.no_probe:
             result["probe_read_gbs"] = probe_read(torch, q4, stream)
         if not args.no_cpu_baseline:

@@ -9,8 +9,9 @@
 #include <string>
 #include <vector>
 
-#include "../../include/q4f16.h"
+#include "q4f16.h"
 #include "q4_internal.h"
+#include "q4_step.h"
 
 namespace {
 
@@ -208,9 +209,83 @@ int q4_gemv_batched(const uint32_t* words, const uint16_t* scales, const uint16_
   return gemv_common("q4_gemv_batched", words, scales, X, Y, M, N, K, 0, ws, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Device copies of step descriptor tables, keyed by their contents (pointers,
+// shapes, dependencies) and device.  A table is uploaded on first use of a
+// layer list and reused by every later call with the same list; the least
+// recently used of kMaxTables entries is freed when a new one is needed.
+struct TableEntry {
+  int dev = -1;
+  std::vector<q4::StepDesc> desc;
+  q4::StepDesc* dptr = nullptr;
+  uint64_t last_use = 0;
+};
+constexpr size_t kMaxTables = 16;
+std::mutex g_table_mutex;
+std::vector<TableEntry> g_tables;
+uint64_t g_table_clock = 0;
+
+const q4::StepDesc* device_table(const q4::StepPlan& p, int dev, hipStream_t s, hipError_t* err) {
+  std::lock_guard<std::mutex> lock(g_table_mutex);
+  const size_t bytes = p.desc.size() * sizeof(q4::StepDesc);
+  for (TableEntry& e : g_tables) {
+    if (e.dev == dev && e.desc.size() == p.desc.size() &&
+        memcmp(e.desc.data(), p.desc.data(), bytes) == 0) {
+      e.last_use = ++g_table_clock;
+      return e.dptr;
+    }
+  }
+  if (g_tables.size() >= kMaxTables) {
+    size_t lru = 0;
+    for (size_t i = 1; i < g_tables.size(); ++i)
+      if (g_tables[i].last_use < g_tables[lru].last_use) lru = i;
+    (void)hipFree(g_tables[lru].dptr);      // synchronises: no launch still reads it
+    g_tables.erase(g_tables.begin() + (ptrdiff_t)lru);
+  }
+  TableEntry e;
+  e.dev = dev;
+  e.desc = p.desc;
+  if ((*err = hipMalloc(&e.dptr, bytes)) != hipSuccess) return nullptr;
+  if ((*err = hipMemcpyAsync(e.dptr, e.desc.data(), bytes, hipMemcpyHostToDevice, s)) !=
+      hipSuccess) {
+    (void)hipFree(e.dptr);
+    return nullptr;
+  }
+  e.last_use = ++g_table_clock;
+  g_tables.push_back(std::move(e));
+  return g_tables.back().dptr;
+}
+
+std::vector<q4::StepLayer> to_step_layers(const q4_layer* layers, int64_t n) {
+  std::vector<q4::StepLayer> v((size_t)n);
+  for (int64_t i = 0; i < n; ++i)
+    v[(size_t)i] = q4::StepLayer{layers[i].words, layers[i].scales, layers[i].x, layers[i].y,
+                                 layers[i].N, layers[i].K};
+  return v;
+}
+
+// The persistent path applies to M == 1 lists whose rows fit its item shape,
+// when one workgroup of the step kernel fits on every compute unit.
+bool use_persistent(const q4::DeviceInfo& d, const q4::StepPlan& p, int64_t M, uint32_t flags) {
+  if (M != 1 || (flags & Q4_STEP_LAUNCH_EACH) || !p.ok) return false;
+  int per_cu = 0;
+  if (q4::step_occupancy(p, &per_cu) != hipSuccess || per_cu < 1) {
+    (void)hipGetLastError();
+    return false;
+  }
+  (void)d;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, int64_t M,
                                       uint32_t flags) {
-  (void)flags;
   if (!layers || n_layers < 1 || M < 1 || M > q4::kMaxM) return 0;
   const q4::DeviceInfo* d = q4::device_info();
   if (!d) return 0;
@@ -221,6 +296,12 @@ size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, 
     const size_t b = q4::plan_auto(*d, M, L.N, L.K).ws_bytes;
     if (b > need) need = b;
   }
+  if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
+    std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
+    q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
+    const size_t b = q4::step_workspace_bytes(p);
+    if (b > need) need = b;
+  }
   return need;
 }
 
@@ -229,7 +310,10 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (!layers) return fail(Q4_ERR_NULL, "q4_decode_step: layers is NULL");
   if (n_layers < 1) return fail(Q4_ERR_SHAPE, "q4_decode_step: n_layers = %lld: must be >= 1",
                                 (long long)n_layers);
-  if (flags & ~Q4_STEP_LAUNCH_EACH)
+  if (n_layers > (1 << 20))
+    return fail(Q4_ERR_UNSUPPORTED, "q4_decode_step: n_layers = %lld: too many",
+                (long long)n_layers);
+  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED))
     return fail(Q4_ERR_SHAPE, "q4_decode_step: unknown flags 0x%x", flags);
   char what[64];
   for (int64_t i = 0; i < n_layers; ++i) {
@@ -239,6 +323,22 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   }
   const q4::DeviceInfo* d = q4::device_info();
   if (!d) return fail(Q4_ERR_DEVICE, "q4_decode_step: no HIP device");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
+    std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
+    q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
+    if (use_persistent(*d, p, M, flags)) {
+      if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_workspace_bytes(p)))
+        return rc;
+      hipError_t e = hipSuccess;
+      const q4::StepDesc* table = device_table(p, d->id, s, &e);
+      if (!table) return device_error(e, "q4_decode_step: descriptor table");
+      e = q4::launch_step(p, table, ws, s);
+      return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
+    }
+  }
+
   std::vector<q4::GemvPlan> plans((size_t)n_layers);
   size_t need = 0;
   for (int64_t i = 0; i < n_layers; ++i) {
@@ -246,7 +346,6 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
     if (plans[(size_t)i].ws_bytes > need) need = plans[(size_t)i].ws_bytes;
   }
   if (int rc = check_ws("q4_decode_step", ws, ws_bytes, need)) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   for (int64_t i = 0; i < n_layers; ++i) {
     const q4_layer& L = layers[i];
     q4::GemvArgs a{L.words, L.scales, L.x, L.y, M, L.N, L.K};

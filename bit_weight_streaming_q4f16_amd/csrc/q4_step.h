@@ -1,0 +1,56 @@
+// Internal interface of the persistent decode-step kernel (q4_step.hip).
+#pragma once
+
+#include <vector>
+
+#include "q4_internal.h"
+
+namespace q4 {
+
+constexpr int kStepThreads = 1024;   // one workgroup of 16 waves per compute unit
+constexpr int kXBufs = 8;            // x buffers: waves may run up to 8 GEMVs apart
+
+// One GEMV as the persistent kernel reads it (device-resident table, 64 bytes).
+struct StepDesc {
+  const uint4* W;        // words, one uint4 per 32-weight group: [N][G]
+  const uint16_t* S;     // scales [N][G]
+  const uint4* X;        // x as blocks of 8 halves: [4G]
+  uint16_t* Y;           // y [N]
+  int N, G;              // rows, groups per row (K / 32)
+  int lpr_log2;          // lanes per row = 2^lpr_log2 (4..64)
+  int C;                 // groups per lane (<= 4)
+  int steps;             // row-steps: ceil(N / (64 / lanes per row))
+  int dep;               // descriptor that must be complete before x is read (-1: none)
+  int signal;            // 1 if a later descriptor waits for this one
+  int pad;
+};
+static_assert(sizeof(StepDesc) == 64, "StepDesc layout");
+
+struct StepLayer {
+  const uint32_t* words;
+  const uint16_t* scales;
+  const uint16_t* x;
+  uint16_t* y;
+  int64_t N, K;
+};
+
+struct StepPlan {
+  bool ok = false;       // false: the list needs the one-kernel-per-GEMV path
+  int grid = 0;          // workgroups (one per compute unit)
+  int maxG = 0;
+  int ybuf_rows = 0;
+  int counters = 0;      // completion counters + error word in the workspace
+  size_t lds_bytes = 0;
+  std::vector<StepDesc> desc;
+};
+
+// ordered: every descriptor waits for its predecessor (a chain of dependent GEMVs);
+// otherwise only for earlier descriptors whose memory it shares.
+StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool ordered);
+size_t step_workspace_bytes(const StepPlan& p);
+// dev_desc: p.desc copied to device memory.  Zeroes the counters in ws, then
+// runs the cooperative kernel.
+hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, hipStream_t s);
+hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu);
+
+}  // namespace q4

@@ -1,0 +1,615 @@
+// Persistent decode-step kernel: every M = 1 GEMV of a layer list in ONE launch.
+//
+// The Zero TVM decode loop runs the projections of every layer and then the LM
+// head ("Decode loop"); decode is bandwidth-bound, so what matters is that the
+// weight stream never stops (everything-webgpu AI.md: time per token scales with
+// weight bytes; the launches themselves are a separate cost term).  Separate
+// kernels per GEMV stop the stream at every boundary: the next kernel cannot
+// issue a load before the previous one drains, and each small GEMV pays a fixed
+// latency chain (stage x, first load round trip, reduction, drain).  Here the
+// weights of later GEMVs are already in flight while earlier ones finish,
+// because weights never depend on activations.
+//
+// One workgroup of 16 waves per compute unit (cooperative launch: all resident):
+//  * waves 1..15 (compute): walk a static list of items -- row-steps of every
+//    GEMV in list order -- with a P-deep ring of 128-bit loads in registers
+//    (item i + P is issued right after item i is consumed).  An item is one row
+//    per team of 2^lpr lanes; each lane holds up to 4 groups (4 x dwordx4), so
+//    rows up to K = 8192.  Results go to an LDS y buffer, so these waves never
+//    wait on a store (on gfx9 stores and loads share one in-order counter).
+//  * wave 0 (sync): stages x of GEMV k into one of two LDS buffers once the
+//    GEMVs it depends on are complete on every workgroup, copies finished y rows
+//    from LDS to memory, and publishes per-GEMV completion with a release atomic
+//    that other workgroups poll.  Its waits never hold back the weight stream.
+//
+// Dependencies (decided on the host): descriptor k waits for descriptor dep[k]
+// (and, by list order, everything before it) to complete on all workgroups
+// before its x is read.  Default: only where an earlier descriptor writes memory
+// that k reads or writes; the "ordered" mode makes every descriptor wait for its
+// predecessor, as in a decode step whose GEMVs feed each other.
+#include "q4_step.h"
+
+namespace q4 {
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+template <typename T, typename F>
+__device__ __forceinline__ T bits(F v) {
+  return __builtin_bit_cast(T, v);
+}
+
+// Pointers read from the descriptor table are generic; casting them to the
+// global address space makes the compiler emit global_* (not flat_*) memory
+// instructions, which count only in vmcnt (flat ones also count in lgkmcnt,
+// which would make every LDS wait also wait for the weight stream).
+#define Q4_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const Q4_GLOBAL T* gptr(const T* p) {
+  return (const Q4_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ Q4_GLOBAL T* gptr_mut(T* p) {
+  return (Q4_GLOBAL T*)p;
+}
+typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt_g(const Q4_GLOBAL uint4* p) {
+  const u32x4_g v = __builtin_nontemporal_load((const Q4_GLOBAL u32x4_g*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint4 pair_order(uint4 v) {
+  uint4 o;
+  o.x = (v.x & 0xFFFFu) | (v.z << 16);
+  o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+  o.z = (v.y & 0xFFFFu) | (v.w << 16);
+  o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+  return o;
+}
+
+// The nibble-pair constants.  OR-ing nibbles 0 and 4 (mask 0x000F000F) into two
+// fp16 values with exponent 2^10 gives (1024 + q0, 1024 + q4); nibbles 1 and 5
+// (mask 0x00F000F0, place value 16) under exponent 2^6 (ulp 1/16) give
+// (64 + q1, 64 + q5); the same on word >> 8 gives elements 2, 6 and 3, 7.  The
+// masks live in VGPRs and the exponents in SGPRs, so each pair is ONE
+// v_and_or_b32 (gfx9 VOP3 takes one scalar operand and no literal).
+struct Nibbles {
+  uint32_t m_lo, m_hi;   // VGPR: 0x000F000F, 0x00F000F0
+  uint32_t e_lo, e_hi;   // SGPR: 0x64006400 (1024, 1024), 0x54005400 (64, 64)
+};
+
+__device__ __forceinline__ Nibbles make_nibbles() {
+  Nibbles n{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+  asm volatile("" : "+v"(n.m_lo), "+v"(n.m_hi));
+  asm volatile("" : "+s"(n.e_lo), "+s"(n.e_hi));
+  return n;
+}
+
+// One 32-weight group: sum_k (q_k - 7) x_k in fp32.  The dequantised values are
+// t_k = 1024 + q_k (k even) or 64 + q_k (k odd); the chain is seeded with minus
+// the group's bias term 1031 * sum(x at even k) + 71 * sum(x at odd k), so what
+// is left is the wanted sum.  x holds the group's four pair-ordered blocks.
+__device__ __forceinline__ float group_dot(uint4 w, const uint4 (&x)[4], float neg_bias,
+                                          const Nibbles& nb) {
+  const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
+  float a = neg_bias, b = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t v = wj[j], v8 = v >> 8;
+    a = __builtin_amdgcn_fdot2(bits<h2_t>((v & nb.m_lo) | nb.e_lo), bits<h2_t>(x[j].x), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>((v & nb.m_hi) | nb.e_hi), bits<h2_t>(x[j].y), b, false);
+    a = __builtin_amdgcn_fdot2(bits<h2_t>((v8 & nb.m_lo) | nb.e_lo), bits<h2_t>(x[j].z), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>((v8 & nb.m_hi) | nb.e_hi), bits<h2_t>(x[j].w), b, false);
+  }
+  return a + b;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return bits<float>(__builtin_amdgcn_update_dpp(0, bits<int>(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned teams of 2^lg lanes (lg in [2, 6], uniform).
+__device__ __forceinline__ float team_sum(float v, int lg) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  if (lg >= 3) v += dpp<0x141>(v);
+  if (lg >= 4) v += dpp<0x140>(v);
+  if (lg >= 5) {
+    const auto r = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(v), bits<uint32_t>(v),
+                                                    false, false);
+    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
+  }
+  if (lg >= 6) {
+    const auto r = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(v), bits<uint32_t>(v),
+                                                    false, false);
+    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
+  }
+  return v;
+}
+
+// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt left at their maxima): LDS ops of
+// this wave are complete, outstanding vector-memory loads are not waited for.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ int lds_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+constexpr int kWaves = kStepThreads / 64;   // 16
+constexpr int kSync = 4;                    // sync waves (stage x, copy out y)
+constexpr int kCompute = kWaves - kSync;    // compute waves
+static_assert(kXBufs % kSync == 0, "a GEMV and the one whose x buffer it reuses share an owner");
+constexpr unsigned kSpinLimit = 1u << 24;   // bounded waits (about a second)
+constexpr int kCoherent = 1 | 16;           // cache policy sc0 | sc1: device-coherent access
+constexpr int kWaitVm0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt untouched)
+
+struct Shared {
+  int x_ready[kXBufs];   // GEMV index whose x sits in buffer b (-1: none yet)
+  int local_done[kXBufs];// compute-wave completions per buffer (monotonic)
+  int err;               // a compute wave's wait ran out (copied out by the sync wave)
+};
+
+// First row-step of workgroup wg for a GEMV with `steps` row-steps
+// (steps * wg < 2^31 for every supported shape: steps <= N < 2^24, wg < 128).
+__device__ __forceinline__ int wg_step(int steps, int wg, int nwg) {
+  return (int)(((unsigned)steps * (unsigned)wg) / (unsigned)nwg);
+}
+
+// LDS layout, per x buffer b (kXBufs of them):
+//   xbuf[b]: 4 planes of maxG pair-ordered blocks (uint4); maxG is the largest
+//            padded group count (lanes per row x groups per lane) of the list,
+//            blocks past a GEMV's own G are zero
+//   cbuf[b]: maxG floats, the bias term of each group (zero past G)
+//   ybuf[b]: ybuf_rows fp16 results of this workgroup's rows
+template <int B>
+__global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restrict__ D, int n,
+                                                       unsigned* __restrict__ done,
+                                                       unsigned* __restrict__ err, int maxG,
+                                                       int ybuf_rows) {
+  extern __shared__ uint4 smem[];
+  __shared__ Shared sh;
+  uint4* xbuf = smem;                                                           // [NX][4][maxG]
+  float* cbuf = reinterpret_cast<float*>(smem + kXBufs * 4 * maxG);             // [NX][maxG]
+  uint16_t* ybuf = reinterpret_cast<uint16_t*>(cbuf + kXBufs * maxG);          // [NX][rows]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  if (threadIdx.x < kXBufs) {
+    sh.x_ready[threadIdx.x] = -1;
+    sh.local_done[threadIdx.x] = 0;
+  }
+  if (threadIdx.x == 0) sh.err = 0;
+  __syncthreads();
+
+  if (wave < kSync) {
+    // ----------------------------------------------------------- sync waves
+    // Sync wave `wave` owns GEMVs k = wave (mod kSync): it stages their x and
+    // copies out / publishes their y.  kXBufs is a multiple of kSync, so GEMV k
+    // and the GEMV k - kXBufs whose buffer it reuses have the same owner.
+    const int me = wave;
+    int next_fin = me;                 // next own GEMV to copy out and publish
+    auto complete = [&](int i) {
+      return (unsigned)lds_load(&sh.local_done[i % kXBufs]) >=
+             (unsigned)kCompute * (unsigned)(i / kXBufs + 1);
+    };
+    auto finish_one = [&](int i) {
+      const StepDesc& d = D[i];
+      const int b = i % kXBufs;
+      const int rps = 64 >> d.lpr_log2;
+      const int r0 = wg_step(d.steps, wg, nwg) * rps;
+      int r1 = wg_step(d.steps, wg + 1, nwg) * rps;
+      if (r1 > d.N) r1 = d.N;
+      const uint16_t* yb = ybuf + b * ybuf_rows;
+      if (!d.signal) {
+        Q4_GLOBAL uint16_t* Y = gptr_mut(d.Y);
+        for (int r = r0 + lane; r < r1; r += 64) Y[r] = yb[r - r0];
+      } else {
+        // device-coherent stores (written through to the coherence point), then
+        // wait for them and count this workgroup in: no cache-wide write-back
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+            d.Y, 0, 0x7FFFFFFF, 0x00020000);
+        for (int r = r0 + lane; r < r1; r += 64)
+          __builtin_amdgcn_raw_buffer_store_b16(yb[r - r0], ry, 2 * r, 0, kCoherent);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        if (lane == 0)
+          __hip_atomic_fetch_add(&done[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+    // finish own GEMVs <= last in order; block: wait for each to complete locally,
+    // otherwise stop at the first one that has not
+    auto finish_upto = [&](int last, bool block) {
+      while (next_fin <= last && next_fin < n) {
+        if (!complete(next_fin)) {
+          if (!block) return;
+          for (unsigned it = 0; !complete(next_fin); ++it) {
+            if (it > kSpinLimit) { err[0] = 1u; break; }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+        finish_one(next_fin);
+        next_fin += kSync;
+      }
+    };
+    for (int k = me; k < n; k += kSync) {
+      const StepDesc& d = D[k];
+      const int G = d.G, nblk = 4 * G;
+      finish_upto(k - kSync, false);             // publish what is already complete
+      if (k >= kXBufs) finish_upto(k - kXBufs, true);   // buffer k % kXBufs is free again
+      const bool coherent = d.dep >= 0;
+      if (coherent) {
+        if (d.dep % kSync == me) finish_upto(d.dep, true);
+        for (unsigned it = 0;
+             __hip_atomic_load(&done[d.dep], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+             (unsigned)nwg;
+             ++it) {
+          if (it > kSpinLimit) { err[0] = 2u; break; }
+          finish_upto(k - kSync, false);         // others may be waiting for those
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint4*>(d.X), 0, 0x7FFFFFFF, 0x00020000);
+      const Q4_GLOBAL u32x4_g* X = (const Q4_GLOBAL u32x4_g*)d.X;
+      const int b = k % kXBufs;
+      uint4* xb = xbuf + b * 4 * maxG;
+      float* cb = cbuf + b * maxG;
+      // x_k in (at most) two batches of 8 blocks per lane: one round trip for
+      // K <= 4096
+      for (int i0 = 0; i0 < nblk; i0 += 8 * 64) {
+        uint4 v[8];
+        if (coherent) {
+          // x may have been written by other workgroups in this launch: read it
+          // from the coherence point, past every cache
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * 64 + lane;
+            if (i < nblk) {
+              const u32x4_g t = __builtin_amdgcn_raw_buffer_load_b128(rx, 16 * i, 0, kCoherent);
+              v[u] = make_uint4(t[0], t[1], t[2], t[3]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * 64 + lane;
+            if (i < nblk) {
+              const u32x4_g t = X[i];
+              v[u] = make_uint4(t[0], t[1], t[2], t[3]);
+            }
+          }
+        }
+        // pair-order the blocks into plane j = word j, and per group the bias
+        // term 1031 * sum(x at even k) + 71 * sum(x at odd k)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * 64 + lane;
+          if (i0 + u * 64 < nblk) {           // whole quads (nblk % 4 == 0): uniform
+            float se = 0.f, so = 0.f;
+            if (i < nblk) {
+              xb[(i & 3) * maxG + (i >> 2)] = pair_order(v[u]);
+              const uint32_t wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const h2_t h = bits<h2_t>(wv[e]);
+                se += (float)h[0];
+                so += (float)h[1];
+              }
+            }
+            // the four blocks of a group sit in four consecutive lanes
+            se += dpp<0xB1>(se);
+            so += dpp<0xB1>(so);
+            se += dpp<0x4E>(se);
+            so += dpp<0x4E>(so);
+            if (i < nblk && (i & 3) == 0) cb[i >> 2] = __builtin_fmaf(1031.0f, se, 71.0f * so);
+          }
+        }
+      }
+      // groups past G up to the padded count read x = 0 and bias 0, so the
+      // duplicated weights loaded for them contribute nothing
+      const int Gp = (1 << d.lpr_log2) * d.C;
+      for (int i = 4 * G + lane; i < 4 * Gp; i += 64) {
+        xb[(i & 3) * maxG + (i >> 2)] = make_uint4(0u, 0u, 0u, 0u);
+        if ((i & 3) == 0) cb[i >> 2] = 0.f;
+      }
+      wait_lds();
+      if (lane == 0) __hip_atomic_store(&sh.x_ready[b], k, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    finish_upto(n - 1, true);
+    if (me == 0) {
+      // every compute wave has signalled the last GEMV (so none will still set
+      // the error word) once the owner of GEMV n - 1 is done; wave 0 waits for
+      // the last completion before reading it
+      for (unsigned it = 0; !complete(n - 1); ++it) {
+        if (it > kSpinLimit) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0) {
+        const int e = lds_load(&sh.err);
+        if (e) err[0] = (unsigned)e;
+      }
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- compute waves
+  const int c = wave - kSync;
+  const Nibbles nb = make_nibbles();
+  // Issue cursor: the next item of this wave.  A workgroup's items of all GEMVs,
+  // in list order, form one sequence dealt round-robin to its compute waves, so
+  // every wave gets the same share of the whole step (to one item) instead of
+  // the first waves taking the remainder of every GEMV.  The cursor keeps the
+  // current GEMV's descriptor in (scalar) registers: the table is read only at
+  // GEMV transitions, never per item.
+  struct Cursor {
+    const Q4_GLOBAL uint4* W;
+    const Q4_GLOBAL uint16_t* S;
+    int j, s, s_end;             // GEMV, next row-step, end row-step (this workgroup)
+    int N, G, lg, C, r0;         // its shape, and its first row in this workgroup
+  } cu;
+  int base = 0;                  // items of GEMVs before cu.j in this workgroup, mod kCompute
+  // enter GEMV j or, if this wave has no item there, the next one that has
+  auto enter = [&](int j) {
+    for (; j < n; ++j) {
+      const StepDesc& d = D[j];
+      const int s0 = wg_step(d.steps, wg, nwg);
+      const int s1 = wg_step(d.steps, wg + 1, nwg);
+      int off = c - base;
+      if (off < 0) off += kCompute;
+      base = (base + (s1 - s0)) % kCompute;      // GEMV j's items are dealt either way
+      if (s0 + off < s1) {
+        cu.W = gptr(d.W);
+        cu.S = gptr(d.S);
+        cu.N = d.N;
+        cu.G = d.G;
+        cu.lg = d.lpr_log2;
+        cu.C = d.C;
+        cu.j = j;
+        cu.s = s0 + off;
+        cu.s_end = s1;
+        cu.r0 = s0 * (64 >> d.lpr_log2);
+        return;
+      }
+    }
+    cu.j = n;
+  };
+  enter(0);
+
+  auto wait_x = [&](int j) {
+    for (unsigned it = 0; lds_load(&sh.x_ready[j % kXBufs]) != j; ++it) {
+      if (it > kSpinLimit) {
+        __hip_atomic_store(&sh.err, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
+  int cur = 0;                    // GEMVs [0, cur) have been signalled by this wave
+  auto signal_upto = [&](int j) { // signal completion of GEMVs [cur, j)
+    for (; cur < j; ++cur) {
+      wait_x(cur);
+      wait_lds();                 // this wave's y rows of `cur` are in LDS
+      if (lane == 0) __hip_atomic_fetch_add(&sh.local_done[cur % kXBufs], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  };
+
+  // Bursts of B items: all loads of a burst are issued before any is consumed,
+  // so no loaded value crosses the loop's back edge (the compiler then waits
+  // exactly for the item being consumed).  Every issue is exactly eight loads
+  // (four dwordx4 + four ushort), also past the end of the list (then it
+  // re-reads the last GEMV's first row and the item is marked empty).
+  const StepDesc& last = D[n - 1];
+  const Q4_GLOBAL uint4* const W_last = gptr(last.W);
+  const Q4_GLOBAL uint16_t* const S_last = gptr(last.S);
+  while (true) {
+    uint4 rw[B][4];
+    uint16_t rs[B][4];
+    int rj[B], rrow[B], rN[B], rG[B], rlg[B], rC[B], rr0[B];
+#pragma unroll
+    for (int p = 0; p < B; ++p) {
+      const bool live = cu.j < n;
+      const int lg = live ? cu.lg : 2, lpr = 1 << lg;
+      const int G = live ? cu.G : 1;
+      const int li = lane & (lpr - 1);
+      const int row0 = live ? cu.s * (64 >> lg) : 0;
+      int row = row0 + (lane >> lg);
+      if (live && row > cu.N - 1) row = cu.N - 1;
+      if (!live) row = 0;
+      const Q4_GLOBAL uint4* wr = (live ? cu.W : W_last) + (int64_t)row * G;
+      const Q4_GLOBAL uint16_t* sr = (live ? cu.S : S_last) + (int64_t)row * G;
+      // slots past the row's groups re-read a group already being fetched
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        int g = li + lpr * t;
+        g = g < G ? g : li;
+        if (!live) g = 0;
+        rw[p][t] = load_nt_g(wr + g);
+        rs[p][t] = sr[g];
+      }
+      rj[p] = live ? cu.j : -1;
+      rrow[p] = row0;
+      rN[p] = cu.N;
+      rG[p] = G;
+      rlg[p] = lg;
+      rC[p] = cu.C;
+      rr0[p] = cu.r0;
+      if (live) {
+        cu.s += kCompute;
+        if (cu.s >= cu.s_end) enter(cu.j + 1);
+      }
+    }
+    // All items of the burst in one GEMV (the common case): x of each group is
+    // read from LDS once and used for all B rows, which also gives B independent
+    // dot-product chains.
+    if (rj[B - 1] >= 0 && rj[0] == rj[B - 1]) {
+      const int j = rj[0];
+      signal_upto(j);
+      wait_x(j);
+      const int lg = rlg[0], lpr = 1 << lg;
+      const int li = lane & (lpr - 1);
+      const int xi = j % kXBufs;
+      const uint4* xb = xbuf + xi * 4 * maxG + li;
+      const float* cb = cbuf + xi * maxG + li;
+      float acc[B];
+#pragma unroll
+      for (int p = 0; p < B; ++p) acc[p] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < rC[0]) {
+          uint4 x[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
+          const float nbias = -cb[lpr * t];
+#pragma unroll
+          for (int p = 0; p < B; ++p) {
+            const float pd = group_dot(rw[p][t], x, nbias, nb);
+            acc[p] = __builtin_fmaf(pd, (float)bits<_Float16>(rs[p][t]), acc[p]);
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < B; ++p) {
+        const float r = team_sum(acc[p], lg);
+        const int row = rrow[p] + (lane >> lg);
+        if (li == 0 && row < rN[p])
+          ybuf[xi * ybuf_rows + (row - rr0[p])] = bits<uint16_t>((_Float16)r);
+      }
+      continue;
+    }
+#pragma unroll
+    for (int p = 0; p < B; ++p) {
+      const int j = rj[p];
+      if (j < 0) goto drained;
+      signal_upto(j);
+      wait_x(j);
+      const int lg = rlg[p], lpr = 1 << lg;
+      const int li = lane & (lpr - 1);
+      const int row = rrow[p] + (lane >> lg);
+      const int xi = j % kXBufs;
+      const uint4* xb = xbuf + xi * 4 * maxG + li;
+      const float* cb = cbuf + xi * maxG + li;
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < rC[p]) {
+          uint4 x[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
+          const float pd = group_dot(rw[p][t], x, -cb[lpr * t], nb);
+          acc = __builtin_fmaf(pd, (float)bits<_Float16>(rs[p][t]), acc);
+        }
+      }
+      acc = team_sum(acc, lg);
+      if (li == 0 && row < rN[p])
+        ybuf[xi * ybuf_rows + (row - rr0[p])] = bits<uint16_t>((_Float16)acc);
+    }
+  }
+drained:
+  signal_upto(n);
+}
+
+__global__ void k_zero(unsigned* __restrict__ p, int count) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+constexpr int kBurst = 3;
+
+}  // namespace
+
+StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool ordered) {
+  StepPlan p;
+  p.ok = false;
+  if (n < 1) return p;
+  p.grid = d.cus;
+  p.desc.resize((size_t)n);
+  int maxG = 1, ybuf_rows = 1;
+  for (int64_t k = 0; k < n; ++k) {
+    const StepLayer& L = layers[k];
+    const int64_t G = L.K / 32;
+    if (G > 256) return p;                    // rows beyond 4 groups per lane
+    int lg = 2;
+    while ((4 << lg) < G && lg < 6) ++lg;     // 2^lg lanes x 4 groups >= G
+    const int lpr = 1 << lg;
+    const int C = (int)((G + lpr - 1) / lpr);
+    const int rps = 64 / lpr;
+    StepDesc& s = p.desc[(size_t)k];
+    s.W = reinterpret_cast<const uint4*>(L.words);
+    s.S = L.scales;
+    s.X = reinterpret_cast<const uint4*>(L.x);
+    s.Y = L.y;
+    s.N = (int)L.N;
+    s.G = (int)G;
+    s.lpr_log2 = lg;
+    s.C = C;
+    s.steps = (int)((L.N + rps - 1) / rps);
+    s.dep = -1;
+    s.signal = 0;
+    s.pad = 0;
+    if (lpr * C > maxG) maxG = lpr * C;         // padded group count
+    const int rows_wg = ((s.steps + p.grid - 1) / p.grid) * rps;
+    if (rows_wg > ybuf_rows) ybuf_rows = rows_wg;
+  }
+  // dependencies: k waits for the latest earlier descriptor that writes what k
+  // reads or writes (or, ordered, simply its predecessor)
+  auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+  };
+  for (int64_t k = 1; k < n; ++k) {
+    int dep = -1;
+    if (ordered) {
+      dep = (int)k - 1;
+    } else {
+      const StepLayer& Lk = layers[k];
+      for (int64_t i = k - 1; i >= 0 && dep < 0; --i) {
+        const StepLayer& Li = layers[i];
+        const int64_t yi = 2 * Li.N;
+        if (overlap(Li.y, yi, Lk.x, 2 * Lk.K) || overlap(Li.y, yi, Lk.y, 2 * Lk.N) ||
+            overlap(Li.x, 2 * Li.K, Lk.y, 2 * Lk.N))
+          dep = (int)i;
+      }
+    }
+    p.desc[(size_t)k].dep = dep;
+    if (dep >= 0) p.desc[(size_t)dep].signal = 1;
+  }
+  p.maxG = maxG;
+  p.ybuf_rows = (ybuf_rows + 7) & ~7;
+  p.lds_bytes = (size_t)kXBufs * ((size_t)4 * maxG * 16 + (size_t)maxG * 4 + (size_t)p.ybuf_rows * 2);
+  p.counters = (int)n + 4;
+  p.ok = p.lds_bytes <= d.lds_per_block - sizeof(int) * 8;
+  return p;
+}
+
+size_t step_workspace_bytes(const StepPlan& p) {
+  return ((size_t)p.counters * sizeof(unsigned) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, hipStream_t s) {
+  unsigned* done = static_cast<unsigned*>(ws);
+  unsigned* err = done + (p.counters - 1);
+  hipLaunchKernelGGL(k_zero, dim3(1), dim3(256), 0, s, done, p.counters);
+  if (hipError_t e = hipGetLastError()) return e;
+  auto kern = k_step<kBurst>;
+  if (p.lds_bytes > 65536) {
+    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)p.lds_bytes))
+      return e;
+  }
+  int n = (int)p.desc.size(), maxG = p.maxG, yr = p.ybuf_rows;
+  void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&done, (void*)&err, (void*)&maxG,
+                  (void*)&yr};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(p.grid),
+                                    dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
+}
+
+hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks_per_cu, reinterpret_cast<const void*>(k_step<kBurst>), kStepThreads,
+      p.lds_bytes);
+}
+
+}  // namespace q4

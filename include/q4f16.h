@@ -129,8 +129,14 @@ typedef struct q4_layer {
   int64_t K;
 } q4_layer;
 
-/* Launch one kernel per descriptor on the stream (stream-ordered). */
+/* Run every descriptor as its own kernel launch, in list order on the stream. */
 #define Q4_STEP_LAUNCH_EACH 0x1u
+/* Treat every descriptor as dependent on the one before it: descriptor k reads
+ * its x only after descriptor k - 1 is complete (a chain of GEMVs, each feeding
+ * the next, as the projections of a decode step do through the operations
+ * between them).  Without this flag a descriptor waits only for earlier
+ * descriptors whose y overlaps its x or y, or whose x overlaps its y. */
+#define Q4_STEP_ORDERED 0x2u
 
 /* q4_decode_step: run the GEMVs of layers[0 .. n_layers) in list order, as the
  * Zero TVM decode loop walks the projections of every layer and then the LM
@@ -138,7 +144,19 @@ typedef struct q4_layer {
  * q4_gemv_batched (M > 1) on each descriptor in turn; a descriptor's x may be an
  * earlier descriptor's y.  Every descriptor is validated before anything is
  * enqueued.  `layers` is host memory, read during the call only.
- * ws: q4_decode_step_workspace_bytes(...) bytes. */
+ *
+ * With M == 1, rows of at most K = 8192 and without Q4_STEP_LAUNCH_EACH, the
+ * whole list runs as ONE persistent kernel (after a small kernel that clears the
+ * workspace's completion counters): the weights of later GEMVs stream while
+ * earlier ones finish, and dependencies are kept with per-GEMV completion
+ * counters in the workspace.  Its descriptor table is copied to device memory
+ * the first time a given list is used (the library allocates that copy and keeps
+ * it for later calls with the same list; at most 16 lists are kept, the least
+ * recently used is freed with hipFree, which synchronises the device).  Make
+ * the first call with a given list outside stream capture.  Other lists run one
+ * kernel per descriptor.
+ * ws: q4_decode_step_workspace_bytes(...) bytes, 16-byte aligned; calls that
+ * share a workspace must be ordered on one stream. */
 Q4_API int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t flags,
                    void* ws, size_t ws_bytes, q4_stream_t stream);
 

@@ -1,0 +1,135 @@
+"""The decode-step driver (q4_decode_step) in its three modes: one persistent
+kernel honouring memory hazards (default), one persistent kernel with every
+descriptor waiting for its predecessor (ordered), one kernel per descriptor.
+Every output is checked against the oracle on the inputs the GPU actually read."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import synth
+import bit_weight_streaming_q4f16_amd as q4
+from gpuhelp import assert_gemv_close, dev_half, dev_words, half_f64, host_half, host_words
+
+pytestmark = pytest.mark.gpu
+
+MODES = {"hazards": 0, "ordered": q4.STEP_ORDERED, "launch_each": q4.STEP_LAUNCH_EACH}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q4.load()
+
+
+def mat(label, N, K, chain=False):
+    kw = dict(sigma=2.0 / K, floor=0.5 / K) if chain else {}
+    m = synth.Matrix(label, N, K, **kw)
+    return m, dev_words(m.words()), dev_half(m.scales())
+
+
+def run(descs, flags):
+    layers = q4.make_layers(descs)
+    q4.q4_decode_step(layers, 1, flags)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_dependent_chain(mode):
+    """Each descriptor reads the previous one's output (RAW hazards)."""
+    dims = [3072, 8192, 3072, 9216, 3072, 2048, 6144, 512, 1024]
+    x0 = dev_half(synth.activations("stepchain/x", 0, dims[0]))
+    descs, mats = [], []
+    x = x0
+    for i in range(len(dims) - 1):
+        m, W, S = mat(f"stepchain/{i}", dims[i + 1], dims[i], chain=True)
+        y = torch.full((dims[i + 1],), float("nan"), dtype=torch.float16, device="cuda")
+        descs.append((W, S, x, y))
+        mats.append(m)
+        x = y
+    run(descs, MODES[mode])
+    for m, (W, S, X, Y) in zip(mats, descs):
+        y = host_half(Y)
+        assert np.all(np.isfinite(half_f64(y)))
+        assert_gemv_close(y, m.words(), m.scales(), host_half(X))
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_write_after_read_and_write_after_write(mode):
+    K = 1024
+    mA, WA, SA = mat("war/a", K, K)
+    mB, WB, SB = mat("war/b", K, K)
+    mC, WC, SC = mat("war/c", K, K)
+    xa = synth.activations("war/xa", 0, K)
+    xb = synth.activations("war/xb", 0, K)
+    A = dev_half(xa)
+    B = dev_half(xb)
+    out = torch.empty(K, dtype=torch.float16, device="cuda")
+    # 0: out = WA A   1: A = WB B (overwrites 0's input)   2: out = WC B (overwrites 0's output)
+    run([(WA, SA, A, out), (WB, SB, B, A), (WC, SC, B, out)], MODES[mode])
+    assert_gemv_close(host_half(A), mB.words(), mB.scales(), xb)
+    assert_gemv_close(host_half(out), mC.words(), mC.scales(), xb)
+    # and the first descriptor read the original A: recompute it alone
+    A2 = dev_half(xa)
+    out0 = torch.empty(K, dtype=torch.float16, device="cuda")
+    run([(WA, SA, A2, out0)], MODES[mode])
+    assert_gemv_close(host_half(out0), mA.words(), mA.scales(), xa)
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+@pytest.mark.parametrize("shapes", [
+    [(1, 32)], [(3, 544), (1000, 32), (257, 96)], [(7, 8192), (64, 64), (5000, 2048)],
+    [(32064, 3072)], [(17, 256)] * 9,
+], ids=["tiny", "ragged", "mixed", "lm_head", "many_small"])
+def test_independent_lists(mode, shapes):
+    descs, mats, xs = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        m, W, S = mat(f"ind/{i}/{N}x{K}", N, K)
+        x = synth.activations(f"ind/x/{i}", 0, K)
+        descs.append((W, S, dev_half(x), torch.empty(N, dtype=torch.float16, device="cuda")))
+        mats.append(m)
+        xs.append(x)
+    run(descs, MODES[mode])
+    for m, x, (W, S, X, Y) in zip(mats, xs, descs):
+        assert_gemv_close(host_half(Y), m.words(), m.scales(), x)
+
+
+def test_fallback_for_long_rows_and_repeat_determinism():
+    m1, W1, S1 = mat("fb/1", 300, 16384)     # K > 8192: one kernel per descriptor
+    m2, W2, S2 = mat("fb/2", 700, 3072)
+    x1 = synth.activations("fb/x1", 0, 16384)
+    x2 = synth.activations("fb/x2", 0, 3072)
+    y1 = torch.empty(300, dtype=torch.float16, device="cuda")
+    y2 = torch.empty(700, dtype=torch.float16, device="cuda")
+    descs = [(W1, S1, dev_half(x1), y1), (W2, S2, dev_half(x2), y2)]
+    run(descs, 0)
+    assert_gemv_close(host_half(y1), m1.words(), m1.scales(), x1)
+    assert_gemv_close(host_half(y2), m2.words(), m2.scales(), x2)
+    # the persistent kernel on its own, called repeatedly: bitwise the same
+    first = None
+    for _ in range(5):
+        run([descs[1]], q4.STEP_ORDERED)
+        cur = host_half(y2)
+        if first is None:
+            first = cur
+        assert np.array_equal(first, cur)
+
+
+def test_modes_agree_on_the_phi3_layer():
+    shapes = [(9216, 3072), (3072, 3072), (16384, 3072), (3072, 8192)]
+    outs = {}
+    mats = [mat(f"agree/{i}", N, K) for i, (N, K) in enumerate(shapes)]
+    x3 = dev_half(synth.activations("agree/x3", 0, 3072))
+    x8 = dev_half(synth.activations("agree/x8", 0, 8192))
+    for mode, flags in MODES.items():
+        descs = [(W, S, x8 if K == 8192 else x3, torch.empty(N, dtype=torch.float16, device="cuda"))
+                 for (m, W, S), (N, K) in zip(mats, shapes)]
+        run(descs, flags)
+        outs[mode] = [host_half(d[3]) for d in descs]
+    # the two persistent modes use the same arithmetic: bitwise equal
+    for a, b in zip(outs["hazards"], outs["ordered"]):
+        assert np.array_equal(a, b)
+    for (m, W, S), y, (N, K) in zip(mats, outs["ordered"], shapes):
+        x = host_half(x8 if K == 8192 else x3)
+        assert_gemv_close(y, m.words(), m.scales(), x)
