@@ -13,10 +13,20 @@ Prints ONE JSON line (rank 0):
   roofline = the dominant kernel's algorithmic bytes per launch / its average
              launch duration (HIP events on the stream it runs on) vs 8 TB/s;
   cpu_baseline = the CPU oracle on this host over one full step (single thread).
+
+Profiling aids (see profiles/):
+  --copy-probe BYTES        run only a plain device copy of BYTES (counter calibration)
+  --summarize-profiles DIR  turn the rocprofv3 CSV output under DIR (stats/, fetch/,
+                            write/, copy_fetch/, copy_write/, commands.txt) into the
+                            summaries profiles/k_step_phi3_decode_sweep.{md,json}
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,6 +34,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0          # MI355X HBM3E, published
+# the dominant kernel and the sources it is built from: traffic figures measured
+# with hardware counters are reported only while these are unchanged
+KERNEL = "k_step"
+KERNEL_SOURCES = ["bit_weight_streaming_q4f16_amd/csrc/q4_step.hip",
+                  "bit_weight_streaming_q4f16_amd/csrc/q4_step.h",
+                  "bit_weight_streaming_q4f16_amd/csrc/q4_internal.h"]
+PROFILE = os.path.join(ROOT, "profiles", "k_step_phi3_decode_sweep")
 METRIC = "achieved HBM GB/s (% of peak) and projected decode tok/s, q4 GEMV sweep"
 
 
@@ -43,6 +60,10 @@ def parse():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--only-step", action="store_true",
                     help="time only the decode step (for profiler runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="run only a plain device copy of BYTES, 3 times (counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from rocprofv3 CSV output under DIR")
     return ap.parse_args()
 
 
@@ -65,6 +86,9 @@ def build_sweep(torch, q4, synth, np, model="phi3", M=1):
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -78,6 +102,9 @@ def main():
     torch.cuda.set_device(0)
     q4.load()
     stream = torch.cuda.Stream()          # default priority
+    if args.copy_probe:
+        copy_probe(torch, q4, stream, args.copy_probe)
+        return
     t0 = time.time()
     descs, meta = build_sweep(torch, q4, synth, np)
     torch.cuda.synchronize()
@@ -132,9 +159,12 @@ def main():
     # dominant kernel: the persistent step kernel, one launch per step; its
     # algorithmic bytes per launch are the step's, its duration the event time per
     # step (which also holds the counter-clearing kernel launched before it)
+    result["us_per_gemv"] = round(ms * 1e3 / len(meta), 3)
     result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
-                          "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4), "traffic": None,
-                          "kernel": "k_step" if args.mode != "launch_each" else "k_gemv_m1 (all)"}
+                          "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4),
+                          "traffic": measured_traffic() if args.mode == "hazards" else None,
+                          "kernel": KERNEL if args.mode != "launch_each" else "k_gemv_m1 (all)",
+                          "algorithmic_bytes_per_launch": step_bytes}
     if not args.only_step:
         other = {}
         for mode in MODES:
@@ -149,6 +179,146 @@ def main():
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(np, torch, descs, meta)
     print(json.dumps(result), flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when there is none or the kernel has changed since."""
+    try:
+        with open(PROFILE + ".json") as fh:
+            prof = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if prof.get("source_sha256") != source_hash():
+        return None
+    return prof.get("traffic_bytes_per_launch")
+
+
+def copy_probe(torch, q4, stream, nbytes, reps=3):
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            q4.q4_probe_copy(src, dst, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    ok = bool(torch.equal(src[:1 << 20], dst[:1 << 20]))
+    print(json.dumps({"copy_bytes": nbytes, "launches": reps, "ms_per_launch": round(ms, 4),
+                      "gbs_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+                      "copied": ok}), flush=True)
+
+
+def _csv_rows(d, suffix):
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _is_kernel(name, kernel):
+    return re.search(r"(^|[\s:])" + re.escape(kernel) + r"(\(|<|$|\s)", name or "") is not None
+
+
+def _counter_per_dispatch(d, kernel, counter):
+    """Mean over the kernel's dispatches of the counter summed over its instances."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if not _is_kernel(r.get("Kernel_Name", ""), kernel) or r.get("Counter_Name") != counter:
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{counter} of {kernel}: no rows under {d}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize_profiles(d):
+    """Write profiles/k_step_phi3_decode_sweep.{md,json} from rocprofv3 output."""
+    import synth
+    shapes = synth.sweep_shapes("phi3")
+    step_bytes = sum(synth.algorithmic_bytes(1, N, K) for _, N, K in shapes)
+    stats = {}
+    for r in _csv_rows(os.path.join(d, "stats"), "kernel_stats.csv"):
+        for k in (KERNEL, "k_zero"):
+            if _is_kernel(r["Name"], k):
+                stats[k] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                            "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
+                            "percentage": float(r["Percentage"])}
+    fetch, nf = _counter_per_dispatch(os.path.join(d, "fetch"), KERNEL, "FETCH_SIZE")
+    write, nw = _counter_per_dispatch(os.path.join(d, "write"), KERNEL, "WRITE_SIZE")
+    cfetch, _ = _counter_per_dispatch(os.path.join(d, "copy_fetch"), "k_probe_copy", "FETCH_SIZE")
+    cwrite, _ = _counter_per_dispatch(os.path.join(d, "copy_write"), "k_probe_copy", "WRITE_SIZE")
+    copy_bytes = None
+    for f in glob.glob(os.path.join(d, "copy_*", "*.out")):
+        for line in open(f):
+            if line.startswith("{") and "copy_bytes" in line:
+                copy_bytes = json.loads(line)["copy_bytes"]
+    if copy_bytes is None:
+        raise SystemExit("copy probe output (copy_*/*.out) not found")
+    ff = copy_bytes / (cfetch * 1024)
+    fw = copy_bytes / (cwrite * 1024)
+    traffic = fetch * 1024 * ff + write * 1024 * fw
+    commands = open(os.path.join(d, "commands.txt")).read().strip()
+    avg = stats[KERNEL]["avg_us"]
+    out = {
+        "kernel": KERNEL, "workload": "phi3-mini decode-step weight sweep, M=1 (129 GEMVs)",
+        "source_sha256": source_hash(), "sources": KERNEL_SOURCES,
+        "kernel_stats": stats,
+        "algorithmic_bytes_per_launch": step_bytes,
+        "achieved_gbs_from_avg_duration": round(step_bytes / (avg * 1e-6) / 1e9, 1),
+        "FETCH_SIZE_KiB_per_dispatch": fetch, "WRITE_SIZE_KiB_per_dispatch": write,
+        "dispatches_counted": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+        "copy_calibration": {"bytes_read_and_written": copy_bytes, "FETCH_SIZE_KiB": cfetch,
+                             "WRITE_SIZE_KiB": cwrite, "fetch_factor": ff, "write_factor": fw},
+        "traffic_bytes_per_launch": round(traffic),
+        "traffic_over_algorithmic": round(traffic / step_bytes, 4),
+        "commands": commands.splitlines(),
+    }
+    with open(PROFILE + ".json", "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    lines = [
+        f"# {KERNEL}: Phi-3-mini decode-step weight sweep, M=1 (129 GEMVs, one launch)", "",
+        "Commands (run from the repository root; TMPDIR=/tmp):", "",
+        *["    " + c for c in commands.splitlines()], "",
+        "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+        "| kernel | calls | avg us | min us | max us | % of GPU time |",
+        "|---|---|---|---|---|---|",
+        *[f"| {k} | {v['calls']} | {v['avg_us']:.2f} | {v['min_us']:.2f} | {v['max_us']:.2f} | "
+          f"{v['percentage']:.2f} |" for k, v in stats.items()], "",
+        f"Algorithmic bytes per launch: {step_bytes:,} -> {out['achieved_gbs_from_avg_duration']}"
+        f" GB/s at the average duration ({100 * out['achieved_gbs_from_avg_duration'] / PEAK_GBS:.1f}"
+        " % of 8 TB/s).", "",
+        "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
+        f"- {KERNEL}: FETCH_SIZE {fetch:,.0f} KiB, WRITE_SIZE {write:,.0f} KiB per dispatch "
+        f"(mean of {nf} / {nw} dispatches)",
+        f"- calibration, k_probe_copy of {copy_bytes:,} bytes: FETCH_SIZE {cfetch:,.0f} KiB, "
+        f"WRITE_SIZE {cwrite:,.0f} KiB -> factors {ff:.4f} (fetch), {fw:.4f} (write)",
+        f"- traffic per launch = FETCH x 1024 x {ff:.4f} + WRITE x 1024 x {fw:.4f} = "
+        f"{traffic:,.0f} bytes = {traffic / step_bytes:.4f} x algorithmic", "",
+        f"Kernel sources (sha256 {out['source_sha256'][:16]}...): " + ", ".join(KERNEL_SOURCES),
+    ]
+    with open(PROFILE + ".md", "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def probe_read(torch, q4, stream, nbytes=4 << 30, reps=10):
@@ -177,8 +347,8 @@ def probe_read(torch, q4, stream, nbytes=4 << 30, reps=10):
             "sweep": {str(k): round(v, 1) for k, v in best.items()}}
 
 
-def cpu_baseline(np, torch, descs, meta):
-    """The CPU oracle (plain C, fp64, one thread) over one full step."""
+def cpu_baseline(np, torch, descs, meta, reps=4):
+    """The CPU oracle (plain C, fp64, one thread) over the full step, `reps` times."""
     import oracle
     import synth
     x_host = {}
@@ -189,12 +359,14 @@ def cpu_baseline(np, torch, descs, meta):
         if K not in x_host:
             x_host[K] = X.view(torch.int16).cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
-        oracle.gemv_f64(w, s, x_host[K])
+        for _ in range(reps):
+            oracle.gemv_f64(w, s, x_host[K])
         t += time.perf_counter() - t0
-        total_bytes += synth.algorithmic_bytes(1, N, K)
+        total_bytes += reps * synth.algorithmic_bytes(1, N, K)
     return {"value": round(total_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds": round(t, 2),
-            "sample": f"one full step ({len(meta)} GEMVs, all rows), fp64 plain C oracle"}
+            "sample": f"the full step ({len(meta)} GEMVs, all rows) {reps} times, "
+                      "fp64 plain C oracle, one thread"}
 
 
 if __name__ == "__main__":

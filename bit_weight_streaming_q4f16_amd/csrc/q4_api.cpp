@@ -12,6 +12,7 @@
 #include "q4f16.h"
 #include "q4_internal.h"
 #include "q4_step.h"
+#include "q4_step_dma.h"
 
 namespace {
 
@@ -219,8 +220,8 @@ namespace {
 // recently used of kMaxTables entries is freed when a new one is needed.
 struct TableEntry {
   int dev = -1;
-  std::vector<q4::StepDesc> desc;
-  q4::StepDesc* dptr = nullptr;
+  std::vector<uint8_t> bytes;
+  void* dptr = nullptr;
   uint64_t last_use = 0;
 };
 constexpr size_t kMaxTables = 16;
@@ -228,12 +229,10 @@ std::mutex g_table_mutex;
 std::vector<TableEntry> g_tables;
 uint64_t g_table_clock = 0;
 
-const q4::StepDesc* device_table(const q4::StepPlan& p, int dev, hipStream_t s, hipError_t* err) {
+const void* device_table(const void* host, size_t bytes, int dev, hipStream_t s, hipError_t* err) {
   std::lock_guard<std::mutex> lock(g_table_mutex);
-  const size_t bytes = p.desc.size() * sizeof(q4::StepDesc);
   for (TableEntry& e : g_tables) {
-    if (e.dev == dev && e.desc.size() == p.desc.size() &&
-        memcmp(e.desc.data(), p.desc.data(), bytes) == 0) {
+    if (e.dev == dev && e.bytes.size() == bytes && memcmp(e.bytes.data(), host, bytes) == 0) {
       e.last_use = ++g_table_clock;
       return e.dptr;
     }
@@ -247,9 +246,9 @@ const q4::StepDesc* device_table(const q4::StepPlan& p, int dev, hipStream_t s, 
   }
   TableEntry e;
   e.dev = dev;
-  e.desc = p.desc;
+  e.bytes.assign(static_cast<const uint8_t*>(host), static_cast<const uint8_t*>(host) + bytes);
   if ((*err = hipMalloc(&e.dptr, bytes)) != hipSuccess) return nullptr;
-  if ((*err = hipMemcpyAsync(e.dptr, e.desc.data(), bytes, hipMemcpyHostToDevice, s)) !=
+  if ((*err = hipMemcpyAsync(e.dptr, e.bytes.data(), bytes, hipMemcpyHostToDevice, s)) !=
       hipSuccess) {
     (void)hipFree(e.dptr);
     return nullptr;
@@ -299,8 +298,15 @@ size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, 
   if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
     std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
-    const size_t b = q4::step_workspace_bytes(p);
+    size_t b = q4::step_workspace_bytes(p);
     if (b > need) need = b;
+    std::vector<int> dep(p.desc.size()), sig(p.desc.size());
+    for (size_t i = 0; i < p.desc.size(); ++i) { dep[i] = p.desc[i].dep; sig[i] = p.desc[i].signal; }
+    if (!p.desc.empty() && (flags & Q4_STEP_LDS_RING)) {
+      q4::DmaPlan dp = q4::plan_step_dma(*d, sl.data(), n_layers, dep, sig);
+      b = q4::step_dma_workspace_bytes(dp);
+      if (b > need) need = b;
+    }
   }
   return need;
 }
@@ -313,7 +319,7 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (n_layers > (1 << 20))
     return fail(Q4_ERR_UNSUPPORTED, "q4_decode_step: n_layers = %lld: too many",
                 (long long)n_layers);
-  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED))
+  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED | Q4_STEP_LDS_RING))
     return fail(Q4_ERR_SHAPE, "q4_decode_step: unknown flags 0x%x", flags);
   char what[64];
   for (int64_t i = 0; i < n_layers; ++i) {
@@ -328,13 +334,31 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
     std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
+    if (p.ok && (flags & Q4_STEP_LDS_RING)) {
+      std::vector<int> dep(p.desc.size()), sig(p.desc.size());
+      for (size_t i = 0; i < p.desc.size(); ++i) { dep[i] = p.desc[i].dep; sig[i] = p.desc[i].signal; }
+      q4::DmaPlan dp = q4::plan_step_dma(*d, sl.data(), n_layers, dep, sig);
+      int per_cu = 0;
+      if (dp.ok && q4::step_dma_occupancy(dp, &per_cu) == hipSuccess && per_cu >= 1) {
+        if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_dma_workspace_bytes(dp)))
+          return rc;
+        hipError_t e = hipSuccess;
+        const void* table = device_table(dp.desc.data(), dp.desc.size() * sizeof(q4::DmaDesc),
+                                         d->id, s, &e);
+        if (!table) return device_error(e, "q4_decode_step: descriptor table");
+        e = q4::launch_step_dma(dp, static_cast<const q4::DmaDesc*>(table), ws, s);
+        return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
+      }
+      (void)hipGetLastError();
+    }
     if (use_persistent(*d, p, M, flags)) {
       if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_workspace_bytes(p)))
         return rc;
       hipError_t e = hipSuccess;
-      const q4::StepDesc* table = device_table(p, d->id, s, &e);
+      const void* table = device_table(p.desc.data(), p.desc.size() * sizeof(q4::StepDesc),
+                                       d->id, s, &e);
       if (!table) return device_error(e, "q4_decode_step: descriptor table");
-      e = q4::launch_step(p, table, ws, s);
+      e = q4::launch_step(p, static_cast<const q4::StepDesc*>(table), ws, s);
       return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
     }
   }

@@ -137,6 +137,12 @@ typedef struct q4_layer {
  * between them).  Without this flag a descriptor waits only for earlier
  * descriptors whose y overlaps its x or y, or whose x overlaps its y. */
 #define Q4_STEP_ORDERED 0x2u
+/* Use the persistent kernel variant that copies the weights into an LDS ring by
+ * DMA (global_load_lds) instead of streaming them through registers.  It applies
+ * when every K is a multiple of 256 and every scales pointer is 16-byte aligned;
+ * other lists ignore the flag.  Same results; slower on the lists measured so far,
+ * kept for comparison. */
+#define Q4_STEP_LDS_RING 0x4u
 
 /* q4_decode_step: run the GEMVs of layers[0 .. n_layers) in list order, as the
  * Zero TVM decode loop walks the projections of every layer and then the LM
@@ -149,7 +155,8 @@ typedef struct q4_layer {
  * whole list runs as ONE persistent kernel (after a small kernel that clears the
  * workspace's completion counters): the weights of later GEMVs stream while
  * earlier ones finish, and dependencies are kept with per-GEMV completion
- * counters in the workspace.  Its descriptor table is copied to device memory
+ * counters in the workspace.  The weights stream through registers (or, with
+ * Q4_STEP_LDS_RING, through an LDS ring).  Its descriptor table is copied to device memory
  * the first time a given list is used (the library allocates that copy and keeps
  * it for later calls with the same list; at most 16 lists are kept, the least
  * recently used is freed with hipFree, which synchronises the device).  Make

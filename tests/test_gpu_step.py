@@ -13,7 +13,11 @@ from gpuhelp import assert_gemv_close, dev_half, dev_words, half_f64, host_half,
 
 pytestmark = pytest.mark.gpu
 
-MODES = {"hazards": 0, "ordered": q4.STEP_ORDERED, "launch_each": q4.STEP_LAUNCH_EACH}
+# default: the register-streaming persistent kernel; *_ring: the LDS-ring kernel
+# where it applies (every K % 256 == 0, K <= 8192), else the register one
+MODES = {"hazards": 0, "ordered": q4.STEP_ORDERED, "launch_each": q4.STEP_LAUNCH_EACH,
+         "hazards_ring": q4.STEP_LDS_RING,
+         "ordered_ring": q4.STEP_ORDERED | q4.STEP_LDS_RING}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -36,9 +40,11 @@ def run(descs, flags):
 
 
 @pytest.mark.parametrize("mode", sorted(MODES))
-def test_dependent_chain(mode):
+@pytest.mark.parametrize("dims", [[3072, 8192, 3072, 6144, 2048, 512, 1024, 256, 3072],
+                                  [3072, 9216, 3072, 544, 96, 2048]],
+                         ids=["k256", "ragged_k"])
+def test_dependent_chain(mode, dims):
     """Each descriptor reads the previous one's output (RAW hazards)."""
-    dims = [3072, 8192, 3072, 9216, 3072, 2048, 6144, 512, 1024]
     x0 = dev_half(synth.activations("stepchain/x", 0, dims[0]))
     descs, mats = [], []
     x = x0
@@ -80,8 +86,8 @@ def test_write_after_read_and_write_after_write(mode):
 @pytest.mark.parametrize("mode", sorted(MODES))
 @pytest.mark.parametrize("shapes", [
     [(1, 32)], [(3, 544), (1000, 32), (257, 96)], [(7, 8192), (64, 64), (5000, 2048)],
-    [(32064, 3072)], [(17, 256)] * 9,
-], ids=["tiny", "ragged", "mixed", "lm_head", "many_small"])
+    [(32064, 3072)], [(17, 256)] * 9, [(1, 256), (3, 8192), (5, 512), (2049, 2048)],
+], ids=["tiny", "ragged", "mixed", "lm_head", "many_small", "k256_ragged_rows"])
 def test_independent_lists(mode, shapes):
     descs, mats, xs = [], [], []
     for i, (N, K) in enumerate(shapes):
@@ -127,9 +133,11 @@ def test_modes_agree_on_the_phi3_layer():
                  for (m, W, S), (N, K) in zip(mats, shapes)]
         run(descs, flags)
         outs[mode] = [host_half(d[3]) for d in descs]
-    # the two persistent modes use the same arithmetic: bitwise equal
-    for a, b in zip(outs["hazards"], outs["ordered"]):
-        assert np.array_equal(a, b)
+    # the persistent kernels use the same lane mapping and arithmetic for these
+    # shapes (32 lanes x 3 groups, 64 x 4): bitwise equal across modes and kernels
+    for m in ("ordered", "hazards_ring", "ordered_ring"):
+        for a, b in zip(outs["hazards"], outs[m]):
+            assert np.array_equal(a, b), m
     for (m, W, S), y, (N, K) in zip(mats, outs["ordered"], shapes):
         x = host_half(x8 if K == 8192 else x3)
         assert_gemv_close(y, m.words(), m.scales(), x)
