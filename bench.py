@@ -58,6 +58,8 @@ def parse():
                          "launch_each: one kernel per GEMV")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config figures (single GEMV, one MLP, the M=8 sweep)")
     ap.add_argument("--only-step", action="store_true",
                     help="time only the decode step (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -174,11 +176,119 @@ def main():
             other[mode] = {"ms_per_step": round(m_ms, 5),
                            "gbs": round(step_bytes / (m_ms * 1e-3) / 1e9, 1)}
         result["other_modes"] = other
+        if not args.no_configs:
+            result["per_config"] = per_config(torch, q4, synth, np, stream)
         if not args.no_probe:
             result["probe_read_gbs"] = probe_read(torch, q4, stream)
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(np, torch, descs, meta)
     print(json.dumps(result), flush=True)
+
+
+def _timed(torch, stream, fn, calls):
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            fn(0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(calls):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / calls
+
+
+def _fig(nbytes, ms, **kw):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(us=round(ms * 1e3, 2), gbs=round(gbs, 1), pct_of_peak=round(100 * gbs / PEAK_GBS, 2),
+                **kw)
+
+
+def per_config(torch, q4, synth, np, stream):
+    """The other workloads: a single qkv GEMV and one MLP (gate_up then down), each
+    over distinct weight copies totalling > 512 MB so every call streams from HBM,
+    timed as back-to-back calls and as one decode-step list; and the 2B-class
+    sweep at M = 8."""
+    import synth as S
+    out = {}
+
+    def mats(prefix, shapes, copies, M=1):
+        xs = {}
+        descs = []
+        for c in range(copies):
+            for role, N, K in shapes:
+                if K not in xs:
+                    h = S.activations(f"{prefix}/x{K}", 0, M * K)
+                    xs[K] = torch.from_numpy(h.view(np.int16)).cuda().view(torch.float16)
+                m = S.Matrix(f"{prefix}/c{c}/{role}", N, K)
+                sc = torch.from_numpy(m.scales().view(np.int16)).cuda().view(torch.float16)
+                y = torch.empty(M * N, dtype=torch.float16, device="cuda")
+                descs.append((m.words_torch("cuda"), sc, xs[K], y, N, K))
+        return descs
+
+    def gemv_calls(descs):
+        ws = {}
+        for (W, Sc, x, y, N, K) in descs:
+            nb = q4.q4_workspace_bytes(1, N, K)
+            if nb and nb > ws.get("n", 0):
+                ws["n"] = nb
+        wsb = torch.empty(max(ws.get("n", 0), 16), dtype=torch.uint8, device="cuda")
+
+        def fn(i):
+            W, Sc, x, y, N, K = descs[i % len(descs)]
+            q4.q4_gemv(W, Sc, x, y, ws=wsb, stream=stream)
+        return fn
+
+    def step_call(descs, M=1):
+        layers = q4.make_layers([d[:4] for d in descs])
+        nb = q4.q4_decode_step_workspace_bytes(layers, M, 0)
+        wsb = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+
+        def fn(i):
+            q4.q4_decode_step(layers, M, 0, ws=wsb, ws_bytes=nb, stream=stream)
+        return fn
+
+    # single qkv GEMV 3072 -> 9216
+    qkv = [("qkv", 9216, 3072)]
+    d = mats("bench/qkv", qkv, 34)
+    b1 = synth.algorithmic_bytes(1, 9216, 3072)
+    ms_launch = _timed(torch, stream, gemv_calls(d), 4 * len(d))
+    ms_step = _timed(torch, stream, step_call(d), 5) / len(d)
+    out["qkv_3072x9216_m1"] = {"q4_gemv": _fig(b1, ms_launch, copies=len(d)),
+                               "in_decode_step": _fig(b1, ms_step, copies=len(d))}
+    del d
+    # one MLP: gate_up 3072 -> 16384, then down 8192 -> 3072
+    mlp = [("gate_up", 16384, 3072), ("down", 3072, 8192)]
+    d = mats("bench/mlp", mlp, 13)
+    b2 = synth.algorithmic_bytes(1, 16384, 3072) + synth.algorithmic_bytes(1, 3072, 8192)
+    ms_launch = _timed(torch, stream, gemv_calls(d), 4 * len(d)) * 2
+    ms_step = _timed(torch, stream, step_call(d), 5) / (len(d) // 2)
+    out["mlp_gate_up_down_m1"] = {"q4_gemv": _fig(b2, ms_launch, copies=len(d) // 2),
+                                  "in_decode_step": _fig(b2, ms_step, copies=len(d) // 2)}
+    del d
+    # 2B-class sweep at M = 8 (one q4_gemv_batched kernel per GEMV)
+    shapes = synth.sweep_shapes("2b")
+    descs = []
+    xs = {}
+    for label, N, K in shapes:
+        if K not in xs:
+            h = S.activations(f"2b/X{K}", 0, 8 * K)
+            xs[K] = torch.from_numpy(h.view(np.int16)).cuda().view(torch.float16)
+        m = S.Matrix(label, N, K)
+        sc = torch.from_numpy(m.scales().view(np.int16)).cuda().view(torch.float16)
+        descs.append((m.words_torch("cuda"), sc, xs[K], torch.empty(8 * N, dtype=torch.float16,
+                                                                       device="cuda"), N, K))
+    b5 = sum(synth.algorithmic_bytes(8, N, K) for _, N, K in shapes)
+    ms = _timed(torch, stream, step_call(descs, 8), 10)
+    flops = sum(2 * 8 * N * K for _, N, K in shapes)
+    out["twob_sweep_m8"] = _fig(b5, ms, gemvs=len(shapes), steps_per_s=round(1e3 / ms, 1),
+                                tok_per_s=round(8e3 / ms, 1),
+                                tflops=round(flops / (ms * 1e-3) / 1e12, 2))
+    del descs
+    torch.cuda.empty_cache()
+    return out
 
 
 def source_hash():

@@ -11,16 +11,19 @@
 // because weights never depend on activations.
 //
 // One workgroup of 16 waves per compute unit (cooperative launch: all resident):
-//  * waves 1..15 (compute): walk a static list of items -- row-steps of every
-//    GEMV in list order -- with a P-deep ring of 128-bit loads in registers
-//    (item i + P is issued right after item i is consumed).  An item is one row
-//    per team of 2^lpr lanes; each lane holds up to 4 groups (4 x dwordx4), so
-//    rows up to K = 8192.  Results go to an LDS y buffer, so these waves never
-//    wait on a store (on gfx9 stores and loads share one in-order counter).
-//  * wave 0 (sync): stages x of GEMV k into one of two LDS buffers once the
-//    GEMVs it depends on are complete on every workgroup, copies finished y rows
-//    from LDS to memory, and publishes per-GEMV completion with a release atomic
-//    that other workgroups poll.  Its waits never hold back the weight stream.
+//  * 12 compute waves: a workgroup's items -- row-steps of every GEMV, in list
+//    order -- are dealt round-robin to them.  A wave works in bursts of 3 items:
+//    it issues all loads of a burst (per item and lane, 4 x dwordx4 of packed
+//    words and 4 fp16 scales), then consumes them, so the loads of the next
+//    burst overlap this burst's arithmetic on the other waves.  An item is one
+//    row per team of 2^lpr lanes, each lane holding up to 4 groups, so rows up
+//    to K = 8192.  Results go to an LDS y buffer: these waves never wait on a
+//    global store (on gfx9 stores and loads share one in-order counter).
+//  * 4 sync waves, each owning every 4th GEMV: stage x of the GEMV into one of
+//    8 LDS buffers (pair-ordered, with per-group bias terms) once the GEMVs it
+//    depends on are complete on every workgroup, copy finished y rows from LDS
+//    to memory, and publish per-GEMV completion with an agent-scope atomic that
+//    other workgroups poll.  Their waits never hold back the weight stream.
 //
 // Dependencies (decided on the host): descriptor k waits for descriptor dep[k]
 // (and, by list order, everything before it) to complete on all workgroups
