@@ -120,10 +120,14 @@ def main():
         ws_bytes = q4.q4_decode_step_workspace_bytes(layers, 1, flags)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
-        def step():
-            q4.q4_decode_step(layers, 1, flags, ws=ws, ws_bytes=ws_bytes, stream=stream)
+        # the first call clears the workspace's counters; the kernel leaves them
+        # zero, so the following calls skip the clearing kernel
+        def step(first=False):
+            f = flags if first else flags | q4.STEP_WS_CLEAN
+            q4.q4_decode_step(layers, 1, f, ws=ws, ws_bytes=ws_bytes, stream=stream)
 
         with torch.cuda.stream(stream):
+            step(first=True)
             for _ in range(warmup):
                 step()
             torch.cuda.synchronize()
@@ -244,10 +248,10 @@ def per_config(torch, q4, synth, np, stream):
     def step_call(descs, M=1):
         layers = q4.make_layers([d[:4] for d in descs])
         nb = q4.q4_decode_step_workspace_bytes(layers, M, 0)
-        wsb = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        wsb = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")   # counters clean
 
         def fn(i):
-            q4.q4_decode_step(layers, M, 0, ws=wsb, ws_bytes=nb, stream=stream)
+            q4.q4_decode_step(layers, M, q4.STEP_WS_CLEAN, ws=wsb, ws_bytes=nb, stream=stream)
         return fn
 
     # single qkv GEMV 3072 -> 9216

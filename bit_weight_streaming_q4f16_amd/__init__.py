@@ -20,7 +20,7 @@ __all__ = [
     "Q4Error", "load", "lib_path", "q4_version", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemv_splitk", "q4_gemv_batched", "q4_workspace_bytes", "q4_splitk_workspace_bytes",
     "q4_decode_step", "q4_decode_step_workspace_bytes", "q4_probe_read", "q4_probe_copy",
-    "Layer", "STEP_LAUNCH_EACH", "STEP_ORDERED", "STEP_LDS_RING", "make_layers",
+    "Layer", "STEP_LAUNCH_EACH", "STEP_ORDERED", "STEP_LDS_RING", "STEP_WS_CLEAN", "make_layers",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +31,7 @@ _lib = None
 STEP_LAUNCH_EACH = 0x1
 STEP_ORDERED = 0x2
 STEP_LDS_RING = 0x4
+STEP_WS_CLEAN = 0x8
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
           4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED"}

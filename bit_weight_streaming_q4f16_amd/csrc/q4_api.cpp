@@ -319,7 +319,7 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (n_layers > (1 << 20))
     return fail(Q4_ERR_UNSUPPORTED, "q4_decode_step: n_layers = %lld: too many",
                 (long long)n_layers);
-  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED | Q4_STEP_LDS_RING))
+  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED | Q4_STEP_LDS_RING | Q4_STEP_WS_CLEAN))
     return fail(Q4_ERR_SHAPE, "q4_decode_step: unknown flags 0x%x", flags);
   char what[64];
   for (int64_t i = 0; i < n_layers; ++i) {
@@ -358,7 +358,8 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
       const void* table = device_table(p.desc.data(), p.desc.size() * sizeof(q4::StepDesc),
                                        d->id, s, &e);
       if (!table) return device_error(e, "q4_decode_step: descriptor table");
-      e = q4::launch_step(p, static_cast<const q4::StepDesc*>(table), ws, s);
+      e = q4::launch_step(p, static_cast<const q4::StepDesc*>(table), ws,
+                          (flags & Q4_STEP_WS_CLEAN) != 0, s);
       return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
     }
   }

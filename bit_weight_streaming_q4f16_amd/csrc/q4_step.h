@@ -39,7 +39,7 @@ struct StepPlan {
   int grid = 0;          // workgroups (one per compute unit)
   int maxG = 0;
   int ybuf_rows = 0;
-  int counters = 0;      // completion counters + error word in the workspace
+  int counters = 0;      // completion counters, exit counter, spare, error word
   size_t lds_bytes = 0;
   std::vector<StepDesc> desc;
 };
@@ -48,9 +48,11 @@ struct StepPlan {
 // otherwise only for earlier descriptors whose memory it shares.
 StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool ordered);
 size_t step_workspace_bytes(const StepPlan& p);
-// dev_desc: p.desc copied to device memory.  Zeroes the counters in ws, then
-// runs the cooperative kernel.
-hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, hipStream_t s);
+// dev_desc: p.desc copied to device memory.  Zeroes the counters in ws (unless
+// ws_clean: they are already zero, as the kernel leaves them), then runs the
+// cooperative kernel.
+hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, bool ws_clean,
+                       hipStream_t s);
 hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu);
 
 }  // namespace q4

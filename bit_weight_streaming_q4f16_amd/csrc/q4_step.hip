@@ -61,6 +61,41 @@ __device__ __forceinline__ uint4 load_nt_g(const Q4_GLOBAL uint4* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// The fields of a descriptor a compute wave needs, read with scalar loads issued
+// as inline assembly.  Read as ordinary loads, they become vector loads (the
+// compiler cannot prove the table unchanged across the kernel's own stores), and
+// using one would first drain every weight load the wave has in flight
+// (vmcnt(0)) -- at every GEMV boundary, in the middle of a burst.
+struct CursorDesc {
+  const Q4_GLOBAL uint4* W;
+  const Q4_GLOBAL uint16_t* S;
+  int N, G, lg, C, steps;
+};
+typedef uint32_t u32x8_s __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
+  u32x4_g ws;
+  u32x8_s rest;        // N, G, lpr_log2, C, steps, dep, signal, pad
+  asm volatile(
+      "s_load_dwordx4 %0, %2, 0x0\n\t"
+      "s_load_dwordx8 %1, %2, 0x20\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(ws), "=&s"(rest)
+      : "s"(d));
+  static_assert(offsetof(StepDesc, S) == 8 && offsetof(StepDesc, N) == 32 &&
+                    offsetof(StepDesc, G) == 36 && offsetof(StepDesc, lpr_log2) == 40 &&
+                    offsetof(StepDesc, C) == 44 && offsetof(StepDesc, steps) == 48,
+                "descriptor offsets read by the compute waves");
+  CursorDesc r;
+  r.W = (const Q4_GLOBAL uint4*)(((uint64_t)ws[1] << 32) | ws[0]);
+  r.S = (const Q4_GLOBAL uint16_t*)(((uint64_t)ws[3] << 32) | ws[2]);
+  r.N = (int)rest[0];
+  r.G = (int)rest[1];
+  r.lg = (int)rest[2];
+  r.C = (int)rest[3];
+  r.steps = (int)rest[4];
+  return r;
+}
+
 __device__ __forceinline__ uint4 pair_order(uint4 v) {
   uint4 o;
   o.x = (v.x & 0xFFFFu) | (v.z << 16);
@@ -146,6 +181,7 @@ static_assert(kXBufs % kSync == 0, "a GEMV and the one whose x buffer it reuses 
 constexpr unsigned kSpinLimit = 1u << 24;   // bounded waits (about a second)
 constexpr int kCoherent = 1 | 16;           // cache policy sc0 | sc1: device-coherent access
 constexpr int kWaitVm0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt untouched)
+constexpr int kNonTemporal = 2;             // cache policy nt: streamed once
 
 struct Shared {
   int x_ready[kXBufs];   // GEMV index whose x sits in buffer b (-1: none yet)
@@ -225,9 +261,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       while (next_fin <= last && next_fin < n) {
         if (!complete(next_fin)) {
           if (!block) return;
+          // a long sleep: polling issues vector instructions that the
+          // compute waves on this SIMD would otherwise use
           for (unsigned it = 0; !complete(next_fin); ++it) {
-            if (it > kSpinLimit) { err[0] = 1u; break; }
-            __builtin_amdgcn_s_sleep(1);
+            if (it > kSpinLimit / 8) { err[0] = 1u; break; }
+            __builtin_amdgcn_s_sleep(8);
           }
         }
         finish_one(next_fin);
@@ -333,8 +371,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         if (e) err[0] = (unsigned)e;
       }
     }
-    return;
-  }
+  } else {
 
   // -------------------------------------------------------------- compute waves
   const int c = wave - kSync;
@@ -350,28 +387,33 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     const Q4_GLOBAL uint16_t* S;
     int j, s, s_end;             // GEMV, next row-step, end row-step (this workgroup)
     int N, G, lg, C, r0;         // its shape, and its first row in this workgroup
+    int voff, voff_s;            // this lane's byte offsets in an item's words, scales
   } cu;
+  cu.voff = 0;
+  cu.voff_s = 0;
   int base = 0;                  // items of GEMVs before cu.j in this workgroup, mod kCompute
   // enter GEMV j or, if this wave has no item there, the next one that has
   auto enter = [&](int j) {
     for (; j < n; ++j) {
-      const StepDesc& d = D[j];
+      const CursorDesc d = read_desc(D + j);
       const int s0 = wg_step(d.steps, wg, nwg);
       const int s1 = wg_step(d.steps, wg + 1, nwg);
       int off = c - base;
       if (off < 0) off += kCompute;
       base = (base + (s1 - s0)) % kCompute;      // GEMV j's items are dealt either way
       if (s0 + off < s1) {
-        cu.W = gptr(d.W);
-        cu.S = gptr(d.S);
+        cu.W = d.W;
+        cu.S = d.S;
         cu.N = d.N;
         cu.G = d.G;
-        cu.lg = d.lpr_log2;
+        cu.lg = d.lg;
         cu.C = d.C;
         cu.j = j;
         cu.s = s0 + off;
         cu.s_end = s1;
-        cu.r0 = s0 * (64 >> d.lpr_log2);
+        cu.r0 = s0 * (64 >> d.lg);
+        cu.voff_s = ((lane >> d.lg) * d.G + (lane & ((1 << d.lg) - 1))) * 2;
+        cu.voff = cu.voff_s * 8;
         return;
       }
     }
@@ -401,11 +443,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   // Bursts of B items: all loads of a burst are issued before any is consumed,
   // so no loaded value crosses the loop's back edge (the compiler then waits
   // exactly for the item being consumed).  Every issue is exactly eight loads
-  // (four dwordx4 + four ushort), also past the end of the list (then it
-  // re-reads the last GEMV's first row and the item is marked empty).
-  const StepDesc& last = D[n - 1];
-  const Q4_GLOBAL uint4* const W_last = gptr(last.W);
-  const Q4_GLOBAL uint16_t* const S_last = gptr(last.S);
+  // (four dwordx4 + four ushort).  They are buffer loads: the item's first row is
+  // the base of a buffer resource (scalar arithmetic) bounded by the end of the
+  // matrix, so rows past it read as zero without touching memory; a lane's offset
+  // within an item is fixed per GEMV and a slot's offset is a scalar, so issuing
+  // costs no vector arithmetic.  Slots past a lane's groups re-read its first
+  // group; items past the end of the list use an empty resource.
+  const Q4_GLOBAL uint4* const W_last = read_desc(D + (n - 1)).W;
   while (true) {
     uint4 rw[B][4];
     uint16_t rs[B][4];
@@ -415,28 +459,53 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const bool live = cu.j < n;
       const int lg = live ? cu.lg : 2, lpr = 1 << lg;
       const int G = live ? cu.G : 1;
-      const int li = lane & (lpr - 1);
+      const int C = live ? cu.C : 1;
       const int row0 = live ? cu.s * (64 >> lg) : 0;
-      int row = row0 + (lane >> lg);
-      if (live && row > cu.N - 1) row = cu.N - 1;
-      if (!live) row = 0;
-      const Q4_GLOBAL uint4* wr = (live ? cu.W : W_last) + (int64_t)row * G;
-      const Q4_GLOBAL uint16_t* sr = (live ? cu.S : S_last) + (int64_t)row * G;
-      // slots past the row's groups re-read a group already being fetched
+      const uint64_t left = live ? (uint64_t)(cu.N - row0) * (uint64_t)G : 0;   // groups
+      const uint32_t nw = left * 16 < 0xFFFFFFF0ull ? (uint32_t)(left * 16) : 0xFFFFFFF0u;
+      const uint32_t ns = left * 2 < 0xFFFFFFF0ull ? (uint32_t)(left * 2) : 0xFFFFFFF0u;
+      const __amdgpu_buffer_rsrc_t bw = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint4*>(live ? (const uint4*)(cu.W + (int64_t)row0 * G) : (const uint4*)W_last),
+          0, (int)nw, 0x00020000);
+      const __amdgpu_buffer_rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(live ? (const uint16_t*)(cu.S + (int64_t)row0 * G)
+                                     : (const uint16_t*)W_last),
+          0, (int)ns, 0x00020000);
+      const int voff = cu.voff, voff_s = cu.voff_s;   // any offset reads zero when empty
+      if (live && C * lpr > G) {
+        // Padded rows (G not a multiple of the team): a slot past the row's
+        // groups re-reads the lane's first group.  The slot offset goes into the
+        // per-lane offset here, because only that part is range-checked: a
+        // scalar offset could carry the matrix's last row past its end.
+        const int li = lane & (lpr - 1);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        int g = li + lpr * t;
-        g = g < G ? g : li;
-        if (!live) g = 0;
-        rw[p][t] = load_nt_g(wr + g);
-        rs[p][t] = sr[g];
+        for (int t = 0; t < 4; ++t) {
+          const bool in = t < C && li + lpr * t < G;
+          const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(
+              bw, in ? voff + t * lpr * 16 : voff, 0, kNonTemporal);
+          rw[p][t] = make_uint4(v[0], v[1], v[2], v[3]);
+          rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, in ? voff_s + t * lpr * 2 : voff_s,
+                                                          0, 0);
+        }
+      } else {
+        // Unpadded: slot t of a row lies inside the row, so a lane in range keeps
+        // its slots in range, and a lane past the end (or any lane of an empty
+        // resource) reads zeros whatever the scalar offset.
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // uniform, and kept scalar so that it is the loads' soffset operand
+          const int so = __builtin_amdgcn_readfirstlane((t < C ? t : 0) * lpr);
+          const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, voff, so * 16, kNonTemporal);
+          rw[p][t] = make_uint4(v[0], v[1], v[2], v[3]);
+          rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, voff_s, so * 2, 0);
+        }
       }
       rj[p] = live ? cu.j : -1;
       rrow[p] = row0;
       rN[p] = cu.N;
       rG[p] = G;
       rlg[p] = lg;
-      rC[p] = cu.C;
+      rC[p] = C;
       rr0[p] = cu.r0;
       if (live) {
         cu.s += kCompute;
@@ -455,6 +524,14 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const int xi = j % kXBufs;
       const uint4* xb = xbuf + xi * 4 * maxG + li;
       const float* cb = cbuf + xi * maxG + li;
+      if (rC[0] * lpr > rG[0]) {      // padded rows: slots past G hold other data
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bool ok = li + lpr * t < rG[0];
+#pragma unroll
+          for (int p = 0; p < B; ++p) rs[p][t] = ok ? rs[p][t] : (uint16_t)0;
+        }
+      }
       float acc[B];
 #pragma unroll
       for (int p = 0; p < B; ++p) acc[p] = 0.f;
@@ -493,6 +570,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const int xi = j % kXBufs;
       const uint4* xb = xbuf + xi * 4 * maxG + li;
       const float* cb = cbuf + xi * maxG + li;
+      if (rC[p] * lpr > rG[p]) {      // padded rows: slots past G hold other data
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rs[p][t] = li + lpr * t < rG[p] ? rs[p][t] : (uint16_t)0;
+      }
       float acc = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -509,8 +590,23 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         ybuf[xi * ybuf_rows + (row - rr0[p])] = bits<uint16_t>((_Float16)acc);
     }
   }
-drained:
-  signal_upto(n);
+  drained:
+    signal_upto(n);
+  }
+
+  // Leave the counters zeroed for the next call: the last workgroup to get here
+  // (every other one has finished with them) clears them.
+  __syncthreads();
+  if (wave == 0) {
+    unsigned old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(done + n, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == (unsigned)nwg - 1u) {
+      for (int i = lane; i <= n; i += 64)
+        __hip_atomic_store(done + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 __global__ void k_zero(unsigned* __restrict__ p, int count) {
@@ -590,11 +686,14 @@ size_t step_workspace_bytes(const StepPlan& p) {
   return ((size_t)p.counters * sizeof(unsigned) + 255) & ~(size_t)255;
 }
 
-hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, hipStream_t s) {
+hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, bool ws_clean,
+                       hipStream_t s) {
   unsigned* done = static_cast<unsigned*>(ws);
   unsigned* err = done + (p.counters - 1);
-  hipLaunchKernelGGL(k_zero, dim3(1), dim3(256), 0, s, done, p.counters);
-  if (hipError_t e = hipGetLastError()) return e;
+  if (!ws_clean) {
+    hipLaunchKernelGGL(k_zero, dim3(1), dim3(256), 0, s, done, p.counters);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
   auto kern = k_step<kBurst>;
   if (p.lds_bytes > 65536) {
     if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -8,10 +8,9 @@
 namespace q4 {
 
 constexpr int kLoaders = 4;                  // loader waves (one per SIMD)
-constexpr int kSlots = 8;                    // LDS ring slots, kSlots / kLoaders per loader
-constexpr int kSlotWordBytes = 12288;        // words of one tile (at most): 8 rows of K = 3072
-                                             // or 3 rows of K = 8192 fill it exactly
-constexpr int kSlotScaleBytes = 2048;        // room for its scales (copies write 1 KB each)
+constexpr int kSlots = 12;                   // LDS ring slots, kSlots / kLoaders per loader
+constexpr int kSlotWordBytes = 8192;         // words of one tile (at most)
+constexpr int kSlotScaleBytes = 1024;        // room for its scales (one 1 KB copy)
 constexpr int kSlotBytes = kSlotWordBytes + kSlotScaleBytes;
 constexpr int kDmaXBufs = 2;                 // x buffers
 

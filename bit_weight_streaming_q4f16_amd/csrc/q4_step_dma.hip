@@ -104,21 +104,97 @@ __device__ __forceinline__ void lds_store(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// One 16-byte-per-lane copy global -> LDS at `lds_byte` + 16 * lane.  Issued as
-// inline assembly so that the compiler does not treat every later LDS read as
-// possibly aliasing it (it would wait for all copies before each one); the
-// loader tracks completion itself with the in-order vector-memory counter.  m0
-// (which holds the LDS address) is saved and restored around the copy.
-__device__ __forceinline__ void dma16(const Q4_GLOBAL void* g, uint32_t lds_byte) {
-  uint32_t saved;
+// The loaders move tiles with plain 16-byte-per-lane loads into registers (the
+// same access as a streaming read) and 16-byte LDS writes, two register tiles
+// alternating.  One step is a single inline-assembly block: issue the nine loads
+// of the next tile into one register set, wait until only those nine are
+// outstanding (the vector-memory counter drains in order, so the previous tile
+// has landed), write the previous tile from the other set to its LDS slot, and
+// wait for the writes.  The compiler sees both sets as read and written by every
+// step, so it never copies or reuses them while loads are in flight, and it
+// inserts no waits of its own (it would drain every load before each write).
+// Loader waves issue no other vector-memory instruction.
+typedef const Q4_GLOBAL uint8_t* gaddr_t;
+constexpr int kTileLoads = 9;                     // 8 x 1 KB of words + 1 KB of scales
+
+#define Q4_TILE_LOADS(R, A)                                      \
+  "global_load_dwordx4 %[" #R "0], %[" #A "0], off nt\n\t"       \
+  "global_load_dwordx4 %[" #R "1], %[" #A "1], off nt\n\t"       \
+  "global_load_dwordx4 %[" #R "2], %[" #A "2], off nt\n\t"       \
+  "global_load_dwordx4 %[" #R "3], %[" #A "3], off nt\n\t"       \
+  "global_load_dwordx4 %[" #R "4], %[" #A "4], off nt\n\t"       \
+  "global_load_dwordx4 %[" #R "5], %[" #A "5], off nt\n\t"       \
+  "global_load_dwordx4 %[" #R "6], %[" #A "6], off nt\n\t"       \
+  "global_load_dwordx4 %[" #R "7], %[" #A "7], off nt\n\t"       \
+  "global_load_dwordx4 %[" #R "8], %[" #A "8], off nt\n\t"
+#define Q4_TILE_WRITES(R)                                        \
+  "ds_write_b128 %[l], %[" #R "0]\n\t"                           \
+  "ds_write_b128 %[l], %[" #R "1] offset:1024\n\t"               \
+  "ds_write_b128 %[l], %[" #R "2] offset:2048\n\t"               \
+  "ds_write_b128 %[l], %[" #R "3] offset:3072\n\t"               \
+  "ds_write_b128 %[l], %[" #R "4] offset:4096\n\t"               \
+  "ds_write_b128 %[l], %[" #R "5] offset:5120\n\t"               \
+  "ds_write_b128 %[l], %[" #R "6] offset:6144\n\t"               \
+  "ds_write_b128 %[l], %[" #R "7] offset:7168\n\t"               \
+  "ds_write_b128 %[l], %[" #R "8] offset:8192\n\t"
+#define Q4_REGS(N, R)                                                                   \
+  [N##0] "+v"(R[0]), [N##1] "+v"(R[1]), [N##2] "+v"(R[2]), [N##3] "+v"(R[3]),           \
+      [N##4] "+v"(R[4]), [N##5] "+v"(R[5]), [N##6] "+v"(R[6]), [N##7] "+v"(R[7]),       \
+      [N##8] "+v"(R[8])
+#define Q4_ADDRS(A)                                                                     \
+  [a0] "v"(A[0]), [a1] "v"(A[1]), [a2] "v"(A[2]), [a3] "v"(A[3]), [a4] "v"(A[4]),       \
+      [a5] "v"(A[5]), [a6] "v"(A[6]), [a7] "v"(A[7]), [a8] "v"(A[8])
+
+// issue the loads of a tile into nx
+__device__ __forceinline__ void tile_issue(u32x4_g (&nx)[kTileLoads], u32x4_g (&other)[kTileLoads],
+                                           const gaddr_t (&a)[kTileLoads]) {
+  asm volatile(Q4_TILE_LOADS(n, a) "" : Q4_REGS(n, nx), Q4_REGS(c, other) : Q4_ADDRS(a) : "memory");
+}
+// issue the loads of the next tile into nx, then write cur (loaded before) to LDS
+__device__ __forceinline__ void tile_step(u32x4_g (&nx)[kTileLoads], u32x4_g (&cur)[kTileLoads],
+                                          const gaddr_t (&a)[kTileLoads], uint32_t lds) {
+  asm volatile(Q4_TILE_LOADS(n, a) "s_waitcnt vmcnt(9)\n\t" Q4_TILE_WRITES(c) "s_waitcnt lgkmcnt(0)"
+               : Q4_REGS(n, nx), Q4_REGS(c, cur)
+               : Q4_ADDRS(a), [l] "v"(lds)
+               : "memory");
+}
+// wait for every load (the last, never written tile)
+__device__ __forceinline__ void tile_drain(u32x4_g (&x)[kTileLoads], u32x4_g (&y)[kTileLoads]) {
+  asm volatile("s_waitcnt vmcnt(0)" : Q4_REGS(n, x), Q4_REGS(c, y) : : "memory");
+}
+
+// What a loader needs of a descriptor, read with scalar loads issued as inline
+// assembly: ordinary loads after the assembly above may not be proven unchanged,
+// so the compiler would make them vector loads and drain the whole tile stream
+// (vmcnt(0)) before using them.
+struct LoaderDesc {
+  const Q4_GLOBAL uint8_t* W;
+  const Q4_GLOBAL uint8_t* S;
+  int N, G, tr, tiles;
+};
+typedef uint32_t u32x2_s __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ LoaderDesc read_desc(const DmaDesc* d) {
+  u32x4_g ws;
+  u32x2_s ng, tt;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_byte), "v"(g)
-      : "memory");
+      "s_load_dwordx4 %0, %3, 0x0\n\t"
+      "s_load_dwordx2 %1, %3, 0x20\n\t"
+      "s_load_dwordx2 %2, %3, 0x30\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(ws), "=&s"(ng), "=&s"(tt)
+      : "s"(d));
+  static_assert(offsetof(DmaDesc, S) == 8 && offsetof(DmaDesc, N) == 32 &&
+                    offsetof(DmaDesc, G) == 36 && offsetof(DmaDesc, tr) == 48 &&
+                    offsetof(DmaDesc, tiles) == 52,
+                "descriptor offsets read by the loaders");
+  LoaderDesc r;
+  r.W = (const Q4_GLOBAL uint8_t*)(((uint64_t)ws[1] << 32) | ws[0]);
+  r.S = (const Q4_GLOBAL uint8_t*)(((uint64_t)ws[3] << 32) | ws[2]);
+  r.N = (int)ng[0];
+  r.G = (int)ng[1];
+  r.tr = (int)tt[0];
+  r.tiles = (int)tt[1];
+  return r;
 }
 
 constexpr int kWaves = kStepThreads / 64;        // 16
@@ -126,16 +202,16 @@ constexpr int kSync = 2;                         // sync waves
 constexpr int kLoader0 = kSync;                  // first loader wave
 constexpr int kCompute = kWaves - kSync - kLoaders;   // compute waves
 constexpr int kPerLoader = kSlots / kLoaders;    // slots (and tiles in flight) per loader
-constexpr int kWordDmas = kSlotWordBytes / 1024;
-constexpr int kScaleDmas = (kSlotWordBytes / 8 + 1023) / 1024;
-constexpr int kDmaPerTile = kWordDmas + kScaleDmas;
+constexpr int kWordLoads = kSlotWordBytes / 1024;      // per lane and tile
+constexpr int kScaleLoads = (kSlotWordBytes / 8 + 1023) / 1024;
 constexpr unsigned kSpinLimit = 1u << 24;
 constexpr int kCoherent = 1 | 16;                // sc0 | sc1
 constexpr int kWaitVm0 = 0x0F70;                 // s_waitcnt vmcnt(0)
 static_assert(kDmaXBufs % kSync == 0, "x-buffer owner");
 static_assert(kSlots % kLoaders == 0 && kPerLoader >= 1, "slots per loader");
-static_assert(kPerLoader <= 4 && kDmaPerTile * (kPerLoader - 1) <= 63, "vmcnt range");
-static_assert(kScaleDmas * 1024 <= kSlotScaleBytes, "scale copies fit the slot");
+static_assert(kWordLoads == 8 && kScaleLoads == 1 && kWordLoads + kScaleLoads == kTileLoads,
+              "the loader's register tiles");
+static_assert(kScaleLoads * 1024 <= kSlotScaleBytes, "scale copies fit the slot");
 static_assert(kCompute >= 4, "compute waves");
 
 struct Shared {
@@ -185,79 +261,96 @@ __global__ __launch_bounds__(kStepThreads) void k_step_dma(const DmaDesc* __rest
 
   if (wave >= kLoader0 && wave < kLoader0 + kLoaders) {
     // ---------------------------------------------------------------- loaders
-    // Loader l copies tiles l, l + kLoaders, ... of this workgroup's tile list
+    // Loader l moves tiles l, l + kLoaders, ... of this workgroup's tile list
     // (GEMVs in list order, each GEMV's tiles split evenly over workgroups) into
-    // slots l, l + kLoaders, ...  Its tiles [landed, issued) are in flight; it
-    // issues while one of its slots is free, else waits for its oldest tile (the
-    // vector-memory counter drains in order) and marks that one full.
+    // slots l, l + kLoaders, ...  Two register tiles alternate: the loads of the
+    // next tile are issued before the current one is waited for and written to
+    // its slot, so the stream does not stop while a slot is still being read.
     const int l = wave - kLoader0;
     const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
     int total = 0;
     for (int i = 0; i < n; ++i) total += split(D[i].tiles, wg + 1, nwg) - split(D[i].tiles, wg, nwg);
     const int mine = total > l ? (total - l + kLoaders - 1) / kLoaders : 0;
-    int j = 0, tt = split(D[0].tiles, wg, nwg), tend = split(D[0].tiles, wg + 1, nwg);
+    int j = 0;
+    LoaderDesc cd = read_desc(D);
+    int tt = split(cd.tiles, wg, nwg), tend = split(cd.tiles, wg + 1, nwg);
     auto advance = [&](int by) {                 // move the cursor `by` tiles on
       tt += by;
       while (tt >= tend && j + 1 < n) {
         const int over = tt - tend;
         ++j;
-        tt = split(D[j].tiles, wg, nwg) + over;
-        tend = split(D[j].tiles, wg + 1, nwg);
+        cd = read_desc(D + j);
+        tt = split(cd.tiles, wg, nwg) + over;
+        tend = split(cd.tiles, wg + 1, nwg);
       }
     };
     advance(l);
-    auto wait_oldest = [&](int outstanding) {   // let `outstanding` tiles stay in flight
-      switch (outstanding) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(1 * kDmaPerTile) : "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerTile) : "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kDmaPerTile) : "memory"); break;
-      }
+    struct Meta {                                // the tile a register set holds
+      int j, row0, rows;
     };
-    int issued = 0, landed = 0;                  // counts of this loader's tiles
-    for (unsigned it = 0; landed < mine; ++it) {
-      if (it > kSpinLimit * 4u) { lds_store(&sh.err, 4); break; }
-      const int t = l + issued * kLoaders;       // workgroup-local tile index
+    // the cursor's tile: its metadata and the nine per-lane addresses
+    auto address = [&](Meta& m, gaddr_t (&a)[kTileLoads]) {
+      const int wrow = cd.G * 16, srow = cd.G * 2;     // bytes per row: words, scales
+      m.j = j;
+      m.row0 = tt * cd.tr;
+      m.rows = cd.N - m.row0 < cd.tr ? cd.N - m.row0 : cd.tr;
+      const int wbytes = m.rows * wrow, sbytes = m.rows * srow;   // multiples of 16
+      const gaddr_t wt = cd.W + (int64_t)m.row0 * wrow;
+#pragma unroll
+      for (int c = 0; c < kWordLoads; ++c) {
+        int off = c * 1024 + lane * 16;
+        if (off >= wbytes) off = wbytes - 16;       // past the tile: re-read its last chunk
+        a[c] = wt + off;
+      }
+      int off = lane * 16;
+      if (off >= sbytes) off = sbytes - 16;
+      a[kWordLoads] = cd.S + (int64_t)m.row0 * srow + off;
+    };
+    auto claim = [&](const Meta& m, int i) {      // wait for tile i's slot; its header
+      const int t = l + i * kLoaders;
       const int slot = t % kSlots;
-      const bool room = issued < mine && issued - landed < kPerLoader &&
-                        (t < kSlots || lds_load(&sh.slot_free[slot]) >= t - kSlots);
-      if (room) {
-        const DmaDesc& d = D[j];
-        const int wrow = d.G * 16, srow = d.G * 2;     // bytes per row: words, scales
-        const int row0 = tt * d.tr;
-        const int rows = d.N - row0 < d.tr ? d.N - row0 : d.tr;
-        if (lane == 0) {
-          sh.slot_j[slot] = j;
-          sh.slot_row0[slot] = row0;
-          sh.slot_rows[slot] = rows;
+      if (t >= kSlots) {
+        for (unsigned it = 0; lds_load(&sh.slot_free[slot]) < t - kSlots; ++it) {
+          if (it > kSpinLimit) { lds_store(&sh.err, 4); break; }
+          __builtin_amdgcn_s_sleep(1);
         }
-        const int wbytes = rows * wrow, sbytes = rows * srow;   // multiples of 16
-        const uint32_t sl = ring_lds + (uint32_t)slot * kSlotBytes;
-        const Q4_GLOBAL uint8_t* wt = (const Q4_GLOBAL uint8_t*)d.W + (int64_t)row0 * wrow;
-        const Q4_GLOBAL uint8_t* st = (const Q4_GLOBAL uint8_t*)d.S + (int64_t)row0 * srow;
-#pragma unroll
-        for (int c = 0; c < kWordDmas; ++c) {
-          int off = c * 1024 + lane * 16;
-          if (off >= wbytes) off = wbytes - 16;     // past the tile: re-read its last chunk
-          dma16(wt + off, sl + c * 1024);
-        }
-#pragma unroll
-        for (int c = 0; c < kScaleDmas; ++c) {
-          int off = c * 1024 + lane * 16;
-          if (off >= sbytes) off = sbytes - 16;
-          dma16(st + off, sl + kSlotWordBytes + c * 1024);
-        }
-        ++issued;
-        if (issued < mine) advance(kLoaders);
-        continue;
       }
-      if (issued > landed) {
-        wait_oldest(issued - landed - 1);
-        if (lane == 0) lds_store(&sh.slot_tile[(l + landed * kLoaders) % kSlots], l + landed * kLoaders);
-        ++landed;
-        continue;
+      if (lane == 0) {
+        sh.slot_j[slot] = m.j;
+        sh.slot_row0[slot] = m.row0;
+        sh.slot_rows[slot] = m.rows;
       }
-      __builtin_amdgcn_s_sleep(1);               // every slot is still being read
+      return ring_lds + (uint32_t)slot * kSlotBytes + lane * 16;
+    };
+    auto publish = [&](int i) {
+      const int t = l + i * kLoaders;
+      if (lane == 0) lds_store(&sh.slot_tile[t % kSlots], t);
+    };
+    // Every step issues one tile's loads (after the last tile the cursor stays
+    // put and its tile is read again, never written), so the in-flight count at
+    // each wait is exactly one tile.
+    if (mine > 0) {
+      u32x4_g A[kTileLoads], B[kTileLoads];
+      gaddr_t adr[kTileLoads];
+      Meta mA, mB;
+      int issued = 0;
+      auto next = [&](Meta& m) {
+        address(m, adr);
+        if (++issued < mine) advance(kLoaders);
+      };
+      next(mA);
+      tile_issue(A, B, adr);
+      for (int i = 0;;) {
+        next(mB);
+        tile_step(B, A, adr, claim(mA, i));
+        publish(i);
+        if (++i == mine) break;
+        next(mA);
+        tile_step(A, B, adr, claim(mB, i));
+        publish(i);
+        if (++i == mine) break;
+      }
+      tile_drain(A, B);
     }
     return;
   }

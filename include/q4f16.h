@@ -143,6 +143,14 @@ typedef struct q4_layer {
  * other lists ignore the flag.  Same results; slower on the lists measured so far,
  * kept for comparison. */
 #define Q4_STEP_LDS_RING 0x4u
+/* The workspace's counters are already zero: the workspace is fresh from a
+ * zeroing allocation or was last used by a q4_decode_step call with the same
+ * layer list and M (the persistent register-streaming kernel leaves them zero
+ * when it finishes).  Skips the small kernel that clears them before every
+ * call.  Passing it for a workspace that holds anything else can let a GEMV read
+ * its input before the GEMV producing it has finished (wrong results) or make
+ * the kernel's bounded waits run out.  The other paths ignore the flag. */
+#define Q4_STEP_WS_CLEAN 0x8u
 
 /* q4_decode_step: run the GEMVs of layers[0 .. n_layers) in list order, as the
  * Zero TVM decode loop walks the projections of every layer and then the LM

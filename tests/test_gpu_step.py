@@ -141,3 +141,40 @@ def test_modes_agree_on_the_phi3_layer():
     for (m, W, S), y, (N, K) in zip(mats, outs["ordered"], shapes):
         x = host_half(x8 if K == 8192 else x3)
         assert_gemv_close(y, m.words(), m.scales(), x)
+
+
+@pytest.mark.parametrize("flags", [0, q4.STEP_ORDERED], ids=["hazards", "ordered"])
+def test_workspace_left_clean_and_ws_clean_calls(flags):
+    """The persistent kernel leaves its counters zero, so later calls with the same
+    list may skip clearing them (STEP_WS_CLEAN); results stay bitwise the same."""
+    dims = [3072, 8192, 3072, 6144, 2048, 512, 1024, 256, 3072]
+    x = dev_half(synth.activations("wsclean/x", 0, dims[0]))
+    descs = []
+    for i in range(len(dims) - 1):
+        m, W, S = mat(f"wsclean/{i}", dims[i + 1], dims[i], chain=True)
+        y = torch.empty(dims[i + 1], dtype=torch.float16, device="cuda")
+        descs.append((W, S, x, y))
+        x = y
+    layers = q4.make_layers(descs)
+    n = len(descs)
+    need = q4.q4_decode_step_workspace_bytes(layers, 1, flags)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")   # garbage
+    q4.q4_decode_step(layers, 1, flags, ws=ws)                         # clears, runs
+    torch.cuda.synchronize()
+    ref = [host_half(d[3]) for d in descs]
+    counters = ws[: 4 * (n + 1)].view(torch.int32).cpu().numpy()
+    assert not counters.any()
+    for _ in range(4):
+        for d in descs:
+            d[3].fill_(float("nan"))
+        q4.q4_decode_step(layers, 1, flags | q4.STEP_WS_CLEAN, ws=ws)
+        torch.cuda.synchronize()
+        for r, d in zip(ref, descs):
+            assert np.array_equal(r, host_half(d[3]))
+        assert not ws[: 4 * (n + 1)].view(torch.int32).cpu().numpy().any()
+    # a zero-filled new workspace is clean too
+    ws2 = torch.zeros_like(ws)
+    q4.q4_decode_step(layers, 1, flags | q4.STEP_WS_CLEAN, ws=ws2)
+    torch.cuda.synchronize()
+    for r, d in zip(ref, descs):
+        assert np.array_equal(r, host_half(d[3]))
