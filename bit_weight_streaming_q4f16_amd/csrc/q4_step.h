@@ -17,12 +17,13 @@ struct StepDesc {
   const uint4* X;        // x as blocks of 8 halves: [4G]
   uint16_t* Y;           // y [N]
   int N, G;              // rows, groups per row (K / 32)
-  int lpr_log2;          // lanes per row = 2^lpr_log2 (4..64)
-  int C;                 // groups per lane (<= 4)
+  int16_t lpr_log2;      // lanes per row = 2^lpr_log2 (4..64)
+  int16_t C;             // groups per lane (<= 4)
   int steps;             // row-steps: ceil(N / (64 / lanes per row))
   int dep;               // descriptor that must be complete before x is read (-1: none)
   int signal;            // 1 if a later descriptor waits for this one
-  int pad;
+  int sbase, srem;       // workgroup w owns row-steps from w * sbase + min(w, srem):
+                         // steps split evenly over the grid, the first srem get one more
 };
 static_assert(sizeof(StepDesc) == 64, "StepDesc layout");
 

@@ -69,12 +69,12 @@ __device__ __forceinline__ uint4 load_nt_g(const Q4_GLOBAL uint4* p) {
 struct CursorDesc {
   const Q4_GLOBAL uint4* W;
   const Q4_GLOBAL uint16_t* S;
-  int N, G, lg, C, steps;
+  int N, G, lg, C, sbase, srem;
 };
 typedef uint32_t u32x8_s __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
   u32x4_g ws;
-  u32x8_s rest;        // N, G, lpr_log2, C, steps, dep, signal, pad
+  u32x8_s rest;        // N, G, lpr_log2 | C << 16, steps, dep, signal, sbase, srem
   asm volatile(
       "s_load_dwordx4 %0, %2, 0x0\n\t"
       "s_load_dwordx8 %1, %2, 0x20\n\t"
@@ -83,16 +83,18 @@ __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
       : "s"(d));
   static_assert(offsetof(StepDesc, S) == 8 && offsetof(StepDesc, N) == 32 &&
                     offsetof(StepDesc, G) == 36 && offsetof(StepDesc, lpr_log2) == 40 &&
-                    offsetof(StepDesc, C) == 44 && offsetof(StepDesc, steps) == 48,
+                    offsetof(StepDesc, C) == 42 && offsetof(StepDesc, sbase) == 56 &&
+                    offsetof(StepDesc, srem) == 60,
                 "descriptor offsets read by the compute waves");
   CursorDesc r;
   r.W = (const Q4_GLOBAL uint4*)(((uint64_t)ws[1] << 32) | ws[0]);
   r.S = (const Q4_GLOBAL uint16_t*)(((uint64_t)ws[3] << 32) | ws[2]);
   r.N = (int)rest[0];
   r.G = (int)rest[1];
-  r.lg = (int)rest[2];
-  r.C = (int)rest[3];
-  r.steps = (int)rest[4];
+  r.lg = (int)(rest[2] & 0xFFFFu);
+  r.C = (int)(rest[2] >> 16);
+  r.sbase = (int)rest[6];
+  r.srem = (int)rest[7];
   return r;
 }
 
@@ -130,9 +132,21 @@ __device__ __forceinline__ Nibbles make_nibbles() {
 __device__ __forceinline__ float group_dot(uint4 w, const uint4 (&x)[4], float neg_bias,
                                           const Nibbles& nb) {
   const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
-  float a = neg_bias, b = 0.f;
+  // the first product of each chain in the three-operand form: the compiler
+  // would otherwise copy the start value into the accumulator of v_dot2c
+  float a, b;
+  {
+    const uint32_t v = wj[0];
+    asm("v_dot2_f32_f16 %0, %1, %2, %3"
+        : "=v"(a)
+        : "v"((v & nb.m_lo) | nb.e_lo), "v"(x[0].x), "v"(neg_bias));
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(b) : "v"((v & nb.m_hi) | nb.e_hi), "v"(x[0].y));
+    const uint32_t v8 = v >> 8;
+    a = __builtin_amdgcn_fdot2(bits<h2_t>((v8 & nb.m_lo) | nb.e_lo), bits<h2_t>(x[0].z), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>((v8 & nb.m_hi) | nb.e_hi), bits<h2_t>(x[0].w), b, false);
+  }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 1; j < 4; ++j) {
     const uint32_t v = wj[j], v8 = v >> 8;
     a = __builtin_amdgcn_fdot2(bits<h2_t>((v & nb.m_lo) | nb.e_lo), bits<h2_t>(x[j].x), a, false);
     b = __builtin_amdgcn_fdot2(bits<h2_t>((v & nb.m_hi) | nb.e_hi), bits<h2_t>(x[j].y), b, false);
@@ -189,10 +203,10 @@ struct Shared {
   int err;               // a compute wave's wait ran out (copied out by the sync wave)
 };
 
-// First row-step of workgroup wg for a GEMV with `steps` row-steps
-// (steps * wg < 2^31 for every supported shape: steps <= N < 2^24, wg < 128).
-__device__ __forceinline__ int wg_step(int steps, int wg, int nwg) {
-  return (int)(((unsigned)steps * (unsigned)wg) / (unsigned)nwg);
+// First row-step of workgroup wg (the even split of the descriptor's row-steps
+// computed on the host; wg == grid size gives the end).
+__device__ __forceinline__ int wg_step(int sbase, int srem, int wg) {
+  return wg * sbase + (wg < srem ? wg : srem);
 }
 
 // LDS layout, per x buffer b (kXBufs of them):
@@ -236,8 +250,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const StepDesc& d = D[i];
       const int b = i % kXBufs;
       const int rps = 64 >> d.lpr_log2;
-      const int r0 = wg_step(d.steps, wg, nwg) * rps;
-      int r1 = wg_step(d.steps, wg + 1, nwg) * rps;
+      const int r0 = wg_step(d.sbase, d.srem, wg) * rps;
+      int r1 = wg_step(d.sbase, d.srem, wg + 1) * rps;
       if (r1 > d.N) r1 = d.N;
       const uint16_t* yb = ybuf + b * ybuf_rows;
       if (!d.signal) {
@@ -387,17 +401,17 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     const Q4_GLOBAL uint16_t* S;
     int j, s, s_end;             // GEMV, next row-step, end row-step (this workgroup)
     int N, G, lg, C, r0;         // its shape, and its first row in this workgroup
-    int voff, voff_s;            // this lane's byte offsets in an item's words, scales
+    int vo[4];                   // this lane's byte offset of each slot in an item's words
   } cu;
-  cu.voff = 0;
-  cu.voff_s = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) cu.vo[t] = 0;
   int base = 0;                  // items of GEMVs before cu.j in this workgroup, mod kCompute
   // enter GEMV j or, if this wave has no item there, the next one that has
   auto enter = [&](int j) {
     for (; j < n; ++j) {
       const CursorDesc d = read_desc(D + j);
-      const int s0 = wg_step(d.steps, wg, nwg);
-      const int s1 = wg_step(d.steps, wg + 1, nwg);
+      const int s0 = wg_step(d.sbase, d.srem, wg);
+      const int s1 = wg_step(d.sbase, d.srem, wg + 1);
       int off = c - base;
       if (off < 0) off += kCompute;
       base = (base + (s1 - s0)) % kCompute;      // GEMV j's items are dealt either way
@@ -412,8 +426,14 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         cu.s = s0 + off;
         cu.s_end = s1;
         cu.r0 = s0 * (64 >> d.lg);
-        cu.voff_s = ((lane >> d.lg) * d.G + (lane & ((1 << d.lg) - 1))) * 2;
-        cu.voff = cu.voff_s * 8;
+        {
+          const int li = lane & ((1 << d.lg) - 1), g0 = (lane >> d.lg) * d.G + li;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const bool in = t < d.C && li + (t << d.lg) < d.G;
+            cu.vo[t] = (in ? g0 + (t << d.lg) : g0) * 16;
+          }
+        }
         return;
       }
     }
@@ -450,10 +470,14 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   // costs no vector arithmetic.  Slots past a lane's groups re-read its first
   // group; items past the end of the list use an empty resource.
   const Q4_GLOBAL uint4* const W_last = read_desc(D + (n - 1)).W;
-  while (true) {
+  // One burst of B items: the loads of every item (as loaded registers) and what
+  // consuming them needs.
+  struct Burst {
     uint4 rw[B][4];
     uint16_t rs[B][4];
     int rj[B], rrow[B], rN[B], rG[B], rlg[B], rC[B], rr0[B];
+  };
+  auto issue = [&](Burst& U) {
 #pragma unroll
     for (int p = 0; p < B; ++p) {
       const bool live = cu.j < n;
@@ -471,65 +495,50 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           const_cast<uint16_t*>(live ? (const uint16_t*)(cu.S + (int64_t)row0 * G)
                                      : (const uint16_t*)W_last),
           0, (int)ns, 0x00020000);
-      const int voff = cu.voff, voff_s = cu.voff_s;   // any offset reads zero when empty
-      if (live && C * lpr > G) {
-        // Padded rows (G not a multiple of the team): a slot past the row's
-        // groups re-reads the lane's first group.  The slot offset goes into the
-        // per-lane offset here, because only that part is range-checked: a
-        // scalar offset could carry the matrix's last row past its end.
-        const int li = lane & (lpr - 1);
+      // Per-lane slot offsets are fixed per GEMV (the cursor's): a slot past the
+      // row's groups (padded rows, or t >= C) re-reads the lane's first group,
+      // so a lane of a row in range stays in range.  Only this per-lane part of
+      // a buffer address is range-checked, so the scalar offset stays 0; lanes
+      // past the end of the matrix (or of an empty resource) read zeros.
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bool in = t < C && li + lpr * t < G;
-          const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(
-              bw, in ? voff + t * lpr * 16 : voff, 0, kNonTemporal);
-          rw[p][t] = make_uint4(v[0], v[1], v[2], v[3]);
-          rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, in ? voff_s + t * lpr * 2 : voff_s,
-                                                          0, 0);
-        }
-      } else {
-        // Unpadded: slot t of a row lies inside the row, so a lane in range keeps
-        // its slots in range, and a lane past the end (or any lane of an empty
-        // resource) reads zeros whatever the scalar offset.
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // uniform, and kept scalar so that it is the loads' soffset operand
-          const int so = __builtin_amdgcn_readfirstlane((t < C ? t : 0) * lpr);
-          const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, voff, so * 16, kNonTemporal);
-          rw[p][t] = make_uint4(v[0], v[1], v[2], v[3]);
-          rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, voff_s, so * 2, 0);
-        }
+      for (int t = 0; t < 4; ++t) {
+        const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, cu.vo[t], 0, kNonTemporal);
+        U.rw[p][t] = make_uint4(v[0], v[1], v[2], v[3]);
+        U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, cu.vo[t] >> 3, 0, 0);
       }
-      rj[p] = live ? cu.j : -1;
-      rrow[p] = row0;
-      rN[p] = cu.N;
-      rG[p] = G;
-      rlg[p] = lg;
-      rC[p] = C;
-      rr0[p] = cu.r0;
+      U.rj[p] = live ? cu.j : -1;
+      U.rrow[p] = row0;
+      U.rN[p] = cu.N;
+      U.rG[p] = G;
+      U.rlg[p] = lg;
+      U.rC[p] = C;
+      U.rr0[p] = cu.r0;
       if (live) {
         cu.s += kCompute;
         if (cu.s >= cu.s_end) enter(cu.j + 1);
       }
     }
+  };
+  // Consume a burst in item order; false once an item past the end is reached.
+  auto consume = [&](Burst& U) -> bool {
     // All items of the burst in one GEMV (the common case): x of each group is
     // read from LDS once and used for all B rows, which also gives B independent
     // dot-product chains.
-    if (rj[B - 1] >= 0 && rj[0] == rj[B - 1]) {
-      const int j = rj[0];
+    if (U.rj[B - 1] >= 0 && U.rj[0] == U.rj[B - 1]) {
+      const int j = U.rj[0];
       signal_upto(j);
       wait_x(j);
-      const int lg = rlg[0], lpr = 1 << lg;
+      const int lg = U.rlg[0], lpr = 1 << lg;
       const int li = lane & (lpr - 1);
       const int xi = j % kXBufs;
       const uint4* xb = xbuf + xi * 4 * maxG + li;
       const float* cb = cbuf + xi * maxG + li;
-      if (rC[0] * lpr > rG[0]) {      // padded rows: slots past G hold other data
+      if (U.rC[0] * lpr > U.rG[0]) {      // padded rows: slots past G hold other data
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const bool ok = li + lpr * t < rG[0];
+          const bool ok = li + lpr * t < U.rG[0];
 #pragma unroll
-          for (int p = 0; p < B; ++p) rs[p][t] = ok ? rs[p][t] : (uint16_t)0;
+          for (int p = 0; p < B; ++p) U.rs[p][t] = ok ? U.rs[p][t] : (uint16_t)0;
         }
       }
       float acc[B];
@@ -537,60 +546,68 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       for (int p = 0; p < B; ++p) acc[p] = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if (t < rC[0]) {
+        if (t < U.rC[0]) {
           uint4 x[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
           const float nbias = -cb[lpr * t];
 #pragma unroll
           for (int p = 0; p < B; ++p) {
-            const float pd = group_dot(rw[p][t], x, nbias, nb);
-            acc[p] = __builtin_fmaf(pd, (float)bits<_Float16>(rs[p][t]), acc[p]);
+            const float pd = group_dot(U.rw[p][t], x, nbias, nb);
+            acc[p] = __builtin_fmaf(pd, (float)bits<_Float16>(U.rs[p][t]), acc[p]);
           }
         }
       }
 #pragma unroll
       for (int p = 0; p < B; ++p) {
         const float r = team_sum(acc[p], lg);
-        const int row = rrow[p] + (lane >> lg);
-        if (li == 0 && row < rN[p])
-          ybuf[xi * ybuf_rows + (row - rr0[p])] = bits<uint16_t>((_Float16)r);
+        const int row = U.rrow[p] + (lane >> lg);
+        if (li == 0 && row < U.rN[p])
+          ybuf[xi * ybuf_rows + (row - U.rr0[p])] = bits<uint16_t>((_Float16)r);
       }
-      continue;
+      return true;
     }
 #pragma unroll
     for (int p = 0; p < B; ++p) {
-      const int j = rj[p];
-      if (j < 0) goto drained;
+      const int j = U.rj[p];
+      if (j < 0) return false;
       signal_upto(j);
       wait_x(j);
-      const int lg = rlg[p], lpr = 1 << lg;
+      const int lg = U.rlg[p], lpr = 1 << lg;
       const int li = lane & (lpr - 1);
-      const int row = rrow[p] + (lane >> lg);
+      const int row = U.rrow[p] + (lane >> lg);
       const int xi = j % kXBufs;
       const uint4* xb = xbuf + xi * 4 * maxG + li;
       const float* cb = cbuf + xi * maxG + li;
-      if (rC[p] * lpr > rG[p]) {      // padded rows: slots past G hold other data
+      if (U.rC[p] * lpr > U.rG[p]) {      // padded rows: slots past G hold other data
 #pragma unroll
-        for (int t = 0; t < 4; ++t) rs[p][t] = li + lpr * t < rG[p] ? rs[p][t] : (uint16_t)0;
+        for (int t = 0; t < 4; ++t) U.rs[p][t] = li + lpr * t < U.rG[p] ? U.rs[p][t] : (uint16_t)0;
       }
       float acc = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if (t < rC[p]) {
+        if (t < U.rC[p]) {
           uint4 x[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
-          const float pd = group_dot(rw[p][t], x, -cb[lpr * t], nb);
-          acc = __builtin_fmaf(pd, (float)bits<_Float16>(rs[p][t]), acc);
+          const float pd = group_dot(U.rw[p][t], x, -cb[lpr * t], nb);
+          acc = __builtin_fmaf(pd, (float)bits<_Float16>(U.rs[p][t]), acc);
         }
       }
       acc = team_sum(acc, lg);
-      if (li == 0 && row < rN[p])
-        ybuf[xi * ybuf_rows + (row - rr0[p])] = bits<uint16_t>((_Float16)acc);
+      if (li == 0 && row < U.rN[p])
+        ybuf[xi * ybuf_rows + (row - U.rr0[p])] = bits<uint16_t>((_Float16)acc);
     }
+      return true;
+  };
+  // All loads of a burst are issued before any is consumed, so no loaded value
+  // crosses the loop's back edge and every issue is the same eight loads per
+  // item: the compiler then waits exactly for the item being consumed.
+  while (true) {
+    Burst U;
+    issue(U);
+    if (!consume(U)) break;
   }
-  drained:
     signal_upto(n);
   }
 
@@ -614,7 +631,7 @@ __global__ void k_zero(unsigned* __restrict__ p, int count) {
     p[i] = 0u;
 }
 
-constexpr int kBurst = 3;
+constexpr int kBurst = 2;
 
 }  // namespace
 
@@ -646,7 +663,8 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
     s.steps = (int)((L.N + rps - 1) / rps);
     s.dep = -1;
     s.signal = 0;
-    s.pad = 0;
+    s.sbase = s.steps / p.grid;
+    s.srem = s.steps % p.grid;
     if (lpr * C > maxG) maxG = lpr * C;         // padded group count
     const int rows_wg = ((s.steps + p.grid - 1) / p.grid) * rps;
     if (rows_wg > ybuf_rows) ybuf_rows = rows_wg;
