@@ -41,6 +41,8 @@ struct StepPlan {
   int maxG = 0;
   int ybuf_rows = 0;
   int counters = 0;      // completion counters, exit counter, spare, error word
+  bool cross_wg = false; // some descriptor waits for others on every workgroup: all
+                         // workgroups must be resident at once (cooperative launch)
   size_t lds_bytes = 0;
   std::vector<StepDesc> desc;
 };

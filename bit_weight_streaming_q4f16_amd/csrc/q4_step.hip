@@ -690,7 +690,10 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
       }
     }
     p.desc[(size_t)k].dep = dep;
-    if (dep >= 0) p.desc[(size_t)dep].signal = 1;
+    if (dep >= 0) {
+      p.desc[(size_t)dep].signal = 1;
+      p.cross_wg = true;
+    }
   }
   p.maxG = maxG;
   p.ybuf_rows = (ybuf_rows + 7) & ~7;
@@ -722,8 +725,15 @@ hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, bo
   int n = (int)p.desc.size(), maxG = p.maxG, yr = p.ybuf_rows;
   void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&done, (void*)&err, (void*)&maxG,
                   (void*)&yr};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(p.grid),
-                                    dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
+  // Only waits across workgroups need every workgroup resident at once; without
+  // them (no descriptor depends on another) a plain launch does, and it costs
+  // far less at the kernel boundary than a cooperative one.
+  if (p.cross_wg)
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(p.grid),
+                                      dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kStepThreads), p.lds_bytes, s, dev_desc, n, done,
+                     err, maxG, yr);
+  return hipGetLastError();
 }
 
 hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu) {
