@@ -12,7 +12,11 @@
 #include "q4f16.h"
 #include "q4_internal.h"
 #include "q4_step.h"
+#include <algorithm>
+#include <cstring>
+
 #include "q4_step_dma.h"
+#include "q4_step_mfma.h"
 
 namespace {
 
@@ -295,6 +299,12 @@ size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, 
     const size_t b = q4::plan_auto(*d, M, L.N, L.K).ws_bytes;
     if (b > need) need = b;
   }
+  if (M > 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
+    std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
+    q4::MStepPlan p = q4::plan_step_mfma(*d, sl.data(), n_layers, (int)M,
+                                         (flags & Q4_STEP_ORDERED) != 0);
+    if (p.ok) need = std::max(need, q4::step_mfma_workspace_bytes(p));
+  }
   if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
     std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
@@ -331,6 +341,24 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (!d) return fail(Q4_ERR_DEVICE, "q4_decode_step: no HIP device");
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  if (M > 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
+    std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
+    q4::MStepPlan p = q4::plan_step_mfma(*d, sl.data(), n_layers, (int)M,
+                                         (flags & Q4_STEP_ORDERED) != 0);
+    int per_cu = 0;
+    if (p.ok && q4::step_mfma_occupancy(p, &per_cu) == hipSuccess && per_cu >= 1) {
+      if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_mfma_workspace_bytes(p)))
+        return rc;
+      hipError_t e = hipSuccess;
+      const void* table = device_table(p.desc.data(), p.desc.size() * sizeof(q4::MStepDesc),
+                                       d->id, s, &e);
+      if (!table) return device_error(e, "q4_decode_step: descriptor table");
+      e = q4::launch_step_mfma(p, static_cast<const q4::MStepDesc*>(table), ws,
+                               (flags & Q4_STEP_WS_CLEAN) != 0, s);
+      return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
+    }
+    (void)hipGetLastError();
+  }
   if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
     std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
@@ -355,10 +383,16 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
       if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_workspace_bytes(p)))
         return rc;
       hipError_t e = hipSuccess;
-      const void* table = device_table(p.desc.data(), p.desc.size() * sizeof(q4::StepDesc),
-                                       d->id, s, &e);
+      // descriptors, then (range mode) the per-workgroup ranges
+      const size_t db = p.desc.size() * sizeof(q4::StepDesc);
+      std::vector<uint8_t> host(db + p.ranges.size() * sizeof(int));
+      std::memcpy(host.data(), p.desc.data(), db);
+      if (!p.ranges.empty())
+        std::memcpy(host.data() + db, p.ranges.data(), p.ranges.size() * sizeof(int));
+      const void* table = device_table(host.data(), host.size(), d->id, s, &e);
       if (!table) return device_error(e, "q4_decode_step: descriptor table");
-      e = q4::launch_step(p, static_cast<const q4::StepDesc*>(table), ws,
+      const int4* ranges = reinterpret_cast<const int4*>(static_cast<const uint8_t*>(table) + db);
+      e = q4::launch_step(p, static_cast<const q4::StepDesc*>(table), ranges, ws,
                           (flags & Q4_STEP_WS_CLEAN) != 0, s);
       return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
     }

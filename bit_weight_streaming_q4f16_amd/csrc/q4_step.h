@@ -43,6 +43,11 @@ struct StepPlan {
   int counters = 0;      // completion counters, exit counter, spare, error word
   bool cross_wg = false; // some descriptor waits for others on every workgroup: all
                          // workgroups must be resident at once (cooperative launch)
+  int nx = 0;            // x buffers (kXBufs, or 4 in range mode)
+  // Range mode (no dependencies): per workgroup {first row-step, end row-step,
+  // first GEMV, last GEMV} of the row-steps of all GEMVs laid end to end,
+  // balanced by weight bytes.  Empty otherwise.
+  std::vector<int> ranges;
   size_t lds_bytes = 0;
   std::vector<StepDesc> desc;
 };
@@ -54,8 +59,9 @@ size_t step_workspace_bytes(const StepPlan& p);
 // dev_desc: p.desc copied to device memory.  Zeroes the counters in ws (unless
 // ws_clean: they are already zero, as the kernel leaves them), then runs the
 // cooperative kernel.
-hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, bool ws_clean,
-                       hipStream_t s);
+// dev_ranges: p.ranges copied to device memory (nullptr when p.ranges is empty).
+hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, const int4* dev_ranges,
+                       void* ws, bool ws_clean, hipStream_t s);
 hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu);
 
 }  // namespace q4

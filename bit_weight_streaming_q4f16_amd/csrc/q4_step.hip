@@ -30,6 +30,9 @@
 // before its x is read.  Default: only where an earlier descriptor writes memory
 // that k reads or writes; the "ordered" mode makes every descriptor wait for its
 // predecessor, as in a decode step whose GEMVs feed each other.
+#include <algorithm>
+#include <climits>
+
 #include "q4_step.h"
 
 namespace q4 {
@@ -69,7 +72,7 @@ __device__ __forceinline__ uint4 load_nt_g(const Q4_GLOBAL uint4* p) {
 struct CursorDesc {
   const Q4_GLOBAL uint4* W;
   const Q4_GLOBAL uint16_t* S;
-  int N, G, lg, C, sbase, srem;
+  int N, G, lg, C, steps, sbase, srem;
 };
 typedef uint32_t u32x8_s __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
@@ -83,7 +86,8 @@ __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
       : "s"(d));
   static_assert(offsetof(StepDesc, S) == 8 && offsetof(StepDesc, N) == 32 &&
                     offsetof(StepDesc, G) == 36 && offsetof(StepDesc, lpr_log2) == 40 &&
-                    offsetof(StepDesc, C) == 42 && offsetof(StepDesc, sbase) == 56 &&
+                    offsetof(StepDesc, C) == 42 && offsetof(StepDesc, steps) == 44 &&
+                    offsetof(StepDesc, sbase) == 56 &&
                     offsetof(StepDesc, srem) == 60,
                 "descriptor offsets read by the compute waves");
   CursorDesc r;
@@ -93,6 +97,7 @@ __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
   r.G = (int)rest[1];
   r.lg = (int)(rest[2] & 0xFFFFu);
   r.C = (int)(rest[2] >> 16);
+  r.steps = (int)rest[3];
   r.sbase = (int)rest[6];
   r.srem = (int)rest[7];
   return r;
@@ -215,16 +220,18 @@ __device__ __forceinline__ int wg_step(int sbase, int srem, int wg) {
 //            blocks past a GEMV's own G are zero
 //   cbuf[b]: maxG floats, the bias term of each group (zero past G)
 //   ybuf[b]: ybuf_rows fp16 results of this workgroup's rows
-template <int B>
+template <int B, int NX>
 __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restrict__ D, int n,
                                                        unsigned* __restrict__ done,
                                                        unsigned* __restrict__ err, int maxG,
-                                                       int ybuf_rows) {
+                                                       int ybuf_rows,
+                                                       const int4* __restrict__ ranges) {
+  static_assert(NX <= kXBufs && NX % kSync == 0, "x buffers");
   extern __shared__ uint4 smem[];
   __shared__ Shared sh;
   uint4* xbuf = smem;                                                           // [NX][4][maxG]
-  float* cbuf = reinterpret_cast<float*>(smem + kXBufs * 4 * maxG);             // [NX][maxG]
-  uint16_t* ybuf = reinterpret_cast<uint16_t*>(cbuf + kXBufs * maxG);          // [NX][rows]
+  float* cbuf = reinterpret_cast<float*>(smem + NX * 4 * maxG);                 // [NX][maxG]
+  uint16_t* ybuf = reinterpret_cast<uint16_t*>(cbuf + NX * maxG);              // [NX][rows]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wg = blockIdx.x, nwg = gridDim.x;
@@ -235,23 +242,49 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   if (threadIdx.x == 0) sh.err = 0;
   __syncthreads();
 
+  // This workgroup's share: in range mode (a list without dependencies) the
+  // row-steps [ra, rb) of all GEMVs laid end to end, which lie in GEMVs j0..j1;
+  // otherwise an even share of every GEMV (j0 = 0, j1 = n - 1).
+  int ra = 0, rb = 0, j0 = 0, j1 = n - 1;
+  if (ranges) {
+    const int4 rr = ranges[wg];
+    ra = __builtin_amdgcn_readfirstlane(rr.x);
+    rb = __builtin_amdgcn_readfirstlane(rr.y);
+    j0 = __builtin_amdgcn_readfirstlane(rr.z);
+    j1 = __builtin_amdgcn_readfirstlane(rr.w);
+  }
+  // row-steps [lo, hi) of a GEMV in this workgroup: sbase is the GEMV's first
+  // row-step in the concatenation when srem < 0 (range mode), else the even split
+  auto item_range = [&](int sbase, int srem, int steps, int& lo, int& hi) {
+    if (srem < 0) {
+      lo = min(max(ra - sbase, 0), steps);
+      hi = min(max(rb - sbase, 0), steps);
+    } else {
+      lo = wg_step(sbase, srem, wg);
+      hi = wg_step(sbase, srem, wg + 1);
+    }
+  };
+
   if (wave < kSync) {
     // ----------------------------------------------------------- sync waves
-    // Sync wave `wave` owns GEMVs k = wave (mod kSync): it stages their x and
-    // copies out / publishes their y.  kXBufs is a multiple of kSync, so GEMV k
-    // and the GEMV k - kXBufs whose buffer it reuses have the same owner.
+    // Sync wave `wave` owns this workgroup's GEMVs k = j0 + wave (mod kSync): it
+    // stages their x and copies out / publishes their y.  NX is a multiple of
+    // kSync, so GEMV k and the GEMV k - NX whose buffer it reuses have the same
+    // owner.  Buffers and counters are indexed from j0.
     const int me = wave;
-    int next_fin = me;                 // next own GEMV to copy out and publish
+    int next_fin = j0 + me;            // next own GEMV to copy out and publish
     auto complete = [&](int i) {
-      return (unsigned)lds_load(&sh.local_done[i % kXBufs]) >=
-             (unsigned)kCompute * (unsigned)(i / kXBufs + 1);
+      return (unsigned)lds_load(&sh.local_done[(i - j0) % NX]) >=
+             (unsigned)kCompute * (unsigned)((i - j0) / NX + 1);
     };
     auto finish_one = [&](int i) {
       const StepDesc& d = D[i];
-      const int b = i % kXBufs;
+      const int b = (i - j0) % NX;
       const int rps = 64 >> d.lpr_log2;
-      const int r0 = wg_step(d.sbase, d.srem, wg) * rps;
-      int r1 = wg_step(d.sbase, d.srem, wg + 1) * rps;
+      int lo, hi;
+      item_range(d.sbase, d.srem, d.steps, lo, hi);
+      const int r0 = lo * rps;
+      int r1 = hi * rps;
       if (r1 > d.N) r1 = d.N;
       const uint16_t* yb = ybuf + b * ybuf_rows;
       if (!d.signal) {
@@ -272,7 +305,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     // finish own GEMVs <= last in order; block: wait for each to complete locally,
     // otherwise stop at the first one that has not
     auto finish_upto = [&](int last, bool block) {
-      while (next_fin <= last && next_fin < n) {
+      while (next_fin <= last && next_fin <= j1) {
         if (!complete(next_fin)) {
           if (!block) return;
           // a long sleep: polling issues vector instructions that the
@@ -286,14 +319,14 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         next_fin += kSync;
       }
     };
-    for (int k = me; k < n; k += kSync) {
+    for (int k = j0 + me; k <= j1; k += kSync) {
       const StepDesc& d = D[k];
       const int G = d.G, nblk = 4 * G;
       finish_upto(k - kSync, false);             // publish what is already complete
-      if (k >= kXBufs) finish_upto(k - kXBufs, true);   // buffer k % kXBufs is free again
+      if (k - j0 >= NX) finish_upto(k - NX, true);   // buffer (k - j0) % NX is free again
       const bool coherent = d.dep >= 0;
       if (coherent) {
-        if (d.dep % kSync == me) finish_upto(d.dep, true);
+        if ((d.dep - j0) % kSync == me) finish_upto(d.dep, true);
         for (unsigned it = 0;
              __hip_atomic_load(&done[d.dep], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
              (unsigned)nwg;
@@ -306,7 +339,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint4*>(d.X), 0, 0x7FFFFFFF, 0x00020000);
       const Q4_GLOBAL u32x4_g* X = (const Q4_GLOBAL u32x4_g*)d.X;
-      const int b = k % kXBufs;
+      const int b = (k - j0) % NX;
       uint4* xb = xbuf + b * 4 * maxG;
       float* cb = cbuf + b * maxG;
       // x_k in (at most) two batches of 8 blocks per lane: one round trip for
@@ -371,12 +404,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       if (lane == 0) __hip_atomic_store(&sh.x_ready[b], k, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    finish_upto(n - 1, true);
+    finish_upto(j1, true);
     if (me == 0) {
       // every compute wave has signalled the last GEMV (so none will still set
-      // the error word) once the owner of GEMV n - 1 is done; wave 0 waits for
+      // the error word) once the owner of GEMV j1 is done; wave 0 waits for
       // the last completion before reading it
-      for (unsigned it = 0; !complete(n - 1); ++it) {
+      for (unsigned it = 0; j0 <= j1 && !complete(j1); ++it) {
         if (it > kSpinLimit) break;
         __builtin_amdgcn_s_sleep(1);
       }
@@ -408,10 +441,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   int base = 0;                  // items of GEMVs before cu.j in this workgroup, mod kCompute
   // enter GEMV j or, if this wave has no item there, the next one that has
   auto enter = [&](int j) {
-    for (; j < n; ++j) {
+    for (; j <= j1; ++j) {
       const CursorDesc d = read_desc(D + j);
-      const int s0 = wg_step(d.sbase, d.srem, wg);
-      const int s1 = wg_step(d.sbase, d.srem, wg + 1);
+      int s0, s1;
+      item_range(d.sbase, d.srem, d.steps, s0, s1);
       int off = c - base;
       if (off < 0) off += kCompute;
       base = (base + (s1 - s0)) % kCompute;      // GEMV j's items are dealt either way
@@ -437,12 +470,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         return;
       }
     }
-    cu.j = n;
+    cu.j = j1 + 1;
   };
-  enter(0);
+  enter(j0);
 
   auto wait_x = [&](int j) {
-    for (unsigned it = 0; lds_load(&sh.x_ready[j % kXBufs]) != j; ++it) {
+    for (unsigned it = 0; lds_load(&sh.x_ready[(j - j0) % NX]) != j; ++it) {
       if (it > kSpinLimit) {
         __hip_atomic_store(&sh.err, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         break;
@@ -450,12 +483,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       __builtin_amdgcn_s_sleep(1);
     }
   };
-  int cur = 0;                    // GEMVs [0, cur) have been signalled by this wave
+  int cur = j0;                   // GEMVs [j0, cur) have been signalled by this wave
   auto signal_upto = [&](int j) { // signal completion of GEMVs [cur, j)
     for (; cur < j; ++cur) {
       wait_x(cur);
       wait_lds();                 // this wave's y rows of `cur` are in LDS
-      if (lane == 0) __hip_atomic_fetch_add(&sh.local_done[cur % kXBufs], 1, __ATOMIC_RELAXED,
+      if (lane == 0) __hip_atomic_fetch_add(&sh.local_done[(cur - j0) % NX], 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   };
@@ -480,7 +513,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   auto issue = [&](Burst& U) {
 #pragma unroll
     for (int p = 0; p < B; ++p) {
-      const bool live = cu.j < n;
+      const bool live = cu.j <= j1;
       const int lg = live ? cu.lg : 2, lpr = 1 << lg;
       const int G = live ? cu.G : 1;
       const int C = live ? cu.C : 1;
@@ -530,7 +563,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       wait_x(j);
       const int lg = U.rlg[0], lpr = 1 << lg;
       const int li = lane & (lpr - 1);
-      const int xi = j % kXBufs;
+      const int xi = (j - j0) % NX;
       const uint4* xb = xbuf + xi * 4 * maxG + li;
       const float* cb = cbuf + xi * maxG + li;
       if (U.rC[0] * lpr > U.rG[0]) {      // padded rows: slots past G hold other data
@@ -576,7 +609,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const int lg = U.rlg[p], lpr = 1 << lg;
       const int li = lane & (lpr - 1);
       const int row = U.rrow[p] + (lane >> lg);
-      const int xi = j % kXBufs;
+      const int xi = (j - j0) % NX;
       const uint4* xb = xbuf + xi * 4 * maxG + li;
       const float* cb = cbuf + xi * maxG + li;
       if (U.rC[p] * lpr > U.rG[p]) {      // padded rows: slots past G hold other data
@@ -608,7 +641,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     issue(U);
     if (!consume(U)) break;
   }
-    signal_upto(n);
+    signal_upto(j1 + 1);
   }
 
   // Leave the counters zeroed for the next call: the last workgroup to get here
@@ -696,10 +729,76 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
     }
   }
   p.maxG = maxG;
-  p.ybuf_rows = (ybuf_rows + 7) & ~7;
-  p.lds_bytes = (size_t)kXBufs * ((size_t)4 * maxG * 16 + (size_t)maxG * 4 + (size_t)p.ybuf_rows * 2);
   p.counters = (int)n + 4;
-  p.ok = p.lds_bytes <= d.lds_per_block - sizeof(int) * 8;
+  const size_t lds_cap = d.lds_per_block - sizeof(int) * 32;
+  auto lds_for = [&](int nx, int rows) {
+    return (size_t)nx * ((size_t)4 * maxG * 16 + (size_t)maxG * 4 + (size_t)rows * 2);
+  };
+  // Range mode: without dependencies, each workgroup streams one contiguous
+  // stretch of the row-steps of all GEMVs laid end to end (balanced by weight
+  // bytes), so it meets only a few GEMV boundaries instead of every one.
+  if (!p.cross_wg) {
+    std::vector<int64_t> first((size_t)n + 1), cum((size_t)n + 1);   // row-steps, bytes
+    for (int64_t k = 0; k < n; ++k) {
+      const StepDesc& s = p.desc[(size_t)k];
+      const int64_t step_bytes = (int64_t)(64 >> s.lpr_log2) * s.G * 18;
+      first[(size_t)k + 1] = first[(size_t)k] + s.steps;
+      cum[(size_t)k + 1] = cum[(size_t)k] + step_bytes * s.steps;
+    }
+    const int64_t total = cum[(size_t)n];
+    std::vector<int64_t> cut((size_t)p.grid + 1);
+    for (int w = 0; w <= p.grid; ++w) {
+      const int64_t target = (int64_t)(((__int128)total * w) / p.grid);
+      int64_t k = std::upper_bound(cum.begin(), cum.end(), target) - cum.begin() - 1;
+      if (k >= n) k = n - 1;
+      const StepDesc& s = p.desc[(size_t)k];
+      const int64_t step_bytes = (int64_t)(64 >> s.lpr_log2) * s.G * 18;
+      int64_t st = (target - cum[(size_t)k]) / step_bytes;
+      if (st > s.steps) st = s.steps;
+      cut[(size_t)w] = w == p.grid ? first[(size_t)n] : first[(size_t)k] + st;
+    }
+    auto gemv_of = [&](int64_t item) {   // GEMV holding row-step `item`
+      return (int)(std::upper_bound(first.begin(), first.end(), item) - first.begin() - 1);
+    };
+    std::vector<int> ranges((size_t)p.grid * 4);
+    int rows = 8;
+    bool fits = first[(size_t)n] < INT32_MAX;
+    for (int w = 0; w < p.grid && fits; ++w) {
+      const int64_t a = cut[(size_t)w], b = cut[(size_t)w + 1];
+      int j0 = 1, j1 = 0;                  // empty
+      if (b > a) {
+        j0 = gemv_of(a);
+        j1 = gemv_of(b - 1);
+        for (int j = j0; j <= j1; ++j) {
+          const StepDesc& s = p.desc[(size_t)j];
+          const int64_t lo = std::max<int64_t>(a - first[(size_t)j], 0);
+          const int64_t hi = std::min<int64_t>(b - first[(size_t)j], s.steps);
+          rows = std::max<int64_t>(rows, (hi - lo) * (64 >> s.lpr_log2));
+        }
+      }
+      ranges[(size_t)w * 4 + 0] = (int)a;
+      ranges[(size_t)w * 4 + 1] = (int)b;
+      ranges[(size_t)w * 4 + 2] = j0;
+      ranges[(size_t)w * 4 + 3] = j1;
+    }
+    rows = (rows + 7) & ~7;
+    if (fits && lds_for(4, rows) <= lds_cap) {
+      p.nx = 4;
+      p.ybuf_rows = rows;
+      p.ranges = std::move(ranges);
+      for (int64_t k = 0; k < n; ++k) {
+        p.desc[(size_t)k].sbase = (int)first[(size_t)k];
+        p.desc[(size_t)k].srem = -1;
+      }
+      p.lds_bytes = lds_for(4, rows);
+      p.ok = true;
+      return p;
+    }
+  }
+  p.nx = kXBufs;
+  p.ybuf_rows = (ybuf_rows + 7) & ~7;
+  p.lds_bytes = lds_for(kXBufs, p.ybuf_rows);
+  p.ok = p.lds_bytes <= lds_cap;
   return p;
 }
 
@@ -707,15 +806,15 @@ size_t step_workspace_bytes(const StepPlan& p) {
   return ((size_t)p.counters * sizeof(unsigned) + 255) & ~(size_t)255;
 }
 
-hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, bool ws_clean,
-                       hipStream_t s) {
+hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, const int4* dev_ranges,
+                       void* ws, bool ws_clean, hipStream_t s) {
   unsigned* done = static_cast<unsigned*>(ws);
   unsigned* err = done + (p.counters - 1);
   if (!ws_clean) {
     hipLaunchKernelGGL(k_zero, dim3(1), dim3(256), 0, s, done, p.counters);
     if (hipError_t e = hipGetLastError()) return e;
   }
-  auto kern = k_step<kBurst>;
+  auto kern = p.nx == 4 ? k_step<kBurst, 4> : k_step<kBurst, kXBufs>;
   if (p.lds_bytes > 65536) {
     if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -723,8 +822,9 @@ hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, bo
       return e;
   }
   int n = (int)p.desc.size(), maxG = p.maxG, yr = p.ybuf_rows;
+  const int4* rg = p.ranges.empty() ? nullptr : dev_ranges;
   void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&done, (void*)&err, (void*)&maxG,
-                  (void*)&yr};
+                  (void*)&yr, (void*)&rg};
   // Only waits across workgroups need every workgroup resident at once; without
   // them (no descriptor depends on another) a plain launch does, and it costs
   // far less at the kernel boundary than a cooperative one.
@@ -732,14 +832,15 @@ hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, void* ws, bo
     return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(p.grid),
                                       dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kStepThreads), p.lds_bytes, s, dev_desc, n, done,
-                     err, maxG, yr);
+                     err, maxG, yr, rg);
   return hipGetLastError();
 }
 
 hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      blocks_per_cu, reinterpret_cast<const void*>(k_step<kBurst>), kStepThreads,
-      p.lds_bytes);
+      blocks_per_cu,
+      reinterpret_cast<const void*>(p.nx == 4 ? k_step<kBurst, 4> : k_step<kBurst, kXBufs>),
+      kStepThreads, p.lds_bytes);
 }
 
 }  // namespace q4

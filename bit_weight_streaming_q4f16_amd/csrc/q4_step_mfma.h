@@ -1,0 +1,43 @@
+// Internal interface of the persistent small-M decode-step kernel (q4_step_mfma.hip).
+#pragma once
+
+#include <vector>
+
+#include "q4_step.h"
+
+namespace q4 {
+
+// One GEMV as the small-M kernel reads it (device-resident table, 64 bytes).
+struct MStepDesc {
+  const uint4* W;        // words [N][G] (one uint4 per group)
+  const uint16_t* S;     // scales [N][G]
+  const uint4* X;        // X [M][K] as blocks of 8 halves
+  uint16_t* Y;           // Y [M][N]
+  int N, G;
+  int tbase, trem;       // 16-row tiles split over the grid: workgroup w owns tiles from
+                         // w * tbase + min(w, trem), the first trem get one more
+  int dep, signal;       // as in StepDesc
+  int xoff;              // byte offset of the GEMV's LDS region (X, bias terms, y rows)
+  int rel;               // GEMV whose LDS region overlaps this one (-1: none): it must
+                         // be finished before this one's X is staged
+};
+static_assert(sizeof(MStepDesc) == 64, "MStepDesc layout");
+
+struct MStepPlan {
+  bool ok = false;
+  bool cross_wg = false;     // some descriptor waits for another on every workgroup
+  int grid = 0, M = 0, counters = 0;
+  size_t lds_bytes = 0;
+  std::vector<MStepDesc> desc;
+};
+
+// Persistent kernel for 2 <= M <= 8: every K a multiple of 128 and at most 8192,
+// every GEMV's LDS region (M*K*2 + K + rows*M*2 bytes) within the LDS.
+MStepPlan plan_step_mfma(const DeviceInfo& d, const StepLayer* layers, int64_t n, int M,
+                         bool ordered);
+size_t step_mfma_workspace_bytes(const MStepPlan& p);
+hipError_t step_mfma_occupancy(const MStepPlan& p, int* blocks_per_cu);
+hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc, void* ws,
+                            bool ws_clean, hipStream_t s);
+
+}  // namespace q4

@@ -1,0 +1,546 @@
+// Persistent decode-step kernel for small M (2..8 rows of X per GEMV): the whole
+// layer list in one launch, each GEMV's weights read once for all M rows (the
+// Splash page's batched decode: several tokens or sequences share one pass over
+// the weights), the products on matrix cores.
+//
+// v_mfma_f32_16x16x32_f16 multiplies a 16 x 32 A by a 32 x 16 B.  Here A = the M
+// rows of X over one 32-weight group (rows past M are zero) and B = the group of
+// 16 weight rows, so one MFMA is one group of one 16-row tile and its per-group
+// scale is applied exactly, in fp32, to the result.  The weights enter B as the
+// exact fp16 values 1024 + q or 64 + q (one v_and_or_b32 per pair, as in the M = 1
+// kernels); the MFMA's accumulator input carries minus the per-group bias term
+// (1031 * sum of even-position x + 71 * sum of odd-position x, per row of X), so
+// each product is (q - 7) * x without a subtraction.
+//
+// One workgroup of 16 waves per compute unit:
+//  * 12 compute waves take this workgroup's 16-row tiles of every GEMV in list
+//    order, dealt round-robin.  A tile streams in bursts of kChunks chunks of four
+//    groups: per lane one dwordx4 (group c of row r, for lane = 16c + r) and one
+//    8-byte load of the row's four scales; a 4 x 4 exchange between lanes r,
+//    r + 16, r + 32, r + 48 leaves word c of each of the four groups in lane
+//    (c, r), which is the B layout.  X and the bias terms come from LDS; results
+//    go to LDS.
+//  * 4 sync waves, each owning every 4th GEMV: stage its X (pair-ordered, with the
+//    bias terms) into the GEMV's LDS region once the GEMVs it depends on are
+//    complete on every workgroup and the region's previous user is finished,
+//    copy finished rows of Y out, publish completion (as in the M = 1 kernel).
+// LDS regions are planned on the host as a ring: a GEMV's region is reused only
+// after the GEMVs that used it before are finished.
+#include "q4_step_mfma.h"
+
+namespace q4 {
+namespace {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_g __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8_s __attribute__((ext_vector_type(8)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+#define Q4_GLOBAL __attribute__((address_space(1)))
+
+template <typename T, typename F>
+__device__ __forceinline__ T bits(F v) {
+  return __builtin_bit_cast(T, v);
+}
+
+constexpr int kWaves = kStepThreads / 64;   // 16
+constexpr int kSync = 4;
+constexpr int kCompute = kWaves - kSync;
+constexpr int kSlots = 8;                   // x_ready slots: GEMVs up to 8 apart in flight
+constexpr int kChunks = 8;                  // chunks (of four groups) per burst
+constexpr unsigned kSpinLimit = 1u << 24;
+constexpr int kCoherent = 1 | 16;           // sc0 | sc1
+constexpr int kNonTemporal = 2;
+constexpr int kWaitVm0 = 0x0F70;            // s_waitcnt vmcnt(0)
+constexpr int kRsrcFlags = 0x00020000;
+static_assert(kSlots % kSync == 0, "a GEMV and the one whose slot it reuses share an owner");
+
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ int lds_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// A block of 8 consecutive x values reordered into the pairs (x0,x4) (x1,x5)
+// (x2,x6) (x3,x7) in which a word's nibble pairs are dequantised.
+__device__ __forceinline__ uint4 pair_order(uint4 v) {
+  uint4 o;
+  o.x = (v.x & 0xFFFFu) | (v.z << 16);
+  o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+  o.z = (v.y & 0xFFFFu) | (v.w << 16);
+  o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+  return o;
+}
+
+// rows {0,1} <-> {2,3} of a 4 x 4 block spread over lanes r, r+16, r+32, r+48,
+// then rows 0 <-> 1 and 2 <-> 3: afterwards lane row R register t holds what lane
+// row t register R held.
+__device__ __forceinline__ void transpose4(uint32_t (&v)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  v[0] = a[0]; v[2] = a[1]; v[1] = b[0]; v[3] = b[1];
+  auto c = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
+  v[0] = c[0]; v[1] = c[1]; v[2] = d[0]; v[3] = d[1];
+}
+
+struct Shared {
+  int x_ready[kSlots];    // GEMV whose X is staged, per slot (-1: none)
+  int local_done[kSlots]; // compute-wave completions per slot (monotonic)
+  int fin[kSync];         // highest GEMV each sync wave has finished (copied out)
+  int err;
+};
+
+__device__ __forceinline__ int tile_of(int tbase, int trem, int wg) {
+  return wg * tbase + (wg < trem ? wg : trem);
+}
+
+// The fields a compute wave needs, read with scalar loads (see the M = 1 kernel:
+// ordinary loads of the table would become vector loads and drain the stream).
+struct TileDesc {
+  const Q4_GLOBAL uint4* W;
+  const Q4_GLOBAL uint16_t* S;
+  int N, G, tbase, trem, xoff;
+};
+__device__ __forceinline__ TileDesc read_desc(const MStepDesc* d) {
+  u32x4_g ws;
+  u32x8_s rest;        // N, G, tbase, trem, dep, signal, xoff, rel
+  asm volatile(
+      "s_load_dwordx4 %0, %2, 0x0\n\t"
+      "s_load_dwordx8 %1, %2, 0x20\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(ws), "=&s"(rest)
+      : "s"(d));
+  static_assert(offsetof(MStepDesc, N) == 32 && offsetof(MStepDesc, tbase) == 40 &&
+                    offsetof(MStepDesc, xoff) == 56,
+                "descriptor offsets read by the compute waves");
+  TileDesc r;
+  r.W = (const Q4_GLOBAL uint4*)(((uint64_t)ws[1] << 32) | ws[0]);
+  r.S = (const Q4_GLOBAL uint16_t*)(((uint64_t)ws[3] << 32) | ws[2]);
+  r.N = (int)rest[0];
+  r.G = (int)rest[1];
+  r.tbase = (int)rest[2];
+  r.trem = (int)rest[3];
+  r.xoff = (int)rest[6];
+  return r;
+}
+
+// LDS region of a GEMV (byte offsets from xoff): X planes [G][4][M] uint4, then the
+// bias terms [G][8] float, then y [M][rows] fp16 (rows: the most any workgroup owns).
+__device__ __forceinline__ int corr_off(int M, int G) { return M * G * 64; }
+__device__ __forceinline__ int ybuf_off(int M, int G) { return M * G * 64 + G * 32; }
+__device__ __forceinline__ int rows_of(int tbase, int trem) { return (tbase + (trem > 0)) * 16; }
+
+__global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __restrict__ D, int n,
+                                                            int M, unsigned* __restrict__ done,
+                                                            unsigned* __restrict__ err) {
+  extern __shared__ uint4 smem[];
+  __shared__ Shared sh;
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  if (threadIdx.x < kSlots) {
+    sh.x_ready[threadIdx.x] = -1;
+    sh.local_done[threadIdx.x] = 0;
+  }
+  if (threadIdx.x < kSync) sh.fin[threadIdx.x] = -1;
+  if (threadIdx.x == 0) sh.err = 0;
+  __syncthreads();
+
+  auto complete = [&](int i) {        // every compute wave is past GEMV i here
+    return (unsigned)lds_load(&sh.local_done[i % kSlots]) >=
+           (unsigned)kCompute * (unsigned)(i / kSlots + 1);
+  };
+
+  if (wave < kSync) {
+    // ------------------------------------------------------------ sync waves
+    const int me = wave;
+    int next_fin = me;
+    auto finish_one = [&](int i) {
+      const MStepDesc& d = D[i];
+      const int t0 = tile_of(d.tbase, d.trem, wg), t1 = tile_of(d.tbase, d.trem, wg + 1);
+      const int r0 = t0 * 16;
+      int r1 = t1 * 16;
+      if (r1 > d.N) r1 = d.N;
+      const int rows = rows_of(d.tbase, d.trem), nr = r1 - r0;
+      const uint16_t* yb = reinterpret_cast<const uint16_t*>(lds + d.xoff + ybuf_off(M, d.G));
+      if (nr > 0) {
+        if (!d.signal) {
+          Q4_GLOBAL uint16_t* Y = (Q4_GLOBAL uint16_t*)d.Y;
+          for (int e = lane; e < M * nr; e += 64) {
+            const int m = e / nr, r = e - m * nr;
+            Y[(int64_t)m * d.N + r0 + r] = yb[m * rows + r];
+          }
+        } else {
+          const __amdgpu_buffer_rsrc_t ry =
+              __builtin_amdgcn_make_buffer_rsrc(d.Y, 0, 0x7FFFFFFF, kRsrcFlags);
+          for (int e = lane; e < M * nr; e += 64) {
+            const int m = e / nr, r = e - m * nr;
+            __builtin_amdgcn_raw_buffer_store_b16(yb[m * rows + r], ry,
+                                                  2 * (m * d.N + r0 + r), 0, kCoherent);
+          }
+        }
+      }
+      if (d.signal) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        if (lane == 0)
+          __hip_atomic_fetch_add(&done[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      wait_lds();
+      if (lane == 0) lds_store(&sh.fin[me], i);
+    };
+    auto finish_upto = [&](int last, bool block) {
+      while (next_fin <= last && next_fin < n) {
+        if (!complete(next_fin)) {
+          if (!block) return;
+          for (unsigned it = 0; !complete(next_fin); ++it) {
+            if (it > kSpinLimit / 8) { err[0] = 1u; break; }
+            __builtin_amdgcn_s_sleep(8);
+          }
+        }
+        finish_one(next_fin);
+        next_fin += kSync;
+      }
+    };
+    // every GEMV <= i finished (copied out) by its owner
+    auto finished_upto = [&](int i) {
+      for (int o = 0; o < kSync; ++o) {
+        const int last = i - ((i - o) % kSync + kSync) % kSync;   // largest <= i owned by o
+        if (last >= 0 && lds_load(&sh.fin[o]) < last) return false;
+      }
+      return true;
+    };
+    for (int k = me; k < n; k += kSync) {
+      const MStepDesc& d = D[k];
+      const int G = d.G;
+      finish_upto(k - kSync, false);
+      if (k >= kSlots) finish_upto(k - kSlots, true);   // slot k % kSlots is free again
+      if (d.rel >= 0) {
+        for (unsigned it = 0; !finished_upto(d.rel); ++it) {
+          if (it > kSpinLimit) { err[0] = 5u; break; }
+          finish_upto(k - kSync, false);
+          finish_upto(d.rel, false);
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      const bool coherent = d.dep >= 0;
+      if (coherent) {
+        if (d.dep % kSync == me) finish_upto(d.dep, true);
+        for (unsigned it = 0;
+             __hip_atomic_load(&done[d.dep], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+             (unsigned)nwg;
+             ++it) {
+          if (it > kSpinLimit) { err[0] = 2u; break; }
+          finish_upto(k - kSync, false);
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      // X rows m < M: lane takes (m, g) pairs; bias terms for rows M..7 are zero
+      const __amdgpu_buffer_rsrc_t rx =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(d.X), 0, 0x7FFFFFFF, kRsrcFlags);
+      const Q4_GLOBAL u32x4_g* X = (const Q4_GLOBAL u32x4_g*)d.X;
+      uint4* xs = reinterpret_cast<uint4*>(lds + d.xoff);
+      float* cs = reinterpret_cast<float*>(lds + d.xoff + corr_off(M, G));
+      for (int e = lane; e < 8 * G; e += 64) {
+        const int g = e >> 3, m = e & 7;
+        float se = 0.f, so = 0.f;
+        if (m < M) {
+          uint4 v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int i = (m * G + g) * 4 + c;
+            u32x4_g tv;
+            if (coherent)
+              tv = __builtin_amdgcn_raw_buffer_load_b128(rx, 16 * i, 0, kCoherent);
+            else
+              tv = X[i];
+            v[c] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            xs[(g * 4 + c) * M + m] = pair_order(v[c]);
+            const uint32_t wv[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const h2_t p = bits<h2_t>(wv[h]);
+              se += (float)p[0];
+              so += (float)p[1];
+            }
+          }
+        }
+        cs[g * 8 + m] = -__builtin_fmaf(1031.0f, se, 71.0f * so);
+      }
+      wait_lds();
+      if (lane == 0) lds_store(&sh.x_ready[k % kSlots], k);
+    }
+    finish_upto(n - 1, true);
+    if (me == 0) {
+      for (unsigned it = 0; !complete(n - 1); ++it) {
+        if (it > kSpinLimit) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (lane == 0) {
+        const int e = lds_load(&sh.err);
+        if (e) err[0] = (unsigned)e;
+      }
+    }
+  } else {
+    // ---------------------------------------------------------- compute waves
+    const int cw = wave - kSync;
+    const int c = lane >> 4, r = lane & 15;
+    uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, e_lo = 0x64006400u, e_hi = 0x54005400u;
+    asm volatile("" : "+v"(m_lo), "+v"(m_hi));
+    asm volatile("" : "+s"(e_lo), "+s"(e_hi));
+    struct Cursor {
+      TileDesc d;
+      int j, t, t_end, row0;     // GEMV, next tile, end tile, first row of the workgroup
+    } cu;
+    int base = 0;
+    auto enter = [&](int j) {
+      for (; j < n; ++j) {
+        const TileDesc d = read_desc(D + j);
+        const int t0 = tile_of(d.tbase, d.trem, wg), t1 = tile_of(d.tbase, d.trem, wg + 1);
+        int off = cw - base;
+        if (off < 0) off += kCompute;
+        base = (base + (t1 - t0)) % kCompute;
+        if (t0 + off < t1) {
+          cu.d = d;
+          cu.j = j;
+          cu.t = t0 + off;
+          cu.t_end = t1;
+          cu.row0 = t0 * 16;
+          return;
+        }
+      }
+      cu.j = n;
+    };
+    enter(0);
+    auto wait_x = [&](int j) {
+      for (unsigned it = 0; lds_load(&sh.x_ready[j % kSlots]) != j; ++it) {
+        if (it > kSpinLimit) {
+          lds_store(&sh.err, 3);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    };
+    int cur = 0;
+    auto signal_upto = [&](int j) {
+      for (; cur < j; ++cur) {
+        wait_x(cur);
+        wait_lds();
+        if (lane == 0) __hip_atomic_fetch_add(&sh.local_done[cur % kSlots], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    };
+
+    while (cu.j < n) {
+      const TileDesc d = cu.d;
+      const int j = cu.j, G = d.G, tile = cu.t;
+      const int tr0 = tile * 16;                      // first row of the tile
+      const uint64_t left = (uint64_t)(d.N - tr0) * (uint64_t)G;
+      const uint32_t nw = left * 16 < 0xFFFFFFF0ull ? (uint32_t)(left * 16) : 0xFFFFFFF0u;
+      const uint32_t ns = left * 2 < 0xFFFFFFF0ull ? (uint32_t)(left * 2) : 0xFFFFFFF0u;
+      const __amdgpu_buffer_rsrc_t bw = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint4*>((const uint4*)(d.W + (int64_t)tr0 * G)), 0, (int)nw, kRsrcFlags);
+      const __amdgpu_buffer_rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>((const uint16_t*)(d.S + (int64_t)tr0 * G)), 0, (int)ns,
+          kRsrcFlags);
+      // rows past the matrix end read zero: only the per-lane offset is range-checked,
+      // and a row past the end is past the end at every chunk
+      const int vo_w = (r * G + c) * 16, vo_s = r * G * 2;
+      const int nch = G / 4;
+      const int xo = d.xoff, co = d.xoff + corr_off(M, G);
+      const int rows = rows_of(d.tbase, d.trem);
+      const int wrow0 = cu.row0;
+      // advance the cursor before the loads are consumed
+      cu.t += kCompute;
+      if (cu.t >= cu.t_end) enter(cu.j + 1);
+
+      f4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ch0 = 0; ch0 < nch; ch0 += kChunks) {
+        uint4 w[kChunks];
+        u32x2_g s[kChunks];
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+          const int ch = ch0 + q < nch ? ch0 + q : nch - 1;   // past the row: re-read
+          const int so = __builtin_amdgcn_readfirstlane(ch);
+          const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, vo_w, so * 64, kNonTemporal);
+          w[q] = make_uint4(v[0], v[1], v[2], v[3]);
+          s[q] = __builtin_amdgcn_raw_buffer_load_b64(bs, vo_s, so * 8, 0);
+        }
+        if (ch0 == 0) {
+          signal_upto(j);
+          wait_x(j);
+        }
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+          if (ch0 + q < nch) {
+            const int g0 = (ch0 + q) * 4;
+            uint32_t v[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+            transpose4(v);                      // v[t]: word c of group g0 + t, row r
+            const uint32_t sc[4] = {s[q][0] & 0xFFFFu, s[q][0] >> 16, s[q][1] & 0xFFFFu,
+                                    s[q][1] >> 16};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int g = g0 + t;
+              const uint32_t x8 = v[t] >> 8;
+              const uint4 bq = make_uint4((v[t] & m_lo) | e_lo, (v[t] & m_hi) | e_hi,
+                                          (x8 & m_lo) | e_lo, (x8 & m_hi) | e_hi);
+              uint4 a = make_uint4(0u, 0u, 0u, 0u);
+              if (r < M) a = *reinterpret_cast<const uint4*>(lds + xo + ((g * 4 + c) * M + r) * 16);
+              f4_t cin = {0.f, 0.f, 0.f, 0.f};
+              if (c < 2) cin = *reinterpret_cast<const f4_t*>(lds + co + g * 32 + c * 16);
+              const f4_t dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits<h8_t>(a), bits<h8_t>(bq),
+                                                                    cin, 0, 0, 0);
+              const float sv = (float)bits<_Float16>((uint16_t)sc[t]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sv, dd[e], acc[e]);
+            }
+          }
+        }
+      }
+      // lane (c, r) holds rows m = 4c + e of column n = tr0 + r
+      if (c < 2 && tr0 + r < d.N) {
+        uint16_t* yb = reinterpret_cast<uint16_t*>(lds + xo + ybuf_off(M, G));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 4 * c + e;
+          if (m < M) yb[m * rows + (tr0 + r - wrow0)] = bits<uint16_t>((_Float16)acc[e]);
+        }
+      }
+    }
+    signal_upto(n);
+  }
+
+  // leave the counters zeroed for the next call (the last workgroup clears them)
+  __syncthreads();
+  if (wave == 0) {
+    unsigned old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(done + n, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == (unsigned)nwg - 1u) {
+      for (int i = lane; i <= n; i += 64)
+        __hip_atomic_store(done + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__global__ void k_zero_m(unsigned* __restrict__ p, int count) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t n, int M,
+                         bool ordered) {
+  MStepPlan p;
+  if (n < 1 || M < 2 || M > 8) return p;
+  p.grid = dev.cus;
+  p.M = M;
+  p.desc.resize((size_t)n);
+  const size_t cap = (size_t)dev.lds_per_block - 1024;   // static LDS and margin
+  std::vector<size_t> off((size_t)n), size((size_t)n);
+  size_t cur = 0;
+  for (int64_t k = 0; k < n; ++k) {
+    const StepLayer& L = layers[k];
+    if (L.K % 128 || L.K > 8192 || L.N >= (1 << 24)) return p;
+    if (reinterpret_cast<uintptr_t>(L.scales) % 8) return p;   // 8-byte scale loads
+    const int G = (int)(L.K / 32);
+    const int tiles = (int)((L.N + 15) / 16);
+    MStepDesc& s = p.desc[(size_t)k];
+    s.W = reinterpret_cast<const uint4*>(L.words);
+    s.S = L.scales;
+    s.X = reinterpret_cast<const uint4*>(L.x);
+    s.Y = L.y;
+    s.N = (int)L.N;
+    s.G = G;
+    s.tbase = tiles / p.grid;
+    s.trem = tiles % p.grid;
+    s.dep = -1;
+    s.signal = 0;
+    const size_t rows = (size_t)(s.tbase + (s.trem > 0)) * 16;
+    const size_t sz = (size_t)M * G * 64 + (size_t)G * 32 + ((rows * M * 2 + 15) & ~(size_t)15);
+    if (sz > cap) return p;
+    if (cur + sz > cap) cur = 0;
+    off[(size_t)k] = cur;
+    size[(size_t)k] = sz;
+    s.xoff = (int)cur;
+    cur += sz;
+    s.rel = -1;
+    for (int64_t i = k - 1; i >= 0; --i) {     // latest earlier user of the space
+      if (off[(size_t)i] < cur && cur - sz < off[(size_t)i] + size[(size_t)i]) {
+        s.rel = (int)i;
+        break;
+      }
+    }
+  }
+  auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+  };
+  for (int64_t k = 1; k < n; ++k) {
+    int dep = -1;
+    if (ordered) {
+      dep = (int)k - 1;
+    } else {
+      const StepLayer& Lk = layers[k];
+      for (int64_t i = k - 1; i >= 0 && dep < 0; --i) {
+        const StepLayer& Li = layers[i];
+        const int64_t yi = 2 * M * Li.N, xk = 2 * M * Lk.K, yk = 2 * M * Lk.N;
+        if (overlap(Li.y, yi, Lk.x, xk) || overlap(Li.y, yi, Lk.y, yk) ||
+            overlap(Li.x, 2 * M * Li.K, Lk.y, yk))
+          dep = (int)i;
+      }
+    }
+    p.desc[(size_t)k].dep = dep;
+    if (dep >= 0) {
+      p.desc[(size_t)dep].signal = 1;
+      p.cross_wg = true;
+    }
+  }
+  p.lds_bytes = cap;
+  p.counters = (int)n + 4;
+  p.ok = true;
+  return p;
+}
+
+size_t step_mfma_workspace_bytes(const MStepPlan& p) {
+  return ((size_t)p.counters * sizeof(unsigned) + 255) & ~(size_t)255;
+}
+
+hipError_t step_mfma_occupancy(const MStepPlan& p, int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks_per_cu, reinterpret_cast<const void*>(k_step_mfma), kStepThreads, p.lds_bytes);
+}
+
+hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc, void* ws,
+                            bool ws_clean, hipStream_t s) {
+  unsigned* done = static_cast<unsigned*>(ws);
+  unsigned* err = done + (p.counters - 1);
+  if (!ws_clean) {
+    hipLaunchKernelGGL(k_zero_m, dim3(1), dim3(256), 0, s, done, p.counters);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_step_mfma),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)p.lds_bytes))
+    return e;
+  int n = (int)p.desc.size(), M = p.M;
+  if (p.cross_wg) {
+    void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&M, (void*)&done, (void*)&err};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_step_mfma), dim3(p.grid),
+                                      dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
+  }
+  hipLaunchKernelGGL(k_step_mfma, dim3(p.grid), dim3(kStepThreads), p.lds_bytes, s, dev_desc, n,
+                     M, done, err);
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -178,3 +178,92 @@ def test_workspace_left_clean_and_ws_clean_calls(flags):
     torch.cuda.synchronize()
     for r, d in zip(ref, descs):
         assert np.array_equal(r, host_half(d[3]))
+
+
+def _m_chain(prefix, M, dims):
+    x = dev_half(synth.activations(f"{prefix}/x", 0, M * dims[0]).reshape(M, dims[0]))
+    descs, mats = [], []
+    for i in range(len(dims) - 1):
+        m, W, S = mat(f"{prefix}/{i}", dims[i + 1], dims[i], chain=True)
+        y = torch.full((M, dims[i + 1]), float("nan"), dtype=torch.float16, device="cuda")
+        descs.append((W, S, x, y))
+        mats.append(m)
+        x = y
+    return descs, mats
+
+
+@pytest.mark.parametrize("M", [2, 3, 5, 8])
+@pytest.mark.parametrize("flags", [0, q4.STEP_ORDERED], ids=["hazards", "ordered"])
+def test_small_m_dependent_chain(M, flags):
+    """M rows per GEMV in one persistent kernel: each descriptor reads the previous
+    one's Y; ragged rows (N not a multiple of 16, N < 16) and K from 128 to 8192."""
+    # K must be a multiple of 128 for the persistent path: the ragged sizes are on N
+    dims = [2048, 6144, 2048, 8192, 384, 1024, 128, 2048]
+    descs, mats = _m_chain(f"mchain{M}", M, dims)
+    # ragged N on independent tails that read the chain's last Y
+    x_last = descs[-1][3]
+    for N in (300, 17, 5):
+        m, W, S = mat(f"mchain{M}/tail{N}", N, dims[-1], chain=True)
+        descs.append((W, S, x_last, torch.full((M, N), float("nan"), dtype=torch.float16,
+                                                device="cuda")))
+        mats.append(m)
+    run_m(descs, M, flags)
+    for m, (W, S, X, Y) in zip(mats, descs):
+        y = host_half(Y)
+        assert np.all(np.isfinite(half_f64(y)))
+        assert_gemv_close(y, m.words(), m.scales(), host_half(X))
+
+
+def run_m(descs, M, flags):
+    layers = q4.make_layers(descs)
+    q4.q4_decode_step(layers, M, flags)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [2, 8])
+def test_small_m_matches_batched_calls(M):
+    """The persistent small-M path and one q4_gemv_batched call per GEMV agree
+    within tolerance on an independent list, and the one-kernel-per-GEMV fallback
+    (K not a multiple of 128) is taken for a list that needs it."""
+    shapes = [(4096, 2048), (2048, 2048), (12288, 2048), (2048, 6144), (777, 8192), (16, 128)]
+    Ks = sorted({K for _, K in shapes})
+    xs = {K: dev_half(synth.activations(f"mb{M}/x{K}", 0, M * K).reshape(M, K)) for K in Ks}
+    descs, mats = [], []
+    for i, (N, K) in enumerate(shapes):
+        m, W, S = mat(f"mb{M}/{i}", N, K)
+        descs.append((W, S, xs[K], torch.empty((M, N), dtype=torch.float16, device="cuda")))
+        mats.append(m)
+    run_m(descs, M, 0)
+    for m, (W, S, X, Y) in zip(mats, descs):
+        ref = q4.q4_gemv_batched(W, S, X)
+        torch.cuda.synchronize()
+        assert_gemv_close(host_half(Y), m.words(), m.scales(), host_half(X))
+        assert_gemv_close(host_half(ref), m.words(), m.scales(), host_half(X))
+    # a K that is not a multiple of 128 sends the whole list one kernel per GEMV
+    m, W, S = mat(f"mb{M}/odd", 64, 544)
+    x = dev_half(synth.activations(f"mb{M}/x544", 0, M * 544).reshape(M, 544))
+    y = torch.empty((M, 64), dtype=torch.float16, device="cuda")
+    run_m(descs + [(W, S, x, y)], M, 0)
+    assert_gemv_close(host_half(y), m.words(), m.scales(), host_half(x))
+
+
+def test_small_m_workspace_left_clean():
+    M = 8
+    descs, mats = _m_chain("mclean", M, [2048, 6144, 2048, 8192, 2048])
+    layers = q4.make_layers(descs)
+    need = q4.q4_decode_step_workspace_bytes(layers, M, 0)
+    ws = torch.full((need,), 0x33, dtype=torch.uint8, device="cuda")
+    q4.q4_decode_step(layers, M, 0, ws=ws)
+    torch.cuda.synchronize()
+    ref = [host_half(d[3]) for d in descs]
+    n = len(descs)
+    assert not ws[: 4 * (n + 1)].view(torch.int32).cpu().numpy().any()
+    for _ in range(3):
+        for d in descs:
+            d[3].fill_(float("nan"))
+        q4.q4_decode_step(layers, M, q4.STEP_WS_CLEAN, ws=ws)
+        torch.cuda.synchronize()
+        for r, d in zip(ref, descs):
+            assert np.array_equal(r, host_half(d[3]))
+    for m, (W, S, X, Y) in zip(mats, descs):
+        assert_gemv_close(host_half(Y), m.words(), m.scales(), host_half(X))
