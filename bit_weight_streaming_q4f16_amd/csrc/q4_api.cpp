@@ -350,10 +350,15 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
       if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_mfma_workspace_bytes(p)))
         return rc;
       hipError_t e = hipSuccess;
-      const void* table = device_table(p.desc.data(), p.desc.size() * sizeof(q4::MStepDesc),
-                                       d->id, s, &e);
+      const size_t db = p.desc.size() * sizeof(q4::MStepDesc);
+      std::vector<uint8_t> host(db + p.ranges.size() * sizeof(int));
+      std::memcpy(host.data(), p.desc.data(), db);
+      if (!p.ranges.empty())
+        std::memcpy(host.data() + db, p.ranges.data(), p.ranges.size() * sizeof(int));
+      const void* table = device_table(host.data(), host.size(), d->id, s, &e);
       if (!table) return device_error(e, "q4_decode_step: descriptor table");
-      e = q4::launch_step_mfma(p, static_cast<const q4::MStepDesc*>(table), ws,
+      const int4* ranges = reinterpret_cast<const int4*>(static_cast<const uint8_t*>(table) + db);
+      e = q4::launch_step_mfma(p, static_cast<const q4::MStepDesc*>(table), ranges, ws,
                                (flags & Q4_STEP_WS_CLEAN) != 0, s);
       return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
     }

@@ -15,7 +15,9 @@ struct MStepDesc {
   uint16_t* Y;           // Y [M][N]
   int N, G;
   int tbase, trem;       // 16-row tiles split over the grid: workgroup w owns tiles from
-                         // w * tbase + min(w, trem), the first trem get one more
+                         // w * tbase + min(w, trem), the first trem get one more; or,
+                         // with trem < 0 (range mode), tbase is the GEMV's first tile
+                         // among the tiles of all GEMVs laid end to end
   int dep, signal;       // as in StepDesc
   int xoff;              // byte offset of the GEMV's LDS region (X, bias terms, y rows)
   int rel;               // GEMV whose LDS region overlaps this one (-1: none): it must
@@ -29,6 +31,9 @@ struct MStepPlan {
   int grid = 0, M = 0, counters = 0;
   size_t lds_bytes = 0;
   std::vector<MStepDesc> desc;
+  // range mode (no dependencies): per workgroup {first tile, end tile, first GEMV,
+  // last GEMV} of the tiles of all GEMVs laid end to end; empty otherwise
+  std::vector<int> ranges;
 };
 
 // Persistent kernel for 2 <= M <= 8: every K a multiple of 128 and at most 8192,
@@ -37,7 +42,7 @@ MStepPlan plan_step_mfma(const DeviceInfo& d, const StepLayer* layers, int64_t n
                          bool ordered);
 size_t step_mfma_workspace_bytes(const MStepPlan& p);
 hipError_t step_mfma_occupancy(const MStepPlan& p, int* blocks_per_cu);
-hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc, void* ws,
-                            bool ws_clean, hipStream_t s);
+hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc,
+                            const int4* dev_ranges, void* ws, bool ws_clean, hipStream_t s);
 
 }  // namespace q4

@@ -26,6 +26,9 @@
 //    copy finished rows of Y out, publish completion (as in the M = 1 kernel).
 // LDS regions are planned on the host as a ring: a GEMV's region is reused only
 // after the GEMVs that used it before are finished.
+#include <algorithm>
+#include <climits>
+
 #include "q4_step_mfma.h"
 
 namespace q4 {
@@ -129,14 +132,15 @@ __device__ __forceinline__ TileDesc read_desc(const MStepDesc* d) {
 }
 
 // LDS region of a GEMV (byte offsets from xoff): X planes [G][4][M] uint4, then the
-// bias terms [G][8] float, then y [M][rows] fp16 (rows: the most any workgroup owns).
+// bias terms [G][8] float, then y [M][rows] fp16 (rows: this workgroup's rows of the
+// GEMV; the host sizes the region for the most any workgroup has).
 __device__ __forceinline__ int corr_off(int M, int G) { return M * G * 64; }
 __device__ __forceinline__ int ybuf_off(int M, int G) { return M * G * 64 + G * 32; }
-__device__ __forceinline__ int rows_of(int tbase, int trem) { return (tbase + (trem > 0)) * 16; }
 
 __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __restrict__ D, int n,
                                                             int M, unsigned* __restrict__ done,
-                                                            unsigned* __restrict__ err) {
+                                                            unsigned* __restrict__ err,
+                                                            const int4* __restrict__ ranges) {
   extern __shared__ uint4 smem[];
   __shared__ Shared sh;
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
@@ -151,22 +155,47 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
   if (threadIdx.x == 0) sh.err = 0;
   __syncthreads();
 
+  // This workgroup's share (as in the M = 1 kernel): in range mode the tiles
+  // [ra, rb) of all GEMVs laid end to end, lying in GEMVs j0..j1; otherwise an
+  // even share of every GEMV.  Slots, owners and counters are indexed from j0.
+  int ra = 0, rb = 0, j0 = 0, j1 = n - 1;
+  if (ranges) {
+    const int4 rr = ranges[wg];
+    ra = __builtin_amdgcn_readfirstlane(rr.x);
+    rb = __builtin_amdgcn_readfirstlane(rr.y);
+    j0 = __builtin_amdgcn_readfirstlane(rr.z);
+    j1 = __builtin_amdgcn_readfirstlane(rr.w);
+  }
+  // tiles [lo, hi) of a GEMV in this workgroup: tbase is the GEMV's first tile in
+  // the concatenation when trem < 0 (range mode), else the even split
+  auto tile_range = [&](int tbase, int trem, int N, int& lo, int& hi) {
+    if (trem < 0) {
+      const int tiles = (N + 15) / 16;
+      lo = min(max(ra - tbase, 0), tiles);
+      hi = min(max(rb - tbase, 0), tiles);
+    } else {
+      lo = tile_of(tbase, trem, wg);
+      hi = tile_of(tbase, trem, wg + 1);
+    }
+  };
+
   auto complete = [&](int i) {        // every compute wave is past GEMV i here
-    return (unsigned)lds_load(&sh.local_done[i % kSlots]) >=
-           (unsigned)kCompute * (unsigned)(i / kSlots + 1);
+    return (unsigned)lds_load(&sh.local_done[(i - j0) % kSlots]) >=
+           (unsigned)kCompute * (unsigned)((i - j0) / kSlots + 1);
   };
 
   if (wave < kSync) {
     // ------------------------------------------------------------ sync waves
     const int me = wave;
-    int next_fin = me;
+    int next_fin = j0 + me;
     auto finish_one = [&](int i) {
       const MStepDesc& d = D[i];
-      const int t0 = tile_of(d.tbase, d.trem, wg), t1 = tile_of(d.tbase, d.trem, wg + 1);
+      int t0, t1;
+      tile_range(d.tbase, d.trem, d.N, t0, t1);
       const int r0 = t0 * 16;
       int r1 = t1 * 16;
       if (r1 > d.N) r1 = d.N;
-      const int rows = rows_of(d.tbase, d.trem), nr = r1 - r0;
+      const int rows = (t1 - t0) * 16, nr = r1 - r0;
       const uint16_t* yb = reinterpret_cast<const uint16_t*>(lds + d.xoff + ybuf_off(M, d.G));
       if (nr > 0) {
         if (!d.signal) {
@@ -194,7 +223,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       if (lane == 0) lds_store(&sh.fin[me], i);
     };
     auto finish_upto = [&](int last, bool block) {
-      while (next_fin <= last && next_fin < n) {
+      while (next_fin <= last && next_fin <= j1) {
         if (!complete(next_fin)) {
           if (!block) return;
           for (unsigned it = 0; !complete(next_fin); ++it) {
@@ -206,19 +235,21 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
         next_fin += kSync;
       }
     };
-    // every GEMV <= i finished (copied out) by its owner
+    // every GEMV <= i finished (copied out) by its owner; this workgroup has no
+    // part in GEMVs before j0
     auto finished_upto = [&](int i) {
       for (int o = 0; o < kSync; ++o) {
-        const int last = i - ((i - o) % kSync + kSync) % kSync;   // largest <= i owned by o
-        if (last >= 0 && lds_load(&sh.fin[o]) < last) return false;
+        const int r = i - j0;
+        const int last = r - ((r - o) % kSync + kSync) % kSync;   // largest <= r owned by o
+        if (last >= 0 && lds_load(&sh.fin[o]) < j0 + last) return false;
       }
       return true;
     };
-    for (int k = me; k < n; k += kSync) {
+    for (int k = j0 + me; k <= j1; k += kSync) {
       const MStepDesc& d = D[k];
       const int G = d.G;
       finish_upto(k - kSync, false);
-      if (k >= kSlots) finish_upto(k - kSlots, true);   // slot k % kSlots is free again
+      if (k - j0 >= kSlots) finish_upto(k - kSlots, true);   // slot (k - j0) % kSlots is free
       if (d.rel >= 0) {
         for (unsigned it = 0; !finished_upto(d.rel); ++it) {
           if (it > kSpinLimit) { err[0] = 5u; break; }
@@ -229,7 +260,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       }
       const bool coherent = d.dep >= 0;
       if (coherent) {
-        if (d.dep % kSync == me) finish_upto(d.dep, true);
+        if ((d.dep - j0) % kSync == me) finish_upto(d.dep, true);
         for (unsigned it = 0;
              __hip_atomic_load(&done[d.dep], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
              (unsigned)nwg;
@@ -275,11 +306,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
         cs[g * 8 + m] = -__builtin_fmaf(1031.0f, se, 71.0f * so);
       }
       wait_lds();
-      if (lane == 0) lds_store(&sh.x_ready[k % kSlots], k);
+      if (lane == 0) lds_store(&sh.x_ready[(k - j0) % kSlots], k);
     }
-    finish_upto(n - 1, true);
+    finish_upto(j1, true);
     if (me == 0) {
-      for (unsigned it = 0; !complete(n - 1); ++it) {
+      for (unsigned it = 0; j0 <= j1 && !complete(j1); ++it) {
         if (it > kSpinLimit) break;
         __builtin_amdgcn_s_sleep(8);
       }
@@ -298,12 +329,14 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
     struct Cursor {
       TileDesc d;
       int j, t, t_end, row0;     // GEMV, next tile, end tile, first row of the workgroup
+      int rows;                  // rows of the workgroup's y buffer for the GEMV
     } cu;
     int base = 0;
     auto enter = [&](int j) {
-      for (; j < n; ++j) {
+      for (; j <= j1; ++j) {
         const TileDesc d = read_desc(D + j);
-        const int t0 = tile_of(d.tbase, d.trem, wg), t1 = tile_of(d.tbase, d.trem, wg + 1);
+        int t0, t1;
+        tile_range(d.tbase, d.trem, d.N, t0, t1);
         int off = cw - base;
         if (off < 0) off += kCompute;
         base = (base + (t1 - t0)) % kCompute;
@@ -313,14 +346,15 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
           cu.t = t0 + off;
           cu.t_end = t1;
           cu.row0 = t0 * 16;
+          cu.rows = (t1 - t0) * 16;
           return;
         }
       }
-      cu.j = n;
+      cu.j = j1 + 1;
     };
-    enter(0);
+    enter(j0);
     auto wait_x = [&](int j) {
-      for (unsigned it = 0; lds_load(&sh.x_ready[j % kSlots]) != j; ++it) {
+      for (unsigned it = 0; lds_load(&sh.x_ready[(j - j0) % kSlots]) != j; ++it) {
         if (it > kSpinLimit) {
           lds_store(&sh.err, 3);
           break;
@@ -328,17 +362,17 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
         __builtin_amdgcn_s_sleep(1);
       }
     };
-    int cur = 0;
+    int cur = j0;
     auto signal_upto = [&](int j) {
       for (; cur < j; ++cur) {
         wait_x(cur);
         wait_lds();
-        if (lane == 0) __hip_atomic_fetch_add(&sh.local_done[cur % kSlots], 1, __ATOMIC_RELAXED,
+        if (lane == 0) __hip_atomic_fetch_add(&sh.local_done[(cur - j0) % kSlots], 1, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     };
 
-    while (cu.j < n) {
+    while (cu.j <= j1) {
       const TileDesc d = cu.d;
       const int j = cu.j, G = d.G, tile = cu.t;
       const int tr0 = tile * 16;                      // first row of the tile
@@ -355,7 +389,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       const int vo_w = (r * G + c) * 16, vo_s = r * G * 2;
       const int nch = G / 4;
       const int xo = d.xoff, co = d.xoff + corr_off(M, G);
-      const int rows = rows_of(d.tbase, d.trem);
+      const int rows = cu.rows;
       const int wrow0 = cu.row0;
       // advance the cursor before the loads are consumed
       cu.t += kCompute;
@@ -414,7 +448,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
         }
       }
     }
-    signal_upto(n);
+    signal_upto(j1 + 1);
   }
 
   // leave the counters zeroed for the next call (the last workgroup clears them)
@@ -445,41 +479,22 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
   p.grid = dev.cus;
   p.M = M;
   p.desc.resize((size_t)n);
-  const size_t cap = (size_t)dev.lds_per_block - 1024;   // static LDS and margin
-  std::vector<size_t> off((size_t)n), size((size_t)n);
-  size_t cur = 0;
+  std::vector<int64_t> tiles((size_t)n);
   for (int64_t k = 0; k < n; ++k) {
     const StepLayer& L = layers[k];
     if (L.K % 128 || L.K > 8192 || L.N >= (1 << 24)) return p;
     if (reinterpret_cast<uintptr_t>(L.scales) % 8) return p;   // 8-byte scale loads
-    const int G = (int)(L.K / 32);
-    const int tiles = (int)((L.N + 15) / 16);
     MStepDesc& s = p.desc[(size_t)k];
     s.W = reinterpret_cast<const uint4*>(L.words);
     s.S = L.scales;
     s.X = reinterpret_cast<const uint4*>(L.x);
     s.Y = L.y;
     s.N = (int)L.N;
-    s.G = G;
-    s.tbase = tiles / p.grid;
-    s.trem = tiles % p.grid;
+    s.G = (int)(L.K / 32);
     s.dep = -1;
     s.signal = 0;
-    const size_t rows = (size_t)(s.tbase + (s.trem > 0)) * 16;
-    const size_t sz = (size_t)M * G * 64 + (size_t)G * 32 + ((rows * M * 2 + 15) & ~(size_t)15);
-    if (sz > cap) return p;
-    if (cur + sz > cap) cur = 0;
-    off[(size_t)k] = cur;
-    size[(size_t)k] = sz;
-    s.xoff = (int)cur;
-    cur += sz;
     s.rel = -1;
-    for (int64_t i = k - 1; i >= 0; --i) {     // latest earlier user of the space
-      if (off[(size_t)i] < cur && cur - sz < off[(size_t)i] + size[(size_t)i]) {
-        s.rel = (int)i;
-        break;
-      }
-    }
+    tiles[(size_t)k] = (L.N + 15) / 16;
   }
   auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -505,6 +520,94 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
       p.cross_wg = true;
     }
   }
+  const size_t cap = (size_t)dev.lds_per_block - 1024;   // static LDS and margin
+  // the most rows any workgroup holds of each GEMV, per mode
+  std::vector<int64_t> rows((size_t)n);
+  // LDS regions as a ring in list order; rel: the latest earlier user of the space
+  auto place = [&]() {
+    std::vector<size_t> off((size_t)n), size((size_t)n);
+    size_t cur = 0;
+    for (int64_t k = 0; k < n; ++k) {
+      MStepDesc& s = p.desc[(size_t)k];
+      const size_t sz = (size_t)M * s.G * 64 + (size_t)s.G * 32 +
+                        (((size_t)rows[(size_t)k] * M * 2 + 15) & ~(size_t)15);
+      if (sz > cap) return false;
+      if (cur + sz > cap) cur = 0;
+      off[(size_t)k] = cur;
+      size[(size_t)k] = sz;
+      s.xoff = (int)cur;
+      cur += sz;
+      s.rel = -1;
+      for (int64_t i = k - 1; i >= 0; --i) {
+        if (off[(size_t)i] < cur && cur - sz < off[(size_t)i] + size[(size_t)i]) {
+          s.rel = (int)i;
+          break;
+        }
+      }
+    }
+    return true;
+  };
+  // Range mode (no dependencies): each workgroup takes one contiguous stretch of
+  // the 16-row tiles of all GEMVs laid end to end, balanced by weight bytes.
+  if (!p.cross_wg) {
+    std::vector<int64_t> first((size_t)n + 1), cum((size_t)n + 1);
+    for (int64_t k = 0; k < n; ++k) {
+      const int64_t tb = 16 * (int64_t)p.desc[(size_t)k].G * 18;
+      first[(size_t)k + 1] = first[(size_t)k] + tiles[(size_t)k];
+      cum[(size_t)k + 1] = cum[(size_t)k] + tb * tiles[(size_t)k];
+    }
+    const int64_t total = cum[(size_t)n];
+    std::vector<int64_t> cut((size_t)p.grid + 1);
+    for (int w = 0; w <= p.grid; ++w) {
+      const int64_t target = (int64_t)(((__int128)total * w) / p.grid);
+      int64_t k = std::upper_bound(cum.begin(), cum.end(), target) - cum.begin() - 1;
+      if (k >= n) k = n - 1;
+      const int64_t tb = 16 * (int64_t)p.desc[(size_t)k].G * 18;
+      int64_t t = (target - cum[(size_t)k]) / tb;
+      if (t > tiles[(size_t)k]) t = tiles[(size_t)k];
+      cut[(size_t)w] = w == p.grid ? first[(size_t)n] : first[(size_t)k] + t;
+    }
+    auto gemv_of = [&](int64_t t) {
+      return (int)(std::upper_bound(first.begin(), first.end(), t) - first.begin() - 1);
+    };
+    std::vector<int> ranges((size_t)p.grid * 4);
+    std::fill(rows.begin(), rows.end(), 16);
+    for (int w = 0; w < p.grid; ++w) {
+      const int64_t a = cut[(size_t)w], b = cut[(size_t)w + 1];
+      int j0 = 1, j1 = 0;
+      if (b > a) {
+        j0 = gemv_of(a);
+        j1 = gemv_of(b - 1);
+        for (int j = j0; j <= j1; ++j) {
+          const int64_t lo = std::max<int64_t>(a - first[(size_t)j], 0);
+          const int64_t hi = std::min<int64_t>(b - first[(size_t)j], tiles[(size_t)j]);
+          rows[(size_t)j] = std::max<int64_t>(rows[(size_t)j], (hi - lo) * 16);
+        }
+      }
+      ranges[(size_t)w * 4 + 0] = (int)a;
+      ranges[(size_t)w * 4 + 1] = (int)b;
+      ranges[(size_t)w * 4 + 2] = j0;
+      ranges[(size_t)w * 4 + 3] = j1;
+    }
+    if (first[(size_t)n] < INT32_MAX && place()) {
+      for (int64_t k = 0; k < n; ++k) {
+        p.desc[(size_t)k].tbase = (int)first[(size_t)k];
+        p.desc[(size_t)k].trem = -1;
+      }
+      p.ranges = std::move(ranges);
+      p.lds_bytes = cap;
+      p.counters = (int)n + 4;
+      p.ok = true;
+      return p;
+    }
+  }
+  for (int64_t k = 0; k < n; ++k) {
+    MStepDesc& s = p.desc[(size_t)k];
+    s.tbase = (int)(tiles[(size_t)k] / p.grid);
+    s.trem = (int)(tiles[(size_t)k] % p.grid);
+    rows[(size_t)k] = (int64_t)(s.tbase + (s.trem > 0)) * 16;
+  }
+  if (!place()) return p;
   p.lds_bytes = cap;
   p.counters = (int)n + 4;
   p.ok = true;
@@ -520,8 +623,8 @@ hipError_t step_mfma_occupancy(const MStepPlan& p, int* blocks_per_cu) {
       blocks_per_cu, reinterpret_cast<const void*>(k_step_mfma), kStepThreads, p.lds_bytes);
 }
 
-hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc, void* ws,
-                            bool ws_clean, hipStream_t s) {
+hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc,
+                            const int4* dev_ranges, void* ws, bool ws_clean, hipStream_t s) {
   unsigned* done = static_cast<unsigned*>(ws);
   unsigned* err = done + (p.counters - 1);
   if (!ws_clean) {
@@ -533,13 +636,15 @@ hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc, void*
                                          (int)p.lds_bytes))
     return e;
   int n = (int)p.desc.size(), M = p.M;
+  const int4* rg = p.ranges.empty() ? nullptr : dev_ranges;
   if (p.cross_wg) {
-    void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&M, (void*)&done, (void*)&err};
+    void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&M, (void*)&done, (void*)&err,
+                    (void*)&rg};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_step_mfma), dim3(p.grid),
                                       dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
   }
   hipLaunchKernelGGL(k_step_mfma, dim3(p.grid), dim3(kStepThreads), p.lds_bytes, s, dev_desc, n,
-                     M, done, err);
+                     M, done, err, rg);
   return hipGetLastError();
 }
 
