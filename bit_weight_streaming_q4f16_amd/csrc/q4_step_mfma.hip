@@ -18,7 +18,9 @@
 //    groups: per lane one dwordx4 (group c of row r, for lane = 16c + r) and one
 //    8-byte load of the row's four scales; a 4 x 4 exchange between lanes r,
 //    r + 16, r + 32, r + 48 leaves word c of each of the four groups in lane
-//    (c, r), which is the B layout.  X and the bias terms come from LDS; results
+//    (c, r), which is the B layout.  Where G is a multiple of 8 (and the scales
+//    16-byte aligned) the same sixteen groups come as pairs of adjacent groups per
+//    lane, so each row is read in 128-byte runs.  X and the bias terms come from LDS; results
 //    go to LDS.
 //  * 4 sync waves, each owning every 4th GEMV: stage its X (pair-ordered, with the
 //    bias terms) into the GEMV's LDS region once the GEMVs it depends on are
@@ -51,7 +53,7 @@ constexpr int kWaves = kStepThreads / 64;   // 16
 constexpr int kSync = 4;
 constexpr int kCompute = kWaves - kSync;
 constexpr int kSlots = 8;                   // x_ready slots: GEMVs up to 8 apart in flight
-constexpr int kChunks = 8;                  // chunks (of four groups) per burst
+constexpr int kChunks = 4;                  // chunks (of four groups) per burst
 constexpr unsigned kSpinLimit = 1u << 24;
 constexpr int kCoherent = 1 | 16;           // sc0 | sc1
 constexpr int kNonTemporal = 2;
@@ -388,6 +390,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       // and a row past the end is past the end at every chunk
       const int vo_w = (r * G + c) * 16, vo_s = r * G * 2;
       const int nch = G / 4;
+      // 16-byte scale loads need G % 8 == 0 and 16-byte aligned scales
+      const bool wide = G % 8 == 0 && (reinterpret_cast<uintptr_t>(d.S) & 15u) == 0;
       const int xo = d.xoff, co = d.xoff + corr_off(M, G);
       const int rows = cu.rows;
       const int wrow0 = cu.row0;
@@ -396,44 +400,87 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       if (cu.t >= cu.t_end) enter(cu.j + 1);
 
       f4_t acc = {0.f, 0.f, 0.f, 0.f};
-      for (int ch0 = 0; ch0 < nch; ch0 += kChunks) {
-        uint4 w[kChunks];
-        u32x2_g s[kChunks];
+      // one group of the tile: B from word c of the group in lane (c, r), A = X rows
+      auto group_mma = [&](uint32_t vt, int g, uint32_t sbits) {
+        const uint32_t x8 = vt >> 8;
+        const uint4 bq = make_uint4((vt & m_lo) | e_lo, (vt & m_hi) | e_hi,
+                                    (x8 & m_lo) | e_lo, (x8 & m_hi) | e_hi);
+        uint4 a = make_uint4(0u, 0u, 0u, 0u);
+        if (r < M) a = *reinterpret_cast<const uint4*>(lds + xo + ((g * 4 + c) * M + r) * 16);
+        f4_t cin = {0.f, 0.f, 0.f, 0.f};
+        if (c < 2) cin = *reinterpret_cast<const f4_t*>(lds + co + g * 32 + c * 16);
+        const f4_t dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits<h8_t>(a), bits<h8_t>(bq),
+                                                              cin, 0, 0, 0);
+        const float sv = (float)bits<_Float16>((uint16_t)sbits);
 #pragma unroll
-        for (int q = 0; q < kChunks; ++q) {
-          const int ch = ch0 + q < nch ? ch0 + q : nch - 1;   // past the row: re-read
-          const int so = __builtin_amdgcn_readfirstlane(ch);
-          const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, vo_w, so * 64, kNonTemporal);
-          w[q] = make_uint4(v[0], v[1], v[2], v[3]);
-          s[q] = __builtin_amdgcn_raw_buffer_load_b64(bs, vo_s, so * 8, 0);
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sv, dd[e], acc[e]);
+      };
+      if (wide) {
+        // chunks of eight groups: the four lanes of a row read two adjacent groups
+        // each (128 contiguous bytes of the row per pair of loads) and one 16-byte
+        // load of the row's eight scales; groups are still taken in order
+        const int nch8 = G / 8, vo8 = (r * G + 2 * c) * 16;
+        for (int ch0 = 0; ch0 < nch8; ch0 += kChunks / 2) {
+          uint4 w0[kChunks / 2], w1[kChunks / 2];
+          u32x4_g s8[kChunks / 2];
+#pragma unroll
+          for (int q = 0; q < kChunks / 2; ++q) {
+            const int ch = ch0 + q < nch8 ? ch0 + q : nch8 - 1;   // past the row: re-read
+            const int so = __builtin_amdgcn_readfirstlane(ch);
+            const u32x4_g v0 = __builtin_amdgcn_raw_buffer_load_b128(bw, vo8, so * 128, kNonTemporal);
+            const u32x4_g v1 = __builtin_amdgcn_raw_buffer_load_b128(bw, vo8 + 16, so * 128,
+                                                                    kNonTemporal);
+            w0[q] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+            w1[q] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+            s8[q] = __builtin_amdgcn_raw_buffer_load_b128(bs, vo_s, so * 16, 0);
+          }
+          if (ch0 == 0) {
+            signal_upto(j);
+            wait_x(j);
+          }
+#pragma unroll
+          for (int q = 0; q < kChunks / 2; ++q) {
+            if (ch0 + q < nch8) {
+              const int g0 = (ch0 + q) * 8;
+              uint32_t va[4] = {w0[q].x, w0[q].y, w0[q].z, w0[q].w};
+              uint32_t vb[4] = {w1[q].x, w1[q].y, w1[q].z, w1[q].w};
+              transpose4(va);                   // va[t]: word c of group g0 + 2t, row r
+              transpose4(vb);                   // vb[t]: word c of group g0 + 2t + 1
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const uint32_t sw = s8[q][t];   // scales of groups g0 + 2t and g0 + 2t + 1
+                group_mma(va[t], g0 + 2 * t, sw & 0xFFFFu);
+                group_mma(vb[t], g0 + 2 * t + 1, sw >> 16);
+              }
+            }
+          }
         }
-        if (ch0 == 0) {
-          signal_upto(j);
-          wait_x(j);
-        }
+      } else {
+        for (int ch0 = 0; ch0 < nch; ch0 += kChunks) {
+          uint4 w[kChunks];
+          u32x2_g s[kChunks];
 #pragma unroll
-        for (int q = 0; q < kChunks; ++q) {
-          if (ch0 + q < nch) {
-            const int g0 = (ch0 + q) * 4;
-            uint32_t v[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
-            transpose4(v);                      // v[t]: word c of group g0 + t, row r
-            const uint32_t sc[4] = {s[q][0] & 0xFFFFu, s[q][0] >> 16, s[q][1] & 0xFFFFu,
-                                    s[q][1] >> 16};
+          for (int q = 0; q < kChunks; ++q) {
+            const int ch = ch0 + q < nch ? ch0 + q : nch - 1;   // past the row: re-read
+            const int so = __builtin_amdgcn_readfirstlane(ch);
+            const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, vo_w, so * 64, kNonTemporal);
+            w[q] = make_uint4(v[0], v[1], v[2], v[3]);
+            s[q] = __builtin_amdgcn_raw_buffer_load_b64(bs, vo_s, so * 8, 0);
+          }
+          if (ch0 == 0) {
+            signal_upto(j);
+            wait_x(j);
+          }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int g = g0 + t;
-              const uint32_t x8 = v[t] >> 8;
-              const uint4 bq = make_uint4((v[t] & m_lo) | e_lo, (v[t] & m_hi) | e_hi,
-                                          (x8 & m_lo) | e_lo, (x8 & m_hi) | e_hi);
-              uint4 a = make_uint4(0u, 0u, 0u, 0u);
-              if (r < M) a = *reinterpret_cast<const uint4*>(lds + xo + ((g * 4 + c) * M + r) * 16);
-              f4_t cin = {0.f, 0.f, 0.f, 0.f};
-              if (c < 2) cin = *reinterpret_cast<const f4_t*>(lds + co + g * 32 + c * 16);
-              const f4_t dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits<h8_t>(a), bits<h8_t>(bq),
-                                                                    cin, 0, 0, 0);
-              const float sv = (float)bits<_Float16>((uint16_t)sc[t]);
+          for (int q = 0; q < kChunks; ++q) {
+            if (ch0 + q < nch) {
+              const int g0 = (ch0 + q) * 4;
+              uint32_t v[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+              transpose4(v);                    // v[t]: word c of group g0 + t, row r
+              const uint32_t sc[4] = {s[q][0] & 0xFFFFu, s[q][0] >> 16, s[q][1] & 0xFFFFu,
+                                      s[q][1] >> 16};
 #pragma unroll
-              for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sv, dd[e], acc[e]);
+              for (int t = 0; t < 4; ++t) group_mma(v[t], g0 + t, sc[t]);
             }
           }
         }
