@@ -50,8 +50,8 @@ MODES = {"ordered": 0x2, "hazards": 0x0, "launch_each": 0x1}
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--mode", choices=["ordered", "hazards", "launch_each"], default="hazards",
                     help="ordered: every GEMV waits for its predecessor (a decode step's "
                          "dependency chain); hazards: waits only on shared memory; "
@@ -162,9 +162,10 @@ def main():
         "host_ms_per_step": round(host_ms, 5),
         "setup_s": round(setup_s, 1),
     }
-    # dominant kernel: the persistent step kernel, one launch per step; its
-    # algorithmic bytes per launch are the step's, its duration the event time per
-    # step (which also holds the counter-clearing kernel launched before it)
+    # dominant kernel: the persistent step kernel, one launch per step (its
+    # counters are left zero by the previous call, so nothing else is launched);
+    # its algorithmic bytes per launch are the step's, its duration the event time
+    # per step
     result["us_per_gemv"] = round(ms * 1e3 / len(meta), 3)
     result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
                           "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4),
@@ -176,7 +177,7 @@ def main():
         for mode in MODES:
             if mode == args.mode:
                 continue
-            m_ms, _ = time_mode(mode, max(5, args.steps // 2), 3)
+            m_ms, _ = time_mode(mode, max(5, args.steps // 5), max(3, args.warmup // 4))
             other[mode] = {"ms_per_step": round(m_ms, 5),
                            "gbs": round(step_bytes / (m_ms * 1e-3) / 1e9, 1)}
         result["other_modes"] = other
