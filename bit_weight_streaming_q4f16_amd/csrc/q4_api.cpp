@@ -283,6 +283,21 @@ bool use_persistent(const q4::DeviceInfo& d, const q4::StepPlan& p, int64_t M, u
   return true;
 }
 
+// The register kernel's dependencies with completion counters only (no tagged
+// hand-over), as the LDS-ring kernel keeps them.
+q4::StepPlan counter_plan(const q4::DeviceInfo& d, const std::vector<q4::StepLayer>& sl,
+                          int64_t n, uint32_t flags, std::vector<int>* dep,
+                          std::vector<int>* sig) {
+  q4::StepPlan cp = q4::plan_step(d, sl.data(), n, (flags & Q4_STEP_ORDERED) != 0, false);
+  dep->assign(cp.desc.size(), -1);
+  sig->assign(cp.desc.size(), 0);
+  for (size_t i = 0; i < cp.desc.size(); ++i) {
+    (*dep)[i] = cp.desc[i].dep;
+    (*sig)[i] = (cp.desc[i].flags & q4::kPublish) != 0;
+  }
+  return cp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -310,12 +325,14 @@ size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, 
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
     size_t b = q4::step_workspace_bytes(p);
     if (b > need) need = b;
-    std::vector<int> dep(p.desc.size()), sig(p.desc.size());
-    for (size_t i = 0; i < p.desc.size(); ++i) { dep[i] = p.desc[i].dep; sig[i] = p.desc[i].signal; }
-    if (!p.desc.empty() && (flags & Q4_STEP_LDS_RING)) {
-      q4::DmaPlan dp = q4::plan_step_dma(*d, sl.data(), n_layers, dep, sig);
-      b = q4::step_dma_workspace_bytes(dp);
-      if (b > need) need = b;
+    if (flags & Q4_STEP_LDS_RING) {
+      std::vector<int> dep, sig;
+      q4::StepPlan cp = counter_plan(*d, sl, n_layers, flags, &dep, &sig);
+      if (cp.ok) {
+        q4::DmaPlan dp = q4::plan_step_dma(*d, sl.data(), n_layers, dep, sig);
+        b = q4::step_dma_workspace_bytes(dp);
+        if (b > need) need = b;
+      }
     }
   }
   return need;
@@ -367,12 +384,12 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
     std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
-    if (p.ok && (flags & Q4_STEP_LDS_RING)) {
-      std::vector<int> dep(p.desc.size()), sig(p.desc.size());
-      for (size_t i = 0; i < p.desc.size(); ++i) { dep[i] = p.desc[i].dep; sig[i] = p.desc[i].signal; }
+    if (flags & Q4_STEP_LDS_RING) {
+      std::vector<int> dep, sig;
+      q4::StepPlan cp = counter_plan(*d, sl, n_layers, flags, &dep, &sig);
       q4::DmaPlan dp = q4::plan_step_dma(*d, sl.data(), n_layers, dep, sig);
       int per_cu = 0;
-      if (dp.ok && q4::step_dma_occupancy(dp, &per_cu) == hipSuccess && per_cu >= 1) {
+      if (cp.ok && dp.ok && q4::step_dma_occupancy(dp, &per_cu) == hipSuccess && per_cu >= 1) {
         if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_dma_workspace_bytes(dp)))
           return rc;
         hipError_t e = hipSuccess;

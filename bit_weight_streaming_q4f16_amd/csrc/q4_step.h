@@ -10,7 +10,13 @@ namespace q4 {
 constexpr int kStepThreads = 1024;   // one workgroup of 16 waves per compute unit
 constexpr int kXBufs = 8;            // x buffers: waves may run up to 8 GEMVs apart
 
-// One GEMV as the persistent kernel reads it (device-resident table, 64 bytes).
+// Descriptor flags.
+constexpr int kPublish = 1;  // later descriptors wait for this one's completion counter
+constexpr int kTagOut = 2;   // y also goes to the workspace as epoch-tagged pairs
+constexpr int kTagIn = 4;    // x is read from an earlier descriptor's tagged pairs
+constexpr int kPairs = 8;    // workgroup shares are split in pairs of row-steps (even rows)
+
+// One GEMV as the persistent kernel reads it (device-resident table, 80 bytes).
 struct StepDesc {
   const uint4* W;        // words, one uint4 per 32-weight group: [N][G]
   const uint16_t* S;     // scales [N][G]
@@ -21,11 +27,15 @@ struct StepDesc {
   int16_t C;             // groups per lane (<= 4)
   int steps;             // row-steps: ceil(N / (64 / lanes per row))
   int dep;               // descriptor that must be complete before x is read (-1: none)
-  int signal;            // 1 if a later descriptor waits for this one
-  int sbase, srem;       // workgroup w owns row-steps from w * sbase + min(w, srem):
-                         // steps split evenly over the grid, the first srem get one more
+  int flags;             // kPublish | kTagOut | kTagIn | kPairs
+  int sbase, srem;       // workgroup w owns row-steps from w * sbase + min(w, srem)
+                         // (pairs of row-steps with kPairs): split evenly over the
+                         // grid, the first srem get one more
+  int tag_in;            // kTagIn: workspace byte offset of the tagged pairs x is read from
+  int tag_out;           // kTagOut: workspace byte offset of this GEMV's tagged pairs
+  int pad[2];
 };
-static_assert(sizeof(StepDesc) == 64, "StepDesc layout");
+static_assert(sizeof(StepDesc) == 80, "StepDesc layout");
 
 struct StepLayer {
   const uint32_t* words;
@@ -41,6 +51,8 @@ struct StepPlan {
   int maxG = 0;
   int ybuf_rows = 0;
   int counters = 0;      // completion counters, exit counter, spare, error word
+  size_t tag_base = 0;   // workspace byte offset of the tagged pairs (after the counters)
+  size_t tag_bytes = 0;  // their size (0: no descriptor hands its y over that way)
   bool cross_wg = false; // some descriptor waits for others on every workgroup: all
                          // workgroups must be resident at once (cooperative launch)
   int nx = 0;            // x buffers (kXBufs, or 4 in range mode)
@@ -54,7 +66,8 @@ struct StepPlan {
 
 // ordered: every descriptor waits for its predecessor (a chain of dependent GEMVs);
 // otherwise only for earlier descriptors whose memory it shares.
-StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool ordered);
+StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool ordered,
+                   bool tags = true);
 size_t step_workspace_bytes(const StepPlan& p);
 // dev_desc: p.desc copied to device memory.  Zeroes the counters in ws (unless
 // ws_clean: they are already zero, as the kernel leaves them), then runs the
@@ -62,6 +75,8 @@ size_t step_workspace_bytes(const StepPlan& p);
 // dev_ranges: p.ranges copied to device memory (nullptr when p.ranges is empty).
 hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, const int4* dev_ranges,
                        void* ws, bool ws_clean, hipStream_t s);
+// The epoch the next launch tags its handed-over pairs with (never 0, increasing).
+uint32_t next_step_epoch();
 hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu);
 
 }  // namespace q4

@@ -31,6 +31,7 @@
 // that k reads or writes; the "ordered" mode makes every descriptor wait for its
 // predecessor, as in a decode step whose GEMVs feed each other.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 
 #include "q4_step.h"
@@ -59,10 +60,7 @@ __device__ __forceinline__ Q4_GLOBAL T* gptr_mut(T* p) {
   return (Q4_GLOBAL T*)p;
 }
 typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_nt_g(const Q4_GLOBAL uint4* p) {
-  const u32x4_g v = __builtin_nontemporal_load((const Q4_GLOBAL u32x4_g*)p);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
+typedef uint32_t u32x2_g __attribute__((ext_vector_type(2)));
 
 // The fields of a descriptor a compute wave needs, read with scalar loads issued
 // as inline assembly.  Read as ordinary loads, they become vector loads (the
@@ -72,12 +70,12 @@ __device__ __forceinline__ uint4 load_nt_g(const Q4_GLOBAL uint4* p) {
 struct CursorDesc {
   const Q4_GLOBAL uint4* W;
   const Q4_GLOBAL uint16_t* S;
-  int N, G, lg, C, steps, sbase, srem;
+  int N, G, lg, C, steps, flags, sbase, srem;
 };
 typedef uint32_t u32x8_s __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
   u32x4_g ws;
-  u32x8_s rest;        // N, G, lpr_log2 | C << 16, steps, dep, signal, sbase, srem
+  u32x8_s rest;        // N, G, lpr_log2 | C << 16, steps, dep, flags, sbase, srem
   asm volatile(
       "s_load_dwordx4 %0, %2, 0x0\n\t"
       "s_load_dwordx8 %1, %2, 0x20\n\t"
@@ -87,7 +85,7 @@ __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
   static_assert(offsetof(StepDesc, S) == 8 && offsetof(StepDesc, N) == 32 &&
                     offsetof(StepDesc, G) == 36 && offsetof(StepDesc, lpr_log2) == 40 &&
                     offsetof(StepDesc, C) == 42 && offsetof(StepDesc, steps) == 44 &&
-                    offsetof(StepDesc, sbase) == 56 &&
+                    offsetof(StepDesc, flags) == 52 && offsetof(StepDesc, sbase) == 56 &&
                     offsetof(StepDesc, srem) == 60,
                 "descriptor offsets read by the compute waves");
   CursorDesc r;
@@ -98,6 +96,7 @@ __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
   r.lg = (int)(rest[2] & 0xFFFFu);
   r.C = (int)(rest[2] >> 16);
   r.steps = (int)rest[3];
+  r.flags = (int)rest[5];
   r.sbase = (int)rest[6];
   r.srem = (int)rest[7];
   return r;
@@ -198,6 +197,7 @@ constexpr int kSync = 4;                    // sync waves (stage x, copy out y)
 constexpr int kCompute = kWaves - kSync;    // compute waves
 static_assert(kXBufs % kSync == 0, "a GEMV and the one whose x buffer it reuses share an owner");
 constexpr unsigned kSpinLimit = 1u << 24;   // bounded waits (about a second)
+constexpr unsigned kTagSpinLimit = 1u << 18; // polls of tagged pairs (a memory round trip each)
 constexpr int kCoherent = 1 | 16;           // cache policy sc0 | sc1: device-coherent access
 constexpr int kWaitVm0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt untouched)
 constexpr int kNonTemporal = 2;             // cache policy nt: streamed once
@@ -225,7 +225,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
                                                        unsigned* __restrict__ done,
                                                        unsigned* __restrict__ err, int maxG,
                                                        int ybuf_rows,
-                                                       const int4* __restrict__ ranges) {
+                                                       const int4* __restrict__ ranges,
+                                                       unsigned epoch) {
   static_assert(NX <= kXBufs && NX % kSync == 0, "x buffers");
   extern __shared__ uint4 smem[];
   __shared__ Shared sh;
@@ -255,10 +256,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   }
   // row-steps [lo, hi) of a GEMV in this workgroup: sbase is the GEMV's first
   // row-step in the concatenation when srem < 0 (range mode), else the even split
-  auto item_range = [&](int sbase, int srem, int steps, int& lo, int& hi) {
+  auto item_range = [&](int sbase, int srem, int steps, int flags, int& lo, int& hi) {
     if (srem < 0) {
       lo = min(max(ra - sbase, 0), steps);
       hi = min(max(rb - sbase, 0), steps);
+    } else if (flags & kPairs) {
+      lo = min(2 * wg_step(sbase, srem, wg), steps);
+      hi = min(2 * wg_step(sbase, srem, wg + 1), steps);
     } else {
       lo = wg_step(sbase, srem, wg);
       hi = wg_step(sbase, srem, wg + 1);
@@ -282,12 +286,25 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const int b = (i - j0) % NX;
       const int rps = 64 >> d.lpr_log2;
       int lo, hi;
-      item_range(d.sbase, d.srem, d.steps, lo, hi);
+      item_range(d.sbase, d.srem, d.steps, d.flags, lo, hi);
       const int r0 = lo * rps;
       int r1 = hi * rps;
       if (r1 > d.N) r1 = d.N;
       const uint16_t* yb = ybuf + b * ybuf_rows;
-      if (!d.signal) {
+      if (d.flags & kTagOut) {
+        // the rows as tagged pairs for the GEMV that reads them: one 64-bit store
+        // per pair (two values and the epoch land together), written through to
+        // the coherence point; nothing waits for them here (r0 is even)
+        const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<unsigned char*>(done) + d.tag_out, 0, 0x7FFFFFFF, 0x00020000);
+        for (int q = (r0 >> 1) + lane; 2 * q < r1; q += 64) {
+          const uint32_t lo16 = yb[2 * q - r0];
+          const uint32_t hi16 = 2 * q + 1 < r1 ? yb[2 * q + 1 - r0] : 0u;
+          const u32x2_g t = {lo16 | (hi16 << 16), epoch};
+          __builtin_amdgcn_raw_buffer_store_b64(t, rt, 8 * q, 0, kCoherent);
+        }
+      }
+      if (!(d.flags & kPublish)) {
         Q4_GLOBAL uint16_t* Y = gptr_mut(d.Y);
         for (int r = r0 + lane; r < r1; r += 64) Y[r] = yb[r - r0];
       } else {
@@ -324,7 +341,20 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const int G = d.G, nblk = 4 * G;
       finish_upto(k - kSync, false);             // publish what is already complete
       if (k - j0 >= NX) finish_upto(k - NX, true);   // buffer (k - j0) % NX is free again
-      const bool coherent = d.dep >= 0;
+      const bool tagged = (d.flags & kTagIn) != 0;
+      const bool coherent = d.dep >= 0 && !tagged;
+      if (tagged) {
+        // this workgroup's own share of the producer comes first (the others
+        // finish at about the same time): poll the pairs only after it
+        for (unsigned it = 0; d.dep >= j0 && !complete(d.dep); ++it) {
+          if (it > kSpinLimit) { err[0] = 4u; break; }
+          finish_upto(k - kSync, false);
+          __builtin_amdgcn_s_sleep(1);
+        }
+        // every own GEMV up to the producer is complete here: publish them before
+        // polling (other workgroups' shares of the producer may depend on them)
+        finish_upto(k - kSync, false);
+      }
       if (coherent) {
         if ((d.dep - j0) % kSync == me) finish_upto(d.dep, true);
         for (unsigned it = 0;
@@ -346,7 +376,35 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       // K <= 4096
       for (int i0 = 0; i0 < nblk; i0 += 8 * 64) {
         uint4 v[8];
-        if (coherent) {
+        if (tagged) {
+          // block i = tagged pairs 4i .. 4i + 3 (two 16-byte loads from the
+          // coherence point); a block is taken once all four carry this call's
+          // epoch, and re-read until then
+          const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+              reinterpret_cast<unsigned char*>(done) + d.tag_in, 0, 0x7FFFFFFF, 0x00020000);
+          unsigned pend = 0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (i0 + u * 64 + lane < nblk) pend |= 1u << u;
+          for (unsigned it = 0;; ++it) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              if (pend & (1u << u)) {
+                const int i = i0 + u * 64 + lane;
+                const u32x4_g a = __builtin_amdgcn_raw_buffer_load_b128(rt, 32 * i, 0, kCoherent);
+                const u32x4_g c2 = __builtin_amdgcn_raw_buffer_load_b128(rt, 32 * i + 16, 0, kCoherent);
+                if (a[1] == epoch && a[3] == epoch && c2[1] == epoch && c2[3] == epoch) {
+                  v[u] = make_uint4(a[0], a[2], c2[0], c2[2]);
+                  pend &= ~(1u << u);
+                }
+              }
+            }
+            if (!__builtin_amdgcn_ballot_w64(pend != 0u)) break;
+            if (it > kTagSpinLimit) { err[0] = 4u; break; }
+            finish_upto(k - kSync, false);
+            __builtin_amdgcn_s_sleep(1);
+          }
+        } else if (coherent) {
           // x may have been written by other workgroups in this launch: read it
           // from the coherence point, past every cache
 #pragma unroll
@@ -444,7 +502,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     for (; j <= j1; ++j) {
       const CursorDesc d = read_desc(D + j);
       int s0, s1;
-      item_range(d.sbase, d.srem, d.steps, s0, s1);
+      item_range(d.sbase, d.srem, d.steps, d.flags, s0, s1);
       int off = c - base;
       if (off < 0) off += kCompute;
       base = (base + (s1 - s0)) % kCompute;      // GEMV j's items are dealt either way
@@ -514,7 +572,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
 #pragma unroll
     for (int p = 0; p < B; ++p) {
       const bool live = cu.j <= j1;
-      const int lg = live ? cu.lg : 2, lpr = 1 << lg;
+      const int lg = live ? cu.lg : 2;
       const int G = live ? cu.G : 1;
       const int C = live ? cu.C : 1;
       const int row0 = live ? cu.s * (64 >> lg) : 0;
@@ -668,7 +726,15 @@ constexpr int kBurst = 2;
 
 }  // namespace
 
-StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool ordered) {
+uint32_t next_step_epoch() {
+  static std::atomic<uint32_t> epoch{0};
+  uint32_t e = epoch.fetch_add(1u) + 1u;
+  if (e == 0u) e = epoch.fetch_add(1u) + 1u;   // 0 marks pairs never written
+  return e;
+}
+
+StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool ordered,
+                   bool tags) {
   StepPlan p;
   p.ok = false;
   if (n < 1) return p;
@@ -695,41 +761,106 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
     s.C = C;
     s.steps = (int)((L.N + rps - 1) / rps);
     s.dep = -1;
-    s.signal = 0;
+    s.flags = 0;
+    s.tag_in = s.tag_out = 0;
+    s.pad[0] = s.pad[1] = 0;
     s.sbase = s.steps / p.grid;
     s.srem = s.steps % p.grid;
     if (lpr * C > maxG) maxG = lpr * C;         // padded group count
     const int rows_wg = ((s.steps + p.grid - 1) / p.grid) * rps;
     if (rows_wg > ybuf_rows) ybuf_rows = rows_wg;
   }
-  // dependencies: k waits for the latest earlier descriptor that writes what k
-  // reads or writes (or, ordered, simply its predecessor)
+  // Dependencies.  Descriptor k conflicts with an earlier h whose y overlaps k's x
+  // (k reads what h writes) or k's y (both write it), and with an earlier g whose x
+  // overlaps k's y (k overwrites what g reads); ordered, also with k - 1.
+  //  * Hand-over: when k's only conflict is one h whose y holds all of k's x (at
+  //    an even element offset), h also writes its y as epoch-tagged pairs to the
+  //    workspace and k reads x from those as soon as they are there: no
+  //    completion counter, no wait for the rest of h.
+  //  * Otherwise k waits for the completion counter of its latest conflict.  A
+  //    workgroup publishes a GEMV only after staging the x of every GEMV before
+  //    it, and stages x only after its own counter wait, so that wait also covers
+  //    a writer reached from it through counter waits (and every reader before
+  //    it); a list with a writer not covered so runs one kernel per GEMV.
   auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
     return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
   };
+  std::vector<int> tag_src((size_t)n, -1);
   for (int64_t k = 1; k < n; ++k) {
-    int dep = -1;
-    if (ordered) {
-      dep = (int)k - 1;
-    } else {
-      const StepLayer& Lk = layers[k];
-      for (int64_t i = k - 1; i >= 0 && dep < 0; --i) {
-        const StepLayer& Li = layers[i];
-        const int64_t yi = 2 * Li.N;
-        if (overlap(Li.y, yi, Lk.x, 2 * Lk.K) || overlap(Li.y, yi, Lk.y, 2 * Lk.N) ||
-            overlap(Li.x, 2 * Li.K, Lk.y, 2 * Lk.N))
-          dep = (int)i;
+    const StepLayer& Lk = layers[k];
+    int last = ordered ? (int)k - 1 : -1, raw_h = -1, raw_n = 0;
+    bool other = false;
+    std::vector<int> writers;
+    for (int64_t i = k - 1; i >= 0; --i) {
+      const StepLayer& Li = layers[i];
+      const bool raw = overlap(Li.y, 2 * Li.N, Lk.x, 2 * Lk.K);
+      const bool waw = overlap(Li.y, 2 * Li.N, Lk.y, 2 * Lk.N);
+      const bool war = overlap(Li.x, 2 * Li.K, Lk.y, 2 * Lk.N);
+      if (raw || waw) writers.push_back((int)i);
+      if (raw) { ++raw_n; raw_h = (int)i; }
+      if (waw || war) other = true;
+      if ((raw || waw || war) && (int)i > last) last = (int)i;
+    }
+    StepDesc& sk = p.desc[(size_t)k];
+    if (tags && raw_n == 1 && !other && (!ordered || raw_h == (int)k - 1)) {
+      const uintptr_t y0 = reinterpret_cast<uintptr_t>(layers[raw_h].y);
+      const uintptr_t x0 = reinterpret_cast<uintptr_t>(Lk.x);
+      if (x0 >= y0 && x0 + 2 * (uintptr_t)Lk.K <= y0 + 2 * (uintptr_t)layers[raw_h].N &&
+          (x0 - y0) % 4 == 0) {
+        tag_src[(size_t)k] = raw_h;
+        sk.dep = raw_h;
+        sk.flags |= kTagIn;
+        p.desc[(size_t)raw_h].flags |= kTagOut;
+        p.cross_wg = true;
+        continue;
       }
     }
-    p.desc[(size_t)k].dep = dep;
-    if (dep >= 0) {
-      p.desc[(size_t)dep].signal = 1;
-      p.cross_wg = true;
+    if (last < 0) continue;
+    sk.dep = last;
+    p.desc[(size_t)last].flags |= kPublish;
+    p.cross_wg = true;
+    for (int h : writers) {
+      int i = last;
+      while (i > h && !(p.desc[(size_t)i].flags & kTagIn) && p.desc[(size_t)i].dep >= 0)
+        i = p.desc[(size_t)i].dep;
+      if (i != h) return p;                     // not covered: one kernel per GEMV
+    }
+  }
+  // tagged pairs: after the counters, one 256-byte aligned run per producer; a
+  // producer with one row per row-step splits its rows over the workgroups in
+  // pairs, so every workgroup's first row is even
+  p.counters = (int)n + 4;
+  p.tag_base = ((size_t)p.counters * sizeof(unsigned) + 255) & ~(size_t)255;
+  std::vector<size_t> tag_off((size_t)n, 0);
+  size_t tag_end = p.tag_base;
+  for (int64_t k = 0; k < n; ++k) {
+    StepDesc& sk = p.desc[(size_t)k];
+    if (!(sk.flags & kTagOut)) continue;
+    tag_off[(size_t)k] = tag_end;
+    tag_end += ((size_t)((sk.N + 1) / 2) * 8 + 255) & ~(size_t)255;
+    if (sk.lpr_log2 == 6) {
+      const int pairs = (sk.steps + 1) / 2;
+      sk.flags |= kPairs;
+      sk.sbase = pairs / p.grid;
+      sk.srem = pairs % p.grid;
+      const int rows_wg = 2 * ((pairs + p.grid - 1) / p.grid);
+      if (rows_wg > ybuf_rows) ybuf_rows = rows_wg;
+    }
+  }
+  if (tag_end > (size_t)INT32_MAX) return p;
+  p.tag_bytes = tag_end - p.tag_base;
+  for (int64_t k = 0; k < n; ++k) {
+    StepDesc& sk = p.desc[(size_t)k];
+    if (sk.flags & kTagOut) sk.tag_out = (int)tag_off[(size_t)k];
+    if (sk.flags & kTagIn) {
+      const int h = tag_src[(size_t)k];
+      const uintptr_t off = reinterpret_cast<uintptr_t>(layers[k].x) -
+                            reinterpret_cast<uintptr_t>(layers[h].y);
+      sk.tag_in = (int)(tag_off[(size_t)h] + 2 * off);   // 8 bytes per 4 bytes of x
     }
   }
   p.maxG = maxG;
-  p.counters = (int)n + 4;
   const size_t lds_cap = d.lds_per_block - sizeof(int) * 32;
   auto lds_for = [&](int nx, int rows) {
     return (size_t)nx * ((size_t)4 * maxG * 16 + (size_t)maxG * 4 + (size_t)rows * 2);
@@ -803,6 +934,7 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
 }
 
 size_t step_workspace_bytes(const StepPlan& p) {
+  if (p.tag_bytes) return p.tag_base + p.tag_bytes;
   return ((size_t)p.counters * sizeof(unsigned) + 255) & ~(size_t)255;
 }
 
@@ -811,9 +943,13 @@ hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, const int4* 
   unsigned* done = static_cast<unsigned*>(ws);
   unsigned* err = done + (p.counters - 1);
   if (!ws_clean) {
-    hipLaunchKernelGGL(k_zero, dim3(1), dim3(256), 0, s, done, p.counters);
+    // counters, and the tagged pairs (so no stale word can carry this epoch)
+    const int words = (int)(step_workspace_bytes(p) / sizeof(unsigned));
+    const int blocks = std::max(1, std::min(1024, words / 4096));
+    hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(256), 0, s, done, words);
     if (hipError_t e = hipGetLastError()) return e;
   }
+  unsigned epoch = next_step_epoch();
   auto kern = p.nx == 4 ? k_step<kBurst, 4> : k_step<kBurst, kXBufs>;
   if (p.lds_bytes > 65536) {
     if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -824,7 +960,7 @@ hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, const int4* 
   int n = (int)p.desc.size(), maxG = p.maxG, yr = p.ybuf_rows;
   const int4* rg = p.ranges.empty() ? nullptr : dev_ranges;
   void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&done, (void*)&err, (void*)&maxG,
-                  (void*)&yr, (void*)&rg};
+                  (void*)&yr, (void*)&rg, (void*)&epoch};
   // Only waits across workgroups need every workgroup resident at once; without
   // them (no descriptor depends on another) a plain launch does, and it costs
   // far less at the kernel boundary than a cooperative one.
@@ -832,7 +968,7 @@ hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, const int4* 
     return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(p.grid),
                                       dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kStepThreads), p.lds_bytes, s, dev_desc, n, done,
-                     err, maxG, yr, rg);
+                     err, maxG, yr, rg, epoch);
   return hipGetLastError();
 }
 
