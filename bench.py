@@ -115,16 +115,23 @@ def main():
     step_bytes = sum(synth.algorithmic_bytes(1, N, K) for _, N, K in meta)
     weight_bytes = sum(synth.Matrix(l, N, K).weight_bytes for l, N, K in meta)
 
-    def time_mode(mode, steps, warmup):
+    # the same GEMVs with each x a prefix of the previous GEMV's y: a decode
+    # step's dependency chain with the operations between the GEMVs left out
+    chain_layers = q4.make_layers(
+        [descs[0]] + [(W, S, descs[i - 1][3][:x.numel()], y)
+                      for i, (W, S, x, y) in enumerate(descs) if i > 0])
+
+    def time_mode(mode, steps, warmup, lay=None):
         flags = MODES[mode]
-        ws_bytes = q4.q4_decode_step_workspace_bytes(layers, 1, flags)
+        layers_ = layers if lay is None else lay
+        ws_bytes = q4.q4_decode_step_workspace_bytes(layers_, 1, flags)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
         # the first call clears the workspace's counters; the kernel leaves them
         # zero, so the following calls skip the clearing kernel
         def step(first=False):
             f = flags if first else flags | q4.STEP_WS_CLEAN
-            q4.q4_decode_step(layers, 1, f, ws=ws, ws_bytes=ws_bytes, stream=stream)
+            q4.q4_decode_step(layers_, 1, f, ws=ws, ws_bytes=ws_bytes, stream=stream)
 
         with torch.cuda.stream(stream):
             step(first=True)
@@ -180,6 +187,11 @@ def main():
             m_ms, _ = time_mode(mode, max(5, args.steps // 5), max(3, args.warmup // 4))
             other[mode] = {"ms_per_step": round(m_ms, 5),
                            "gbs": round(step_bytes / (m_ms * 1e-3) / 1e9, 1)}
+        for mode in ("hazards", "launch_each"):
+            m_ms, _ = time_mode(mode, max(5, args.steps // 5), max(3, args.warmup // 4),
+                                chain_layers)
+            other[f"chain_{mode}"] = {"ms_per_step": round(m_ms, 5),
+                                      "gbs": round(step_bytes / (m_ms * 1e-3) / 1e9, 1)}
         result["other_modes"] = other
         if not args.no_configs:
             result["per_config"] = per_config(torch, q4, synth, np, stream)

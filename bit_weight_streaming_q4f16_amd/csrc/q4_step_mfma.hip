@@ -547,24 +547,32 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
     return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
   };
+  // k waits for its latest conflict (an earlier GEMV writing what k reads or
+  // writes, or reading what k writes; ordered: also k - 1).  A workgroup publishes
+  // a GEMV only after staging the X of every GEMV before it, and stages X only
+  // after its own wait, so the wait also covers every writer reached from it
+  // through waits (and every reader before it); a list with a writer not covered
+  // so runs one kernel per GEMV.
   for (int64_t k = 1; k < n; ++k) {
-    int dep = -1;
-    if (ordered) {
-      dep = (int)k - 1;
-    } else {
-      const StepLayer& Lk = layers[k];
-      for (int64_t i = k - 1; i >= 0 && dep < 0; --i) {
-        const StepLayer& Li = layers[i];
-        const int64_t yi = 2 * M * Li.N, xk = 2 * M * Lk.K, yk = 2 * M * Lk.N;
-        if (overlap(Li.y, yi, Lk.x, xk) || overlap(Li.y, yi, Lk.y, yk) ||
-            overlap(Li.x, 2 * M * Li.K, Lk.y, yk))
-          dep = (int)i;
-      }
+    int dep = ordered ? (int)k - 1 : -1;
+    std::vector<int> writers;
+    const StepLayer& Lk = layers[k];
+    for (int64_t i = k - 1; i >= 0; --i) {
+      const StepLayer& Li = layers[i];
+      const int64_t yi = 2 * M * Li.N, xk = 2 * M * Lk.K, yk = 2 * M * Lk.N;
+      const bool w = overlap(Li.y, yi, Lk.x, xk) || overlap(Li.y, yi, Lk.y, yk);
+      if (w) writers.push_back((int)i);
+      if ((w || overlap(Li.x, 2 * M * Li.K, Lk.y, yk)) && (int)i > dep) dep = (int)i;
     }
     p.desc[(size_t)k].dep = dep;
     if (dep >= 0) {
       p.desc[(size_t)dep].signal = 1;
       p.cross_wg = true;
+    }
+    for (int h : writers) {
+      int i = dep;
+      while (i > h && p.desc[(size_t)i].dep >= 0) i = p.desc[(size_t)i].dep;
+      if (i != h) return p;                     // not covered: one kernel per GEMV
     }
   }
   const size_t cap = (size_t)dev.lds_per_block - 1024;   // static LDS and margin

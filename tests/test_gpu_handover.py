@@ -78,26 +78,37 @@ def test_offsets_into_odd_row_producer():
         check(m, X, Y)
 
 
+@pytest.mark.parametrize("M", [1, 2])
 @pytest.mark.parametrize("chained", [False, True], ids=["independent", "second_reads_first"])
-def test_reader_of_two_writers(chained):
+def test_reader_of_two_writers(chained, M):
     """x spans the outputs of two GEMVs: one counter wait cannot cover both unless
     the later writer waits for the earlier through counters, so the list runs one
-    kernel per GEMV; results are right either way."""
-    K = 3072
-    buf = nan_half(K)
-    m1, W1, S1 = mat("ho/two/1", K // 2, K)
-    x1 = dev_half(synth.activations("ho/two/x1", 0, K))
+    kernel per GEMV; results are right either way (M = 2: the small-M planner)."""
+    K, H = 3072, 1536
+    buf = torch.full((M * K,), float("nan"), dtype=torch.float16, device="cuda")
+    y1 = buf[:M * H].view(M, H)
+    y2 = buf[M * H:].view(M, H)
+    m1, W1, S1 = mat("ho/two/1", H, K)
+    x1 = dev_half(synth.activations("ho/two/x1", 0, M * K).reshape(M, K))
     if chained:
-        m2, W2, S2 = mat("ho/two/2c", K // 2, K // 2)
-        x2 = buf[:K // 2]
+        m2, W2, S2 = mat("ho/two/2c", H, H)
+        x2 = y1
     else:
-        m2, W2, S2 = mat("ho/two/2", K // 2, K)
-        x2 = dev_half(synth.activations("ho/two/x2", 0, K))
+        m2, W2, S2 = mat("ho/two/2", H, K)
+        x2 = dev_half(synth.activations("ho/two/x2", 0, M * K).reshape(M, K))
     m3, W3, S3 = mat("ho/two/3", 2048, K)
-    descs = [(W1, S1, x1, buf[:K // 2]), (W2, S2, x2, buf[K // 2:]), (W3, S3, buf, nan_half(2048))]
-    run(descs)
+    y3 = torch.full((M, 2048), float("nan"), dtype=torch.float16, device="cuda")
+    if M == 1:
+        descs = [(W1, S1, x1[0], y1[0]), (W2, S2, x2[0], y2[0]), (W3, S3, buf, y3[0])]
+    else:
+        descs = [(W1, S1, x1, y1), (W2, S2, x2, y2), (W3, S3, buf.view(M, K), y3)]
+    layers = q4.make_layers(descs)
+    q4.q4_decode_step(layers, M, 0)
+    torch.cuda.synchronize()
     for m, (W, S, X, Y) in zip([m1, m2, m3], descs):
-        check(m, X, Y)
+        y = host_half(Y)
+        assert np.all(np.isfinite(half_f64(y)))
+        assert_gemv_close(y, m.words(), m.scales(), host_half(X).reshape(M, -1))
 
 
 def test_ping_pong_buffers_match_separate_buffers():
