@@ -8,6 +8,8 @@ it; the HIP library never does, and the two share no code.
 Definitions (Zero TVM documentation, section "Q4F16 quantization format"):
 eight 4-bit codes per uint32 word, nibble ``i`` = ``(word >> 4i) & 0xF``, one
 fp16 scale per 32 weights, weight = ``(code - 7) * scale``; y = W x.
+The feed-forward glue between the gate/up and down projections ("Decode loop"):
+fp16(silu(gate) * up).
 
 Parity pins for every function here live in ``tests/test_oracle.py``.
 """
@@ -65,6 +67,8 @@ def _load():
             lib.orc_gemv_exact.restype = C.c_int
             lib.orc_row_norms.argtypes = [p, p, i64, i64, p, i64, p]
             lib.orc_row_norms.restype = C.c_int
+            lib.orc_silu_mul.argtypes = [p, p, i64, i64]
+            lib.orc_silu_mul.restype = None
             lib.orc_vec_norm.argtypes = [p, i64]
             lib.orc_vec_norm.restype = C.c_double
             _lib = lib
@@ -168,6 +172,19 @@ def row_norms(words, scales, rows=None) -> np.ndarray:
     if _load().orc_row_norms(_ptr(w), _ptr(s), N, K, _ptr(r), nr, _ptr(out)):
         raise ValueError("orc_row_norms failed")
     return out
+
+
+def silu_mul(gu, H: int | None = None) -> np.ndarray:
+    """fp16 bits [M][2H] (gate | up) -> fp16 bits [M][H] of fp16(silu(gate) * up),
+    in fp64 (Zero TVM documentation, "Decode loop": the FFN's SiLU and multiply)."""
+    g = _c(gu, np.uint16)
+    g2 = g.reshape(-1, g.shape[-1])
+    if g2.shape[1] % 2:
+        raise ValueError("last axis must be 2H")
+    Hh = g2.shape[1] // 2
+    out = np.empty((g2.shape[0], Hh), np.uint16)
+    _load().orc_silu_mul(_ptr(g2), _ptr(out), g2.shape[0], Hh)
+    return out.reshape(g.shape[:-1] + (Hh,))
 
 
 def vec_norm(x) -> float:

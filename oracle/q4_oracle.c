@@ -17,6 +17,8 @@
  *   GEMV -- for every input row m and output row n:
  *       y[m][n] = sum_k (q[n][k] - 7) * s[n][k/32] * x[m][k].
  *
+ *   MLP glue (orc_silu_mul) -- fp16(silu(gate) * up), see below.
+ *
  * Two independent evaluations of that sum are provided:
  *   orc_gemv_f64   -- fp64 accumulation in ascending k; every product is exact
  *                     in fp64 (at most 4 + 11 + 11 significant bits), only the
@@ -235,6 +237,32 @@ ORC_EXPORT int orc_row_norms(const uint32_t* words, const uint16_t* scales, int6
     out[i] = sqrt(acc);
   }
   return 0;
+}
+
+/* ---------------------------------------------------------------- MLP glue */
+
+/* The step between the gate/up projection and the down projection of the
+ * decode loop's feed-forward block (Zero TVM documentation, section "Decode
+ * loop": gate, up, SiLU, multiply and down form the FFN).  GU is [M][2H] fp16:
+ * gate = GU[m][0 .. H), up = GU[m][H .. 2H) (the fp16 outputs of the gate/up
+ * GEMV).  For every m, i:
+ *     g = gate[m][i], u = up[m][i],
+ *     silu(g) = g / (1 + exp(-g)),
+ *     OUT[m][i] = fp16_rne(silu(g) * u),
+ * evaluated in fp64 (the fp16 inputs are exact in fp64).  silu(+inf) = +inf,
+ * silu(-inf) = -0 (its limits); NaN propagates. */
+ORC_EXPORT void orc_silu_mul(const uint16_t* GU, uint16_t* OUT, int64_t M, int64_t H) {
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t i = 0; i < H; ++i) {
+      double g = orc_half_to_f64(GU[m * 2 * H + i]);
+      double u = orc_half_to_f64(GU[m * 2 * H + H + i]);
+      double sg;
+      if (isinf(g))
+        sg = g > 0 ? g : -0.0;
+      else
+        sg = g / (1.0 + exp(-g));
+      OUT[m * H + i] = orc_f64_to_half(sg * u);
+    }
 }
 
 /* ||x||_2 of an fp16 vector. */

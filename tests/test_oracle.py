@@ -332,3 +332,87 @@ def test_pins_catch_planted_mistake(name):
     with tempfile.TemporaryDirectory() as tmp:
         lib = _build_mutant(tmp, name)
         assert not _pins_pass(lambda w, s, x: _mutant_gemv(lib, w, s, x)), name
+
+
+# ---------------------------------------------------------------- MLP glue pins
+
+def _np_silu_mul(g16, u16):
+    """numpy's exp and float16 cast (independent of the oracle's own rounding)."""
+    g = g16.view(np.float16).astype(np.float64)
+    u = u16.view(np.float16).astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        sg = g / (1.0 + np.exp(-g))
+    sg = np.where(np.isposinf(g), g, np.where(np.isneginf(g), -0.0, sg))
+    with np.errstate(over="ignore", invalid="ignore"):
+        return (sg * u).astype(np.float16).view(np.uint16)
+
+
+def test_silu_mul_every_gate_value_vs_numpy():
+    """All 65 536 fp16 gate values against numpy, with up = 1 and with a few other
+    up values (any dropped term, wrong sign or swapped half shows here)."""
+    g = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for u_val in (1.0, -2.0, 0.5, 3.5, -0.0078125):
+        u = np.full(65536, np.float16(u_val)).view(np.uint16)
+        gu = np.concatenate([g, u]).reshape(1, -1)
+        got = oracle.silu_mul(gu)[0]
+        ref = _np_silu_mul(g, u)
+        nan = np.isnan(ref.view(np.float16))
+        assert np.array_equal(np.isnan(got.view(np.float16)), nan), u_val
+        assert np.array_equal(got[~nan], ref[~nan]), u_val
+
+
+def test_silu_mul_closed_forms_and_layout():
+    # silu(0) = 0; large positive gate: silu(g) = g; large negative: -> -0
+    H = 4
+    gate = np.array([0.0, 20.0, -30.0, 1.0], np.float16)
+    up = np.array([5.0, 0.5, 2.0, 2.0], np.float16)
+    gu = np.concatenate([gate, up]).view(np.uint16).reshape(1, 2 * H)
+    out = oracle.silu_mul(gu)[0].view(np.float16).astype(np.float64)
+    assert out[0] == 0.0
+    assert out[1] == 10.0
+    assert out[2] == 0.0 and np.signbit(out[2])
+    # silu(1) * 2 = 2 / (1 + 1/e) = 1.46211715726...: the nearest fp16 (step 2^-10)
+    assert out[3] == np.float16(2.0 / (1.0 + np.exp(-1.0)))
+    assert abs(out[3] - 1.4621171572600098) <= 2.0 ** -11
+    # rows are independent and the halves are [gate | up] per row
+    rng = np.random.default_rng(3)
+    M, H = 3, 40
+    gu = rng.standard_normal((M, 2 * H)).astype(np.float16).view(np.uint16)
+    out = oracle.silu_mul(gu)
+    for m in range(M):
+        assert np.array_equal(out[m], _np_silu_mul(gu[m, :H], gu[m, H:]))
+    swapped = np.concatenate([gu[:, H:], gu[:, :H]], axis=1)
+    assert not np.array_equal(oracle.silu_mul(swapped), out)
+
+
+SILU_MUTATIONS = {
+    "sign_of_exponent": ("sg = g / (1.0 + exp(-g));", "sg = g / (1.0 + exp(g));"),
+    "halves_swapped": ("double u = orc_half_to_f64(GU[m * 2 * H + H + i]);",
+                       "double u = orc_half_to_f64(GU[m * 2 * H + i]);"),
+    "sigmoid_only": ("OUT[m * H + i] = orc_f64_to_half(sg * u);",
+                     "OUT[m * H + i] = orc_f64_to_half(sg / g * u);"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+@pytest.mark.parametrize("name", sorted(SILU_MUTATIONS))
+def test_silu_pins_catch_planted_mistake(name):
+    src = open(os.path.join(ROOT, "oracle", "q4_oracle.c")).read()
+    a, b = SILU_MUTATIONS[name]
+    assert a in src, name
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "m.c")
+        open(path, "w").write(src.replace(a, b))
+        so = os.path.join(tmp, "m.so")
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-o", so,
+                               path, "-lm"])
+        lib = C.CDLL(so)
+        lib.orc_silu_mul.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64]
+        g = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+        u = np.full(len(g), np.float16(-2.0)).view(np.uint16)
+        gu = np.ascontiguousarray(np.concatenate([g, u]))
+        out = np.empty(len(g), np.uint16)
+        lib.orc_silu_mul(gu.ctypes.data, out.ctypes.data, 1, len(g))
+        ref = _np_silu_mul(g, u)
+        ok = ~np.isnan(ref.view(np.float16))
+        assert not np.array_equal(out[ok], ref[ok]), name
