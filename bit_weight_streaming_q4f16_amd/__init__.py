@@ -32,6 +32,8 @@ STEP_LAUNCH_EACH = 0x1
 STEP_ORDERED = 0x2
 STEP_LDS_RING = 0x4
 STEP_WS_CLEAN = 0x8
+X_PLAIN = 0
+X_SILU_MUL = 1
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
           4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED"}
@@ -48,7 +50,8 @@ class Q4Error(RuntimeError):
 class Layer(C.Structure):
     """q4_layer: one GEMV of a decode step (device pointers and sizes)."""
     _fields_ = [("words", C.c_void_p), ("scales", C.c_void_p), ("x", C.c_void_p),
-                ("y", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64)]
+                ("y", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64),
+                ("x_op", C.c_uint32), ("reserved", C.c_uint32)]
 
 
 def lib_path() -> str:
@@ -80,6 +83,7 @@ def load():
             "q4_splitk_workspace_bytes": ([i64, i64, i64], sz),
             "q4_decode_step": ([p, i64, i64, C.c_uint32, p, sz, p], i32),
             "q4_decode_step_workspace_bytes": ([p, i64, i64, C.c_uint32], sz),
+            "q4_silu_mul": ([p, p, i64, i64, p], i32),
             "q4_probe_read": ([p, sz, p, i64, p], i32),
             "q4_probe_copy": ([p, p, sz, p], i32),
         }
@@ -229,12 +233,15 @@ def q4_gemv_batched(words, scales, X, Y=None, ws=None, stream=None):
 
 
 def make_layers(descs):
-    """descs: iterable of (words, scales, x, y) tensors -> ctypes array of Layer."""
+    """descs: iterable of (words, scales, x, y) or (words, scales, x, y, x_op)
+    tensors -> ctypes array of Layer."""
     descs = list(descs)
     arr = (Layer * len(descs))()
-    for i, (w, s, x, y) in enumerate(descs):
+    for i, d in enumerate(descs):
+        w, s, x, y = d[:4]
+        x_op = d[4] if len(d) > 4 else X_PLAIN
         N, K8 = w.shape
-        arr[i] = Layer(w.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), N, 8 * K8)
+        arr[i] = Layer(w.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), N, 8 * K8, x_op, 0)
     return arr
 
 
@@ -251,6 +258,18 @@ def q4_decode_step(layers, M: int = 1, flags: int = 0, ws=None, ws_bytes=None, s
     wsb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
     _check(load().q4_decode_step(layers, len(layers), M, flags, _ptr(ws), wsb, _stream(stream)))
     return ws
+
+
+def q4_silu_mul(gu, out=None, stream=None):
+    """fp16 [M][2H] (gate | up) -> fp16 [M][H] = fp16(silu(gate) * up)."""
+    torch = _torch()
+    g = gu if gu.dim() == 2 else gu.reshape(1, -1)
+    M, H2 = g.shape
+    H = H2 // 2
+    if out is None:
+        out = torch.empty((M, H) if gu.dim() == 2 else (H,), dtype=torch.float16, device=gu.device)
+    _check(load().q4_silu_mul(_ptr(gu), _ptr(out), M, H, _stream(stream)))
+    return out
 
 
 def q4_probe_read(buf, sink, blocks: int = 0, stream=None):

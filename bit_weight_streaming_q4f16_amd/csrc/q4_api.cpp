@@ -55,8 +55,10 @@ int check_shape(int64_t N, int64_t K) {
 }
 
 // Validate one GEMV's tensors.  `what` names the call for the error text.
+// x_cols: elements per row of x (K, or 2K when x holds gate | up).
 int check_gemv(const char* what, const uint32_t* words, const uint16_t* scales,
-               const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K) {
+               const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K,
+               int64_t x_cols) {
   if (!words) return fail(Q4_ERR_NULL, "%s: words is NULL", what);
   if (!scales) return fail(Q4_ERR_NULL, "%s: scales is NULL", what);
   if (!x) return fail(Q4_ERR_NULL, "%s: x is NULL", what);
@@ -79,7 +81,7 @@ int check_gemv(const char* what, const uint32_t* words, const uint16_t* scales,
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + (uintptr_t)bytes;
     return a0 < y1 && y0 < a1;
   };
-  if (overlaps(words, N * K / 2) || overlaps(scales, N * K / 16) || overlaps(x, 2 * M * K))
+  if (overlaps(words, N * K / 2) || overlaps(scales, N * K / 16) || overlaps(x, 2 * M * x_cols))
     return fail(Q4_ERR_SHAPE, "%s: y overlaps an input", what);
   return Q4_OK;
 }
@@ -176,7 +178,7 @@ size_t q4_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
 static int gemv_common(const char* what, const uint32_t* words, const uint16_t* scales,
                        const uint16_t* x, uint16_t* y, int64_t M, int64_t N, int64_t K,
                        int64_t splits, void* ws, size_t ws_bytes, q4_stream_t stream) {
-  if (int rc = check_gemv(what, words, scales, x, y, M, N, K)) return rc;
+  if (int rc = check_gemv(what, words, scales, x, y, M, N, K, K)) return rc;
   if (splits != 0 && (splits < 1 || splits > q4::kMaxSplits || splits > K / 32))
     return fail(Q4_ERR_SHAPE, "%s: splits = %lld: must be in [1, min(64, K/32 = %lld)]", what,
                 (long long)splits, (long long)(K / 32));
@@ -266,7 +268,7 @@ std::vector<q4::StepLayer> to_step_layers(const q4_layer* layers, int64_t n) {
   std::vector<q4::StepLayer> v((size_t)n);
   for (int64_t i = 0; i < n; ++i)
     v[(size_t)i] = q4::StepLayer{layers[i].words, layers[i].scales, layers[i].x, layers[i].y,
-                                 layers[i].N, layers[i].K};
+                                 layers[i].N, layers[i].K, layers[i].x_op};
   return v;
 }
 
@@ -298,6 +300,32 @@ q4::StepPlan counter_plan(const q4::DeviceInfo& d, const std::vector<q4::StepLay
   return cp;
 }
 
+// One kernel per descriptor: the largest split-K partials of any descriptor, then
+// (for descriptors with Q4_X_SILU_MUL) the largest glue output, M * K fp16.
+struct EachLayout {
+  std::vector<q4::GemvPlan> plans;
+  size_t glue_off = 0, bytes = 0;
+};
+EachLayout each_layout(const q4::DeviceInfo& d, const q4_layer* layers, int64_t n, int64_t M) {
+  EachLayout e;
+  e.plans.resize((size_t)n);
+  size_t part = 0, glue = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    e.plans[(size_t)i] = q4::plan_auto(d, M, layers[i].N, layers[i].K);
+    part = std::max(part, e.plans[(size_t)i].ws_bytes);
+    if (layers[i].x_op) glue = std::max(glue, (size_t)(2 * M * layers[i].K));
+  }
+  e.glue_off = (part + 255) & ~(size_t)255;
+  e.bytes = glue ? e.glue_off + glue : part;
+  return e;
+}
+
+bool any_x_op(const q4_layer* layers, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (layers[i].x_op) return true;
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -307,13 +335,11 @@ size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, 
   if (!layers || n_layers < 1 || M < 1 || M > q4::kMaxM) return 0;
   const q4::DeviceInfo* d = q4::device_info();
   if (!d) return 0;
-  size_t need = 0;
   for (int64_t i = 0; i < n_layers; ++i) {
     const q4_layer& L = layers[i];
     if (L.N < 1 || L.K < 32 || L.K % 32) return 0;
-    const size_t b = q4::plan_auto(*d, M, L.N, L.K).ws_bytes;
-    if (b > need) need = b;
   }
+  size_t need = each_layout(*d, layers, n_layers, M).bytes;
   if (M > 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
     std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
     q4::MStepPlan p = q4::plan_step_mfma(*d, sl.data(), n_layers, (int)M,
@@ -325,7 +351,7 @@ size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, 
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
     size_t b = q4::step_workspace_bytes(p);
     if (b > need) need = b;
-    if (flags & Q4_STEP_LDS_RING) {
+    if ((flags & Q4_STEP_LDS_RING) && !any_x_op(layers, n_layers)) {
       std::vector<int> dep, sig;
       q4::StepPlan cp = counter_plan(*d, sl, n_layers, flags, &dep, &sig);
       if (cp.ok) {
@@ -352,7 +378,12 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   for (int64_t i = 0; i < n_layers; ++i) {
     const q4_layer& L = layers[i];
     snprintf(what, sizeof what, "q4_decode_step: layers[%lld]", (long long)i);
-    if (int rc = check_gemv(what, L.words, L.scales, L.x, L.y, M, L.N, L.K)) return rc;
+    if (L.x_op > Q4_X_SILU_MUL)
+      return fail(Q4_ERR_SHAPE, "%s: x_op = %u: unknown", what, L.x_op);
+    if (L.reserved) return fail(Q4_ERR_SHAPE, "%s: reserved = %u: must be 0", what, L.reserved);
+    if (int rc = check_gemv(what, L.words, L.scales, L.x, L.y, M, L.N, L.K,
+                            L.x_op ? 2 * L.K : L.K))
+      return rc;
   }
   const q4::DeviceInfo* d = q4::device_info();
   if (!d) return fail(Q4_ERR_DEVICE, "q4_decode_step: no HIP device");
@@ -384,7 +415,7 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
     std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
-    if (flags & Q4_STEP_LDS_RING) {
+    if ((flags & Q4_STEP_LDS_RING) && !any_x_op(layers, n_layers)) {
       std::vector<int> dep, sig;
       q4::StepPlan cp = counter_plan(*d, sl, n_layers, flags, &dep, &sig);
       q4::DmaPlan dp = q4::plan_step_dma(*d, sl.data(), n_layers, dep, sig);
@@ -420,23 +451,41 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
     }
   }
 
-  std::vector<q4::GemvPlan> plans((size_t)n_layers);
-  size_t need = 0;
-  for (int64_t i = 0; i < n_layers; ++i) {
-    plans[(size_t)i] = q4::plan_auto(*d, M, layers[i].N, layers[i].K);
-    if (plans[(size_t)i].ws_bytes > need) need = plans[(size_t)i].ws_bytes;
-  }
-  if (int rc = check_ws("q4_decode_step", ws, ws_bytes, need)) return rc;
+  const EachLayout el = each_layout(*d, layers, n_layers, M);
+  if (int rc = check_ws("q4_decode_step", ws, ws_bytes, el.bytes)) return rc;
+  uint16_t* glue = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + el.glue_off);
   for (int64_t i = 0; i < n_layers; ++i) {
     const q4_layer& L = layers[i];
-    q4::GemvArgs a{L.words, L.scales, L.x, L.y, M, L.N, L.K};
-    hipError_t e = q4::launch_gemv(*d, a, plans[(size_t)i], ws, s);
+    hipError_t e = hipSuccess;
+    const uint16_t* x = L.x;
+    if (L.x_op == Q4_X_SILU_MUL) {
+      e = q4::launch_silu_mul(L.x, glue, M, L.K, s);
+      x = glue;
+    }
+    q4::GemvArgs a{L.words, L.scales, x, L.y, M, L.N, L.K};
+    if (e == hipSuccess) e = q4::launch_gemv(*d, a, el.plans[(size_t)i], ws, s);
     if (e != hipSuccess) {
       snprintf(what, sizeof what, "q4_decode_step: layers[%lld]", (long long)i);
       return device_error(e, what);
     }
   }
   return ok();
+}
+
+int q4_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t H, q4_stream_t stream) {
+  if (!gu || !out) return fail(Q4_ERR_NULL, "q4_silu_mul: NULL pointer");
+  if (M < 1 || H < 8 || H % 8)
+    return fail(Q4_ERR_SHAPE, "q4_silu_mul: M = %lld, H = %lld: need M >= 1, H %% 8 == 0",
+                (long long)M, (long long)H);
+  if (M * H >= ((int64_t)1 << 31))
+    return fail(Q4_ERR_UNSUPPORTED, "q4_silu_mul: M * H = %lld: too large", (long long)(M * H));
+  if (!aligned(gu, 16) || !aligned(out, 16))
+    return fail(Q4_ERR_ALIGN, "q4_silu_mul: pointers not 16-byte aligned");
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(gu), b0 = reinterpret_cast<uintptr_t>(out);
+  if (a0 < b0 + (uintptr_t)(2 * M * H) && b0 < a0 + (uintptr_t)(4 * M * H))
+    return fail(Q4_ERR_SHAPE, "q4_silu_mul: out overlaps gu");
+  hipError_t e = q4::launch_silu_mul(gu, out, M, H, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_silu_mul");
 }
 
 int q4_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t blocks,

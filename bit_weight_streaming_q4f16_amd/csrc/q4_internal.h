@@ -61,6 +61,23 @@ hipError_t launch_pack(const uint8_t* codes, uint32_t* words, int64_t N, int64_t
 hipError_t launch_unpack(const uint32_t* words, uint8_t* codes, int64_t N, int64_t K,
                          hipStream_t s);
 
+// The feed-forward glue of the decode loop (Zero TVM documentation, "Decode
+// loop"): fp16(silu(g) * u) with silu(g) = g / (1 + exp(-g)), in fp32, rounded to
+// nearest even; silu(+inf) = +inf, silu(-inf) = -0 (its limits).
+__device__ __forceinline__ _Float16 silu_mul_h(_Float16 g, _Float16 u) {
+  const float gf = (float)g;
+  float sg;
+  if (__builtin_isinf(gf))
+    sg = gf > 0.f ? gf : -0.f;
+  else
+    sg = gf / (1.f + __expf(-gf));
+  return (_Float16)(sg * (float)u);
+}
+
+// out[m][i] = silu_mul_h(gu[m][i], gu[m][H + i]); H % 8 == 0, 16-byte aligned.
+hipError_t launch_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t H,
+                           hipStream_t s);
+
 hipError_t launch_probe_read(const DeviceInfo& d, const void* buf, size_t bytes, uint32_t* sink,
                              int64_t blocks, hipStream_t s);
 hipError_t launch_probe_copy(const DeviceInfo& d, const void* src, void* dst, size_t bytes,

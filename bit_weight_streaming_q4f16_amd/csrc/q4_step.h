@@ -15,6 +15,7 @@ constexpr int kPublish = 1;  // later descriptors wait for this one's completion
 constexpr int kTagOut = 2;   // y also goes to the workspace as epoch-tagged pairs
 constexpr int kTagIn = 4;    // x is read from an earlier descriptor's tagged pairs
 constexpr int kPairs = 8;    // workgroup shares are split in pairs of row-steps (even rows)
+constexpr int kSiluMul = 16; // x is [gate | up]: the input is fp16(silu(gate) * up)
 
 // One GEMV as the persistent kernel reads it (device-resident table, 80 bytes).
 struct StepDesc {
@@ -27,7 +28,7 @@ struct StepDesc {
   int16_t C;             // groups per lane (<= 4)
   int steps;             // row-steps: ceil(N / (64 / lanes per row))
   int dep;               // descriptor that must be complete before x is read (-1: none)
-  int flags;             // kPublish | kTagOut | kTagIn | kPairs
+  int flags;             // kPublish | kTagOut | kTagIn | kPairs | kSiluMul
   int sbase, srem;       // workgroup w owns row-steps from w * sbase + min(w, srem)
                          // (pairs of row-steps with kPairs): split evenly over the
                          // grid, the first srem get one more
@@ -43,6 +44,8 @@ struct StepLayer {
   const uint16_t* x;
   uint16_t* y;
   int64_t N, K;
+  uint32_t x_op;          // Q4_X_PLAIN (x is [M][K]) or Q4_X_SILU_MUL (x is [M][2K])
+  int64_t x_cols() const { return x_op ? 2 * K : K; }
 };
 
 struct StepPlan {

@@ -61,6 +61,7 @@ __device__ __forceinline__ Q4_GLOBAL T* gptr_mut(T* p) {
 }
 typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_g __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 
 // The fields of a descriptor a compute wave needs, read with scalar loads issued
 // as inline assembly.  Read as ordinary loads, they become vector loads (the
@@ -373,10 +374,68 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       uint4* xb = xbuf + b * 4 * maxG;
       float* cb = cbuf + b * maxG;
       // x_k in (at most) two batches of 8 blocks per lane: one round trip for
-      // K <= 4096
-      for (int i0 = 0; i0 < nblk; i0 += 8 * 64) {
+      // K <= 4096.  With the feed-forward glue, x is [gate | up] (block i of h
+      // from blocks i and nblk + i) in batches of 4 blocks per lane.
+      const bool silu = (d.flags & kSiluMul) != 0;
+      const int batch = silu ? 4 * 64 : 8 * 64;
+      for (int i0 = 0; i0 < nblk; i0 += batch) {
         uint4 v[8];
-        if (tagged) {
+        if (silu) {
+          // h = fp16(silu(gate) * up), formed as soon as both blocks are in
+          auto glue = [&](uint4 g4, uint4 u4) {
+            const h8_t g = bits<h8_t>(g4), uu = bits<h8_t>(u4);
+            h8_t h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = silu_mul_h(g[e], uu[e]);
+            return bits<uint4>(h);
+          };
+          if (tagged) {
+            const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+                reinterpret_cast<unsigned char*>(done) + d.tag_in, 0, 0x7FFFFFFF, 0x00020000);
+            unsigned pend = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (i0 + u * 64 + lane < nblk) pend |= 1u << u;
+            for (unsigned it = 0;; ++it) {
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                if (pend & (1u << u)) {
+                  const int i = i0 + u * 64 + lane, iu = i + nblk;
+                  const u32x4_g a = __builtin_amdgcn_raw_buffer_load_b128(rt, 32 * i, 0, kCoherent);
+                  const u32x4_g c2 = __builtin_amdgcn_raw_buffer_load_b128(rt, 32 * i + 16, 0, kCoherent);
+                  const u32x4_g e = __builtin_amdgcn_raw_buffer_load_b128(rt, 32 * iu, 0, kCoherent);
+                  const u32x4_g f = __builtin_amdgcn_raw_buffer_load_b128(rt, 32 * iu + 16, 0, kCoherent);
+                  if (a[1] == epoch && a[3] == epoch && c2[1] == epoch && c2[3] == epoch &&
+                      e[1] == epoch && e[3] == epoch && f[1] == epoch && f[3] == epoch) {
+                    v[u] = glue(make_uint4(a[0], a[2], c2[0], c2[2]),
+                                make_uint4(e[0], e[2], f[0], f[2]));
+                    pend &= ~(1u << u);
+                  }
+                }
+              }
+              if (!__builtin_amdgcn_ballot_w64(pend != 0u)) break;
+              if (it > kTagSpinLimit) { err[0] = 4u; break; }
+              finish_upto(k - kSync, false);
+              __builtin_amdgcn_s_sleep(1);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int i = i0 + u * 64 + lane;
+              if (i < nblk) {
+                u32x4_g a, e;
+                if (coherent) {
+                  a = __builtin_amdgcn_raw_buffer_load_b128(rx, 16 * i, 0, kCoherent);
+                  e = __builtin_amdgcn_raw_buffer_load_b128(rx, 16 * (i + nblk), 0, kCoherent);
+                } else {
+                  a = __builtin_amdgcn_raw_buffer_load_b128(rx, 16 * i, 0, 0);
+                  e = __builtin_amdgcn_raw_buffer_load_b128(rx, 16 * (i + nblk), 0, 0);
+                }
+                v[u] = glue(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(e[0], e[1], e[2], e[3]));
+              }
+            }
+          }
+        } else if (tagged) {
           // block i = tagged pairs 4i .. 4i + 3 (two 16-byte loads from the
           // coherence point); a block is taken once all four carry this call's
           // epoch, and re-read until then
@@ -430,7 +489,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int i = i0 + u * 64 + lane;
-          if (i0 + u * 64 < nblk) {           // whole quads (nblk % 4 == 0): uniform
+          if (u * 64 < batch && i0 + u * 64 < nblk) {   // whole quads (nblk % 4 == 0): uniform
             float se = 0.f, so = 0.f;
             if (i < nblk) {
               xb[(i & 3) * maxG + (i >> 2)] = pair_order(v[u]);
@@ -761,7 +820,7 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
     s.C = C;
     s.steps = (int)((L.N + rps - 1) / rps);
     s.dep = -1;
-    s.flags = 0;
+    s.flags = L.x_op ? kSiluMul : 0;
     s.tag_in = s.tag_out = 0;
     s.pad[0] = s.pad[1] = 0;
     s.sbase = s.steps / p.grid;
@@ -794,9 +853,9 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
     std::vector<int> writers;
     for (int64_t i = k - 1; i >= 0; --i) {
       const StepLayer& Li = layers[i];
-      const bool raw = overlap(Li.y, 2 * Li.N, Lk.x, 2 * Lk.K);
+      const bool raw = overlap(Li.y, 2 * Li.N, Lk.x, 2 * Lk.x_cols());
       const bool waw = overlap(Li.y, 2 * Li.N, Lk.y, 2 * Lk.N);
-      const bool war = overlap(Li.x, 2 * Li.K, Lk.y, 2 * Lk.N);
+      const bool war = overlap(Li.x, 2 * Li.x_cols(), Lk.y, 2 * Lk.N);
       if (raw || waw) writers.push_back((int)i);
       if (raw) { ++raw_n; raw_h = (int)i; }
       if (waw || war) other = true;
@@ -806,7 +865,7 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
     if (tags && raw_n == 1 && !other && (!ordered || raw_h == (int)k - 1)) {
       const uintptr_t y0 = reinterpret_cast<uintptr_t>(layers[raw_h].y);
       const uintptr_t x0 = reinterpret_cast<uintptr_t>(Lk.x);
-      if (x0 >= y0 && x0 + 2 * (uintptr_t)Lk.K <= y0 + 2 * (uintptr_t)layers[raw_h].N &&
+      if (x0 >= y0 && x0 + 2 * (uintptr_t)Lk.x_cols() <= y0 + 2 * (uintptr_t)layers[raw_h].N &&
           (x0 - y0) % 4 == 0) {
         tag_src[(size_t)k] = raw_h;
         sk.dep = raw_h;

@@ -529,7 +529,7 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
   std::vector<int64_t> tiles((size_t)n);
   for (int64_t k = 0; k < n; ++k) {
     const StepLayer& L = layers[k];
-    if (L.K % 128 || L.K > 8192 || L.N >= (1 << 24)) return p;
+    if (L.K % 128 || L.K > 8192 || L.N >= (1 << 24) || L.x_op) return p;
     if (reinterpret_cast<uintptr_t>(L.scales) % 8) return p;   // 8-byte scale loads
     MStepDesc& s = p.desc[(size_t)k];
     s.W = reinterpret_cast<const uint4*>(L.words);

@@ -118,15 +118,30 @@ Q4_API size_t q4_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
 
 /* ------------------------------------------------------------ decode step -- */
 
-/* One GEMV of a decode step: y = W x (or Y = W X for M rows).  x/X: fp16 [M][K];
+/* How a descriptor's GEMV input is formed from the memory at x. */
+/* x is the input itself: fp16 [M][K]. */
+#define Q4_X_PLAIN 0u
+/* x is fp16 [M][2K], the output of a gate/up projection: gate = x[m][0 .. K),
+ * up = x[m][K .. 2K); the GEMV input is h[m][k] = fp16(silu(gate[m][k]) *
+ * up[m][k]) with silu(g) = g / (1 + exp(-g)), formed in fp32 and rounded to
+ * nearest even -- the step between the gate/up and down projections of the
+ * decode loop's feed-forward block (Zero TVM documentation, "Decode loop": gate,
+ * up, SiLU, multiply and down are one fused FFN).  h is never written to memory
+ * by the persistent kernel; it equals what q4_silu_mul writes (or differs from
+ * the exactly rounded value by at most one fp16 unit in the last place). */
+#define Q4_X_SILU_MUL 1u
+
+/* One GEMV of a decode step: y = W h(x) (or Y = W h(X) for M rows), h per x_op.
  * y/Y: fp16 [M][N]. */
 typedef struct q4_layer {
   const uint32_t* words;   /* [N][K/8]  */
   const uint16_t* scales;  /* [N][K/32] */
-  const uint16_t* x;       /* [M][K]    */
+  const uint16_t* x;       /* [M][K], or [M][2K] with Q4_X_SILU_MUL */
   uint16_t* y;             /* [M][N]    */
   int64_t N;
   int64_t K;
+  uint32_t x_op;           /* Q4_X_PLAIN or Q4_X_SILU_MUL */
+  uint32_t reserved;       /* must be 0 */
 } q4_layer;
 
 /* Run every descriptor as its own kernel launch, in list order on the stream. */
@@ -155,21 +170,27 @@ typedef struct q4_layer {
 /* q4_decode_step: run the GEMVs of layers[0 .. n_layers) in list order, as the
  * Zero TVM decode loop walks the projections of every layer and then the LM
  * head ("Decode loop").  The results are those of calling q4_gemv (M == 1) or
- * q4_gemv_batched (M > 1) on each descriptor in turn; a descriptor's x may be an
- * earlier descriptor's y.  Every descriptor is validated before anything is
- * enqueued.  `layers` is host memory, read during the call only.
+ * q4_gemv_batched (M > 1) on each descriptor in turn, after forming its input
+ * per x_op; a descriptor's x may lie in an earlier descriptor's y.  Every
+ * descriptor is validated before anything is enqueued.  `layers` is host memory,
+ * read during the call only.
  *
- * With M == 1, rows of at most K = 8192 and without Q4_STEP_LAUNCH_EACH, the
- * whole list runs as ONE persistent kernel (after a small kernel that clears the
- * workspace's completion counters): the weights of later GEMVs stream while
- * earlier ones finish, and dependencies are kept with per-GEMV completion
- * counters in the workspace.  The weights stream through registers (or, with
- * Q4_STEP_LDS_RING, through an LDS ring).  Its descriptor table is copied to device memory
- * the first time a given list is used (the library allocates that copy and keeps
- * it for later calls with the same list; at most 16 lists are kept, the least
- * recently used is freed with hipFree, which synchronises the device).  Make
- * the first call with a given list outside stream capture.  Other lists run one
- * kernel per descriptor.
+ * Without Q4_STEP_LAUNCH_EACH, a list whose rows are at most K = 8192 runs as ONE
+ * persistent kernel (M == 1; for 2 <= M <= 8, when every K is a multiple of 128,
+ * every scales pointer 8-byte aligned and every x_op Q4_X_PLAIN): the weights of
+ * later GEMVs stream while earlier ones finish.  A descriptor waits only for
+ * earlier ones it conflicts with (an earlier y overlapping its x or y, an earlier
+ * x overlapping its y; with Q4_STEP_ORDERED also its predecessor).  When its
+ * only conflict is one earlier descriptor whose y holds all of its x (M == 1),
+ * that y is also handed over through the workspace as tagged values the reader
+ * polls; other conflicts wait on per-descriptor completion counters in the
+ * workspace.  Lists whose conflicts one such wait cannot cover, and all other
+ * lists, run one kernel per descriptor.  The descriptor table of a persistent
+ * list is copied to device memory the first time the list is used (the library
+ * allocates that copy and keeps it for later calls with the same list; at most
+ * 16 lists are kept, the least recently used is freed with hipFree, which
+ * synchronises the device).  Make the first call with a given list outside
+ * stream capture.
  * ws: q4_decode_step_workspace_bytes(...) bytes, 16-byte aligned; calls that
  * share a workspace must be ordered on one stream. */
 Q4_API int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t flags,
@@ -177,6 +198,15 @@ Q4_API int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, u
 
 Q4_API size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, int64_t M,
                                       uint32_t flags);
+
+/* q4_silu_mul: out[m][i] = fp16(silu(gu[m][i]) * gu[m][H + i]) for m < M, i < H,
+ * with silu(g) = g / (1 + exp(-g)) in fp32, rounded to nearest even (silu(+inf)
+ * = +inf, silu(-inf) = -0, NaN propagates): the feed-forward glue between the
+ * gate/up and down projections (Zero TVM documentation, "Decode loop").  gu: fp16
+ * [M][2H] (gate | up per row); out: fp16 [M][H].  H % 8 == 0; both 16-byte
+ * aligned; out must not overlap gu.  M >= 1, M * H < 2^31. */
+Q4_API int q4_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t H,
+                       q4_stream_t stream);
 
 /* ------------------------------------------------------ measurement aids -- */
 

@@ -49,12 +49,15 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_layer_struct_matches_header():
-    # six 8-byte fields: four pointers and two int64
-    assert C.sizeof(q4.Layer) == 48
+    # four pointers, two int64, two uint32
+    assert C.sizeof(q4.Layer) == 56
     text = open(HEADER).read()
     body = re.search(r"typedef struct q4_layer \{(.*?)\} q4_layer;", text, re.S).group(1)
-    fields = re.findall(r"\b(words|scales|x|y|N|K)\s*;", body)
+    fields = re.findall(r"\b(words|scales|x|y|N|K|x_op|reserved)\s*;", body)
     assert fields == [f[0] for f in q4.Layer._fields_]
+    for name, val in (("Q4_X_PLAIN", q4.X_PLAIN), ("Q4_X_SILU_MUL", q4.X_SILU_MUL)):
+        m = re.search(r"#define %s (\w+)u" % name, text)
+        assert m and int(m.group(1), 0) == val, name
 
 
 def test_status_strings(lib):
@@ -126,6 +129,31 @@ def test_decode_step_validates_every_descriptor_first(lib):
     assert lib.q4_decode_step(layers, 0, 1, 0, None, 0, None) == 2
     assert lib.q4_decode_step(layers, 2, 9, 0, None, 0, None) == 2
     assert lib.q4_decode_step(layers, 2, 1, 0x80, None, 0, None) == 2 and "flags" in _err(lib)
+
+
+def test_decode_step_x_op_errors(lib):
+    layers = (q4.Layer * 2)()
+    layers[0] = q4.Layer(0x10000, 0x20000, 0x30000, 0x40000, 16, 64, 0, 0)
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x40000, 0x70000, 16, 64, 2, 0)   # unknown x_op
+    assert lib.q4_decode_step(layers, 2, 1, 0, None, 0, None) == 2
+    assert "layers[1]" in _err(lib) and "x_op" in _err(lib)
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x40000, 0x70000, 16, 64, 1, 7)   # reserved != 0
+    assert lib.q4_decode_step(layers, 2, 1, 0, None, 0, None) == 2 and "reserved" in _err(lib)
+    # with the glue, x spans 2K: a y inside that span overlaps it
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x80000, 0x80000 + 2 * 64 + 16, 16, 64, 1, 0)
+    assert lib.q4_decode_step(layers, 2, 1, 0, None, 0, None) == 2 and "overlap" in _err(lib)
+
+
+def test_silu_mul_argument_errors(lib):
+    f = lib.q4_silu_mul
+    assert f(None, Y, 1, 64, None) == 1
+    assert f(X, None, 1, 64, None) == 1
+    assert f(X, Y, 0, 64, None) == 2
+    assert f(X, Y, 1, 60, None) == 2 and "H" in _err(lib)
+    assert f(P(0x30008), Y, 1, 64, None) == 3
+    assert f(X, P(0x40008), 1, 64, None) == 3
+    assert f(X, P(0x30000 + 128), 1, 64, None) == 2 and "overlap" in _err(lib)
+    assert f(X, Y, 1 << 20, 1 << 12, None) == 6
 
 
 def test_probe_argument_errors(lib):
