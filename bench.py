@@ -285,6 +285,53 @@ def per_config(torch, q4, synth, np, stream):
     out["mlp_gate_up_down_m1"] = {"q4_gemv": _fig(b2, ms_launch, copies=len(d) // 2),
                                   "in_decode_step": _fig(b2, ms_step, copies=len(d) // 2)}
     del d
+    # the MLP with its glue: gate_up 3072 -> 16384, then down over fp16(silu(gate)
+    # * up): fused (the glue formed while down's input is staged, one decode-step
+    # list), as three calls per MLP (q4_gemv, q4_silu_mul, q4_gemv), and one
+    # kernel per GEMV (glue kernel, then each GEMV)
+    copies = 13
+    pairs = []
+    for c in range(copies):
+        mg = S.Matrix(f"bench/mlpg/c{c}/gate_up", 16384, 3072)
+        md = S.Matrix(f"bench/mlpg/c{c}/down", 3072, 8192)
+        to_t = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16)
+        pairs.append((mg.words_torch("cuda"), to_t(mg.scales()), md.words_torch("cuda"),
+                      to_t(md.scales()), torch.empty(16384, dtype=torch.float16, device="cuda"),
+                      torch.empty(3072, dtype=torch.float16, device="cuda")))
+    xg = torch.from_numpy(S.activations("bench/mlpg/x", 0, 3072).view(np.int16)).cuda().view(
+        torch.float16)
+    hbuf = torch.empty(8192, dtype=torch.float16, device="cuda")
+    b3 = (synth.algorithmic_bytes(1, 16384, 3072) + synth.algorithmic_bytes(1, 3072, 8192) +
+          2 * 8192)                                  # down reads gate | up
+    glue_layers = q4.make_layers(
+        [t for (Wg, Sg, Wd, Sd, gu, y) in pairs
+         for t in ((Wg, Sg, xg, gu), (Wd, Sd, gu, y, q4.X_SILU_MUL))])
+
+    def glue_step(flags):
+        nb = q4.q4_decode_step_workspace_bytes(glue_layers, 1, flags)
+        wsb = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
+
+        def fn(i):
+            q4.q4_decode_step(glue_layers, 1, flags | (q4.STEP_WS_CLEAN if i else 0), ws=wsb,
+                              ws_bytes=nb, stream=stream)
+        return fn
+    wsg = torch.empty(max(q4.q4_workspace_bytes(1, 16384, 3072),
+                          q4.q4_workspace_bytes(1, 3072, 8192), 16), dtype=torch.uint8,
+                      device="cuda")
+
+    def unfused(i):
+        Wg, Sg, Wd, Sd, gu, y = pairs[i % copies]
+        q4.q4_gemv(Wg, Sg, xg, gu, ws=wsg, stream=stream)
+        q4.q4_silu_mul(gu, hbuf, stream=stream)
+        q4.q4_gemv(Wd, Sd, hbuf, y, ws=wsg, stream=stream)
+    out["mlp_silu_gate_up_down_m1"] = {
+        "fused_decode_step": _fig(b3, _timed(torch, stream, glue_step(0), 5) / copies,
+                                  copies=copies),
+        "three_calls": _fig(b3, _timed(torch, stream, unfused, 4 * copies), copies=copies),
+        "decode_step_one_kernel_per_gemv": _fig(
+            b3, _timed(torch, stream, glue_step(q4.STEP_LAUNCH_EACH), 5) / copies,
+            copies=copies)}
+    del pairs, glue_layers
     # 2B-class sweep at M = 8 (one q4_gemv_batched kernel per GEMV)
     shapes = synth.sweep_shapes("2b")
     descs = []
