@@ -9,7 +9,8 @@ Definitions (Zero TVM documentation, section "Q4F16 quantization format"):
 eight 4-bit codes per uint32 word, nibble ``i`` = ``(word >> 4i) & 0xF``, one
 fp16 scale per 32 weights, weight = ``(code - 7) * scale``; y = W x.
 The feed-forward glue between the gate/up and down projections ("Decode loop"):
-fp16(silu(gate) * up).
+fp16(silu(gate) * up); and the steps around the GEMVs: the token's embedding row,
+RMSNorm, the residual add with RMSNorm, the argmax over the logits.
 
 Parity pins for every function here live in ``tests/test_oracle.py``.
 """
@@ -69,6 +70,14 @@ def _load():
             lib.orc_row_norms.restype = C.c_int
             lib.orc_silu_mul.argtypes = [p, p, i64, i64]
             lib.orc_silu_mul.restype = None
+            lib.orc_embed_rows.argtypes = [p, p, i64, i64, p, i64, p]
+            lib.orc_embed_rows.restype = None
+            lib.orc_rmsnorm.argtypes = [p, p, C.c_double, i64, i64, p]
+            lib.orc_rmsnorm.restype = None
+            lib.orc_add_rmsnorm.argtypes = [p, p, p, C.c_double, i64, i64, p, p]
+            lib.orc_add_rmsnorm.restype = None
+            lib.orc_argmax.argtypes = [p, i64, i64, p]
+            lib.orc_argmax.restype = None
             lib.orc_vec_norm.argtypes = [p, i64]
             lib.orc_vec_norm.restype = C.c_double
             _lib = lib
@@ -185,6 +194,51 @@ def silu_mul(gu, H: int | None = None) -> np.ndarray:
     out = np.empty((g2.shape[0], Hh), np.uint16)
     _load().orc_silu_mul(_ptr(g2), _ptr(out), g2.shape[0], Hh)
     return out.reshape(g.shape[:-1] + (Hh,))
+
+
+def embed_rows(words, scales, tokens) -> np.ndarray:
+    """fp16 bits [M][K]: the dequantised rows tokens[m] of a q4f16_1 table."""
+    w = _c(words, np.uint32)
+    sc = _c(scales, np.uint16)
+    t = _c(tokens, np.int32).reshape(-1)
+    N, K = w.shape[0], 8 * w.shape[1]
+    out = np.empty((len(t), K), np.uint16)
+    _load().orc_embed_rows(_ptr(w), _ptr(sc), N, K, _ptr(t), len(t), _ptr(out))
+    return out
+
+
+def rmsnorm(x, gamma, eps: float) -> np.ndarray:
+    """fp16 bits of RMSNorm(x) * gamma per row (fp64; eps as the fp32 the kernels take)."""
+    xs = _c(x, np.uint16)
+    x2 = xs.reshape(-1, xs.shape[-1])
+    g = _c(gamma, np.uint16).reshape(-1)
+    out = np.empty_like(x2)
+    _load().orc_rmsnorm(_ptr(x2), _ptr(g), float(np.float32(eps)), x2.shape[0], x2.shape[1],
+                        _ptr(out))
+    return out.reshape(xs.shape)
+
+
+def add_rmsnorm(delta, res_in, gamma, eps: float):
+    """(res_out, out) fp16 bits: res_out = fp16(res_in + delta), out = RMSNorm(res_out)."""
+    d = _c(delta, np.uint16)
+    r = _c(res_in, np.uint16)
+    d2 = d.reshape(-1, d.shape[-1])
+    r2 = r.reshape(d2.shape)
+    g = _c(gamma, np.uint16).reshape(-1)
+    res_out = np.empty_like(d2)
+    out = np.empty_like(d2)
+    _load().orc_add_rmsnorm(_ptr(d2), _ptr(r2), _ptr(g), float(np.float32(eps)), d2.shape[0],
+                            d2.shape[1], _ptr(res_out), _ptr(out))
+    return res_out.reshape(d.shape), out.reshape(d.shape)
+
+
+def argmax(x) -> np.ndarray:
+    """int32 [M]: largest fp16 value per row, ties to the lowest index, NaN skipped."""
+    xs = _c(x, np.uint16)
+    x2 = xs.reshape(-1, xs.shape[-1])
+    out = np.empty(x2.shape[0], np.int32)
+    _load().orc_argmax(_ptr(x2), x2.shape[0], x2.shape[1], _ptr(out))
+    return out
 
 
 def vec_norm(x) -> float:

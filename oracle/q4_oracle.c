@@ -265,6 +265,76 @@ ORC_EXPORT void orc_silu_mul(const uint16_t* GU, uint16_t* OUT, int64_t M, int64
     }
 }
 
+/* ------------------------------------------------ the rest of a decode step */
+
+/* The steps of the decode loop around its GEMVs (Zero TVM documentation,
+ * "Decode loop"): the token's embedding row, RMSNorm, the residual add fused with
+ * RMSNorm ("addNorm"), and the argmax over the LM head's logits. */
+
+/* OUT[m][k] = fp16((q[t][k] - 7) * s[t][k/32]) with t = TOK[m], the embedding
+ * table being a q4f16_1 matrix [N][K] (one row per token); a token outside
+ * [0, N) gives a row of NaN. */
+ORC_EXPORT void orc_embed_rows(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
+                               const int32_t* TOK, int64_t M, uint16_t* OUT) {
+  for (int64_t m = 0; m < M; ++m) {
+    const int64_t t = TOK[m];
+    for (int64_t k = 0; k < K; ++k) {
+      if (t < 0 || t >= N) {
+        OUT[m * K + k] = 0x7E00;
+        continue;
+      }
+      double w = (double)((int)code_at(words, K, t, k) - 7) *
+                 orc_half_to_f64(scales[t * (K / 32) + k / 32]);
+      OUT[m * K + k] = orc_f64_to_half(w);
+    }
+  }
+}
+
+/* RMSNorm of fp16 rows: OUT[m][k] = fp16(X[m][k] / sqrt(mean_k X[m][k]^2 + eps)
+ * * GAMMA[k]), in fp64. */
+ORC_EXPORT void orc_rmsnorm(const uint16_t* X, const uint16_t* GAMMA, double eps, int64_t M,
+                            int64_t K, uint16_t* OUT) {
+  for (int64_t m = 0; m < M; ++m) {
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double v = orc_half_to_f64(X[m * K + k]);
+      ss += v * v;
+    }
+    double r = 1.0 / sqrt(ss / (double)K + eps);
+    for (int64_t k = 0; k < K; ++k)
+      OUT[m * K + k] = orc_f64_to_half(orc_half_to_f64(X[m * K + k]) * r *
+                                       orc_half_to_f64(GAMMA[k]));
+  }
+}
+
+/* The residual add and RMSNorm: RES_OUT = fp16(RES_IN + DELTA) (the exact sum
+ * rounded once), OUT = RMSNorm(RES_OUT) as orc_rmsnorm. */
+ORC_EXPORT void orc_add_rmsnorm(const uint16_t* DELTA, const uint16_t* RES_IN,
+                                const uint16_t* GAMMA, double eps, int64_t M, int64_t K,
+                                uint16_t* RES_OUT, uint16_t* OUT) {
+  for (int64_t i = 0; i < M * K; ++i)
+    RES_OUT[i] = orc_f64_to_half(orc_half_to_f64(RES_IN[i]) + orc_half_to_f64(DELTA[i]));
+  orc_rmsnorm(RES_OUT, GAMMA, eps, M, K, OUT);
+}
+
+/* OUT[m] = the index of the largest value of row m of X [M][N] (fp16); ties go to
+ * the lowest index; NaN entries are skipped (a row of NaN gives 0). */
+ORC_EXPORT void orc_argmax(const uint16_t* X, int64_t M, int64_t N, int32_t* OUT) {
+  for (int64_t m = 0; m < M; ++m) {
+    int64_t best = -1;
+    double bv = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      double v = orc_half_to_f64(X[m * N + n]);
+      if (isnan(v)) continue;
+      if (best < 0 || v > bv) {
+        best = n;
+        bv = v;
+      }
+    }
+    OUT[m] = (int32_t)(best < 0 ? 0 : best);
+  }
+}
+
 /* ||x||_2 of an fp16 vector. */
 ORC_EXPORT double orc_vec_norm(const uint16_t* x, int64_t K) {
   double acc = 0.0;

@@ -416,3 +416,129 @@ def test_silu_pins_catch_planted_mistake(name):
         ref = _np_silu_mul(g, u)
         ok = ~np.isnan(ref.view(np.float16))
         assert not np.array_equal(out[ok], ref[ok]), name
+
+
+# ------------------------------------------- embedding, norms and argmax pins
+
+def test_embed_rows_vs_numpy_decode():
+    """Rows picked by token id, dequantised as (code - 7) * scale and rounded by
+    numpy's float16 cast; out-of-range ids give NaN rows."""
+    N, K = 50, 96
+    c = synth.codes("t/emb", 1, N * K).reshape(N, K)
+    w = oracle.pack(c)
+    s = synth.scales_uniform("t/embs", 1, N * K // 32, 0.005, 0.02).reshape(N, K // 32)
+    tok = np.array([0, 7, 49, 7, -1, 50], np.int32)
+    out = oracle.embed_rows(w, s, tok)
+    sv = s.view(np.float16).astype(np.float64)
+    for m, t in enumerate(tok):
+        if 0 <= t < N:
+            ref = ((c[t].astype(np.float64) - 7) * np.repeat(sv[t], 32)).astype(np.float16)
+            assert np.array_equal(out[m], ref.view(np.uint16))
+        else:
+            assert np.all(np.isnan(out[m].view(np.float16)))
+    # large scales: products beyond fp16's 11 bits round (to nearest even)
+    s2 = np.full((N, K // 32), np.float16(1000.0 + 1.0 / 4)).view(np.uint16)
+    out2 = oracle.embed_rows(w, s2, np.array([3], np.int32))[0]
+    ref2 = ((c[3].astype(np.float64) - 7) * 1000.25).astype(np.float16).view(np.uint16)
+    assert np.array_equal(out2, ref2)
+
+
+def _np_rmsnorm(x16, g16, eps):
+    x = x16.view(np.float16).astype(np.float64)
+    g = g16.view(np.float16).astype(np.float64)
+    r = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + float(np.float32(eps)))
+    return (x * r * g).astype(np.float16).view(np.uint16)
+
+
+def test_rmsnorm_vs_numpy_and_closed_forms():
+    rng = np.random.default_rng(5)
+    M, K = 4, 3072
+    x = (rng.standard_normal((M, K)) * 3).astype(np.float16).view(np.uint16)
+    g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float16).view(np.uint16)
+    for eps in (1e-5, 1e-6, 0.5):
+        assert np.array_equal(oracle.rmsnorm(x, g, eps), _np_rmsnorm(x, g, eps))
+    # a constant row c with gamma 1: every output is c / sqrt(c^2 + eps)
+    c = np.full((1, 256), np.float16(2.0)).view(np.uint16)
+    one = np.full(256, np.float16(1.0)).view(np.uint16)
+    out = oracle.rmsnorm(c, one, 1e-5)[0].view(np.float16).astype(np.float64)
+    assert np.all(out == np.float16(2.0 / np.sqrt(4.0 + float(np.float32(1e-5)))))
+    # one-hot row: x_k = a at one k -> a / sqrt(a^2 / K + eps) there, 0 elsewhere
+    oh = np.zeros((1, 64), np.float16)
+    oh[0, 5] = 3.0
+    out = oracle.rmsnorm(oh.view(np.uint16), np.full(64, np.float16(1.0)).view(np.uint16), 0.0)
+    out = out[0].view(np.float16).astype(np.float64)
+    assert out[5] == np.float16(8.0) and not out[:5].any() and not out[6:].any()
+
+
+def test_add_rmsnorm_vs_numpy():
+    rng = np.random.default_rng(6)
+    M, K = 3, 1024
+    a = (rng.standard_normal((M, K)) * 50).astype(np.float16).view(np.uint16)
+    b = (rng.standard_normal((M, K)) * 0.01).astype(np.float16).view(np.uint16)
+    g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float16).view(np.uint16)
+    res, out = oracle.add_rmsnorm(b, a, g, 1e-5)
+    ref_res = (a.view(np.float16).astype(np.float64) +
+               b.view(np.float16).astype(np.float64)).astype(np.float16).view(np.uint16)
+    assert np.array_equal(res, ref_res)
+    assert np.array_equal(out, _np_rmsnorm(ref_res, g, 1e-5))
+    # fp16 overflow of the sum gives inf, as fp16 rounding does
+    big = np.full((1, 32), np.float16(60000.0)).view(np.uint16)
+    res2, _ = oracle.add_rmsnorm(big, big, np.full(32, np.float16(1.0)).view(np.uint16), 1e-5)
+    assert np.all(np.isposinf(res2.view(np.float16)))
+
+
+def test_argmax_vs_numpy_ties_and_nan():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, 32064)).astype(np.float16)
+    x[1, [100, 2000, 30000]] = np.float16(60000.0)      # ties: lowest index
+    x[2, :] = np.float16(-np.inf)
+    x[2, 777] = np.float16(-65504.0)
+    x[3, 10] = np.float16(np.nan)
+    x[3, 11] = np.float16(30000.0)
+    out = oracle.argmax(x.view(np.uint16))
+    assert list(out[:4]) == [int(np.argmax(x[0])), 100, 777, 11]
+    assert out[4] == int(np.nanargmax(x[4].astype(np.float64)))
+    allnan = np.full((1, 8), np.float16(np.nan)).view(np.uint16)
+    assert oracle.argmax(allnan)[0] == 0
+
+
+STEP_MUTATIONS = {
+    "embed_zero_point": ("double w = (double)((int)code_at(words, K, t, k) - 7) *",
+                         "double w = (double)((int)code_at(words, K, t, k) - 8) *"),
+    "rms_mean_not_sum": ("double r = 1.0 / sqrt(ss / (double)K + eps);",
+                         "double r = 1.0 / sqrt(ss + eps);"),
+    "argmax_last_tie": ("if (best < 0 || v > bv) {", "if (best < 0 || v >= bv) {"),
+    "add_drops_delta": ("RES_OUT[i] = orc_f64_to_half(orc_half_to_f64(RES_IN[i]) + orc_half_to_f64(DELTA[i]));",
+                        "RES_OUT[i] = orc_f64_to_half(orc_half_to_f64(RES_IN[i]));"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+@pytest.mark.parametrize("name", sorted(STEP_MUTATIONS))
+def test_step_pins_catch_planted_mistake(name, monkeypatch):
+    """Each planted mistake makes one of the pins above fail."""
+    src = open(os.path.join(ROOT, "oracle", "q4_oracle.c")).read()
+    a, b = STEP_MUTATIONS[name]
+    assert a in src, name
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "m.c")
+        open(path, "w").write(src.replace(a, b))
+        so = os.path.join(tmp, "m.so")
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-o", so,
+                               path, "-lm"])
+        real = oracle._load()
+        mutant = C.CDLL(so)
+        for fn in ("orc_embed_rows", "orc_rmsnorm", "orc_add_rmsnorm", "orc_argmax",
+                   "orc_half_to_f64", "orc_f64_to_half", "orc_unpack", "orc_pack"):
+            f = getattr(mutant, fn)
+            f.argtypes = getattr(real, fn).argtypes
+            f.restype = getattr(real, fn).restype
+        monkeypatch.setattr(oracle, "_lib", mutant)
+        failed = 0
+        for pin in (test_embed_rows_vs_numpy_decode, test_rmsnorm_vs_numpy_and_closed_forms,
+                    test_add_rmsnorm_vs_numpy, test_argmax_vs_numpy_ties_and_nan):
+            try:
+                pin()
+            except AssertionError:
+                failed += 1
+        assert failed, name
