@@ -34,6 +34,7 @@ STEP_LDS_RING = 0x4
 STEP_WS_CLEAN = 0x8
 X_PLAIN = 0
 X_SILU_MUL = 1
+TOKENS_EAGER = 0x1
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
           4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED"}
@@ -52,6 +53,24 @@ class Layer(C.Structure):
     _fields_ = [("words", C.c_void_p), ("scales", C.c_void_p), ("x", C.c_void_p),
                 ("y", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64),
                 ("x_op", C.c_uint32), ("reserved", C.c_uint32)]
+
+
+class Weight(C.Structure):
+    """q4_weight: one q4f16_1 matrix in device memory."""
+    _fields_ = [("words", C.c_void_p), ("scales", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64)]
+
+
+class Block(C.Structure):
+    """q4_block: one transformer block (attention at a single position)."""
+    _fields_ = [("qkv", Weight), ("o", Weight), ("gate_up", Weight), ("down", Weight),
+                ("attn_norm", C.c_void_p), ("ffn_norm", C.c_void_p)]
+
+
+class ModelDesc(C.Structure):
+    """q4_model."""
+    _fields_ = [("n_blocks", C.c_int64), ("D", C.c_int64), ("F", C.c_int64), ("V", C.c_int64),
+                ("embed", Weight), ("blocks", C.c_void_p), ("final_norm", C.c_void_p),
+                ("lm_head", Weight), ("eps", C.c_float)]
 
 
 def lib_path() -> str:
@@ -84,6 +103,13 @@ def load():
             "q4_decode_step": ([p, i64, i64, C.c_uint32, p, sz, p], i32),
             "q4_decode_step_workspace_bytes": ([p, i64, i64, C.c_uint32], sz),
             "q4_silu_mul": ([p, p, i64, i64, p], i32),
+            "q4_embed_rows": ([p, p, i64, i64, p, i64, p, p], i32),
+            "q4_rmsnorm": ([p, p, C.c_float, i64, i64, p, p], i32),
+            "q4_add_rmsnorm": ([p, p, p, C.c_float, i64, i64, p, p, p], i32),
+            "q4_argmax": ([p, i64, i64, p, p], i32),
+            "q4_decode_token_workspace_bytes": ([p], sz),
+            "q4_decode_token": ([p, p, p, p, p, sz, p], i32),
+            "q4_decode_tokens": ([p, p, i64, p, sz, C.c_uint32, p], i32),
             "q4_probe_read": ([p, sz, p, i64, p], i32),
             "q4_probe_copy": ([p, p, sz, p], i32),
         }
@@ -270,6 +296,110 @@ def q4_silu_mul(gu, out=None, stream=None):
         out = torch.empty((M, H) if gu.dim() == 2 else (H,), dtype=torch.float16, device=gu.device)
     _check(load().q4_silu_mul(_ptr(gu), _ptr(out), M, H, _stream(stream)))
     return out
+
+
+def q4_embed_rows(words, scales, tokens, out=None, stream=None):
+    """Dequantised rows tokens[m] (int32 device tensor) of a q4f16_1 table."""
+    torch = _torch()
+    N, K = words.shape[0], 8 * words.shape[1]
+    M = tokens.numel()
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float16, device=words.device)
+    _check(load().q4_embed_rows(_ptr(words), _ptr(scales), N, K, _ptr(tokens), M, _ptr(out),
+                                _stream(stream)))
+    return out
+
+
+def q4_rmsnorm(x, gamma, eps: float, out=None, stream=None):
+    torch = _torch()
+    K = gamma.numel()
+    M = x.numel() // K
+    if out is None:
+        out = torch.empty_like(x)
+    _check(load().q4_rmsnorm(_ptr(x), _ptr(gamma), float(eps), M, K, _ptr(out), _stream(stream)))
+    return out
+
+
+def q4_add_rmsnorm(delta, res_in, gamma, eps: float, res_out=None, out=None, stream=None):
+    """(res_out, out): res_out = res_in + delta, out = RMSNorm(res_out) * gamma."""
+    torch = _torch()
+    K = gamma.numel()
+    M = delta.numel() // K
+    if res_out is None:
+        res_out = torch.empty_like(res_in)
+    if out is None:
+        out = torch.empty_like(res_in)
+    _check(load().q4_add_rmsnorm(_ptr(delta), _ptr(res_in), _ptr(gamma), float(eps), M, K,
+                                 _ptr(res_out), _ptr(out), _stream(stream)))
+    return res_out, out
+
+
+def q4_argmax(x, out=None, stream=None):
+    """int32 [M]: index of the largest value per row (ties: lowest; NaN skipped)."""
+    torch = _torch()
+    x2 = x if x.dim() == 2 else x.reshape(1, -1)
+    M, N = x2.shape
+    if out is None:
+        out = torch.empty(M, dtype=torch.int32, device=x.device)
+    _check(load().q4_argmax(_ptr(x), M, N, _ptr(out), _stream(stream)))
+    return out
+
+
+def _weight(ws):
+    w, sc = ws
+    return Weight(w.data_ptr(), sc.data_ptr(), w.shape[0], 8 * w.shape[1])
+
+
+class Model:
+    """A q4_model for q4_decode_token(s): keeps every tensor it points at alive.
+
+    embed, lm_head: (words, scales); blocks: sequence of dicts with keys qkv, o,
+    gate_up, down ((words, scales) each), attn_norm, ffn_norm (fp16 tensors)."""
+
+    def __init__(self, embed, blocks, final_norm, lm_head, eps: float = 1e-5):
+        self._keep = [embed, blocks, final_norm, lm_head]
+        blocks = list(blocks)
+        self.blocks = (Block * max(len(blocks), 1))()
+        for i, b in enumerate(blocks):
+            self.blocks[i] = Block(_weight(b["qkv"]), _weight(b["o"]), _weight(b["gate_up"]),
+                                   _weight(b["down"]), b["attn_norm"].data_ptr(),
+                                   b["ffn_norm"].data_ptr())
+        D = embed[0].shape[1] * 8
+        F = blocks[0]["down"][0].shape[1] * 8 if blocks else 32
+        V = embed[0].shape[0]
+        self.desc = ModelDesc(len(blocks), D, F, V, _weight(embed),
+                              C.cast(self.blocks, C.c_void_p).value if blocks else None,
+                              final_norm.data_ptr(), _weight(lm_head), eps)
+        self.D, self.F, self.V = D, F, V
+
+    def ref(self):
+        return C.byref(self.desc)
+
+
+def q4_decode_token_workspace_bytes(model: Model) -> int:
+    return int(load().q4_decode_token_workspace_bytes(model.ref()))
+
+
+def q4_decode_token(model: Model, token_in, token_out, logits=None, ws=None, stream=None):
+    """One decode step: token_in[0] -> token_out[0] (int32 device tensors)."""
+    torch = _torch()
+    need = q4_decode_token_workspace_bytes(model)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _check(load().q4_decode_token(model.ref(), _ptr(token_in), _ptr(token_out), _ptr(logits),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def q4_decode_tokens(model: Model, tokens, steps: int, ws=None, flags: int = 0, stream=None):
+    """`steps` decode steps: tokens[i] -> tokens[i + 1] (int32 device tensor)."""
+    torch = _torch()
+    need = q4_decode_token_workspace_bytes(model)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _check(load().q4_decode_tokens(model.ref(), _ptr(tokens), steps, _ptr(ws), ws.numel(), flags,
+                                   _stream(stream)))
+    return ws
 
 
 def q4_probe_read(buf, sink, blocks: int = 0, stream=None):

@@ -102,6 +102,18 @@ q4::DeviceInfo g_dev[64];
 
 namespace q4 {
 
+int api_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int api_ok() { return ok(); }
+
 const DeviceInfo* device_info() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
@@ -486,6 +498,80 @@ int q4_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t H, q4_stre
     return fail(Q4_ERR_SHAPE, "q4_silu_mul: out overlaps gu");
   hipError_t e = q4::launch_silu_mul(gu, out, M, H, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : device_error(e, "q4_silu_mul");
+}
+
+int q4_embed_rows(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
+                  const int32_t* tokens, int64_t M, uint16_t* out, q4_stream_t stream) {
+  if (!words || !scales || !tokens || !out) return fail(Q4_ERR_NULL, "q4_embed_rows: NULL pointer");
+  if (int rc = check_shape(N, K)) return fail(rc, "q4_embed_rows: %s", g_error.c_str());
+  if (M < 1 || M > 65535) return fail(Q4_ERR_SHAPE, "q4_embed_rows: M = %lld", (long long)M);
+  if (!aligned(words, 16) || !aligned(out, 16) || !aligned(scales, 2) || !aligned(tokens, 4))
+    return fail(Q4_ERR_ALIGN, "q4_embed_rows: misaligned pointer");
+  hipError_t e = q4::launch_embed_rows(words, scales, N, K, tokens, M, out,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_embed_rows");
+}
+
+namespace {
+bool spans_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+int check_rows(const char* what, int64_t M, int64_t K) {
+  if (M < 1 || K < 8 || K % 8)
+    return fail(Q4_ERR_SHAPE, "%s: M = %lld, K = %lld: need M >= 1, K %% 8 == 0", what,
+                (long long)M, (long long)K);
+  if (M > INT32_MAX || K / 8 > INT32_MAX)
+    return fail(Q4_ERR_UNSUPPORTED, "%s: M = %lld, K = %lld: too large", what, (long long)M,
+                (long long)K);
+  return Q4_OK;
+}
+}  // namespace
+
+int q4_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M, int64_t K,
+               uint16_t* out, q4_stream_t stream) {
+  if (!x || !gamma || !out) return fail(Q4_ERR_NULL, "q4_rmsnorm: NULL pointer");
+  if (int rc = check_rows("q4_rmsnorm", M, K)) return rc;
+  if (!(eps >= 0.f)) return fail(Q4_ERR_SHAPE, "q4_rmsnorm: eps must be >= 0");
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(out, 16))
+    return fail(Q4_ERR_ALIGN, "q4_rmsnorm: pointers not 16-byte aligned");
+  if (spans_overlap(out, 2 * M * K, x, 2 * M * K) || spans_overlap(out, 2 * M * K, gamma, 2 * K))
+    return fail(Q4_ERR_SHAPE, "q4_rmsnorm: out overlaps an input");
+  hipError_t e = q4::launch_rmsnorm(nullptr, x, gamma, eps, M, K, nullptr, out,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_rmsnorm");
+}
+
+int q4_add_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const uint16_t* gamma, float eps,
+                   int64_t M, int64_t K, uint16_t* res_out, uint16_t* out, q4_stream_t stream) {
+  if (!delta || !res_in || !gamma || !res_out || !out)
+    return fail(Q4_ERR_NULL, "q4_add_rmsnorm: NULL pointer");
+  if (int rc = check_rows("q4_add_rmsnorm", M, K)) return rc;
+  if (!(eps >= 0.f)) return fail(Q4_ERR_SHAPE, "q4_add_rmsnorm: eps must be >= 0");
+  if (!aligned(delta, 16) || !aligned(res_in, 16) || !aligned(gamma, 16) ||
+      !aligned(res_out, 16) || !aligned(out, 16))
+    return fail(Q4_ERR_ALIGN, "q4_add_rmsnorm: pointers not 16-byte aligned");
+  const int64_t rb = 2 * M * K;
+  if ((res_out != res_in && spans_overlap(res_out, rb, res_in, rb)) ||
+      spans_overlap(res_out, rb, delta, rb) || spans_overlap(res_out, rb, gamma, 2 * K))
+    return fail(Q4_ERR_SHAPE, "q4_add_rmsnorm: res_out overlaps an input");
+  if (spans_overlap(out, rb, delta, rb) || spans_overlap(out, rb, res_in, rb) ||
+      spans_overlap(out, rb, gamma, 2 * K) || spans_overlap(out, rb, res_out, rb))
+    return fail(Q4_ERR_SHAPE, "q4_add_rmsnorm: out overlaps another argument");
+  hipError_t e = q4::launch_rmsnorm(delta, res_in, gamma, eps, M, K, res_out, out,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_add_rmsnorm");
+}
+
+int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_stream_t stream) {
+  if (!x || !out) return fail(Q4_ERR_NULL, "q4_argmax: NULL pointer");
+  if (M < 1 || N < 1 || M > INT32_MAX || N > INT32_MAX)
+    return fail(Q4_ERR_SHAPE, "q4_argmax: M = %lld, N = %lld", (long long)M, (long long)N);
+  if (!aligned(x, 2) || !aligned(out, 4)) return fail(Q4_ERR_ALIGN, "q4_argmax: misaligned");
+  if (spans_overlap(out, 4 * M, x, 2 * M * N))
+    return fail(Q4_ERR_SHAPE, "q4_argmax: out overlaps x");
+  hipError_t e = q4::launch_argmax(x, M, N, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_argmax");
 }
 
 int q4_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t blocks,

@@ -29,6 +29,11 @@ struct DeviceInfo {
 // Properties of the current device (cached per device); nullptr if no device.
 const DeviceInfo* device_info();
 
+// The entry points' error reporting (q4_api.cpp): set the calling thread's error
+// text and return the status.
+int api_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int api_ok();
+
 // One GEMV as the kernels see it.
 struct GemvArgs {
   const uint32_t* words;             // [N][K/8]
@@ -77,6 +82,23 @@ __device__ __forceinline__ _Float16 silu_mul_h(_Float16 g, _Float16 u) {
 // out[m][i] = silu_mul_h(gu[m][i], gu[m][H + i]); H % 8 == 0, 16-byte aligned.
 hipError_t launch_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t H,
                            hipStream_t s);
+
+// The operations around the GEMVs (q4_ops.hip).  delta == nullptr: plain RMSNorm.
+hipError_t launch_embed_rows(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
+                             const int32_t* tokens, int64_t M, uint16_t* out, hipStream_t s);
+hipError_t launch_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const uint16_t* gamma,
+                          float eps, int64_t M, int64_t K, uint16_t* res_out, uint16_t* out,
+                          hipStream_t s);
+hipError_t launch_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, hipStream_t s);
+
+// Device-side token bookkeeping of a multi-step decode (q4_ops.hip):
+// cur[0] = tokens[counter[0]]; tokens[counter[0] + 1] = out[0] and counter[0] += 1;
+// counter[0] = 0.
+hipError_t launch_token_fetch(const int32_t* tokens, const int32_t* counter, int32_t* cur,
+                              hipStream_t s);
+hipError_t launch_token_store(int32_t* tokens, int32_t* counter, const int32_t* out,
+                              hipStream_t s);
+hipError_t launch_counter_reset(int32_t* counter, hipStream_t s);
 
 hipError_t launch_probe_read(const DeviceInfo& d, const void* buf, size_t bytes, uint32_t* sink,
                              int64_t blocks, hipStream_t s);

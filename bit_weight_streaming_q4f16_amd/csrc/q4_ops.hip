@@ -1,0 +1,195 @@
+// The steps of the decode loop around its GEMVs (Zero TVM documentation, "Decode
+// loop"): the token's embedding row from a q4f16_1 table, RMSNorm, the residual
+// add fused with RMSNorm ("addNorm"), and the argmax over the LM head's logits.
+// Each is one small kernel, one workgroup per row; they move a few KB each, so
+// what they cost is their launch and one memory round trip.
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+
+template <typename T, typename F>
+__device__ __forceinline__ T bits(F v) {
+  return __builtin_bit_cast(T, v);
+}
+
+// Sum over the 256 threads of a workgroup (every thread gets the total).
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float t = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return t;
+}
+
+// One thread per 32-weight group of the chosen row: (q - 7) * s is exact in fp32
+// (a 4-bit integer times an fp16), so each output is rounded once.
+__global__ __launch_bounds__(kBlock) void k_embed_rows(const uint4* __restrict__ words,
+                                                       const uint16_t* __restrict__ scales,
+                                                       int64_t N, int G,
+                                                       const int32_t* __restrict__ tokens,
+                                                       uint4* __restrict__ out) {
+  const int m = blockIdx.y;
+  const int g = blockIdx.x * kBlock + threadIdx.x;
+  if (g >= G) return;
+  const int64_t t = tokens[m];
+  uint4* o = out + ((int64_t)m * G + g) * 4;
+  if (t < 0 || t >= N) {
+    const uint4 nan4 = make_uint4(0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = nan4;
+    return;
+  }
+  const uint4 w = words[t * G + g];
+  const float s = (float)bits<_Float16>(scales[t * G + g]);
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h8_t h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)((float)((int)((wv[j] >> (4 * i)) & 0xFu) - 7) * s);
+    o[j] = bits<uint4>(h);
+  }
+}
+
+// RMSNorm of one row per workgroup, blocks of 8 halves; with `delta`, the row is
+// first res_out = fp16(res_in + delta) (a native fp16 add: rounded once).  The
+// second pass re-reads what this thread read or wrote in the first.
+__global__ __launch_bounds__(kBlock) void k_rmsnorm(const uint4* __restrict__ delta,
+                                                    const uint4* res_in,
+                                                    const uint4* __restrict__ gamma, float eps,
+                                                    int blocks, uint4* res_out,
+                                                    uint4* __restrict__ out) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint4* x = res_in + row * blocks;
+  uint4* r = res_out ? res_out + row * blocks : nullptr;
+  float ss = 0.f;
+  for (int b = threadIdx.x; b < blocks; b += kBlock) {
+    h8_t v = bits<h8_t>(x[b]);
+    if (delta) {
+      v = v + bits<h8_t>(delta[row * blocks + b]);
+      r[b] = bits<uint4>(v);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float f = (float)v[i];
+      ss = __builtin_fmaf(f, f, ss);
+    }
+  }
+  const float tot = block_sum(ss, red);
+  const float rs = 1.f / __builtin_sqrtf(tot / (float)(blocks * 8) + eps);
+  const uint4* src = delta ? r : x;
+  for (int b = threadIdx.x; b < blocks; b += kBlock) {
+    const h8_t v = bits<h8_t>(src[b]), g = bits<h8_t>(gamma[b]);
+    h8_t o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (_Float16)((float)v[i] * rs * (float)g[i]);
+    out[row * blocks + b] = bits<uint4>(o);
+  }
+}
+
+// Largest value of a row, ties to the lowest index, NaN skipped (none: 0).
+__global__ __launch_bounds__(kBlock) void k_argmax(const uint16_t* __restrict__ x, int64_t N,
+                                                   int32_t* __restrict__ out) {
+  __shared__ float sv[4];
+  __shared__ int64_t si[4];
+  const int64_t row = blockIdx.x;
+  float bv = 0.f;
+  int64_t bi = -1;
+  for (int64_t n = threadIdx.x; n < N; n += kBlock) {
+    const float v = (float)bits<_Float16>(x[row * N + n]);
+    if (v != v) continue;
+    if (bi < 0 || v > bv) {
+      bv = v;
+      bi = n;
+    }
+  }
+  // better: a value (bi >= 0) that is larger, or equal with a lower index
+  auto take = [](float& v, int64_t& i, float ov, int64_t oi) {
+    if (oi >= 0 && (i < 0 || ov > v || (ov == v && oi < i))) {
+      v = ov;
+      i = oi;
+    }
+  };
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int64_t oi = __shfl_xor(bi, o, 64);
+    take(bv, bi, ov, oi);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = sv[0];
+    int64_t i = si[0];
+    for (int w = 1; w < 4; ++w) take(v, i, sv[w], si[w]);
+    out[row] = (int32_t)(i < 0 ? 0 : i);
+  }
+}
+
+__global__ void k_token_fetch(const int32_t* tokens, const int32_t* counter, int32_t* cur) {
+  cur[0] = tokens[counter[0]];
+}
+
+__global__ void k_token_store(int32_t* tokens, int32_t* counter, const int32_t* out) {
+  const int32_t c = counter[0];
+  tokens[c + 1] = out[0];
+  counter[0] = c + 1;
+}
+
+__global__ void k_counter_reset(int32_t* counter) { counter[0] = 0; }
+
+}  // namespace
+
+hipError_t launch_token_fetch(const int32_t* tokens, const int32_t* counter, int32_t* cur,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_token_fetch, dim3(1), dim3(1), 0, s, tokens, counter, cur);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_store(int32_t* tokens, int32_t* counter, const int32_t* out,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_token_store, dim3(1), dim3(1), 0, s, tokens, counter, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_counter_reset(int32_t* counter, hipStream_t s) {
+  hipLaunchKernelGGL(k_counter_reset, dim3(1), dim3(1), 0, s, counter);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_rows(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
+                             const int32_t* tokens, int64_t M, uint16_t* out, hipStream_t s) {
+  const int G = (int)(K / 32);
+  hipLaunchKernelGGL(k_embed_rows, dim3((G + kBlock - 1) / kBlock, (unsigned)M), dim3(kBlock), 0,
+                     s, reinterpret_cast<const uint4*>(words), scales, N, G, tokens,
+                     reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const uint16_t* gamma,
+                          float eps, int64_t M, int64_t K, uint16_t* res_out, uint16_t* out,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)M), dim3(kBlock), 0, s,
+                     reinterpret_cast<const uint4*>(delta), reinterpret_cast<const uint4*>(res_in),
+                     reinterpret_cast<const uint4*>(gamma), eps, (int)(K / 8),
+                     reinterpret_cast<uint4*>(res_out), reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax, dim3((unsigned)M), dim3(kBlock), 0, s, x, N, out);
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -1,0 +1,300 @@
+// Decode tokens end to end: the decode loop of the Zero TVM documentation
+// ("Decode loop") over q4f16_1 weights, with attention at a single position.
+//
+// One step is a fixed sequence of kernels: embedding row, RMSNorm, then per block
+// qkv, o (reading the value part of qkv), residual add + RMSNorm, gate/up,
+// SiLU-multiply, down, residual add + RMSNorm, then the LM head and the argmax.
+// Each projection is one GEMV kernel (one kernel per GEMV is the faster choice
+// for a chain in which every GEMV waits for the one before it).  Every buffer
+// between the kernels lives in the caller's workspace; the residual is updated
+// in place.  A multi-step decode captures one step, with two one-thread kernels
+// that take the step's token from and put the next one into the caller's token
+// array at a device-side counter, as a HIP graph and replays it: no host
+// round trip between tokens (the pages' host-side lever is to submit a whole
+// token in one command; here several tokens go per host call).
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "q4f16.h"
+#include "q4_internal.h"
+
+namespace {
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Byte offsets in the workspace: split-K partials first, then the activations,
+// then the token bookkeeping (int32: current token, next token, counter).
+struct Layout {
+  q4::GemvPlan qkv, o, gate_up, down, lm_head;
+  size_t res = 0, h = 0, qkv_out = 0, attn = 0, gu = 0, hf = 0, dn = 0, logits = 0, tok = 0;
+  size_t bytes = 0;
+};
+
+Layout layout_for(const q4::DeviceInfo& d, const q4_model& m) {
+  Layout L;
+  L.qkv = q4::plan_auto(d, 1, 3 * m.D, m.D);
+  L.o = q4::plan_auto(d, 1, m.D, m.D);
+  L.gate_up = q4::plan_auto(d, 1, 2 * m.F, m.D);
+  L.down = q4::plan_auto(d, 1, m.D, m.F);
+  L.lm_head = q4::plan_auto(d, 1, m.V, m.D);
+  size_t off = up256(std::max({L.qkv.ws_bytes, L.o.ws_bytes, L.gate_up.ws_bytes,
+                               L.down.ws_bytes, L.lm_head.ws_bytes}));
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up256(bytes);
+    return o;
+  };
+  L.res = take(2 * m.D);
+  L.h = take(2 * m.D);
+  L.qkv_out = take(2 * 3 * m.D);
+  L.attn = take(2 * m.D);
+  L.gu = take(2 * 2 * m.F);
+  L.hf = take(2 * m.F);
+  L.dn = take(2 * m.D);
+  L.logits = take(2 * m.V);
+  L.tok = take(16);
+  L.bytes = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_weight(const char* what, const q4_weight& w, int64_t N, int64_t K) {
+  if (!w.words || !w.scales) return q4::api_fail(Q4_ERR_NULL, "%s: NULL weight pointer", what);
+  if (w.N != N || w.K != K)
+    return q4::api_fail(Q4_ERR_SHAPE, "%s: shape [%lld][%lld], expected [%lld][%lld]", what,
+                        (long long)w.N, (long long)w.K, (long long)N, (long long)K);
+  if (!aligned(w.words, 16) || !aligned(w.scales, 2))
+    return q4::api_fail(Q4_ERR_ALIGN, "%s: words must be 16-byte, scales 2-byte aligned", what);
+  return Q4_OK;
+}
+
+int check_gamma(const char* what, const uint16_t* g) {
+  if (!g) return q4::api_fail(Q4_ERR_NULL, "%s is NULL", what);
+  if (!aligned(g, 16)) return q4::api_fail(Q4_ERR_ALIGN, "%s not 16-byte aligned", what);
+  return Q4_OK;
+}
+
+int check_model(const q4_model* m) {
+  if (!m) return q4::api_fail(Q4_ERR_NULL, "model is NULL");
+  if (m->n_blocks < 0 || (m->n_blocks > 0 && !m->blocks))
+    return q4::api_fail(Q4_ERR_SHAPE, "n_blocks = %lld with blocks %p", (long long)m->n_blocks,
+                        (const void*)m->blocks);
+  if (m->D < 32 || m->D % 32 || m->F < 32 || m->F % 32 || m->V < 1)
+    return q4::api_fail(Q4_ERR_SHAPE, "D = %lld, F = %lld, V = %lld: D and F must be positive "
+                        "multiples of 32, V >= 1", (long long)m->D, (long long)m->F,
+                        (long long)m->V);
+  if (m->D > (1 << 20) || m->F > (1 << 20) || m->V > INT32_MAX)
+    return q4::api_fail(Q4_ERR_UNSUPPORTED, "D, F or V too large");
+  if (!(m->eps >= 0.f)) return q4::api_fail(Q4_ERR_SHAPE, "eps must be >= 0");
+  if (int rc = check_weight("embed", m->embed, m->V, m->D)) return rc;
+  if (int rc = check_weight("lm_head", m->lm_head, m->V, m->D)) return rc;
+  if (int rc = check_gamma("final_norm", m->final_norm)) return rc;
+  char what[64];
+  for (int64_t b = 0; b < m->n_blocks; ++b) {
+    const q4_block& B = m->blocks[b];
+    snprintf(what, sizeof what, "blocks[%lld].qkv", (long long)b);
+    if (int rc = check_weight(what, B.qkv, 3 * m->D, m->D)) return rc;
+    snprintf(what, sizeof what, "blocks[%lld].o", (long long)b);
+    if (int rc = check_weight(what, B.o, m->D, m->D)) return rc;
+    snprintf(what, sizeof what, "blocks[%lld].gate_up", (long long)b);
+    if (int rc = check_weight(what, B.gate_up, 2 * m->F, m->D)) return rc;
+    snprintf(what, sizeof what, "blocks[%lld].down", (long long)b);
+    if (int rc = check_weight(what, B.down, m->D, m->F)) return rc;
+    snprintf(what, sizeof what, "blocks[%lld].attn_norm", (long long)b);
+    if (int rc = check_gamma(what, B.attn_norm)) return rc;
+    snprintf(what, sizeof what, "blocks[%lld].ffn_norm", (long long)b);
+    if (int rc = check_gamma(what, B.ffn_norm)) return rc;
+  }
+  return Q4_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (!ws) return q4::api_fail(Q4_ERR_WORKSPACE, "needs %zu workspace bytes, ws is NULL", need);
+  if (have < need)
+    return q4::api_fail(Q4_ERR_WORKSPACE, "needs %zu workspace bytes, got %zu", need, have);
+  if (!aligned(ws, 16)) return q4::api_fail(Q4_ERR_ALIGN, "ws not 16-byte aligned");
+  return Q4_OK;
+}
+
+// Enqueue one decode step: token tok_in[0] -> tok_out[0] (and the logits).
+hipError_t enqueue_step(const q4::DeviceInfo& d, const q4_model& m, const Layout& L,
+                        const int32_t* tok_in, int32_t* tok_out, uint16_t* logits, uint8_t* ws,
+                        hipStream_t s) {
+  auto buf = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  uint16_t *res = buf(L.res), *h = buf(L.h), *qkv = buf(L.qkv_out), *gu = buf(L.gu);
+  uint16_t *attn = buf(L.attn), *hf = buf(L.hf), *dn = buf(L.dn);
+  uint16_t* lg = logits ? logits : buf(L.logits);
+  auto gemv = [&](const q4_weight& w, const q4::GemvPlan& p, const uint16_t* x, uint16_t* y) {
+    const q4::GemvArgs a{w.words, w.scales, x, y, 1, w.N, w.K};
+    return q4::launch_gemv(d, a, p, ws, s);
+  };
+#define Q4_TRY(call)                          \
+  do {                                        \
+    if (hipError_t e_ = (call)) return e_;    \
+  } while (0)
+  Q4_TRY(q4::launch_embed_rows(m.embed.words, m.embed.scales, m.V, m.D, tok_in, 1, res, s));
+  const uint16_t* g0 = m.n_blocks ? m.blocks[0].attn_norm : m.final_norm;
+  Q4_TRY(q4::launch_rmsnorm(nullptr, res, g0, m.eps, 1, m.D, nullptr, h, s));
+  for (int64_t b = 0; b < m.n_blocks; ++b) {
+    const q4_block& B = m.blocks[b];
+    Q4_TRY(gemv(B.qkv, L.qkv, h, qkv));
+    // attention at a single position: its output is the value vector
+    Q4_TRY(gemv(B.o, L.o, qkv + 2 * m.D, attn));
+    Q4_TRY(q4::launch_rmsnorm(attn, res, B.ffn_norm, m.eps, 1, m.D, res, h, s));
+    Q4_TRY(gemv(B.gate_up, L.gate_up, h, gu));
+    Q4_TRY(q4::launch_silu_mul(gu, hf, 1, m.F, s));
+    Q4_TRY(gemv(B.down, L.down, hf, dn));
+    const uint16_t* next = b + 1 < m.n_blocks ? m.blocks[b + 1].attn_norm : m.final_norm;
+    Q4_TRY(q4::launch_rmsnorm(dn, res, next, m.eps, 1, m.D, res, h, s));
+  }
+  Q4_TRY(gemv(m.lm_head, L.lm_head, h, lg));
+  Q4_TRY(q4::launch_argmax(lg, 1, m.V, tok_out, s));
+#undef Q4_TRY
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- graphs
+
+struct GraphEntry {
+  std::vector<uint8_t> key;
+  hipGraphExec_t exec = nullptr;
+  uint64_t last_use = 0;
+};
+constexpr size_t kMaxGraphs = 4;
+std::mutex g_graph_mutex;
+std::vector<GraphEntry> g_graphs;
+uint64_t g_graph_clock = 0;
+hipStream_t g_capture_stream[64] = {};
+
+std::vector<uint8_t> graph_key(const q4_model& m, const void* ws, size_t ws_bytes,
+                               const int32_t* tokens, int dev) {
+  std::vector<uint8_t> k;
+  auto put = [&](const void* p, size_t n) {
+    const uint8_t* b = static_cast<const uint8_t*>(p);
+    k.insert(k.end(), b, b + n);
+  };
+  put(&m, sizeof m);
+  if (m.n_blocks > 0) put(m.blocks, sizeof(q4_block) * (size_t)m.n_blocks);
+  put(&ws, sizeof ws);
+  put(&ws_bytes, sizeof ws_bytes);
+  put(&tokens, sizeof tokens);
+  put(&dev, sizeof dev);
+  return k;
+}
+
+// The graph of one step of tokens[counter] -> tokens[counter + 1]; captured on a
+// private stream (the caller's may be the null stream, which cannot be captured).
+hipError_t step_graph(const q4::DeviceInfo& d, const q4_model& m, const Layout& L,
+                      int32_t* tokens, uint8_t* ws, size_t ws_bytes, hipGraphExec_t* out) {
+  std::lock_guard<std::mutex> lock(g_graph_mutex);
+  std::vector<uint8_t> key = graph_key(m, ws, ws_bytes, tokens, d.id);
+  for (GraphEntry& e : g_graphs)
+    if (e.key == key) {
+      e.last_use = ++g_graph_clock;
+      *out = e.exec;
+      return hipSuccess;
+    }
+  hipStream_t& cs = g_capture_stream[d.id];
+  if (!cs)
+    if (hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking)) return e;
+  int32_t* tok = reinterpret_cast<int32_t*>(ws + L.tok);   // cur, next, counter
+  if (hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal)) return e;
+  hipError_t err = q4::launch_token_fetch(tokens, tok + 2, tok, cs);
+  if (err == hipSuccess) err = enqueue_step(d, m, L, tok, tok + 1, nullptr, ws, cs);
+  if (err == hipSuccess) err = q4::launch_token_store(tokens, tok + 2, tok + 1, cs);
+  hipGraph_t graph = nullptr;
+  const hipError_t end = hipStreamEndCapture(cs, &graph);
+  if (err == hipSuccess) err = end;
+  hipGraphExec_t exec = nullptr;
+  if (err == hipSuccess) err = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (err != hipSuccess) return err;
+  if (g_graphs.size() >= kMaxGraphs) {
+    size_t lru = 0;
+    for (size_t i = 1; i < g_graphs.size(); ++i)
+      if (g_graphs[i].last_use < g_graphs[lru].last_use) lru = i;
+    (void)hipDeviceSynchronize();          // no launch of it still in flight
+    (void)hipGraphExecDestroy(g_graphs[lru].exec);
+    g_graphs.erase(g_graphs.begin() + (ptrdiff_t)lru);
+  }
+  GraphEntry e;
+  e.key = std::move(key);
+  e.exec = exec;
+  e.last_use = ++g_graph_clock;
+  g_graphs.push_back(std::move(e));
+  *out = exec;
+  return hipSuccess;
+}
+
+int device_error(hipError_t e, const char* what) {
+  return q4::api_fail(Q4_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q4_decode_token_workspace_bytes(const q4_model* model) {
+  if (check_model(model)) return 0;
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return 0;
+  return layout_for(*d, *model).bytes;
+}
+
+int q4_decode_token(const q4_model* model, const int32_t* token_in, int32_t* token_out,
+                    uint16_t* logits, void* ws, size_t ws_bytes, q4_stream_t stream) {
+  if (int rc = check_model(model)) return q4::api_fail(rc, "q4_decode_token: %s", q4_last_error());
+  if (!token_in || !token_out)
+    return q4::api_fail(Q4_ERR_NULL, "q4_decode_token: token pointer is NULL");
+  if (!aligned(token_in, 4) || !aligned(token_out, 4) || (logits && !aligned(logits, 2)))
+    return q4::api_fail(Q4_ERR_ALIGN, "q4_decode_token: misaligned token or logits pointer");
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return q4::api_fail(Q4_ERR_DEVICE, "q4_decode_token: no HIP device");
+  const Layout L = layout_for(*d, *model);
+  if (int rc = check_ws(ws, ws_bytes, L.bytes))
+    return q4::api_fail(rc, "q4_decode_token: %s", q4_last_error());
+  hipError_t e = enqueue_step(*d, *model, L, token_in, token_out, logits,
+                              static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? q4::api_ok() : device_error(e, "q4_decode_token");
+}
+
+int q4_decode_tokens(const q4_model* model, int32_t* tokens, int64_t steps, void* ws,
+                     size_t ws_bytes, uint32_t flags, q4_stream_t stream) {
+  if (int rc = check_model(model)) return q4::api_fail(rc, "q4_decode_tokens: %s", q4_last_error());
+  if (!tokens) return q4::api_fail(Q4_ERR_NULL, "q4_decode_tokens: tokens is NULL");
+  if (!aligned(tokens, 4)) return q4::api_fail(Q4_ERR_ALIGN, "q4_decode_tokens: tokens misaligned");
+  if (steps < 0 || steps > INT32_MAX - 1)
+    return q4::api_fail(Q4_ERR_SHAPE, "q4_decode_tokens: steps = %lld", (long long)steps);
+  if (flags & ~Q4_TOKENS_EAGER)
+    return q4::api_fail(Q4_ERR_SHAPE, "q4_decode_tokens: unknown flags 0x%x", flags);
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return q4::api_fail(Q4_ERR_DEVICE, "q4_decode_tokens: no HIP device");
+  const Layout L = layout_for(*d, *model);
+  if (int rc = check_ws(ws, ws_bytes, L.bytes))
+    return q4::api_fail(rc, "q4_decode_tokens: %s", q4_last_error());
+  if (steps == 0) return q4::api_ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  int32_t* tok = reinterpret_cast<int32_t*>(w + L.tok);
+  hipError_t e = hipSuccess;
+  if (flags & Q4_TOKENS_EAGER) {
+    e = q4::launch_counter_reset(tok + 2, s);
+    for (int64_t i = 0; i < steps && e == hipSuccess; ++i) {
+      e = q4::launch_token_fetch(tokens, tok + 2, tok, s);
+      if (e == hipSuccess) e = enqueue_step(*d, *model, L, tok, tok + 1, nullptr, w, s);
+      if (e == hipSuccess) e = q4::launch_token_store(tokens, tok + 2, tok + 1, s);
+    }
+  } else {
+    hipGraphExec_t exec = nullptr;
+    e = step_graph(*d, *model, L, tokens, w, ws_bytes, &exec);
+    if (e == hipSuccess) e = q4::launch_counter_reset(tok + 2, s);
+    for (int64_t i = 0; i < steps && e == hipSuccess; ++i) e = hipGraphLaunch(exec, s);
+  }
+  return e == hipSuccess ? q4::api_ok() : device_error(e, "q4_decode_tokens");
+}
+
+}  // extern "C"

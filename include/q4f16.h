@@ -208,6 +208,105 @@ Q4_API size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_l
 Q4_API int q4_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t H,
                        q4_stream_t stream);
 
+/* ---------------------------------------- the operations around the GEMVs -- */
+/* The decode loop's steps between its projections (Zero TVM documentation,
+ * "Decode loop"): the token's embedding row, RMSNorm, the residual add with
+ * RMSNorm ("addNorm"), the argmax over the LM head's logits.  Rows are
+ * independent; every fp16 pointer is 16-byte aligned and K % 8 == 0. */
+
+/* q4_embed_rows: out[m][k] = fp16((q[t][k] - 7) * s[t][k/32]) with t = tokens[m]:
+ * row t of a q4f16_1 embedding table (words [N][K/8], scales [N][K/32]).  tokens
+ * is DEVICE memory (int32 [M]), read by the kernel, so a captured sequence can
+ * take the token an earlier kernel wrote; a token outside [0, N) gives a row of
+ * NaN (0x7E00).  Each output is the exact product rounded once. */
+Q4_API int q4_embed_rows(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
+                         const int32_t* tokens, int64_t M, uint16_t* out, q4_stream_t stream);
+
+/* q4_rmsnorm: out[m][k] = fp16(x[m][k] / sqrt(mean_k x[m][k]^2 + eps) * gamma[k]),
+ * the sum of squares in fp32.  x, out: [M][K]; gamma: [K].  out must not overlap
+ * x or gamma.  Results are within one fp16 unit in the last place of the
+ * exactly computed value. */
+Q4_API int q4_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M, int64_t K,
+                      uint16_t* out, q4_stream_t stream);
+
+/* q4_add_rmsnorm: res_out = fp16(res_in + delta) (rounded once), then out =
+ * RMSNorm(res_out) * gamma as q4_rmsnorm.  res_out may be res_in itself (in
+ * place) but must not otherwise overlap an input; out must not overlap any other
+ * argument. */
+Q4_API int q4_add_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const uint16_t* gamma,
+                          float eps, int64_t M, int64_t K, uint16_t* res_out, uint16_t* out,
+                          q4_stream_t stream);
+
+/* q4_argmax: out[m] = the index of the largest value of x[m][0 .. N) (fp16); ties
+ * go to the lowest index; NaN entries are skipped (a row of NaN gives 0).  out:
+ * int32 [M], device memory.  x 2-byte aligned. */
+Q4_API int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_stream_t stream);
+
+/* -------------------------------------------------------- decode tokens -- */
+/* The decode loop end to end (Zero TVM documentation, "Decode loop"), weights
+ * only: the token's embedding row; an RMSNorm; per block qkv, attention, o, the
+ * residual add with RMSNorm, gate/up, SiLU-multiply, down, the residual add with
+ * RMSNorm; the LM head; the argmax.  Attention runs at a single position: the
+ * token attends only to itself, the softmax over its one score is 1, and the
+ * attention output is the token's own value vector -- the last D values of the
+ * qkv output (rotary embedding leaves values unchanged).  There is no KV cache.
+ * The RMSNorm after each block's residual add uses the next block's attention
+ * norm (the final norm after the last block). */
+
+/* One q4f16_1 weight in device memory: words [N][K/8], scales [N][K/32]. */
+typedef struct q4_weight {
+  const uint32_t* words;
+  const uint16_t* scales;
+  int64_t N;
+  int64_t K;
+} q4_weight;
+
+typedef struct q4_block {
+  q4_weight qkv;                /* [3D][D]: q, k, v */
+  q4_weight o;                  /* [D][D]  */
+  q4_weight gate_up;            /* [2F][D]: gate rows, then up rows */
+  q4_weight down;               /* [D][F]  */
+  const uint16_t* attn_norm;    /* fp16 [D]: RMSNorm weight before qkv */
+  const uint16_t* ffn_norm;     /* fp16 [D]: RMSNorm weight before gate/up */
+} q4_block;
+
+typedef struct q4_model {
+  int64_t n_blocks;             /* >= 0 */
+  int64_t D, F, V;              /* hidden size, FFN size, vocabulary (D, F % 32 == 0) */
+  q4_weight embed;              /* [V][D] embedding table */
+  const q4_block* blocks;       /* HOST array of n_blocks (read during the call) */
+  const uint16_t* final_norm;   /* fp16 [D] */
+  q4_weight lm_head;            /* [V][D] */
+  float eps;                    /* RMSNorm epsilon, >= 0 */
+} q4_model;
+
+/* Workspace bytes q4_decode_token and q4_decode_tokens need for this model
+ * (activations, split-K partials, token bookkeeping); 0 if the model is invalid. */
+Q4_API size_t q4_decode_token_workspace_bytes(const q4_model* model);
+
+/* q4_decode_token: one decode step for token_in[0] (DEVICE int32); writes the
+ * argmax of the logits to token_out[0] (DEVICE int32) and, if logits is not NULL,
+ * the logits (DEVICE fp16 [V]).  One kernel per operation, enqueued on `stream`.
+ * ws: q4_decode_token_workspace_bytes(model), 16-byte aligned. */
+Q4_API int q4_decode_token(const q4_model* model, const int32_t* token_in, int32_t* token_out,
+                           uint16_t* logits, void* ws, size_t ws_bytes, q4_stream_t stream);
+
+/* Run every step's kernels from the host instead of replaying a graph. */
+#define Q4_TOKENS_EAGER 0x1u
+
+/* q4_decode_tokens: `steps` decode steps back to back with no host
+ * synchronisation, each step's argmax the next step's token: tokens is DEVICE
+ * int32 [steps + 1]; step i reads tokens[i] and writes tokens[i + 1].  One step's
+ * kernels are captured once as a HIP graph (per model, workspace and tokens
+ * pointer; the library keeps the last 4, freeing older ones) and the graph is
+ * replayed `steps` times on `stream`; with Q4_TOKENS_EAGER the kernels are
+ * enqueued for every step instead.  The results are those of `steps` calls of
+ * q4_decode_token.  ws as for q4_decode_token; calls sharing it must be ordered
+ * on one stream.  Make the first call for a given model, workspace and tokens
+ * pointer outside stream capture. */
+Q4_API int q4_decode_tokens(const q4_model* model, int32_t* tokens, int64_t steps, void* ws,
+                            size_t ws_bytes, uint32_t flags, q4_stream_t stream);
+
 /* ------------------------------------------------------ measurement aids -- */
 
 /* Streaming-read ceiling probe (the everything-webgpu page measures the same

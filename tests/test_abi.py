@@ -4,6 +4,7 @@ no compute call)."""
 import ctypes as C
 import os
 import re
+import shutil
 import subprocess
 
 import pytest
@@ -168,3 +169,52 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(q4, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         q4.load()
+
+
+STRUCTS = {"q4_layer": "Layer", "q4_weight": "Weight", "q4_block": "Block", "q4_model": "ModelDesc"}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+def test_struct_layouts_match_the_header(tmp_path):
+    """sizeof and every field offset of the header's structs, as gcc lays them out,
+    equal the binding's ctypes mirrors."""
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "q4f16.h"', 'int main(void) {']
+    for cname, pyname in STRUCTS.items():
+        py = getattr(q4, pyname)
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), "-o", str(exe), str(src)])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out.splitlines()}
+    for cname, pyname in STRUCTS.items():
+        py = getattr(q4, pyname)
+        assert got[(cname, "size")] == C.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def test_token_argument_errors(lib):
+    m = q4.ModelDesc()
+    assert lib.q4_decode_token(None, X, Y, None, A, 1 << 20, None) == 1
+    m.n_blocks, m.D, m.F, m.V = 0, 48, 64, 10      # D not a multiple of 32
+    assert lib.q4_decode_token(C.byref(m), X, Y, None, A, 1 << 20, None) == 2 and "D" in _err(lib)
+    m.D, m.n_blocks = 64, 1
+    assert lib.q4_decode_token(C.byref(m), X, Y, None, A, 1 << 20, None) == 2   # blocks NULL
+    assert "blocks" in _err(lib)
+    m.n_blocks = 0
+    assert lib.q4_decode_token(C.byref(m), X, Y, None, A, 1 << 20, None) == 1   # weights NULL
+    m.embed = q4.Weight(0x10000, 0x20000, 10, 64)
+    m.lm_head = q4.Weight(0x30000, 0x40000, 11, 64)                            # wrong N
+    m.final_norm = 0x50000
+    assert lib.q4_decode_token(C.byref(m), X, Y, None, A, 1 << 20, None) == 2
+    assert "lm_head" in _err(lib)
+    m.lm_head = q4.Weight(0x30000, 0x40000, 10, 64)
+    assert lib.q4_decode_tokens(C.byref(m), None, 4, A, 1 << 20, 0, None) == 1
+    assert lib.q4_decode_tokens(C.byref(m), X, -1, A, 1 << 20, 0, None) == 2
+    assert lib.q4_decode_tokens(C.byref(m), X, 4, A, 1 << 20, 0x10, None) == 2
+    assert lib.q4_decode_token_workspace_bytes(None) == 0

@@ -1,0 +1,180 @@
+"""Decode tokens end to end (q4_decode_token, q4_decode_tokens): the step composed
+from the separate entry points, every intermediate kept and checked against the
+oracle on the inputs the GPU read; the driver's logits and token bitwise equal to
+that composition; and graph replays of several steps equal to the same number of
+single steps, replay after replay."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+import bit_weight_streaming_q4f16_amd as q4
+from gpuhelp import assert_gemv_close, dev_half, dev_words, host_half
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q4.load()
+
+
+def within_one_ulp(got, ref):
+    g = np.asarray(got, np.uint16).reshape(-1).view(np.float16).astype(np.float64)
+    r = np.asarray(ref, np.uint16).reshape(-1).view(np.float16).astype(np.float64)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -14))) - 10)
+    assert np.all(np.abs(g - r) <= ulp)
+
+
+class Weights:
+    """Seeded weights of a model with D, F, V and n blocks (host copies kept for
+    the oracle when `host`)."""
+
+    def __init__(self, tag, n, D, F, V, host=True):
+        self.D, self.F, self.V, self.n = D, F, V, n
+        self.mats = {}
+
+        def w(name, N, K, sigma):
+            m = synth.Matrix(f"tok/{tag}/{name}", N, K, sigma=sigma, floor=sigma / 4)
+            self.mats[name] = m if host else None
+            return (m.words_torch("cuda"), dev_half(m.scales()))
+
+        def g(name):
+            v = (1.0 + 0.1 * synth.normal(f"tok/{tag}/{name}", 0, 0, D)).astype(np.float16)
+            return dev_half(v.view(np.uint16))
+        self.embed = w("embed", V, D, 0.05)
+        self.lm_head = w("lm_head", V, D, 2.0 / D)
+        self.final_norm = g("final_norm")
+        self.blocks = [dict(qkv=w(f"{b}/qkv", 3 * D, D, 2.0 / D), o=w(f"{b}/o", D, D, 2.0 / D),
+                            gate_up=w(f"{b}/gate_up", 2 * F, D, 2.0 / D),
+                            down=w(f"{b}/down", D, F, 2.0 / F),
+                            attn_norm=g(f"{b}/attn_norm"), ffn_norm=g(f"{b}/ffn_norm"))
+                       for b in range(n)]
+        self.model = q4.Model(self.embed, self.blocks, self.final_norm, self.lm_head, EPS)
+
+
+def composed_step(W, token, check):
+    """The decode step from the separate entry points, distinct buffers for every
+    intermediate; with `check`, each against the oracle. Returns (logits, token)."""
+    D, F = W.D, W.F
+    f16 = lambda n: torch.full((n,), float("nan"), dtype=torch.float16, device="cuda")
+    tok = torch.tensor([token], dtype=torch.int32, device="cuda")
+    keep = []
+    res = q4.q4_embed_rows(*W.embed, tok).reshape(-1)
+    h = q4.q4_rmsnorm(res, W.blocks[0]["attn_norm"] if W.n else W.final_norm, EPS)
+    torch.cuda.synchronize()
+    if check:
+        m = W.mats["embed"]
+        ref = oracle.embed_rows(m.words(), m.scales(), np.array([token], np.int32))[0]
+        assert np.array_equal(host_half(res), ref)
+        g0 = W.blocks[0]["attn_norm"] if W.n else W.final_norm
+        within_one_ulp(host_half(h), oracle.rmsnorm(host_half(res), host_half(g0), EPS))
+    for b, B in enumerate(W.blocks):
+        qkv, attn, gu, dn = f16(3 * D), f16(D), f16(2 * F), f16(D)
+        q4.q4_gemv(*B["qkv"], h, qkv)
+        v = qkv[2 * D:]
+        q4.q4_gemv(*B["o"], v, attn)
+        res2, h2 = q4.q4_add_rmsnorm(attn, res, B["ffn_norm"], EPS)
+        q4.q4_gemv(*B["gate_up"], h2, gu)
+        hf = q4.q4_silu_mul(gu)
+        q4.q4_gemv(*B["down"], hf, dn)
+        nxt = W.blocks[b + 1]["attn_norm"] if b + 1 < W.n else W.final_norm
+        res3, h3 = q4.q4_add_rmsnorm(dn, res2, nxt, EPS)
+        torch.cuda.synchronize()
+        if check:
+            mm = lambda name: W.mats[f"{b}/{name}"]
+            assert_gemv_close(host_half(qkv), mm("qkv").words(), mm("qkv").scales(), host_half(h))
+            assert_gemv_close(host_half(attn), mm("o").words(), mm("o").scales(), host_half(v))
+            r_ref, h_ref = oracle.add_rmsnorm(host_half(attn), host_half(res),
+                                              host_half(B["ffn_norm"]), EPS)
+            assert np.array_equal(host_half(res2), r_ref)
+            within_one_ulp(host_half(h2), h_ref)
+            assert_gemv_close(host_half(gu), mm("gate_up").words(), mm("gate_up").scales(),
+                              host_half(h2))
+            within_one_ulp(host_half(hf), oracle.silu_mul(host_half(gu).reshape(1, -1))[0])
+            assert_gemv_close(host_half(dn), mm("down").words(), mm("down").scales(),
+                              host_half(hf))
+            r_ref, h_ref = oracle.add_rmsnorm(host_half(dn), host_half(res2), host_half(nxt), EPS)
+            assert np.array_equal(host_half(res3), r_ref)
+            within_one_ulp(host_half(h3), h_ref)
+        keep += [qkv, attn, gu, dn, hf, res2, h2]
+        res, h = res3, h3
+    logits = f16(W.V)
+    q4.q4_gemv(*W.lm_head, h, logits)
+    out = q4.q4_argmax(logits)
+    torch.cuda.synchronize()
+    lg = host_half(logits)
+    if check:
+        m = W.mats["lm_head"]
+        assert_gemv_close(lg, m.words(), m.scales(), host_half(h))
+    # the argmax always against the oracle on the logits the GPU produced
+    assert int(out.cpu()[0]) == int(oracle.argmax(lg.reshape(1, -1))[0])
+    return lg, int(out.cpu()[0])
+
+
+@pytest.fixture(scope="module")
+def small():
+    return Weights("small", 3, 256, 512, 1000)
+
+
+def test_step_matches_composition_and_oracle(small):
+    W = small
+    lg_ref, t_ref = composed_step(W, 17, check=True)
+    tin = torch.tensor([17], dtype=torch.int32, device="cuda")
+    tout = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(W.V, dtype=torch.float16, device="cuda")
+    q4.q4_decode_token(W.model, tin, tout, logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_half(logits), lg_ref)
+    assert int(tout.cpu()[0]) == t_ref
+
+
+@pytest.mark.parametrize("flags", [0, q4.TOKENS_EAGER], ids=["graph", "eager"])
+def test_multi_step_equals_single_steps(small, flags):
+    W = small
+    steps = 6
+    # single steps, host round trip between them
+    ws = torch.empty(q4.q4_decode_token_workspace_bytes(W.model), dtype=torch.uint8, device="cuda")
+    seq = [5]
+    for _ in range(steps):
+        tin = torch.tensor([seq[-1]], dtype=torch.int32, device="cuda")
+        tout = torch.empty(1, dtype=torch.int32, device="cuda")
+        q4.q4_decode_token(W.model, tin, tout, ws=ws)
+        torch.cuda.synchronize()
+        seq.append(int(tout.cpu()[0]))
+    # the same steps in one call, twice (a graph is replayed again), with eager
+    # work and synchronisation in between
+    tokens = torch.full((steps + 1,), -1, dtype=torch.int32, device="cuda")
+    for rep in range(3):
+        tokens.fill_(-1)
+        tokens[0] = seq[0]
+        q4.q4_decode_tokens(W.model, tokens, steps, ws=ws, flags=flags)
+        torch.cuda.synchronize()
+        assert tokens.cpu().tolist() == seq, rep
+        junk = torch.randn(1 << 16, device="cuda").sum()        # eager work between replays
+        torch.cuda.synchronize()
+        del junk
+    # and the sequence is a chain of argmaxes: recompute the last step by composition
+    lg, t = composed_step(W, seq[-2], check=False)
+    assert t == seq[-1]
+
+
+def test_phi3_shaped_step():
+    """Two blocks at Phi-3 sizes (D 3072, FFN 8192, vocabulary 32064): the driver's
+    logits equal the composition's bitwise; the token is the oracle's argmax of them."""
+    W = Weights("phi3", 2, 3072, 8192, 32064, host=False)
+    lg_ref, t_ref = composed_step(W, 1234, check=False)
+    tin = torch.tensor([1234], dtype=torch.int32, device="cuda")
+    tout = torch.empty(1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(W.V, dtype=torch.float16, device="cuda")
+    q4.q4_decode_token(W.model, tin, tout, logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_half(logits), lg_ref)
+    assert int(tout.cpu()[0]) == t_ref
+    assert np.all(np.isfinite(host_half(logits).view(np.float16)))
