@@ -195,6 +195,7 @@ def main():
         result["other_modes"] = other
         if not args.no_configs:
             result["per_config"] = per_config(torch, q4, synth, np, stream)
+            result["decode_tokens"] = token_figures(torch, q4, synth, np, stream, descs, meta)
         if not args.no_probe:
             result["probe_read_gbs"] = probe_read(torch, q4, stream)
         if not args.no_cpu_baseline:
@@ -352,6 +353,63 @@ def per_config(torch, q4, synth, np, stream):
                                 tflops=round(flops / (ms * 1e-3) / 1e12, 2))
     del descs
     torch.cuda.empty_cache()
+    return out
+
+
+def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
+    """The whole weights-only decode step of a Phi-3-mini-shaped model (32 blocks,
+    the sweep's weights, a seeded q4 embedding table),
+    attention at a single position (timing does not depend on the values; norm
+    weights near 0.1 keep them finite): one q4_decode_token per token with a host
+    synchronisation after each (one token per host call), and q4_decode_tokens
+    with `steps` tokens per host call, kernels enqueued per step or one captured
+    step replayed as a graph."""
+    D, F, V = 3072, 8192, 32064
+    labels = [l for l, _, _ in meta]
+    assert len(descs) == 129 and labels[-1].endswith("lm_head"), labels[-1]
+    emb = synth.Matrix("tokens/embed", V, D, sigma=0.05, floor=0.0125)
+    embed = (emb.words_torch("cuda"),
+             torch.from_numpy(emb.scales().view(np.int16)).cuda().view(torch.float16))
+    # norm weights near 0.1 keep the residual stream of these (uncalibrated) weights
+    # within fp16 over 32 blocks
+    gamma = torch.from_numpy((0.1 + 0.01 * synth.normal("tokens/gamma", 0, 0, D)).astype(
+        np.float16).view(np.int16)).cuda().view(torch.float16)
+    blocks = [dict(qkv=descs[4 * b][:2], o=descs[4 * b + 1][:2], gate_up=descs[4 * b + 2][:2],
+                   down=descs[4 * b + 3][:2], attn_norm=gamma, ffn_norm=gamma) for b in range(32)]
+    model = q4.Model(embed, blocks, gamma, descs[128][:2], 1e-5)
+    ws = torch.empty(q4.q4_decode_token_workspace_bytes(model), dtype=torch.uint8, device="cuda")
+    weight_bytes = sum(synth.Matrix(l, N, K).weight_bytes for l, N, K in meta) + D // 2 + D // 16
+    tok_in = torch.tensor([1], dtype=torch.int32, device="cuda")
+    tok_out = torch.empty(1, dtype=torch.int32, device="cuda")
+    tokens = torch.zeros(steps + 1, dtype=torch.int32, device="cuda")
+    out = {"model": "phi3-mini-shaped, 32 blocks, vocabulary 32064, attention at one position",
+           "weight_bytes_per_token": weight_bytes, "tokens_per_call": steps}
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            q4.q4_decode_token(model, tok_in, tok_out, ws=ws, stream=stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = 50
+        for _ in range(n):
+            q4.q4_decode_token(model, tok_in, tok_out, ws=ws, stream=stream)
+            stream.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / n
+        out["one_token_per_call"] = {"ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 1),
+                                     "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
+        for name, flags in (("tokens_per_call_eager", q4.TOKENS_EAGER),
+                            ("tokens_per_call_graph", 0)):
+            q4.q4_decode_tokens(model, tokens, steps, ws=ws, flags=flags, stream=stream)
+            torch.cuda.synchronize()
+            reps = 5
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                q4.q4_decode_tokens(model, tokens, steps, ws=ws, flags=flags, stream=stream)
+            stream.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / (reps * steps)
+            out[name] = {"ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 1),
+                         "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
+    out["tokens"] = tokens[: min(steps + 1, 9)].cpu().tolist()
+    del ws, model
     return out
 
 
