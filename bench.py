@@ -44,7 +44,9 @@ PROFILE = os.path.join(ROOT, "profiles", "k_step_phi3_decode_sweep")
 METRIC = "achieved HBM GB/s (% of peak) and projected decode tok/s, q4 GEMV sweep"
 
 
-MODES = {"ordered": 0x2, "hazards": 0x0, "launch_each": 0x1}
+# ordered: every GEMV waits for its predecessor, kept in the persistent kernel
+# (0x10) where the driver would otherwise launch one kernel per GEMV
+MODES = {"ordered": 0x2 | 0x10, "hazards": 0x0, "launch_each": 0x1, "persistent": 0x10}
 
 
 def parse():
@@ -182,15 +184,16 @@ def main():
     if not args.only_step:
         other = {}
         for mode in MODES:
-            if mode == args.mode:
+            if mode in (args.mode, "persistent"):
                 continue
             m_ms, _ = time_mode(mode, max(5, args.steps // 5), max(3, args.warmup // 4))
             other[mode] = {"ms_per_step": round(m_ms, 5),
                            "gbs": round(step_bytes / (m_ms * 1e-3) / 1e9, 1)}
-        for mode in ("hazards", "launch_each"):
+        for mode in ("persistent", "launch_each", "hazards"):
             m_ms, _ = time_mode(mode, max(5, args.steps // 5), max(3, args.warmup // 4),
                                 chain_layers)
-            other[f"chain_{mode}"] = {"ms_per_step": round(m_ms, 5),
+            key = "chain_default_choice" if mode == "hazards" else f"chain_{mode}"
+            other[key] = {"ms_per_step": round(m_ms, 5),
                                       "gbs": round(step_bytes / (m_ms * 1e-3) / 1e9, 1)}
         result["other_modes"] = other
         if not args.no_configs:
@@ -326,8 +329,8 @@ def per_config(torch, q4, synth, np, stream):
         q4.q4_silu_mul(gu, hbuf, stream=stream)
         q4.q4_gemv(Wd, Sd, hbuf, y, ws=wsg, stream=stream)
     out["mlp_silu_gate_up_down_m1"] = {
-        "fused_decode_step": _fig(b3, _timed(torch, stream, glue_step(0), 5) / copies,
-                                  copies=copies),
+        "fused_decode_step": _fig(b3, _timed(torch, stream, glue_step(q4.STEP_PERSISTENT), 5) /
+                                  copies, copies=copies),
         "three_calls": _fig(b3, _timed(torch, stream, unfused, 4 * copies), copies=copies),
         "decode_step_one_kernel_per_gemv": _fig(
             b3, _timed(torch, stream, glue_step(q4.STEP_LAUNCH_EACH), 5) / copies,

@@ -32,6 +32,7 @@ STEP_LAUNCH_EACH = 0x1
 STEP_ORDERED = 0x2
 STEP_LDS_RING = 0x4
 STEP_WS_CLEAN = 0x8
+STEP_PERSISTENT = 0x10
 X_PLAIN = 0
 X_SILU_MUL = 1
 TOKENS_EAGER = 0x1

@@ -286,8 +286,20 @@ std::vector<q4::StepLayer> to_step_layers(const q4_layer* layers, int64_t n) {
 
 // The persistent path applies to M == 1 lists whose rows fit its item shape,
 // when one workgroup of the step kernel fits on every compute unit.
+// Lists in which many descriptors wait for another run faster as one kernel per
+// GEMV: in the persistent kernel every waiting GEMV pays its hand-over and its
+// arithmetic on the critical path (measured on MI355X: 9.3 us per dependent GEMV
+// against about 7 us per launched GEMV), so beyond a quarter of the list waiting the
+// launches win, unless the caller asks for the persistent kernel.
+bool dependency_bound(int64_t n, int waiting, uint32_t flags) {
+  return !(flags & Q4_STEP_PERSISTENT) && 4 * (int64_t)waiting > n;
+}
+
 bool use_persistent(const q4::DeviceInfo& d, const q4::StepPlan& p, int64_t M, uint32_t flags) {
   if (M != 1 || (flags & Q4_STEP_LAUNCH_EACH) || !p.ok) return false;
+  int waiting = 0;
+  for (const q4::StepDesc& sd : p.desc) waiting += sd.dep >= 0;
+  if (dependency_bound((int64_t)p.desc.size(), waiting, flags)) return false;
   int per_cu = 0;
   if (q4::step_occupancy(p, &per_cu) != hipSuccess || per_cu < 1) {
     (void)hipGetLastError();
@@ -384,7 +396,8 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (n_layers > (1 << 20))
     return fail(Q4_ERR_UNSUPPORTED, "q4_decode_step: n_layers = %lld: too many",
                 (long long)n_layers);
-  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED | Q4_STEP_LDS_RING | Q4_STEP_WS_CLEAN))
+  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED | Q4_STEP_LDS_RING | Q4_STEP_WS_CLEAN |
+                Q4_STEP_PERSISTENT))
     return fail(Q4_ERR_SHAPE, "q4_decode_step: unknown flags 0x%x", flags);
   char what[64];
   for (int64_t i = 0; i < n_layers; ++i) {
@@ -406,7 +419,10 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
     q4::MStepPlan p = q4::plan_step_mfma(*d, sl.data(), n_layers, (int)M,
                                          (flags & Q4_STEP_ORDERED) != 0);
     int per_cu = 0;
-    if (p.ok && q4::step_mfma_occupancy(p, &per_cu) == hipSuccess && per_cu >= 1) {
+    int waiting = 0;
+    for (const q4::MStepDesc& sd : p.desc) waiting += sd.dep >= 0;
+    if (p.ok && !dependency_bound(n_layers, waiting, flags) &&
+        q4::step_mfma_occupancy(p, &per_cu) == hipSuccess && per_cu >= 1) {
       if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_mfma_workspace_bytes(p)))
         return rc;
       hipError_t e = hipSuccess;

@@ -166,6 +166,10 @@ typedef struct q4_layer {
  * its input before the GEMV producing it has finished (wrong results) or make
  * the kernel's bounded waits run out.  The other paths ignore the flag. */
 #define Q4_STEP_WS_CLEAN 0x8u
+/* Use the persistent kernel even for a list in which more than a quarter of the
+ * descriptors wait for another (such lists otherwise run one kernel per
+ * descriptor, which is faster for them). */
+#define Q4_STEP_PERSISTENT 0x10u
 
 /* q4_decode_step: run the GEMVs of layers[0 .. n_layers) in list order, as the
  * Zero TVM decode loop walks the projections of every layer and then the LM
@@ -184,8 +188,9 @@ typedef struct q4_layer {
  * only conflict is one earlier descriptor whose y holds all of its x (M == 1),
  * that y is also handed over through the workspace as tagged values the reader
  * polls; other conflicts wait on per-descriptor completion counters in the
- * workspace.  Lists whose conflicts one such wait cannot cover, and all other
- * lists, run one kernel per descriptor.  The descriptor table of a persistent
+ * workspace.  Lists in which more than a quarter of the descriptors wait for
+ * another (unless Q4_STEP_PERSISTENT), lists whose conflicts one such wait cannot
+ * cover, and all other lists run one kernel per descriptor.  The descriptor table of a persistent
  * list is copied to device memory the first time the list is used (the library
  * allocates that copy and keeps it for later calls with the same list; at most
  * 16 lists are kept, the least recently used is freed with hipFree, which

@@ -14,8 +14,9 @@ from gpuhelp import assert_gemv_close, dev_half, dev_words, half_f64, host_half
 
 pytestmark = pytest.mark.gpu
 
-MODES = {"hazards": 0, "ordered": q4.STEP_ORDERED, "launch_each": q4.STEP_LAUNCH_EACH,
-         "hazards_ring": q4.STEP_LDS_RING}
+MODES = {"hazards": q4.STEP_PERSISTENT, "ordered": q4.STEP_ORDERED | q4.STEP_PERSISTENT,
+         "launch_each": q4.STEP_LAUNCH_EACH, "auto": 0,
+         "hazards_ring": q4.STEP_LDS_RING | q4.STEP_PERSISTENT}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -99,7 +100,8 @@ def test_fused_glue_equals_standalone_glue_bitwise():
     mdn, Wdn, Sdn = mat("glue/bit/down", D, H)
     x = dev_half(synth.activations("glue/bit/x", 0, D))
     gu, y = nan_half(2 * H), nan_half(D)
-    q4.q4_decode_step(q4.make_layers([(Wgu, Sgu, x, gu), (Wdn, Sdn, gu, y, q4.X_SILU_MUL)]), 1, 0)
+    q4.q4_decode_step(q4.make_layers([(Wgu, Sgu, x, gu), (Wdn, Sdn, gu, y, q4.X_SILU_MUL)]), 1,
+                      q4.STEP_PERSISTENT)
     h = q4.q4_silu_mul(gu)
     y2 = nan_half(D)
     q4.q4_decode_step(q4.make_layers([(Wdn, Sdn, h, y2)]), 1, 0)
@@ -125,7 +127,7 @@ def test_glue_behind_a_counter_wait():
     gu, z, y = nan_half(2 * H), nan_half(1000), nan_half(D)
     layers = q4.make_layers([(Wgu, Sgu, x, gu), (Wmid, Smid, x, z),
                              (Wdn, Sdn, gu, y, q4.X_SILU_MUL)])
-    q4.q4_decode_step(layers, 1, q4.STEP_ORDERED)
+    q4.q4_decode_step(layers, 1, q4.STEP_ORDERED | q4.STEP_PERSISTENT)
     torch.cuda.synchronize()
     gu_h = host_half(gu)
     assert_gemv_close(gu_h, mgu.words(), mgu.scales(), host_half(x))

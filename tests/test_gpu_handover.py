@@ -33,7 +33,8 @@ def nan_half(n):
     return torch.full((n,), float("nan"), dtype=torch.float16, device="cuda")
 
 
-def run(descs, flags=0, ws=None):
+def run(descs, flags=q4.STEP_PERSISTENT, ws=None):
+    # the persistent kernel even where the driver would launch one kernel per GEMV
     layers = q4.make_layers(descs)
     q4.q4_decode_step(layers, 1, flags, ws=ws)
     torch.cuda.synchronize()
@@ -45,7 +46,8 @@ def check(m, X, Y):
     assert_gemv_close(y, m.words(), m.scales(), host_half(X))
 
 
-@pytest.mark.parametrize("flags", [0, q4.STEP_ORDERED], ids=["hazards", "ordered"])
+@pytest.mark.parametrize("flags", [q4.STEP_PERSISTENT, q4.STEP_ORDERED | q4.STEP_PERSISTENT, 0],
+                         ids=["hazards", "ordered", "auto"])
 def test_consumers_of_slices(flags):
     """Three GEMVs read the three thirds of one qkv-shaped output (even element
     offsets); in ordered mode each also waits for its predecessor."""
@@ -103,7 +105,7 @@ def test_reader_of_two_writers(chained, M):
     else:
         descs = [(W1, S1, x1, y1), (W2, S2, x2, y2), (W3, S3, buf.view(M, K), y3)]
     layers = q4.make_layers(descs)
-    q4.q4_decode_step(layers, M, 0)
+    q4.q4_decode_step(layers, M, q4.STEP_PERSISTENT)
     torch.cuda.synchronize()
     for m, (W, S, X, Y) in zip([m1, m2, m3], descs):
         y = host_half(Y)
@@ -149,9 +151,10 @@ def test_repeated_calls_on_one_workspace():
         mats.append(m)
         x = y
     layers = q4.make_layers(descs)
-    need = q4.q4_decode_step_workspace_bytes(layers, 1, 0)
+    P = q4.STEP_PERSISTENT
+    need = q4.q4_decode_step_workspace_bytes(layers, 1, P)
     ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
-    q4.q4_decode_step(layers, 1, 0, ws=ws)
+    q4.q4_decode_step(layers, 1, P, ws=ws)
     torch.cuda.synchronize()
     ref = [host_half(d[3]) for d in descs]
     for m, (W, S, X, Y) in zip(mats, descs):
@@ -159,7 +162,7 @@ def test_repeated_calls_on_one_workspace():
     for _ in range(6):
         for d in descs:
             d[3].fill_(float("nan"))
-        q4.q4_decode_step(layers, 1, q4.STEP_WS_CLEAN, ws=ws)
+        q4.q4_decode_step(layers, 1, P | q4.STEP_WS_CLEAN, ws=ws)
         torch.cuda.synchronize()
         for r, d in zip(ref, descs):
             assert np.array_equal(r, host_half(d[3]))

@@ -15,9 +15,12 @@ pytestmark = pytest.mark.gpu
 
 # default: the register-streaming persistent kernel; *_ring: the LDS-ring kernel
 # where it applies (every K % 256 == 0, K <= 8192), else the register one
-MODES = {"hazards": 0, "ordered": q4.STEP_ORDERED, "launch_each": q4.STEP_LAUNCH_EACH,
-         "hazards_ring": q4.STEP_LDS_RING,
-         "ordered_ring": q4.STEP_ORDERED | q4.STEP_LDS_RING}
+# (STEP_PERSISTENT keeps dependency-heavy lists in the persistent kernel; "auto"
+# lets the driver choose)
+MODES = {"hazards": q4.STEP_PERSISTENT, "ordered": q4.STEP_ORDERED | q4.STEP_PERSISTENT,
+         "launch_each": q4.STEP_LAUNCH_EACH, "auto": 0,
+         "hazards_ring": q4.STEP_LDS_RING | q4.STEP_PERSISTENT,
+         "ordered_ring": q4.STEP_ORDERED | q4.STEP_LDS_RING | q4.STEP_PERSISTENT}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -135,7 +138,7 @@ def test_modes_agree_on_the_phi3_layer():
         outs[mode] = [host_half(d[3]) for d in descs]
     # the persistent kernels use the same lane mapping and arithmetic for these
     # shapes (32 lanes x 3 groups, 64 x 4): bitwise equal across modes and kernels
-    for m in ("ordered", "hazards_ring", "ordered_ring"):
+    for m in ("ordered", "auto", "hazards_ring", "ordered_ring"):
         for a, b in zip(outs["hazards"], outs[m]):
             assert np.array_equal(a, b), m
     for (m, W, S), y, (N, K) in zip(mats, outs["ordered"], shapes):
@@ -143,7 +146,8 @@ def test_modes_agree_on_the_phi3_layer():
         assert_gemv_close(y, m.words(), m.scales(), x)
 
 
-@pytest.mark.parametrize("flags", [0, q4.STEP_ORDERED], ids=["hazards", "ordered"])
+@pytest.mark.parametrize("flags", [q4.STEP_PERSISTENT, q4.STEP_ORDERED | q4.STEP_PERSISTENT],
+                         ids=["hazards", "ordered"])
 def test_workspace_left_clean_and_ws_clean_calls(flags):
     """The persistent kernel leaves its counters zero, so later calls with the same
     list may skip clearing them (STEP_WS_CLEAN); results stay bitwise the same."""
@@ -193,7 +197,8 @@ def _m_chain(prefix, M, dims):
 
 
 @pytest.mark.parametrize("M", [2, 3, 5, 8])
-@pytest.mark.parametrize("flags", [0, q4.STEP_ORDERED], ids=["hazards", "ordered"])
+@pytest.mark.parametrize("flags", [q4.STEP_PERSISTENT, q4.STEP_ORDERED | q4.STEP_PERSISTENT, 0],
+                         ids=["hazards", "ordered", "auto"])
 def test_small_m_dependent_chain(M, flags):
     """M rows per GEMV in one persistent kernel: each descriptor reads the previous
     one's Y; ragged rows (N not a multiple of 16, N < 16) and K from 128 to 8192."""
@@ -251,9 +256,9 @@ def test_small_m_workspace_left_clean():
     M = 8
     descs, mats = _m_chain("mclean", M, [2048, 6144, 2048, 8192, 2048])
     layers = q4.make_layers(descs)
-    need = q4.q4_decode_step_workspace_bytes(layers, M, 0)
+    need = q4.q4_decode_step_workspace_bytes(layers, M, q4.STEP_PERSISTENT)
     ws = torch.full((need,), 0x33, dtype=torch.uint8, device="cuda")
-    q4.q4_decode_step(layers, M, 0, ws=ws)
+    q4.q4_decode_step(layers, M, q4.STEP_PERSISTENT, ws=ws)
     torch.cuda.synchronize()
     ref = [host_half(d[3]) for d in descs]
     n = len(descs)
@@ -261,7 +266,7 @@ def test_small_m_workspace_left_clean():
     for _ in range(3):
         for d in descs:
             d[3].fill_(float("nan"))
-        q4.q4_decode_step(layers, M, q4.STEP_WS_CLEAN, ws=ws)
+        q4.q4_decode_step(layers, M, q4.STEP_PERSISTENT | q4.STEP_WS_CLEAN, ws=ws)
         torch.cuda.synchronize()
         for r, d in zip(ref, descs):
             assert np.array_equal(r, host_half(d[3]))
