@@ -78,6 +78,8 @@ def _load():
             lib.orc_add_rmsnorm.restype = None
             lib.orc_argmax.argtypes = [p, i64, i64, p]
             lib.orc_argmax.restype = None
+            lib.orc_gemv_format.argtypes = [C.c_int, p, p, p, p, i64, i64, p, i64, p, p]
+            lib.orc_gemv_format.restype = C.c_int
             lib.orc_vec_norm.argtypes = [p, i64]
             lib.orc_vec_norm.restype = C.c_double
             _lib = lib
@@ -239,6 +241,28 @@ def argmax(x) -> np.ndarray:
     out = np.empty(x2.shape[0], np.int32)
     _load().orc_argmax(_ptr(x2), x2.shape[0], x2.shape[1], _ptr(out))
     return out
+
+
+FORMATS = {"q3f16_1": 1, "q4f32_1": 2, "af4g64": 3}
+
+
+def gemv_format(fmt: str, words, scales, biases, x, K: int, rows=None):
+    """fp64 y = W x for a format variant (see orc_gemv_format) and the row norms:
+    returns (y [n_rows], norms [n_rows]).  x: fp16 bits, or fp32 for q4f32_1."""
+    f = FORMATS[fmt]
+    w = _c(words, np.uint32)
+    sc = _c(scales, np.float32 if f == 2 else np.uint16)
+    bi = _c(biases, np.uint16) if biases is not None else None
+    xs = _c(x, np.float32 if f == 2 else np.uint16).reshape(-1)
+    N = w.shape[0]
+    r, nr = _rows_arg(rows, N)
+    y = np.empty(nr, np.float64)
+    nrm = np.empty(nr, np.float64)
+    rc = _load().orc_gemv_format(f, _ptr(w), _ptr(sc), _ptr(bi), _ptr(xs), N, K, _ptr(r), nr,
+                                 _ptr(y), _ptr(nrm))
+    if rc:
+        raise ValueError(f"orc_gemv_format failed ({rc})")
+    return y, nrm
 
 
 def vec_norm(x) -> float:

@@ -265,6 +265,65 @@ ORC_EXPORT void orc_silu_mul(const uint16_t* GU, uint16_t* OUT, int64_t M, int64
     }
 }
 
+/* ---------------------------------------------------------- other formats */
+
+/* The format variants of the everything-webgpu AI.md quantization table and of
+ * the MLX checkpoints the Zero TVM documentation loads, each as a plain decode:
+ *   format 1, q3f16_1: 12 bytes of codes + an fp16 scale per 32 weights; the
+ *     group's 32 codes are the 3-bit fields [3i, 3i + 3) of its three
+ *     little-endian words taken as one 96-bit value; weight = (q - 3) * s.
+ *   format 2, q4f32_1: q4f16_1's codes with fp32 scales; x and y fp32.
+ *   format 3, MLX affine 4-bit, group 64: q4f16_1's nibble order, an fp16 scale
+ *     and an fp16 bias per 64 weights; weight = s * q + b.
+ * W[n][k] for one element, in fp64. */
+static double fmt_weight(int format, const uint32_t* words, const void* scales,
+                         const void* biases, int64_t K, int64_t n, int64_t k) {
+  if (format == 1) {
+    const int64_t g = k / 32, i = k % 32;
+    const uint32_t* w = words + n * (K / 32) * 3 + g * 3;
+    unsigned q = 0;
+    for (int b = 0; b < 3; ++b) {
+      const int64_t bit = 3 * i + b;
+      q |= ((w[bit / 32] >> (bit % 32)) & 1u) << b;
+    }
+    const double s = orc_half_to_f64(((const uint16_t*)scales)[n * (K / 32) + g]);
+    return ((double)q - 3.0) * s;
+  }
+  const unsigned q = code_at(words, K, n, k);
+  if (format == 2) {
+    const float s = ((const float*)scales)[n * (K / 32) + k / 32];
+    return ((double)q - 7.0) * (double)s;
+  }
+  const double s = orc_half_to_f64(((const uint16_t*)scales)[n * (K / 64) + k / 64]);
+  const double b = orc_half_to_f64(((const uint16_t*)biases)[n * (K / 64) + k / 64]);
+  return s * (double)q + b;
+}
+
+/* Y[i] = sum_k W[n][k] * x[k] (n = rows[i], or i when rows is NULL), fp64, k
+ * ascending; x is fp16 bits (formats 1, 3) or fp32 (format 2).  Also the row
+ * norms ||W_n||_2 into NORMS when not NULL.  Returns 0, or -1 on a bad shape. */
+ORC_EXPORT int orc_gemv_format(int format, const uint32_t* words, const void* scales,
+                               const void* biases, const void* X, int64_t N, int64_t K,
+                               const int64_t* rows, int64_t n_rows, double* Y, double* NORMS) {
+  if (format < 1 || format > 3 || N < 1 || K < 32 || K % 32 || (format == 3 && K % 64))
+    return -1;
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const int64_t n = rows ? rows[i] : i;
+    if (n < 0 || n >= N) return -1;
+    double acc = 0.0, nn = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double w = fmt_weight(format, words, scales, biases, K, n, k);
+      const double x = format == 2 ? (double)((const float*)X)[k]
+                                   : orc_half_to_f64(((const uint16_t*)X)[k]);
+      acc += w * x;
+      nn += w * w;
+    }
+    Y[i] = acc;
+    if (NORMS) NORMS[i] = sqrt(nn);
+  }
+  return 0;
+}
+
 /* ------------------------------------------------ the rest of a decode step */
 
 /* The steps of the decode loop around its GEMVs (Zero TVM documentation,

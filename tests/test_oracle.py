@@ -542,3 +542,122 @@ def test_step_pins_catch_planted_mistake(name, monkeypatch):
             except AssertionError:
                 failed += 1
         assert failed, name
+
+
+# ------------------------------------------------------------ format variant pins
+
+def _pack_q3(codes):
+    """Independent packer: 32 3-bit codes per group -> three little-endian words
+    holding bits [3i, 3i + 3) of one 96-bit value (Python integers)."""
+    N, K = codes.shape
+    out = np.zeros((N, K // 32 * 3), np.uint32)
+    for n in range(N):
+        for g in range(K // 32):
+            v = 0
+            for i in range(32):
+                v |= int(codes[n, 32 * g + i]) << (3 * i)
+            for j in range(3):
+                out[n, 3 * g + j] = (v >> (32 * j)) & 0xFFFFFFFF
+    return out
+
+
+def _format_case(fmt, N=6, K=128, seed=3):
+    rng = np.random.default_rng(seed)
+    if fmt == "q3f16_1":
+        c = rng.integers(0, 8, (N, K)).astype(np.uint8)
+        w = _pack_q3(c)
+        s16 = (rng.standard_normal((N, K // 32)) * 0.02).astype(np.float16)
+        W = (c.astype(np.float64) - 3) * np.repeat(s16.astype(np.float64), 32, axis=1)
+        return w, s16.view(np.uint16), None, W
+    c = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    w = oracle.pack(c)
+    if fmt == "q4f32_1":
+        s32 = (rng.standard_normal((N, K // 32)) * 0.02).astype(np.float32)
+        W = (c.astype(np.float64) - 7) * np.repeat(s32.astype(np.float64), 32, axis=1)
+        return w, s32, None, W
+    s16 = (rng.standard_normal((N, K // 64)) * 0.02).astype(np.float16)
+    b16 = (rng.standard_normal((N, K // 64)) * 0.1).astype(np.float16)
+    W = (c.astype(np.float64) * np.repeat(s16.astype(np.float64), 64, axis=1) +
+         np.repeat(b16.astype(np.float64), 64, axis=1))
+    return w, s16.view(np.uint16), b16.view(np.uint16), W
+
+
+@pytest.mark.parametrize("fmt", ["q3f16_1", "q4f32_1", "af4g64"])
+def test_format_gemv_vs_numpy(fmt):
+    N, K = 6, 128
+    w, s, b, W = _format_case(fmt, N, K)
+    rng = np.random.default_rng(9)
+    if fmt == "q4f32_1":
+        x = rng.standard_normal(K).astype(np.float32)
+        xf = x.astype(np.float64)
+    else:
+        x = rng.standard_normal(K).astype(np.float16).view(np.uint16)
+        xf = x.view(np.float16).astype(np.float64)
+    y, norms = oracle.gemv_format(fmt, w, s, b, x, K)
+    assert np.allclose(y, W @ xf, rtol=1e-12, atol=1e-12)
+    assert np.allclose(norms, np.sqrt((W * W).sum(axis=1)), rtol=1e-12)
+    # one-hot x picks column k of W exactly
+    for k in (0, 31, 32, 63, 64, 127):
+        oh = np.zeros(K, np.float32) if fmt == "q4f32_1" else np.zeros(K, np.uint16)
+        oh[k] = 1.0 if fmt == "q4f32_1" else 0x3C00
+        yk, _ = oracle.gemv_format(fmt, w, s, b, oh, K)
+        assert np.array_equal(yk, W[:, k]), (fmt, k)
+
+
+def test_format_closed_forms():
+    K = 64
+    # q3f16_1: every code 3 -> zero weights; codes 7 with scale 1 -> weight 4
+    c = np.full((2, K), 3, np.uint8)
+    c[1] = 7
+    s = np.full((2, K // 32), np.float16(1.0)).view(np.uint16)
+    x = np.full(K, np.float16(1.0)).view(np.uint16)
+    y, _ = oracle.gemv_format("q3f16_1", _pack_q3(c), s, None, x, K)
+    assert list(y) == [0.0, 4.0 * K]
+    # affine: codes 0, bias b -> b * sum(x)
+    w = oracle.pack(np.zeros((1, K), np.uint8))
+    sc = np.full((1, 1), np.float16(0.5)).view(np.uint16)
+    bi = np.full((1, 1), np.float16(0.25)).view(np.uint16)
+    y, _ = oracle.gemv_format("af4g64", w, sc, bi, x, K)
+    assert y[0] == 0.25 * K
+
+
+FORMAT_MUTATIONS = {
+    "q3_zero_point": ("return ((double)q - 3.0) * s;", "return ((double)q - 4.0) * s;"),
+    "q3_bit_order": ("const int64_t bit = 3 * i + b;", "const int64_t bit = 3 * i + (2 - b);"),
+    "q4f32_zero_point": ("return ((double)q - 7.0) * (double)s;", "return ((double)q - 8.0) * (double)s;"),
+    "affine_group_32": ("const double s = orc_half_to_f64(((const uint16_t*)scales)[n * (K / 64) + k / 64]);",
+                        "const double s = orc_half_to_f64(((const uint16_t*)scales)[n * (K / 64) + k / 32 % (K / 64)]);"),
+    "affine_no_bias": ("return s * (double)q + b;", "return s * (double)q;"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+@pytest.mark.parametrize("name", sorted(FORMAT_MUTATIONS))
+def test_format_pins_catch_planted_mistake(name, monkeypatch):
+    src = open(os.path.join(ROOT, "oracle", "q4_oracle.c")).read()
+    a, b = FORMAT_MUTATIONS[name]
+    assert a in src, name
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "m.c")
+        open(path, "w").write(src.replace(a, b))
+        so = os.path.join(tmp, "m.so")
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-o", so,
+                               path, "-lm"])
+        real = oracle._load()
+        mutant = C.CDLL(so)
+        for fn in ("orc_gemv_format", "orc_pack", "orc_unpack", "orc_half_to_f64"):
+            f = getattr(mutant, fn)
+            f.argtypes = getattr(real, fn).argtypes
+            f.restype = getattr(real, fn).restype
+        monkeypatch.setattr(oracle, "_lib", mutant)
+        failed = 0
+        for fmt in ("q3f16_1", "q4f32_1", "af4g64"):
+            try:
+                test_format_gemv_vs_numpy(fmt)
+            except AssertionError:
+                failed += 1
+        try:
+            test_format_closed_forms()
+        except AssertionError:
+            failed += 1
+        assert failed, name
