@@ -36,6 +36,9 @@ STEP_PERSISTENT = 0x10
 X_PLAIN = 0
 X_SILU_MUL = 1
 TOKENS_EAGER = 0x1
+FMT_Q3F16_1 = 1
+FMT_Q4F32_1 = 2
+FMT_AF4_G64 = 3
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
           4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED"}
@@ -108,6 +111,8 @@ def load():
             "q4_rmsnorm": ([p, p, C.c_float, i64, i64, p, p], i32),
             "q4_add_rmsnorm": ([p, p, p, C.c_float, i64, i64, p, p, p], i32),
             "q4_argmax": ([p, i64, i64, p, p], i32),
+            "q4_gemv_format": ([C.c_uint32, p, p, p, p, p, i64, i64, p], i32),
+            "q4_format_weight_bytes": ([C.c_uint32, i64, i64], sz),
             "q4_decode_token_workspace_bytes": ([p], sz),
             "q4_decode_token": ([p, p, p, p, p, sz, p], i32),
             "q4_decode_tokens": ([p, p, i64, p, sz, C.c_uint32, p], i32),
@@ -401,6 +406,23 @@ def q4_decode_tokens(model: Model, tokens, steps: int, ws=None, flags: int = 0, 
     _check(load().q4_decode_tokens(model.ref(), _ptr(tokens), steps, _ptr(ws), ws.numel(), flags,
                                    _stream(stream)))
     return ws
+
+
+def q4_gemv_format(fmt: int, words, scales, x, K: int, biases=None, y=None, stream=None):
+    """y = W x for a format variant (FMT_*); words: int32 tensor of the format's
+    layout with N rows; K the logical row length."""
+    torch = _torch()
+    N = words.shape[0]
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32 if fmt == FMT_Q4F32_1 else torch.float16,
+                        device=words.device)
+    _check(load().q4_gemv_format(fmt, _ptr(words), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y),
+                                 N, K, _stream(stream)))
+    return y
+
+
+def q4_format_weight_bytes(fmt: int, N: int, K: int) -> int:
+    return int(load().q4_format_weight_bytes(fmt, N, K))
 
 
 def q4_probe_read(buf, sink, blocks: int = 0, stream=None):

@@ -590,6 +590,46 @@ int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_stream_t
   return e == hipSuccess ? ok() : device_error(e, "q4_argmax");
 }
 
+size_t q4_format_weight_bytes(uint32_t format, int64_t N, int64_t K) {
+  if (N < 1 || K < 32 || K % 32 || format > Q4_FMT_AF4_G64) return 0;
+  if (format == Q4_FMT_AF4_G64 && K % 64) return 0;
+  switch (format) {
+    case Q4_FMT_Q3F16_1: return (size_t)N * (size_t)(K / 32) * (12 + 2);
+    case Q4_FMT_Q4F32_1: return (size_t)N * (size_t)(K / 32) * (16 + 4);
+    case Q4_FMT_AF4_G64: return (size_t)N * (size_t)(K / 64) * (32 + 2 + 2);
+    default: return (size_t)N * (size_t)(K / 32) * (16 + 2);
+  }
+}
+
+int q4_gemv_format(uint32_t format, const uint32_t* words, const void* scales,
+                   const uint16_t* biases, const void* x, void* y, int64_t N, int64_t K,
+                   q4_stream_t stream) {
+  if (format < Q4_FMT_Q3F16_1 || format > Q4_FMT_AF4_G64)
+    return fail(Q4_ERR_SHAPE, "q4_gemv_format: format = %u: unknown", format);
+  if (!words || !scales || !x || !y) return fail(Q4_ERR_NULL, "q4_gemv_format: NULL pointer");
+  const bool affine = format == Q4_FMT_AF4_G64, f32 = format == Q4_FMT_Q4F32_1;
+  if (affine != (biases != nullptr))
+    return fail(affine ? Q4_ERR_NULL : Q4_ERR_SHAPE,
+                "q4_gemv_format: biases must be given for the affine format only");
+  if (N < 1 || N > INT32_MAX || K < 32 || K > 32768 || K % (affine ? 64 : 32))
+    return fail(Q4_ERR_SHAPE, "q4_gemv_format: N = %lld, K = %lld", (long long)N, (long long)K);
+  const size_t es = f32 ? 4 : 2;
+  if (!aligned(words, format == Q4_FMT_Q3F16_1 ? 4 : 16) || !aligned(scales, es) ||
+      (biases && !aligned(biases, 2)) || !aligned(x, es) || !aligned(y, es))
+    return fail(Q4_ERR_ALIGN, "q4_gemv_format: misaligned pointer");
+  const int64_t wb = N * (K / 32) * (format == Q4_FMT_Q3F16_1 ? 12 : 16);
+  const int64_t groups = N * (K / (affine ? 64 : 32));
+  const int64_t yb = N * (int64_t)es;
+  if (spans_overlap(y, yb, words, wb) || spans_overlap(y, yb, scales, groups * (int64_t)es) ||
+      (biases && spans_overlap(y, yb, biases, 2 * groups)) || spans_overlap(y, yb, x, K * (int64_t)es))
+    return fail(Q4_ERR_SHAPE, "q4_gemv_format: y overlaps an input");
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return fail(Q4_ERR_DEVICE, "q4_gemv_format: no HIP device");
+  hipError_t e = q4::launch_gemv_format(*d, (int)format, words, scales, biases, x, y, N, K,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, "q4_gemv_format");
+}
+
 int q4_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t blocks,
                   q4_stream_t stream) {
   if (!buf || !sink) return fail(Q4_ERR_NULL, "q4_probe_read: NULL pointer");

@@ -100,6 +100,12 @@ hipError_t launch_token_store(int32_t* tokens, int32_t* counter, const int32_t* 
                               hipStream_t s);
 hipError_t launch_counter_reset(int32_t* counter, hipStream_t s);
 
+// GEMV of a format variant at M = 1 (q4_formats.hip): format 1 q3f16_1, 2 q4f32_1,
+// 3 af4g64 (see include/q4f16.h); K <= 32768.
+hipError_t launch_gemv_format(const DeviceInfo& d, int format, const uint32_t* W, const void* S,
+                              const uint16_t* B, const void* X, void* Y, int64_t N, int64_t K,
+                              hipStream_t s);
+
 hipError_t launch_probe_read(const DeviceInfo& d, const void* buf, size_t bytes, uint32_t* sink,
                              int64_t blocks, hipStream_t s);
 hipError_t launch_probe_copy(const DeviceInfo& d, const void* src, void* dst, size_t bytes,

@@ -247,6 +247,36 @@ Q4_API int q4_add_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const u
  * int32 [M], device memory.  x 2-byte aligned. */
 Q4_API int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_stream_t stream);
 
+/* ------------------------------------------------------ format variants -- */
+/* Formats beside q4f16_1 (everything-webgpu AI.md, "Which quantization to
+ * recompile with": q3f16_1 at 14 bytes and q4f32_1 at 20 bytes per 32 weights;
+ * Zero TVM documentation: MLX affine checkpoints, w = s * q + b in groups of 64):
+ *   Q4_FMT_Q3F16_1: words uint32 [N][3K/32] -- a group of 32 weights is three
+ *     consecutive words read as one little-endian 96-bit value, code i in its
+ *     bits [3i, 3i + 3); scales fp16 [N][K/32]; weight = (q - 3) * s; x, y fp16.
+ *   Q4_FMT_Q4F32_1: words as q4f16_1 ([N][K/8]); scales fp32 [N][K/32];
+ *     weight = (q - 7) * s; x, y fp32.
+ *   Q4_FMT_AF4_G64: words as q4f16_1; scales and biases fp16 [N][K/64];
+ *     weight = s * q + b; x, y fp16.  K % 64 == 0.
+ * The 3-bit packing and its zero point (2^(bits - 1) - 1, as q4f16_1's 7) are
+ * our reading: the table gives only the bytes per group. */
+#define Q4_FMT_Q3F16_1 1u
+#define Q4_FMT_Q4F32_1 2u
+#define Q4_FMT_AF4_G64 3u
+
+/* q4_gemv_format: y = W x (M = 1) for a format variant, fp32 accumulation, fp16
+ * outputs rounded to nearest even (fp32 outputs for Q4_FMT_Q4F32_1).  biases: NULL
+ * except for Q4_FMT_AF4_G64.  32 <= K <= 32768, K % 32 == 0 (% 64 for affine);
+ * words 16-byte aligned (4-byte for q3f16_1), the rest aligned to their element;
+ * y must not overlap an input. */
+Q4_API int q4_gemv_format(uint32_t format, const uint32_t* words, const void* scales,
+                          const uint16_t* biases, const void* x, void* y, int64_t N, int64_t K,
+                          q4_stream_t stream);
+
+/* Bytes of words, scales and biases of an N x K matrix in a format (0 = q4f16_1);
+ * 0 for an invalid format or shape. */
+Q4_API size_t q4_format_weight_bytes(uint32_t format, int64_t N, int64_t K);
+
 /* -------------------------------------------------------- decode tokens -- */
 /* The decode loop end to end (Zero TVM documentation, "Decode loop"), weights
  * only: the token's embedding row; an RMSNorm; per block qkv, attention, o, the

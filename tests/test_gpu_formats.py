@@ -1,0 +1,86 @@
+"""The format variants (q3f16_1, q4f32_1, MLX affine 4-bit group 64) through
+q4_gemv_format against the oracle's plain decode of the same words, at small
+ragged shapes and at the Phi-3 projection shapes."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+import bit_weight_streaming_q4f16_amd as q4
+from gpuhelp import dev_half, dev_words, half_f64, host_half
+
+pytestmark = pytest.mark.gpu
+
+FMTS = {"q3f16_1": q4.FMT_Q3F16_1, "q4f32_1": q4.FMT_Q4F32_1, "af4g64": q4.FMT_AF4_G64}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q4.load()
+
+
+def make(fmt, N, K, tag):
+    """Seeded words (uniform codes), scales, biases and x in the format's layout."""
+    lab = f"fmt/{fmt}/{tag}/{N}x{K}"
+    if fmt == "q3f16_1":
+        words = synth.words(lab + "/w", 0, N * K // 32 * 3).reshape(N, K // 32 * 3)
+        scales = synth.scales_halfnormal(lab + "/s", 0, 0, N * K // 32, 0.01, 1e-3).reshape(N, -1)
+        biases = None
+    elif fmt == "q4f32_1":
+        words = synth.words(lab + "/w", 0, N * K // 8).reshape(N, K // 8)
+        scales = (np.abs(synth.normal(lab + "/s", 0, 0, N * K // 32)) * 0.01 + 1e-3).astype(
+            np.float32).reshape(N, -1)
+        biases = None
+    else:
+        words = synth.words(lab + "/w", 0, N * K // 8).reshape(N, K // 8)
+        scales = synth.scales_halfnormal(lab + "/s", 0, 0, N * K // 64, 0.01, 1e-3).reshape(N, -1)
+        biases = synth.to_half_bits(0.05 * synth.normal(lab + "/b", 0, 0, N * K // 64)).reshape(N, -1)
+    if fmt == "q4f32_1":
+        x = synth.normal(lab + "/x", 0, 0, K).astype(np.float32)
+    else:
+        x = synth.activations(lab + "/x", 0, K)
+    return words, scales, biases, x
+
+
+def to_dev(a):
+    if a is None:
+        return None
+    if a.dtype == np.float32:
+        return torch.from_numpy(a).cuda()
+    if a.dtype == np.uint32:
+        return dev_words(a)
+    return dev_half(a)
+
+
+@pytest.mark.parametrize("fmt", sorted(FMTS))
+@pytest.mark.parametrize("N,K", [(33, 128), (1000, 64 * 3), (9216, 3072), (3072, 8192)])
+def test_format_gemv_matches_oracle(fmt, N, K):
+    words, scales, biases, x = make(fmt, N, K, "par")
+    y = q4.q4_gemv_format(FMTS[fmt], to_dev(words), to_dev(scales), to_dev(x), K,
+                          biases=to_dev(biases))
+    torch.cuda.synchronize()
+    rows = np.arange(N) if N <= 4096 else np.unique(np.linspace(0, N - 1, 2048).astype(np.int64))
+    ref, norms = oracle.gemv_format(fmt, words, scales, biases, x, K, rows=rows)
+    if fmt == "q4f32_1":
+        got = y.cpu().numpy().astype(np.float64)[rows]
+        xn = float(np.linalg.norm(x.astype(np.float64)))
+        tol = 1e-5 * xn * norms.max()
+    else:
+        got = half_f64(host_half(y))[rows]
+        xn = oracle.vec_norm(x)
+        tol = 2e-3 * xn * norms.max()
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    assert err.max() <= tol, (err.max(), tol)
+
+
+def test_format_weight_bytes():
+    assert q4.q4_format_weight_bytes(0, 9216, 3072) == 9216 * 96 * 18
+    assert q4.q4_format_weight_bytes(q4.FMT_Q3F16_1, 9216, 3072) == 9216 * 96 * 14
+    assert q4.q4_format_weight_bytes(q4.FMT_Q4F32_1, 9216, 3072) == 9216 * 96 * 20
+    assert q4.q4_format_weight_bytes(q4.FMT_AF4_G64, 9216, 3072) == 9216 * 48 * 36
+    assert q4.q4_format_weight_bytes(q4.FMT_AF4_G64, 10, 96) == 0
