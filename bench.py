@@ -336,6 +336,44 @@ def per_config(torch, q4, synth, np, stream):
             b3, _timed(torch, stream, glue_step(q4.STEP_LAUNCH_EACH), 5) / copies,
             copies=copies)}
     del pairs, glue_layers
+    # the format variants: the qkv-shaped GEMV 3072 -> 9216 in each format, over
+    # distinct copies (> 512 MB) so every call streams from HBM; bytes counted in
+    # each format's own size (words + scales + biases + x + y)
+    fmts = {}
+    N, K = 9216, 3072
+    for name, f in (("q4f16_1", 0), ("q3f16_1", q4.FMT_Q3F16_1), ("q4f32_1", q4.FMT_Q4F32_1),
+                    ("af4g64", q4.FMT_AF4_G64)):
+        wb = q4.q4_format_weight_bytes(f, N, K)
+        copies = max(8, (600 << 20) // wb)
+        es = 4 if f == q4.FMT_Q4F32_1 else 2
+        nwords = N * K // 32 * (3 if f == q4.FMT_Q3F16_1 else 4)
+        per_group = 64 if f == q4.FMT_AF4_G64 else 32
+        mk = []
+        for c in range(copies):
+            lab = f"bench/fmt/{name}/c{c}"
+            W = S.words_torch(lab + "/w", 0, nwords).reshape(N, -1)
+            sc = (torch.rand(N, K // per_group, device="cuda") * 0.01 + 1e-3).to(
+                torch.float32 if es == 4 else torch.float16)
+            bi = ((torch.rand(N, K // per_group, device="cuda") - 0.5) * 0.1).half() \
+                if f == q4.FMT_AF4_G64 else None
+            mk.append((W, sc, bi))
+        xdt = torch.float32 if es == 4 else torch.float16
+        xf = torch.randn(K, device="cuda").to(xdt)
+        yf = torch.empty(N, device="cuda", dtype=xdt)
+        wsf = torch.empty(max(q4.q4_workspace_bytes(1, N, K), 16), dtype=torch.uint8,
+                          device="cuda")
+
+        def fn(i, mk=mk, f=f, xf=xf, yf=yf, wsf=wsf):
+            W, sc, bi = mk[i % len(mk)]
+            if f == 0:
+                q4.q4_gemv(W, sc, xf, yf, ws=wsf, stream=stream)
+            else:
+                q4.q4_gemv_format(f, W, sc, xf, K, biases=bi, y=yf, stream=stream)
+        nb = wb + es * (N + K)
+        fmts[name] = _fig(nb, _timed(torch, stream, fn, 4 * copies), copies=copies,
+                          weight_bytes=wb)
+        del mk
+    out["formats_qkv_3072x9216_m1"] = fmts
     # 2B-class sweep at M = 8 (one q4_gemv_batched kernel per GEMV)
     shapes = synth.sweep_shapes("2b")
     descs = []

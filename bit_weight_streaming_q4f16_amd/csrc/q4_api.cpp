@@ -615,7 +615,7 @@ int q4_gemv_format(uint32_t format, const uint32_t* words, const void* scales,
     return fail(Q4_ERR_SHAPE, "q4_gemv_format: N = %lld, K = %lld", (long long)N, (long long)K);
   const size_t es = f32 ? 4 : 2;
   if (!aligned(words, format == Q4_FMT_Q3F16_1 ? 4 : 16) || !aligned(scales, es) ||
-      (biases && !aligned(biases, 2)) || !aligned(x, es) || !aligned(y, es))
+      (biases && !aligned(biases, 2)) || !aligned(x, 16) || !aligned(y, es))
     return fail(Q4_ERR_ALIGN, "q4_gemv_format: misaligned pointer");
   const int64_t wb = N * (K / 32) * (format == Q4_FMT_Q3F16_1 ? 12 : 16);
   const int64_t groups = N * (K / (affine ? 64 : 32));

@@ -54,42 +54,40 @@ template <> struct Fmt<kQ3> { static constexpr int kGroup = 32, kWords = 3; };
 template <> struct Fmt<kQ4F32> { static constexpr int kGroup = 32, kWords = 4; };
 template <> struct Fmt<kAF4> { static constexpr int kGroup = 64, kWords = 8; };
 
-// sum over one group of q * x with x from LDS (xs: the group's first x)
+// code i (0 .. kGroup-1) of a group's words
 template <int F>
-__device__ __forceinline__ float group_qx(const uint32_t (&w)[Fmt<F>::kWords], const float* xs) {
-  float a = 0.f, b = 0.f;
+__device__ __forceinline__ float code_at(const uint32_t (&w)[Fmt<F>::kWords], int i) {
   if constexpr (F == kQ3) {
     // codes 0..20 lie in bits 0..62 of w0 | w1 << 32, codes 21..31 in bits 31..63
     // of w1 | w2 << 32
-    const uint64_t lo = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
-    const uint64_t hi = (uint64_t)w[1] | ((uint64_t)w[2] << 32);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t q = i <= 20 ? (uint32_t)(lo >> (3 * i)) & 7u
-                                 : (uint32_t)(hi >> (3 * i - 32)) & 7u;
-      if (i & 1)
-        b = __builtin_fmaf((float)q, xs[i], b);
-      else
-        a = __builtin_fmaf((float)q, xs[i], a);
-    }
+    const uint64_t v = i <= 20 ? ((uint64_t)w[0] | ((uint64_t)w[1] << 32))
+                               : ((uint64_t)w[1] | ((uint64_t)w[2] << 32));
+    return (float)((uint32_t)(v >> (i <= 20 ? 3 * i : 3 * i - 32)) & 7u);
   } else {
+    return (float)((w[i / 8] >> (4 * (i % 8))) & 0xFu);
+  }
+}
+
+// sum over group g of q * x; x from LDS planes xs4[j][g] = x[GS*g + 4j .. +3], so
+// the lanes of a team (consecutive g) read consecutive 16-byte entries
+template <int F>
+__device__ __forceinline__ float group_qx(const uint32_t (&w)[Fmt<F>::kWords],
+                                          const float4* xs4, int G, int g) {
+  float a = 0.f, b = 0.f;
 #pragma unroll
-    for (int j = 0; j < Fmt<F>::kWords; ++j) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float q = (float)((w[j] >> (4 * i)) & 0xFu);
-        if (i & 1)
-          b = __builtin_fmaf(q, xs[8 * j + i], b);
-        else
-          a = __builtin_fmaf(q, xs[8 * j + i], a);
-      }
-    }
+  for (int j = 0; j < Fmt<F>::kGroup / 4; ++j) {
+    const float4 xv = xs4[j * G + g];
+    a = __builtin_fmaf(code_at<F>(w, 4 * j), xv.x, a);
+    b = __builtin_fmaf(code_at<F>(w, 4 * j + 1), xv.y, b);
+    a = __builtin_fmaf(code_at<F>(w, 4 * j + 2), xv.z, a);
+    b = __builtin_fmaf(code_at<F>(w, 4 * j + 3), xv.w, b);
   }
   return a + b;
 }
 
 // Grid: workgroups striding over rows; a team of LPR lanes per row; lane i takes
-// groups i, i + LPR, ...  LDS: x as fp32 [K], then the sum of x per group [G].
+// groups i, i + LPR, ...  LDS: x as fp32 planes of float4 [GS/4][G], then the sum
+// of x per group [G].
 template <int F, int LPR>
 __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict__ W,
                                                      const void* __restrict__ Sv,
@@ -97,16 +95,29 @@ __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict_
                                                      const void* __restrict__ Xv,
                                                      void* __restrict__ Yv, int N, int K) {
   constexpr int GS = Fmt<F>::kGroup, NW = Fmt<F>::kWords;
-  extern __shared__ float xs[];
+  extern __shared__ float4 xs4[];
   const int G = K / GS;
-  float* gsum = xs + K;
-  for (int k = threadIdx.x; k < K; k += kBlock)
-    xs[k] = F == kQ4F32 ? static_cast<const float*>(Xv)[k]
-                        : (float)bits<_Float16>(static_cast<const uint16_t*>(Xv)[k]);
+  float* gsum = reinterpret_cast<float*>(xs4 + K / 4);
+  for (int c = threadIdx.x; c < K / 4; c += kBlock) {   // 4 consecutive x per chunk
+    float4 v;
+    if constexpr (F == kQ4F32) {
+      v = static_cast<const float4*>(Xv)[c];
+    } else {
+      const uint2 h = static_cast<const uint2*>(Xv)[c];
+      v = make_float4((float)bits<_Float16>((uint16_t)(h.x & 0xFFFFu)),
+                      (float)bits<_Float16>((uint16_t)(h.x >> 16)),
+                      (float)bits<_Float16>((uint16_t)(h.y & 0xFFFFu)),
+                      (float)bits<_Float16>((uint16_t)(h.y >> 16)));
+    }
+    xs4[(c % (GS / 4)) * G + c / (GS / 4)] = v;
+  }
   __syncthreads();
   for (int g = threadIdx.x; g < G; g += kBlock) {
     float t = 0.f;
-    for (int i = 0; i < GS; ++i) t += xs[g * GS + i];
+    for (int j = 0; j < GS / 4; ++j) {
+      const float4 v = xs4[j * G + g];
+      t += (v.x + v.y) + (v.z + v.w);
+    }
     gsum[g] = t;
   }
   __syncthreads();
@@ -129,7 +140,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict_
           w[j] = v.x; w[j + 1] = v.y; w[j + 2] = v.z; w[j + 3] = v.w;
         }
       }
-      const float qx = group_qx<F>(w, xs + g * GS);
+      const float qx = group_qx<F>(w, xs4, G, g);
       const int64_t gi = (int64_t)n * G + g;
       if constexpr (F == kQ3) {
         const float s = (float)bits<_Float16>(static_cast<const uint16_t*>(Sv)[gi]);

@@ -267,7 +267,8 @@ Q4_API int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_s
 /* q4_gemv_format: y = W x (M = 1) for a format variant, fp32 accumulation, fp16
  * outputs rounded to nearest even (fp32 outputs for Q4_FMT_Q4F32_1).  biases: NULL
  * except for Q4_FMT_AF4_G64.  32 <= K <= 32768, K % 32 == 0 (% 64 for affine);
- * words 16-byte aligned (4-byte for q3f16_1), the rest aligned to their element;
+ * words and x 16-byte aligned (words 4-byte for q3f16_1), the rest aligned to
+ * their element;
  * y must not overlap an input. */
 Q4_API int q4_gemv_format(uint32_t format, const uint32_t* words, const void* scales,
                           const uint16_t* biases, const void* x, void* y, int64_t N, int64_t K,
