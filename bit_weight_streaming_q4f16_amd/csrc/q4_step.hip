@@ -12,7 +12,8 @@
 //
 // One workgroup of 16 waves per compute unit (cooperative launch: all resident):
 //  * 12 compute waves: a workgroup's items -- row-steps of every GEMV, in list
-//    order -- are dealt round-robin to them.  A wave works in bursts of 3 items:
+//    order -- are claimed from an LDS counter, B at a time, by whichever wave
+//    is ready for more.  A wave works in bursts of B = 2 items:
 //    it issues all loads of a burst (per item and lane, 4 x dwordx4 of packed
 //    words and 4 fp16 scales), then consumes them, so the loads of the next
 //    burst overlap this burst's arithmetic on the other waves.  An item is one
@@ -207,6 +208,7 @@ struct Shared {
   int x_ready[kXBufs];   // GEMV index whose x sits in buffer b (-1: none yet)
   int local_done[kXBufs];// compute-wave completions per buffer (monotonic)
   int err;               // a compute wave's wait ran out (copied out by the sync wave)
+  int next_item;         // next unclaimed item of this workgroup's sequence
 };
 
 // First row-step of workgroup wg (the even split of the descriptor's row-steps
@@ -241,7 +243,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     sh.x_ready[threadIdx.x] = -1;
     sh.local_done[threadIdx.x] = 0;
   }
-  if (threadIdx.x == 0) sh.err = 0;
+  if (threadIdx.x == 0) {
+    sh.err = 0;
+    sh.next_item = 0;
+  }
   __syncthreads();
 
   // This workgroup's share: in range mode (a list without dependencies) the
@@ -538,58 +543,65 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   } else {
 
   // -------------------------------------------------------------- compute waves
-  const int c = wave - kSync;
   const Nibbles nb = make_nibbles();
-  // Issue cursor: the next item of this wave.  A workgroup's items of all GEMVs,
-  // in list order, form one sequence dealt round-robin to its compute waves, so
-  // every wave gets the same share of the whole step (to one item) instead of
-  // the first waves taking the remainder of every GEMV.  The cursor keeps the
-  // current GEMV's descriptor in (scalar) registers: the table is read only at
-  // GEMV transitions, never per item.
+  // Issue cursor.  A workgroup's items of all GEMVs, in list order, form one
+  // sequence; a wave takes the next B of them from an LDS counter whenever it
+  // issues a burst, so waves that get their loads back sooner take more items
+  // and all of them run out of work together (a fixed deal leaves the last
+  // waves streaming alone while the others idle).  The counter only grows, so a
+  // wave's items come in sequence order and the cursor only moves forward.  It
+  // keeps the current GEMV's descriptor in (scalar) registers: the table is read
+  // only at GEMV transitions, never per item.
   struct Cursor {
     const Q4_GLOBAL uint4* W;
     const Q4_GLOBAL uint16_t* S;
-    int j, s, s_end;             // GEMV, next row-step, end row-step (this workgroup)
+    int j, s0, cnt, first;       // GEMV, its first row-step here, its item count, and
+                                 // the sequence index of its first item
     int N, G, lg, C, r0;         // its shape, and its first row in this workgroup
     int vo[4];                   // this lane's byte offset of each slot in an item's words
   } cu;
 #pragma unroll
   for (int t = 0; t < 4; ++t) cu.vo[t] = 0;
-  int base = 0;                  // items of GEMVs before cu.j in this workgroup, mod kCompute
-  // enter GEMV j or, if this wave has no item there, the next one that has
-  auto enter = [&](int j) {
-    for (; j <= j1; ++j) {
-      const CursorDesc d = read_desc(D + j);
-      int s0, s1;
-      item_range(d.sbase, d.srem, d.steps, d.flags, s0, s1);
-      int off = c - base;
-      if (off < 0) off += kCompute;
-      base = (base + (s1 - s0)) % kCompute;      // GEMV j's items are dealt either way
-      if (s0 + off < s1) {
-        cu.W = d.W;
-        cu.S = d.S;
-        cu.N = d.N;
-        cu.G = d.G;
-        cu.lg = d.lg;
-        cu.C = d.C;
-        cu.j = j;
-        cu.s = s0 + off;
-        cu.s_end = s1;
-        cu.r0 = s0 * (64 >> d.lg);
-        {
-          const int li = lane & ((1 << d.lg) - 1), g0 = (lane >> d.lg) * d.G + li;
+  auto load = [&](int j) {       // make GEMV j the cursor's
+    const CursorDesc d = read_desc(D + j);
+    int s0, s1;
+    item_range(d.sbase, d.srem, d.steps, d.flags, s0, s1);
+    cu.W = d.W;
+    cu.S = d.S;
+    cu.N = d.N;
+    cu.G = d.G;
+    cu.lg = d.lg;
+    cu.C = d.C;
+    cu.j = j;
+    cu.s0 = s0;
+    cu.cnt = s1 - s0;
+    cu.r0 = s0 * (64 >> d.lg);
+    const int li = lane & ((1 << d.lg) - 1), g0 = (lane >> d.lg) * d.G + li;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const bool in = t < d.C && li + (t << d.lg) < d.G;
-            cu.vo[t] = (in ? g0 + (t << d.lg) : g0) * 16;
-          }
-        }
-        return;
-      }
+    for (int t = 0; t < 4; ++t) {
+      const bool in = t < d.C && li + (t << d.lg) < d.G;
+      cu.vo[t] = (in ? g0 + (t << d.lg) : g0) * 16;
     }
-    cu.j = j1 + 1;
   };
-  enter(j0);
+  cu.j = j0;
+  cu.first = 0;
+  cu.cnt = 0;
+  if (j0 <= j1) load(j0);
+  // move the cursor to the GEMV holding sequence item `it` (past j1: none)
+  auto seek = [&](int it) {
+    while (cu.j <= j1 && it >= cu.first + cu.cnt) {
+      cu.first += cu.cnt;
+      if (++cu.j <= j1) load(cu.j);
+    }
+  };
+  // the first of the next B sequence items (the value is lane 0's: read it with
+  // readfirstlane where it is used, so the LDS round trip overlaps other work)
+  auto take = [&]() {
+    int v = 0;
+    if (lane == 0)
+      v = __hip_atomic_fetch_add(&sh.next_item, B, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return v;
+  };
 
   auto wait_x = [&](int j) {
     for (unsigned it = 0; lds_load(&sh.x_ready[(j - j0) % NX]) != j; ++it) {
@@ -627,14 +639,15 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     uint16_t rs[B][4];
     int rj[B], rrow[B], rN[B], rG[B], rlg[B], rC[B], rr0[B];
   };
-  auto issue = [&](Burst& U) {
+  auto issue = [&](Burst& U, int it0) {
 #pragma unroll
     for (int p = 0; p < B; ++p) {
+      seek(it0 + p);
       const bool live = cu.j <= j1;
       const int lg = live ? cu.lg : 2;
       const int G = live ? cu.G : 1;
       const int C = live ? cu.C : 1;
-      const int row0 = live ? cu.s * (64 >> lg) : 0;
+      const int row0 = live ? (cu.s0 + it0 + p - cu.first) * (64 >> lg) : 0;
       const uint64_t left = live ? (uint64_t)(cu.N - row0) * (uint64_t)G : 0;   // groups
       const uint32_t nw = left * 16 < 0xFFFFFFF0ull ? (uint32_t)(left * 16) : 0xFFFFFFF0u;
       const uint32_t ns = left * 2 < 0xFFFFFFF0ull ? (uint32_t)(left * 2) : 0xFFFFFFF0u;
@@ -663,10 +676,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       U.rlg[p] = lg;
       U.rC[p] = C;
       U.rr0[p] = cu.r0;
-      if (live) {
-        cu.s += kCompute;
-        if (cu.s >= cu.s_end) enter(cu.j + 1);
-      }
     }
   };
   // Consume a burst in item order; false once an item past the end is reached.
@@ -753,9 +762,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   // All loads of a burst are issued before any is consumed, so no loaded value
   // crosses the loop's back edge and every issue is the same eight loads per
   // item: the compiler then waits exactly for the item being consumed.
+  int next = take();
   while (true) {
     Burst U;
-    issue(U);
+    issue(U, __builtin_amdgcn_readfirstlane(next));
+    next = take();
     if (!consume(U)) break;
   }
     signal_upto(j1 + 1);
