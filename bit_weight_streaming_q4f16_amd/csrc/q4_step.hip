@@ -580,7 +580,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const bool in = t < d.C && li + (t << d.lg) < d.G;
-      cu.vo[t] = (in ? g0 + (t << d.lg) : g0) * 16;
+      // a slot past the row's groups (padded rows, or t >= C) takes an offset
+      // of 2 GiB - 16: past the end of the resource (which is capped at 4 GiB -
+      // 16) unless more than 2 GiB of the matrix follow the item, and then still
+      // inside it; it is masked off or never consumed.  Reading zeros instead of
+      // re-reading a real group keeps the slot off the memory system.
+      cu.vo[t] = in ? (g0 + (t << d.lg)) * 16 : 0x7FFFFFF0;
     }
   };
   cu.j = j0;
@@ -629,8 +634,9 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   // the base of a buffer resource (scalar arithmetic) bounded by the end of the
   // matrix, so rows past it read as zero without touching memory; a lane's offset
   // within an item is fixed per GEMV and a slot's offset is a scalar, so issuing
-  // costs no vector arithmetic.  Slots past a lane's groups re-read its first
-  // group; items past the end of the list use an empty resource.
+  // costs no vector arithmetic.  Slots past a lane's groups point past the
+  // buffer (no memory access); items past the end of the list use an empty
+  // resource.
   const Q4_GLOBAL uint4* const W_last = read_desc(D + (n - 1)).W;
   // One burst of B items: the loads of every item (as loaded registers) and what
   // consuming them needs.
@@ -658,11 +664,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           const_cast<uint16_t*>(live ? (const uint16_t*)(cu.S + (int64_t)row0 * G)
                                      : (const uint16_t*)W_last),
           0, (int)ns, 0x00020000);
-      // Per-lane slot offsets are fixed per GEMV (the cursor's): a slot past the
-      // row's groups (padded rows, or t >= C) re-reads the lane's first group,
-      // so a lane of a row in range stays in range.  Only this per-lane part of
-      // a buffer address is range-checked, so the scalar offset stays 0; lanes
-      // past the end of the matrix (or of an empty resource) read zeros.
+      // Per-lane slot offsets are fixed per GEMV (the cursor's).  Only this
+      // per-lane part of a buffer address is range-checked, so the scalar offset
+      // stays 0; lanes past the end of the matrix (or of an empty resource) read
+      // zeros without a memory access.
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, cu.vo[t], 0, kNonTemporal);
