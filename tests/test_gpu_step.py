@@ -104,6 +104,45 @@ def test_independent_lists(mode, shapes):
         assert_gemv_close(host_half(Y), m.words(), m.scales(), x)
 
 
+@pytest.mark.parametrize("shapes", [
+    [(100, 256), (37, 128)], [(64, 512)] * 300, [(65536, 4096), (3, 32)],
+    [(9216, 3072), (3072, 3072), (16384, 3072), (3072, 8192)] * 2 + [(32064, 3072)],
+], ids=["most_wgs_idle", "300_gemvs", "tiny_tail", "two_phi3_blocks_lm_head"])
+def test_range_mode_repeat(shapes):
+    """Lists without dependencies (one stretch of row-steps per workgroup, many
+    workgroups with none, or hundreds of GEMVs): every row computed once and
+    right, the counters left zero (so STEP_WS_CLEAN calls work), and repeated
+    calls bitwise equal."""
+    descs, mats, xs = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        m, W, S = mat(f"pool/{i}/{N}x{K}", N, K)
+        x = synth.activations(f"pool/x/{i % 7}/{K}", 0, K)
+        descs.append((W, S, dev_half(x), torch.full((N,), float("nan"), dtype=torch.float16,
+                                                    device="cuda")))
+        mats.append(m)
+        xs.append(x)
+    layers = q4.make_layers(descs)
+    n = len(descs)
+    flags = q4.STEP_PERSISTENT
+    need = q4.q4_decode_step_workspace_bytes(layers, 1, flags)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")   # garbage
+    q4.q4_decode_step(layers, 1, flags, ws=ws)
+    torch.cuda.synchronize()
+    ref = [host_half(d[3]) for d in descs]
+    for m, x, y in zip(mats, xs, ref):
+        assert_gemv_close(y, m.words(), m.scales(), x)
+    # counters 0..n-1, the exit counter and the spare after it
+    assert not ws[: 4 * (n + 2)].view(torch.int32).cpu().numpy().any()
+    for _ in range(3):
+        for d in descs:
+            d[3].fill_(float("nan"))
+        q4.q4_decode_step(layers, 1, flags | q4.STEP_WS_CLEAN, ws=ws)
+        torch.cuda.synchronize()
+        for r, d in zip(ref, descs):
+            assert np.array_equal(r, host_half(d[3]))
+        assert not ws[: 4 * (n + 2)].view(torch.int32).cpu().numpy().any()
+
+
 def test_fallback_for_long_rows_and_repeat_determinism():
     m1, W1, S1 = mat("fb/1", 300, 16384)     # K > 8192: one kernel per descriptor
     m2, W2, S2 = mat("fb/2", 700, 3072)
