@@ -545,11 +545,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   // -------------------------------------------------------------- compute waves
   const Nibbles nb = make_nibbles();
   // Issue cursor.  A workgroup's items of all GEMVs, in list order, form one
-  // sequence; a wave takes the next B of them from an LDS counter whenever it
-  // issues a burst, so waves that get their loads back sooner take more items
-  // and all of them run out of work together (a fixed deal leaves the last
-  // waves streaming alone while the others idle).  The counter only grows, so a
-  // wave's items come in sequence order and the cursor only moves forward.  It
+  // sequence.  In range mode a wave takes the next B of them from an LDS counter
+  // whenever it issues a burst, so waves that get their loads back sooner take
+  // more items and all of them run out of work together (a fixed deal leaves
+  // the last waves streaming alone while the others idle).  Either way a wave's
+  // items come in sequence order and the cursor only moves forward.  It
   // keeps the current GEMV's descriptor in (scalar) registers: the table is read
   // only at GEMV transitions, never per item.
   struct Cursor {
@@ -599,12 +599,26 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       if (++cu.j <= j1) load(cu.j);
     }
   };
-  // the first of the next B sequence items (the value is lane 0's: read it with
-  // readfirstlane where it is used, so the LDS round trip overlaps other work)
+  // The first of the next B sequence items of this wave, which are `stride`
+  // apart.  Range mode: the next B items of the sequence, from the LDS counter
+  // (the value is lane 0's: read it with readfirstlane where it is used, so the
+  // LDS round trip overlaps other work).  Spread mode: a fixed round-robin deal
+  // (wave c takes items c, c + 12, ...).  There a workgroup's share of a GEMV is
+  // a few items that often wait for the GEMV's input, and the deal spreads them
+  // over as many waves as possible, where claiming in twos would let one wave
+  // take two of them in a row -- in a chain of dependent GEMVs every GEMV waits
+  // for its slowest wave.
+  const bool claim = ranges != nullptr;
+  const int stride = claim ? 1 : kCompute;
+  int dealt = wave - kSync;
   auto take = [&]() {
-    int v = 0;
-    if (lane == 0)
-      v = __hip_atomic_fetch_add(&sh.next_item, B, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    int v = dealt;
+    if (claim) {
+      if (lane == 0)
+        v = __hip_atomic_fetch_add(&sh.next_item, B, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      dealt += B * kCompute;
+    }
     return v;
   };
 
@@ -645,15 +659,15 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     uint16_t rs[B][4];
     int rj[B], rrow[B], rN[B], rG[B], rlg[B], rC[B], rr0[B];
   };
-  auto issue = [&](Burst& U, int it0) {
+  auto issue = [&](Burst& U, int it0) {   // items it0 + p * stride
 #pragma unroll
     for (int p = 0; p < B; ++p) {
-      seek(it0 + p);
+      seek(it0 + p * stride);
       const bool live = cu.j <= j1;
       const int lg = live ? cu.lg : 2;
       const int G = live ? cu.G : 1;
       const int C = live ? cu.C : 1;
-      const int row0 = live ? (cu.s0 + it0 + p - cu.first) * (64 >> lg) : 0;
+      const int row0 = live ? (cu.s0 + it0 + p * stride - cu.first) * (64 >> lg) : 0;
       const uint64_t left = live ? (uint64_t)(cu.N - row0) * (uint64_t)G : 0;   // groups
       const uint32_t nw = left * 16 < 0xFFFFFFF0ull ? (uint32_t)(left * 16) : 0xFFFFFFF0u;
       const uint32_t ns = left * 2 < 0xFFFFFFF0ull ? (uint32_t)(left * 2) : 0xFFFFFFF0u;
