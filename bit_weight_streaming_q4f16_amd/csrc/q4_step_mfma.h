@@ -30,6 +30,7 @@ struct MStepPlan {
   bool cross_wg = false;     // some descriptor waits for another on every workgroup
   int grid = 0, M = 0, counters = 0;
   size_t lds_bytes = 0;
+  int stage_off = 0;         // LDS offset of the compute waves' load stages
   std::vector<MStepDesc> desc;
   // range mode (no dependencies): per workgroup {first tile, end tile, first GEMV,
   // last GEMV} of the tiles of all GEMVs laid end to end; empty otherwise

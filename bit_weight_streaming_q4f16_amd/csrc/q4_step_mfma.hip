@@ -14,14 +14,16 @@
 //
 // One workgroup of 16 waves per compute unit:
 //  * 12 compute waves take this workgroup's 16-row tiles of every GEMV in list
-//    order, dealt round-robin.  A tile streams in bursts of kChunks chunks of four
-//    groups: per lane one dwordx4 (group c of row r, for lane = 16c + r) and one
-//    8-byte load of the row's four scales; a 4 x 4 exchange between lanes r,
-//    r + 16, r + 32, r + 48 leaves word c of each of the four groups in lane
-//    (c, r), which is the B layout.  Where G is a multiple of 8 (and the scales
-//    16-byte aligned) the same sixteen groups come as pairs of adjacent groups per
-//    lane, so each row is read in 128-byte runs.  X and the bias terms come from LDS; results
-//    go to LDS.
+//    order, dealt round-robin.  Where G is a multiple of 8 (and the scales
+//    16-byte aligned) a tile streams in bursts of eight groups: two loads of 8
+//    rows x 128 contiguous bytes each, written to the wave's LDS stage as word
+//    planes and read back as word c of eight groups of row r in lane (c, r), the
+//    B layout; the next burst is issued as soon as the current one is in LDS.
+//    Otherwise in bursts of kChunks chunks of four groups: per lane one dwordx4
+//    (group c of row r, for lane = 16c + r) and one 8-byte load of the row's four
+//    scales, and a 4 x 4 exchange between lanes r, r + 16, r + 32, r + 48 leaves
+//    word c of each of the four groups in lane (c, r).  X and the bias terms come
+//    from LDS; results go to LDS.
 //  * 4 sync waves, each owning every 4th GEMV: stage its X (pair-ordered, with the
 //    bias terms) into the GEMV's LDS region once the GEMVs it depends on are
 //    complete on every workgroup and the region's previous user is finished,
@@ -54,6 +56,7 @@ constexpr int kSync = 4;
 constexpr int kCompute = kWaves - kSync;
 constexpr int kSlots = 8;                   // x_ready slots: GEMVs up to 8 apart in flight
 constexpr int kChunks = 4;                  // chunks (of four groups) per burst
+constexpr int kStage = 2048;                // per compute wave: one staged burst (16 rows x 8 groups)
 constexpr unsigned kSpinLimit = 1u << 24;
 constexpr int kCoherent = 1 | 16;           // sc0 | sc1
 constexpr int kNonTemporal = 2;
@@ -133,16 +136,19 @@ __device__ __forceinline__ TileDesc read_desc(const MStepDesc* d) {
   return r;
 }
 
-// LDS region of a GEMV (byte offsets from xoff): X planes [G][4][M] uint4, then the
-// bias terms [G][8] float, then y [M][rows] fp16 (rows: this workgroup's rows of the
-// GEMV; the host sizes the region for the most any workgroup has).
-__device__ __forceinline__ int corr_off(int M, int G) { return M * G * 64; }
-__device__ __forceinline__ int ybuf_off(int M, int G) { return M * G * 64 + G * 32; }
+// LDS region of a GEMV (byte offsets from xoff): X planes [G][4][8] uint4 (rows m <
+// M used; the fixed stride lets the reads of a burst use immediate offsets from one
+// address), then the bias terms [G][8] float, then y [M][rows] fp16 (rows: this
+// workgroup's rows of the GEMV; the host sizes the region for the most any
+// workgroup has).
+__device__ __forceinline__ int corr_off(int, int G) { return 8 * G * 64; }
+__device__ __forceinline__ int ybuf_off(int, int G) { return 8 * G * 64 + G * 32; }
 
 __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __restrict__ D, int n,
                                                             int M, unsigned* __restrict__ done,
                                                             unsigned* __restrict__ err,
-                                                            const int4* __restrict__ ranges) {
+                                                            const int4* __restrict__ ranges,
+                                                            int stage_off) {
   extern __shared__ uint4 smem[];
   __shared__ Shared sh;
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
           }
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            xs[(g * 4 + c) * M + m] = pair_order(v[c]);
+            xs[(g * 4 + c) * 8 + m] = pair_order(v[c]);
             const uint32_t wv[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
@@ -374,6 +380,39 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       }
     };
 
+    // G % 8 == 0 and 16-byte aligned scales, and the stages were planned: the
+    // staged path below
+    auto staged = [&](const TileDesc& t) {
+      return stage_off >= 0 && t.G % 8 == 0 && (reinterpret_cast<uintptr_t>(t.S) & 15u) == 0;
+    };
+    // a staged burst in flight: the raw words of 16 rows x 8 groups, and lane
+    // (c, r)'s row r scales of those groups
+    struct Pre {
+      bool live;
+      uint4 w0, w1;
+      u32x4_g s;
+    } pre;
+    pre.live = false;
+    auto issue_st = [&](Pre& P, const TileDesc& t, int tl, int b) {
+      const int tr = tl * 16;
+      const uint64_t left = (uint64_t)(t.N - tr) * (uint64_t)t.G;
+      const uint32_t nw = left * 16 < 0xFFFFFFF0ull ? (uint32_t)(left * 16) : 0xFFFFFFF0u;
+      const uint32_t ns = left * 2 < 0xFFFFFFF0ull ? (uint32_t)(left * 2) : 0xFFFFFFF0u;
+      const __amdgpu_buffer_rsrc_t bw = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint4*>((const uint4*)(t.W + (int64_t)tr * t.G)), 0, (int)nw, kRsrcFlags);
+      const __amdgpu_buffer_rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>((const uint16_t*)(t.S + (int64_t)tr * t.G)), 0, (int)ns,
+          kRsrcFlags);
+      // rows past the matrix end read zero (only the per-lane offset is range-checked)
+      const int vo = ((lane >> 3) * t.G + (lane & 7)) * 16;
+      const int so = __builtin_amdgcn_readfirstlane(b * 128);
+      const u32x4_g a0 = __builtin_amdgcn_raw_buffer_load_b128(bw, vo, so, kNonTemporal);
+      const u32x4_g a1 = __builtin_amdgcn_raw_buffer_load_b128(bw, vo + 128 * t.G, so, kNonTemporal);
+      P.w0 = make_uint4(a0[0], a0[1], a0[2], a0[3]);
+      P.w1 = make_uint4(a1[0], a1[1], a1[2], a1[3]);
+      P.s = __builtin_amdgcn_raw_buffer_load_b128(bs, r * t.G * 2, __builtin_amdgcn_readfirstlane(b * 16), 0);
+      P.live = true;
+    };
     while (cu.j <= j1) {
       const TileDesc d = cu.d;
       const int j = cu.j, G = d.G, tile = cu.t;
@@ -390,8 +429,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       // and a row past the end is past the end at every chunk
       const int vo_w = (r * G + c) * 16, vo_s = r * G * 2;
       const int nch = G / 4;
-      // 16-byte scale loads need G % 8 == 0 and 16-byte aligned scales
-      const bool wide = G % 8 == 0 && (reinterpret_cast<uintptr_t>(d.S) & 15u) == 0;
+      const bool wide = staged(d);
       const int xo = d.xoff, co = d.xoff + corr_off(M, G);
       const int rows = cu.rows;
       const int wrow0 = cu.row0;
@@ -400,58 +438,88 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       if (cu.t >= cu.t_end) enter(cu.j + 1);
 
       f4_t acc = {0.f, 0.f, 0.f, 0.f};
+      // Lane (c, r) supplies row r of A (X) and receives rows 4c..4c+3 of D (with
+      // the bias terms of those rows as its accumulator input).  Rows of X past M
+      // and the lanes with c >= 2 only feed rows of D that are never stored, so
+      // they read row M - 1 and the biases of rows 0..7 instead of zeros: every
+      // lane reads valid LDS without a branch.  Per group the addresses advance
+      // by a fixed stride from a per-lane base.
+      const uint8_t* a_base = lds + xo + (c * 8 + (r < M ? r : M - 1)) * 16;
+      const uint8_t* c_base = lds + co + (c & 1) * 16;
+      constexpr int a_step = 512;                     // X planes: bytes per group
+      auto x_of = [&](int g) { return *reinterpret_cast<const uint4*>(a_base + g * a_step); };
+      auto bias_of = [&](int g) { return *reinterpret_cast<const f4_t*>(c_base + g * 32); };
       // one group of the tile: B from word c of the group in lane (c, r), A = X rows
-      auto group_mma = [&](uint32_t vt, int g, uint32_t sbits) {
+      auto group_mma = [&](uint32_t vt, uint4 a, f4_t cin) {
         const uint32_t x8 = vt >> 8;
         const uint4 bq = make_uint4((vt & m_lo) | e_lo, (vt & m_hi) | e_hi,
                                     (x8 & m_lo) | e_lo, (x8 & m_hi) | e_hi);
-        uint4 a = make_uint4(0u, 0u, 0u, 0u);
-        if (r < M) a = *reinterpret_cast<const uint4*>(lds + xo + ((g * 4 + c) * M + r) * 16);
-        f4_t cin = {0.f, 0.f, 0.f, 0.f};
-        if (c < 2) cin = *reinterpret_cast<const f4_t*>(lds + co + g * 32 + c * 16);
-        const f4_t dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(bits<h8_t>(a), bits<h8_t>(bq),
-                                                              cin, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(bits<h8_t>(a), bits<h8_t>(bq), cin, 0, 0, 0);
+      };
+      // the group's scale, applied exactly in fp32
+      auto scale_add = [&](f4_t dd, uint32_t sbits) {
         const float sv = (float)bits<_Float16>((uint16_t)sbits);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sv, dd[e], acc[e]);
       };
       if (wide) {
-        // chunks of eight groups: the four lanes of a row read two adjacent groups
-        // each (128 contiguous bytes of the row per pair of loads) and one 16-byte
-        // load of the row's eight scales; groups are still taken in order
-        const int nch8 = G / 8, vo8 = (r * G + 2 * c) * 16;
-        for (int ch0 = 0; ch0 < nch8; ch0 += kChunks / 2) {
-          uint4 w0[kChunks / 2], w1[kChunks / 2];
-          u32x4_g s8[kChunks / 2];
-#pragma unroll
-          for (int q = 0; q < kChunks / 2; ++q) {
-            const int ch = ch0 + q < nch8 ? ch0 + q : nch8 - 1;   // past the row: re-read
-            const int so = __builtin_amdgcn_readfirstlane(ch);
-            const u32x4_g v0 = __builtin_amdgcn_raw_buffer_load_b128(bw, vo8, so * 128, kNonTemporal);
-            const u32x4_g v1 = __builtin_amdgcn_raw_buffer_load_b128(bw, vo8 + 16, so * 128,
-                                                                    kNonTemporal);
-            w0[q] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
-            w1[q] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
-            s8[q] = __builtin_amdgcn_raw_buffer_load_b128(bs, vo_s, so * 16, 0);
+        // Bursts of eight groups of the tile's 16 rows, loaded as two instructions
+        // of 8 rows x 128 contiguous bytes (lane l: row 8h + l / 8, group l % 8), so
+        // each instruction touches 8 whole cache lines -- not 16 half lines, which
+        // streams at two thirds of the rate.  The raw burst goes through this
+        // wave's LDS stage as word planes [word][16 rows][8 groups] of dwords, so
+        // lane (c, r) reads word c of the eight groups of row r as 32 contiguous
+        // bytes: B's layout, with no exchange between lanes.  Once the raw
+        // registers are in LDS, the next burst (of this tile, or the first of the
+        // next one) is issued, so loads stay in flight while a burst is computed.
+        const int nb = G / 8;
+        if (!pre.live) issue_st(pre, d, tile, 0);
+        uint32_t* const st = reinterpret_cast<uint32_t*>(lds + stage_off + cw * kStage);
+        for (int b = 0; b < nb; ++b) {
+          const uint4 raw0 = pre.w0, raw1 = pre.w1;
+          const u32x4_g sc = pre.s;
+          st[0 * 128 + lane] = raw0.x;          // plane w: [row][group] dwords
+          st[1 * 128 + lane] = raw0.y;
+          st[2 * 128 + lane] = raw0.z;
+          st[3 * 128 + lane] = raw0.w;
+          st[0 * 128 + 64 + lane] = raw1.x;     // rows 8..15
+          st[1 * 128 + 64 + lane] = raw1.y;
+          st[2 * 128 + 64 + lane] = raw1.z;
+          st[3 * 128 + 64 + lane] = raw1.w;
+          if (b + 1 < nb) {
+            issue_st(pre, d, tile, b + 1);
+          } else if (cu.j <= j1 && staged(cu.d)) {
+            issue_st(pre, cu.d, cu.t, 0);
+          } else {
+            pre.live = false;
           }
-          if (ch0 == 0) {
+          if (b == 0) {
             signal_upto(j);
             wait_x(j);
           }
+          const int g0 = b * 8;
+          const uint4* const sr = reinterpret_cast<const uint4*>(st + c * 128 + r * 8);
+          // X and bias of the burst's groups: one address each, immediate offsets
+          const uint8_t* const ab = a_base + g0 * a_step;
+          const uint8_t* const cbp = c_base + g0 * 32;
 #pragma unroll
-          for (int q = 0; q < kChunks / 2; ++q) {
-            if (ch0 + q < nch8) {
-              const int g0 = (ch0 + q) * 8;
-              uint32_t va[4] = {w0[q].x, w0[q].y, w0[q].z, w0[q].w};
-              uint32_t vb[4] = {w1[q].x, w1[q].y, w1[q].z, w1[q].w};
-              transpose4(va);                   // va[t]: word c of group g0 + 2t, row r
-              transpose4(vb);                   // vb[t]: word c of group g0 + 2t + 1
+          for (int h = 0; h < 2; ++h) {
+            const uint4 wq = sr[h];
+            const uint32_t v[4] = {wq.x, wq.y, wq.z, wq.w};   // word c of group g0 + 4h + t, row r
+            uint4 xa[4];
+            f4_t cb[4];
 #pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const uint32_t sw = s8[q][t];   // scales of groups g0 + 2t and g0 + 2t + 1
-                group_mma(va[t], g0 + 2 * t, sw & 0xFFFFu);
-                group_mma(vb[t], g0 + 2 * t + 1, sw >> 16);
-              }
+            for (int t = 0; t < 4; ++t) {
+              xa[t] = *reinterpret_cast<const uint4*>(ab + (4 * h + t) * a_step);
+              cb[t] = *reinterpret_cast<const f4_t*>(cbp + (4 * h + t) * 32);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; t += 2) {
+              const uint32_t sw = sc[2 * h + t / 2];   // scales of groups g0 + 4h + t, + t + 1
+              const f4_t d0 = group_mma(v[t], xa[t], cb[t]);
+              const f4_t d1 = group_mma(v[t + 1], xa[t + 1], cb[t + 1]);
+              scale_add(d0, sw & 0xFFFFu);
+              scale_add(d1, sw >> 16);
             }
           }
         }
@@ -475,12 +543,24 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
           for (int q = 0; q < kChunks; ++q) {
             if (ch0 + q < nch) {
               const int g0 = (ch0 + q) * 4;
+              uint4 xa[4];
+              f4_t cb[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                xa[t] = x_of(g0 + t);
+                cb[t] = bias_of(g0 + t);
+              }
               uint32_t v[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
               transpose4(v);                    // v[t]: word c of group g0 + t, row r
               const uint32_t sc[4] = {s[q][0] & 0xFFFFu, s[q][0] >> 16, s[q][1] & 0xFFFFu,
                                       s[q][1] >> 16};
 #pragma unroll
-              for (int t = 0; t < 4; ++t) group_mma(v[t], g0 + t, sc[t]);
+              for (int t = 0; t < 4; t += 2) {
+                const f4_t d0 = group_mma(v[t], xa[t], cb[t]);
+                const f4_t d1 = group_mma(v[t + 1], xa[t + 1], cb[t + 1]);
+                scale_add(d0, sc[t]);
+                scale_add(d1, sc[t + 1]);
+              }
             }
           }
         }
@@ -575,16 +655,21 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
       if (i != h) return p;                     // not covered: one kernel per GEMV
     }
   }
-  const size_t cap = (size_t)dev.lds_per_block - 1024;   // static LDS and margin
+  // static LDS and margin, then the compute waves' stages at the end; the X
+  // regions share the rest.  A list whose regions do not fit beside the stages
+  // goes without them (stage_off < 0: every GEMV takes the unstaged path).
+  const size_t total_lds = (size_t)dev.lds_per_block - 1024;
+  size_t cap = total_lds - (size_t)kCompute * kStage;
+  p.stage_off = (int)cap;
   // the most rows any workgroup holds of each GEMV, per mode
   std::vector<int64_t> rows((size_t)n);
   // LDS regions as a ring in list order; rel: the latest earlier user of the space
-  auto place = [&]() {
+  auto place_in = [&]() {
     std::vector<size_t> off((size_t)n), size((size_t)n);
     size_t cur = 0;
     for (int64_t k = 0; k < n; ++k) {
       MStepDesc& s = p.desc[(size_t)k];
-      const size_t sz = (size_t)M * s.G * 64 + (size_t)s.G * 32 +
+      const size_t sz = (size_t)8 * s.G * 64 + (size_t)s.G * 32 +
                         (((size_t)rows[(size_t)k] * M * 2 + 15) & ~(size_t)15);
       if (sz > cap) return false;
       if (cur + sz > cap) cur = 0;
@@ -601,6 +686,14 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
       }
     }
     return true;
+  };
+  // without the stages if the regions do not fit beside them
+  auto place = [&]() {
+    if (place_in()) return true;
+    if (p.stage_off < 0) return false;
+    p.stage_off = -1;
+    cap = total_lds;
+    return place_in();
   };
   // Range mode (no dependencies): each workgroup takes one contiguous stretch of
   // the 16-row tiles of all GEMVs laid end to end, balanced by weight bytes.
@@ -650,7 +743,7 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
         p.desc[(size_t)k].trem = -1;
       }
       p.ranges = std::move(ranges);
-      p.lds_bytes = cap;
+      p.lds_bytes = total_lds;
       p.counters = (int)n + 4;
       p.ok = true;
       return p;
@@ -663,7 +756,7 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
     rows[(size_t)k] = (int64_t)(s.tbase + (s.trem > 0)) * 16;
   }
   if (!place()) return p;
-  p.lds_bytes = cap;
+  p.lds_bytes = total_lds;
   p.counters = (int)n + 4;
   p.ok = true;
   return p;
@@ -692,14 +785,15 @@ hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc,
     return e;
   int n = (int)p.desc.size(), M = p.M;
   const int4* rg = p.ranges.empty() ? nullptr : dev_ranges;
+  int so = p.stage_off;
   if (p.cross_wg) {
     void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&M, (void*)&done, (void*)&err,
-                    (void*)&rg};
+                    (void*)&rg, (void*)&so};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_step_mfma), dim3(p.grid),
                                       dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
   }
   hipLaunchKernelGGL(k_step_mfma, dim3(p.grid), dim3(kStepThreads), p.lds_bytes, s, dev_desc, n,
-                     M, done, err, rg);
+                     M, done, err, rg, so);
   return hipGetLastError();
 }
 
