@@ -15,10 +15,11 @@
 // One workgroup of 16 waves per compute unit:
 //  * 12 compute waves take this workgroup's 16-row tiles of every GEMV in list
 //    order, dealt round-robin.  Where G is a multiple of 8 (and the scales
-//    16-byte aligned) a tile streams in bursts of eight groups: two loads of 8
-//    rows x 128 contiguous bytes each, written to the wave's LDS stage as word
-//    planes and read back as word c of eight groups of row r in lane (c, r), the
-//    B layout; the next burst is issued as soon as the current one is in LDS.
+//    16-byte aligned) a tile streams in bursts of sixteen groups: the rows'
+//    scales first, then four loads of 8 rows x 128 contiguous bytes, written
+//    (eight groups at a time) to the wave's LDS stage as word planes and read
+//    back as word c of eight groups of row r in lane (c, r), the B layout; the
+//    next burst is issued as soon as the current one is in LDS.
 //    Otherwise in bursts of kChunks chunks of four groups: per lane one dwordx4
 //    (group c of row r, for lane = 16c + r) and one 8-byte load of the row's four
 //    scales, and a 4 x 4 exchange between lanes r, r + 16, r + 32, r + 48 leaves
@@ -385,12 +386,14 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
     auto staged = [&](const TileDesc& t) {
       return stage_off >= 0 && t.G % 8 == 0 && (reinterpret_cast<uintptr_t>(t.S) & 15u) == 0;
     };
-    // a staged burst in flight: the raw words of 16 rows x 8 groups, and lane
-    // (c, r)'s row r scales of those groups
+    // A staged burst in flight: sixteen groups of the tile's 16 rows as four raw
+    // loads of 8 rows x 128 contiguous bytes (w[2e + h]: groups 8e .. 8e + 7 of
+    // the burst, rows 8h .. 8h + 7; lane l holds row 8h + l / 8, group l % 8), and
+    // lane (c, r)'s row r scales of the two halves (s[e]).
     struct Pre {
       bool live;
-      uint4 w0, w1;
-      u32x4_g s;
+      uint4 w[4];
+      u32x4_g s[2];
     } pre;
     pre.live = false;
     auto issue_st = [&](Pre& P, const TileDesc& t, int tl, int b) {
@@ -403,14 +406,28 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       const __amdgpu_buffer_rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>((const uint16_t*)(t.S + (int64_t)tr * t.G)), 0, (int)ns,
           kRsrcFlags);
-      // rows past the matrix end read zero (only the per-lane offset is range-checked)
+      // Only the per-lane offset is range-checked: rows past the matrix read zero
+      // at every offset within the row, and a half past the row (G % 16 == 8, the
+      // last burst) points past the resource (2 GiB - 16: out of range unless more
+      // than 2 GiB follow, and then inside the matrix; never used).
+      const bool two = 16 * b + 8 < t.G;
+      // the scales first: they arrive last otherwise, and every burst waits for them
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int vs = e == 0 || two ? (r * t.G + 16 * b + 8 * e) * 2 : 0x7FFFFFF0;
+        P.s[e] = __builtin_amdgcn_raw_buffer_load_b128(bs, vs, 0, 0);
+      }
       const int vo = ((lane >> 3) * t.G + (lane & 7)) * 16;
-      const int so = __builtin_amdgcn_readfirstlane(b * 128);
-      const u32x4_g a0 = __builtin_amdgcn_raw_buffer_load_b128(bw, vo, so, kNonTemporal);
-      const u32x4_g a1 = __builtin_amdgcn_raw_buffer_load_b128(bw, vo + 128 * t.G, so, kNonTemporal);
-      P.w0 = make_uint4(a0[0], a0[1], a0[2], a0[3]);
-      P.w1 = make_uint4(a1[0], a1[1], a1[2], a1[3]);
-      P.s = __builtin_amdgcn_raw_buffer_load_b128(bs, r * t.G * 2, __builtin_amdgcn_readfirstlane(b * 16), 0);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int so = __builtin_amdgcn_readfirstlane((16 * b + 8 * e) * 16);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int v = e == 0 || two ? vo + h * 128 * t.G : 0x7FFFFFF0;
+          const u32x4_g a = __builtin_amdgcn_raw_buffer_load_b128(bw, v, so, kNonTemporal);
+          P.w[2 * e + h] = make_uint4(a[0], a[1], a[2], a[3]);
+        }
+      }
       P.live = true;
     };
     while (cu.j <= j1) {
@@ -463,29 +480,41 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sv, dd[e], acc[e]);
       };
       if (wide) {
-        // Bursts of eight groups of the tile's 16 rows, loaded as two instructions
-        // of 8 rows x 128 contiguous bytes (lane l: row 8h + l / 8, group l % 8), so
-        // each instruction touches 8 whole cache lines -- not 16 half lines, which
-        // streams at two thirds of the rate.  The raw burst goes through this
+        // Bursts of sixteen groups of the tile's 16 rows, loaded as instructions of
+        // 8 rows x 128 contiguous bytes (lane l: row 8h + l / 8, group l % 8), so
+        // each touches 8 whole cache lines -- not 16 half lines, which streams at
+        // two thirds of the rate.  Each half (eight groups) goes through this
         // wave's LDS stage as word planes [word][16 rows][8 groups] of dwords, so
         // lane (c, r) reads word c of the eight groups of row r as 32 contiguous
         // bytes: B's layout, with no exchange between lanes.  Once the raw
         // registers are in LDS, the next burst (of this tile, or the first of the
         // next one) is issued, so loads stay in flight while a burst is computed.
-        const int nb = G / 8;
+        const int nb = (G + 15) / 16;
         if (!pre.live) issue_st(pre, d, tile, 0);
         uint32_t* const st = reinterpret_cast<uint32_t*>(lds + stage_off + cw * kStage);
+        const uint4* const sr = reinterpret_cast<const uint4*>(st + c * 128 + r * 8);
         for (int b = 0; b < nb; ++b) {
-          const uint4 raw0 = pre.w0, raw1 = pre.w1;
-          const u32x4_g sc = pre.s;
-          st[0 * 128 + lane] = raw0.x;          // plane w: [row][group] dwords
-          st[1 * 128 + lane] = raw0.y;
-          st[2 * 128 + lane] = raw0.z;
-          st[3 * 128 + lane] = raw0.w;
-          st[0 * 128 + 64 + lane] = raw1.x;     // rows 8..15
-          st[1 * 128 + 64 + lane] = raw1.y;
-          st[2 * 128 + 64 + lane] = raw1.z;
-          st[3 * 128 + 64 + lane] = raw1.w;
+          const bool two = 16 * b + 8 < G;
+          const u32x4_g sc0 = pre.s[0], sc1 = pre.s[1];
+          uint4 wq[2][2];                       // [half][groups 0-3, 4-7]: word c, row r
+          auto stage_half = [&](const uint4& lo, const uint4& hi) {
+            st[0 * 128 + lane] = lo.x;          // plane w: [row][group] dwords
+            st[1 * 128 + lane] = lo.y;
+            st[2 * 128 + lane] = lo.z;
+            st[3 * 128 + lane] = lo.w;
+            st[0 * 128 + 64 + lane] = hi.x;     // rows 8..15
+            st[1 * 128 + 64 + lane] = hi.y;
+            st[2 * 128 + 64 + lane] = hi.z;
+            st[3 * 128 + 64 + lane] = hi.w;
+          };
+          stage_half(pre.w[0], pre.w[1]);
+          wq[0][0] = sr[0];
+          wq[0][1] = sr[1];
+          if (two) {                            // the stage is reused in order
+            stage_half(pre.w[2], pre.w[3]);
+            wq[1][0] = sr[0];
+            wq[1][1] = sr[1];
+          }
           if (b + 1 < nb) {
             issue_st(pre, d, tile, b + 1);
           } else if (cu.j <= j1 && staged(cu.d)) {
@@ -497,29 +526,33 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
             signal_upto(j);
             wait_x(j);
           }
-          const int g0 = b * 8;
-          const uint4* const sr = reinterpret_cast<const uint4*>(st + c * 128 + r * 8);
-          // X and bias of the burst's groups: one address each, immediate offsets
-          const uint8_t* const ab = a_base + g0 * a_step;
-          const uint8_t* const cbp = c_base + g0 * 32;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint4 wq = sr[h];
-            const uint32_t v[4] = {wq.x, wq.y, wq.z, wq.w};   // word c of group g0 + 4h + t, row r
-            uint4 xa[4];
-            f4_t cb[4];
+          for (int e = 0; e < 2; ++e) {
+            if (e == 1 && !two) break;
+            const int g0 = 16 * b + 8 * e;
+            const u32x4_g sc = e == 0 ? sc0 : sc1;
+            // X and bias of the half's groups: one address each, immediate offsets
+            const uint8_t* const ab = a_base + g0 * a_step;
+            const uint8_t* const cbp = c_base + g0 * 32;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              xa[t] = *reinterpret_cast<const uint4*>(ab + (4 * h + t) * a_step);
-              cb[t] = *reinterpret_cast<const f4_t*>(cbp + (4 * h + t) * 32);
-            }
+            for (int h = 0; h < 2; ++h) {
+              const uint4 w4 = wq[e][h];
+              const uint32_t v[4] = {w4.x, w4.y, w4.z, w4.w};   // word c of group g0 + 4h + t
+              uint4 xa[4];
+              f4_t cb[4];
 #pragma unroll
-            for (int t = 0; t < 4; t += 2) {
-              const uint32_t sw = sc[2 * h + t / 2];   // scales of groups g0 + 4h + t, + t + 1
-              const f4_t d0 = group_mma(v[t], xa[t], cb[t]);
-              const f4_t d1 = group_mma(v[t + 1], xa[t + 1], cb[t + 1]);
-              scale_add(d0, sw & 0xFFFFu);
-              scale_add(d1, sw >> 16);
+              for (int t = 0; t < 4; ++t) {
+                xa[t] = *reinterpret_cast<const uint4*>(ab + (4 * h + t) * a_step);
+                cb[t] = *reinterpret_cast<const f4_t*>(cbp + (4 * h + t) * 32);
+              }
+#pragma unroll
+              for (int t = 0; t < 4; t += 2) {
+                const uint32_t sw = sc[2 * h + t / 2];   // scales of groups g0 + 4h + t, + t + 1
+                const f4_t d0 = group_mma(v[t], xa[t], cb[t]);
+                const f4_t d1 = group_mma(v[t + 1], xa[t + 1], cb[t + 1]);
+                scale_add(d0, sw & 0xFFFFu);
+                scale_add(d1, sw >> 16);
+              }
             }
           }
         }

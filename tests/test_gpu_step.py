@@ -258,6 +258,29 @@ def test_small_m_dependent_chain(M, flags):
         assert_gemv_close(y, m.words(), m.scales(), host_half(X))
 
 
+@pytest.mark.parametrize("M", [2, 5, 8])
+@pytest.mark.parametrize("flags", [q4.STEP_PERSISTENT, q4.STEP_ORDERED | q4.STEP_PERSISTENT],
+                         ids=["hazards", "ordered"])
+def test_small_m_partial_scale_blocks(M, flags):
+    """Row lengths whose group count is a multiple of 8 but not of 32 (K 256, 768,
+    1280, 2304): the last block of a row's scales is partial, and the list's last
+    GEMV ends its matrix mid-tile, so a partial block meets the end of the scales."""
+    shapes = [(1000, 256), (333, 768), (4097, 1280), (50, 2304), (77, 768)]
+    descs, mats, xs = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        m, W, S = mat(f"mpart{M}/{i}/{N}x{K}", N, K)
+        x = synth.activations(f"mpart{M}/x{i}", 0, M * K).reshape(M, K)
+        descs.append((W, S, dev_half(x), torch.full((M, N), float("nan"), dtype=torch.float16,
+                                                    device="cuda")))
+        mats.append(m)
+        xs.append(x)
+    run_m(descs, M, flags)
+    for m, x, (W, S, X, Y) in zip(mats, xs, descs):
+        y = host_half(Y)
+        assert np.all(np.isfinite(half_f64(y)))
+        assert_gemv_close(y, m.words(), m.scales(), x)
+
+
 def run_m(descs, M, flags):
     layers = q4.make_layers(descs)
     q4.q4_decode_step(layers, M, flags)
