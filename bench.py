@@ -41,6 +41,19 @@ KERNEL_SOURCES = ["bit_weight_streaming_q4f16_amd/csrc/q4_step.hip",
                   "bit_weight_streaming_q4f16_amd/csrc/q4_step.h",
                   "bit_weight_streaming_q4f16_amd/csrc/q4_internal.h"]
 PROFILE = os.path.join(ROOT, "profiles", "k_step_phi3_decode_sweep")
+# the kernels with committed counter summaries: the headline step, and the small-M
+# step on the 2B-class sweep at M = 8
+PROFILED = {
+    "k_step": dict(profile=PROFILE, sources=KERNEL_SOURCES, model="phi3", M=1,
+                   title="Phi-3-mini decode-step weight sweep, M=1 (129 GEMVs, one launch)"),
+    "k_step_mfma": dict(
+        profile=os.path.join(ROOT, "profiles", "k_step_mfma_2b_decode_sweep_m8"),
+        sources=["bit_weight_streaming_q4f16_amd/csrc/q4_step_mfma.hip",
+                 "bit_weight_streaming_q4f16_amd/csrc/q4_step_mfma.h",
+                 "bit_weight_streaming_q4f16_amd/csrc/q4_internal.h"],
+        model="2b", M=8,
+        title="2B-class decode-step weight sweep, M=8 (113 GEMVs, one launch)"),
+}
 METRIC = "achieved HBM GB/s (% of peak) and projected decode tok/s, q4 GEMV sweep"
 
 
@@ -66,8 +79,12 @@ def parse():
                     help="time only the decode step (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run only a plain device copy of BYTES, 3 times (counter calibration)")
+    ap.add_argument("--only-m8", action="store_true",
+                    help="time only the 2B-class sweep at M=8 (for profiler runs)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 CSV output under DIR")
+    ap.add_argument("--kernel", choices=sorted(PROFILED), default="k_step",
+                    help="the kernel --summarize-profiles summarizes")
     return ap.parse_args()
 
 
@@ -91,7 +108,7 @@ def build_sweep(torch, q4, synth, np, model="phi3", M=1):
 def main():
     args = parse()
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles)
+        summarize_profiles(args.summarize_profiles, args.kernel)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -108,6 +125,10 @@ def main():
     stream = torch.cuda.Stream()          # default priority
     if args.copy_probe:
         copy_probe(torch, q4, stream, args.copy_probe)
+        return
+    if args.only_m8:
+        print(json.dumps({"twob_sweep_m8": m8_sweep(torch, q4, synth, np, stream, args.steps,
+                                                    args.warmup)}), flush=True)
         return
     t0 = time.time()
     descs, meta = build_sweep(torch, q4, synth, np)
@@ -206,9 +227,9 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def _timed(torch, stream, fn, calls):
+def _timed(torch, stream, fn, calls, warm=3):
     with torch.cuda.stream(stream):
-        for _ in range(3):
+        for _ in range(warm):
             fn(0)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -374,7 +395,15 @@ def per_config(torch, q4, synth, np, stream):
                           weight_bytes=wb)
         del mk
     out["formats_qkv_3072x9216_m1"] = fmts
-    # 2B-class sweep at M = 8 (one q4_gemv_batched kernel per GEMV)
+    out["twob_sweep_m8"] = m8_sweep(torch, q4, synth, np, stream)
+    return out
+
+
+def m8_sweep(torch, q4, synth, np, stream, steps=300, warmup=50):
+    """The 2B-class sweep at M = 8 (113 GEMVs, eight rows of X each) as one
+    q4_decode_step call per step; with the small-M kernel's HBM traffic from its
+    committed counter summary while that kernel is unchanged."""
+    S = synth
     shapes = synth.sweep_shapes("2b")
     descs = []
     xs = {}
@@ -387,14 +416,22 @@ def per_config(torch, q4, synth, np, stream):
         descs.append((m.words_torch("cuda"), sc, xs[K], torch.empty(8 * N, dtype=torch.float16,
                                                                        device="cuda"), N, K))
     b5 = sum(synth.algorithmic_bytes(8, N, K) for _, N, K in shapes)
-    ms = _timed(torch, stream, step_call(descs, 8), 10)
+    layers = q4.make_layers([d[:4] for d in descs])
+    nb = q4.q4_decode_step_workspace_bytes(layers, 8, 0)
+    wsb = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")   # counters clean
+
+    def fn(i):
+        q4.q4_decode_step(layers, 8, q4.STEP_WS_CLEAN, ws=wsb, ws_bytes=nb, stream=stream)
+    ms = _timed(torch, stream, fn, steps, warm=warmup)
     flops = sum(2 * 8 * N * K for _, N, K in shapes)
-    out["twob_sweep_m8"] = _fig(b5, ms, gemvs=len(shapes), steps_per_s=round(1e3 / ms, 1),
-                                tok_per_s=round(8e3 / ms, 1),
-                                tflops=round(flops / (ms * 1e-3) / 1e12, 2))
+    tr = measured_traffic("k_step_mfma")
+    fig = _fig(b5, ms, gemvs=len(shapes), steps_per_s=round(1e3 / ms, 1),
+               tok_per_s=round(8e3 / ms, 1), tflops=round(flops / (ms * 1e-3) / 1e12, 2),
+               kernel="k_step_mfma", traffic=tr,
+               traffic_over_algorithmic=None if tr is None else round(tr / b5, 4))
     del descs
     torch.cuda.empty_cache()
-    return out
+    return fig
 
 
 def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
@@ -454,23 +491,23 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
     return out
 
 
-def source_hash():
+def source_hash(kernel=KERNEL):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in PROFILED[kernel]["sources"]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
+def measured_traffic(kernel=KERNEL):
+    """HBM bytes per launch of a profiled kernel from its committed counter
     summary, or None when there is none or the kernel has changed since."""
     try:
-        with open(PROFILE + ".json") as fh:
+        with open(PROFILED[kernel]["profile"] + ".json") as fh:
             prof = json.load(fh)
     except (OSError, ValueError):
         return None
-    if prof.get("source_sha256") != source_hash():
+    if prof.get("source_sha256") != source_hash(kernel):
         return None
     return prof.get("traffic_bytes_per_launch")
 
@@ -523,20 +560,22 @@ def _counter_per_dispatch(d, kernel, counter):
     return sum(per.values()) / len(per), len(per)
 
 
-def summarize_profiles(d):
-    """Write profiles/k_step_phi3_decode_sweep.{md,json} from rocprofv3 output."""
+def summarize_profiles(d, kernel=KERNEL):
+    """Write the kernel's profiles/ summary (.md, .json) from rocprofv3 output."""
     import synth
-    shapes = synth.sweep_shapes("phi3")
-    step_bytes = sum(synth.algorithmic_bytes(1, N, K) for _, N, K in shapes)
+    P = PROFILED[kernel]
+    KERNEL_, PROFILE_ = kernel, P["profile"]
+    shapes = synth.sweep_shapes(P["model"])
+    step_bytes = sum(synth.algorithmic_bytes(P["M"], N, K) for _, N, K in shapes)
     stats = {}
     for r in _csv_rows(os.path.join(d, "stats"), "kernel_stats.csv"):
-        for k in (KERNEL, "k_zero"):
+        for k in (KERNEL_, "k_zero", "k_zero_m"):
             if _is_kernel(r["Name"], k):
                 stats[k] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
                             "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
                             "percentage": float(r["Percentage"])}
-    fetch, nf = _counter_per_dispatch(os.path.join(d, "fetch"), KERNEL, "FETCH_SIZE")
-    write, nw = _counter_per_dispatch(os.path.join(d, "write"), KERNEL, "WRITE_SIZE")
+    fetch, nf = _counter_per_dispatch(os.path.join(d, "fetch"), KERNEL_, "FETCH_SIZE")
+    write, nw = _counter_per_dispatch(os.path.join(d, "write"), KERNEL_, "WRITE_SIZE")
     cfetch, _ = _counter_per_dispatch(os.path.join(d, "copy_fetch"), "k_probe_copy", "FETCH_SIZE")
     cwrite, _ = _counter_per_dispatch(os.path.join(d, "copy_write"), "k_probe_copy", "WRITE_SIZE")
     copy_bytes = None
@@ -550,10 +589,10 @@ def summarize_profiles(d):
     fw = copy_bytes / (cwrite * 1024)
     traffic = fetch * 1024 * ff + write * 1024 * fw
     commands = open(os.path.join(d, "commands.txt")).read().strip()
-    avg = stats[KERNEL]["avg_us"]
+    avg = stats[KERNEL_]["avg_us"]
     out = {
-        "kernel": KERNEL, "workload": "phi3-mini decode-step weight sweep, M=1 (129 GEMVs)",
-        "source_sha256": source_hash(), "sources": KERNEL_SOURCES,
+        "kernel": KERNEL_, "workload": P["title"],
+        "source_sha256": source_hash(kernel), "sources": P["sources"],
         "kernel_stats": stats,
         "algorithmic_bytes_per_launch": step_bytes,
         "achieved_gbs_from_avg_duration": round(step_bytes / (avg * 1e-6) / 1e9, 1),
@@ -565,11 +604,11 @@ def summarize_profiles(d):
         "traffic_over_algorithmic": round(traffic / step_bytes, 4),
         "commands": commands.splitlines(),
     }
-    with open(PROFILE + ".json", "w") as fh:
+    with open(PROFILE_ + ".json", "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     lines = [
-        f"# {KERNEL}: Phi-3-mini decode-step weight sweep, M=1 (129 GEMVs, one launch)", "",
+        f"# {KERNEL_}: {P['title']}", "",
         "Commands (run from the repository root; TMPDIR=/tmp):", "",
         *["    " + c for c in commands.splitlines()], "",
         "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
@@ -581,15 +620,15 @@ def summarize_profiles(d):
         f" GB/s at the average duration ({100 * out['achieved_gbs_from_avg_duration'] / PEAK_GBS:.1f}"
         " % of 8 TB/s).", "",
         "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
-        f"- {KERNEL}: FETCH_SIZE {fetch:,.0f} KiB, WRITE_SIZE {write:,.0f} KiB per dispatch "
+        f"- {KERNEL_}: FETCH_SIZE {fetch:,.0f} KiB, WRITE_SIZE {write:,.0f} KiB per dispatch "
         f"(mean of {nf} / {nw} dispatches)",
         f"- calibration, k_probe_copy of {copy_bytes:,} bytes: FETCH_SIZE {cfetch:,.0f} KiB, "
         f"WRITE_SIZE {cwrite:,.0f} KiB -> factors {ff:.4f} (fetch), {fw:.4f} (write)",
         f"- traffic per launch = FETCH x 1024 x {ff:.4f} + WRITE x 1024 x {fw:.4f} = "
         f"{traffic:,.0f} bytes = {traffic / step_bytes:.4f} x algorithmic", "",
-        f"Kernel sources (sha256 {out['source_sha256'][:16]}...): " + ", ".join(KERNEL_SOURCES),
+        f"Kernel sources (sha256 {out['source_sha256'][:16]}...): " + ", ".join(P["sources"]),
     ]
-    with open(PROFILE + ".md", "w") as fh:
+    with open(PROFILE_ + ".md", "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
