@@ -23,7 +23,7 @@
 //    them in ascending slice order, so results are deterministic;
 //  * small M (2..8) uses MFMA: v_mfma_f32_16x16x32_f16 covers 16 rows by one
 //    32-weight group, so the per-group scale is applied exactly to its result.
-#include "q4_internal.h"
+#include "q4_fused.h"
 
 namespace q4 {
 namespace {
@@ -120,9 +120,18 @@ __device__ __forceinline__ int slice_begin(int G, int splits, int s) {
 // ---------------------------------------------------------------- M == 1 ---
 // Grid: x = workgroups striding over rows, y = K slice.  A team of LPR lanes owns
 // a row at a time; lane i of the team takes groups i, i + LPR, ... of the slice,
-// UNR of them per trip (loads first, then arithmetic).  Out-of-range groups load
-// the slice's last group again and are discarded by a select.
-template <int LPR, int UNR>
+// UNR of them per trip (loads first, then arithmetic; the launch picks UNR so that
+// a slice is one trip).  Out-of-range groups load the slice's last group again and
+// are discarded by a select.  A team's first loads are issued before x is staged
+// (weights do not depend on x), so the two round trips overlap.  The next row's
+// loads go out as soon as a row's arithmetic is done.
+//
+// Modes: kPlain writes y (or split-K partials); kGlu (q4_fused.h) computes rows
+// i and F + i (F = N, the matrix has 2N rows) and writes silu_mul_h of the two
+// rounded results.
+enum : int { kPlain = 0, kGlu = 1 };
+
+template <int LPR, int UNR, int MODE>
 __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
                                                     const uint16_t* __restrict__ S,
                                                     const uint4* __restrict__ X,
@@ -133,44 +142,64 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
   const int split = blockIdx.y;
   const int g0 = slice_begin(G, splits, split);
   const int gc = slice_begin(G, splits, split + 1) - g0;
+  const int lane = threadIdx.x & (LPR - 1);
+  const int team = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) / LPR);
+  const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
+  constexpr int R = MODE == kGlu ? 2 : 1;    // rows per team and output
+  uint4 wv[R][UNR];
+  uint16_t sv[R][UNR];
+  auto issue = [&](int n, int t0) {          // trip t0 of output n
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int64_t row = n + (int64_t)q * N;
+      const uint4* wr = W + row * G + g0;
+      const uint16_t* sr = S + row * G + g0;
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        int g = t0 + u * LPR + lane;
+        g = g < gc ? g : gc - 1;
+        wv[q][u] = load_nt(wr + g);
+        sv[q][u] = sr[g];
+      }
+    }
+  };
+  int n = team;
+  if (n < N) issue(n, 0);
   for (int i = threadIdx.x; i < 4 * gc; i += kBlock) {
     const int g = i >> 2, j = i & 3;
     xs[j * gc + g] = pair_order(X[(int64_t)(g0 + g) * 4 + j]);
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & (LPR - 1);
-  const int team = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) / LPR);
-  const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
-  for (int n = team; n < N; n += nteams) {
-    const uint4* wr = W + (int64_t)n * G + g0;
-    const uint16_t* sr = S + (int64_t)n * G + g0;
-    float acc = 0.f;
+  for (; n < N; n += nteams) {
+    float acc[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) acc[q] = 0.f;
     for (int t0 = 0; t0 < gc; t0 += LPR * UNR) {
-      uint4 wv[UNR];
-      uint16_t sv[UNR];
+      if (t0 > 0) issue(n, t0);
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        int g = t0 + u * LPR + lane;
-        g = g < gc ? g : gc - 1;
-        wv[u] = load_nt(wr + g);
-        sv[u] = sr[g];
-      }
+      for (int q = 0; q < R; ++q) {
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int graw = t0 + u * LPR + lane;
-        const int g = graw < gc ? graw : gc - 1;
-        const float p = group_dot(wv[u], xs, gc, g);
-        const float t = __builtin_fmaf(p, half_to_float(sv[u]), acc);
-        acc = graw < gc ? t : acc;
+        for (int u = 0; u < UNR; ++u) {
+          const int graw = t0 + u * LPR + lane;
+          const int g = graw < gc ? graw : gc - 1;
+          const float p = group_dot(wv[q][u], xs, gc, g);
+          const float t = __builtin_fmaf(p, half_to_float(sv[q][u]), acc[q]);
+          acc[q] = graw < gc ? t : acc[q];
+        }
       }
     }
-    acc = team_sum<LPR>(acc);
+    if (n + nteams < N) issue(n + nteams, 0);
+#pragma unroll
+    for (int q = 0; q < R; ++q) acc[q] = team_sum<LPR>(acc[q]);
     if (lane == 0) {
-      if (splits == 1)
-        Y[n] = float_to_half_rne(acc);
-      else
-        P[(int64_t)split * N + n] = acc;
+      if constexpr (MODE == kGlu) {
+        Y[n] = bits<uint16_t>(silu_mul_h((_Float16)acc[0], (_Float16)acc[1]));
+      } else if (splits == 1) {
+        Y[n] = float_to_half_rne(acc[0]);
+      } else {
+        P[(int64_t)split * N + n] = acc[0];
+      }
     }
   }
 }
@@ -295,9 +324,10 @@ int choose_lpr(int64_t G) {
   return l < 4 ? 4 : (l > 64 ? 64 : l);
 }
 
-template <int LPR>
-hipError_t launch_m1(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
-                     hipStream_t s) {
+// a.N: the outputs (kGlu: half the matrix's rows)
+template <int LPR, int UNR, int MODE>
+hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
+                         hipStream_t s) {
   const int64_t G = a.K / 32;
   const int64_t teams_per_block = kBlock / LPR;
   int64_t blocks = (a.N + teams_per_block - 1) / teams_per_block;
@@ -306,11 +336,35 @@ hipError_t launch_m1(const GemvArgs& a, const GemvPlan& p, float* part, const De
   const int64_t gmax = (G + p.splits - 1) / p.splits;
   const size_t lds = (size_t)gmax * 64;
   const dim3 grid((unsigned)blocks, (unsigned)p.splits);
-  if (hipError_t e = allow_lds(k_gemv_m1<LPR, 2>, lds)) return e;
-  hipLaunchKernelGGL((k_gemv_m1<LPR, 2>), grid, dim3(kBlock), lds, s,
+  if (hipError_t e = allow_lds(k_gemv_m1<LPR, UNR, MODE>, lds)) return e;
+  hipLaunchKernelGGL((k_gemv_m1<LPR, UNR, MODE>), grid, dim3(kBlock), lds, s,
                      reinterpret_cast<const uint4*>(a.words), a.scales,
                      reinterpret_cast<const uint4*>(a.x), a.y, part, (int)a.N, (int)G, p.splits);
   return hipGetLastError();
+}
+
+// groups per lane per trip: the whole slice in one trip up to 8 (larger slices,
+// from an explicit split count, take several trips)
+template <int LPR, int MODE>
+hipError_t launch_m1(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
+                     hipStream_t s) {
+  const int64_t G = a.K / 32;
+  const int64_t per_lane = ((G + p.splits - 1) / p.splits + LPR - 1) / LPR;
+  if (per_lane <= 2) return launch_m1_unr<LPR, 2, MODE>(a, p, part, d, s);
+  if (per_lane <= 4) return launch_m1_unr<LPR, 4, MODE>(a, p, part, d, s);
+  return launch_m1_unr<LPR, 8, MODE>(a, p, part, d, s);
+}
+
+template <int MODE>
+hipError_t launch_m1_lpr(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
+                         hipStream_t s) {
+  switch (p.lanes_per_row) {
+    case 4: return launch_m1<4, MODE>(a, p, part, d, s);
+    case 8: return launch_m1<8, MODE>(a, p, part, d, s);
+    case 16: return launch_m1<16, MODE>(a, p, part, d, s);
+    case 32: return launch_m1<32, MODE>(a, p, part, d, s);
+    default: return launch_m1<64, MODE>(a, p, part, d, s);
+  }
 }
 
 }  // namespace
@@ -343,8 +397,10 @@ GemvPlan plan_auto(const DeviceInfo& d, int64_t M, int64_t N, int64_t K) {
   } else {
     blocks = (N + 15) / 16;
   }
-  // too few workgroups to cover every compute unit twice: split K as well
-  const int64_t want = 2 * (int64_t)d.cus;
+  // too few workgroups to give every compute unit one: split K as well (a
+  // workgroup's loads are all in flight at once, so one per unit already
+  // streams; a second split-K pass costs more than the rows it would add)
+  const int64_t want = M == 1 ? (int64_t)d.cus : 2 * (int64_t)d.cus;
   if (blocks * splits < want) {
     int64_t s2 = (want + blocks - 1) / blocks;
     const int64_t smax = M == 1 ? G / 8 : G / 16;
@@ -362,13 +418,7 @@ hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p
   uint16_t* out = a.y;
   hipError_t e;
   if (a.M == 1) {
-    switch (p.lanes_per_row) {
-      case 4: e = launch_m1<4>(a, p, part, d, s); break;
-      case 8: e = launch_m1<8>(a, p, part, d, s); break;
-      case 16: e = launch_m1<16>(a, p, part, d, s); break;
-      case 32: e = launch_m1<32>(a, p, part, d, s); break;
-      default: e = launch_m1<64>(a, p, part, d, s); break;
-    }
+    e = launch_m1_lpr<kPlain>(a, p, part, d, s);
   } else {
     const int64_t G = a.K / 32;
     const int64_t gmax = (G + p.splits - 1) / p.splits;
@@ -388,6 +438,14 @@ hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p
   hipLaunchKernelGGL(k_combine, dim3((unsigned)blocks), dim3(kBlock), 0, s, part, out, count,
                      p.splits);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_glu(const DeviceInfo& d, const uint32_t* words, const uint16_t* scales,
+                           const uint16_t* x, uint16_t* h, int64_t F, int64_t K,
+                           const GemvPlan& p, hipStream_t s) {
+  if (p.splits != 1) return hipErrorInvalidValue;
+  const GemvArgs a{words, scales, x, h, 1, F, K};
+  return launch_m1_lpr<kGlu>(a, p, nullptr, d, s);
 }
 
 }  // namespace q4

@@ -69,6 +69,9 @@ hipError_t launch_unpack(const uint32_t* words, uint8_t* codes, int64_t N, int64
 // The feed-forward glue of the decode loop (Zero TVM documentation, "Decode
 // loop"): fp16(silu(g) * u) with silu(g) = g / (1 + exp(-g)), in fp32, rounded to
 // nearest even; silu(+inf) = +inf, silu(-inf) = -0 (its limits).
+// The product is rounded to fp32 and then to fp16, as written: the empty asm keeps
+// the compiler from fusing the two into one mixed-precision instruction (which
+// rounds once), so every kernel that forms the glue gets the same bits.
 __device__ __forceinline__ _Float16 silu_mul_h(_Float16 g, _Float16 u) {
   const float gf = (float)g;
   float sg;
@@ -76,7 +79,9 @@ __device__ __forceinline__ _Float16 silu_mul_h(_Float16 g, _Float16 u) {
     sg = gf > 0.f ? gf : -0.f;
   else
     sg = gf / (1.f + __expf(-gf));
-  return (_Float16)(sg * (float)u);
+  float p = sg * (float)u;
+  asm volatile("" : "+v"(p));
+  return (_Float16)p;
 }
 
 // out[m][i] = silu_mul_h(gu[m][i], gu[m][H + i]); H % 8 == 0, 16-byte aligned.

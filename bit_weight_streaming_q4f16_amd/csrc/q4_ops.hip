@@ -94,22 +94,53 @@ __global__ __launch_bounds__(kBlock) void k_rmsnorm(const uint4* __restrict__ de
   }
 }
 
-// Largest value of a row, ties to the lowest index, NaN skipped (none: 0).
-__global__ __launch_bounds__(kBlock) void k_argmax(const uint16_t* __restrict__ x, int64_t N,
-                                                   int32_t* __restrict__ out) {
-  __shared__ float sv[4];
-  __shared__ int64_t si[4];
+// Largest value of a row, ties to the lowest index, NaN skipped (none: 0).  One
+// workgroup of kArgThreads per row; a 16-byte aligned row is read as chunks of 8
+// values, four chunks per thread in flight (a row of the LM head's 32064 logits is
+// then one or two memory round trips, not a hundred dependent loads).  Within a
+// thread values are seen in increasing index order and only a larger value
+// replaces the best, so ties keep the lowest index; across threads the merge
+// compares indices.
+constexpr int kArgThreads = 1024;
+__global__ __launch_bounds__(kArgThreads) void k_argmax(const uint16_t* __restrict__ x,
+                                                        int64_t N, int32_t* __restrict__ out) {
+  __shared__ float sv[kArgThreads / 64];
+  __shared__ int64_t si[kArgThreads / 64];
   const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * N;
   float bv = 0.f;
   int64_t bi = -1;
-  for (int64_t n = threadIdx.x; n < N; n += kBlock) {
-    const float v = (float)bits<_Float16>(x[row * N + n]);
-    if (v != v) continue;
-    if (bi < 0 || v > bv) {
+  auto see = [&](float v, int64_t n) {
+    if (v == v && (bi < 0 || v > bv)) {
       bv = v;
       bi = n;
     }
+  };
+  int64_t head = 0;
+  if ((reinterpret_cast<uintptr_t>(xr) & 15u) == 0) {
+    const int64_t nch = N / 8;
+    const uint4* xv = reinterpret_cast<const uint4*>(xr);
+    for (int64_t c0 = threadIdx.x; c0 < nch; c0 += 4 * kArgThreads) {
+      uint4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + (int64_t)u * kArgThreads;
+        w[u] = c < nch ? xv[c] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + (int64_t)u * kArgThreads;
+        if (c < nch) {
+          const h8_t h = bits<h8_t>(w[u]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) see((float)h[e], c * 8 + e);
+        }
+      }
+    }
+    head = nch * 8;
   }
+  for (int64_t n = head + threadIdx.x; n < N; n += kArgThreads)
+    see((float)bits<_Float16>(xr[n]), n);
   // better: a value (bi >= 0) that is larger, or equal with a lower index
   auto take = [](float& v, int64_t& i, float ov, int64_t oi) {
     if (oi >= 0 && (i < 0 || ov > v || (ov == v && oi < i))) {
@@ -132,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void k_argmax(const uint16_t* __restrict__ 
   if (threadIdx.x == 0) {
     float v = sv[0];
     int64_t i = si[0];
-    for (int w = 1; w < 4; ++w) take(v, i, sv[w], si[w]);
+    for (int w = 1; w < kArgThreads / 64; ++w) take(v, i, sv[w], si[w]);
     out[row] = (int32_t)(i < 0 ? 0 : i);
   }
 }
@@ -188,7 +219,7 @@ hipError_t launch_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const u
 }
 
 hipError_t launch_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax, dim3((unsigned)M), dim3(kBlock), 0, s, x, N, out);
+  hipLaunchKernelGGL(k_argmax, dim3((unsigned)M), dim3(kArgThreads), 0, s, x, N, out);
   return hipGetLastError();
 }
 

@@ -5,7 +5,9 @@
 // qkv, o (reading the value part of qkv), residual add + RMSNorm, gate/up,
 // SiLU-multiply, down, residual add + RMSNorm, then the LM head and the argmax.
 // Each projection is one GEMV kernel (one kernel per GEMV is the faster choice
-// for a chain in which every GEMV waits for the one before it).  Every buffer
+// for a chain in which every GEMV waits for the one before it).  Where gate/up
+// needs no split-K pass the glue runs inside it (q4_fused.h): six kernels per
+// block instead of seven, with bitwise the same results.  Every buffer
 // between the kernels lives in the caller's workspace; the residual is updated
 // in place.  A multi-step decode captures one step, with two one-thread kernels
 // that take the step's token from and put the next one into the caller's token
@@ -19,6 +21,7 @@
 #include <vector>
 
 #include "q4f16.h"
+#include "q4_fused.h"
 #include "q4_internal.h"
 
 namespace {
@@ -29,6 +32,7 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 // then the token bookkeeping (int32: current token, next token, counter).
 struct Layout {
   q4::GemvPlan qkv, o, gate_up, down, lm_head;
+  bool fuse = false;       // the glue inside the gate/up GEMV (no split-K pass in it)
   size_t res = 0, h = 0, qkv_out = 0, attn = 0, gu = 0, hf = 0, dn = 0, logits = 0, tok = 0;
   size_t bytes = 0;
 };
@@ -40,6 +44,7 @@ Layout layout_for(const q4::DeviceInfo& d, const q4_model& m) {
   L.gate_up = q4::plan_auto(d, 1, 2 * m.F, m.D);
   L.down = q4::plan_auto(d, 1, m.D, m.F);
   L.lm_head = q4::plan_auto(d, 1, m.V, m.D);
+  L.fuse = L.gate_up.splits == 1;
   size_t off = up256(std::max({L.qkv.ws_bytes, L.o.ws_bytes, L.gate_up.ws_bytes,
                                L.down.ws_bytes, L.lm_head.ws_bytes}));
   auto take = [&](size_t bytes) {
@@ -55,7 +60,7 @@ Layout layout_for(const q4::DeviceInfo& d, const q4_model& m) {
   L.hf = take(2 * m.F);
   L.dn = take(2 * m.D);
   L.logits = take(2 * m.V);
-  L.tok = take(16);
+  L.tok = take(16);            // int32: current token, next token, step counter
   L.bytes = off;
   return L;
 }
@@ -141,14 +146,19 @@ hipError_t enqueue_step(const q4::DeviceInfo& d, const q4_model& m, const Layout
   Q4_TRY(q4::launch_rmsnorm(nullptr, res, g0, m.eps, 1, m.D, nullptr, h, s));
   for (int64_t b = 0; b < m.n_blocks; ++b) {
     const q4_block& B = m.blocks[b];
+    const uint16_t* next = b + 1 < m.n_blocks ? m.blocks[b + 1].attn_norm : m.final_norm;
     Q4_TRY(gemv(B.qkv, L.qkv, h, qkv));
     // attention at a single position: its output is the value vector
     Q4_TRY(gemv(B.o, L.o, qkv + 2 * m.D, attn));
     Q4_TRY(q4::launch_rmsnorm(attn, res, B.ffn_norm, m.eps, 1, m.D, res, h, s));
-    Q4_TRY(gemv(B.gate_up, L.gate_up, h, gu));
-    Q4_TRY(q4::launch_silu_mul(gu, hf, 1, m.F, s));
+    if (L.fuse) {
+      Q4_TRY(q4::launch_gemv_glu(d, B.gate_up.words, B.gate_up.scales, h, hf, m.F, m.D,
+                                 L.gate_up, s));
+    } else {
+      Q4_TRY(gemv(B.gate_up, L.gate_up, h, gu));
+      Q4_TRY(q4::launch_silu_mul(gu, hf, 1, m.F, s));
+    }
     Q4_TRY(gemv(B.down, L.down, hf, dn));
-    const uint16_t* next = b + 1 < m.n_blocks ? m.blocks[b + 1].attn_norm : m.final_norm;
     Q4_TRY(q4::launch_rmsnorm(dn, res, next, m.eps, 1, m.D, res, h, s));
   }
   Q4_TRY(gemv(m.lm_head, L.lm_head, h, lg));

@@ -73,6 +73,20 @@ def test_add_rmsnorm(inplace):
     within_one_ulp(host_half(out), ref_out)
 
 
+@pytest.mark.parametrize("M,N", [(3, 1001), (4, 5), (2, 8 * 1024 * 4 + 5), (5, 64)])
+def test_argmax_shapes(M, N):
+    """Rows not 16-byte aligned (N % 8 != 0), rows shorter than a chunk, a tail
+    after the chunks, and ties inside one chunk and across threads."""
+    rng = np.random.default_rng(N)
+    x = rng.standard_normal((M, N)).astype(np.float16)
+    x[0, [N // 2, N - 1]] = np.float16(9.0)                   # tie: lowest index
+    if N >= 8:
+        x[-1, [1, 2, 7]] = np.float16(9.5)                    # ties inside one chunk
+    out = q4.q4_argmax(dev_half(x.view(np.uint16)))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.argmax(x.view(np.uint16)))
+
+
 def test_argmax_bit_exact():
     rng = np.random.default_rng(11)
     M, N = 6, 32064

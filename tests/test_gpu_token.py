@@ -135,9 +135,17 @@ def test_step_matches_composition_and_oracle(small):
     assert int(tout.cpu()[0]) == t_ref
 
 
+@pytest.fixture(scope="module")
+def wide():
+    """Phi-3 width (D 3072, FFN 8192): wide enough that no projection needs a
+    split-K pass, so the driver runs the glue and the norms inside the GEMVs."""
+    return Weights("wide", 2, 3072, 8192, 2048, host=False)
+
+
+@pytest.mark.parametrize("model", ["small", "wide"])
 @pytest.mark.parametrize("flags", [0, q4.TOKENS_EAGER], ids=["graph", "eager"])
-def test_multi_step_equals_single_steps(small, flags):
-    W = small
+def test_multi_step_equals_single_steps(request, model, flags):
+    W = request.getfixturevalue(model)
     steps = 6
     # single steps, host round trip between them
     ws = torch.empty(q4.q4_decode_token_workspace_bytes(W.model), dtype=torch.uint8, device="cuda")
