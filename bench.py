@@ -395,7 +395,56 @@ def per_config(torch, q4, synth, np, stream):
                           weight_bytes=wb)
         del mk
     out["formats_qkv_3072x9216_m1"] = fmts
+    out["formats_large_m1"] = formats_large(torch, q4, S, stream)
     out["twob_sweep_m8"] = m8_sweep(torch, q4, synth, np, stream)
+    return out
+
+
+def formats_large(torch, q4, S, stream, N=262144, K=3072, calls=20):
+    """Each format on one GEMV of 262144 x 3072 (350-500 MB: larger than the 256 MB
+    last-level cache, and long enough that the fixed cost of a launch is a few per
+    cent): what each format's decode streams at, and its time per weight -- whether
+    fewer bytes per weight buy time here.  q4f16_1 also in the persistent
+    decode-step kernel, one descriptor."""
+    out = {}
+    for name, f in (("q4f16_1", 0), ("q3f16_1", q4.FMT_Q3F16_1), ("q4f32_1", q4.FMT_Q4F32_1),
+                    ("af4g64", q4.FMT_AF4_G64)):
+        wb = q4.q4_format_weight_bytes(f, N, K)
+        es = 4 if f == q4.FMT_Q4F32_1 else 2
+        nwords = N * K // 32 * (3 if f == q4.FMT_Q3F16_1 else 4)
+        per_group = 64 if f == q4.FMT_AF4_G64 else 32
+        W = S.words_torch(f"bench/fmtL/{name}/w", 0, nwords).reshape(N, -1)
+        sc = (torch.rand(N, K // per_group, device="cuda") * 0.01 + 1e-3).to(
+            torch.float32 if es == 4 else torch.float16)
+        bi = ((torch.rand(N, K // per_group, device="cuda") - 0.5) * 0.1).half() \
+            if f == q4.FMT_AF4_G64 else None
+        xdt = torch.float32 if es == 4 else torch.float16
+        xf = torch.randn(K, device="cuda").to(xdt)
+        yf = torch.empty(N, device="cuda", dtype=xdt)
+        wsf = torch.empty(max(q4.q4_workspace_bytes(1, N, K), 16), dtype=torch.uint8,
+                          device="cuda")
+
+        def fn(i, W=W, sc=sc, bi=bi, f=f, xf=xf, yf=yf, wsf=wsf):
+            if f == 0:
+                q4.q4_gemv(W, sc, xf, yf, ws=wsf, stream=stream)
+            else:
+                q4.q4_gemv_format(f, W, sc, xf, K, biases=bi, y=yf, stream=stream)
+        nb = wb + es * (N + K)
+        ms = _timed(torch, stream, fn, calls, warm=5)
+        out[name] = _fig(nb, ms, weight_bytes=wb, ns_per_kweight=round(ms * 1e6 / (N * K / 1e3), 4))
+        if f == 0:
+            layers = q4.make_layers([(W, sc, xf, yf)])
+            nbs = q4.q4_decode_step_workspace_bytes(layers, 1, 0)
+            wss = torch.zeros(max(nbs, 16), dtype=torch.uint8, device="cuda")
+
+            def fs(i):
+                q4.q4_decode_step(layers, 1, q4.STEP_WS_CLEAN, ws=wss, ws_bytes=nbs,
+                                  stream=stream)
+            ms = _timed(torch, stream, fs, calls, warm=5)
+            out["q4f16_1_decode_step"] = _fig(nb, ms, weight_bytes=wb,
+                                              ns_per_kweight=round(ms * 1e6 / (N * K / 1e3), 4))
+        del W, sc, bi
+        torch.cuda.empty_cache()
     return out
 
 
