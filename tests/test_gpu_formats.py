@@ -78,6 +78,32 @@ def test_format_gemv_matches_oracle(fmt, N, K):
     assert err.max() <= tol, (err.max(), tol)
 
 
+@pytest.mark.parametrize("N,K", [(257, 128 * 37), (64, 32768), (5, 128), (700, 128 * 20)])
+def test_q3_vector_path_shapes(N, K):
+    """q3f16_1 with K % 128 == 0 takes the four-groups-per-lane kernel: several
+    trips per lane, lanes left idle in the last trip, and the largest K."""
+    test_format_gemv_matches_oracle("q3f16_1", N, K)
+
+
+def test_q3_misaligned_words_take_the_generic_path():
+    """Words 4-byte but not 16-byte aligned: same results through the per-group
+    decode."""
+    N, K = 300, 1024
+    words, scales, _, x = make("q3f16_1", N, K, "mis")
+    flat = torch.zeros(N * (K // 32) * 3 + 4, dtype=torch.int32, device="cuda")
+    view = flat[1:1 + words.size]
+    view.copy_(to_dev(words).view(-1).view(torch.int32))
+    assert view.data_ptr() % 16 != 0
+    y = q4.q4_gemv_format(q4.FMT_Q3F16_1, view.view(N, -1), to_dev(scales), to_dev(x), K)
+    y2 = q4.q4_gemv_format(q4.FMT_Q3F16_1, to_dev(words), to_dev(scales), to_dev(x), K)
+    torch.cuda.synchronize()
+    ref, norms = oracle.gemv_format("q3f16_1", words, scales, None, x, K, rows=np.arange(N))
+    tol = 2e-3 * oracle.vec_norm(x) * norms.max()
+    for out in (y, y2):
+        got = half_f64(host_half(out))
+        assert np.abs(got - ref).max() <= tol
+
+
 def test_format_weight_bytes():
     assert q4.q4_format_weight_bytes(0, 9216, 3072) == 9216 * 96 * 18
     assert q4.q4_format_weight_bytes(q4.FMT_Q3F16_1, 9216, 3072) == 9216 * 96 * 14
