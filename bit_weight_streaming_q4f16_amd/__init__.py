@@ -39,6 +39,8 @@ TOKENS_EAGER = 0x1
 FMT_Q3F16_1 = 1
 FMT_Q4F32_1 = 2
 FMT_AF4_G64 = 3
+FMT_LOAD_STAGED = 0x100   # OR-ed into FMT_Q3F16_1: force one way of loading
+FMT_LOAD_DIRECT = 0x200
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
           4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED"}
@@ -414,7 +416,7 @@ def q4_gemv_format(fmt: int, words, scales, x, K: int, biases=None, y=None, stre
     torch = _torch()
     N = words.shape[0]
     if y is None:
-        y = torch.empty(N, dtype=torch.float32 if fmt == FMT_Q4F32_1 else torch.float16,
+        y = torch.empty(N, dtype=torch.float32 if (fmt & 0xFF) == FMT_Q4F32_1 else torch.float16,
                         device=words.device)
     _check(load().q4_gemv_format(fmt, _ptr(words), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y),
                                  N, K, _stream(stream)))

@@ -17,6 +17,7 @@
 
 #include "q4_step_dma.h"
 #include "q4_step_mfma.h"
+#include "q4_formats.h"
 
 namespace {
 
@@ -604,8 +605,12 @@ size_t q4_format_weight_bytes(uint32_t format, int64_t N, int64_t K) {
 int q4_gemv_format(uint32_t format, const uint32_t* words, const void* scales,
                    const uint16_t* biases, const void* x, void* y, int64_t N, int64_t K,
                    q4_stream_t stream) {
+  const uint32_t load = format & (Q4_FMT_LOAD_STAGED | Q4_FMT_LOAD_DIRECT);
+  format &= ~(Q4_FMT_LOAD_STAGED | Q4_FMT_LOAD_DIRECT);
   if (format < Q4_FMT_Q3F16_1 || format > Q4_FMT_AF4_G64)
     return fail(Q4_ERR_SHAPE, "q4_gemv_format: format = %u: unknown", format);
+  if (load && (format != Q4_FMT_Q3F16_1 || load == (Q4_FMT_LOAD_STAGED | Q4_FMT_LOAD_DIRECT)))
+    return fail(Q4_ERR_SHAPE, "q4_gemv_format: a load bit is for q3f16_1 only, one at a time");
   if (!words || !scales || !x || !y) return fail(Q4_ERR_NULL, "q4_gemv_format: NULL pointer");
   const bool affine = format == Q4_FMT_AF4_G64, f32 = format == Q4_FMT_Q4F32_1;
   if (affine != (biases != nullptr))
@@ -625,8 +630,14 @@ int q4_gemv_format(uint32_t format, const uint32_t* words, const void* scales,
     return fail(Q4_ERR_SHAPE, "q4_gemv_format: y overlaps an input");
   const q4::DeviceInfo* d = q4::device_info();
   if (!d) return fail(Q4_ERR_DEVICE, "q4_gemv_format: no HIP device");
-  hipError_t e = q4::launch_gemv_format(*d, (int)format, words, scales, biases, x, y, N, K,
-                                        static_cast<hipStream_t>(stream));
+  const int staged = load == Q4_FMT_LOAD_STAGED ? 1 : load == Q4_FMT_LOAD_DIRECT ? 0 : -1;
+  hipError_t e =
+      format == Q4_FMT_Q3F16_1
+          ? q4::launch_gemv_q3(*d, words, static_cast<const uint16_t*>(scales),
+                               static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), N, K,
+                               staged, static_cast<hipStream_t>(stream))
+          : q4::launch_gemv_format(*d, (int)format, words, scales, biases, x, y, N, K,
+                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : device_error(e, "q4_gemv_format");
 }
 

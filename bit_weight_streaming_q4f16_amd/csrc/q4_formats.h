@@ -1,0 +1,15 @@
+// The q3f16_1 GEMV with its loading way chosen by the caller (q4_formats.hip).
+#pragma once
+
+#include "q4_internal.h"
+
+namespace q4 {
+
+// y = W x at M = 1 in q3f16_1 (see include/q4f16.h); staged: 1 the words as
+// 16-byte pieces through an LDS stage, 0 one 12-byte load per group, -1 chosen
+// by size.  The results do not depend on it.
+hipError_t launch_gemv_q3(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
+                          const uint16_t* X, uint16_t* Y, int64_t N, int64_t K, int staged,
+                          hipStream_t s);
+
+}  // namespace q4

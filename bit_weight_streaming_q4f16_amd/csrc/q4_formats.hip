@@ -1,18 +1,18 @@
 // GEMV for the format variants beside q4f16_1 (everything-webgpu AI.md,
 // quantization table; Zero TVM documentation, the MLX affine checkpoints), at
 // M = 1, on the skeleton of the q4f16_1 kernels: a team of lanes per row, x
-// staged once per workgroup in LDS, each lane taking every LPR-th group of its
-// row, a DPP/lane-swap reduction.  Only the decode differs:
+// staged once per workgroup in LDS, a DPP/lane-swap reduction.  Only the decode
+// and the load pattern differ:
 //   q3f16_1: a group is three words (12 bytes) holding 32 3-bit codes as one
-//     96-bit value; weight = (q - 3) * s, s fp16 per 32.
+//     96-bit value; weight = (q - 3) * s, s fp16 per 32 (k_gemv_q3).
 //   q4f32_1: q4f16_1's words with fp32 scales; x and y fp32.
 //   af4g64 (MLX affine): q4f16_1's nibble order, fp16 scale s and bias b per 64
 //     weights; weight = s * q + b.
-// Per group a lane forms sum(q * x) in fp32 (codes converted exactly), and the
-// zero point or bias enters through the group's sum of x, staged beside x:
-// (q - z) * s summed = s * (sum q x - z * sum x); s * q + b summed = s * sum q x
-// + b * sum x.
-#include "q4_internal.h"
+// For the last two (k_gemv_fmt) a lane forms sum(q * x) per group in fp32 (codes
+// converted exactly), and the zero point or bias enters through the group's sum
+// of x, staged beside x: (q - z) * s summed = s * (sum q x - z * sum x);
+// s * q + b summed = s * sum q x + b * sum x.
+#include "q4_formats.h"
 
 namespace q4 {
 namespace {
@@ -50,22 +50,13 @@ enum : int { kQ3 = 1, kQ4F32 = 2, kAF4 = 3 };
 
 // Weights per group and words per group of a format.
 template <int F> struct Fmt;
-template <> struct Fmt<kQ3> { static constexpr int kGroup = 32, kWords = 3; };
 template <> struct Fmt<kQ4F32> { static constexpr int kGroup = 32, kWords = 4; };
 template <> struct Fmt<kAF4> { static constexpr int kGroup = 64, kWords = 8; };
 
 // code i (0 .. kGroup-1) of a group's words
 template <int F>
 __device__ __forceinline__ float code_at(const uint32_t (&w)[Fmt<F>::kWords], int i) {
-  if constexpr (F == kQ3) {
-    // codes 0..20 lie in bits 0..62 of w0 | w1 << 32, codes 21..31 in bits 31..63
-    // of w1 | w2 << 32
-    const uint64_t v = i <= 20 ? ((uint64_t)w[0] | ((uint64_t)w[1] << 32))
-                               : ((uint64_t)w[1] | ((uint64_t)w[2] << 32));
-    return (float)((uint32_t)(v >> (i <= 20 ? 3 * i : 3 * i - 32)) & 7u);
-  } else {
-    return (float)((w[i / 8] >> (4 * (i % 8))) & 0xFu);
-  }
+  return (float)((w[i / 8] >> (4 * (i % 8))) & 0xFu);
 }
 
 // sum over group g of q * x; x from LDS planes xs4[j][g] = x[GS*g + 4j .. +3], so
@@ -130,22 +121,14 @@ __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict_
     for (int g = lane; g < G; g += LPR) {
       uint32_t w[NW];
       const uint32_t* wp = W + ((int64_t)n * G + g) * NW;
-      if constexpr (NW == 3) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j) w[j] = __builtin_nontemporal_load(wp + j);
-      } else {
-#pragma unroll
-        for (int j = 0; j < NW; j += 4) {
-          const uint4 v = load_nt(reinterpret_cast<const uint4*>(wp + j));
-          w[j] = v.x; w[j + 1] = v.y; w[j + 2] = v.z; w[j + 3] = v.w;
-        }
+      for (int j = 0; j < NW; j += 4) {
+        const uint4 v = load_nt(reinterpret_cast<const uint4*>(wp + j));
+        w[j] = v.x; w[j + 1] = v.y; w[j + 2] = v.z; w[j + 3] = v.w;
       }
       const float qx = group_qx<F>(w, xs4, G, g);
       const int64_t gi = (int64_t)n * G + g;
-      if constexpr (F == kQ3) {
-        const float s = (float)bits<_Float16>(static_cast<const uint16_t*>(Sv)[gi]);
-        acc = __builtin_fmaf(s, qx - 3.f * gsum[g], acc);
-      } else if constexpr (F == kQ4F32) {
+      if constexpr (F == kQ4F32) {
         const float s = static_cast<const float*>(Sv)[gi];
         acc = __builtin_fmaf(s, qx - 7.f * gsum[g], acc);
       } else {
@@ -164,20 +147,20 @@ __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict_
   }
 }
 
-// q3f16_1 when K % 128 == 0 and the words are 16-byte aligned: a lane takes
-// four consecutive groups (48 bytes, three 128-bit loads) per trip, and the
-// codes become fp16 pairs without extracting them one by one.  A 32-bit window
-// of the group's 96-bit value, taken at bit 3i - 4 (one shift or funnel shift),
-// holds code i at bits 4-6, code i+1 at 7-9, code i+4 at 16-18 and code i+5 at
-// 19-21.  Masking two of those fields and OR-ing in an exponent chosen per
-// field so that the field's lowest bit has place value 1 gives fp16 values
-// 2^E + q exactly (E = 6, 3, 10, 7 for the four fields), one AND-OR per pair;
-// v_dot2_f32_f16 multiplies a pair by the matching x pair.  Per group the sum
-// of (2^E + 3) * x over its codes is staged beside x and subtracted once, which
-// leaves sum (q - 3) * x.  Windows at i = 0, 2, 8, 10, 16, 18, 24, 26 cover the
-// 32 codes as the pairs (i, i+4), (i+1, i+5).
+// q3f16_1: the codes become fp16 pairs without extracting them one by one.  A
+// 32-bit window of a group's 96-bit value, taken at bit 3i - 4 (one shift or
+// funnel shift), holds code i at bits 4-6, code i+1 at 7-9, code i+4 at 16-18
+// and code i+5 at 19-21.  Masking two of those fields and OR-ing in an exponent
+// chosen per field so that the field's lowest bit has place value 1 gives fp16
+// values 2^E + q exactly (E = 6, 3, 10, 7 for the four fields), one AND-OR per
+// pair; v_dot2_f32_f16 multiplies a pair by the matching x pair.  Per group the
+// sum of (2^E + 3) * x over its codes is staged beside x and subtracted once,
+// which leaves sum (q - 3) * x.  Windows at i = 0, 2, 8, 10, 16, 18, 24, 26
+// cover the 32 codes as the pairs (i, i+4), (i+1, i+5).
 constexpr uint32_t kQ3MaskA = 0x00070070u, kQ3MaskB = 0x00380380u;
 constexpr uint32_t kQ3ExpA = 0x64005400u, kQ3ExpB = 0x58004800u;
+constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
+constexpr int kNonTemporal = 2;
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
@@ -201,29 +184,89 @@ __device__ __forceinline__ float q3_group_dot(uint32_t w0, uint32_t w1, uint32_t
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const uint4 xv = xq[c * cstride];
-    a = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c] & ma) | kQ3ExpA), bits<h2_t>(xv.x), a,
+    a = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c] & ma) | kQ3ExpA), bits<h2_t>(xv.x), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c] & mb) | kQ3ExpB), bits<h2_t>(xv.y), b, false);
+    a = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c + 1] & ma) | kQ3ExpA), bits<h2_t>(xv.z), a,
                                false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c] & mb) | kQ3ExpB), bits<h2_t>(xv.y), b,
+    b = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c + 1] & mb) | kQ3ExpB), bits<h2_t>(xv.w), b,
                                false);
-    a = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c + 1] & ma) | kQ3ExpA),
-                               bits<h2_t>(xv.z), a, false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c + 1] & mb) | kQ3ExpB),
-                               bits<h2_t>(xv.w), b, false);
   }
   return a + b;
 }
 
-// LDS: the pairs as uint4 at xq[(c * 4 + t) * Q + u] for group g = 4u + t, chunk
-// c (so the lanes of a team, consecutive u, read consecutive 16-byte entries),
-// then the per-group correction [G].
-template <int LPR>
-__global__ __launch_bounds__(kBlock) void k_gemv_q3(const uint4* __restrict__ W,
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+
+// Grid: workgroups striding over rows, a team of LPR lanes per row.  A trip of a
+// team covers 4 * LPR consecutive groups of its row (48 LPR bytes); lane i
+// computes groups i, i + LPR, i + 2 LPR, i + 3 LPR of it.  Every load instruction
+// reads one contiguous span per team (a lane taking four adjacent groups as
+// three 16-byte loads made each instruction touch every cache line of the span,
+// and streamed at two thirds of the rate).  Two ways to load:
+//  * STAGED: three 16-byte loads per lane (lane i load j: bytes 16 (j LPR + i)),
+//    the raw bytes through the wave's own LDS stage, from which lane i reads
+//    its four groups (12-byte entries: consecutive lanes, consecutive banks).  A
+//    wave's LDS operations complete in order, so the stage needs no barrier.
+//  * otherwise: one 12-byte load per group.  Those stream a fifth slower than
+//    16-byte ones, but the stage adds latency to every trip, which costs more
+//    when a team has only a few trips.
+// Loads go through a buffer resource based at the wave's first row (its teams
+// hold consecutive rows), so offsets stay 32-bit and rows past the matrix read
+// zero.  The next trip's loads are issued before a trip is computed, the first
+// trip's before x is staged.  LDS: the pairs as uint4 at xq[c * G + g] (chunk c
+// of group g; the lanes of a team read consecutive entries), the per-group
+// correction [G] (rounded up to 16 bytes), then one 3 KB stage per wave.
+template <int LPR, bool STAGED>
+__global__ __launch_bounds__(kBlock) void k_gemv_q3(const uint32_t* __restrict__ W,
                                                     const uint16_t* __restrict__ S,
                                                     const uint4* __restrict__ X,
                                                     uint16_t* __restrict__ Y, int N, int K) {
   extern __shared__ uint4 xq[];
-  const int G = K / 32, Q = G / 4;
+  const int G = K / 32;
   float* corr = reinterpret_cast<float*>(xq + 4 * G);
+  const int lane = threadIdx.x & (LPR - 1);
+  const int team = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) / LPR);
+  const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
+  const int T = (G + 4 * LPR - 1) / (4 * LPR);   // trips per row
+  // this lane's places in its wave's stage: where it writes load j, where it
+  // reads group t (in dwords)
+  uint32_t* const stage = reinterpret_cast<uint32_t*>(xq + 4 * G + (G + 3) / 4) +
+                          (threadIdx.x >> 6) * 768;
+  uint32_t* const st_team = stage + ((threadIdx.x & 63) / LPR) * 12 * LPR;
+  struct Trip {
+    uint4 r[3];     // STAGED: the trip's bytes 16 (j LPR + lane) .. + 15
+    u32x3_t w[4];   // otherwise: groups lane + t LPR of the trip
+    uint32_t s[4];  // their scales
+  };
+  auto fetch = [&](Trip& f, int n, int tr) {
+    const int n0 = __builtin_amdgcn_readfirstlane(n);   // the wave's first row
+    const int64_t left = N > n0 ? (int64_t)(N - n0) * G : 0;
+    const uint32_t nw = left * 12 < 0xFFFFFFF0ll ? (uint32_t)(left * 12) : 0xFFFFFFF0u;
+    const uint32_t ns = left * 2 < 0xFFFFFFF0ll ? (uint32_t)(left * 2) : 0xFFFFFFF0u;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(W + (int64_t)n0 * G * 3), 0, (int)nw, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(S + (int64_t)n0 * G), 0, (int)ns, kRsrcFlags);
+    const int gt = (n - n0) * G + tr * 4 * LPR;   // the trip's first group
+    if constexpr (STAGED) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+            rw, gt * 12 + (j * LPR + lane) * 16, 0, kNonTemporal);
+        f.r[j] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        f.w[t] = __builtin_amdgcn_raw_buffer_load_b96(rw, (gt + t * LPR + lane) * 12, 0,
+                                                      kNonTemporal);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      f.s[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, (gt + t * LPR + lane) * 2, 0, 0);
+  };
+  Trip cur;
+  int n = team, tr = 0;
+  fetch(cur, n, 0);
   for (int e = threadIdx.x; e < 4 * G; e += kBlock) {   // e: x[8e .. 8e+7]
     const uint4 v = X[e];
     uint4 o;
@@ -231,8 +274,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q3(const uint4* __restrict__ W,
     o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
     o.z = (v.y & 0xFFFFu) | (v.w << 16);
     o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-    const int g = e >> 2, c = e & 3;
-    xq[(c * 4 + (g & 3)) * Q + (g >> 2)] = o;
+    xq[(e & 3) * G + (e >> 2)] = o;
   }
   // 2^E + 3 for the codes 8c .. 8c+7 of a chunk
   constexpr float kOff[8] = {67.f, 11.f, 67.f, 11.f, 1027.f, 131.f, 1027.f, 131.f};
@@ -252,59 +294,105 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q3(const uint4* __restrict__ W,
 
   uint32_t ma = kQ3MaskA, mb = kQ3MaskB;
   asm volatile("" : "+v"(ma), "+v"(mb));
-  const int lane = threadIdx.x & (LPR - 1);
-  const int team = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) / LPR);
-  const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
-  for (int n = team; n < N; n += nteams) {
-    float acc = 0.f;
-    for (int u = lane; u < Q; u += LPR) {
-      const uint4* wp = W + ((int64_t)n * Q + u) * 3;   // groups 4u .. 4u+3: 12 words
-      const uint4 a = load_nt(wp), b = load_nt(wp + 1), c = load_nt(wp + 2);
-      const uint2 sv = *reinterpret_cast<const uint2*>(S + (int64_t)n * G + 4 * u);
-      const uint32_t w[12] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w};
-      const uint32_t sw[2] = {sv.x, sv.y};
+  float acc = 0.f;
+  // Compute the trip held in `use` after issuing the next one into `fill`; two
+  // buffers taken in turn, so no register copy waits for the loads in flight.
+  auto step = [&](Trip& use, Trip& fill) {
+    int n2 = n, tr2 = tr + 1;
+    if (tr2 == T) {
+      tr2 = 0;
+      n2 += nteams;
+    }
+    uint32_t w[4][3];
+    if constexpr (STAGED) {
+      // the stage is read by other lanes: keep its writes and reads in program order
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float d =
-            q3_group_dot(w[3 * t], w[3 * t + 1], w[3 * t + 2], xq + t * Q + u, 4 * Q, ma, mb);
-        const float sc = (float)bits<_Float16>((uint16_t)(sw[t / 2] >> (16 * (t & 1))));
-        acc = __builtin_fmaf(sc, d - corr[4 * u + t], acc);
+      for (int j = 0; j < 3; ++j)
+        *reinterpret_cast<uint4*>(st_team + 4 * (j * LPR + lane)) = use.r[j];
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) w[t][k] = st_team[3 * (t * LPR + lane) + k];
+      asm volatile("" ::: "memory");
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) w[t][k] = use.w[t][k];
+    }
+    fetch(fill, n2, tr2);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int g = tr * 4 * LPR + t * LPR + lane;
+      if (g < G) {
+        const float d = q3_group_dot(w[t][0], w[t][1], w[t][2], xq + g, G, ma, mb);
+        const float sc = (float)bits<_Float16>((uint16_t)use.s[t]);
+        acc = __builtin_fmaf(sc, d - corr[g], acc);
       }
     }
-    acc = team_sum<LPR>(acc);
-    if (lane == 0) Y[n] = bits<uint16_t>((_Float16)acc);
+    if (tr == T - 1) {
+      acc = team_sum<LPR>(acc);
+      if (lane == 0) Y[n] = bits<uint16_t>((_Float16)acc);
+      acc = 0.f;
+    }
+    n = n2;
+    tr = tr2;
+  };
+  Trip other;
+  while (n < N) {
+    step(cur, other);
+    if (n >= N) break;
+    step(other, cur);
   }
 }
 
-template <int LPR>
-hipError_t launch_q3_lpr(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
-                         const uint16_t* X, uint16_t* Y, int64_t N, int64_t K, hipStream_t s) {
+template <int LPR, bool STAGED>
+hipError_t launch_q3_kern(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
+                          const uint16_t* X, uint16_t* Y, int64_t N, int64_t K, int64_t blocks,
+                          hipStream_t s) {
   const int64_t G = K / 32;
-  const size_t lds = (size_t)G * 64 + (size_t)G * sizeof(float);
-  auto kern = k_gemv_q3<LPR>;
+  const size_t lds =
+      (size_t)G * 64 + (size_t)(G + 3) / 4 * 16 + (STAGED ? (kBlock / 64) * 3072 : 0);
+  auto kern = k_gemv_q3<LPR, STAGED>;
   if (lds > 65536)
     if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds))
       return e;
-  const int64_t rows_per_block = kBlock / LPR;
-  int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
-  if (blocks > (int64_t)d.cus * 8) blocks = (int64_t)d.cus * 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBlock), lds, s,
-                     reinterpret_cast<const uint4*>(W), S, reinterpret_cast<const uint4*>(X), Y,
-                     (int)N, (int)K);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBlock), lds, s, W, S,
+                     reinterpret_cast<const uint4*>(X), Y, (int)N, (int)K);
   return hipGetLastError();
 }
 
-// K % 128 == 0, W 16-byte and S 8-byte aligned.  Lanes per row: a power of two
-// with at most four trips of four groups per lane.
+// staged < 0: the staged loads once a team has at least eight trips (A/B on one
+// GPU: a 262144 x 3072 GEMV 64.8 -> 59.5 us staged; qkv- and LM-head-sized ones,
+// one or two rows per team, 7.6 -> 8.5 us).
+template <int LPR>
+hipError_t launch_q3_lpr(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
+                         const uint16_t* X, uint16_t* Y, int64_t N, int64_t K, int staged,
+                         hipStream_t s) {
+  const int64_t G = K / 32;
+  const int64_t rows_per_block = kBlock / LPR;
+  int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
+  if (blocks > (int64_t)d.cus * 8) blocks = (int64_t)d.cus * 8;
+  const int64_t teams = blocks * rows_per_block;
+  const int64_t trips = (N + teams - 1) / teams * ((G + 4 * LPR - 1) / (4 * LPR));
+  if (staged > 0 || (staged < 0 && trips >= 8))
+    return launch_q3_kern<LPR, true>(d, W, S, X, Y, N, K, blocks, s);
+  return launch_q3_kern<LPR, false>(d, W, S, X, Y, N, K, blocks, s);
+}
+
+// Lanes per row: a power of two with at most four trips per row.
 hipError_t launch_q3(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
-                     const uint16_t* X, uint16_t* Y, int64_t N, int64_t K, hipStream_t s) {
-  const int64_t Q = K / 128;
-  if (Q <= 16) return launch_q3_lpr<4>(d, W, S, X, Y, N, K, s);
-  if (Q <= 32) return launch_q3_lpr<8>(d, W, S, X, Y, N, K, s);
-  if (Q <= 64) return launch_q3_lpr<16>(d, W, S, X, Y, N, K, s);
-  if (Q <= 128) return launch_q3_lpr<32>(d, W, S, X, Y, N, K, s);
-  return launch_q3_lpr<64>(d, W, S, X, Y, N, K, s);
+                     const uint16_t* X, uint16_t* Y, int64_t N, int64_t K, int staged,
+                     hipStream_t s) {
+  const int64_t G = K / 32;
+  if (G <= 64) return launch_q3_lpr<4>(d, W, S, X, Y, N, K, staged, s);
+  if (G <= 128) return launch_q3_lpr<8>(d, W, S, X, Y, N, K, staged, s);
+  if (G <= 256) return launch_q3_lpr<16>(d, W, S, X, Y, N, K, staged, s);
+  if (G <= 512) return launch_q3_lpr<32>(d, W, S, X, Y, N, K, staged, s);
+  return launch_q3_lpr<64>(d, W, S, X, Y, N, K, staged, s);
 }
 
 template <int F, int LPR>
@@ -340,16 +428,19 @@ hipError_t launch_fmt(const DeviceInfo& d, const uint32_t* W, const void* S, con
 
 }  // namespace
 
+hipError_t launch_gemv_q3(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
+                          const uint16_t* X, uint16_t* Y, int64_t N, int64_t K, int staged,
+                          hipStream_t s) {
+  return launch_q3(d, W, S, X, Y, N, K, staged, s);
+}
+
 hipError_t launch_gemv_format(const DeviceInfo& d, int format, const uint32_t* W, const void* S,
                               const uint16_t* B, const void* X, void* Y, int64_t N, int64_t K,
                               hipStream_t s) {
   switch (format) {
     case kQ3:
-      if (K % 128 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0 &&
-          reinterpret_cast<uintptr_t>(S) % 8 == 0)
-        return launch_q3(d, W, static_cast<const uint16_t*>(S), static_cast<const uint16_t*>(X),
-                         static_cast<uint16_t*>(Y), N, K, s);
-      return launch_fmt<kQ3>(d, W, S, B, X, Y, N, K, s);
+      return launch_q3(d, W, static_cast<const uint16_t*>(S), static_cast<const uint16_t*>(X),
+                       static_cast<uint16_t*>(Y), N, K, -1, s);
     case kQ4F32: return launch_fmt<kQ4F32>(d, W, S, B, X, Y, N, K, s);
     default: return launch_fmt<kAF4>(d, W, S, B, X, Y, N, K, s);
   }

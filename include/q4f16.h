@@ -263,8 +263,15 @@ Q4_API int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_s
 #define Q4_FMT_Q3F16_1 1u
 #define Q4_FMT_Q4F32_1 2u
 #define Q4_FMT_AF4_G64 3u
+/* OR-ed into the format of a q3f16_1 call: load the words as 16-byte pieces
+ * through an LDS stage, or as one 12-byte load per group.  Without either, the
+ * first is taken when each team of lanes has at least eight trips of its rows
+ * (large matrices), the second otherwise.  Results are bitwise the same. */
+#define Q4_FMT_LOAD_STAGED 0x100u
+#define Q4_FMT_LOAD_DIRECT 0x200u
 
-/* q4_gemv_format: y = W x (M = 1) for a format variant, fp32 accumulation, fp16
+/* q4_gemv_format: y = W x (M = 1) for a format variant (one of Q4_FMT_*, for
+ * q3f16_1 optionally with one Q4_FMT_LOAD_* bit), fp32 accumulation, fp16
  * outputs rounded to nearest even (fp32 outputs for Q4_FMT_Q4F32_1).  biases: NULL
  * except for Q4_FMT_AF4_G64.  32 <= K <= 32768, K % 32 == 0 (% 64 for affine);
  * words and x 16-byte aligned (words 4-byte for q3f16_1), the rest aligned to

@@ -78,16 +78,58 @@ def test_format_gemv_matches_oracle(fmt, N, K):
     assert err.max() <= tol, (err.max(), tol)
 
 
-@pytest.mark.parametrize("N,K", [(257, 128 * 37), (64, 32768), (5, 128), (700, 128 * 20)])
-def test_q3_vector_path_shapes(N, K):
-    """q3f16_1 with K % 128 == 0 takes the four-groups-per-lane kernel: several
-    trips per lane, lanes left idle in the last trip, and the largest K."""
-    test_format_gemv_matches_oracle("q3f16_1", N, K)
+@pytest.mark.parametrize("load", [0, q4.FMT_LOAD_STAGED, q4.FMT_LOAD_DIRECT])
+@pytest.mark.parametrize("N,K", [(257, 128 * 37), (64, 32768), (5, 128), (700, 128 * 20),
+                                 (1000, 192), (3000, 3072)])
+def test_q3_shapes_both_loads(N, K, load):
+    """q3f16_1 through either way of loading the words: several trips per row,
+    lanes left idle in the last trip, group counts not a multiple of 4, a row
+    count that leaves most of the first wave's rows past the matrix, the largest
+    K; both ways give the same bits."""
+    words, scales, _, x = make("q3f16_1", N, K, "load")
+    args = (to_dev(words), to_dev(scales), to_dev(x), K)
+    y = q4.q4_gemv_format(q4.FMT_Q3F16_1 | load, *args)
+    other = q4.FMT_LOAD_DIRECT if load == q4.FMT_LOAD_STAGED else q4.FMT_LOAD_STAGED
+    y2 = q4.q4_gemv_format(q4.FMT_Q3F16_1 | other, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    rows = np.arange(N) if N <= 4096 else np.unique(np.linspace(0, N - 1, 2048).astype(np.int64))
+    ref, norms = oracle.gemv_format("q3f16_1", words, scales, None, x, K, rows=rows)
+    got = half_f64(host_half(y))[rows]
+    assert np.abs(got - ref).max() <= 2e-3 * oracle.vec_norm(x) * norms.max()
 
 
-def test_q3_misaligned_words_take_the_generic_path():
-    """Words 4-byte but not 16-byte aligned: same results through the per-group
-    decode."""
+def test_q3_large_takes_the_stage_by_default():
+    """Enough rows that every team has eight trips (K = 32768, four trips a row):
+    the default choice matches the forced ways and the oracle on sampled rows."""
+    N, K = 8300, 32768
+    words, scales, _, x = make("q3f16_1", N, K, "big")
+    args = (to_dev(words), to_dev(scales), to_dev(x), K)
+    ys = [q4.q4_gemv_format(q4.FMT_Q3F16_1 | load, *args)
+          for load in (0, q4.FMT_LOAD_STAGED, q4.FMT_LOAD_DIRECT)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
+    rows = np.unique(np.linspace(0, N - 1, 1024).astype(np.int64))
+    ref, norms = oracle.gemv_format("q3f16_1", words, scales, None, x, K, rows=rows)
+    got = half_f64(host_half(ys[0]))[rows]
+    assert np.abs(got - ref).max() <= 2e-3 * oracle.vec_norm(x) * norms.max()
+
+
+def test_format_load_bits_rejected_off_q3():
+    x = torch.zeros(64, dtype=torch.float16, device="cuda")
+    w = torch.zeros(4, 8, dtype=torch.int32, device="cuda")
+    s = torch.zeros(4, 2, dtype=torch.float16, device="cuda")
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemv_format(q4.FMT_AF4_G64 | q4.FMT_LOAD_STAGED, w, s, x, 64, biases=s)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_gemv_format(q4.FMT_Q3F16_1 | q4.FMT_LOAD_STAGED | q4.FMT_LOAD_DIRECT,
+                          w[:, :6], s, x, 64)
+
+
+def test_q3_words_4_byte_aligned():
+    """Words 4-byte but not 16-byte aligned (the kernel's 12-byte loads need
+    no more): the same results."""
     N, K = 300, 1024
     words, scales, _, x = make("q3f16_1", N, K, "mis")
     flat = torch.zeros(N * (K // 32) * 3 + 4, dtype=torch.int32, device="cuda")
