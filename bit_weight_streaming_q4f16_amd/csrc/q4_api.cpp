@@ -631,13 +631,18 @@ int q4_gemv_format(uint32_t format, const uint32_t* words, const void* scales,
   const q4::DeviceInfo* d = q4::device_info();
   if (!d) return fail(Q4_ERR_DEVICE, "q4_gemv_format: no HIP device");
   const int staged = load == Q4_FMT_LOAD_STAGED ? 1 : load == Q4_FMT_LOAD_DIRECT ? 0 : -1;
-  hipError_t e =
-      format == Q4_FMT_Q3F16_1
-          ? q4::launch_gemv_q3(*d, words, static_cast<const uint16_t*>(scales),
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (format == Q4_FMT_Q3F16_1)
+    e = q4::launch_gemv_q3(*d, words, static_cast<const uint16_t*>(scales),
+                           static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), N, K,
+                           staged, st);
+  else if (affine)
+    e = q4::launch_gemv_affine(*d, words, static_cast<const uint16_t*>(scales), biases,
                                static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), N, K,
-                               staged, static_cast<hipStream_t>(stream))
-          : q4::launch_gemv_format(*d, (int)format, words, scales, biases, x, y, N, K,
-                                   static_cast<hipStream_t>(stream));
+                               st);
+  else
+    e = q4::launch_gemv_format(*d, (int)format, words, scales, biases, x, y, N, K, st);
   return e == hipSuccess ? ok() : device_error(e, "q4_gemv_format");
 }
 

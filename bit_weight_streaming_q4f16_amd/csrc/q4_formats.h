@@ -1,4 +1,4 @@
-// The q3f16_1 GEMV with its loading way chosen by the caller (q4_formats.hip).
+// Format-variant GEMVs beside q4f16_1 that the entry point calls directly.
 #pragma once
 
 #include "q4_internal.h"
@@ -11,5 +11,11 @@ namespace q4 {
 hipError_t launch_gemv_q3(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
                           const uint16_t* X, uint16_t* Y, int64_t N, int64_t K, int staged,
                           hipStream_t s);
+
+// y = W x at M = 1 in the MLX affine 4-bit format, group 64 (q4_gemv.hip: the
+// q4f16_1 GEMV with a scale and a bias per two of its groups).  K <= 32768.
+hipError_t launch_gemv_affine(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
+                              const uint16_t* B, const uint16_t* X, uint16_t* Y, int64_t N,
+                              int64_t K, hipStream_t s);
 
 }  // namespace q4

@@ -1,17 +1,14 @@
-// GEMV for the format variants beside q4f16_1 (everything-webgpu AI.md,
-// quantization table; Zero TVM documentation, the MLX affine checkpoints), at
-// M = 1, on the skeleton of the q4f16_1 kernels: a team of lanes per row, x
-// staged once per workgroup in LDS, a DPP/lane-swap reduction.  Only the decode
-// and the load pattern differ:
+// GEMV for format variants beside q4f16_1 (everything-webgpu AI.md,
+// quantization table), at M = 1, on the skeleton of the q4f16_1 kernels: a team
+// of lanes per row, x staged once per workgroup in LDS, a DPP/lane-swap
+// reduction.  Only the decode and the load pattern differ:
 //   q3f16_1: a group is three words (12 bytes) holding 32 3-bit codes as one
 //     96-bit value; weight = (q - 3) * s, s fp16 per 32 (k_gemv_q3).
-//   q4f32_1: q4f16_1's words with fp32 scales; x and y fp32.
-//   af4g64 (MLX affine): q4f16_1's nibble order, fp16 scale s and bias b per 64
-//     weights; weight = s * q + b.
-// For the last two (k_gemv_fmt) a lane forms sum(q * x) per group in fp32 (codes
-// converted exactly), and the zero point or bias enters through the group's sum
-// of x, staged beside x: (q - z) * s summed = s * (sum q x - z * sum x);
-// s * q + b summed = s * sum q x + b * sum x.
+//   q4f32_1: q4f16_1's words with fp32 scales; x and y fp32 (k_gemv_fmt): a lane
+//     forms sum(q * x) per group in fp32 (codes converted exactly), and the zero
+//     point enters through the group's sum of x, staged beside x:
+//     (q - 7) * s summed = s * (sum q x - 7 sum x).
+// The MLX affine format runs on the q4f16_1 GEMV itself (q4_gemv.hip).
 #include "q4_formats.h"
 
 namespace q4 {
@@ -46,12 +43,11 @@ __device__ __forceinline__ float team_sum(float v) {
   return v;
 }
 
-enum : int { kQ3 = 1, kQ4F32 = 2, kAF4 = 3 };
+enum : int { kQ3 = 1, kQ4F32 = 2 };
 
 // Weights per group and words per group of a format.
 template <int F> struct Fmt;
 template <> struct Fmt<kQ4F32> { static constexpr int kGroup = 32, kWords = 4; };
-template <> struct Fmt<kAF4> { static constexpr int kGroup = 64, kWords = 8; };
 
 // code i (0 .. kGroup-1) of a group's words
 template <int F>
@@ -82,7 +78,6 @@ __device__ __forceinline__ float group_qx(const uint32_t (&w)[Fmt<F>::kWords],
 template <int F, int LPR>
 __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict__ W,
                                                      const void* __restrict__ Sv,
-                                                     const uint16_t* __restrict__ Bv,
                                                      const void* __restrict__ Xv,
                                                      void* __restrict__ Yv, int N, int K) {
   constexpr int GS = Fmt<F>::kGroup, NW = Fmt<F>::kWords;
@@ -128,14 +123,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict_
       }
       const float qx = group_qx<F>(w, xs4, G, g);
       const int64_t gi = (int64_t)n * G + g;
-      if constexpr (F == kQ4F32) {
-        const float s = static_cast<const float*>(Sv)[gi];
-        acc = __builtin_fmaf(s, qx - 7.f * gsum[g], acc);
-      } else {
-        const float s = (float)bits<_Float16>(static_cast<const uint16_t*>(Sv)[gi]);
-        const float b = (float)bits<_Float16>(Bv[gi]);
-        acc = __builtin_fmaf(s, qx, __builtin_fmaf(b, gsum[g], acc));
-      }
+      const float s = static_cast<const float*>(Sv)[gi];
+      acc = __builtin_fmaf(s, qx - 7.f * gsum[g], acc);
     }
     acc = team_sum<LPR>(acc);
     if (lane == 0) {
@@ -396,9 +385,8 @@ hipError_t launch_q3(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
 }
 
 template <int F, int LPR>
-hipError_t launch_fmt_lpr(const DeviceInfo& d, const uint32_t* W, const void* S,
-                          const uint16_t* B, const void* X, void* Y, int64_t N, int64_t K,
-                          hipStream_t s) {
+hipError_t launch_fmt_lpr(const DeviceInfo& d, const uint32_t* W, const void* S, const void* X,
+                          void* Y, int64_t N, int64_t K, hipStream_t s) {
   const int G = (int)(K / Fmt<F>::kGroup);
   const size_t lds = (size_t)(K + G) * sizeof(float);
   auto kern = k_gemv_fmt<F, LPR>;
@@ -409,21 +397,21 @@ hipError_t launch_fmt_lpr(const DeviceInfo& d, const uint32_t* W, const void* S,
   const int64_t rows_per_block = kBlock / LPR;
   int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
   if (blocks > (int64_t)d.cus * 8) blocks = (int64_t)d.cus * 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBlock), lds, s, W, S, B, X, Y, (int)N,
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBlock), lds, s, W, S, X, Y, (int)N,
                      (int)K);
   return hipGetLastError();
 }
 
 template <int F>
-hipError_t launch_fmt(const DeviceInfo& d, const uint32_t* W, const void* S, const uint16_t* B,
-                      const void* X, void* Y, int64_t N, int64_t K, hipStream_t s) {
+hipError_t launch_fmt(const DeviceInfo& d, const uint32_t* W, const void* S, const void* X,
+                      void* Y, int64_t N, int64_t K, hipStream_t s) {
   // lanes per row: a power of two with at most four groups per lane
   const int64_t G = K / Fmt<F>::kGroup;
-  if (G <= 16) return launch_fmt_lpr<F, 4>(d, W, S, B, X, Y, N, K, s);
-  if (G <= 32) return launch_fmt_lpr<F, 8>(d, W, S, B, X, Y, N, K, s);
-  if (G <= 64) return launch_fmt_lpr<F, 16>(d, W, S, B, X, Y, N, K, s);
-  if (G <= 128) return launch_fmt_lpr<F, 32>(d, W, S, B, X, Y, N, K, s);
-  return launch_fmt_lpr<F, 64>(d, W, S, B, X, Y, N, K, s);
+  if (G <= 16) return launch_fmt_lpr<F, 4>(d, W, S, X, Y, N, K, s);
+  if (G <= 32) return launch_fmt_lpr<F, 8>(d, W, S, X, Y, N, K, s);
+  if (G <= 64) return launch_fmt_lpr<F, 16>(d, W, S, X, Y, N, K, s);
+  if (G <= 128) return launch_fmt_lpr<F, 32>(d, W, S, X, Y, N, K, s);
+  return launch_fmt_lpr<F, 64>(d, W, S, X, Y, N, K, s);
 }
 
 }  // namespace
@@ -441,8 +429,11 @@ hipError_t launch_gemv_format(const DeviceInfo& d, int format, const uint32_t* W
     case kQ3:
       return launch_q3(d, W, static_cast<const uint16_t*>(S), static_cast<const uint16_t*>(X),
                        static_cast<uint16_t*>(Y), N, K, -1, s);
-    case kQ4F32: return launch_fmt<kQ4F32>(d, W, S, B, X, Y, N, K, s);
-    default: return launch_fmt<kAF4>(d, W, S, B, X, Y, N, K, s);
+    case kQ4F32: return launch_fmt<kQ4F32>(d, W, S, X, Y, N, K, s);
+    default:
+      return launch_gemv_affine(d, W, static_cast<const uint16_t*>(S), B,
+                                static_cast<const uint16_t*>(X), static_cast<uint16_t*>(Y), N, K,
+                                s);
   }
 }
 

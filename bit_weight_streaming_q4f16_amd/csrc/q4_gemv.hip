@@ -23,6 +23,7 @@
 //    them in ascending slice order, so results are deterministic;
 //  * small M (2..8) uses MFMA: v_mfma_f32_16x16x32_f16 covers 16 rows by one
 //    32-weight group, so the per-group scale is applied exactly to its result.
+#include "q4_formats.h"
 #include "q4_fused.h"
 
 namespace q4 {
@@ -128,17 +129,22 @@ __device__ __forceinline__ int slice_begin(int G, int splits, int s) {
 //
 // Modes: kPlain writes y (or split-K partials); kGlu (q4_fused.h) computes rows
 // i and F + i (F = N, the matrix has 2N rows) and writes silu_mul_h of the two
-// rounded results.
-enum : int { kPlain = 0, kGlu = 1 };
+// rounded results; kAffine (q4_formats.h, MLX affine 4-bit: the same nibble
+// layout, one fp16 scale s and bias b per 64 weights, i.e. per two 16-byte
+// groups) adds s * sum((q - 7) x) + (b + 7 s) * sum(x) per 32 weights, the sums
+// of x staged beside x.  kAffine needs one slice.
+enum : int { kPlain = 0, kGlu = 1, kAffine = 2 };
 
 template <int LPR, int UNR, int MODE>
 __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
                                                     const uint16_t* __restrict__ S,
+                                                    const uint16_t* __restrict__ Bq,
                                                     const uint4* __restrict__ X,
                                                     uint16_t* __restrict__ Y,
                                                     float* __restrict__ P, int N, int G,
                                                     int splits) {
   extern __shared__ uint4 xs[];
+  constexpr bool kAff = MODE == kAffine;
   const int split = blockIdx.y;
   const int g0 = slice_begin(G, splits, split);
   const int gc = slice_begin(G, splits, split + 1) - g0;
@@ -147,19 +153,20 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
   const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
   constexpr int R = MODE == kGlu ? 2 : 1;    // rows per team and output
   uint4 wv[R][UNR];
-  uint16_t sv[R][UNR];
+  uint16_t sv[R][UNR], bv[R][UNR];
   auto issue = [&](int n, int t0) {          // trip t0 of output n
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       const int64_t row = n + (int64_t)q * N;
       const uint4* wr = W + row * G + g0;
-      const uint16_t* sr = S + row * G + g0;
+      const uint16_t* sr = kAff ? S + row * (G / 2) : S + row * G + g0;
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         int g = t0 + u * LPR + lane;
         g = g < gc ? g : gc - 1;
         wv[q][u] = load_nt(wr + g);
-        sv[q][u] = sr[g];
+        sv[q][u] = sr[kAff ? g >> 1 : g];
+        if constexpr (kAff) bv[q][u] = Bq[row * (G / 2) + (g >> 1)];
       }
     }
   };
@@ -168,6 +175,20 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
   for (int i = threadIdx.x; i < 4 * gc; i += kBlock) {
     const int g = i >> 2, j = i & 3;
     xs[j * gc + g] = pair_order(X[(int64_t)(g0 + g) * 4 + j]);
+  }
+  float* const xsum = reinterpret_cast<float*>(xs + 4 * gc);   // kAffine: sum of x per group
+  if constexpr (kAff) {
+    for (int g = threadIdx.x; g < gc; g += kBlock) {
+      float t = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const uint4 v = X[(int64_t)(g0 + g) * 4 + j];
+        const uint32_t hw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          t += half_to_float((uint16_t)(hw[i] & 0xFFFFu)) + half_to_float((uint16_t)(hw[i] >> 16));
+      }
+      xsum[g] = t;
+    }
   }
   __syncthreads();
 
@@ -184,7 +205,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
           const int graw = t0 + u * LPR + lane;
           const int g = graw < gc ? graw : gc - 1;
           const float p = group_dot(wv[q][u], xs, gc, g);
-          const float t = __builtin_fmaf(p, half_to_float(sv[q][u]), acc[q]);
+          const float sc = half_to_float(sv[q][u]);
+          float t = __builtin_fmaf(p, sc, acc[q]);
+          if constexpr (kAff)
+            t = __builtin_fmaf(__builtin_fmaf(7.f, sc, half_to_float(bv[q][u])), xsum[g], t);
           acc[q] = graw < gc ? t : acc[q];
         }
       }
@@ -327,7 +351,7 @@ int choose_lpr(int64_t G) {
 // a.N: the outputs (kGlu: half the matrix's rows)
 template <int LPR, int UNR, int MODE>
 hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
-                         hipStream_t s) {
+                         hipStream_t s, const uint16_t* biases) {
   const int64_t G = a.K / 32;
   const int64_t teams_per_block = kBlock / LPR;
   int64_t blocks = (a.N + teams_per_block - 1) / teams_per_block;
@@ -337,11 +361,11 @@ hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, cons
   const int64_t cap = (int64_t)d.cus * 8;
   if (blocks > cap) blocks = cap;
   const int64_t gmax = (G + p.splits - 1) / p.splits;
-  const size_t lds = (size_t)gmax * 64;
+  const size_t lds = (size_t)gmax * (MODE == kAffine ? 68 : 64);
   const dim3 grid((unsigned)blocks, (unsigned)p.splits);
   if (hipError_t e = allow_lds(k_gemv_m1<LPR, UNR, MODE>, lds)) return e;
   hipLaunchKernelGGL((k_gemv_m1<LPR, UNR, MODE>), grid, dim3(kBlock), lds, s,
-                     reinterpret_cast<const uint4*>(a.words), a.scales,
+                     reinterpret_cast<const uint4*>(a.words), a.scales, biases,
                      reinterpret_cast<const uint4*>(a.x), a.y, part, (int)a.N, (int)G, p.splits);
   return hipGetLastError();
 }
@@ -350,23 +374,24 @@ hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, cons
 // from an explicit split count, take several trips)
 template <int LPR, int MODE>
 hipError_t launch_m1(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
-                     hipStream_t s) {
+                     hipStream_t s, const uint16_t* biases) {
   const int64_t G = a.K / 32;
   const int64_t per_lane = ((G + p.splits - 1) / p.splits + LPR - 1) / LPR;
-  if (per_lane <= 2) return launch_m1_unr<LPR, 2, MODE>(a, p, part, d, s);
-  if (per_lane <= 4) return launch_m1_unr<LPR, 4, MODE>(a, p, part, d, s);
-  return launch_m1_unr<LPR, 8, MODE>(a, p, part, d, s);
+  if (per_lane <= 2) return launch_m1_unr<LPR, 2, MODE>(a, p, part, d, s, biases);
+  if (per_lane <= 4) return launch_m1_unr<LPR, 4, MODE>(a, p, part, d, s, biases);
+  return launch_m1_unr<LPR, 8, MODE>(a, p, part, d, s, biases);
 }
 
+// biases: kAffine only
 template <int MODE>
 hipError_t launch_m1_lpr(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
-                         hipStream_t s) {
+                         hipStream_t s, const uint16_t* biases = nullptr) {
   switch (p.lanes_per_row) {
-    case 4: return launch_m1<4, MODE>(a, p, part, d, s);
-    case 8: return launch_m1<8, MODE>(a, p, part, d, s);
-    case 16: return launch_m1<16, MODE>(a, p, part, d, s);
-    case 32: return launch_m1<32, MODE>(a, p, part, d, s);
-    default: return launch_m1<64, MODE>(a, p, part, d, s);
+    case 4: return launch_m1<4, MODE>(a, p, part, d, s, biases);
+    case 8: return launch_m1<8, MODE>(a, p, part, d, s, biases);
+    case 16: return launch_m1<16, MODE>(a, p, part, d, s, biases);
+    case 32: return launch_m1<32, MODE>(a, p, part, d, s, biases);
+    default: return launch_m1<64, MODE>(a, p, part, d, s, biases);
   }
 }
 
@@ -441,6 +466,15 @@ hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p
   hipLaunchKernelGGL(k_combine, dim3((unsigned)blocks), dim3(kBlock), 0, s, part, out, count,
                      p.splits);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_affine(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
+                              const uint16_t* B, const uint16_t* X, uint16_t* Y, int64_t N,
+                              int64_t K, hipStream_t s) {
+  const GemvArgs a{W, S, X, Y, 1, N, K};
+  const GemvPlan p = plan_splits(d, 1, N, K, 1);
+  if ((size_t)(K / 32) * 68 > d.lds_per_block) return hipErrorInvalidValue;
+  return launch_m1_lpr<kAffine>(a, p, nullptr, d, s, B);
 }
 
 hipError_t launch_gemv_glu(const DeviceInfo& d, const uint32_t* words, const uint16_t* scales,
