@@ -49,25 +49,30 @@ enum : int { kQ3 = 1, kQ4F32 = 2 };
 template <int F> struct Fmt;
 template <> struct Fmt<kQ4F32> { static constexpr int kGroup = 32, kWords = 4; };
 
-// code i (0 .. kGroup-1) of a group's words
-template <int F>
-__device__ __forceinline__ float code_at(const uint32_t (&w)[Fmt<F>::kWords], int i) {
-  return (float)((w[i / 8] >> (4 * (i % 8))) & 0xFu);
-}
-
 // sum over group g of q * x; x from LDS planes xs4[j][g] = x[GS*g + 4j .. +3], so
-// the lanes of a team (consecutive g) read consecutive 16-byte entries
+// the lanes of a team (consecutive g) read consecutive 16-byte entries.  A
+// word's even and odd nibbles are split into the bytes of two words, so that
+// each code is converted by one byte-to-float instruction.
 template <int F>
 __device__ __forceinline__ float group_qx(const uint32_t (&w)[Fmt<F>::kWords],
                                           const float4* xs4, int G, int g) {
   float a = 0.f, b = 0.f;
 #pragma unroll
-  for (int j = 0; j < Fmt<F>::kGroup / 4; ++j) {
-    const float4 xv = xs4[j * G + g];
-    a = __builtin_fmaf(code_at<F>(w, 4 * j), xv.x, a);
-    b = __builtin_fmaf(code_at<F>(w, 4 * j + 1), xv.y, b);
-    a = __builtin_fmaf(code_at<F>(w, 4 * j + 2), xv.z, a);
-    b = __builtin_fmaf(code_at<F>(w, 4 * j + 3), xv.w, b);
+  for (int k = 0; k < Fmt<F>::kWords; ++k) {
+    uint32_t ev = w[k] & 0x0F0F0F0Fu;          // codes 8k, 8k+2, 8k+4, 8k+6
+    uint32_t od = (w[k] >> 4) & 0x0F0F0F0Fu;   // codes 8k+1, 8k+3, 8k+5, 8k+7
+    // hide the known zero bits: with them the compiler turns a byte's shift and
+    // mask into a 4-bit extract plus a conversion, not one v_cvt_f32_ubyteN
+    asm volatile("" : "+v"(ev), "+v"(od));
+    const float4 x0 = xs4[(2 * k) * G + g], x1 = xs4[(2 * k + 1) * G + g];
+    a = __builtin_fmaf((float)(ev & 0xFFu), x0.x, a);
+    b = __builtin_fmaf((float)(od & 0xFFu), x0.y, b);
+    a = __builtin_fmaf((float)((ev >> 8) & 0xFFu), x0.z, a);
+    b = __builtin_fmaf((float)((od >> 8) & 0xFFu), x0.w, b);
+    a = __builtin_fmaf((float)((ev >> 16) & 0xFFu), x1.x, a);
+    b = __builtin_fmaf((float)((od >> 16) & 0xFFu), x1.y, b);
+    a = __builtin_fmaf((float)(ev >> 24), x1.z, a);
+    b = __builtin_fmaf((float)(od >> 24), x1.w, b);
   }
   return a + b;
 }

@@ -129,10 +129,11 @@ __device__ __forceinline__ int slice_begin(int G, int splits, int s) {
 //
 // Modes: kPlain writes y (or split-K partials); kGlu (q4_fused.h) computes rows
 // i and F + i (F = N, the matrix has 2N rows) and writes silu_mul_h of the two
-// rounded results; kAffine (q4_formats.h, MLX affine 4-bit: the same nibble
-// layout, one fp16 scale s and bias b per 64 weights, i.e. per two 16-byte
-// groups) adds s * sum((q - 7) x) + (b + 7 s) * sum(x) per 32 weights, the sums
-// of x staged beside x.  kAffine needs one slice.
+// rounded results; kAffine (q4_formats.h; the MLX affine 4-bit checkpoints of
+// the Zero TVM documentation: the same nibble layout, one fp16 scale s and bias
+// b per 64 weights, i.e. per two 16-byte groups) adds s * sum((q - 7) x) +
+// (b + 7 s) * sum(x) per 32 weights, the sums of x staged beside x.  kAffine
+// needs one slice.
 enum : int { kPlain = 0, kGlu = 1, kAffine = 2 };
 
 template <int LPR, int UNR, int MODE>
