@@ -372,15 +372,23 @@ hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, cons
 }
 
 // groups per lane per trip: the whole slice in one trip up to 8 (larger slices,
-// from an explicit split count, take several trips)
+// from an explicit split count, take several trips), with no group beyond the
+// slice up to 6: a lane's groups past the slice are loaded and computed before
+// being discarded, and K = 3072 (96 groups, 32 lanes) at 4 per lane spent a
+// quarter of every lane's work there (262144 x 3072: 91.9 -> 72.1 us at 3)
 template <int LPR, int MODE>
 hipError_t launch_m1(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
                      hipStream_t s, const uint16_t* biases) {
   const int64_t G = a.K / 32;
   const int64_t per_lane = ((G + p.splits - 1) / p.splits + LPR - 1) / LPR;
-  if (per_lane <= 2) return launch_m1_unr<LPR, 2, MODE>(a, p, part, d, s, biases);
-  if (per_lane <= 4) return launch_m1_unr<LPR, 4, MODE>(a, p, part, d, s, biases);
-  return launch_m1_unr<LPR, 8, MODE>(a, p, part, d, s, biases);
+  switch (per_lane) {
+    case 0: case 1: case 2: return launch_m1_unr<LPR, 2, MODE>(a, p, part, d, s, biases);
+    case 3: return launch_m1_unr<LPR, 3, MODE>(a, p, part, d, s, biases);
+    case 4: return launch_m1_unr<LPR, 4, MODE>(a, p, part, d, s, biases);
+    case 5: return launch_m1_unr<LPR, 5, MODE>(a, p, part, d, s, biases);
+    case 6: return launch_m1_unr<LPR, 6, MODE>(a, p, part, d, s, biases);
+    default: return launch_m1_unr<LPR, 8, MODE>(a, p, part, d, s, biases);
+  }
 }
 
 // biases: kAffine only
