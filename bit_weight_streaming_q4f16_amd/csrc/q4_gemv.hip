@@ -230,8 +230,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
 }
 
 // ------------------------------------------------------------- M in 2..8 ---
-// One workgroup = 16 rows x one K slice; its four waves take interleaved chunks
-// of four groups.  In a chunk, lane (c = lane/16, r = lane%16) loads group c of
+// A workgroup stages X once and loops over tiles of 16 rows x one K slice (a
+// workgroup per tile staged X once per 16 rows: at M = 8, K = 2048 that was 32 KB
+// of X per 18 KB of weights); its four waves take interleaved chunks of four
+// groups.  In a chunk, lane (c = lane/16, r = lane%16) loads group c of
 // row r with one dwordx4; a 4x4 exchange among lanes r, r+16, r+32, r+48
 // (permlane32/permlane16 swaps) leaves word c of every group of the chunk in lane
 // (c, r), which is the B-operand layout of v_mfma_f32_16x16x32_f16 (column = row
@@ -267,54 +269,58 @@ __global__ __launch_bounds__(kBlock) void k_gemv_mfma(const uint4* __restrict__ 
   __syncthreads();
 
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, c = l >> 4, r = l & 15;
-  const int n0 = blockIdx.x * 16;
-  const int n = n0 + r < N ? n0 + r : N - 1;
-  const uint4* wr = W + (int64_t)n * G + g0;
-  const uint16_t* sr = S + (int64_t)n * G + g0;
   const bool has_x = r < M;
-  f4_t acc = {0.f, 0.f, 0.f, 0.f};
   const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-  for (int gb = 4 * wave; gb < gc; gb += 16) {
-    const int gl = gb + c < gc ? gb + c : gc - 1;
-    const uint4 wv = load_nt(wr + gl);
-    float s[4];
+  // workgroups loop over tiles of 16 rows, so X is staged once per workgroup, not
+  // once per tile
+  for (int n0 = blockIdx.x * 16; n0 < N; n0 += gridDim.x * 16) {
+    const int n = n0 + r < N ? n0 + r : N - 1;
+    const uint4* wr = W + (int64_t)n * G + g0;
+    const uint16_t* sr = S + (int64_t)n * G + g0;
+    f4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int gb = 4 * wave; gb < gc; gb += 16) {
+      const int gl = gb + c < gc ? gb + c : gc - 1;
+      const uint4 wv = load_nt(wr + gl);
+      float s[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) s[t] = half_to_float(sr[gb + t < gc ? gb + t : gc - 1]);
-    uint32_t v[4] = {wv.x, wv.y, wv.z, wv.w};
-    transpose4(v);
+      for (int t = 0; t < 4; ++t) s[t] = half_to_float(sr[gb + t < gc ? gb + t : gc - 1]);
+      uint32_t v[4] = {wv.x, wv.y, wv.z, wv.w};
+      transpose4(v);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int gt = gb + t < gc ? gb + t : gc - 1;
-      h2_t q[4];
-      dequant_word(v[t], q);
-      const h8_t B = {q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
-      h8_t A = {};
-      if (has_x) A = bits<h8_t>(xs[r * pitch + 4 * gt + c]);
-      const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, zero, 0, 0, 0);
-      if (gb + t < gc) {
+      for (int t = 0; t < 4; ++t) {
+        const int gt = gb + t < gc ? gb + t : gc - 1;
+        h2_t q[4];
+        dequant_word(v[t], q);
+        const h8_t B = {q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+        h8_t A = {};
+        if (has_x) A = bits<h8_t>(xs[r * pitch + 4 * gt + c]);
+        const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, zero, 0, 0, 0);
+        if (gb + t < gc) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(s[t], d[e], acc[e]);
-      }
-    }
-  }
-  // add the four waves' partials in a fixed order
-  if (wave > 0) red[wave - 1][l] = acc;
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 0; w < 3; ++w) acc += red[w][l];
-    if (n0 + r < N) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 4 * c + e;
-        if (m < M) {
-          if (splits == 1)
-            Y[(int64_t)m * N + n0 + r] = float_to_half_rne(acc[e]);
-          else
-            P[((int64_t)split * M + m) * N + n0 + r] = acc[e];
+          for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(s[t], d[e], acc[e]);
         }
       }
     }
+    // add the four waves' partials in a fixed order
+    if (wave > 0) red[wave - 1][l] = acc;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < 3; ++w) acc += red[w][l];
+      if (n0 + r < N) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 4 * c + e;
+          if (m < M) {
+            if (splits == 1)
+              Y[(int64_t)m * N + n0 + r] = float_to_half_rne(acc[e]);
+            else
+              P[((int64_t)split * M + m) * N + n0 + r] = acc[e];
+          }
+        }
+      }
+    }
+    __syncthreads();   // red is reused by the next tile
   }
 }
 
@@ -460,7 +466,13 @@ hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p
     const int64_t G = a.K / 32;
     const int64_t gmax = (G + p.splits - 1) / p.splits;
     const size_t lds = (size_t)a.M * (4 * gmax + 1) * 16;
-    const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)p.splits);
+    // as many workgroups as fit the device at once (LDS bounds them: X is M rows
+    // of the slice), each looping over tiles
+    int64_t tiles = (a.N + 15) / 16;
+    const int64_t per_cu = lds > 0 ? (int64_t)(d.lds_per_block / (lds + 3 * 64 * 16)) : 8;
+    const int64_t cap = (int64_t)d.cus * (per_cu < 1 ? 1 : per_cu > 8 ? 8 : per_cu);
+    if (tiles * p.splits > cap) tiles = (cap + p.splits - 1) / p.splits;
+    const dim3 grid((unsigned)tiles, (unsigned)p.splits);
     if (hipError_t e2 = allow_lds(k_gemv_mfma, lds)) return e2;
     hipLaunchKernelGGL(k_gemv_mfma, grid, dim3(kBlock), lds, s,
                        reinterpret_cast<const uint4*>(a.words), a.scales,
