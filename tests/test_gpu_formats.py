@@ -146,6 +146,13 @@ def test_q3_words_4_byte_aligned():
         assert np.abs(got - ref).max() <= tol
 
 
+@pytest.mark.parametrize("N,K", [(300, 2560), (77, 11264), (5, 64)])
+def test_affine_groups_per_lane(N, K):
+    """The affine format on the q4f16_1 GEMV at row lengths of 5 and 6 groups per
+    lane and at one 64-weight group."""
+    test_format_gemv_matches_oracle("af4g64", N, K)
+
+
 def test_format_weight_bytes():
     assert q4.q4_format_weight_bytes(0, 9216, 3072) == 9216 * 96 * 18
     assert q4.q4_format_weight_bytes(q4.FMT_Q3F16_1, 9216, 3072) == 9216 * 96 * 14

@@ -145,6 +145,15 @@ def test_random_shapes(N, K):
     assert_gemv_close(gemv_gpu(w, s, x), w, s, x, exact=True)
 
 
+@pytest.mark.parametrize("N", [33, 1000])
+@pytest.mark.parametrize("K", [1536, 2560, 5120, 11264])
+def test_groups_per_lane_3_5_6(N, K):
+    """Row lengths whose groups split into exactly 3, 5, 5 and 6 per lane of a
+    row's team (each an instantiation of its own)."""
+    w, s, x = rand_case(N + 3 * K, N, K, neg=True)
+    assert_gemv_close(gemv_gpu(w, s, x), w, s, x, exact=True)
+
+
 def test_subnormal_inputs():
     N, K = 64, 512
     w, s, x = rand_case(5, N, K)
