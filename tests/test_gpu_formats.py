@@ -127,17 +127,18 @@ def test_format_load_bits_rejected_off_q3():
                           w[:, :6], s, x, 64)
 
 
-def test_q3_words_4_byte_aligned():
-    """Words 4-byte but not 16-byte aligned (the kernel's 12-byte loads need
-    no more): the same results."""
+@pytest.mark.parametrize("load", [0, q4.FMT_LOAD_STAGED, q4.FMT_LOAD_DIRECT])
+def test_q3_words_4_byte_aligned(load):
+    """Words 4-byte but not 16-byte aligned (both ways of loading need no
+    more): the same results."""
     N, K = 300, 1024
     words, scales, _, x = make("q3f16_1", N, K, "mis")
     flat = torch.zeros(N * (K // 32) * 3 + 4, dtype=torch.int32, device="cuda")
     view = flat[1:1 + words.size]
     view.copy_(to_dev(words).view(-1).view(torch.int32))
     assert view.data_ptr() % 16 != 0
-    y = q4.q4_gemv_format(q4.FMT_Q3F16_1, view.view(N, -1), to_dev(scales), to_dev(x), K)
-    y2 = q4.q4_gemv_format(q4.FMT_Q3F16_1, to_dev(words), to_dev(scales), to_dev(x), K)
+    y = q4.q4_gemv_format(q4.FMT_Q3F16_1 | load, view.view(N, -1), to_dev(scales), to_dev(x), K)
+    y2 = q4.q4_gemv_format(q4.FMT_Q3F16_1 | load, to_dev(words), to_dev(scales), to_dev(x), K)
     torch.cuda.synchronize()
     ref, norms = oracle.gemv_format("q3f16_1", words, scales, None, x, K, rows=np.arange(N))
     tol = 2e-3 * oracle.vec_norm(x) * norms.max()
