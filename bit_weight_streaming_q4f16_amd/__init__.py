@@ -41,6 +41,7 @@ FMT_Q4F32_1 = 2
 FMT_AF4_G64 = 3
 FMT_LOAD_STAGED = 0x100   # OR-ed into FMT_Q3F16_1: force one way of loading
 FMT_LOAD_DIRECT = 0x200
+MODEL_FACTORED_NORM = 0x1   # q4_model.options: norms folded into the GEMVs they feed
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
           4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED"}
@@ -76,7 +77,7 @@ class ModelDesc(C.Structure):
     """q4_model."""
     _fields_ = [("n_blocks", C.c_int64), ("D", C.c_int64), ("F", C.c_int64), ("V", C.c_int64),
                 ("embed", Weight), ("blocks", C.c_void_p), ("final_norm", C.c_void_p),
-                ("lm_head", Weight), ("eps", C.c_float)]
+                ("lm_head", Weight), ("eps", C.c_float), ("options", C.c_uint32)]
 
 
 def lib_path() -> str:
@@ -364,7 +365,7 @@ class Model:
     embed, lm_head: (words, scales); blocks: sequence of dicts with keys qkv, o,
     gate_up, down ((words, scales) each), attn_norm, ffn_norm (fp16 tensors)."""
 
-    def __init__(self, embed, blocks, final_norm, lm_head, eps: float = 1e-5):
+    def __init__(self, embed, blocks, final_norm, lm_head, eps: float = 1e-5, options: int = 0):
         self._keep = [embed, blocks, final_norm, lm_head]
         blocks = list(blocks)
         self.blocks = (Block * max(len(blocks), 1))()
@@ -377,7 +378,7 @@ class Model:
         V = embed[0].shape[0]
         self.desc = ModelDesc(len(blocks), D, F, V, _weight(embed),
                               C.cast(self.blocks, C.c_void_p).value if blocks else None,
-                              final_norm.data_ptr(), _weight(lm_head), eps)
+                              final_norm.data_ptr(), _weight(lm_head), eps, options)
         self.D, self.F, self.V = D, F, V
 
     def ref(self):

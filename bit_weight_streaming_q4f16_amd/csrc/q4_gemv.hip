@@ -133,8 +133,13 @@ __device__ __forceinline__ int slice_begin(int G, int splits, int s) {
 // the Zero TVM documentation: the same nibble layout, one fp16 scale s and bias
 // b per 64 weights, i.e. per two 16-byte groups) adds s * sum((q - 7) x) +
 // (b + 7 s) * sum(x) per 32 weights, the sums of x staged beside x.  kAffine
-// needs one slice.
-enum : int { kPlain = 0, kGlu = 1, kAffine = 2 };
+// needs one slice.  kPlainNorm and kGluNorm (q4_fused.h) are kPlain and kGlu
+// with the residual add and RMSNorm of their input folded in, factored so that no
+// reduction precedes the staging: x = h * gamma is staged (h = res_in + delta,
+// rounded to fp16 as the RMSNorm kernel rounds it, and written to res_out by
+// workgroup 0), sum(h^2) is formed alongside, and every output is scaled by
+// 1 / sqrt(sum(h^2) / K + eps) before its rounding.  They need one slice.
+enum : int { kPlain = 0, kGlu = 1, kAffine = 2, kPlainNorm = 3, kGluNorm = 4 };
 
 template <int LPR, int UNR, int MODE>
 __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
@@ -143,16 +148,18 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
                                                     const uint4* __restrict__ X,
                                                     uint16_t* __restrict__ Y,
                                                     float* __restrict__ P, int N, int G,
-                                                    int splits) {
+                                                    int splits, NormIn nin) {
   extern __shared__ uint4 xs[];
+  __shared__ float ssw[kBlock / 64];
   constexpr bool kAff = MODE == kAffine;
+  constexpr bool kNin = MODE == kPlainNorm || MODE == kGluNorm;
   const int split = blockIdx.y;
   const int g0 = slice_begin(G, splits, split);
   const int gc = slice_begin(G, splits, split + 1) - g0;
   const int lane = threadIdx.x & (LPR - 1);
   const int team = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) / LPR);
   const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
-  constexpr int R = MODE == kGlu ? 2 : 1;    // rows per team and output
+  constexpr int R = MODE == kGlu || MODE == kGluNorm ? 2 : 1;   // rows per team and output
   uint4 wv[R][UNR];
   uint16_t sv[R][UNR], bv[R][UNR];
   auto issue = [&](int n, int t0) {          // trip t0 of output n
@@ -173,9 +180,30 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
   };
   int n = team;
   if (n < N) issue(n, 0);
+  float ss = 0.f;                                 // kNin: this thread's sum of h^2
   for (int i = threadIdx.x; i < 4 * gc; i += kBlock) {
     const int g = i >> 2, j = i & 3;
-    xs[j * gc + g] = pair_order(X[(int64_t)(g0 + g) * 4 + j]);
+    if constexpr (kNin) {
+      const int64_t e = (int64_t)(g0 + g) * 4 + j;   // x[8e .. 8e + 7]
+      h8_t v = bits<h8_t>(reinterpret_cast<const uint4*>(nin.res_in)[e]);
+      if (nin.delta) v = v + bits<h8_t>(reinterpret_cast<const uint4*>(nin.delta)[e]);
+      if (nin.res_out && blockIdx.x == 0) reinterpret_cast<uint4*>(nin.res_out)[e] = bits<uint4>(v);
+      const h8_t gm = bits<h8_t>(reinterpret_cast<const uint4*>(nin.gamma)[e]);
+      h8_t o;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float f = (float)v[k];
+        ss = __builtin_fmaf(f, f, ss);
+        o[k] = (_Float16)(f * (float)gm[k]);
+      }
+      xs[j * gc + g] = pair_order(bits<uint4>(o));
+    } else {
+      xs[j * gc + g] = pair_order(X[(int64_t)(g0 + g) * 4 + j]);
+    }
+  }
+  if constexpr (kNin) {
+    ss = team_sum<64>(ss);
+    if ((threadIdx.x & 63) == 0) ssw[threadIdx.x >> 6] = ss;
   }
   float* const xsum = reinterpret_cast<float*>(xs + 4 * gc);   // kAffine: sum of x per group
   if constexpr (kAff) {
@@ -192,6 +220,13 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
     }
   }
   __syncthreads();
+  float rs = 1.f;                                 // kNin: 1 / rms of h
+  if constexpr (kNin) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) tot += ssw[w];
+    rs = 1.f / __builtin_sqrtf(tot / (float)(G * 32) + nin.eps);
+  }
 
   for (; n < N; n += nteams) {
     float acc[R];
@@ -220,6 +255,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
     if (lane == 0) {
       if constexpr (MODE == kGlu) {
         Y[n] = bits<uint16_t>(silu_mul_h((_Float16)acc[0], (_Float16)acc[1]));
+      } else if constexpr (MODE == kGluNorm) {
+        Y[n] = bits<uint16_t>(silu_mul_h((_Float16)(acc[0] * rs), (_Float16)(acc[1] * rs)));
+      } else if constexpr (MODE == kPlainNorm) {
+        Y[n] = float_to_half_rne(acc[0] * rs);
       } else if (splits == 1) {
         Y[n] = float_to_half_rne(acc[0]);
       } else {
@@ -358,7 +397,7 @@ int choose_lpr(int64_t G) {
 // a.N: the outputs (kGlu: half the matrix's rows)
 template <int LPR, int UNR, int MODE>
 hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
-                         hipStream_t s, const uint16_t* biases) {
+                         hipStream_t s, const uint16_t* biases, const NormIn& nin) {
   const int64_t G = a.K / 32;
   const int64_t teams_per_block = kBlock / LPR;
   int64_t blocks = (a.N + teams_per_block - 1) / teams_per_block;
@@ -373,7 +412,8 @@ hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, cons
   if (hipError_t e = allow_lds(k_gemv_m1<LPR, UNR, MODE>, lds)) return e;
   hipLaunchKernelGGL((k_gemv_m1<LPR, UNR, MODE>), grid, dim3(kBlock), lds, s,
                      reinterpret_cast<const uint4*>(a.words), a.scales, biases,
-                     reinterpret_cast<const uint4*>(a.x), a.y, part, (int)a.N, (int)G, p.splits);
+                     reinterpret_cast<const uint4*>(a.x), a.y, part, (int)a.N, (int)G, p.splits,
+                     nin);
   return hipGetLastError();
 }
 
@@ -384,29 +424,30 @@ hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, cons
 // quarter of every lane's work there (262144 x 3072: 91.9 -> 72.1 us at 3)
 template <int LPR, int MODE>
 hipError_t launch_m1(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
-                     hipStream_t s, const uint16_t* biases) {
+                     hipStream_t s, const uint16_t* biases, const NormIn& nin) {
   const int64_t G = a.K / 32;
   const int64_t per_lane = ((G + p.splits - 1) / p.splits + LPR - 1) / LPR;
   switch (per_lane) {
-    case 0: case 1: case 2: return launch_m1_unr<LPR, 2, MODE>(a, p, part, d, s, biases);
-    case 3: return launch_m1_unr<LPR, 3, MODE>(a, p, part, d, s, biases);
-    case 4: return launch_m1_unr<LPR, 4, MODE>(a, p, part, d, s, biases);
-    case 5: return launch_m1_unr<LPR, 5, MODE>(a, p, part, d, s, biases);
-    case 6: return launch_m1_unr<LPR, 6, MODE>(a, p, part, d, s, biases);
-    default: return launch_m1_unr<LPR, 8, MODE>(a, p, part, d, s, biases);
+    case 0: case 1: case 2: return launch_m1_unr<LPR, 2, MODE>(a, p, part, d, s, biases, nin);
+    case 3: return launch_m1_unr<LPR, 3, MODE>(a, p, part, d, s, biases, nin);
+    case 4: return launch_m1_unr<LPR, 4, MODE>(a, p, part, d, s, biases, nin);
+    case 5: return launch_m1_unr<LPR, 5, MODE>(a, p, part, d, s, biases, nin);
+    case 6: return launch_m1_unr<LPR, 6, MODE>(a, p, part, d, s, biases, nin);
+    default: return launch_m1_unr<LPR, 8, MODE>(a, p, part, d, s, biases, nin);
   }
 }
 
-// biases: kAffine only
+// biases: kAffine only; nin: kPlainNorm and kGluNorm only
 template <int MODE>
 hipError_t launch_m1_lpr(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
-                         hipStream_t s, const uint16_t* biases = nullptr) {
+                         hipStream_t s, const uint16_t* biases = nullptr,
+                         const NormIn& nin = NormIn{}) {
   switch (p.lanes_per_row) {
-    case 4: return launch_m1<4, MODE>(a, p, part, d, s, biases);
-    case 8: return launch_m1<8, MODE>(a, p, part, d, s, biases);
-    case 16: return launch_m1<16, MODE>(a, p, part, d, s, biases);
-    case 32: return launch_m1<32, MODE>(a, p, part, d, s, biases);
-    default: return launch_m1<64, MODE>(a, p, part, d, s, biases);
+    case 4: return launch_m1<4, MODE>(a, p, part, d, s, biases, nin);
+    case 8: return launch_m1<8, MODE>(a, p, part, d, s, biases, nin);
+    case 16: return launch_m1<16, MODE>(a, p, part, d, s, biases, nin);
+    case 32: return launch_m1<32, MODE>(a, p, part, d, s, biases, nin);
+    default: return launch_m1<64, MODE>(a, p, part, d, s, biases, nin);
   }
 }
 
@@ -496,6 +537,17 @@ hipError_t launch_gemv_affine(const DeviceInfo& d, const uint32_t* W, const uint
   const GemvPlan p = plan_splits(d, 1, N, K, 1);
   if ((size_t)(K / 32) * 68 > d.lds_per_block) return hipErrorInvalidValue;
   return launch_m1_lpr<kAffine>(a, p, nullptr, d, s, B);
+}
+
+hipError_t launch_gemv_norm_in(const DeviceInfo& d, const uint32_t* words,
+                               const uint16_t* scales, const NormIn& nin, uint16_t* y,
+                               int64_t N, int64_t K, bool glu, hipStream_t s) {
+  if (!nin.res_in || !nin.gamma || (size_t)(K / 32) * 64 > d.lds_per_block)
+    return hipErrorInvalidValue;
+  const GemvArgs a{words, scales, nullptr, y, 1, N, K};
+  const GemvPlan p = plan_splits(d, 1, glu ? 2 * N : N, K, 1);
+  return glu ? launch_m1_lpr<kGluNorm>(a, p, nullptr, d, s, nullptr, nin)
+             : launch_m1_lpr<kPlainNorm>(a, p, nullptr, d, s, nullptr, nin);
 }
 
 hipError_t launch_gemv_glu(const DeviceInfo& d, const uint32_t* words, const uint16_t* scales,

@@ -7,9 +7,12 @@
 // Each projection is one GEMV kernel (one kernel per GEMV is the faster choice
 // for a chain in which every GEMV waits for the one before it).  Where gate/up
 // needs no split-K pass the glue runs inside it (q4_fused.h): six kernels per
-// block instead of seven, with bitwise the same results.  Every buffer
-// between the kernels lives in the caller's workspace; the residual is updated
-// in place.  A multi-step decode captures one step, with two one-thread kernels
+// block instead of seven, with bitwise the same results.  With the model option
+// Q4_MODEL_FACTORED_NORM every residual add + RMSNorm is folded into the GEMV it
+// feeds (q4_fused.h): four kernels per block, results within rounding of the
+// unfolded step, not bitwise.  Every buffer between the kernels lives in the
+// caller's workspace; the residual is updated in place (unfolded) or alternates
+// between two buffers (folded).  A multi-step decode captures one step, with two one-thread kernels
 // that take the step's token from and put the next one into the caller's token
 // array at a device-side counter, as a HIP graph and replays it: no host
 // round trip between tokens (the pages' host-side lever is to submit a whole
@@ -33,7 +36,8 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Layout {
   q4::GemvPlan qkv, o, gate_up, down, lm_head;
   bool fuse = false;       // the glue inside the gate/up GEMV (no split-K pass in it)
-  size_t res = 0, h = 0, qkv_out = 0, attn = 0, gu = 0, hf = 0, dn = 0, logits = 0, tok = 0;
+  size_t res = 0, res2 = 0, h = 0, qkv_out = 0, attn = 0, gu = 0, hf = 0, dn = 0, logits = 0,
+         tok = 0;
   size_t bytes = 0;
 };
 
@@ -53,6 +57,7 @@ Layout layout_for(const q4::DeviceInfo& d, const q4_model& m) {
     return o;
   };
   L.res = take(2 * m.D);
+  L.res2 = take(2 * m.D);      // the factored-norm chain's second residual buffer
   L.h = take(2 * m.D);
   L.qkv_out = take(2 * 3 * m.D);
   L.attn = take(2 * m.D);
@@ -95,6 +100,8 @@ int check_model(const q4_model* m) {
   if (m->D > (1 << 20) || m->F > (1 << 20) || m->V > INT32_MAX)
     return q4::api_fail(Q4_ERR_UNSUPPORTED, "D, F or V too large");
   if (!(m->eps >= 0.f)) return q4::api_fail(Q4_ERR_SHAPE, "eps must be >= 0");
+  if (m->options & ~Q4_MODEL_FACTORED_NORM)
+    return q4::api_fail(Q4_ERR_SHAPE, "options = 0x%x: unknown bits", m->options);
   if (int rc = check_weight("embed", m->embed, m->V, m->D)) return rc;
   if (int rc = check_weight("lm_head", m->lm_head, m->V, m->D)) return rc;
   if (int rc = check_gamma("final_norm", m->final_norm)) return rc;
@@ -143,6 +150,38 @@ hipError_t enqueue_step(const q4::DeviceInfo& d, const q4_model& m, const Layout
   } while (0)
   Q4_TRY(q4::launch_embed_rows(m.embed.words, m.embed.scales, m.V, m.D, tok_in, 1, res, s));
   const uint16_t* g0 = m.n_blocks ? m.blocks[0].attn_norm : m.final_norm;
+  if (m.options & Q4_MODEL_FACTORED_NORM) {
+    // every residual add + RMSNorm folded into the GEMV it feeds (q4_fused.h);
+    // the residual alternates between two buffers (its GEMV's workgroups all read
+    // the old one while one of them writes the new one)
+    uint16_t *cur = res, *other = buf(L.res2);
+    q4::NormIn pend;                // the add + norm the next normed GEMV applies
+    pend.gamma = g0;
+    pend.eps = m.eps;
+    auto normed = [&](const q4_weight& w, uint16_t* y, int64_t n_out, bool glu) {
+      q4::NormIn a = pend;
+      a.res_in = cur;
+      a.res_out = pend.delta ? other : nullptr;
+      const hipError_t e = q4::launch_gemv_norm_in(d, w.words, w.scales, a, y, n_out, w.K, glu, s);
+      if (pend.delta) std::swap(cur, other);
+      return e;
+    };
+    for (int64_t b = 0; b < m.n_blocks; ++b) {
+      const q4_block& B = m.blocks[b];
+      const uint16_t* next = b + 1 < m.n_blocks ? m.blocks[b + 1].attn_norm : m.final_norm;
+      Q4_TRY(normed(B.qkv, qkv, 3 * m.D, false));
+      Q4_TRY(gemv(B.o, L.o, qkv + 2 * m.D, attn));
+      pend.delta = attn;
+      pend.gamma = B.ffn_norm;
+      Q4_TRY(normed(B.gate_up, hf, m.F, true));
+      Q4_TRY(gemv(B.down, L.down, hf, dn));
+      pend.delta = dn;
+      pend.gamma = next;
+    }
+    Q4_TRY(normed(m.lm_head, lg, m.V, false));
+    Q4_TRY(q4::launch_argmax(lg, 1, m.V, tok_out, s));
+    return hipSuccess;
+  }
   Q4_TRY(q4::launch_rmsnorm(nullptr, res, g0, m.eps, 1, m.D, nullptr, h, s));
   for (int64_t b = 0; b < m.n_blocks; ++b) {
     const q4_block& B = m.blocks[b];

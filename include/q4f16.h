@@ -321,7 +321,18 @@ typedef struct q4_model {
   const uint16_t* final_norm;   /* fp16 [D] */
   q4_weight lm_head;            /* [V][D] */
   float eps;                    /* RMSNorm epsilon, >= 0 */
+  uint32_t options;             /* 0 or Q4_MODEL_FACTORED_NORM */
 } q4_model;
+
+/* Fold every residual add + RMSNorm into the GEMV it feeds: that GEMV stages
+ * h * gamma (h = residual + the previous projection's output), forms sum(h^2)
+ * alongside, and scales its outputs by 1 / sqrt(sum(h^2) / D + eps) -- the same
+ * normalisation with the scalar applied after the product instead of before it,
+ * so no reduction precedes the GEMV and the step has no separate norm kernels.
+ * The rounding differs from the unfolded step (there the normalised vector is
+ * rounded to fp16 before the product): results agree with it within fp16
+ * rounding per stage, not bit for bit. */
+#define Q4_MODEL_FACTORED_NORM 0x1u
 
 /* Workspace bytes q4_decode_token and q4_decode_tokens need for this model
  * (activations, split-K partials, token bookkeeping); 0 if the model is invalid. */
