@@ -490,7 +490,8 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
     weights near 0.1 keep them finite): one q4_decode_token per token with a host
     synchronisation after each (one token per host call), and q4_decode_tokens
     with `steps` tokens per host call, kernels enqueued per step or one captured
-    step replayed as a graph."""
+    step replayed as a graph; and the graph replay with the norms folded into the
+    GEMVs they feed (Q4_MODEL_FACTORED_NORM)."""
     D, F, V = 3072, 8192, 32064
     labels = [l for l, _, _ in meta]
     assert len(descs) == 129 and labels[-1].endswith("lm_head"), labels[-1]
@@ -536,7 +537,25 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
             out[name] = {"ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 1),
                          "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
     out["tokens"] = tokens[: min(steps + 1, 9)].cpu().tolist()
-    del ws, model
+    # the same loop with every residual add + RMSNorm folded into the GEMV it feeds
+    folded = q4.Model(embed, blocks, gamma, descs[128][:2], 1e-5,
+                      options=q4.MODEL_FACTORED_NORM)
+    wsf = torch.empty(q4.q4_decode_token_workspace_bytes(folded), dtype=torch.uint8,
+                      device="cuda")
+    with torch.cuda.stream(stream):
+        q4.q4_decode_tokens(folded, tokens, steps, ws=wsf, stream=stream)
+        torch.cuda.synchronize()
+        reps = 5
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            q4.q4_decode_tokens(folded, tokens, steps, ws=wsf, stream=stream)
+        stream.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / (reps * steps)
+    out["tokens_per_call_graph_norms_folded"] = {
+        "ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 1),
+        "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
+        "tokens": tokens[: min(steps + 1, 9)].cpu().tolist()}
+    del ws, wsf, model, folded
     return out
 
 
