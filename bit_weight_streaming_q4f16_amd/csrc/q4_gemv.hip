@@ -309,6 +309,11 @@ __global__ __launch_bounds__(kBlock) void k_gemv_mfma(const uint4* __restrict__ 
 
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, c = l >> 4, r = l & 15;
   const bool has_x = r < M;
+  // the eight-group blocks need whole blocks in the slice and 16-byte aligned
+  // scale runs
+  const bool wide = gc % 8 == 0 && g0 % 8 == 0 && G % 8 == 0 &&
+                    (reinterpret_cast<uintptr_t>(S) & 15u) == 0;
+  uint32_t* const stage = reinterpret_cast<uint32_t*>(xs + M * pitch) + wave * 512;
   const f4_t zero = {0.f, 0.f, 0.f, 0.f};
   // workgroups loop over tiles of 16 rows, so X is staged once per workgroup, not
   // once per tile
@@ -317,7 +322,51 @@ __global__ __launch_bounds__(kBlock) void k_gemv_mfma(const uint4* __restrict__ 
     const uint4* wr = W + (int64_t)n * G + g0;
     const uint16_t* sr = S + (int64_t)n * G + g0;
     f4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int gb = 4 * wave; gb < gc; gb += 16) {
+    if (wide) {
+      // blocks of eight groups: two loads of 8 rows x 128 contiguous bytes (lane l:
+      // row 8h + l / 8, group l % 8; whole cache lines, where one group per lane of
+      // 16 rows touches 16 half lines), through this wave's stage as word planes
+      // [word][16 rows][8 groups], from which lane (c, r) reads word c of row r's
+      // eight groups as 32 contiguous bytes; the row's eight scales in one load.
+      const uint4* wt = W + (int64_t)n0 * G + g0;
+      const int64_t rows_left = (int64_t)(N - n0);
+      for (int gb = 8 * wave; gb < gc; gb += 32) {
+        uint4 raw[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t row = 8 * h + (l >> 3);
+          raw[h] = load_nt(wt + (row < rows_left ? row : rows_left - 1) * G + gb + (l & 7));
+        }
+        const uint4 sv = *reinterpret_cast<const uint4*>(sr + gb);
+        // the stage is read by other lanes of the wave: keep its writes and reads
+        // in program order (a wave's LDS operations complete in order)
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          stage[j * 128 + l] = (&raw[0].x)[j];
+          stage[j * 128 + 64 + l] = (&raw[1].x)[j];
+        }
+        asm volatile("" ::: "memory");
+        const uint4* sp = reinterpret_cast<const uint4*>(stage + c * 128 + r * 8);
+        const uint4 wq0 = sp[0], wq1 = sp[1];
+        asm volatile("" ::: "memory");
+        const uint32_t wc[8] = {wq0.x, wq0.y, wq0.z, wq0.w, wq1.x, wq1.y, wq1.z, wq1.w};
+        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          h2_t q[4];
+          dequant_word(wc[t], q);
+          const h8_t B = {q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+          h8_t A = {};
+          if (has_x) A = bits<h8_t>(xs[r * pitch + 4 * (gb + t) + c]);
+          const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, zero, 0, 0, 0);
+          const float sc = half_to_float((uint16_t)(sw[t >> 1] >> (16 * (t & 1))));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, d[e], acc[e]);
+        }
+      }
+    }
+    for (int gb = 4 * wave; !wide && gb < gc; gb += 16) {
       const int gl = gb + c < gc ? gb + c : gc - 1;
       const uint4 wv = load_nt(wr + gl);
       float s[4];
@@ -459,10 +508,10 @@ hipError_t launch_m1_lpr(const GemvArgs& a, const GemvPlan& p, float* part, cons
 
 int64_t max_groups_per_slice(const DeviceInfo& d, int64_t M) {
   // M == 1: 64 bytes of LDS per group.  M > 1: M rows of (4 g + 1) uint4 plus 3 KB
-  // of cross-wave partials.
+  // of cross-wave partials and 2 KB of stage per wave.
   const int64_t lds = (int64_t)d.lds_per_block;
   if (M <= 1) return lds / 64;
-  return ((lds - 3 * 64 * 16) / (16 * M) - 1) / 4;
+  return ((lds - 3 * 64 * 16 - (kBlock / 64) * 2048) / (16 * M) - 1) / 4;
 }
 
 GemvPlan plan_splits(const DeviceInfo& d, int64_t M, int64_t N, int64_t K, int splits) {
@@ -510,7 +559,7 @@ hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p
   } else {
     const int64_t G = a.K / 32;
     const int64_t gmax = (G + p.splits - 1) / p.splits;
-    const size_t lds = (size_t)a.M * (4 * gmax + 1) * 16;
+    const size_t lds = (size_t)a.M * (4 * gmax + 1) * 16 + (kBlock / 64) * 2048;
     // as many workgroups as fit the device at once (LDS bounds them: X is M rows
     // of the slice), each looping over tiles
     int64_t tiles = (a.N + 15) / 16;
