@@ -222,6 +222,28 @@ def test_batched_vs_oracle(M, N, K):
     assert_gemv_close(Y, w, s, X, exact=(N * K <= 100_000))
 
 
+@pytest.mark.parametrize("M", [3, 8])
+def test_batched_mixed_slices(M):
+    """Few row tiles, so K is split: slices of 16 and 17 groups, some taken as
+    eight-group blocks and some one group per lane."""
+    N, K = 40, 6400
+    w, s, X = rand_case(77 + M, N, K, M=M, neg=True)
+    assert_gemv_close(batched_gpu(w, s, X), w, s, X)
+
+
+def test_batched_scales_2_byte_aligned():
+    """Scales not 16-byte aligned: the one-group-per-lane path, same results."""
+    N, K, M = 600, 2048, 4
+    w, s, X = rand_case(78, N, K, M=M, neg=True)
+    big = torch.zeros(s.size + 8, dtype=torch.int16, device="cuda")
+    sv = big[1:1 + s.size]
+    sv.copy_(dev_half(s).reshape(-1).view(torch.int16))
+    assert sv.data_ptr() % 16 != 0
+    Y = q4.q4_gemv_batched(dev_words(w), sv.view(torch.float16).view(N, -1), dev_half(X))
+    torch.cuda.synchronize()
+    assert_gemv_close(host_half(Y), w, s, X)
+
+
 def test_batched_rows_equal_single_row_calls_within_tolerance():
     w, s, X = rand_case(21, 300, 2048, M=8)
     Y = batched_gpu(w, s, X)
