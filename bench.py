@@ -433,13 +433,15 @@ def formats_large(torch, q4, S, stream, N=262144, K=3072, calls=20):
         ms = _timed(torch, stream, fn, calls, warm=5)
         out[name] = _fig(nb, ms, weight_bytes=wb, ns_per_kweight=round(ms * 1e6 / (N * K / 1e3), 4))
         if f == 0:
+            # the persistent kernel on this one GEMV (the driver alone would run a
+            # one-descriptor list as one GEMV kernel)
             layers = q4.make_layers([(W, sc, xf, yf)])
-            nbs = q4.q4_decode_step_workspace_bytes(layers, 1, 0)
+            nbs = q4.q4_decode_step_workspace_bytes(layers, 1, q4.STEP_PERSISTENT)
             wss = torch.zeros(max(nbs, 16), dtype=torch.uint8, device="cuda")
 
             def fs(i):
-                q4.q4_decode_step(layers, 1, q4.STEP_WS_CLEAN, ws=wss, ws_bytes=nbs,
-                                  stream=stream)
+                q4.q4_decode_step(layers, 1, q4.STEP_WS_CLEAN | q4.STEP_PERSISTENT, ws=wss,
+                                  ws_bytes=nbs, stream=stream)
             ms = _timed(torch, stream, fs, calls, warm=5)
             out["q4f16_1_decode_step"] = _fig(nb, ms, weight_bytes=wb,
                                               ns_per_kweight=round(ms * 1e6 / (N * K / 1e3), 4))

@@ -104,11 +104,13 @@ def test_fused_glue_equals_standalone_glue_bitwise():
                       q4.STEP_PERSISTENT)
     h = q4.q4_silu_mul(gu)
     y2 = nan_half(D)
-    q4.q4_decode_step(q4.make_layers([(Wdn, Sdn, h, y2)]), 1, 0)
+    # one-descriptor lists run as one GEMV kernel unless the persistent one is asked for
+    q4.q4_decode_step(q4.make_layers([(Wdn, Sdn, h, y2)]), 1, q4.STEP_PERSISTENT)
     # and the glue from a plain input buffer (no producer in the list); the copy
     # must outlive the call (make_layers keeps only its address)
     gu2, y3 = gu.clone(), nan_half(D)
-    q4.q4_decode_step(q4.make_layers([(Wdn, Sdn, gu2, y3, q4.X_SILU_MUL)]), 1, 0)
+    q4.q4_decode_step(q4.make_layers([(Wdn, Sdn, gu2, y3, q4.X_SILU_MUL)]), 1,
+                      q4.STEP_PERSISTENT)
     torch.cuda.synchronize()
     assert np.array_equal(host_half(y), host_half(y2))
     assert np.array_equal(host_half(y), host_half(y3))
