@@ -81,6 +81,8 @@ def parse():
                     help="run only a plain device copy of BYTES, 3 times (counter calibration)")
     ap.add_argument("--only-m8", action="store_true",
                     help="time only the 2B-class sweep at M=8 (for profiler runs)")
+    ap.add_argument("--only-tokens", action="store_true",
+                    help="time only the Phi-3-shaped decode-token loop (for profiler runs)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 CSV output under DIR")
     ap.add_argument("--kernel", choices=sorted(PROFILED), default="k_step",
@@ -125,6 +127,11 @@ def main():
     stream = torch.cuda.Stream()          # default priority
     if args.copy_probe:
         copy_probe(torch, q4, stream, args.copy_probe)
+        return
+    if args.only_tokens:
+        descs, meta = build_sweep(torch, q4, synth, np)
+        print(json.dumps({"decode_tokens": token_figures(torch, q4, synth, np, stream, descs,
+                                                         meta)}), flush=True)
         return
     if args.only_m8:
         print(json.dumps({"twob_sweep_m8": m8_sweep(torch, q4, synth, np, stream, args.steps,
