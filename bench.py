@@ -113,7 +113,7 @@ def main():
         summarize_profiles(args.summarize_profiles, args.kernel)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
