@@ -18,7 +18,7 @@ import threading
 
 __all__ = [
     "Q4Error", "load", "lib_path", "q4_version", "q4_pack", "q4_unpack", "q4_gemv",
-    "q4_gemv_splitk", "q4_gemv_batched", "q4_workspace_bytes", "q4_splitk_workspace_bytes",
+    "q4_gemv_splitk", "q4_gemv_batched", "q4_gemv_batched_noalloc", "q4_workspace_bytes", "q4_splitk_workspace_bytes",
     "q4_decode_step", "q4_decode_step_workspace_bytes", "q4_probe_read", "q4_probe_copy",
     "Layer", "STEP_LAUNCH_EACH", "STEP_ORDERED", "STEP_LDS_RING", "STEP_WS_CLEAN", "make_layers",
 ]
@@ -28,6 +28,7 @@ _LIB = os.path.join(_HERE, "_lib", "libq4f16.so")
 _lock = threading.Lock()
 _lib = None
 
+Q4_NOALLOC_SCRATCH_BYTES = 4 * 1024 * 1024   # include/q4f16.h
 STEP_LAUNCH_EACH = 0x1
 STEP_ORDERED = 0x2
 STEP_LDS_RING = 0x4
@@ -105,6 +106,7 @@ def load():
             "q4_gemv": ([p, p, p, p, i64, i64, p, sz, p], i32),
             "q4_gemv_splitk": ([p, p, p, p, i64, i64, i64, p, sz, p], i32),
             "q4_gemv_batched": ([p, p, p, p, i64, i64, i64, p, sz, p], i32),
+            "q4_gemv_batched_noalloc": ([p, p, p, p, i64, i64, i64, p], i32),
             "q4_workspace_bytes": ([i64, i64, i64], sz),
             "q4_splitk_workspace_bytes": ([i64, i64, i64], sz),
             "q4_decode_step": ([p, i64, i64, C.c_uint32, p, sz, p], i32),
@@ -264,6 +266,24 @@ def q4_gemv_batched(words, scales, X, Y=None, ws=None, stream=None):
     ws, wsb = _ws(q4_workspace_bytes(M, N, K), ws, words.device)
     _check(load().q4_gemv_batched(_ptr(words), _ptr(scales), _ptr(X), _ptr(Y), M, N, K,
                                   _ptr(ws), wsb, _stream(stream)))
+    return Y
+
+
+def q4_gemv_batched_noalloc(words, scales, X, Y=None, stream=None):
+    """q4_gemv_batched without a workspace: split-K partials in the library's
+    static device array (nothing is allocated by the call; Y is allocated here
+    only when not given)."""
+    torch = _torch()
+    N, K = _gemv_shapes(words, scales)
+    _dev(X, "X", torch.float16)
+    if X.dim() != 2 or X.shape[1] != K:
+        raise Q4Error(2, f"X shape {tuple(X.shape)} must be [M][{K}]")
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=words.device)
+    _dev(Y, "Y", torch.float16)
+    _check(load().q4_gemv_batched_noalloc(_ptr(words), _ptr(scales), _ptr(X), _ptr(Y), M, N, K,
+                                          _stream(stream)))
     return Y
 
 

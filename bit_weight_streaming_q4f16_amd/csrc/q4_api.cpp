@@ -188,9 +188,18 @@ size_t q4_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
   return (size_t)4 * (size_t)splits * (size_t)M * (size_t)N;
 }
 
-static int gemv_common(const char* what, const uint32_t* words, const uint16_t* scales,
-                       const uint16_t* x, uint16_t* y, int64_t M, int64_t N, int64_t K,
-                       int64_t splits, void* ws, size_t ws_bytes, q4_stream_t stream) {
+}  // extern "C"
+
+namespace q4 {
+
+int gemv_validate(const char* what, const uint32_t* words, const uint16_t* scales,
+                  const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K) {
+  return check_gemv(what, words, scales, x, y, M, N, K, K);
+}
+
+int gemv_common(const char* what, const uint32_t* words, const uint16_t* scales,
+                const uint16_t* x, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                int64_t splits, void* ws, size_t ws_bytes, void* stream) {
   if (int rc = check_gemv(what, words, scales, x, y, M, N, K, K)) return rc;
   if (splits != 0 && (splits < 1 || splits > q4::kMaxSplits || splits > K / 32))
     return fail(Q4_ERR_SHAPE, "%s: splits = %lld: must be in [1, min(64, K/32 = %lld)]", what,
@@ -209,9 +218,13 @@ static int gemv_common(const char* what, const uint32_t* words, const uint16_t* 
   return e == hipSuccess ? ok() : device_error(e, what);
 }
 
+}  // namespace q4
+
+extern "C" {
+
 int q4_gemv(const uint32_t* words, const uint16_t* scales, const uint16_t* x, uint16_t* y,
             int64_t N, int64_t K, void* ws, size_t ws_bytes, q4_stream_t stream) {
-  return gemv_common("q4_gemv", words, scales, x, y, 1, N, K, 0, ws, ws_bytes, stream);
+  return q4::gemv_common("q4_gemv", words, scales, x, y, 1, N, K, 0, ws, ws_bytes, stream);
 }
 
 int q4_gemv_splitk(const uint32_t* words, const uint16_t* scales, const uint16_t* x,
@@ -219,14 +232,14 @@ int q4_gemv_splitk(const uint32_t* words, const uint16_t* scales, const uint16_t
                    size_t ws_bytes, q4_stream_t stream) {
   if (splits < 1) return fail(Q4_ERR_SHAPE, "q4_gemv_splitk: splits = %lld: must be >= 1",
                               (long long)splits);
-  return gemv_common("q4_gemv_splitk", words, scales, x, y, 1, N, K, splits, ws, ws_bytes,
+  return q4::gemv_common("q4_gemv_splitk", words, scales, x, y, 1, N, K, splits, ws, ws_bytes,
                      stream);
 }
 
 int q4_gemv_batched(const uint32_t* words, const uint16_t* scales, const uint16_t* X,
                     uint16_t* Y, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
                     q4_stream_t stream) {
-  return gemv_common("q4_gemv_batched", words, scales, X, Y, M, N, K, 0, ws, ws_bytes, stream);
+  return q4::gemv_common("q4_gemv_batched", words, scales, X, Y, M, N, K, 0, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

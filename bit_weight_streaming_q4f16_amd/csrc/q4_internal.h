@@ -34,6 +34,15 @@ const DeviceInfo* device_info();
 int api_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int api_ok();
 
+// The argument checks of q4_gemv_batched (null pointers, shape, alignment, overlap).
+int gemv_validate(const char* what, const uint32_t* words, const uint16_t* scales,
+                  const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K);
+// The body of q4_gemv / q4_gemv_batched / q4_gemv_splitk (q4_api.cpp): validate the
+// arguments, plan (splits == 0: automatic), check the workspace, launch.
+int gemv_common(const char* what, const uint32_t* words, const uint16_t* scales,
+                const uint16_t* x, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                int64_t splits, void* ws, size_t ws_bytes, void* stream);
+
 // One GEMV as the kernels see it.
 struct GemvArgs {
   const uint32_t* words;             // [N][K/8]

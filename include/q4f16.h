@@ -116,6 +116,29 @@ Q4_API size_t q4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 /* Workspace bytes of q4_gemv_splitk (M == 1) with `splits` slices. */
 Q4_API size_t q4_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
 
+/* Size of the device array in which q4_gemv_batched_noalloc keeps its split-K
+ * partials: 4 MiB, one copy per GPU the library runs on, held until the process
+ * ends. */
+#define Q4_NOALLOC_SCRATCH_BYTES (4 * 1024 * 1024)
+
+/* q4_gemv_batched_noalloc: q4_gemv_batched (M == 1: q4_gemv) for callers that
+ * cannot allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments without the workspace:
+ * the split-K partials go to a library-owned static device array of
+ * Q4_NOALLOC_SCRATCH_BYTES bytes, so the call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).  The caller still owns X, Y and the
+ * weights.  Results are bitwise those of q4_gemv_batched with a workspace.
+ * A shape whose split-K plan needs more than Q4_NOALLOC_SCRATCH_BYTES
+ * (q4_workspace_bytes(M, N, K) > Q4_NOALLOC_SCRATCH_BYTES) is rejected with
+ * Q4_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (on different streams,
+ * or from several threads without ordering) race on it and may give wrong
+ * results; calls ordered on one stream are safe.  The array needs no clearing:
+ * every partial a call reads was written by that call. */
+Q4_API int q4_gemv_batched_noalloc(const uint32_t* words, const uint16_t* scales,
+                                   const uint16_t* X, uint16_t* Y, int64_t M, int64_t N,
+                                   int64_t K, q4_stream_t stream);
+
 /* ------------------------------------------------------------ decode step -- */
 
 /* How a descriptor's GEMV input is formed from the memory at x. */

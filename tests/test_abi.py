@@ -110,6 +110,17 @@ def test_batched_and_splitk_argument_errors(lib):
     assert lib.q4_workspace_bytes(1, 16, 48) == 0
 
 
+def test_noalloc_gemv_argument_errors(lib):
+    f = lib.q4_gemv_batched_noalloc
+    f.argtypes = [C.c_void_p] * 4 + [C.c_int64] * 3 + [C.c_void_p]
+    f.restype = C.c_int
+    # argument errors come before any device query: they need no GPU
+    assert f(None, B, X, Y, 1, 16, 64, None) == 1 and "words" in _err(lib)
+    assert f(A, B, X, Y, 9, 16, 64, None) == 2 and "M = 9" in _err(lib)
+    assert f(A, B, X, Y, 1, 16, 48, None) == 2
+    assert f(A, B, P(0x30008), Y, 1, 16, 64, None) == 3
+
+
 def test_codec_argument_errors(lib):
     assert lib.q4_pack(None, A, 4, 64, None) == 1
     assert lib.q4_pack(X, None, 4, 64, None) == 1
