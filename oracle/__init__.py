@@ -37,7 +37,8 @@ def build(force: bool = True) -> str:
             os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-                               "-fPIC", "-shared", "-fvisibility=hidden", "-o", tmp, _SRC, "-lm"])
+                               "-fopenmp", "-fPIC", "-shared", "-fvisibility=hidden", "-o", tmp,
+                               _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -54,6 +55,12 @@ def _load():
             i64 = C.c_int64
             lib.orc_half_to_f64.argtypes = [C.c_uint16]
             lib.orc_half_to_f64.restype = C.c_double
+            lib.orc_bf16_to_f64.argtypes = [C.c_uint16]
+            lib.orc_bf16_to_f64.restype = C.c_double
+            lib.orc_set_threads.argtypes = [C.c_int]
+            lib.orc_set_threads.restype = None
+            lib.orc_get_threads.argtypes = []
+            lib.orc_get_threads.restype = C.c_int
             lib.orc_f64_to_half.argtypes = [C.c_double]
             lib.orc_f64_to_half.restype = C.c_uint16
             lib.orc_unpack.argtypes = [p, p, i64, i64]
@@ -96,6 +103,19 @@ def _c(a, dtype):
 
 def half_to_f64(h: int) -> float:
     return _load().orc_half_to_f64(int(h))
+
+
+def bf16_to_f64(h: int) -> float:
+    return _load().orc_bf16_to_f64(int(h))
+
+
+def set_threads(n: int) -> None:
+    """Host threads of the GEMV row loops (1: the plain single-threaded oracle)."""
+    _load().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().orc_get_threads())
 
 
 def f64_to_half(v: float) -> int:
@@ -243,7 +263,9 @@ def argmax(x) -> np.ndarray:
     return out
 
 
-FORMATS = {"q3f16_1": 1, "q4f32_1": 2, "af4g64": 3}
+# af4g64: bf16 scales and biases (the pages' MLX affine format);
+# af4g64_f16: the same with fp16 scales and biases (an extra variant)
+FORMATS = {"q3f16_1": 1, "q4f32_1": 2, "af4g64": 3, "af4g64_f16": 4}
 
 
 def gemv_format(fmt: str, words, scales, biases, x, K: int, rows=None):

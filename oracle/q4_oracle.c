@@ -30,8 +30,12 @@
  *
  * fp16 <-> fp64 conversions are written from the IEEE 754 binary16 definition
  * (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits; exponent 0 is
- * zero/subnormal, exponent 31 is inf/NaN).  Codes above 15 given to orc_pack
- * are reduced to their low nibble.
+ * zero/subnormal, exponent 31 is inf/NaN), bf16 -> fp64 from the bfloat16
+ * definition.  Codes above 15 given to orc_pack are reduced to their low nibble.
+ *
+ * The GEMV row loops may run on several host threads (orc_set_threads; OpenMP
+ * when built with -fopenmp): an OpenMP "parallel for" over output rows, each row
+ * computed by the same steps, so the results are those of one thread.
  *
  * parity pins: see the CPU tests (closed forms, exact brute force, numpy
  * float16 conversions, byte-view nibble decoding, hand-worked fixtures).
@@ -54,6 +58,21 @@ ORC_EXPORT double orc_half_to_f64(uint16_t h) {
     v = f ? NAN : INFINITY;
   else
     v = ldexp((double)(1024 + f), e - 25);    /* (1 + f/1024) * 2^(e - 15) */
+  return sign ? -v : v;
+}
+
+/* bfloat16 from its definition: 1 sign bit, 8 exponent bits with bias 127, 7
+ * fraction bits (the upper half of an IEEE 754 binary32); exponent 0 is
+ * zero/subnormal, exponent 255 is inf/NaN. */
+ORC_EXPORT double orc_bf16_to_f64(uint16_t h) {
+  int sign = h >> 15, e = (h >> 7) & 255, f = h & 127;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -133);               /* subnormal: f * 2^-133     */
+  else if (e == 255)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(128 + f), e - 134);    /* (1 + f/128) * 2^(e - 127) */
   return sign ? -v : v;
 }
 
@@ -165,6 +184,15 @@ ORC_EXPORT int64_t orc_roundtrip_mismatches(uint64_t w0, uint64_t w1) {
 
 /* -------------------------------------------------------------------- GEMV */
 
+/* Threads the row loops below run on (OpenMP, when the library is built with it):
+ * 1 by default, the plain single-threaded oracle.  Rows are independent and each
+ * is computed by exactly the same steps whatever the thread count, so results
+ * do not depend on it. */
+static int g_threads = 1;
+
+ORC_EXPORT void orc_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+ORC_EXPORT int orc_get_threads(void) { return g_threads; }
+
 /* Y[m][i] = sum_k (q[n][k] - 7) * s[n][k/32] * X[m][k], n = rows[i] (or i when
  * rows is NULL), accumulated in fp64 in ascending k.  X is [M][K], Y is
  * [M][n_rows].  Returns 0, or -1 on a bad shape. */
@@ -172,26 +200,34 @@ ORC_EXPORT int orc_gemv_f64(const uint32_t* words, const uint16_t* scales, const
                             int64_t M, int64_t N, int64_t K, const int64_t* rows,
                             int64_t n_rows, double* Y) {
   if (M < 1 || N < 1 || K < 32 || K % 32) return -1;
+  for (int64_t i = 0; i < n_rows; ++i)
+    if ((rows ? rows[i] : i) < 0 || (rows ? rows[i] : i) >= N) return -1;
   double* x = (double*)malloc(sizeof(double) * (size_t)K);
-  double* s = (double*)malloc(sizeof(double) * (size_t)(K / 32));
-  if (!x || !s) { free(x); free(s); return -1; }
+  if (!x) return -1;
+  int bad = 0;
   for (int64_t m = 0; m < M; ++m) {
     for (int64_t k = 0; k < K; ++k) x[k] = orc_half_to_f64(X[m * K + k]);
-    for (int64_t i = 0; i < n_rows; ++i) {
-      int64_t n = rows ? rows[i] : i;
-      if (n < 0 || n >= N) { free(x); free(s); return -1; }
-      for (int64_t g = 0; g < K / 32; ++g) s[g] = orc_half_to_f64(scales[n * (K / 32) + g]);
-      double acc = 0.0;
-      for (int64_t k = 0; k < K; ++k) {
-        int q = (int)code_at(words, K, n, k);
-        acc += ((double)(q - 7) * s[k / 32]) * x[k];
+#pragma omp parallel num_threads(g_threads) reduction(| : bad)
+    {
+      double* s = (double*)malloc(sizeof(double) * (size_t)(K / 32));
+      bad |= !s;
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t i = 0; i < n_rows; ++i) {
+        if (!s) continue;
+        int64_t n = rows ? rows[i] : i;
+        for (int64_t g = 0; g < K / 32; ++g) s[g] = orc_half_to_f64(scales[n * (K / 32) + g]);
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          int q = (int)code_at(words, K, n, k);
+          acc += ((double)(q - 7) * s[k / 32]) * x[k];
+        }
+        Y[m * n_rows + i] = acc;
       }
-      Y[m * n_rows + i] = acc;
+      free(s);
     }
   }
   free(x);
-  free(s);
-  return 0;
+  return bad ? -1 : 0;
 }
 
 /* Exact evaluation of the same sum in __int128 (units of 2^-48), rounded once
@@ -201,33 +237,45 @@ ORC_EXPORT int orc_gemv_exact(const uint32_t* words, const uint16_t* scales, con
                               int64_t M, int64_t N, int64_t K, const int64_t* rows,
                               int64_t n_rows, double* Y64, uint16_t* Y16) {
   if (M < 1 || N < 1 || K < 32 || K % 32 || K > (1 << 20)) return -1;
-  for (int64_t m = 0; m < M; ++m)
+  for (int64_t i = 0; i < n_rows; ++i)
+    if ((rows ? rows[i] : i) < 0 || (rows ? rows[i] : i) >= N) return -1;
+  int bad = 0;
+  for (int64_t m = 0; m < M; ++m) {
+#pragma omp parallel for num_threads(g_threads) schedule(dynamic, 16) reduction(| : bad)
     for (int64_t i = 0; i < n_rows; ++i) {
       int64_t n = rows ? rows[i] : i;
-      if (n < 0 || n >= N) return -1;
       __int128 acc = 0;
-      for (int64_t k = 0; k < K; ++k) {
+      int finite = 1;
+      for (int64_t k = 0; k < K && finite; ++k) {
         int64_t sv, xv;
-        if (!half_to_fixed24(scales[n * (K / 32) + k / 32], &sv)) return -2;
-        if (!half_to_fixed24(X[m * K + k], &xv)) return -2;
+        finite = half_to_fixed24(scales[n * (K / 32) + k / 32], &sv) &&
+                 half_to_fixed24(X[m * K + k], &xv);
+        if (!finite) break;
         int q = (int)code_at(words, K, n, k);
         acc += (__int128)(q - 7) * (__int128)sv * (__int128)xv;
+      }
+      if (!finite) {
+        bad = 1;
+        continue;
       }
       int neg = acc < 0;
       unsigned __int128 mag = neg ? (unsigned __int128)(-acc) : (unsigned __int128)acc;
       if (Y64) Y64[m * n_rows + i] = exact_to_f64(neg, mag, -48);
       if (Y16) Y16[m * n_rows + i] = exact_to_half(neg, mag, -48);
     }
-  return 0;
+  }
+  return bad ? -2 : 0;
 }
 
 /* ||W_n||_2 with W_n[k] = (q[n][k] - 7) * s[n][k/32], for n = rows[i]. */
 ORC_EXPORT int orc_row_norms(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
                              const int64_t* rows, int64_t n_rows, double* out) {
   if (N < 1 || K < 32 || K % 32) return -1;
+  for (int64_t i = 0; i < n_rows; ++i)
+    if ((rows ? rows[i] : i) < 0 || (rows ? rows[i] : i) >= N) return -1;
+#pragma omp parallel for num_threads(g_threads) schedule(dynamic, 16)
   for (int64_t i = 0; i < n_rows; ++i) {
     int64_t n = rows ? rows[i] : i;
-    if (n < 0 || n >= N) return -1;
     double acc = 0.0;
     for (int64_t k = 0; k < K; ++k) {
       double w = (double)((int)code_at(words, K, n, k) - 7) *
@@ -273,8 +321,13 @@ ORC_EXPORT void orc_silu_mul(const uint16_t* GU, uint16_t* OUT, int64_t M, int64
  *     group's 32 codes are the 3-bit fields [3i, 3i + 3) of its three
  *     little-endian words taken as one 96-bit value; weight = (q - 3) * s.
  *   format 2, q4f32_1: q4f16_1's codes with fp32 scales; x and y fp32.
- *   format 3, MLX affine 4-bit, group 64: q4f16_1's nibble order, an fp16 scale
- *     and an fp16 bias per 64 weights; weight = s * q + b.
+ *   format 3, MLX affine 4-bit, group 64 (af4g64): q4f16_1's nibble order, a
+ *     bf16 scale and a bf16 bias per 64 weights; weight = s * q + b (Splash
+ *     docs/models.md, "MLX targets": an affine weight is s * q + z for its
+ *     group's bf16 .scales and .biases, codes packed little-endian in 32-bit
+ *     words; Zero TVM documentation: affine w = s*q + b, group 64).
+ *   format 4, the same with fp16 scales and biases (an extra variant, not the
+ *     pages' format).
  * W[n][k] for one element, in fp64. */
 static double fmt_weight(int format, const uint32_t* words, const void* scales,
                          const void* biases, int64_t K, int64_t n, int64_t k) {
@@ -294,18 +347,20 @@ static double fmt_weight(int format, const uint32_t* words, const void* scales,
     const float s = ((const float*)scales)[n * (K / 32) + k / 32];
     return ((double)q - 7.0) * (double)s;
   }
-  const double s = orc_half_to_f64(((const uint16_t*)scales)[n * (K / 64) + k / 64]);
-  const double b = orc_half_to_f64(((const uint16_t*)biases)[n * (K / 64) + k / 64]);
+  const uint16_t sh = ((const uint16_t*)scales)[n * (K / 64) + k / 64];
+  const uint16_t bh = ((const uint16_t*)biases)[n * (K / 64) + k / 64];
+  const double s = format == 3 ? orc_bf16_to_f64(sh) : orc_half_to_f64(sh);
+  const double b = format == 3 ? orc_bf16_to_f64(bh) : orc_half_to_f64(bh);
   return s * (double)q + b;
 }
 
 /* Y[i] = sum_k W[n][k] * x[k] (n = rows[i], or i when rows is NULL), fp64, k
- * ascending; x is fp16 bits (formats 1, 3) or fp32 (format 2).  Also the row
+ * ascending; x is fp16 bits (formats 1, 3, 4) or fp32 (format 2).  Also the row
  * norms ||W_n||_2 into NORMS when not NULL.  Returns 0, or -1 on a bad shape. */
 ORC_EXPORT int orc_gemv_format(int format, const uint32_t* words, const void* scales,
                                const void* biases, const void* X, int64_t N, int64_t K,
                                const int64_t* rows, int64_t n_rows, double* Y, double* NORMS) {
-  if (format < 1 || format > 3 || N < 1 || K < 32 || K % 32 || (format == 3 && K % 64))
+  if (format < 1 || format > 4 || N < 1 || K < 32 || K % 32 || (format >= 3 && K % 64))
     return -1;
   for (int64_t i = 0; i < n_rows; ++i) {
     const int64_t n = rows ? rows[i] : i;

@@ -272,8 +272,8 @@ MUTATIONS = {
              "acc += ((double)(7 - q) * s[k / 32]) * x[k];"),
     "scale_index": ("acc += ((double)(q - 7) * s[k / 32]) * x[k];",
                     "acc += ((double)(q - 7) * s[k / 8 % (K / 32)]) * x[k];"),
-    "dropped_term": ("for (int64_t k = 0; k < K; ++k) {\n        int q = (int)code_at(words, K, n, k);\n        acc +=",
-                     "for (int64_t k = 0; k < K - 1; ++k) {\n        int q = (int)code_at(words, K, n, k);\n        acc +="),
+    "dropped_term": ("for (int64_t k = 0; k < K; ++k) {\n          int q = (int)code_at(words, K, n, k);\n          acc +=",
+                     "for (int64_t k = 0; k < K - 1; ++k) {\n          int q = (int)code_at(words, K, n, k);\n          acc +="),
     "nibble_order": ("return (w >> (4 * (k % 8))) & 0xFu;", "return (w >> (4 * (7 - k % 8))) & 0xFu;"),
     "transposed": ("uint32_t w = words[n * (K / 8) + k / 8];", "uint32_t w = words[(k / 8) * (K / 8) + n % (K / 8)];"),
     "zero_point_8": ("acc += ((double)(q - 7) * s[k / 32]) * x[k];",
@@ -575,6 +575,16 @@ def _format_case(fmt, N=6, K=128, seed=3):
         s32 = (rng.standard_normal((N, K // 32)) * 0.02).astype(np.float32)
         W = (c.astype(np.float64) - 7) * np.repeat(s32.astype(np.float64), 32, axis=1)
         return w, s32, None, W
+    if fmt == "af4g64":
+        # bf16 scales and biases: the upper halves of fp32 values, decoded through
+        # numpy's float32 view of (bits << 16)
+        sb = ((rng.standard_normal((N, K // 64)) * 0.02).astype(np.float32).view(np.uint32)
+              >> 16).astype(np.uint16)
+        bb = ((rng.standard_normal((N, K // 64)) * 0.1).astype(np.float32).view(np.uint32)
+              >> 16).astype(np.uint16)
+        sv, bv = _np_bf16(sb), _np_bf16(bb)
+        W = (c.astype(np.float64) * np.repeat(sv, 64, axis=1) + np.repeat(bv, 64, axis=1))
+        return w, sb, bb, W
     s16 = (rng.standard_normal((N, K // 64)) * 0.02).astype(np.float16)
     b16 = (rng.standard_normal((N, K // 64)) * 0.1).astype(np.float16)
     W = (c.astype(np.float64) * np.repeat(s16.astype(np.float64), 64, axis=1) +
@@ -582,7 +592,26 @@ def _format_case(fmt, N=6, K=128, seed=3):
     return w, s16.view(np.uint16), b16.view(np.uint16), W
 
 
-@pytest.mark.parametrize("fmt", ["q3f16_1", "q4f32_1", "af4g64"])
+def _np_bf16(h):
+    """bf16 bit patterns -> float64 through numpy's float32 (bits << 16)."""
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_bf16_decode_every_pattern():
+    # every bf16 bit pattern against numpy's float32 view of the same bits << 16
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = _np_bf16(h)
+    got = np.array([oracle.bf16_to_f64(int(v)) for v in h])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))   # -0
+    # closed forms: 1.0 = 0x3F80, -2.0 = 0xC000, smallest subnormal 2^-133
+    assert oracle.bf16_to_f64(0x3F80) == 1.0 and oracle.bf16_to_f64(0xC000) == -2.0
+    assert oracle.bf16_to_f64(0x0001) == 2.0 ** -133
+
+
+@pytest.mark.parametrize("fmt", ["q3f16_1", "q4f32_1", "af4g64", "af4g64_f16"])
 def test_format_gemv_vs_numpy(fmt):
     N, K = 6, 128
     w, s, b, W = _format_case(fmt, N, K)
@@ -613,21 +642,34 @@ def test_format_closed_forms():
     x = np.full(K, np.float16(1.0)).view(np.uint16)
     y, _ = oracle.gemv_format("q3f16_1", _pack_q3(c), s, None, x, K)
     assert list(y) == [0.0, 4.0 * K]
-    # affine: codes 0, bias b -> b * sum(x)
+    # affine: codes 0, bias b -> b * sum(x); codes 15, scale s, bias 0 -> 15 s sum(x)
     w = oracle.pack(np.zeros((1, K), np.uint8))
     sc = np.full((1, 1), np.float16(0.5)).view(np.uint16)
     bi = np.full((1, 1), np.float16(0.25)).view(np.uint16)
-    y, _ = oracle.gemv_format("af4g64", w, sc, bi, x, K)
+    y, _ = oracle.gemv_format("af4g64_f16", w, sc, bi, x, K)
     assert y[0] == 0.25 * K
+    # bf16 0.25 = 0x3E80, 0.5 = 0x3F00 (the same values, other bit patterns)
+    y, _ = oracle.gemv_format("af4g64", w, np.full((1, 1), 0x3F00, np.uint16),
+                              np.full((1, 1), 0x3E80, np.uint16), x, K)
+    assert y[0] == 0.25 * K
+    w15 = oracle.pack(np.full((1, K), 15, np.uint8))
+    y, _ = oracle.gemv_format("af4g64", w15, np.full((1, 1), 0x3F00, np.uint16),
+                              np.zeros((1, 1), np.uint16), x, K)
+    assert y[0] == 15 * 0.5 * K
 
 
 FORMAT_MUTATIONS = {
     "q3_zero_point": ("return ((double)q - 3.0) * s;", "return ((double)q - 4.0) * s;"),
     "q3_bit_order": ("const int64_t bit = 3 * i + b;", "const int64_t bit = 3 * i + (2 - b);"),
     "q4f32_zero_point": ("return ((double)q - 7.0) * (double)s;", "return ((double)q - 8.0) * (double)s;"),
-    "affine_group_32": ("const double s = orc_half_to_f64(((const uint16_t*)scales)[n * (K / 64) + k / 64]);",
-                        "const double s = orc_half_to_f64(((const uint16_t*)scales)[n * (K / 64) + k / 32 % (K / 64)]);"),
+    "affine_group_32": ("const uint16_t sh = ((const uint16_t*)scales)[n * (K / 64) + k / 64];",
+                        "const uint16_t sh = ((const uint16_t*)scales)[n * (K / 64) + k / 32 % (K / 64)];"),
     "affine_no_bias": ("return s * (double)q + b;", "return s * (double)q;"),
+    # the pages' affine format has bf16 scales and biases: reading them as fp16
+    "affine_bf16_read_as_fp16": ("const double s = format == 3 ? orc_bf16_to_f64(sh) : orc_half_to_f64(sh);",
+                                 "const double s = orc_half_to_f64(sh);"),
+    "affine_bf16_bias_as_fp16": ("const double b = format == 3 ? orc_bf16_to_f64(bh) : orc_half_to_f64(bh);",
+                                 "const double b = orc_half_to_f64(bh);"),
 }
 
 
@@ -645,13 +687,14 @@ def test_format_pins_catch_planted_mistake(name, monkeypatch):
                                path, "-lm"])
         real = oracle._load()
         mutant = C.CDLL(so)
-        for fn in ("orc_gemv_format", "orc_pack", "orc_unpack", "orc_half_to_f64"):
+        for fn in ("orc_gemv_format", "orc_pack", "orc_unpack", "orc_half_to_f64",
+                   "orc_bf16_to_f64"):
             f = getattr(mutant, fn)
             f.argtypes = getattr(real, fn).argtypes
             f.restype = getattr(real, fn).restype
         monkeypatch.setattr(oracle, "_lib", mutant)
         failed = 0
-        for fmt in ("q3f16_1", "q4f32_1", "af4g64"):
+        for fmt in ("q3f16_1", "q4f32_1", "af4g64", "af4g64_f16"):
             try:
                 test_format_gemv_vs_numpy(fmt)
             except AssertionError:
@@ -661,3 +704,24 @@ def test_format_pins_catch_planted_mistake(name, monkeypatch):
         except AssertionError:
             failed += 1
         assert failed, name
+
+
+def test_thread_count_does_not_change_results():
+    # the row loops on several threads compute every row by the same steps
+    m = synth.Matrix("t/threads", 300, 1024)
+    w, sc = m.words(), m.scales()
+    X = synth.activations("t/threads/x", 0, 3 * 1024).reshape(3, 1024)
+    rows = np.array([299, 0, 17, 150])
+    old = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
+        a = oracle.gemv_f64(w, sc, X), oracle.gemv_exact(w, sc, X), oracle.row_norms(w, sc)
+        ar = oracle.gemv_f64(w, sc, X, rows=rows)
+        oracle.set_threads(7)
+        b = oracle.gemv_f64(w, sc, X), oracle.gemv_exact(w, sc, X), oracle.row_norms(w, sc)
+        br = oracle.gemv_f64(w, sc, X, rows=rows)
+    finally:
+        oracle.set_threads(old)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+    assert np.array_equal(a[1][0], b[1][0]) and np.array_equal(a[1][1], b[1][1])
+    assert np.array_equal(ar, br) and np.array_equal(ar, a[0][:, rows])
