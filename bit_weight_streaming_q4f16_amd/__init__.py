@@ -20,7 +20,7 @@ __all__ = [
     "Q4Error", "load", "lib_path", "q4_version", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemv_splitk", "q4_gemv_batched", "q4_gemv_batched_noalloc", "q4_workspace_bytes", "q4_splitk_workspace_bytes",
     "q4_decode_step", "q4_decode_step_workspace_bytes", "q4_probe_read", "q4_probe_copy",
-    "Layer", "STEP_LAUNCH_EACH", "STEP_ORDERED", "STEP_LDS_RING", "STEP_WS_CLEAN", "make_layers",
+    "Layer", "STEP_LAUNCH_EACH", "STEP_ORDERED", "STEP_WS_CLEAN", "make_layers",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +31,6 @@ _lib = None
 Q4_NOALLOC_SCRATCH_BYTES = 4 * 1024 * 1024   # include/q4f16.h
 STEP_LAUNCH_EACH = 0x1
 STEP_ORDERED = 0x2
-STEP_LDS_RING = 0x4
 STEP_WS_CLEAN = 0x8
 STEP_PERSISTENT = 0x10
 X_PLAIN = 0
@@ -39,7 +38,8 @@ X_SILU_MUL = 1
 TOKENS_EAGER = 0x1
 FMT_Q3F16_1 = 1
 FMT_Q4F32_1 = 2
-FMT_AF4_G64 = 3
+FMT_AF4_G64 = 3       # bf16 scales and biases (the pages' MLX affine format)
+FMT_AF4_G64_F16 = 4   # the same with fp16 scales and biases (extra variant)
 FMT_LOAD_STAGED = 0x100   # OR-ed into FMT_Q3F16_1: force one way of loading
 FMT_LOAD_DIRECT = 0x200
 MODEL_FACTORED_NORM = 0x1   # q4_model.options: norms folded into the GEMVs they feed

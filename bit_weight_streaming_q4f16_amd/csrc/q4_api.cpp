@@ -15,7 +15,6 @@
 #include <algorithm>
 #include <cstring>
 
-#include "q4_step_dma.h"
 #include "q4_step_mfma.h"
 #include "q4_formats.h"
 
@@ -326,21 +325,6 @@ bool use_persistent(const q4::DeviceInfo& d, const q4::StepPlan& p, int64_t M, u
   return true;
 }
 
-// The register kernel's dependencies with completion counters only (no tagged
-// hand-over), as the LDS-ring kernel keeps them.
-q4::StepPlan counter_plan(const q4::DeviceInfo& d, const std::vector<q4::StepLayer>& sl,
-                          int64_t n, uint32_t flags, std::vector<int>* dep,
-                          std::vector<int>* sig) {
-  q4::StepPlan cp = q4::plan_step(d, sl.data(), n, (flags & Q4_STEP_ORDERED) != 0, false);
-  dep->assign(cp.desc.size(), -1);
-  sig->assign(cp.desc.size(), 0);
-  for (size_t i = 0; i < cp.desc.size(); ++i) {
-    (*dep)[i] = cp.desc[i].dep;
-    (*sig)[i] = (cp.desc[i].flags & q4::kPublish) != 0;
-  }
-  return cp;
-}
-
 // One kernel per descriptor: the largest split-K partials of any descriptor, then
 // (for descriptors with Q4_X_SILU_MUL) the largest glue output, M * K fp16.
 struct EachLayout {
@@ -392,15 +376,6 @@ size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, 
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
     size_t b = q4::step_workspace_bytes(p);
     if (b > need) need = b;
-    if ((flags & Q4_STEP_LDS_RING) && !any_x_op(layers, n_layers)) {
-      std::vector<int> dep, sig;
-      q4::StepPlan cp = counter_plan(*d, sl, n_layers, flags, &dep, &sig);
-      if (cp.ok) {
-        q4::DmaPlan dp = q4::plan_step_dma(*d, sl.data(), n_layers, dep, sig);
-        b = q4::step_dma_workspace_bytes(dp);
-        if (b > need) need = b;
-      }
-    }
   }
   return need;
 }
@@ -413,8 +388,7 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (n_layers > (1 << 20))
     return fail(Q4_ERR_UNSUPPORTED, "q4_decode_step: n_layers = %lld: too many",
                 (long long)n_layers);
-  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED | Q4_STEP_LDS_RING | Q4_STEP_WS_CLEAN |
-                Q4_STEP_PERSISTENT))
+  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED | Q4_STEP_WS_CLEAN | Q4_STEP_PERSISTENT))
     return fail(Q4_ERR_SHAPE, "q4_decode_step: unknown flags 0x%x", flags);
   char what[64];
   for (int64_t i = 0; i < n_layers; ++i) {
@@ -460,23 +434,6 @@ int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t
   if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
     std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
     q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
-    if ((flags & Q4_STEP_LDS_RING) && !any_x_op(layers, n_layers)) {
-      std::vector<int> dep, sig;
-      q4::StepPlan cp = counter_plan(*d, sl, n_layers, flags, &dep, &sig);
-      q4::DmaPlan dp = q4::plan_step_dma(*d, sl.data(), n_layers, dep, sig);
-      int per_cu = 0;
-      if (cp.ok && dp.ok && q4::step_dma_occupancy(dp, &per_cu) == hipSuccess && per_cu >= 1) {
-        if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_dma_workspace_bytes(dp)))
-          return rc;
-        hipError_t e = hipSuccess;
-        const void* table = device_table(dp.desc.data(), dp.desc.size() * sizeof(q4::DmaDesc),
-                                         d->id, s, &e);
-        if (!table) return device_error(e, "q4_decode_step: descriptor table");
-        e = q4::launch_step_dma(dp, static_cast<const q4::DmaDesc*>(table), ws, s);
-        return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
-      }
-      (void)hipGetLastError();
-    }
     if (use_persistent(*d, p, M, flags)) {
       if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_workspace_bytes(p)))
         return rc;
@@ -608,12 +565,13 @@ int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_stream_t
 }
 
 size_t q4_format_weight_bytes(uint32_t format, int64_t N, int64_t K) {
-  if (N < 1 || K < 32 || K % 32 || format > Q4_FMT_AF4_G64) return 0;
-  if (format == Q4_FMT_AF4_G64 && K % 64) return 0;
+  if (N < 1 || K < 32 || K % 32 || format > Q4_FMT_AF4_G64_F16) return 0;
+  if (format >= Q4_FMT_AF4_G64 && K % 64) return 0;
   switch (format) {
     case Q4_FMT_Q3F16_1: return (size_t)N * (size_t)(K / 32) * (12 + 2);
     case Q4_FMT_Q4F32_1: return (size_t)N * (size_t)(K / 32) * (16 + 4);
-    case Q4_FMT_AF4_G64: return (size_t)N * (size_t)(K / 64) * (32 + 2 + 2);
+    case Q4_FMT_AF4_G64:
+    case Q4_FMT_AF4_G64_F16: return (size_t)N * (size_t)(K / 64) * (32 + 2 + 2);
     default: return (size_t)N * (size_t)(K / 32) * (16 + 2);
   }
 }
@@ -623,12 +581,13 @@ int q4_gemv_format(uint32_t format, const uint32_t* words, const void* scales,
                    q4_stream_t stream) {
   const uint32_t load = format & (Q4_FMT_LOAD_STAGED | Q4_FMT_LOAD_DIRECT);
   format &= ~(Q4_FMT_LOAD_STAGED | Q4_FMT_LOAD_DIRECT);
-  if (format < Q4_FMT_Q3F16_1 || format > Q4_FMT_AF4_G64)
+  if (format < Q4_FMT_Q3F16_1 || format > Q4_FMT_AF4_G64_F16)
     return fail(Q4_ERR_SHAPE, "q4_gemv_format: format = %u: unknown", format);
   if (load && (format != Q4_FMT_Q3F16_1 || load == (Q4_FMT_LOAD_STAGED | Q4_FMT_LOAD_DIRECT)))
     return fail(Q4_ERR_SHAPE, "q4_gemv_format: a load bit is for q3f16_1 only, one at a time");
   if (!words || !scales || !x || !y) return fail(Q4_ERR_NULL, "q4_gemv_format: NULL pointer");
-  const bool affine = format == Q4_FMT_AF4_G64, f32 = format == Q4_FMT_Q4F32_1;
+  const bool affine = format == Q4_FMT_AF4_G64 || format == Q4_FMT_AF4_G64_F16;
+  const bool f32 = format == Q4_FMT_Q4F32_1;
   if (affine != (biases != nullptr))
     return fail(affine ? Q4_ERR_NULL : Q4_ERR_SHAPE,
                 "q4_gemv_format: biases must be given for the affine format only");
@@ -656,7 +615,7 @@ int q4_gemv_format(uint32_t format, const uint32_t* words, const void* scales,
   else if (affine)
     e = q4::launch_gemv_affine(*d, words, static_cast<const uint16_t*>(scales), biases,
                                static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), N, K,
-                               st);
+                               format == Q4_FMT_AF4_G64, st);
   else
     e = q4::launch_gemv_format(*d, (int)format, words, scales, biases, x, y, N, K, st);
   return e == hipSuccess ? ok() : device_error(e, "q4_gemv_format");

@@ -13,9 +13,10 @@ hipError_t launch_gemv_q3(const DeviceInfo& d, const uint32_t* W, const uint16_t
                           hipStream_t s);
 
 // y = W x at M = 1 in the MLX affine 4-bit format, group 64 (q4_gemv.hip: the
-// q4f16_1 GEMV with a scale and a bias per two of its groups).  K <= 32768.
+// q4f16_1 GEMV with a scale and a bias per two of its groups); bf16 scales and
+// biases (the pages' format) or fp16 ones.  K <= 32768.
 hipError_t launch_gemv_affine(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
                               const uint16_t* B, const uint16_t* X, uint16_t* Y, int64_t N,
-                              int64_t K, hipStream_t s);
+                              int64_t K, bool bf16, hipStream_t s);
 
 }  // namespace q4

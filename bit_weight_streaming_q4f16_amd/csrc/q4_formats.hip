@@ -438,7 +438,7 @@ hipError_t launch_gemv_format(const DeviceInfo& d, int format, const uint32_t* W
     default:
       return launch_gemv_affine(d, W, static_cast<const uint16_t*>(S), B,
                                 static_cast<const uint16_t*>(X), static_cast<uint16_t*>(Y), N, K,
-                                s);
+                                format == 3, s);
   }
 }
 

@@ -129,17 +129,23 @@ __device__ __forceinline__ int slice_begin(int G, int splits, int s) {
 //
 // Modes: kPlain writes y (or split-K partials); kGlu (q4_fused.h) computes rows
 // i and F + i (F = N, the matrix has 2N rows) and writes silu_mul_h of the two
-// rounded results; kAffine (q4_formats.h; the MLX affine 4-bit checkpoints of
-// the Zero TVM documentation: the same nibble layout, one fp16 scale s and bias
-// b per 64 weights, i.e. per two 16-byte groups) adds s * sum((q - 7) x) +
-// (b + 7 s) * sum(x) per 32 weights, the sums of x staged beside x.  kAffine
-// needs one slice.  kPlainNorm and kGluNorm (q4_fused.h) are kPlain and kGlu
+// rounded results; kAffineB (q4_formats.h; the MLX affine 4-bit format of the
+// Splash models page, "MLX targets": the same nibble layout, one bf16 scale s
+// and bf16 bias b per 64 weights, i.e. per two 16-byte groups) adds
+// s * sum((q - 7) x) + (b + 7 s) * sum(x) per 32 weights, the sums of x staged
+// beside x; kAffine is the same with fp16 scales and biases.  Both need one
+// slice.  kPlainNorm and kGluNorm (q4_fused.h) are kPlain and kGlu
 // with the residual add and RMSNorm of their input folded in, factored so that no
 // reduction precedes the staging: x = h * gamma is staged (h = res_in + delta,
 // rounded to fp16 as the RMSNorm kernel rounds it, and written to res_out by
 // workgroup 0), sum(h^2) is formed alongside, and every output is scaled by
 // 1 / sqrt(sum(h^2) / K + eps) before its rounding.  They need one slice.
-enum : int { kPlain = 0, kGlu = 1, kAffine = 2, kPlainNorm = 3, kGluNorm = 4 };
+enum : int { kPlain = 0, kGlu = 1, kAffine = 2, kPlainNorm = 3, kGluNorm = 4, kAffineB = 5 };
+
+// A bf16 bit pattern is the upper half of the fp32 with the same value.
+__device__ __forceinline__ float bf16_to_float(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
 
 template <int LPR, int UNR, int MODE>
 __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
@@ -151,7 +157,9 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
                                                     int splits, NormIn nin) {
   extern __shared__ uint4 xs[];
   __shared__ float ssw[kBlock / 64];
-  constexpr bool kAff = MODE == kAffine;
+  constexpr bool kAff = MODE == kAffine || MODE == kAffineB;
+  // scale (and bias) of a group as fp32
+  auto sval = [](uint16_t h) { return MODE == kAffineB ? bf16_to_float(h) : half_to_float(h); };
   constexpr bool kNin = MODE == kPlainNorm || MODE == kGluNorm;
   const int split = blockIdx.y;
   const int g0 = slice_begin(G, splits, split);
@@ -241,10 +249,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
           const int graw = t0 + u * LPR + lane;
           const int g = graw < gc ? graw : gc - 1;
           const float p = group_dot(wv[q][u], xs, gc, g);
-          const float sc = half_to_float(sv[q][u]);
+          const float sc = sval(sv[q][u]);
           float t = __builtin_fmaf(p, sc, acc[q]);
           if constexpr (kAff)
-            t = __builtin_fmaf(__builtin_fmaf(7.f, sc, half_to_float(bv[q][u])), xsum[g], t);
+            t = __builtin_fmaf(__builtin_fmaf(7.f, sc, sval(bv[q][u])), xsum[g], t);
           acc[q] = graw < gc ? t : acc[q];
         }
       }
@@ -460,7 +468,7 @@ hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, cons
   const int64_t cap = (int64_t)d.cus * (kNin ? 2 : 8);
   if (blocks > cap) blocks = cap;
   const int64_t gmax = (G + p.splits - 1) / p.splits;
-  const size_t lds = (size_t)gmax * (MODE == kAffine ? 68 : 64);
+  const size_t lds = (size_t)gmax * (MODE == kAffine || MODE == kAffineB ? 68 : 64);
   const dim3 grid((unsigned)blocks, (unsigned)p.splits);
   if (hipError_t e = allow_lds(k_gemv_m1<LPR, UNR, MODE>, lds)) return e;
   hipLaunchKernelGGL((k_gemv_m1<LPR, UNR, MODE>), grid, dim3(kBlock), lds, s,
@@ -585,11 +593,12 @@ hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p
 
 hipError_t launch_gemv_affine(const DeviceInfo& d, const uint32_t* W, const uint16_t* S,
                               const uint16_t* B, const uint16_t* X, uint16_t* Y, int64_t N,
-                              int64_t K, hipStream_t s) {
+                              int64_t K, bool bf16, hipStream_t s) {
   const GemvArgs a{W, S, X, Y, 1, N, K};
   const GemvPlan p = plan_splits(d, 1, N, K, 1);
   if ((size_t)(K / 32) * 68 > d.lds_per_block) return hipErrorInvalidValue;
-  return launch_m1_lpr<kAffine>(a, p, nullptr, d, s, B);
+  return bf16 ? launch_m1_lpr<kAffineB>(a, p, nullptr, d, s, B)
+              : launch_m1_lpr<kAffine>(a, p, nullptr, d, s, B);
 }
 
 hipError_t launch_gemv_norm_in(const DeviceInfo& d, const uint32_t* words,

@@ -21,7 +21,7 @@
 //    to K = 8192.  Results go to an LDS y buffer: these waves never wait on a
 //    global store (on gfx9 stores and loads share one in-order counter).
 //  * 4 sync waves, each owning every 4th GEMV: stage x of the GEMV into one of
-//    8 LDS buffers (pair-ordered, with per-group bias terms) once the GEMVs it
+//    8 LDS buffers (pair-ordered, with per-group offset terms) once the GEMVs it
 //    depends on are complete on every workgroup, copy finished y rows from LDS
 //    to memory, and publish per-GEMV completion with an agent-scope atomic that
 //    other workgroups poll.  Their waits never hold back the weight stream.
@@ -113,54 +113,57 @@ __device__ __forceinline__ uint4 pair_order(uint4 v) {
   return o;
 }
 
-// The nibble-pair constants.  OR-ing nibbles 0 and 4 (mask 0x000F000F) into two
-// fp16 values with exponent 2^10 gives (1024 + q0, 1024 + q4); nibbles 1 and 5
-// (mask 0x00F000F0, place value 16) under exponent 2^6 (ulp 1/16) give
-// (64 + q1, 64 + q5); the same on word >> 8 gives elements 2, 6 and 3, 7.  The
-// masks live in VGPRs and the exponents in SGPRs, so each pair is ONE
-// v_and_or_b32 (gfx9 VOP3 takes one scalar operand and no literal).
+// The nibble-pair masks.  AND-ing a word with 0x000F000F leaves nibbles 0 and 4
+// as the mantissas of two fp16 subnormals, the exact values (q0, q4) * 2^-24;
+// with 0x00F000F0, nibbles 1 and 5 sit one mantissa position higher, (q1, q5) *
+// 2^-20; the same on word >> 8 gives elements 2, 6 and 3, 7.  Each pair is ONE
+// v_and_b32, with no exponent to insert and no offset to remove: the zero point
+// is taken off once per group (see group_dot).  The masks live in VGPRs.
 struct Nibbles {
-  uint32_t m_lo, m_hi;   // VGPR: 0x000F000F, 0x00F000F0
-  uint32_t e_lo, e_hi;   // SGPR: 0x64006400 (1024, 1024), 0x54005400 (64, 64)
+  uint32_t m_lo, m_hi;   // 0x000F000F, 0x00F000F0
 };
 
 __device__ __forceinline__ Nibbles make_nibbles() {
-  Nibbles n{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+  Nibbles n{0x000F000Fu, 0x00F000F0u};
   asm volatile("" : "+v"(n.m_lo), "+v"(n.m_hi));
-  asm volatile("" : "+s"(n.e_lo), "+s"(n.e_hi));
   return n;
 }
 
-// One 32-weight group: sum_k (q_k - 7) x_k in fp32.  The dequantised values are
-// t_k = 1024 + q_k (k even) or 64 + q_k (k odd); the chain is seeded with minus
-// the group's bias term 1031 * sum(x at even k) + 71 * sum(x at odd k), so what
-// is left is the wanted sum.  x holds the group's four pair-ordered blocks.
-__device__ __forceinline__ float group_dot(uint4 w, const uint4 (&x)[4], float neg_bias,
-                                          const Nibbles& nb) {
+// One 32-weight group: 2^-20 * sum_k q_k x_k in fp32, from the codes as fp16
+// subnormals (products exact in fp32) and two chains of v_dot2, even and odd
+// positions, joined as 16 * even + odd (exact scaling).  x holds the group's
+// four pair-ordered blocks.  The wanted 2^-20 * sum_k (q_k - 7) x_k is this minus
+// the same function of a word whose codes are all 7 (0x77777777) with the same x,
+// which the sync waves compute once per group when they stage x: both are the
+// same instructions on the same operands, so a group of codes 7 gives exactly
+// zero, and integer codes and x give the exact integer.  The factor 2^20 is
+// applied to the row's sum.
+__device__ __forceinline__ float group_dot(uint4 w, const uint4 (&x)[4], const Nibbles& nb) {
   const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
   // the first product of each chain in the three-operand form: the compiler
   // would otherwise copy the start value into the accumulator of v_dot2c
   float a, b;
   {
     const uint32_t v = wj[0];
-    asm("v_dot2_f32_f16 %0, %1, %2, %3"
-        : "=v"(a)
-        : "v"((v & nb.m_lo) | nb.e_lo), "v"(x[0].x), "v"(neg_bias));
-    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(b) : "v"((v & nb.m_hi) | nb.e_hi), "v"(x[0].y));
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(a) : "v"(v & nb.m_lo), "v"(x[0].x));
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(b) : "v"(v & nb.m_hi), "v"(x[0].y));
     const uint32_t v8 = v >> 8;
-    a = __builtin_amdgcn_fdot2(bits<h2_t>((v8 & nb.m_lo) | nb.e_lo), bits<h2_t>(x[0].z), a, false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>((v8 & nb.m_hi) | nb.e_hi), bits<h2_t>(x[0].w), b, false);
+    a = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_lo), bits<h2_t>(x[0].z), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_hi), bits<h2_t>(x[0].w), b, false);
   }
 #pragma unroll
   for (int j = 1; j < 4; ++j) {
     const uint32_t v = wj[j], v8 = v >> 8;
-    a = __builtin_amdgcn_fdot2(bits<h2_t>((v & nb.m_lo) | nb.e_lo), bits<h2_t>(x[j].x), a, false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>((v & nb.m_hi) | nb.e_hi), bits<h2_t>(x[j].y), b, false);
-    a = __builtin_amdgcn_fdot2(bits<h2_t>((v8 & nb.m_lo) | nb.e_lo), bits<h2_t>(x[j].z), a, false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>((v8 & nb.m_hi) | nb.e_hi), bits<h2_t>(x[j].w), b, false);
+    a = __builtin_amdgcn_fdot2(bits<h2_t>(v & nb.m_lo), bits<h2_t>(x[j].x), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>(v & nb.m_hi), bits<h2_t>(x[j].y), b, false);
+    a = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_lo), bits<h2_t>(x[j].z), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_hi), bits<h2_t>(x[j].w), b, false);
   }
-  return a + b;
+  return __builtin_fmaf(a, 16.f, b);
 }
+
+// 2^20: the factor between group_dot's units and the products' (exact in fp32).
+constexpr float kDotUnit = 1048576.f;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -221,7 +224,7 @@ __device__ __forceinline__ int wg_step(int sbase, int srem, int wg) {
 //   xbuf[b]: 4 planes of maxG pair-ordered blocks (uint4); maxG is the largest
 //            padded group count (lanes per row x groups per lane) of the list,
 //            blocks past a GEMV's own G are zero
-//   cbuf[b]: maxG floats, the bias term of each group (zero past G)
+//   cbuf[b]: maxG floats, the offset term of each group (zero past G)
 //   ybuf[b]: ybuf_rows fp16 results of this workgroup's rows
 template <int B, int NX>
 __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restrict__ D, int n,
@@ -282,6 +285,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     // kSync, so GEMV k and the GEMV k - NX whose buffer it reuses have the same
     // owner.  Buffers and counters are indexed from j0.
     const int me = wave;
+    const Nibbles nbs = make_nibbles();
     int next_fin = j0 + me;            // next own GEMV to copy out and publish
     auto complete = [&](int i) {
       return (unsigned)lds_load(&sh.local_done[(i - j0) % NX]) >=
@@ -489,30 +493,23 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
             }
           }
         }
-        // pair-order the blocks into plane j = word j, and per group the bias
-        // term 1031 * sum(x at even k) + 71 * sum(x at odd k)
+        // pair-order the blocks into plane j = word j
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int i = i0 + u * 64 + lane;
-          if (u * 64 < batch && i0 + u * 64 < nblk) {   // whole quads (nblk % 4 == 0): uniform
-            float se = 0.f, so = 0.f;
-            if (i < nblk) {
-              xb[(i & 3) * maxG + (i >> 2)] = pair_order(v[u]);
-              const uint32_t wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          if (u * 64 < batch && i < nblk) xb[(i & 3) * maxG + (i >> 2)] = pair_order(v[u]);
+        }
+      }
+      // per group the offset term: the compute waves' chain over codes all 7
+      // with this x (see group_dot), read back from the planes just written
+      wait_lds();
+      {
+        const uint4 w7 = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
+        for (int g = lane; g < G; g += 64) {
+          uint4 xq[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const h2_t h = bits<h2_t>(wv[e]);
-                se += (float)h[0];
-                so += (float)h[1];
-              }
-            }
-            // the four blocks of a group sit in four consecutive lanes
-            se += dpp<0xB1>(se);
-            so += dpp<0xB1>(so);
-            se += dpp<0x4E>(se);
-            so += dpp<0x4E>(so);
-            if (i < nblk && (i & 3) == 0) cb[i >> 2] = __builtin_fmaf(1031.0f, se, 71.0f * so);
-          }
+          for (int q = 0; q < 4; ++q) xq[q] = xb[q * maxG + g];
+          cb[g] = group_dot(w7, xq, nbs);
         }
       }
       // groups past G up to the padded count read x = 0 and bias 0, so the
@@ -728,17 +725,17 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           uint4 x[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
-          const float nbias = -cb[lpr * t];
+          const float off = cb[lpr * t];
 #pragma unroll
           for (int p = 0; p < B; ++p) {
-            const float pd = group_dot(U.rw[p][t], x, nbias, nb);
+            const float pd = group_dot(U.rw[p][t], x, nb) - off;
             acc[p] = __builtin_fmaf(pd, (float)bits<_Float16>(U.rs[p][t]), acc[p]);
           }
         }
       }
 #pragma unroll
       for (int p = 0; p < B; ++p) {
-        const float r = team_sum(acc[p], lg);
+        const float r = team_sum(acc[p], lg) * kDotUnit;
         const int row = U.rrow[p] + (lane >> lg);
         if (li == 0 && row < U.rN[p])
           ybuf[xi * ybuf_rows + (row - U.rr0[p])] = bits<uint16_t>((_Float16)r);
@@ -768,11 +765,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           uint4 x[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
-          const float pd = group_dot(U.rw[p][t], x, -cb[lpr * t], nb);
+          const float pd = group_dot(U.rw[p][t], x, nb) - cb[lpr * t];
           acc = __builtin_fmaf(pd, (float)bits<_Float16>(U.rs[p][t]), acc);
         }
       }
-      acc = team_sum(acc, lg);
+      acc = team_sum(acc, lg) * kDotUnit;
       if (li == 0 && row < U.rN[p])
         ybuf[xi * ybuf_rows + (row - U.rr0[p])] = bits<uint16_t>((_Float16)acc);
     }

@@ -19,7 +19,7 @@ struct MStepDesc {
                          // with trem < 0 (range mode), tbase is the GEMV's first tile
                          // among the tiles of all GEMVs laid end to end
   int dep, signal;       // as in StepDesc
-  int xoff;              // byte offset of the GEMV's LDS region (X, bias terms, y rows)
+  int xoff;              // byte offset of the GEMV's LDS region (X, y rows)
   int rel;               // GEMV whose LDS region overlaps this one (-1: none): it must
                          // be finished before this one's X is staged
 };
@@ -38,7 +38,7 @@ struct MStepPlan {
 };
 
 // Persistent kernel for 2 <= M <= 8: every K a multiple of 128 and at most 8192,
-// every GEMV's LDS region (M*K*2 + K + rows*M*2 bytes) within the LDS.
+// every GEMV's LDS region (16 K + 2 M rows bytes) within the LDS.
 MStepPlan plan_step_mfma(const DeviceInfo& d, const StepLayer* layers, int64_t n, int M,
                          bool ordered);
 size_t step_mfma_workspace_bytes(const MStepPlan& p);

@@ -7,10 +7,11 @@
 // rows of X over one 32-weight group (rows past M are zero) and B = the group of
 // 16 weight rows, so one MFMA is one group of one 16-row tile and its per-group
 // scale is applied exactly, in fp32, to the result.  The weights enter B as the
-// exact fp16 values 1024 + q or 64 + q (one v_and_or_b32 per pair, as in the M = 1
-// kernels); the MFMA's accumulator input carries minus the per-group bias term
-// (1031 * sum of even-position x + 71 * sum of odd-position x, per row of X), so
-// each product is (q - 7) * x without a subtraction.
+// exact fp16 values q - 7: one v_and_or_b32 per pair places two codes in fp16
+// mantissas (1024 + q or 64 + q, as in the M = 1 kernels) and one packed fp16
+// add of -1031 or -71 takes the offset off, exactly (q - 7 is in [-7, 8]); the
+// MFMA's accumulator input is zero.  So a group whose codes are all 7 gives
+// exactly zero, and integer codes times integer X give the exact integer.
 //
 // One workgroup of 16 waves per compute unit:
 //  * 12 compute waves take this workgroup's 16-row tiles of every GEMV in list
@@ -23,10 +24,10 @@
 //    Otherwise in bursts of kChunks chunks of four groups: per lane one dwordx4
 //    (group c of row r, for lane = 16c + r) and one 8-byte load of the row's four
 //    scales, and a 4 x 4 exchange between lanes r, r + 16, r + 32, r + 48 leaves
-//    word c of each of the four groups in lane (c, r).  X and the bias terms come
-//    from LDS; results go to LDS.
-//  * 4 sync waves, each owning every 4th GEMV: stage its X (pair-ordered, with the
-//    bias terms) into the GEMV's LDS region once the GEMVs it depends on are
+//    word c of each of the four groups in lane (c, r).  X comes from LDS;
+//    results go to LDS.
+//  * 4 sync waves, each owning every 4th GEMV: stage its X (pair-ordered) into
+//    the GEMV's LDS region once the GEMVs it depends on are
 //    complete on every workgroup and the region's previous user is finished,
 //    copy finished rows of Y out, publish completion (as in the M = 1 kernel).
 // LDS regions are planned on the host as a ring: a GEMV's region is reused only
@@ -139,11 +140,9 @@ __device__ __forceinline__ TileDesc read_desc(const MStepDesc* d) {
 
 // LDS region of a GEMV (byte offsets from xoff): X planes [G][4][8] uint4 (rows m <
 // M used; the fixed stride lets the reads of a burst use immediate offsets from one
-// address), then the bias terms [G][8] float, then y [M][rows] fp16 (rows: this
-// workgroup's rows of the GEMV; the host sizes the region for the most any
-// workgroup has).
-__device__ __forceinline__ int corr_off(int, int G) { return 8 * G * 64; }
-__device__ __forceinline__ int ybuf_off(int, int G) { return 8 * G * 64 + G * 32; }
+// address), then y [M][rows] fp16 (rows: this workgroup's rows of the GEMV; the
+// host sizes the region for the most any workgroup has).
+__device__ __forceinline__ int ybuf_off(int, int G) { return 8 * G * 64; }
 
 __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __restrict__ D, int n,
                                                             int M, unsigned* __restrict__ done,
@@ -279,15 +278,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
           __builtin_amdgcn_s_sleep(1);
         }
       }
-      // X rows m < M: lane takes (m, g) pairs; bias terms for rows M..7 are zero
+      // X rows m < M: lane takes (m, g) pairs
       const __amdgpu_buffer_rsrc_t rx =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(d.X), 0, 0x7FFFFFFF, kRsrcFlags);
       const Q4_GLOBAL u32x4_g* X = (const Q4_GLOBAL u32x4_g*)d.X;
       uint4* xs = reinterpret_cast<uint4*>(lds + d.xoff);
-      float* cs = reinterpret_cast<float*>(lds + d.xoff + corr_off(M, G));
       for (int e = lane; e < 8 * G; e += 64) {
         const int g = e >> 3, m = e & 7;
-        float se = 0.f, so = 0.f;
         if (m < M) {
           uint4 v[4];
 #pragma unroll
@@ -301,18 +298,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
             v[c] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
           }
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            xs[(g * 4 + c) * 8 + m] = pair_order(v[c]);
-            const uint32_t wv[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const h2_t p = bits<h2_t>(wv[h]);
-              se += (float)p[0];
-              so += (float)p[1];
-            }
-          }
+          for (int c = 0; c < 4; ++c) xs[(g * 4 + c) * 8 + m] = pair_order(v[c]);
         }
-        cs[g * 8 + m] = -__builtin_fmaf(1031.0f, se, 71.0f * so);
       }
       wait_lds();
       if (lane == 0) lds_store(&sh.x_ready[(k - j0) % kSlots], k);
@@ -332,9 +319,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
     // ---------------------------------------------------------- compute waves
     const int cw = wave - kSync;
     const int c = lane >> 4, r = lane & 15;
+    // nibble masks (VGPR) and exponents (SGPR) of the pair decode, then the
+    // offsets -1031 and -71 as fp16 pairs (SGPR)
     uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, e_lo = 0x64006400u, e_hi = 0x54005400u;
+    uint32_t z_lo = 0xE407E407u, z_hi = 0xD470D470u;
     asm volatile("" : "+v"(m_lo), "+v"(m_hi));
     asm volatile("" : "+s"(e_lo), "+s"(e_hi));
+    asm volatile("" : "+s"(z_lo), "+s"(z_hi));
     struct Cursor {
       TileDesc d;
       int j, t, t_end, row0;     // GEMV, next tile, end tile, first row of the workgroup
@@ -447,7 +438,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       const int vo_w = (r * G + c) * 16, vo_s = r * G * 2;
       const int nch = G / 4;
       const bool wide = staged(d);
-      const int xo = d.xoff, co = d.xoff + corr_off(M, G);
+      const int xo = d.xoff;
       const int rows = cu.rows;
       const int wrow0 = cu.row0;
       // advance the cursor before the loads are consumed
@@ -455,23 +446,26 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       if (cu.t >= cu.t_end) enter(cu.j + 1);
 
       f4_t acc = {0.f, 0.f, 0.f, 0.f};
-      // Lane (c, r) supplies row r of A (X) and receives rows 4c..4c+3 of D (with
-      // the bias terms of those rows as its accumulator input).  Rows of X past M
-      // and the lanes with c >= 2 only feed rows of D that are never stored, so
-      // they read row M - 1 and the biases of rows 0..7 instead of zeros: every
-      // lane reads valid LDS without a branch.  Per group the addresses advance
-      // by a fixed stride from a per-lane base.
+      // Lane (c, r) supplies row r of A (X) and receives rows 4c..4c+3 of D.  Rows
+      // of X past M and the lanes with c >= 2 only feed rows of D that are never
+      // stored, so they read row M - 1 instead of zeros: every lane reads valid
+      // LDS without a branch.  Per group the addresses advance by a fixed stride
+      // from a per-lane base.
       const uint8_t* a_base = lds + xo + (c * 8 + (r < M ? r : M - 1)) * 16;
-      const uint8_t* c_base = lds + co + (c & 1) * 16;
       constexpr int a_step = 512;                     // X planes: bytes per group
       auto x_of = [&](int g) { return *reinterpret_cast<const uint4*>(a_base + g * a_step); };
-      auto bias_of = [&](int g) { return *reinterpret_cast<const f4_t*>(c_base + g * 32); };
+      // two codes as the exact fp16 pair (q - 7, q' - 7)
+      auto dq = [&](uint32_t t, uint32_t m, uint32_t e, uint32_t z) {
+        return bits<uint32_t>(bits<h2_t>((t & m) | e) + bits<h2_t>(z));
+      };
       // one group of the tile: B from word c of the group in lane (c, r), A = X rows
-      auto group_mma = [&](uint32_t vt, uint4 a, f4_t cin) {
+      const f4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+      auto group_mma = [&](uint32_t vt, uint4 a) {
         const uint32_t x8 = vt >> 8;
-        const uint4 bq = make_uint4((vt & m_lo) | e_lo, (vt & m_hi) | e_hi,
-                                    (x8 & m_lo) | e_lo, (x8 & m_hi) | e_hi);
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(bits<h8_t>(a), bits<h8_t>(bq), cin, 0, 0, 0);
+        const uint4 bq = make_uint4(dq(vt, m_lo, e_lo, z_lo), dq(vt, m_hi, e_hi, z_hi),
+                                    dq(x8, m_lo, e_lo, z_lo), dq(x8, m_hi, e_hi, z_hi));
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(bits<h8_t>(a), bits<h8_t>(bq), zero4, 0, 0,
+                                                      0);
       };
       // the group's scale, applied exactly in fp32
       auto scale_add = [&](f4_t dd, uint32_t sbits) {
@@ -531,25 +525,21 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
             if (e == 1 && !two) break;
             const int g0 = 16 * b + 8 * e;
             const u32x4_g sc = e == 0 ? sc0 : sc1;
-            // X and bias of the half's groups: one address each, immediate offsets
+            // X of the half's groups: one address, immediate offsets
             const uint8_t* const ab = a_base + g0 * a_step;
-            const uint8_t* const cbp = c_base + g0 * 32;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const uint4 w4 = wq[e][h];
               const uint32_t v[4] = {w4.x, w4.y, w4.z, w4.w};   // word c of group g0 + 4h + t
               uint4 xa[4];
-              f4_t cb[4];
 #pragma unroll
-              for (int t = 0; t < 4; ++t) {
+              for (int t = 0; t < 4; ++t)
                 xa[t] = *reinterpret_cast<const uint4*>(ab + (4 * h + t) * a_step);
-                cb[t] = *reinterpret_cast<const f4_t*>(cbp + (4 * h + t) * 32);
-              }
 #pragma unroll
               for (int t = 0; t < 4; t += 2) {
                 const uint32_t sw = sc[2 * h + t / 2];   // scales of groups g0 + 4h + t, + t + 1
-                const f4_t d0 = group_mma(v[t], xa[t], cb[t]);
-                const f4_t d1 = group_mma(v[t + 1], xa[t + 1], cb[t + 1]);
+                const f4_t d0 = group_mma(v[t], xa[t]);
+                const f4_t d1 = group_mma(v[t + 1], xa[t + 1]);
                 scale_add(d0, sw & 0xFFFFu);
                 scale_add(d1, sw >> 16);
               }
@@ -577,20 +567,16 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
             if (ch0 + q < nch) {
               const int g0 = (ch0 + q) * 4;
               uint4 xa[4];
-              f4_t cb[4];
 #pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                xa[t] = x_of(g0 + t);
-                cb[t] = bias_of(g0 + t);
-              }
+              for (int t = 0; t < 4; ++t) xa[t] = x_of(g0 + t);
               uint32_t v[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
               transpose4(v);                    // v[t]: word c of group g0 + t, row r
               const uint32_t sc[4] = {s[q][0] & 0xFFFFu, s[q][0] >> 16, s[q][1] & 0xFFFFu,
                                       s[q][1] >> 16};
 #pragma unroll
               for (int t = 0; t < 4; t += 2) {
-                const f4_t d0 = group_mma(v[t], xa[t], cb[t]);
-                const f4_t d1 = group_mma(v[t + 1], xa[t + 1], cb[t + 1]);
+                const f4_t d0 = group_mma(v[t], xa[t]);
+                const f4_t d1 = group_mma(v[t + 1], xa[t + 1]);
                 scale_add(d0, sc[t]);
                 scale_add(d1, sc[t + 1]);
               }
@@ -702,7 +688,7 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
     size_t cur = 0;
     for (int64_t k = 0; k < n; ++k) {
       MStepDesc& s = p.desc[(size_t)k];
-      const size_t sz = (size_t)8 * s.G * 64 + (size_t)s.G * 32 +
+      const size_t sz = (size_t)8 * s.G * 64 +
                         (((size_t)rows[(size_t)k] * M * 2 + 15) & ~(size_t)15);
       if (sz > cap) return false;
       if (cur + sz > cap) cur = 0;

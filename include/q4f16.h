@@ -175,12 +175,7 @@ typedef struct q4_layer {
  * between them).  Without this flag a descriptor waits only for earlier
  * descriptors whose y overlaps its x or y, or whose x overlaps its y. */
 #define Q4_STEP_ORDERED 0x2u
-/* Use the persistent kernel variant that copies the weights into an LDS ring by
- * DMA (global_load_lds) instead of streaming them through registers.  It applies
- * when every K is a multiple of 256 and every scales pointer is 16-byte aligned;
- * other lists ignore the flag.  Same results; slower on the lists measured so far,
- * kept for comparison. */
-#define Q4_STEP_LDS_RING 0x4u
+/* 0x4 is not used. */
 /* The workspace's counters are already zero: the workspace is fresh from a
  * zeroing allocation or was last used by a q4_decode_step call with the same
  * layer list and M (the persistent register-streaming kernel leaves them zero
@@ -273,19 +268,25 @@ Q4_API int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_s
 /* ------------------------------------------------------ format variants -- */
 /* Formats beside q4f16_1 (everything-webgpu AI.md, "Which quantization to
  * recompile with": q3f16_1 at 14 bytes and q4f32_1 at 20 bytes per 32 weights;
- * Zero TVM documentation: MLX affine checkpoints, w = s * q + b in groups of 64):
+ * Zero TVM documentation: MLX affine checkpoints, w = s * q + b in groups of 64;
+ * Splash docs/models.md, "MLX targets": the affine scale and bias are the
+ * group's bf16 .scales and .biases, the codes packed little-endian in 32-bit
+ * words):
  *   Q4_FMT_Q3F16_1: words uint32 [N][3K/32] -- a group of 32 weights is three
  *     consecutive words read as one little-endian 96-bit value, code i in its
  *     bits [3i, 3i + 3); scales fp16 [N][K/32]; weight = (q - 3) * s; x, y fp16.
  *   Q4_FMT_Q4F32_1: words as q4f16_1 ([N][K/8]); scales fp32 [N][K/32];
  *     weight = (q - 7) * s; x, y fp32.
- *   Q4_FMT_AF4_G64: words as q4f16_1; scales and biases fp16 [N][K/64];
- *     weight = s * q + b; x, y fp16.  K % 64 == 0.
+ *   Q4_FMT_AF4_G64: words as q4f16_1; scales and biases bf16 [N][K/64];
+ *     weight = s * q + b; x, y fp16.  K % 64 == 0.  (The pages' format.)
+ *   Q4_FMT_AF4_G64_F16: the same with fp16 scales and biases (an extra variant,
+ *     not a format the pages describe).
  * The 3-bit packing and its zero point (2^(bits - 1) - 1, as q4f16_1's 7) are
  * our reading: the table gives only the bytes per group. */
 #define Q4_FMT_Q3F16_1 1u
 #define Q4_FMT_Q4F32_1 2u
 #define Q4_FMT_AF4_G64 3u
+#define Q4_FMT_AF4_G64_F16 4u
 /* OR-ed into the format of a q3f16_1 call: load the words as 16-byte pieces
  * through an LDS stage, or as one 12-byte load per group.  Without either, the
  * first is taken when each team of lanes has at least eight trips of its rows
@@ -296,7 +297,7 @@ Q4_API int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_s
 /* q4_gemv_format: y = W x (M = 1) for a format variant (one of Q4_FMT_*, for
  * q3f16_1 optionally with one Q4_FMT_LOAD_* bit), fp32 accumulation, fp16
  * outputs rounded to nearest even (fp32 outputs for Q4_FMT_Q4F32_1).  biases: NULL
- * except for Q4_FMT_AF4_G64.  32 <= K <= 32768, K % 32 == 0 (% 64 for affine);
+ * except for the two affine formats.  32 <= K <= 32768, K % 32 == 0 (% 64 for affine);
  * words and x 16-byte aligned (words 4-byte for q3f16_1), the rest aligned to
  * their element;
  * y must not overlap an input. */

@@ -83,3 +83,91 @@ def assert_gemv_close(y_gpu_bits, words, scales, X, rows=None, rel=2e-3, report=
         flip = diff & ~same_sign
         assert np.all(np.abs(half_f64(y[flip])) <= 2 ** -14)
     return ref
+
+
+# ---------------------------------------------------------------------------
+# Rounding-error bounds of the GEMV kernels, against the exact result
+# ---------------------------------------------------------------------------
+#
+# u = 2^-24 is the unit roundoff of fp32.  Per 32-weight group g of a row, with
+# X_g = sum_{k in g} |x_k| (and its even / odd halves X_e, X_o), a kernel forms
+# D_g ~ T_g = sum_{k in g} (q_k - 7) x_k with an error E_g, and the row's output
+# as the fp32 sum over groups of s_g * D_g, rounded once to fp16.
+#
+#  * "fold" (the M = 1 persistent kernel): D_g is the difference of two fp32
+#    chains of v_dot2 over t_k x_k with t_k = 1024 + q_k (k even) or 64 + q_k
+#    (k odd), the second with every q_k = 7.  Each chain has 8 dot steps per
+#    parity; counting two roundings per step, a chain's error is at most
+#    16 u times the sum of its terms' magnitudes (|t_k| <= 1039 or 79), the add
+#    of the two chains one more rounding, and the subtraction one rounding of
+#    at most u |T_g| <= 8 u X_g (doubled to cover the second-order terms):
+#        E_g <= 2 * 17 u (1039 X_e + 79 X_o) + 2 u * 8 X_g
+#  * "sub" (the M = 1 persistent kernel): the codes enter as fp16 subnormals
+#    (q * 2^-24, or q * 2^-20 at odd positions), products exact; two chains of
+#    8 v_dot2 steps (two roundings each) over terms of at most 15 |x|, joined by
+#    one fma, minus the same function of codes 7 (at most 7 |x| per term), then
+#    one rounding of the difference (at most u |T_g| <= 8 u X_g, doubled):
+#        E_g <= 17 u * 15 X_g + 17 u * 7 X_g + 2 u * 8 X_g = 390 u X_g
+#  * "exact" (every other kernel: q - 7 formed exactly in fp16, one chain of
+#    products of at most 8 |x|, or one MFMA over the group):
+#        E_g <= 34 u * 8 X_g
+# Accumulation over the G groups and a cross-lane reduction of at most 6 steps:
+# at most G + 8 further roundings of partial sums bounded by
+# sum_g |s_g| (8 X_g + E_g).  Then
+#     |y_fp32 - y| <= B = sum_g |s_g| E_g + (G + 8) u sum_g |s_g| (8 X_g + E_g)
+# and the fp16 output is within B + ulp16(|y| + B) / 2 of the exact y.
+
+_U = 2.0 ** -24
+
+
+def group_abs_sums(X):
+    """[M][G] sums of |x| per group, and of the even and odd positions."""
+    Xa = np.asarray(X, np.uint16)
+    x = half_f64(Xa).reshape(Xa.shape[0] if Xa.ndim > 1 else 1, -1)
+    a = np.abs(x).reshape(x.shape[0], -1, 32)
+    return a.sum(axis=2), a[:, :, 0::2].sum(axis=2), a[:, :, 1::2].sum(axis=2)
+
+
+def error_bound(scales, X, kind):
+    """[M][N] bound B on |y_fp32 - y| for fp16 scales bits [N][G] and X [M][K]."""
+    xg, xe, xo = group_abs_sums(X)
+    if kind == "fold":
+        E = 34 * _U * (1039 * xe + 79 * xo) + 2 * _U * 8 * xg
+    elif kind == "sub":
+        E = 390 * _U * xg
+    elif kind == "exact":
+        E = 34 * _U * 8 * xg
+    else:
+        raise ValueError(kind)
+    G = xg.shape[1]
+    C = E + (G + 8) * _U * (8 * xg + E)
+    s = np.abs(half_f64(np.asarray(scales, np.uint16))).reshape(-1, G)
+    return (C @ s.T) * (1 + 2.0 ** -20)
+
+
+def ulp16(v):
+    """Unit in the last place of fp16 at magnitude v (2^-24 below the normal range)."""
+    v = np.maximum(np.abs(np.asarray(v, np.float64)), 2.0 ** -14)
+    return 2.0 ** (np.floor(np.log2(v)) - 10)
+
+
+def assert_within_rounding_bound(y_gpu_bits, y_exact64, y_exact16, scales, X, kind,
+                                 exact_frac=0.99, what=""):
+    """Every output within the kernel's rounding bound of the exact result, and
+    at least `exact_frac` of them equal to the exactly rounded fp16 value (the
+    others within one fp16 ulp).  Returns (worst error / bound, fraction equal)."""
+    y = np.asarray(y_gpu_bits, np.uint16).reshape(np.asarray(y_exact64).shape)
+    B = error_bound(scales, X, kind).reshape(y.shape)
+    got = half_f64(y)
+    ref = np.asarray(y_exact64, np.float64)
+    lim = B + 0.5 * ulp16(np.abs(ref) + B)
+    err = np.abs(got - ref)
+    bad = np.nonzero(~(err <= lim))
+    assert len(bad[0]) == 0, (f"{what}: {len(bad[0])} outputs beyond the rounding bound; first "
+                              f"{[(int(i), got[i], ref[i], lim[i]) for i in zip(*bad)][:3]}")
+    # exactly rounded: the same fp16 value (+0 and -0 count as one)
+    ex16 = np.asarray(y_exact16, np.uint16).reshape(y.shape)
+    same = (ex16 == y) | (((ex16 | y) & 0x7FFF) == 0)
+    frac = float(same.mean())
+    assert frac >= exact_frac, f"{what}: only {frac:.4f} of outputs exactly rounded"
+    return float((err / lim).max()), frac

@@ -13,7 +13,8 @@ from gpuhelp import dev_half, dev_words, half_f64, host_half
 
 pytestmark = pytest.mark.gpu
 
-FMTS = {"q3f16_1": q4.FMT_Q3F16_1, "q4f32_1": q4.FMT_Q4F32_1, "af4g64": q4.FMT_AF4_G64}
+FMTS = {"q3f16_1": q4.FMT_Q3F16_1, "q4f32_1": q4.FMT_Q4F32_1, "af4g64": q4.FMT_AF4_G64,
+        "af4g64_f16": q4.FMT_AF4_G64_F16}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,6 +36,13 @@ def make(fmt, N, K, tag):
         scales = (np.abs(synth.normal(lab + "/s", 0, 0, N * K // 32)) * 0.01 + 1e-3).astype(
             np.float32).reshape(N, -1)
         biases = None
+    elif fmt == "af4g64":
+        # bf16 scales |N(0, 0.01)| + 1e-3 and biases 0.05 N(0, 1), as the pages'
+        # MLX affine checkpoints store them
+        words = synth.words(lab + "/w", 0, N * K // 8).reshape(N, K // 8)
+        scales = synth.to_bf16_bits(np.abs(0.01 * synth.normal(lab + "/s", 0, 0, N * K // 64))
+                                    + 1e-3).reshape(N, -1)
+        biases = synth.to_bf16_bits(0.05 * synth.normal(lab + "/b", 0, 0, N * K // 64)).reshape(N, -1)
     else:
         words = synth.words(lab + "/w", 0, N * K // 8).reshape(N, K // 8)
         scales = synth.scales_halfnormal(lab + "/s", 0, 0, N * K // 64, 0.01, 1e-3).reshape(N, -1)
@@ -147,11 +155,30 @@ def test_q3_words_4_byte_aligned(load):
         assert np.abs(got - ref).max() <= tol
 
 
+@pytest.mark.parametrize("fmt", ["af4g64", "af4g64_f16"])
 @pytest.mark.parametrize("N,K", [(300, 2560), (77, 11264), (5, 64)])
-def test_affine_groups_per_lane(N, K):
+def test_affine_groups_per_lane(fmt, N, K):
     """The affine format on the q4f16_1 GEMV at row lengths of 5 and 6 groups per
     lane and at one 64-weight group."""
-    test_format_gemv_matches_oracle("af4g64", N, K)
+    test_format_gemv_matches_oracle(fmt, N, K)
+
+
+def test_affine_bf16_is_not_read_as_fp16():
+    """The same bits as bf16 and as fp16 scales give different products: the bf16
+    format decodes its scales and biases as bf16 (the closed form codes 15, bias
+    0: y = 15 s sum(x) with s = 0.5 as bf16 0x3F00, which as fp16 is 1.75)."""
+    N, K = 4, 128
+    words = np.full((N, K // 8), 0xFFFFFFFF, np.uint32)
+    sc = np.full((N, K // 64), 0x3F00, np.uint16)
+    bi = np.zeros((N, K // 64), np.uint16)
+    x = np.full(K, 0x3C00, np.uint16)            # ones
+    yb = q4.q4_gemv_format(q4.FMT_AF4_G64, to_dev(words), to_dev(sc), to_dev(x), K,
+                           biases=to_dev(bi))
+    yh = q4.q4_gemv_format(q4.FMT_AF4_G64_F16, to_dev(words), to_dev(sc), to_dev(x), K,
+                           biases=to_dev(bi))
+    torch.cuda.synchronize()
+    assert np.all(half_f64(host_half(yb)) == 15 * 0.5 * K)
+    assert np.all(half_f64(host_half(yh)) == 15 * 1.75 * K)
 
 
 def test_format_weight_bytes():
@@ -160,3 +187,4 @@ def test_format_weight_bytes():
     assert q4.q4_format_weight_bytes(q4.FMT_Q4F32_1, 9216, 3072) == 9216 * 96 * 20
     assert q4.q4_format_weight_bytes(q4.FMT_AF4_G64, 9216, 3072) == 9216 * 48 * 36
     assert q4.q4_format_weight_bytes(q4.FMT_AF4_G64, 10, 96) == 0
+    assert q4.q4_format_weight_bytes(q4.FMT_AF4_G64_F16, 9216, 3072) == 9216 * 48 * 36

@@ -15,8 +15,7 @@ from gpuhelp import assert_gemv_close, dev_half, dev_words, half_f64, host_half
 pytestmark = pytest.mark.gpu
 
 MODES = {"hazards": q4.STEP_PERSISTENT, "ordered": q4.STEP_ORDERED | q4.STEP_PERSISTENT,
-         "launch_each": q4.STEP_LAUNCH_EACH, "auto": 0,
-         "hazards_ring": q4.STEP_LDS_RING | q4.STEP_PERSISTENT}
+         "launch_each": q4.STEP_LAUNCH_EACH, "auto": 0}
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -13,14 +13,10 @@ from gpuhelp import assert_gemv_close, dev_half, dev_words, half_f64, host_half,
 
 pytestmark = pytest.mark.gpu
 
-# default: the register-streaming persistent kernel; *_ring: the LDS-ring kernel
-# where it applies (every K % 256 == 0, K <= 8192), else the register one
-# (STEP_PERSISTENT keeps dependency-heavy lists in the persistent kernel; "auto"
-# lets the driver choose)
+# default: the persistent kernel (STEP_PERSISTENT keeps dependency-heavy lists in
+# it; "auto" lets the driver choose)
 MODES = {"hazards": q4.STEP_PERSISTENT, "ordered": q4.STEP_ORDERED | q4.STEP_PERSISTENT,
-         "launch_each": q4.STEP_LAUNCH_EACH, "auto": 0,
-         "hazards_ring": q4.STEP_LDS_RING | q4.STEP_PERSISTENT,
-         "ordered_ring": q4.STEP_ORDERED | q4.STEP_LDS_RING | q4.STEP_PERSISTENT}
+         "launch_each": q4.STEP_LAUNCH_EACH, "auto": 0}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -177,7 +173,7 @@ def test_modes_agree_on_the_phi3_layer():
         outs[mode] = [host_half(d[3]) for d in descs]
     # the persistent kernels use the same lane mapping and arithmetic for these
     # shapes (32 lanes x 3 groups, 64 x 4): bitwise equal across modes and kernels
-    for m in ("ordered", "auto", "hazards_ring", "ordered_ring"):
+    for m in ("ordered", "auto"):
         for a, b in zip(outs["hazards"], outs[m]):
             assert np.array_equal(a, b), m
     for (m, W, S), y, (N, K) in zip(mats, outs["ordered"], shapes):
