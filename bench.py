@@ -27,6 +27,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -152,37 +153,45 @@ def main():
                       for i, (W, S, x, y) in enumerate(descs) if i > 0])
 
     def time_mode(mode, steps, warmup, lay=None):
+        """One planned list run `steps` times after `warmup` runs, each step between
+        its own pair of HIP events on the stream the kernel runs on; the median,
+        p10, p90 and the mean over the whole bracket, and the host's time per
+        q4_step_run call."""
         flags = MODES[mode]
-        layers_ = layers if lay is None else lay
-        ws_bytes = q4.q4_decode_step_workspace_bytes(layers_, 1, flags)
-        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-
-        # the first call clears the workspace's counters; the kernel leaves them
-        # zero, so the following calls skip the clearing kernel
-        def step(first=False):
-            f = flags if first else flags | q4.STEP_WS_CLEAN
-            q4.q4_decode_step(layers_, 1, f, ws=ws, ws_bytes=ws_bytes, stream=stream)
-
+        plan = q4.StepPlan(layers if lay is None else lay, 1, flags, stream=stream)
+        sp = q4.C.c_void_p(stream.cuda_stream)
         with torch.cuda.stream(stream):
-            step(first=True)
             for _ in range(warmup):
-                step()
+                plan.run_raw(sp)
+            plan.status(stream)                       # waits; the error word must be 0
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            h0 = time.perf_counter()
-            e0.record(stream)
-            for _ in range(steps):
-                step()
-            e1.record(stream)
+            host = 0.0
+            w0.record(stream)
+            for a, b in ev:
+                a.record(stream)
+                h0 = time.perf_counter()
+                rc = plan.run_raw(sp)
+                host += time.perf_counter() - h0
+                b.record(stream)
+                if rc:
+                    raise SystemExit(f"q4_step_run failed: {rc}")
+            w1.record(stream)
             torch.cuda.synchronize()
-            h1 = time.perf_counter()
-        return e0.elapsed_time(e1) / steps, (h1 - h0) * 1e3 / steps
+            plan.status(stream)
+        per = np.sort(np.array([a.elapsed_time(b) for a, b in ev]))
+        return {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
+                "p90": float(np.percentile(per, 90)), "mean": w0.elapsed_time(w1) / steps,
+                "host_us": host / steps * 1e6}
 
-    ms, host_ms = time_mode(args.mode, args.steps, args.warmup)
+    t = time_mode(args.mode, args.steps, args.warmup)
+    ms = t["median"]
     gbs = step_bytes / (ms * 1e-3) / 1e9
     if gbs > PEAK_GBS * 1.02:
         raise SystemExit(f"measured {gbs:.0f} GB/s is above the HBM peak: measurement error")
+    probe = None if args.no_probe else probe_read(torch, q4, stream)
 
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -194,15 +203,20 @@ def main():
                                "3072->32064, q4f16_1 group 32",
                    "gemvs_per_step": len(meta), "algorithmic_bytes_per_step": step_bytes,
                    "weight_bytes_per_step": weight_bytes, "mode": args.mode},
+        "timing": {"statistic": "median of per-step HIP event pairs",
+                   "ms_p10": round(t["p10"], 5), "ms_p90": round(t["p90"], 5),
+                   "ms_mean_over_bracket": round(t["mean"], 5),
+                   "host_enqueue_us_per_step": round(t["host_us"], 2)},
         "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
         "projected_tok_s": round(1e3 / ms, 1),
-        "host_ms_per_step": round(host_ms, 5),
         "setup_s": round(setup_s, 1),
     }
-    # dominant kernel: the persistent step kernel, one launch per step (its
-    # counters are left zero by the previous call, so nothing else is launched);
-    # its algorithmic bytes per launch are the step's, its duration the event time
-    # per step
+    if probe is not None:
+        result["probe_read_gbs"] = probe
+        result["pct_of_probe_ceiling"] = round(100 * gbs / probe["best_gbs"], 2)
+    # dominant kernel: the persistent step kernel, one launch per step (nothing
+    # else is launched); its algorithmic bytes per launch are the step's, its
+    # duration the event time per step
     result["us_per_gemv"] = round(ms * 1e3 / len(meta), 3)
     result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS,
                           "unit": "GB/s", "frac": round(gbs / PEAK_GBS, 4),
@@ -214,23 +228,24 @@ def main():
         for mode in MODES:
             if mode in (args.mode, "persistent"):
                 continue
-            m_ms, _ = time_mode(mode, max(5, args.steps // 5), max(3, args.warmup // 4))
-            other[mode] = {"ms_per_step": round(m_ms, 5),
-                           "gbs": round(step_bytes / (m_ms * 1e-3) / 1e9, 1)}
+            m = time_mode(mode, max(5, args.steps // 5), max(3, args.warmup // 4))
+            other[mode] = {"ms_per_step": round(m["median"], 5),
+                           "gbs": round(step_bytes / (m["median"] * 1e-3) / 1e9, 1)}
         for mode in ("persistent", "launch_each", "hazards"):
-            m_ms, _ = time_mode(mode, max(5, args.steps // 5), max(3, args.warmup // 4),
-                                chain_layers)
+            m = time_mode(mode, max(5, args.steps // 5), max(3, args.warmup // 4), chain_layers)
             key = "chain_default_choice" if mode == "hazards" else f"chain_{mode}"
-            other[key] = {"ms_per_step": round(m_ms, 5),
-                                      "gbs": round(step_bytes / (m_ms * 1e-3) / 1e9, 1)}
+            other[key] = {"ms_per_step": round(m["median"], 5),
+                          "gbs": round(step_bytes / (m["median"] * 1e-3) / 1e9, 1)}
+        # the one-call entry point (plans and writes the tables every call)
+        m = one_call_timing(torch, q4, stream, layers, max(5, args.steps // 10))
+        other["one_call_q4_decode_step"] = {"ms_per_step": round(m, 5),
+                                            "gbs": round(step_bytes / (m * 1e-3) / 1e9, 1)}
         result["other_modes"] = other
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(np, torch, descs, meta)
         if not args.no_configs:
             result["per_config"] = per_config(torch, q4, synth, np, stream)
             result["decode_tokens"] = token_figures(torch, q4, synth, np, stream, descs, meta)
-        if not args.no_probe:
-            result["probe_read_gbs"] = probe_read(torch, q4, stream)
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = cpu_baseline(np, torch, descs, meta)
     print(json.dumps(result), flush=True)
 
 
@@ -291,12 +306,10 @@ def per_config(torch, q4, synth, np, stream):
         return fn
 
     def step_call(descs, M=1):
-        layers = q4.make_layers([d[:4] for d in descs])
-        nb = q4.q4_decode_step_workspace_bytes(layers, M, 0)
-        wsb = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")   # counters clean
+        plan = q4.StepPlan(q4.make_layers([d[:4] for d in descs]), M, 0, stream=stream)
 
         def fn(i):
-            q4.q4_decode_step(layers, M, q4.STEP_WS_CLEAN, ws=wsb, ws_bytes=nb, stream=stream)
+            plan.run(stream)
         return fn
 
     # single qkv GEMV 3072 -> 9216
@@ -340,12 +353,10 @@ def per_config(torch, q4, synth, np, stream):
          for t in ((Wg, Sg, xg, gu), (Wd, Sd, gu, y, q4.X_SILU_MUL))])
 
     def glue_step(flags):
-        nb = q4.q4_decode_step_workspace_bytes(glue_layers, 1, flags)
-        wsb = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
+        plan = q4.StepPlan(glue_layers, 1, flags, stream=stream)
 
         def fn(i):
-            q4.q4_decode_step(glue_layers, 1, flags | (q4.STEP_WS_CLEAN if i else 0), ws=wsb,
-                              ws_bytes=nb, stream=stream)
+            plan.run(stream)
         return fn
     wsg = torch.empty(max(q4.q4_workspace_bytes(1, 16384, 3072),
                           q4.q4_workspace_bytes(1, 3072, 8192), 16), dtype=torch.uint8,
@@ -442,13 +453,11 @@ def formats_large(torch, q4, S, stream, N=262144, K=3072, calls=20):
         if f == 0:
             # the persistent kernel on this one GEMV (the driver alone would run a
             # one-descriptor list as one GEMV kernel)
-            layers = q4.make_layers([(W, sc, xf, yf)])
-            nbs = q4.q4_decode_step_workspace_bytes(layers, 1, q4.STEP_PERSISTENT)
-            wss = torch.zeros(max(nbs, 16), dtype=torch.uint8, device="cuda")
+            plan = q4.StepPlan(q4.make_layers([(W, sc, xf, yf)]), 1, q4.STEP_PERSISTENT,
+                               stream=stream)
 
             def fs(i):
-                q4.q4_decode_step(layers, 1, q4.STEP_WS_CLEAN | q4.STEP_PERSISTENT, ws=wss,
-                                  ws_bytes=nbs, stream=stream)
+                plan.run(stream)
             ms = _timed(torch, stream, fs, calls, warm=5)
             out["q4f16_1_decode_step"] = _fig(nb, ms, weight_bytes=wb,
                                               ns_per_kweight=round(ms * 1e6 / (N * K / 1e3), 4))
@@ -474,17 +483,28 @@ def m8_sweep(torch, q4, synth, np, stream, steps=300, warmup=50):
         descs.append((m.words_torch("cuda"), sc, xs[K], torch.empty(8 * N, dtype=torch.float16,
                                                                        device="cuda"), N, K))
     b5 = sum(synth.algorithmic_bytes(8, N, K) for _, N, K in shapes)
-    layers = q4.make_layers([d[:4] for d in descs])
-    nb = q4.q4_decode_step_workspace_bytes(layers, 8, 0)
-    wsb = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")   # counters clean
-
-    def fn(i):
-        q4.q4_decode_step(layers, 8, q4.STEP_WS_CLEAN, ws=wsb, ws_bytes=nb, stream=stream)
-    ms = _timed(torch, stream, fn, steps, warm=warmup)
+    plan = q4.StepPlan(q4.make_layers([d[:4] for d in descs]), 8, 0, stream=stream)
+    sp = q4.C.c_void_p(stream.cuda_stream)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            plan.run_raw(sp)
+        plan.status(stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            plan.run_raw(sp)
+            b.record(stream)
+        torch.cuda.synchronize()
+        plan.status(stream)
+    per = np.array([a.elapsed_time(b) for a, b in ev])
+    ms = float(np.median(per))
     flops = sum(2 * 8 * N * K for _, N, K in shapes)
     tr = measured_traffic("k_step_mfma")
     fig = _fig(b5, ms, gemvs=len(shapes), steps_per_s=round(1e3 / ms, 1),
                tok_per_s=round(8e3 / ms, 1), tflops=round(flops / (ms * 1e-3) / 1e12, 2),
+               us_p10=round(float(np.percentile(per, 10)) * 1e3, 2),
+               us_p90=round(float(np.percentile(per, 90)) * 1e3, 2), statistic="median",
                kernel="k_step_mfma", traffic=tr,
                traffic_over_algorithmic=None if tr is None else round(tr / b5, 4))
     del descs
@@ -533,18 +553,25 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
         ms = (time.perf_counter() - t0) * 1e3 / n
         out["one_token_per_call"] = {"ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 1),
                                      "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
-        for name, flags in (("tokens_per_call_eager", q4.TOKENS_EAGER),
-                            ("tokens_per_call_graph", 0)):
-            q4.q4_decode_tokens(model, tokens, steps, ws=ws, flags=flags, stream=stream)
+        graph = q4.TokensGraph(model, tokens, ws=ws, stream=stream)
+        for name, graphed in (("tokens_per_call_eager", False), ("tokens_per_call_graph", True)):
+            def call():
+                if graphed:
+                    graph.run(steps, stream=stream)
+                else:
+                    q4.q4_decode_tokens(model, tokens, steps, ws=ws, stream=stream)
+            call()
             torch.cuda.synchronize()
             reps = 5
             t0 = time.perf_counter()
             for _ in range(reps):
-                q4.q4_decode_tokens(model, tokens, steps, ws=ws, flags=flags, stream=stream)
+                call()
             stream.synchronize()
             ms = (time.perf_counter() - t0) * 1e3 / (reps * steps)
             out[name] = {"ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 1),
                          "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
+        torch.cuda.synchronize()
+        graph.close()
     out["tokens"] = tokens[: min(steps + 1, 9)].cpu().tolist()
     # the same loop with every residual add + RMSNorm folded into the GEMV it feeds
     folded = q4.Model(embed, blocks, gamma, descs[128][:2], 1e-5,
@@ -552,14 +579,16 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
     wsf = torch.empty(q4.q4_decode_token_workspace_bytes(folded), dtype=torch.uint8,
                       device="cuda")
     with torch.cuda.stream(stream):
-        q4.q4_decode_tokens(folded, tokens, steps, ws=wsf, stream=stream)
+        graph = q4.TokensGraph(folded, tokens, ws=wsf, stream=stream)
+        graph.run(steps, stream=stream)
         torch.cuda.synchronize()
         reps = 5
         t0 = time.perf_counter()
         for _ in range(reps):
-            q4.q4_decode_tokens(folded, tokens, steps, ws=wsf, stream=stream)
+            graph.run(steps, stream=stream)
         stream.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / (reps * steps)
+        graph.close()
     out["tokens_per_call_graph_norms_folded"] = {
         "ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 1),
         "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
@@ -736,26 +765,94 @@ def probe_read(torch, q4, stream, nbytes=4 << 30, reps=10):
             "sweep": {str(k): round(v, 1) for k, v in best.items()}}
 
 
-def cpu_baseline(np, torch, descs, meta, reps=4):
-    """The CPU oracle (plain C, fp64, one thread) over the full step, `reps` times."""
+def host_cpu():
+    """Host CPU model (lscpu, else /proc/cpuinfo), logical CPUs, and the CPUs this
+    process may run on."""
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return model, os.cpu_count(), usable
+
+
+def cpu_baseline(np, torch, descs, meta, max_threads=16):
+    """The CPU oracle on this host over the full step (129 GEMVs, all rows):
+    plain C in fp64, once on one thread and three times on every usable core
+    (its OpenMP row loops, capped at max_threads, the machine's CPU share); the
+    all-cores output is also checked against every GPU output of the last step
+    (the GEMV tolerance)."""
     import oracle
     import synth
-    x_host = {}
-    total_bytes, t = 0, 0.0
+    model, nproc, usable = host_cpu()
+    threads = max(1, min(usable, max_threads))
+    host = []
     for (W, S, X, Y), (label, N, K) in zip(descs, meta):
-        w = W.cpu().numpy().view(np.uint32)
-        s = S.view(torch.int16).cpu().numpy().view(np.uint16)
-        if K not in x_host:
-            x_host[K] = X.view(torch.int16).cpu().numpy().view(np.uint16)
+        host.append((W.cpu().numpy().view(np.uint32), S.view(torch.int16).cpu().numpy().view(
+            np.uint16), X.view(torch.int16).cpu().numpy().view(np.uint16),
+            Y.view(torch.int16).cpu().numpy().view(np.uint16), N, K))
+    step_bytes = sum(synth.algorithmic_bytes(1, N, K) for _, N, K in meta)
+    old = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
         t0 = time.perf_counter()
-        for _ in range(reps):
-            oracle.gemv_f64(w, s, x_host[K])
-        t += time.perf_counter() - t0
-        total_bytes += reps * synth.algorithmic_bytes(1, N, K)
-    return {"value": round(total_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seconds": round(t, 2),
-            "sample": f"the full step ({len(meta)} GEMVs, all rows) {reps} times, "
-                      "fp64 plain C oracle, one thread"}
+        for w, s, x, _, _, _ in host:
+            oracle.gemv_f64(w, s, x)
+        t1 = time.perf_counter() - t0
+        oracle.set_threads(threads)
+        reps, tn, worst, checked = 3, 0.0, 0.0, 0
+        for r in range(reps):
+            t0 = time.perf_counter()
+            ys = [oracle.gemv_f64(w, s, x) for w, s, x, _, _, _ in host]
+            tn += time.perf_counter() - t0
+        for (w, s, x, y, N, K), ref in zip(host, ys):
+            tol = 2e-3 * oracle.vec_norm(x) * oracle.row_norms(w, s).max()
+            err = np.abs(y.view(np.float16).astype(np.float64) - ref)
+            worst = max(worst, float(err.max() / tol))
+            checked += N
+    finally:
+        oracle.set_threads(old)
+    tn /= reps
+    return {"value": round(step_bytes / tn / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full step ({len(meta)} GEMVs, all rows, {step_bytes:,} algorithmic "
+                      f"bytes), fp64 plain C oracle with OpenMP row loops on {threads} threads, "
+                      f"{reps} times",
+            "seconds_per_step": round(tn, 3), "host_cpu": model, "nproc": nproc,
+            "usable_cpus": usable,
+            "single_thread": {"value": round(step_bytes / t1 / 1e9, 4), "unit": "GB/s",
+                              "seconds_per_step": round(t1, 2)},
+            "parity_all_outputs": {"outputs": checked, "max_error_over_tolerance": round(worst, 4),
+                                   "ok": worst <= 1.0}}
+
+
+def one_call_timing(torch, q4, stream, layers, calls):
+    """ms per q4_decode_step call (planning and table writes on every call)."""
+    ws = torch.empty(max(q4.q4_decode_step_workspace_bytes(layers, 1, 0), 16), dtype=torch.uint8,
+                     device="cuda")
+    with torch.cuda.stream(stream):
+        q4.q4_decode_step(layers, 1, 0, ws=ws, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(calls):
+            q4.q4_decode_step(layers, 1, 0, ws=ws, stream=stream, check=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        q4.q4_step_status(ws, stream)
+    return e0.elapsed_time(e1) / calls
 
 
 if __name__ == "__main__":

@@ -20,7 +20,7 @@ __all__ = [
     "Q4Error", "load", "lib_path", "q4_version", "q4_pack", "q4_unpack", "q4_gemv",
     "q4_gemv_splitk", "q4_gemv_batched", "q4_gemv_batched_noalloc", "q4_workspace_bytes", "q4_splitk_workspace_bytes",
     "q4_decode_step", "q4_decode_step_workspace_bytes", "q4_probe_read", "q4_probe_copy",
-    "Layer", "STEP_LAUNCH_EACH", "STEP_ORDERED", "STEP_WS_CLEAN", "make_layers",
+    "Layer", "STEP_LAUNCH_EACH", "STEP_ORDERED", "StepPlan", "make_layers",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,11 +31,9 @@ _lib = None
 Q4_NOALLOC_SCRATCH_BYTES = 4 * 1024 * 1024   # include/q4f16.h
 STEP_LAUNCH_EACH = 0x1
 STEP_ORDERED = 0x2
-STEP_WS_CLEAN = 0x8
 STEP_PERSISTENT = 0x10
 X_PLAIN = 0
 X_SILU_MUL = 1
-TOKENS_EAGER = 0x1
 FMT_Q3F16_1 = 1
 FMT_Q4F32_1 = 2
 FMT_AF4_G64 = 3       # bf16 scales and biases (the pages' MLX affine format)
@@ -45,7 +43,7 @@ FMT_LOAD_DIRECT = 0x200
 MODEL_FACTORED_NORM = 0x1   # q4_model.options: norms folded into the GEMVs they feed
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
-          4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED"}
+          4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED", 7: "Q4_ERR_TIMEOUT"}
 
 
 class Q4Error(RuntimeError):
@@ -109,8 +107,14 @@ def load():
             "q4_gemv_batched_noalloc": ([p, p, p, p, i64, i64, i64, p], i32),
             "q4_workspace_bytes": ([i64, i64, i64], sz),
             "q4_splitk_workspace_bytes": ([i64, i64, i64], sz),
-            "q4_decode_step": ([p, i64, i64, C.c_uint32, p, sz, p], i32),
+            "q4_last_error_detail": ([], C.c_char_p),
+            "q4_step_plan_bytes": ([i64], sz),
             "q4_decode_step_workspace_bytes": ([p, i64, i64, C.c_uint32], sz),
+            "q4_step_plan_init": ([p, i64, i64, C.c_uint32, p, sz, p, sz, p], i32),
+            "q4_step_run": ([p, p, sz, p], i32),
+            "q4_step_status": ([p, p], i32),
+            "q4_decode_step": ([p, i64, i64, p, sz, p], i32),
+            "q4_decode_step_flags": ([p, i64, i64, C.c_uint32, p, sz, p], i32),
             "q4_silu_mul": ([p, p, i64, i64, p], i32),
             "q4_embed_rows": ([p, p, i64, i64, p, i64, p, p], i32),
             "q4_rmsnorm": ([p, p, C.c_float, i64, i64, p, p], i32),
@@ -120,7 +124,10 @@ def load():
             "q4_format_weight_bytes": ([C.c_uint32, i64, i64], sz),
             "q4_decode_token_workspace_bytes": ([p], sz),
             "q4_decode_token": ([p, p, p, p, p, sz, p], i32),
-            "q4_decode_tokens": ([p, p, i64, p, sz, C.c_uint32, p], i32),
+            "q4_decode_tokens": ([p, p, i64, p, sz, p], i32),
+            "q4_tokens_graph_create": ([p, p, p, sz, p, C.POINTER(p)], i32),
+            "q4_tokens_graph_run": ([p, i64, p], i32),
+            "q4_tokens_graph_destroy": ([p], i32),
             "q4_probe_read": ([p, sz, p, i64, p], i32),
             "q4_probe_copy": ([p, p, sz, p], i32),
         }
@@ -134,7 +141,7 @@ def load():
 
 def _check(rc: int):
     if rc != 0:
-        raise Q4Error(rc, load().q4_last_error().decode())
+        raise Q4Error(rc, load().q4_last_error_detail().decode())
 
 
 def _torch():
@@ -304,15 +311,60 @@ def q4_decode_step_workspace_bytes(layers, M: int = 1, flags: int = 0) -> int:
     return int(load().q4_decode_step_workspace_bytes(layers, len(layers), M, flags))
 
 
-def q4_decode_step(layers, M: int = 1, flags: int = 0, ws=None, ws_bytes=None, stream=None):
-    """Run the GEMVs of a Layer array (see make_layers) in order."""
+def q4_decode_step(layers, M: int = 1, flags: int = 0, ws=None, ws_bytes=None, stream=None,
+                   check: bool = True):
+    """Plan and run the GEMVs of a Layer array (see make_layers) in order, in one
+    call (q4_decode_step_flags); returns the workspace.  check: then wait for the
+    stream and raise if a persistent kernel's bounded wait ran out
+    (q4_step_status)."""
     torch = _torch()
     need = q4_decode_step_workspace_bytes(layers, M, flags)
-    if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    wsb = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
-    _check(load().q4_decode_step(layers, len(layers), M, flags, _ptr(ws), wsb, _stream(stream)))
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    wsb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(load().q4_decode_step_flags(layers, len(layers), M, flags, _ptr(ws), wsb,
+                                       _stream(stream)))
+    if check:
+        q4_step_status(ws, stream)
     return ws
+
+
+def q4_step_status(ws, stream=None):
+    """Wait for the stream and raise Q4Error(Q4_ERR_TIMEOUT) if a bounded wait in a
+    persistent decode-step kernel ran out since the last check."""
+    _check(load().q4_step_status(_ptr(ws), _stream(stream)))
+
+
+class StepPlan:
+    """A planned decode-step list (q4_step_plan_init): the plan in host memory, the
+    workspace on the device, the descriptors kept alive.  run() enqueues one step
+    (q4_step_run), status() checks the error word (q4_step_status)."""
+
+    def __init__(self, layers, M: int = 1, flags: int = 0, ws=None, stream=None, keep=None):
+        torch = _torch()
+        lib = load()
+        n = len(layers)
+        self.layers, self.keep, self.M, self.flags = layers, keep, M, flags
+        self.plan = C.create_string_buffer(int(lib.q4_step_plan_bytes(n)))
+        self.ws_bytes = q4_decode_step_workspace_bytes(layers, M, flags)
+        if ws is None:
+            ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        self.ws = ws
+        self._ws_ptr = _ptr(ws)
+        self._ws_len = ws.numel() * ws.element_size()
+        _check(lib.q4_step_plan_init(layers, n, M, flags, self.plan, len(self.plan),
+                                     self._ws_ptr, self._ws_len, _stream(stream)))
+
+    def run(self, stream=None):
+        _check(load().q4_step_run(self.plan, self._ws_ptr, self._ws_len, _stream(stream)))
+
+    def run_raw(self, stream_ptr):
+        """q4_step_run with the stream given as a ctypes pointer (no Python-side
+        conversions: what the host spends per step is the C call)."""
+        return load().q4_step_run(self.plan, self._ws_ptr, self._ws_len, stream_ptr)
+
+    def status(self, stream=None):
+        q4_step_status(self.ws, stream)
 
 
 def q4_silu_mul(gu, out=None, stream=None):
@@ -420,15 +472,39 @@ def q4_decode_token(model: Model, token_in, token_out, logits=None, ws=None, str
     return ws
 
 
-def q4_decode_tokens(model: Model, tokens, steps: int, ws=None, flags: int = 0, stream=None):
+def q4_decode_tokens(model: Model, tokens, steps: int, ws=None, stream=None):
     """`steps` decode steps: tokens[i] -> tokens[i + 1] (int32 device tensor)."""
     torch = _torch()
     need = q4_decode_token_workspace_bytes(model)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    _check(load().q4_decode_tokens(model.ref(), _ptr(tokens), steps, _ptr(ws), ws.numel(), flags,
+    _check(load().q4_decode_tokens(model.ref(), _ptr(tokens), steps, _ptr(ws), ws.numel(),
                                    _stream(stream)))
     return ws
+
+
+class TokensGraph:
+    """q4_tokens_graph: one decode step captured on `stream` (not the null stream)
+    and replayed per token by run(); close() destroys it (after the caller has
+    synchronised the streams it ran on)."""
+
+    def __init__(self, model: Model, tokens, ws=None, stream=None):
+        torch = _torch()
+        self.model, self.tokens = model, tokens
+        need = q4_decode_token_workspace_bytes(model)
+        self.ws = ws if ws is not None else torch.empty(need, dtype=torch.uint8, device="cuda")
+        h = C.c_void_p()
+        _check(load().q4_tokens_graph_create(model.ref(), _ptr(tokens), _ptr(self.ws),
+                                             self.ws.numel(), _stream(stream), C.byref(h)))
+        self.handle = h
+
+    def run(self, steps: int, stream=None):
+        _check(load().q4_tokens_graph_run(self.handle, steps, _stream(stream)))
+
+    def close(self):
+        if self.handle:
+            _check(load().q4_tokens_graph_destroy(self.handle))
+            self.handle = None
 
 
 def q4_gemv_format(fmt: int, words, scales, x, K: int, biases=None, y=None, stream=None):

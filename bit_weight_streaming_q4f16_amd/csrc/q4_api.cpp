@@ -149,13 +149,16 @@ const char* q4_status_str(int status) {
     case Q4_ERR_WORKSPACE: return "Q4_ERR_WORKSPACE";
     case Q4_ERR_DEVICE: return "Q4_ERR_DEVICE";
     case Q4_ERR_UNSUPPORTED: return "Q4_ERR_UNSUPPORTED";
+    case Q4_ERR_TIMEOUT: return "Q4_ERR_TIMEOUT";
     default: return "Q4_ERR_UNKNOWN";
   }
 }
 
+const char* q4_last_error_detail(void) { return g_error.c_str(); }
+
 const char* q4_last_error(void) { return g_error.c_str(); }
 
-int q4_version(void) { return 100; }
+int q4_version(void) { return 200; }
 
 int q4_pack(const uint8_t* codes, uint32_t* words, int64_t N, int64_t K, q4_stream_t stream) {
   if (!codes) return fail(Q4_ERR_NULL, "q4_pack: codes is NULL");
@@ -192,9 +195,16 @@ size_t q4_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
 namespace q4 {
 
 int gemv_validate(const char* what, const uint32_t* words, const uint16_t* scales,
-                  const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K) {
-  return check_gemv(what, words, scales, x, y, M, N, K, K);
+                  const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K,
+                  int64_t x_cols) {
+  return check_gemv(what, words, scales, x, y, M, N, K, x_cols ? x_cols : K);
 }
+
+int ws_validate(const char* what, void* ws, size_t have, size_t need) {
+  return check_ws(what, ws, have, need);
+}
+
+int device_fail(hipError_t e, const char* what) { return device_error(e, what); }
 
 int gemv_common(const char* what, const uint32_t* words, const uint16_t* scales,
                 const uint16_t* x, uint16_t* y, int64_t M, int64_t N, int64_t K,
@@ -243,236 +253,7 @@ int q4_gemv_batched(const uint32_t* words, const uint16_t* scales, const uint16_
 
 }  // extern "C"
 
-namespace {
-
-// Device copies of step descriptor tables, keyed by their contents (pointers,
-// shapes, dependencies) and device.  A table is uploaded on first use of a
-// layer list and reused by every later call with the same list; the least
-// recently used of kMaxTables entries is freed when a new one is needed.
-struct TableEntry {
-  int dev = -1;
-  std::vector<uint8_t> bytes;
-  void* dptr = nullptr;
-  uint64_t last_use = 0;
-};
-constexpr size_t kMaxTables = 16;
-std::mutex g_table_mutex;
-std::vector<TableEntry> g_tables;
-uint64_t g_table_clock = 0;
-
-const void* device_table(const void* host, size_t bytes, int dev, hipStream_t s, hipError_t* err) {
-  std::lock_guard<std::mutex> lock(g_table_mutex);
-  for (TableEntry& e : g_tables) {
-    if (e.dev == dev && e.bytes.size() == bytes && memcmp(e.bytes.data(), host, bytes) == 0) {
-      e.last_use = ++g_table_clock;
-      return e.dptr;
-    }
-  }
-  if (g_tables.size() >= kMaxTables) {
-    size_t lru = 0;
-    for (size_t i = 1; i < g_tables.size(); ++i)
-      if (g_tables[i].last_use < g_tables[lru].last_use) lru = i;
-    (void)hipFree(g_tables[lru].dptr);      // synchronises: no launch still reads it
-    g_tables.erase(g_tables.begin() + (ptrdiff_t)lru);
-  }
-  TableEntry e;
-  e.dev = dev;
-  e.bytes.assign(static_cast<const uint8_t*>(host), static_cast<const uint8_t*>(host) + bytes);
-  if ((*err = hipMalloc(&e.dptr, bytes)) != hipSuccess) return nullptr;
-  if ((*err = hipMemcpyAsync(e.dptr, e.bytes.data(), bytes, hipMemcpyHostToDevice, s)) !=
-      hipSuccess) {
-    (void)hipFree(e.dptr);
-    return nullptr;
-  }
-  e.last_use = ++g_table_clock;
-  g_tables.push_back(std::move(e));
-  return g_tables.back().dptr;
-}
-
-std::vector<q4::StepLayer> to_step_layers(const q4_layer* layers, int64_t n) {
-  std::vector<q4::StepLayer> v((size_t)n);
-  for (int64_t i = 0; i < n; ++i)
-    v[(size_t)i] = q4::StepLayer{layers[i].words, layers[i].scales, layers[i].x, layers[i].y,
-                                 layers[i].N, layers[i].K, layers[i].x_op};
-  return v;
-}
-
-// The persistent path applies to M == 1 lists whose rows fit its item shape,
-// when one workgroup of the step kernel fits on every compute unit.
-// Lists in which many descriptors wait for another run faster as one kernel per
-// GEMV: in the persistent kernel every waiting GEMV pays its hand-over and its
-// arithmetic on the critical path (measured on MI355X: 9.3 us per dependent GEMV
-// against about 7 us per launched GEMV), so beyond a quarter of the list waiting the
-// launches win, unless the caller asks for the persistent kernel.
-bool dependency_bound(int64_t n, int waiting, uint32_t flags) {
-  return !(flags & Q4_STEP_PERSISTENT) && 4 * (int64_t)waiting > n;
-}
-
-bool use_persistent(const q4::DeviceInfo& d, const q4::StepPlan& p, int64_t M, uint32_t flags) {
-  if (M != 1 || (flags & Q4_STEP_LAUNCH_EACH) || !p.ok) return false;
-  // a single GEMV is faster as one GEMV kernel (262144 x 3072: 73.7 against 80.7 us;
-  // qkv-sized: 8.7 against ~14 us), unless the caller asks for the persistent kernel
-  if (p.desc.size() == 1 && !(flags & Q4_STEP_PERSISTENT)) return false;
-  int waiting = 0;
-  for (const q4::StepDesc& sd : p.desc) waiting += sd.dep >= 0;
-  if (dependency_bound((int64_t)p.desc.size(), waiting, flags)) return false;
-  int per_cu = 0;
-  if (q4::step_occupancy(p, &per_cu) != hipSuccess || per_cu < 1) {
-    (void)hipGetLastError();
-    return false;
-  }
-  (void)d;
-  return true;
-}
-
-// One kernel per descriptor: the largest split-K partials of any descriptor, then
-// (for descriptors with Q4_X_SILU_MUL) the largest glue output, M * K fp16.
-struct EachLayout {
-  std::vector<q4::GemvPlan> plans;
-  size_t glue_off = 0, bytes = 0;
-};
-EachLayout each_layout(const q4::DeviceInfo& d, const q4_layer* layers, int64_t n, int64_t M) {
-  EachLayout e;
-  e.plans.resize((size_t)n);
-  size_t part = 0, glue = 0;
-  for (int64_t i = 0; i < n; ++i) {
-    e.plans[(size_t)i] = q4::plan_auto(d, M, layers[i].N, layers[i].K);
-    part = std::max(part, e.plans[(size_t)i].ws_bytes);
-    if (layers[i].x_op) glue = std::max(glue, (size_t)(2 * M * layers[i].K));
-  }
-  e.glue_off = (part + 255) & ~(size_t)255;
-  e.bytes = glue ? e.glue_off + glue : part;
-  return e;
-}
-
-bool any_x_op(const q4_layer* layers, int64_t n) {
-  for (int64_t i = 0; i < n; ++i)
-    if (layers[i].x_op) return true;
-  return false;
-}
-
-}  // namespace
-
 extern "C" {
-
-size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, int64_t M,
-                                      uint32_t flags) {
-  if (!layers || n_layers < 1 || M < 1 || M > q4::kMaxM) return 0;
-  const q4::DeviceInfo* d = q4::device_info();
-  if (!d) return 0;
-  for (int64_t i = 0; i < n_layers; ++i) {
-    const q4_layer& L = layers[i];
-    if (L.N < 1 || L.K < 32 || L.K % 32) return 0;
-  }
-  size_t need = each_layout(*d, layers, n_layers, M).bytes;
-  if (M > 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
-    std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
-    q4::MStepPlan p = q4::plan_step_mfma(*d, sl.data(), n_layers, (int)M,
-                                         (flags & Q4_STEP_ORDERED) != 0);
-    if (p.ok) need = std::max(need, q4::step_mfma_workspace_bytes(p));
-  }
-  if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
-    std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
-    q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
-    size_t b = q4::step_workspace_bytes(p);
-    if (b > need) need = b;
-  }
-  return need;
-}
-
-int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t flags,
-                   void* ws, size_t ws_bytes, q4_stream_t stream) {
-  if (!layers) return fail(Q4_ERR_NULL, "q4_decode_step: layers is NULL");
-  if (n_layers < 1) return fail(Q4_ERR_SHAPE, "q4_decode_step: n_layers = %lld: must be >= 1",
-                                (long long)n_layers);
-  if (n_layers > (1 << 20))
-    return fail(Q4_ERR_UNSUPPORTED, "q4_decode_step: n_layers = %lld: too many",
-                (long long)n_layers);
-  if (flags & ~(Q4_STEP_LAUNCH_EACH | Q4_STEP_ORDERED | Q4_STEP_WS_CLEAN | Q4_STEP_PERSISTENT))
-    return fail(Q4_ERR_SHAPE, "q4_decode_step: unknown flags 0x%x", flags);
-  char what[64];
-  for (int64_t i = 0; i < n_layers; ++i) {
-    const q4_layer& L = layers[i];
-    snprintf(what, sizeof what, "q4_decode_step: layers[%lld]", (long long)i);
-    if (L.x_op > Q4_X_SILU_MUL)
-      return fail(Q4_ERR_SHAPE, "%s: x_op = %u: unknown", what, L.x_op);
-    if (L.reserved) return fail(Q4_ERR_SHAPE, "%s: reserved = %u: must be 0", what, L.reserved);
-    if (int rc = check_gemv(what, L.words, L.scales, L.x, L.y, M, L.N, L.K,
-                            L.x_op ? 2 * L.K : L.K))
-      return rc;
-  }
-  const q4::DeviceInfo* d = q4::device_info();
-  if (!d) return fail(Q4_ERR_DEVICE, "q4_decode_step: no HIP device");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  if (M > 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
-    std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
-    q4::MStepPlan p = q4::plan_step_mfma(*d, sl.data(), n_layers, (int)M,
-                                         (flags & Q4_STEP_ORDERED) != 0);
-    int per_cu = 0;
-    int waiting = 0;
-    for (const q4::MStepDesc& sd : p.desc) waiting += sd.dep >= 0;
-    if (p.ok && !dependency_bound(n_layers, waiting, flags) &&
-        q4::step_mfma_occupancy(p, &per_cu) == hipSuccess && per_cu >= 1) {
-      if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_mfma_workspace_bytes(p)))
-        return rc;
-      hipError_t e = hipSuccess;
-      const size_t db = p.desc.size() * sizeof(q4::MStepDesc);
-      std::vector<uint8_t> host(db + p.ranges.size() * sizeof(int));
-      std::memcpy(host.data(), p.desc.data(), db);
-      if (!p.ranges.empty())
-        std::memcpy(host.data() + db, p.ranges.data(), p.ranges.size() * sizeof(int));
-      const void* table = device_table(host.data(), host.size(), d->id, s, &e);
-      if (!table) return device_error(e, "q4_decode_step: descriptor table");
-      const int4* ranges = reinterpret_cast<const int4*>(static_cast<const uint8_t*>(table) + db);
-      e = q4::launch_step_mfma(p, static_cast<const q4::MStepDesc*>(table), ranges, ws,
-                               (flags & Q4_STEP_WS_CLEAN) != 0, s);
-      return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
-    }
-    (void)hipGetLastError();
-  }
-  if (M == 1 && !(flags & Q4_STEP_LAUNCH_EACH)) {
-    std::vector<q4::StepLayer> sl = to_step_layers(layers, n_layers);
-    q4::StepPlan p = q4::plan_step(*d, sl.data(), n_layers, (flags & Q4_STEP_ORDERED) != 0);
-    if (use_persistent(*d, p, M, flags)) {
-      if (int rc = check_ws("q4_decode_step", ws, ws_bytes, q4::step_workspace_bytes(p)))
-        return rc;
-      hipError_t e = hipSuccess;
-      // descriptors, then (range mode) the per-workgroup ranges
-      const size_t db = p.desc.size() * sizeof(q4::StepDesc);
-      std::vector<uint8_t> host(db + p.ranges.size() * sizeof(int));
-      std::memcpy(host.data(), p.desc.data(), db);
-      if (!p.ranges.empty())
-        std::memcpy(host.data() + db, p.ranges.data(), p.ranges.size() * sizeof(int));
-      const void* table = device_table(host.data(), host.size(), d->id, s, &e);
-      if (!table) return device_error(e, "q4_decode_step: descriptor table");
-      const int4* ranges = reinterpret_cast<const int4*>(static_cast<const uint8_t*>(table) + db);
-      e = q4::launch_step(p, static_cast<const q4::StepDesc*>(table), ranges, ws,
-                          (flags & Q4_STEP_WS_CLEAN) != 0, s);
-      return e == hipSuccess ? ok() : device_error(e, "q4_decode_step");
-    }
-  }
-
-  const EachLayout el = each_layout(*d, layers, n_layers, M);
-  if (int rc = check_ws("q4_decode_step", ws, ws_bytes, el.bytes)) return rc;
-  uint16_t* glue = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + el.glue_off);
-  for (int64_t i = 0; i < n_layers; ++i) {
-    const q4_layer& L = layers[i];
-    hipError_t e = hipSuccess;
-    const uint16_t* x = L.x;
-    if (L.x_op == Q4_X_SILU_MUL) {
-      e = q4::launch_silu_mul(L.x, glue, M, L.K, s);
-      x = glue;
-    }
-    q4::GemvArgs a{L.words, L.scales, x, L.y, M, L.N, L.K};
-    if (e == hipSuccess) e = q4::launch_gemv(*d, a, el.plans[(size_t)i], ws, s);
-    if (e != hipSuccess) {
-      snprintf(what, sizeof what, "q4_decode_step: layers[%lld]", (long long)i);
-      return device_error(e, what);
-    }
-  }
-  return ok();
-}
 
 int q4_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t H, q4_stream_t stream) {
   if (!gu || !out) return fail(Q4_ERR_NULL, "q4_silu_mul: NULL pointer");

@@ -34,9 +34,15 @@ const DeviceInfo* device_info();
 int api_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int api_ok();
 
-// The argument checks of q4_gemv_batched (null pointers, shape, alignment, overlap).
+// The argument checks of one GEMV (null pointers, shape, alignment, overlap); x_cols:
+// elements per row of x (0: K).
 int gemv_validate(const char* what, const uint32_t* words, const uint16_t* scales,
-                  const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K);
+                  const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K,
+                  int64_t x_cols = 0);
+// The workspace check (NULL, size, 16-byte alignment) when `need` bytes are needed.
+int ws_validate(const char* what, void* ws, size_t have, size_t need);
+// Q4_ERR_DEVICE with the HIP error's text.
+int device_fail(hipError_t e, const char* what);
 // The body of q4_gemv / q4_gemv_batched / q4_gemv_splitk (q4_api.cpp): validate the
 // arguments, plan (splits == 0: automatic), check the workspace, launch.
 int gemv_common(const char* what, const uint32_t* words, const uint16_t* scales,

@@ -8,6 +8,26 @@
 namespace q4 {
 
 constexpr int kStepThreads = 1024;   // one workgroup of 16 waves per compute unit
+
+// The control block at the start of a decode-step workspace (uint32 words), read
+// and written by the persistent kernels: the error word, the hand-over epoch, the
+// exit count, then (from word kCtlWords) one completion counter per descriptor.
+constexpr int kCtlErr = 0;     // a bounded wait ran out: code | (GEMV + 1) << 8 (0: none)
+constexpr int kCtlEpoch = 1;   // epoch the last launch tagged its handed-over values with
+constexpr int kCtlExit = 2;    // workgroups past their work in the current launch
+constexpr int kCtlWords = 64;  // 256 bytes
+// Error codes of kCtlErr (the wait that ran out).
+constexpr unsigned kErrLocal = 1;    // sync wave: this workgroup's compute waves on a GEMV
+constexpr unsigned kErrCounter = 2;  // sync wave: a GEMV's completion counter
+constexpr unsigned kErrX = 3;        // compute wave: a GEMV's x in LDS
+constexpr unsigned kErrTag = 4;      // sync wave: a GEMV's tagged hand-over
+constexpr unsigned kErrRegion = 5;   // sync wave (small M): an LDS region's previous user
+
+// Record the first bounded wait that ran out (any racing writer's value is valid).
+__device__ __forceinline__ void report_error(unsigned* ctl, unsigned code, int gemv) {
+  __hip_atomic_store(ctl + kCtlErr, code | ((unsigned)(gemv + 1) << 8), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
 constexpr int kXBufs = 8;            // x buffers: waves may run up to 8 GEMVs apart
 
 // Descriptor flags.
@@ -53,7 +73,6 @@ struct StepPlan {
   int grid = 0;          // workgroups (one per compute unit)
   int maxG = 0;
   int ybuf_rows = 0;
-  int counters = 0;      // completion counters, exit counter, spare, error word
   size_t tag_base = 0;   // workspace byte offset of the tagged pairs (after the counters)
   size_t tag_bytes = 0;  // their size (0: no descriptor hands its y over that way)
   bool cross_wg = false; // some descriptor waits for others on every workgroup: all
@@ -67,19 +86,37 @@ struct StepPlan {
   std::vector<StepDesc> desc;
 };
 
+// What launching a planned list needs, as plain data (kept in the caller's plan
+// buffer).  Workspace layout: control block and completion counters, tagged
+// pairs, then the device tables (descriptors, then the ranges if any).
+struct StepLaunch {
+  int32_t kind;          // 1: k_step (M = 1), 2: k_step_mfma (2 <= M <= 8)
+  int32_t n, grid, M;
+  int32_t nx, maxG, ybuf_rows, stage_off;
+  int32_t cross_wg, has_ranges;
+  uint32_t lds_bytes, pad;
+  uint64_t table_off, ranges_off, table_bytes;
+  uint64_t clear_bytes;  // bytes cleared at set-up: control block, counters, tags
+  uint64_t ws_bytes;     // total workspace
+};
+
 // ordered: every descriptor waits for its predecessor (a chain of dependent GEMVs);
 // otherwise only for earlier descriptors whose memory it shares.
 StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool ordered,
                    bool tags = true);
-size_t step_workspace_bytes(const StepPlan& p);
-// dev_desc: p.desc copied to device memory.  Zeroes the counters in ws (unless
-// ws_clean: they are already zero, as the kernel leaves them), then runs the
-// cooperative kernel.
-// dev_ranges: p.ranges copied to device memory (nullptr when p.ranges is empty).
-hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, const int4* dev_ranges,
-                       void* ws, bool ws_clean, hipStream_t s);
-// The epoch the next launch tags its handed-over pairs with (never 0, increasing).
-uint32_t next_step_epoch();
+// The launch record and the table bytes of a plan.
+StepLaunch step_launch_of(const StepPlan& p);
+void step_table_bytes(const StepPlan& p, std::vector<uint8_t>* out);
 hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu);
+// The kernel's attribute for the plan's LDS (once per process and device).
+hipError_t step_prepare(const StepLaunch& L);
+// Enqueue one launch of a planned list (tables and counters already in ws).
+hipError_t launch_step(const StepLaunch& L, void* ws, hipStream_t s);
+
+// Set-up helpers shared by both persistent kernels, kernels only (no copy from
+// host memory, no allocation, capturable): write `bytes` (a multiple of 4) of
+// host data to device memory through kernel arguments, and zero device words.
+hipError_t write_table(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t zero_words(void* dst, size_t words, hipStream_t s);
 
 }  // namespace q4

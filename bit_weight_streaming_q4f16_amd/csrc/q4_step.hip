@@ -32,8 +32,8 @@
 // that k reads or writes; the "ordered" mode makes every descriptor wait for its
 // predecessor, as in a decode step whose GEMVs feed each other.
 #include <algorithm>
-#include <atomic>
 #include <climits>
+#include <cstring>
 
 #include "q4_step.h"
 
@@ -228,12 +228,16 @@ __device__ __forceinline__ int wg_step(int sbase, int srem, int wg) {
 //   ybuf[b]: ybuf_rows fp16 results of this workgroup's rows
 template <int B, int NX>
 __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restrict__ D, int n,
-                                                       unsigned* __restrict__ done,
-                                                       unsigned* __restrict__ err, int maxG,
+                                                       unsigned* __restrict__ ctl, int maxG,
                                                        int ybuf_rows,
-                                                       const int4* __restrict__ ranges,
-                                                       unsigned epoch) {
+                                                       const int4* __restrict__ ranges) {
   static_assert(NX <= kXBufs && NX % kSync == 0, "x buffers");
+  unsigned* const done = ctl + kCtlWords;       // completion counters
+  // this launch's hand-over epoch: one past the last launch's (never 0); the
+  // last workgroup to finish stores it for the next launch
+  unsigned epoch = __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  epoch = epoch + 1u == 0u ? 1u : epoch + 1u;
   extern __shared__ uint4 smem[];
   __shared__ Shared sh;
   uint4* xbuf = smem;                                                           // [NX][4][maxG]
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         // per pair (two values and the epoch land together), written through to
         // the coherence point; nothing waits for them here (r0 is even)
         const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-            reinterpret_cast<unsigned char*>(done) + d.tag_out, 0, 0x7FFFFFFF, 0x00020000);
+            reinterpret_cast<unsigned char*>(ctl) + d.tag_out, 0, 0x7FFFFFFF, 0x00020000);
         for (int q = (r0 >> 1) + lane; 2 * q < r1; q += 64) {
           const uint32_t lo16 = yb[2 * q - r0];
           const uint32_t hi16 = 2 * q + 1 < r1 ? yb[2 * q + 1 - r0] : 0u;
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           // a long sleep: polling issues vector instructions that the
           // compute waves on this SIMD would otherwise use
           for (unsigned it = 0; !complete(next_fin); ++it) {
-            if (it > kSpinLimit / 8) { err[0] = 1u; break; }
+            if (it > kSpinLimit / 8) { report_error(ctl, kErrLocal, next_fin); break; }
             __builtin_amdgcn_s_sleep(8);
           }
         }
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         // this workgroup's own share of the producer comes first (the others
         // finish at about the same time): poll the pairs only after it
         for (unsigned it = 0; d.dep >= j0 && !complete(d.dep); ++it) {
-          if (it > kSpinLimit) { err[0] = 4u; break; }
+          if (it > kSpinLimit) { report_error(ctl, kErrTag, k); break; }
           finish_upto(k - kSync, false);
           __builtin_amdgcn_s_sleep(1);
         }
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
              __hip_atomic_load(&done[d.dep], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
              (unsigned)nwg;
              ++it) {
-          if (it > kSpinLimit) { err[0] = 2u; break; }
+          if (it > kSpinLimit) { report_error(ctl, kErrCounter, k); break; }
           finish_upto(k - kSync, false);         // others may be waiting for those
           __builtin_amdgcn_s_sleep(1);
         }
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           };
           if (tagged) {
             const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-                reinterpret_cast<unsigned char*>(done) + d.tag_in, 0, 0x7FFFFFFF, 0x00020000);
+                reinterpret_cast<unsigned char*>(ctl) + d.tag_in, 0, 0x7FFFFFFF, 0x00020000);
             unsigned pend = 0;
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -423,7 +427,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
                 }
               }
               if (!__builtin_amdgcn_ballot_w64(pend != 0u)) break;
-              if (it > kTagSpinLimit) { err[0] = 4u; break; }
+              if (it > kTagSpinLimit) { report_error(ctl, kErrTag, k); break; }
               finish_upto(k - kSync, false);
               __builtin_amdgcn_s_sleep(1);
             }
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           // coherence point); a block is taken once all four carry this call's
           // epoch, and re-read until then
           const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-              reinterpret_cast<unsigned char*>(done) + d.tag_in, 0, 0x7FFFFFFF, 0x00020000);
+              reinterpret_cast<unsigned char*>(ctl) + d.tag_in, 0, 0x7FFFFFFF, 0x00020000);
           unsigned pend = 0;
 #pragma unroll
           for (int u = 0; u < 8; ++u)
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
               }
             }
             if (!__builtin_amdgcn_ballot_w64(pend != 0u)) break;
-            if (it > kTagSpinLimit) { err[0] = 4u; break; }
+            if (it > kTagSpinLimit) { report_error(ctl, kErrTag, k); break; }
             finish_upto(k - kSync, false);
             __builtin_amdgcn_s_sleep(1);
           }
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       }
       if (lane == 0) {
         const int e = lds_load(&sh.err);
-        if (e) err[0] = (unsigned)e;
+        if (e) report_error(ctl, kErrX, e - 1);
       }
     }
   } else {
@@ -622,7 +626,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   auto wait_x = [&](int j) {
     for (unsigned it = 0; lds_load(&sh.x_ready[(j - j0) % NX]) != j; ++it) {
       if (it > kSpinLimit) {
-        __hip_atomic_store(&sh.err, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&sh.err, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -788,35 +792,65 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     signal_upto(j1 + 1);
   }
 
-  // Leave the counters zeroed for the next call: the last workgroup to get here
-  // (every other one has finished with them) clears them.
+  // Leave the counters zeroed for the next call and hand it the epoch: the last
+  // workgroup to get here (every other one has finished with them, and every
+  // one read the epoch when it started) does it.
   __syncthreads();
   if (wave == 0) {
     unsigned old = 0;
     if (lane == 0)
-      old = __hip_atomic_fetch_add(done + n, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      old = __hip_atomic_fetch_add(ctl + kCtlExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);
     if (old == (unsigned)nwg - 1u) {
-      for (int i = lane; i <= n; i += 64)
+      for (int i = lane; i < n; i += 64)
         __hip_atomic_store(done + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) {
+        __hip_atomic_store(ctl + kCtlExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctl + kCtlEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
 
-__global__ void k_zero(unsigned* __restrict__ p, int count) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x)
+__global__ void k_zero(unsigned* __restrict__ p, size_t count) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count;
+       i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0u;
+}
+
+// A piece of a table passed by value in the kernel arguments.
+constexpr int kPieceWords = 240;
+struct TablePiece {
+  uint32_t w[kPieceWords];
+};
+__global__ void k_put(uint32_t* __restrict__ dst, TablePiece piece, int count) {
+  if ((int)threadIdx.x < count) dst[threadIdx.x] = piece.w[threadIdx.x];
 }
 
 constexpr int kBurst = 2;
 
 }  // namespace
 
-uint32_t next_step_epoch() {
-  static std::atomic<uint32_t> epoch{0};
-  uint32_t e = epoch.fetch_add(1u) + 1u;
-  if (e == 0u) e = epoch.fetch_add(1u) + 1u;   // 0 marks pairs never written
-  return e;
+hipError_t write_table(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (bytes % 4) return hipErrorInvalidValue;
+  const uint32_t* w = static_cast<const uint32_t*>(src);
+  uint32_t* d = static_cast<uint32_t*>(dst);
+  const size_t words = bytes / 4;
+  for (size_t i = 0; i < words; i += kPieceWords) {
+    const int c = (int)std::min<size_t>(kPieceWords, words - i);
+    TablePiece piece;
+    std::memcpy(piece.w, w + i, (size_t)c * 4);
+    hipLaunchKernelGGL(k_put, dim3(1), dim3(256), 0, s, d + i, piece, c);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t zero_words(void* dst, size_t words, hipStream_t s) {
+  if (!words) return hipSuccess;
+  const int blocks = (int)std::max<size_t>(1, std::min<size_t>(1024, words / 4096));
+  hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(256), 0, s, static_cast<unsigned*>(dst), words);
+  return hipGetLastError();
 }
 
 StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool ordered,
@@ -913,11 +947,10 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
       if (i != h) return p;                     // not covered: one kernel per GEMV
     }
   }
-  // tagged pairs: after the counters, one 256-byte aligned run per producer; a
-  // producer with one row per row-step splits its rows over the workgroups in
-  // pairs, so every workgroup's first row is even
-  p.counters = (int)n + 4;
-  p.tag_base = ((size_t)p.counters * sizeof(unsigned) + 255) & ~(size_t)255;
+  // tagged pairs: after the control block and the counters, one 256-byte aligned
+  // run per producer; a producer with one row per row-step splits its rows over
+  // the workgroups in pairs, so every workgroup's first row is even
+  p.tag_base = (((size_t)kCtlWords + (size_t)n) * sizeof(unsigned) + 255) & ~(size_t)255;
   std::vector<size_t> tag_off((size_t)n, 0);
   size_t tag_end = p.tag_base;
   for (int64_t k = 0; k < n; ++k) {
@@ -1019,50 +1052,69 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
   return p;
 }
 
-size_t step_workspace_bytes(const StepPlan& p) {
-  if (p.tag_bytes) return p.tag_base + p.tag_bytes;
-  return ((size_t)p.counters * sizeof(unsigned) + 255) & ~(size_t)255;
+StepLaunch step_launch_of(const StepPlan& p) {
+  StepLaunch L{};
+  L.kind = 1;
+  L.n = (int)p.desc.size();
+  L.grid = p.grid;
+  L.M = 1;
+  L.nx = p.nx;
+  L.maxG = p.maxG;
+  L.ybuf_rows = p.ybuf_rows;
+  L.stage_off = -1;
+  L.cross_wg = p.cross_wg;
+  L.has_ranges = !p.ranges.empty();
+  L.lds_bytes = (uint32_t)p.lds_bytes;
+  L.clear_bytes = p.tag_base + p.tag_bytes;
+  L.table_off = (L.clear_bytes + 255) & ~(uint64_t)255;
+  L.ranges_off = L.table_off + p.desc.size() * sizeof(StepDesc);
+  L.table_bytes = p.desc.size() * sizeof(StepDesc) + p.ranges.size() * sizeof(int);
+  L.ws_bytes = L.table_off + L.table_bytes;
+  return L;
 }
 
-hipError_t launch_step(const StepPlan& p, const StepDesc* dev_desc, const int4* dev_ranges,
-                       void* ws, bool ws_clean, hipStream_t s) {
-  unsigned* done = static_cast<unsigned*>(ws);
-  unsigned* err = done + (p.counters - 1);
-  if (!ws_clean) {
-    // counters, and the tagged pairs (so no stale word can carry this epoch)
-    const int words = (int)(step_workspace_bytes(p) / sizeof(unsigned));
-    const int blocks = std::max(1, std::min(1024, words / 4096));
-    hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(256), 0, s, done, words);
-    if (hipError_t e = hipGetLastError()) return e;
-  }
-  unsigned epoch = next_step_epoch();
-  auto kern = p.nx == 4 ? k_step<kBurst, 4> : k_step<kBurst, kXBufs>;
-  if (p.lds_bytes > 65536) {
-    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)p.lds_bytes))
-      return e;
-  }
-  int n = (int)p.desc.size(), maxG = p.maxG, yr = p.ybuf_rows;
-  const int4* rg = p.ranges.empty() ? nullptr : dev_ranges;
-  void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&done, (void*)&err, (void*)&maxG,
-                  (void*)&yr, (void*)&rg, (void*)&epoch};
+void step_table_bytes(const StepPlan& p, std::vector<uint8_t>* out) {
+  const size_t db = p.desc.size() * sizeof(StepDesc);
+  out->resize(db + p.ranges.size() * sizeof(int));
+  std::memcpy(out->data(), p.desc.data(), db);
+  if (!p.ranges.empty())
+    std::memcpy(out->data() + db, p.ranges.data(), p.ranges.size() * sizeof(int));
+}
+
+namespace {
+auto step_kernel(int nx) { return nx == 4 ? k_step<kBurst, 4> : k_step<kBurst, kXBufs>; }
+}  // namespace
+
+hipError_t step_prepare(const StepLaunch& L) {
+  if (L.lds_bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(step_kernel(L.nx)),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds_bytes);
+}
+
+hipError_t launch_step(const StepLaunch& L, void* ws, hipStream_t s) {
+  unsigned* ctl = static_cast<unsigned*>(ws);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const StepDesc* desc = reinterpret_cast<const StepDesc*>(base + L.table_off);
+  const int4* rg = L.has_ranges ? reinterpret_cast<const int4*>(base + L.ranges_off) : nullptr;
+  auto kern = step_kernel(L.nx);
+  int n = L.n, maxG = L.maxG, yr = L.ybuf_rows;
   // Only waits across workgroups need every workgroup resident at once; without
   // them (no descriptor depends on another) a plain launch does, and it costs
   // far less at the kernel boundary than a cooperative one.
-  if (p.cross_wg)
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(p.grid),
-                                      dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
-  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kStepThreads), p.lds_bytes, s, dev_desc, n, done,
-                     err, maxG, yr, rg, epoch);
+  if (L.cross_wg) {
+    void* args[] = {(void*)&desc, (void*)&n, (void*)&ctl, (void*)&maxG, (void*)&yr, (void*)&rg};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(L.grid),
+                                      dim3(kStepThreads), args, L.lds_bytes, s);
+  }
+  hipLaunchKernelGGL(kern, dim3(L.grid), dim3(kStepThreads), L.lds_bytes, s, desc, n, ctl, maxG,
+                     yr, rg);
   return hipGetLastError();
 }
 
 hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
       blocks_per_cu,
-      reinterpret_cast<const void*>(p.nx == 4 ? k_step<kBurst, 4> : k_step<kBurst, kXBufs>),
-      kStepThreads, p.lds_bytes);
+      reinterpret_cast<const void*>(step_kernel(p.nx)), kStepThreads, p.lds_bytes);
 }
 
 }  // namespace q4

@@ -28,7 +28,7 @@ static_assert(sizeof(MStepDesc) == 64, "MStepDesc layout");
 struct MStepPlan {
   bool ok = false;
   bool cross_wg = false;     // some descriptor waits for another on every workgroup
-  int grid = 0, M = 0, counters = 0;
+  int grid = 0, M = 0;
   size_t lds_bytes = 0;
   int stage_off = 0;         // LDS offset of the compute waves' load stages
   std::vector<MStepDesc> desc;
@@ -41,9 +41,12 @@ struct MStepPlan {
 // every GEMV's LDS region (16 K + 2 M rows bytes) within the LDS.
 MStepPlan plan_step_mfma(const DeviceInfo& d, const StepLayer* layers, int64_t n, int M,
                          bool ordered);
-size_t step_mfma_workspace_bytes(const MStepPlan& p);
+// Launch record (workspace: control block and counters, then the tables) and
+// table bytes of a plan.
+StepLaunch step_mfma_launch_of(const MStepPlan& p);
+void step_mfma_table_bytes(const MStepPlan& p, std::vector<uint8_t>* out);
 hipError_t step_mfma_occupancy(const MStepPlan& p, int* blocks_per_cu);
-hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc,
-                            const int4* dev_ranges, void* ws, bool ws_clean, hipStream_t s);
+hipError_t step_mfma_prepare(const StepLaunch& L);
+hipError_t launch_step_mfma(const StepLaunch& L, void* ws, hipStream_t s);
 
 }  // namespace q4

@@ -34,6 +34,7 @@
 // after the GEMVs that used it before are finished.
 #include <algorithm>
 #include <climits>
+#include <cstring>
 
 #include "q4_step_mfma.h"
 
@@ -145,10 +146,10 @@ __device__ __forceinline__ TileDesc read_desc(const MStepDesc* d) {
 __device__ __forceinline__ int ybuf_off(int, int G) { return 8 * G * 64; }
 
 __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __restrict__ D, int n,
-                                                            int M, unsigned* __restrict__ done,
-                                                            unsigned* __restrict__ err,
+                                                            int M, unsigned* __restrict__ ctl,
                                                             const int4* __restrict__ ranges,
                                                             int stage_off) {
+  unsigned* const done = ctl + kCtlWords;       // completion counters
   extern __shared__ uint4 smem[];
   __shared__ Shared sh;
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
         if (!complete(next_fin)) {
           if (!block) return;
           for (unsigned it = 0; !complete(next_fin); ++it) {
-            if (it > kSpinLimit / 8) { err[0] = 1u; break; }
+            if (it > kSpinLimit / 8) { report_error(ctl, kErrLocal, next_fin); break; }
             __builtin_amdgcn_s_sleep(8);
           }
         }
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       if (k - j0 >= kSlots) finish_upto(k - kSlots, true);   // slot (k - j0) % kSlots is free
       if (d.rel >= 0) {
         for (unsigned it = 0; !finished_upto(d.rel); ++it) {
-          if (it > kSpinLimit) { err[0] = 5u; break; }
+          if (it > kSpinLimit) { report_error(ctl, kErrRegion, k); break; }
           finish_upto(k - kSync, false);
           finish_upto(d.rel, false);
           __builtin_amdgcn_s_sleep(2);
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
              __hip_atomic_load(&done[d.dep], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
              (unsigned)nwg;
              ++it) {
-          if (it > kSpinLimit) { err[0] = 2u; break; }
+          if (it > kSpinLimit) { report_error(ctl, kErrCounter, k); break; }
           finish_upto(k - kSync, false);
           __builtin_amdgcn_s_sleep(1);
         }
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       }
       if (lane == 0) {
         const int e = lds_load(&sh.err);
-        if (e) err[0] = (unsigned)e;
+        if (e) report_error(ctl, kErrX, e - 1);
       }
     }
   } else {
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
     auto wait_x = [&](int j) {
       for (unsigned it = 0; lds_load(&sh.x_ready[(j - j0) % kSlots]) != j; ++it) {
         if (it > kSpinLimit) {
-          lds_store(&sh.err, 3);
+          lds_store(&sh.err, j + 1);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -602,18 +603,15 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
   if (wave == 0) {
     unsigned old = 0;
     if (lane == 0)
-      old = __hip_atomic_fetch_add(done + n, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      old = __hip_atomic_fetch_add(ctl + kCtlExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);
     if (old == (unsigned)nwg - 1u) {
-      for (int i = lane; i <= n; i += 64)
+      for (int i = lane; i < n; i += 64)
         __hip_atomic_store(done + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        __hip_atomic_store(ctl + kCtlExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-}
-
-__global__ void k_zero_m(unsigned* __restrict__ p, int count) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x)
-    p[i] = 0u;
 }
 
 }  // namespace
@@ -763,7 +761,6 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
       }
       p.ranges = std::move(ranges);
       p.lds_bytes = total_lds;
-      p.counters = (int)n + 4;
       p.ok = true;
       return p;
     }
@@ -776,13 +773,34 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
   }
   if (!place()) return p;
   p.lds_bytes = total_lds;
-  p.counters = (int)n + 4;
   p.ok = true;
   return p;
 }
 
-size_t step_mfma_workspace_bytes(const MStepPlan& p) {
-  return ((size_t)p.counters * sizeof(unsigned) + 255) & ~(size_t)255;
+StepLaunch step_mfma_launch_of(const MStepPlan& p) {
+  StepLaunch L{};
+  L.kind = 2;
+  L.n = (int)p.desc.size();
+  L.grid = p.grid;
+  L.M = p.M;
+  L.stage_off = p.stage_off;
+  L.cross_wg = p.cross_wg;
+  L.has_ranges = !p.ranges.empty();
+  L.lds_bytes = (uint32_t)p.lds_bytes;
+  L.clear_bytes = (((uint64_t)kCtlWords + p.desc.size()) * 4 + 255) & ~(uint64_t)255;
+  L.table_off = L.clear_bytes;
+  L.ranges_off = L.table_off + p.desc.size() * sizeof(MStepDesc);
+  L.table_bytes = p.desc.size() * sizeof(MStepDesc) + p.ranges.size() * sizeof(int);
+  L.ws_bytes = L.table_off + L.table_bytes;
+  return L;
+}
+
+void step_mfma_table_bytes(const MStepPlan& p, std::vector<uint8_t>* out) {
+  const size_t db = p.desc.size() * sizeof(MStepDesc);
+  out->resize(db + p.ranges.size() * sizeof(int));
+  std::memcpy(out->data(), p.desc.data(), db);
+  if (!p.ranges.empty())
+    std::memcpy(out->data() + db, p.ranges.data(), p.ranges.size() * sizeof(int));
 }
 
 hipError_t step_mfma_occupancy(const MStepPlan& p, int* blocks_per_cu) {
@@ -790,29 +808,24 @@ hipError_t step_mfma_occupancy(const MStepPlan& p, int* blocks_per_cu) {
       blocks_per_cu, reinterpret_cast<const void*>(k_step_mfma), kStepThreads, p.lds_bytes);
 }
 
-hipError_t launch_step_mfma(const MStepPlan& p, const MStepDesc* dev_desc,
-                            const int4* dev_ranges, void* ws, bool ws_clean, hipStream_t s) {
-  unsigned* done = static_cast<unsigned*>(ws);
-  unsigned* err = done + (p.counters - 1);
-  if (!ws_clean) {
-    hipLaunchKernelGGL(k_zero_m, dim3(1), dim3(256), 0, s, done, p.counters);
-    if (hipError_t e = hipGetLastError()) return e;
+hipError_t step_mfma_prepare(const StepLaunch& L) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(k_step_mfma),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds_bytes);
+}
+
+hipError_t launch_step_mfma(const StepLaunch& L, void* ws, hipStream_t s) {
+  unsigned* ctl = static_cast<unsigned*>(ws);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const MStepDesc* desc = reinterpret_cast<const MStepDesc*>(base + L.table_off);
+  const int4* rg = L.has_ranges ? reinterpret_cast<const int4*>(base + L.ranges_off) : nullptr;
+  int n = L.n, M = L.M, so = L.stage_off;
+  if (L.cross_wg) {
+    void* args[] = {(void*)&desc, (void*)&n, (void*)&M, (void*)&ctl, (void*)&rg, (void*)&so};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_step_mfma), dim3(L.grid),
+                                      dim3(kStepThreads), args, L.lds_bytes, s);
   }
-  if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_step_mfma),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)p.lds_bytes))
-    return e;
-  int n = (int)p.desc.size(), M = p.M;
-  const int4* rg = p.ranges.empty() ? nullptr : dev_ranges;
-  int so = p.stage_off;
-  if (p.cross_wg) {
-    void* args[] = {(void*)&dev_desc, (void*)&n, (void*)&M, (void*)&done, (void*)&err,
-                    (void*)&rg, (void*)&so};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_step_mfma), dim3(p.grid),
-                                      dim3(kStepThreads), args, (unsigned)p.lds_bytes, s);
-  }
-  hipLaunchKernelGGL(k_step_mfma, dim3(p.grid), dim3(kStepThreads), p.lds_bytes, s, dev_desc, n,
-                     M, done, err, rg, so);
+  hipLaunchKernelGGL(k_step_mfma, dim3(L.grid), dim3(kStepThreads), L.lds_bytes, s, desc, n, M,
+                     ctl, rg, so);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
+#include <new>
 #include <vector>
 
 #include "q4f16.h"
@@ -208,76 +208,17 @@ hipError_t enqueue_step(const q4::DeviceInfo& d, const q4_model& m, const Layout
 
 // ---------------------------------------------------------------- graphs
 
-struct GraphEntry {
-  std::vector<uint8_t> key;
+}  // namespace
+
+// A captured decode step (the handle of include/q4f16.h): tokens[counter] ->
+// tokens[counter + 1], the counter kept in the workspace.
+struct q4_tokens_graph {
   hipGraphExec_t exec = nullptr;
-  uint64_t last_use = 0;
+  int device = -1;
+  int32_t* counter = nullptr;        // device: the step counter in the workspace
 };
-constexpr size_t kMaxGraphs = 4;
-std::mutex g_graph_mutex;
-std::vector<GraphEntry> g_graphs;
-uint64_t g_graph_clock = 0;
-hipStream_t g_capture_stream[64] = {};
 
-std::vector<uint8_t> graph_key(const q4_model& m, const void* ws, size_t ws_bytes,
-                               const int32_t* tokens, int dev) {
-  std::vector<uint8_t> k;
-  auto put = [&](const void* p, size_t n) {
-    const uint8_t* b = static_cast<const uint8_t*>(p);
-    k.insert(k.end(), b, b + n);
-  };
-  put(&m, sizeof m);
-  if (m.n_blocks > 0) put(m.blocks, sizeof(q4_block) * (size_t)m.n_blocks);
-  put(&ws, sizeof ws);
-  put(&ws_bytes, sizeof ws_bytes);
-  put(&tokens, sizeof tokens);
-  put(&dev, sizeof dev);
-  return k;
-}
-
-// The graph of one step of tokens[counter] -> tokens[counter + 1]; captured on a
-// private stream (the caller's may be the null stream, which cannot be captured).
-hipError_t step_graph(const q4::DeviceInfo& d, const q4_model& m, const Layout& L,
-                      int32_t* tokens, uint8_t* ws, size_t ws_bytes, hipGraphExec_t* out) {
-  std::lock_guard<std::mutex> lock(g_graph_mutex);
-  std::vector<uint8_t> key = graph_key(m, ws, ws_bytes, tokens, d.id);
-  for (GraphEntry& e : g_graphs)
-    if (e.key == key) {
-      e.last_use = ++g_graph_clock;
-      *out = e.exec;
-      return hipSuccess;
-    }
-  hipStream_t& cs = g_capture_stream[d.id];
-  if (!cs)
-    if (hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking)) return e;
-  int32_t* tok = reinterpret_cast<int32_t*>(ws + L.tok);   // cur, next, counter
-  if (hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal)) return e;
-  hipError_t err = q4::launch_token_fetch(tokens, tok + 2, tok, cs);
-  if (err == hipSuccess) err = enqueue_step(d, m, L, tok, tok + 1, nullptr, ws, cs);
-  if (err == hipSuccess) err = q4::launch_token_store(tokens, tok + 2, tok + 1, cs);
-  hipGraph_t graph = nullptr;
-  const hipError_t end = hipStreamEndCapture(cs, &graph);
-  if (err == hipSuccess) err = end;
-  hipGraphExec_t exec = nullptr;
-  if (err == hipSuccess) err = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-  if (graph) (void)hipGraphDestroy(graph);
-  if (err != hipSuccess) return err;
-  if (g_graphs.size() >= kMaxGraphs) {
-    size_t lru = 0;
-    for (size_t i = 1; i < g_graphs.size(); ++i)
-      if (g_graphs[i].last_use < g_graphs[lru].last_use) lru = i;
-    (void)hipDeviceSynchronize();          // no launch of it still in flight
-    (void)hipGraphExecDestroy(g_graphs[lru].exec);
-    g_graphs.erase(g_graphs.begin() + (ptrdiff_t)lru);
-  }
-  GraphEntry e;
-  e.key = std::move(key);
-  e.exec = exec;
-  e.last_use = ++g_graph_clock;
-  g_graphs.push_back(std::move(e));
-  *out = exec;
-  return hipSuccess;
-}
+namespace {
 
 int device_error(hipError_t e, const char* what) {
   return q4::api_fail(Q4_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -312,14 +253,12 @@ int q4_decode_token(const q4_model* model, const int32_t* token_in, int32_t* tok
 }
 
 int q4_decode_tokens(const q4_model* model, int32_t* tokens, int64_t steps, void* ws,
-                     size_t ws_bytes, uint32_t flags, q4_stream_t stream) {
+                     size_t ws_bytes, q4_stream_t stream) {
   if (int rc = check_model(model)) return q4::api_fail(rc, "q4_decode_tokens: %s", q4_last_error());
   if (!tokens) return q4::api_fail(Q4_ERR_NULL, "q4_decode_tokens: tokens is NULL");
   if (!aligned(tokens, 4)) return q4::api_fail(Q4_ERR_ALIGN, "q4_decode_tokens: tokens misaligned");
   if (steps < 0 || steps > INT32_MAX - 1)
     return q4::api_fail(Q4_ERR_SHAPE, "q4_decode_tokens: steps = %lld", (long long)steps);
-  if (flags & ~Q4_TOKENS_EAGER)
-    return q4::api_fail(Q4_ERR_SHAPE, "q4_decode_tokens: unknown flags 0x%x", flags);
   const q4::DeviceInfo* d = q4::device_info();
   if (!d) return q4::api_fail(Q4_ERR_DEVICE, "q4_decode_tokens: no HIP device");
   const Layout L = layout_for(*d, *model);
@@ -329,21 +268,75 @@ int q4_decode_tokens(const q4_model* model, int32_t* tokens, int64_t steps, void
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* w = static_cast<uint8_t*>(ws);
   int32_t* tok = reinterpret_cast<int32_t*>(w + L.tok);
-  hipError_t e = hipSuccess;
-  if (flags & Q4_TOKENS_EAGER) {
-    e = q4::launch_counter_reset(tok + 2, s);
-    for (int64_t i = 0; i < steps && e == hipSuccess; ++i) {
-      e = q4::launch_token_fetch(tokens, tok + 2, tok, s);
-      if (e == hipSuccess) e = enqueue_step(*d, *model, L, tok, tok + 1, nullptr, w, s);
-      if (e == hipSuccess) e = q4::launch_token_store(tokens, tok + 2, tok + 1, s);
-    }
-  } else {
-    hipGraphExec_t exec = nullptr;
-    e = step_graph(*d, *model, L, tokens, w, ws_bytes, &exec);
-    if (e == hipSuccess) e = q4::launch_counter_reset(tok + 2, s);
-    for (int64_t i = 0; i < steps && e == hipSuccess; ++i) e = hipGraphLaunch(exec, s);
+  hipError_t e = q4::launch_counter_reset(tok + 2, s);
+  for (int64_t i = 0; i < steps && e == hipSuccess; ++i) {
+    e = q4::launch_token_fetch(tokens, tok + 2, tok, s);
+    if (e == hipSuccess) e = enqueue_step(*d, *model, L, tok, tok + 1, nullptr, w, s);
+    if (e == hipSuccess) e = q4::launch_token_store(tokens, tok + 2, tok + 1, s);
   }
   return e == hipSuccess ? q4::api_ok() : device_error(e, "q4_decode_tokens");
+}
+
+int q4_tokens_graph_create(const q4_model* model, int32_t* tokens, void* ws, size_t ws_bytes,
+                           q4_stream_t stream, q4_tokens_graph** out) {
+  const char* what = "q4_tokens_graph_create";
+  if (!out) return q4::api_fail(Q4_ERR_NULL, "%s: out is NULL", what);
+  *out = nullptr;
+  if (int rc = check_model(model)) return q4::api_fail(rc, "%s: %s", what, q4_last_error());
+  if (!tokens) return q4::api_fail(Q4_ERR_NULL, "%s: tokens is NULL", what);
+  if (!aligned(tokens, 4)) return q4::api_fail(Q4_ERR_ALIGN, "%s: tokens misaligned", what);
+  if (!stream)
+    return q4::api_fail(Q4_ERR_SHAPE, "%s: the null stream cannot be captured; pass a stream",
+                        what);
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return q4::api_fail(Q4_ERR_DEVICE, "%s: no HIP device", what);
+  const Layout L = layout_for(*d, *model);
+  if (int rc = check_ws(ws, ws_bytes, L.bytes))
+    return q4::api_fail(rc, "%s: %s", what, q4_last_error());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  int32_t* tok = reinterpret_cast<int32_t*>(w + L.tok);   // cur, next, counter
+  if (hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal))
+    return device_error(e, what);
+  hipError_t err = q4::launch_token_fetch(tokens, tok + 2, tok, s);
+  if (err == hipSuccess) err = enqueue_step(*d, *model, L, tok, tok + 1, nullptr, w, s);
+  if (err == hipSuccess) err = q4::launch_token_store(tokens, tok + 2, tok + 1, s);
+  hipGraph_t graph = nullptr;
+  const hipError_t end = hipStreamEndCapture(s, &graph);
+  if (err == hipSuccess) err = end;
+  hipGraphExec_t exec = nullptr;
+  if (err == hipSuccess) err = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (err != hipSuccess) return device_error(err, what);
+  q4_tokens_graph* g = new (std::nothrow) q4_tokens_graph;
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    return q4::api_fail(Q4_ERR_DEVICE, "%s: out of host memory", what);
+  }
+  g->exec = exec;
+  g->device = d->id;
+  g->counter = tok + 2;
+  *out = g;
+  return q4::api_ok();
+}
+
+int q4_tokens_graph_run(q4_tokens_graph* g, int64_t steps, q4_stream_t stream) {
+  const char* what = "q4_tokens_graph_run";
+  if (!g || !g->exec) return q4::api_fail(Q4_ERR_NULL, "%s: graph is NULL", what);
+  if (steps < 0 || steps > INT32_MAX - 1)
+    return q4::api_fail(Q4_ERR_SHAPE, "%s: steps = %lld", what, (long long)steps);
+  if (steps == 0) return q4::api_ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = q4::launch_counter_reset(g->counter, s);
+  for (int64_t i = 0; i < steps && e == hipSuccess; ++i) e = hipGraphLaunch(g->exec, s);
+  return e == hipSuccess ? q4::api_ok() : device_error(e, what);
+}
+
+int q4_tokens_graph_destroy(q4_tokens_graph* g) {
+  if (!g) return q4::api_ok();
+  hipError_t e = g->exec ? hipGraphExecDestroy(g->exec) : hipSuccess;
+  delete g;
+  return e == hipSuccess ? q4::api_ok() : device_error(e, "q4_tokens_graph_destroy");
 }
 
 }  // extern "C"

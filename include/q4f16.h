@@ -19,12 +19,15 @@
  *    function says otherwise.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
  *    enqueued on it; results are valid once the caller synchronises that stream.
- *    No entry point synchronises the host with the device.
+ *    No entry point synchronises the host with the device, allocates or frees
+ *    device memory or creates a stream, except q4_step_status (which waits for
+ *    the stream to read an error word) and the set-up of a token graph
+ *    (q4_tokens_graph_create / _destroy).
  *  - Return value: a q4_status.  Argument errors are detected on the host before
  *    anything is enqueued (no partial execution).  Q4_ERR_DEVICE reports a HIP
  *    error at launch time; faults during execution surface at the caller's
- *    synchronisation.  q4_last_error() gives a text naming the argument and value
- *    (thread-local, valid until the next call on the same thread).
+ *    synchronisation.  q4_last_error_detail() gives a text naming the argument and
+ *    value (thread-local, valid until the next call on the same thread).
  *  - Outputs are fp16, rounded to nearest even from an fp32 accumulation.  Any
  *    fp32 summation order is a correct result; every variant is deterministic
  *    (the same inputs give bitwise the same outputs, run to run).
@@ -52,16 +55,30 @@ typedef enum q4_status {
   Q4_ERR_ALIGN = 3,       /* a pointer is not aligned as documented             */
   Q4_ERR_WORKSPACE = 4,   /* ws NULL or smaller than the size the call needs    */
   Q4_ERR_DEVICE = 5,      /* a HIP call failed (no device, launch failure, ...) */
-  Q4_ERR_UNSUPPORTED = 6  /* a size beyond what the kernels handle              */
+  Q4_ERR_UNSUPPORTED = 6, /* a size beyond what the kernels handle              */
+  Q4_ERR_TIMEOUT = 7      /* a bounded wait inside a persistent kernel ran out  */
 } q4_status;
+
+/* Errors follow the everything-webgpu AI.md engine API ("Fail Fast": validate
+ * early, throw descriptive errors; an error carries a code, a message and a
+ * detail): every entry point returns a q4_status, and the text naming the
+ * argument, value or wait is kept per thread. */
 
 /* Name of a status code ("Q4_OK", ...).  Never NULL. */
 Q4_API const char* q4_status_str(int status);
 
-/* Detail of the last error on this thread ("" after a successful call). */
+/* Detail of the last error on this thread ("" after a successful call), valid
+ * until the next call on the same thread: the detail of the everything-webgpu
+ * AI.md engine error. */
+Q4_API const char* q4_last_error_detail(void);
+
+/* The same text as q4_last_error_detail (everything-webgpu AI.md engine error
+ * detail; the name this library used first). */
 Q4_API const char* q4_last_error(void);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (the MLC Model Artifact
+ * Manifest page: a compiled library carries its contract's version, and a reader
+ * rejects what it does not know). */
 Q4_API int q4_version(void);
 
 /* ------------------------------------------------------------------ codec -- */
@@ -73,8 +90,9 @@ Q4_API int q4_version(void);
  * K % 32 == 0; words 16-byte aligned; codes any alignment.  Bit-exact. */
 Q4_API int q4_pack(const uint8_t* codes, uint32_t* words, int64_t N, int64_t K, q4_stream_t stream);
 
-/* q4_unpack: the inverse of q4_pack, words [N][K/8] -> codes [N][K] (each 0..15).
- * Same shape and alignment rules. */
+/* q4_unpack: the inverse of q4_pack, words [N][K/8] -> codes [N][K] (each 0..15):
+ * code k of row n is (words[n][k/8] >> 4*(k%8)) & 0xF (Zero TVM documentation,
+ * "Q4F16 quantization format").  Same shape and alignment rules. */
 Q4_API int q4_unpack(const uint32_t* words, uint8_t* codes, int64_t N, int64_t K, q4_stream_t stream);
 
 /* ------------------------------------------------------------------- GEMV -- */
@@ -90,7 +108,8 @@ Q4_API int q4_unpack(const uint32_t* words, uint8_t* codes, int64_t N, int64_t K
 Q4_API int q4_gemv(const uint32_t* words, const uint16_t* scales, const uint16_t* x, uint16_t* y,
             int64_t N, int64_t K, void* ws, size_t ws_bytes, q4_stream_t stream);
 
-/* q4_gemv_splitk: the same product with an explicit number of K slices.
+/* q4_gemv_splitk: the same product (Zero TVM documentation, "Decode loop") with
+ * an explicit number of K slices.
  * splits == 1 is the single-pass kernel (ws unused).  splits > 1 runs a first
  * pass writing fp32 partials part[s][n] over slice s of the K groups (groups are
  * divided as evenly as possible, each slice non-empty) into ws, then a second
@@ -110,10 +129,13 @@ Q4_API int q4_gemv_batched(const uint32_t* words, const uint16_t* scales, const 
                     size_t ws_bytes, q4_stream_t stream);
 
 /* Workspace bytes q4_gemv (M == 1) or q4_gemv_batched (M > 1) needs for this
- * shape on the current device (0 = none).  Returns 0 for an invalid shape. */
+ * shape on the current device (0 = none), computed from the shapes as the MLC
+ * Model Artifact Manifest page computes its sizes.  Returns 0 for an invalid
+ * shape. */
 Q4_API size_t q4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-/* Workspace bytes of q4_gemv_splitk (M == 1) with `splits` slices. */
+/* Workspace bytes of q4_gemv_splitk (M == 1) with `splits` slices: 4 * splits *
+ * M * N, from the shapes (MLC Model Artifact Manifest: sizes from shapes). */
 Q4_API size_t q4_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
 
 /* Size of the device array in which q4_gemv_batched_noalloc keeps its split-K
@@ -175,52 +197,92 @@ typedef struct q4_layer {
  * between them).  Without this flag a descriptor waits only for earlier
  * descriptors whose y overlaps its x or y, or whose x overlaps its y. */
 #define Q4_STEP_ORDERED 0x2u
-/* 0x4 is not used. */
-/* The workspace's counters are already zero: the workspace is fresh from a
- * zeroing allocation or was last used by a q4_decode_step call with the same
- * layer list and M (the persistent register-streaming kernel leaves them zero
- * when it finishes).  Skips the small kernel that clears them before every
- * call.  Passing it for a workspace that holds anything else can let a GEMV read
- * its input before the GEMV producing it has finished (wrong results) or make
- * the kernel's bounded waits run out.  The other paths ignore the flag. */
-#define Q4_STEP_WS_CLEAN 0x8u
+/* (0x4 and 0x8 are not used.) */
 /* Use the persistent kernel even for a list in which more than a quarter of the
  * descriptors wait for another (such lists otherwise run one kernel per
- * descriptor, which is faster for them). */
+ * descriptor, which is faster for them), or for a one-descriptor list at M = 1. */
 #define Q4_STEP_PERSISTENT 0x10u
 
-/* q4_decode_step: run the GEMVs of layers[0 .. n_layers) in list order, as the
- * Zero TVM decode loop walks the projections of every layer and then the LM
- * head ("Decode loop").  The results are those of calling q4_gemv (M == 1) or
- * q4_gemv_batched (M > 1) on each descriptor in turn, after forming its input
- * per x_op; a descriptor's x may lie in an earlier descriptor's y.  Every
- * descriptor is validated before anything is enqueued.  `layers` is host memory,
- * read during the call only.
+/* The decode step over a layer list: the GEMVs of layers[0 .. n_layers) in list
+ * order, as the Zero TVM decode loop walks the projections of every layer and then
+ * the LM head ("Decode loop").  The results are those of calling q4_gemv (M == 1)
+ * or q4_gemv_batched (M > 1) on each descriptor in turn, after forming its input
+ * per x_op; a descriptor's x may lie in an earlier descriptor's y.
  *
- * Without Q4_STEP_LAUNCH_EACH, a list whose rows are at most K = 8192 runs as ONE
- * persistent kernel (M == 1; for 2 <= M <= 8, when every K is a multiple of 128,
- * every scales pointer 8-byte aligned and every x_op Q4_X_PLAIN): the weights of
- * later GEMVs stream while earlier ones finish.  A descriptor waits only for
- * earlier ones it conflicts with (an earlier y overlapping its x or y, an earlier
- * x overlapping its y; with Q4_STEP_ORDERED also its predecessor).  When its
- * only conflict is one earlier descriptor whose y holds all of its x (M == 1),
- * that y is also handed over through the workspace as tagged values the reader
- * polls; other conflicts wait on per-descriptor completion counters in the
- * workspace.  Lists in which more than a quarter of the descriptors wait for
- * another (unless Q4_STEP_PERSISTENT), lists whose conflicts one such wait cannot
- * cover, and all other lists run one kernel per descriptor.  The descriptor table of a persistent
- * list is copied to device memory the first time the list is used (the library
- * allocates that copy and keeps it for later calls with the same list; at most
- * 16 lists are kept, the least recently used is freed with hipFree, which
- * synchronises the device).  Make the first call with a given list outside
- * stream capture.
- * ws: q4_decode_step_workspace_bytes(...) bytes, 16-byte aligned; calls that
- * share a workspace must be ordered on one stream. */
-Q4_API int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t flags,
-                   void* ws, size_t ws_bytes, q4_stream_t stream);
+ * How a list runs: a list whose rows are at most K = 8192 runs as ONE persistent
+ * kernel (M == 1; for 2 <= M <= 8 when every K is a multiple of 128, every scales
+ * pointer 8-byte aligned and every x_op Q4_X_PLAIN): the weights of later GEMVs
+ * stream while earlier ones finish.  A descriptor waits only for earlier ones it
+ * conflicts with (an earlier y overlapping its x or y, an earlier x overlapping
+ * its y; with Q4_STEP_ORDERED also its predecessor).  When its only conflict is
+ * one earlier descriptor whose y holds all of its x (M == 1), that y is also
+ * handed over through the workspace as epoch-tagged values the reader polls;
+ * other conflicts wait on per-descriptor completion counters in the workspace.
+ * Every wait is bounded (about a second); one that runs out sets the workspace's
+ * error word (q4_step_status).  Lists in which more than a quarter of the
+ * descriptors wait for another (unless Q4_STEP_PERSISTENT), lists whose conflicts
+ * one such wait cannot cover, and all other lists run one kernel per descriptor.
+ *
+ * Ownership (everything is the caller's): the plan is caller host memory of
+ * q4_step_plan_bytes(n_layers) bytes, 8-byte aligned; the workspace is caller
+ * device memory of q4_decode_step_workspace_bytes(...) bytes, 16-byte aligned,
+ * holding the control block (error word, hand-over epoch, counters), the tagged
+ * values, the list's device tables and split-K partials.  The library allocates
+ * nothing, frees nothing, keeps no state between calls and creates no stream; the
+ * only call that waits for the device is q4_step_status. */
 
+/* Host bytes of the plan of a list of n_layers descriptors (0 if n_layers < 1). */
+Q4_API size_t q4_step_plan_bytes(int64_t n_layers);
+
+/* Workspace bytes a plan of this list needs on the current device (0 for an
+ * invalid list), from the shapes (MLC Model Artifact Manifest: sizes from
+ * shapes).  flags: Q4_STEP_* bits. */
 Q4_API size_t q4_decode_step_workspace_bytes(const q4_layer* layers, int64_t n_layers, int64_t M,
-                                      uint32_t flags);
+                                             uint32_t flags);
+
+/* q4_step_plan_init: set a list up once (the per-token path is q4_step_run), as
+ * the Zero TVM decode loop prepares its per-token buffers before the loop
+ * ("Decode loop").
+ * Validates every descriptor (argument errors return before anything is
+ * enqueued), works out the dependencies, the partition of the rows over the
+ * workgroups and the launch, and writes them into `plan`; then enqueues on
+ * `stream` the writes of the device tables into ws and the clearing of its
+ * control block -- small kernels only: no allocation, no copy from host memory,
+ * no wait, so the call can be captured in a HIP graph.  `layers` is read during
+ * the call only.  The plan records ws: every run of it must pass the same ws, and
+ * runs that share a workspace must be ordered on one stream.  A plan stays valid
+ * while the descriptors' buffers do. */
+Q4_API int q4_step_plan_init(const q4_layer* layers, int64_t n_layers, int64_t M, uint32_t flags,
+                             void* plan, size_t plan_bytes, void* ws, size_t ws_bytes,
+                             q4_stream_t stream);
+
+/* q4_step_run: one decode step of a planned list (Zero TVM documentation,
+ * "Decode loop": every projection of every layer, then the LM head), enqueued
+ * on `stream`: the
+ * persistent kernel's single launch (or one kernel per descriptor).  Host work is
+ * a check of the plan and the launch: no planning, no allocation, no wait. */
+Q4_API int q4_step_run(const void* plan, void* ws, size_t ws_bytes, q4_stream_t stream);
+
+/* q4_step_status: wait for `stream`, then read the workspace's error word (the
+ * everything-webgpu AI.md engine errors: fail fast with a code and a detail).
+ * Q4_OK if no bounded wait inside a persistent kernel has run out since the last
+ * check; otherwise Q4_ERR_TIMEOUT, with q4_last_error_detail() naming the wait
+ * and the descriptor (the outputs of the step that ran out are not valid), and
+ * the word is cleared.  The workspace's counters are left zero either way (every
+ * workgroup of the kernel finishes: the waits are bounded), so later runs start
+ * clean.  ws: a workspace set up by q4_step_plan_init. */
+Q4_API int q4_step_status(void* ws, q4_stream_t stream);
+
+/* q4_decode_step: plan and run a list in one call (Zero TVM documentation,
+ * "Decode loop"), with no plan kept: each call
+ * redoes q4_step_plan_init's work (the host planning and the writes of the
+ * tables into ws) before the run, so it costs a few small kernels more than
+ * q4_step_run.  ws: q4_decode_step_workspace_bytes(layers, n_layers, M, 0)
+ * bytes.  q4_decode_step_flags takes Q4_STEP_* bits. */
+Q4_API int q4_decode_step(const q4_layer* layers, int64_t n_layers, int64_t M, void* ws,
+                          size_t ws_bytes, q4_stream_t stream);
+Q4_API int q4_decode_step_flags(const q4_layer* layers, int64_t n_layers, int64_t M,
+                                uint32_t flags, void* ws, size_t ws_bytes, q4_stream_t stream);
 
 /* q4_silu_mul: out[m][i] = fp16(silu(gu[m][i]) * gu[m][H + i]) for m < M, i < H,
  * with silu(g) = g / (1 + exp(-g)) in fp32, rounded to nearest even (silu(+inf)
@@ -245,14 +307,17 @@ Q4_API int q4_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t H,
 Q4_API int q4_embed_rows(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
                          const int32_t* tokens, int64_t M, uint16_t* out, q4_stream_t stream);
 
-/* q4_rmsnorm: out[m][k] = fp16(x[m][k] / sqrt(mean_k x[m][k]^2 + eps) * gamma[k]),
+/* q4_rmsnorm (Zero TVM documentation, "Decode loop": the norm before each
+ * block's projections):
+ * out[m][k] = fp16(x[m][k] / sqrt(mean_k x[m][k]^2 + eps) * gamma[k]),
  * the sum of squares in fp32.  x, out: [M][K]; gamma: [K].  out must not overlap
  * x or gamma.  Results are within one fp16 unit in the last place of the
  * exactly computed value. */
 Q4_API int q4_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M, int64_t K,
                       uint16_t* out, q4_stream_t stream);
 
-/* q4_add_rmsnorm: res_out = fp16(res_in + delta) (rounded once), then out =
+/* q4_add_rmsnorm (Zero TVM documentation, "Decode loop": addNorm):
+ * res_out = fp16(res_in + delta) (rounded once), then out =
  * RMSNorm(res_out) * gamma as q4_rmsnorm.  res_out may be res_in itself (in
  * place) but must not otherwise overlap an input; out must not overlap any other
  * argument. */
@@ -260,7 +325,8 @@ Q4_API int q4_add_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const u
                           float eps, int64_t M, int64_t K, uint16_t* res_out, uint16_t* out,
                           q4_stream_t stream);
 
-/* q4_argmax: out[m] = the index of the largest value of x[m][0 .. N) (fp16); ties
+/* q4_argmax (Zero TVM documentation, "Decode loop": greedy sampling of the next
+ * token): out[m] = the index of the largest value of x[m][0 .. N) (fp16); ties
  * go to the lowest index; NaN entries are skipped (a row of NaN gives 0).  out:
  * int32 [M], device memory.  x 2-byte aligned. */
 Q4_API int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_stream_t stream);
@@ -305,7 +371,9 @@ Q4_API int q4_gemv_format(uint32_t format, const uint32_t* words, const void* sc
                           const uint16_t* biases, const void* x, void* y, int64_t N, int64_t K,
                           q4_stream_t stream);
 
-/* Bytes of words, scales and biases of an N x K matrix in a format (0 = q4f16_1);
+/* Bytes of words, scales and biases of an N x K matrix in a format (0 = q4f16_1):
+ * the bytes per 32 weights of the everything-webgpu AI.md quantization table
+ * (q4f16_1 18, q3f16_1 14, q4f32_1 20) and 36 per 64 for the affine formats;
  * 0 for an invalid format or shape. */
 Q4_API size_t q4_format_weight_bytes(uint32_t format, int64_t N, int64_t K);
 
@@ -362,28 +430,53 @@ typedef struct q4_model {
  * (activations, split-K partials, token bookkeeping); 0 if the model is invalid. */
 Q4_API size_t q4_decode_token_workspace_bytes(const q4_model* model);
 
-/* q4_decode_token: one decode step for token_in[0] (DEVICE int32); writes the
+/* q4_decode_token: one decode step (Zero TVM documentation, "Decode loop":
+ * decodeToken) for token_in[0] (DEVICE int32); writes the
  * argmax of the logits to token_out[0] (DEVICE int32) and, if logits is not NULL,
  * the logits (DEVICE fp16 [V]).  One kernel per operation, enqueued on `stream`.
  * ws: q4_decode_token_workspace_bytes(model), 16-byte aligned. */
 Q4_API int q4_decode_token(const q4_model* model, const int32_t* token_in, int32_t* token_out,
                            uint16_t* logits, void* ws, size_t ws_bytes, q4_stream_t stream);
 
-/* Run every step's kernels from the host instead of replaying a graph. */
-#define Q4_TOKENS_EAGER 0x1u
-
 /* q4_decode_tokens: `steps` decode steps back to back with no host
  * synchronisation, each step's argmax the next step's token: tokens is DEVICE
- * int32 [steps + 1]; step i reads tokens[i] and writes tokens[i + 1].  One step's
- * kernels are captured once as a HIP graph (per model, workspace and tokens
- * pointer; the library keeps the last 4, freeing older ones) and the graph is
- * replayed `steps` times on `stream`; with Q4_TOKENS_EAGER the kernels are
- * enqueued for every step instead.  The results are those of `steps` calls of
+ * int32 [steps + 1]; step i reads tokens[i] and writes tokens[i + 1] (the Zero
+ * TVM decode loop's per-token dispatches, and the everything-webgpu page's
+ * multi-step decode: several tokens per host submission).  Every step's kernels
+ * are enqueued on `stream`; the results are those of `steps` calls of
  * q4_decode_token.  ws as for q4_decode_token; calls sharing it must be ordered
- * on one stream.  Make the first call for a given model, workspace and tokens
- * pointer outside stream capture. */
+ * on one stream. */
 Q4_API int q4_decode_tokens(const q4_model* model, int32_t* tokens, int64_t steps, void* ws,
-                            size_t ws_bytes, uint32_t flags, q4_stream_t stream);
+                            size_t ws_bytes, q4_stream_t stream);
+
+/* A decode step captured once as a HIP graph and replayed per token (the same
+ * multi-step decode with one graph launch per token instead of ~200 kernel
+ * launches).  The handle is the caller's: created and destroyed explicitly; the
+ * library keeps no graph of its own. */
+typedef struct q4_tokens_graph q4_tokens_graph;
+
+/* q4_tokens_graph_create: set-up of the everything-webgpu page's multi-step
+ * decode ("Multi-step decoding": several tokens per host submission).  Captures
+ * one step (read tokens[counter], the
+ * step, write tokens[counter + 1]) on `stream` -- a stream the caller created;
+ * the null stream cannot be captured -- and instantiates it.  The graph holds
+ * the model's pointers, `tokens` and `ws`: they must stay valid and unchanged
+ * while the handle lives.  Allocates the handle (host) and, inside the HIP
+ * runtime, the graph; nothing is enqueued. */
+Q4_API int q4_tokens_graph_create(const q4_model* model, int32_t* tokens, void* ws,
+                                  size_t ws_bytes, q4_stream_t stream, q4_tokens_graph** out);
+
+/* q4_tokens_graph_run: `steps` decode steps (everything-webgpu AI.md,
+ * "Multi-step decoding") as q4_decode_tokens computes them:
+ * one kernel resets the step counter, then the graph is launched `steps` times
+ * on `stream`.  No allocation, no wait. */
+Q4_API int q4_tokens_graph_run(q4_tokens_graph* graph, int64_t steps, q4_stream_t stream);
+
+/* q4_tokens_graph_destroy: free the handle and its graph (the everything-webgpu
+ * page's multi-step decode, torn down by its owner).  The library does not
+ * wait: the caller synchronises the streams the graph was launched on first.
+ * NULL is accepted. */
+Q4_API int q4_tokens_graph_destroy(q4_tokens_graph* graph);
 
 /* ------------------------------------------------------ measurement aids -- */
 
@@ -397,7 +490,8 @@ Q4_API int q4_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t 
                   q4_stream_t stream);
 
 /* Plain device copy dst[0 .. bytes) = src[0 .. bytes) with 128-bit loads and
- * stores (the reference kernel for counter calibration).  bytes % 16 == 0,
+ * stores: the reference kernel that calibrates the traffic counters, beside the
+ * everything-webgpu page's streaming-read probe ("Why not llama.cpp/Ollama-class").  bytes % 16 == 0,
  * both 16-byte aligned, no overlap. */
 Q4_API int q4_probe_copy(const void* src, void* dst, size_t bytes, q4_stream_t stream);
 

@@ -32,8 +32,58 @@ def lib():
 def test_header_declares_the_path():
     syms = declared_symbols()
     for name in ["q4_pack", "q4_unpack", "q4_gemv", "q4_gemv_splitk", "q4_gemv_batched",
-                 "q4_decode_step", "q4_workspace_bytes", "q4_status_str", "q4_last_error"]:
+                 "q4_decode_step", "q4_workspace_bytes", "q4_status_str", "q4_last_error_detail",
+                 "q4_step_plan_bytes", "q4_step_plan_init", "q4_step_run", "q4_step_status"]:
         assert name in syms
+
+
+# HIP runtime calls that allocate or free device or pinned memory, create
+# streams, or wait for the whole device: no entry point may make them
+FORBIDDEN = ("hipMalloc", "hipFree", "hipHostMalloc", "hipHostFree", "hipHostRegister",
+             "hipMallocAsync", "hipFreeAsync", "hipMallocManaged", "hipExtMallocWithFlags",
+             "hipDeviceSynchronize", "hipStreamCreate", "hipStreamCreateWithFlags",
+             "hipStreamCreateWithPriority", "hipStreamDestroy", "hipMemset", "hipMemsetAsync",
+             "hipMemcpy", "hipEventSynchronize", "hipDeviceReset")
+
+
+def test_library_links_no_allocation_or_device_wide_wait(lib):
+    """The library imports no HIP routine that allocates, frees, creates a stream
+    or synchronises the device: no call path can (hipStreamSynchronize and
+    hipMemcpyAsync are there for q4_step_status alone, which waits for one
+    stream to read the error word)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", q4.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    imported = {l.split()[-1].split("@")[0] for l in out.splitlines() if l.strip()}
+    hip = {f for f in imported if f.startswith("hip")}
+    assert not (hip & set(FORBIDDEN)), sorted(hip & set(FORBIDDEN))
+    assert hip <= {"hipDeviceGetAttribute", "hipFuncSetAttribute", "hipGetDevice",
+                   "hipGetErrorString", "hipGetLastError", "hipGetSymbolAddress",
+                   "hipGraphDestroy", "hipGraphExecDestroy", "hipGraphInstantiate",
+                   "hipGraphLaunch", "hipLaunchCooperativeKernel", "hipLaunchKernel",
+                   "hipMemcpyAsync", "hipOccupancyMaxActiveBlocksPerMultiprocessor",
+                   "hipStreamBeginCapture", "hipStreamEndCapture", "hipStreamSynchronize"}, hip
+
+
+CITES = ("Zero TVM", "everything-webgpu", "Splash", "Model Artifact Manifest",
+         "MobileTransformers", "callers that cannot")
+
+
+def test_every_export_cites_a_passage_or_its_callers():
+    """The comment above each declaration in the header cites a page (by its
+    title, with the section) or, for the allocation-free entry point, names the
+    callers it is for.  Declarations with no comment of their own share the one
+    above them."""
+    text = open(HEADER).read()
+    decls = [(m.start(), m.end(), m.group(1)) for m in
+             re.finditer(r"Q4_API\s+[\w\s\*]*?\b(q4_\w+)\s*\(", text)]
+    assert len(decls) >= 30
+    prev_end, window = 0, ""
+    for start, end, name in decls:
+        gap = text[prev_end:start]
+        if "/*" in gap:
+            window = " ".join(gap.replace("*", " ").split())
+        assert any(k in window for k in CITES), name
+        prev_end = text.index(";", end)
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -76,7 +126,7 @@ Y = P(0x40000)
 
 
 def _err(lib):
-    return lib.q4_last_error().decode()
+    return lib.q4_last_error_detail().decode()
 
 
 def test_gemv_argument_errors(lib):
@@ -135,25 +185,25 @@ def test_decode_step_validates_every_descriptor_first(lib):
     layers[0] = q4.Layer(0x10000, 0x20000, 0x30000, 0x40000, 16, 64)
     layers[1] = q4.Layer(0x50000, 0x60000, 0x40000, 0x70000, 16, 64)
     layers[2] = q4.Layer(0x80000, 0x90000, 0x70000, 0xA0000, 16, 40)   # bad K
-    assert lib.q4_decode_step(layers, 3, 1, 0, None, 0, None) == 2
+    assert lib.q4_decode_step_flags(layers, 3, 1, 0, None, 0, None) == 2
     assert "layers[2]" in _err(lib)
-    assert lib.q4_decode_step(None, 3, 1, 0, None, 0, None) == 1
-    assert lib.q4_decode_step(layers, 0, 1, 0, None, 0, None) == 2
-    assert lib.q4_decode_step(layers, 2, 9, 0, None, 0, None) == 2
-    assert lib.q4_decode_step(layers, 2, 1, 0x80, None, 0, None) == 2 and "flags" in _err(lib)
+    assert lib.q4_decode_step_flags(None, 3, 1, 0, None, 0, None) == 1
+    assert lib.q4_decode_step_flags(layers, 0, 1, 0, None, 0, None) == 2
+    assert lib.q4_decode_step_flags(layers, 2, 9, 0, None, 0, None) == 2
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0x80, None, 0, None) == 2 and "flags" in _err(lib)
 
 
 def test_decode_step_x_op_errors(lib):
     layers = (q4.Layer * 2)()
     layers[0] = q4.Layer(0x10000, 0x20000, 0x30000, 0x40000, 16, 64, 0, 0)
     layers[1] = q4.Layer(0x50000, 0x60000, 0x40000, 0x70000, 16, 64, 2, 0)   # unknown x_op
-    assert lib.q4_decode_step(layers, 2, 1, 0, None, 0, None) == 2
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2
     assert "layers[1]" in _err(lib) and "x_op" in _err(lib)
     layers[1] = q4.Layer(0x50000, 0x60000, 0x40000, 0x70000, 16, 64, 1, 7)   # reserved != 0
-    assert lib.q4_decode_step(layers, 2, 1, 0, None, 0, None) == 2 and "reserved" in _err(lib)
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2 and "reserved" in _err(lib)
     # with the glue, x spans 2K: a y inside that span overlaps it
     layers[1] = q4.Layer(0x50000, 0x60000, 0x80000, 0x80000 + 2 * 64 + 16, 16, 64, 1, 0)
-    assert lib.q4_decode_step(layers, 2, 1, 0, None, 0, None) == 2 and "overlap" in _err(lib)
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2 and "overlap" in _err(lib)
 
 
 def test_silu_mul_argument_errors(lib):
@@ -225,7 +275,11 @@ def test_token_argument_errors(lib):
     assert lib.q4_decode_token(C.byref(m), X, Y, None, A, 1 << 20, None) == 2
     assert "lm_head" in _err(lib)
     m.lm_head = q4.Weight(0x30000, 0x40000, 10, 64)
-    assert lib.q4_decode_tokens(C.byref(m), None, 4, A, 1 << 20, 0, None) == 1
-    assert lib.q4_decode_tokens(C.byref(m), X, -1, A, 1 << 20, 0, None) == 2
-    assert lib.q4_decode_tokens(C.byref(m), X, 4, A, 1 << 20, 0x10, None) == 2
+    assert lib.q4_decode_tokens(C.byref(m), None, 4, A, 1 << 20, None) == 1
+    assert lib.q4_decode_tokens(C.byref(m), X, -1, A, 1 << 20, None) == 2
+    h = C.c_void_p()
+    assert lib.q4_tokens_graph_create(C.byref(m), X, A, 1 << 20, None, C.byref(h)) == 2
+    assert "null stream" in _err(lib) and not h.value
+    assert lib.q4_tokens_graph_run(None, 4, None) == 1
+    assert lib.q4_tokens_graph_destroy(None) == 0
     assert lib.q4_decode_token_workspace_bytes(None) == 0

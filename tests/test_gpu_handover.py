@@ -154,15 +154,16 @@ def test_repeated_calls_on_one_workspace():
     P = q4.STEP_PERSISTENT
     need = q4.q4_decode_step_workspace_bytes(layers, 1, P)
     ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
-    q4.q4_decode_step(layers, 1, P, ws=ws)
-    torch.cuda.synchronize()
+    plan = q4.StepPlan(layers, 1, P, ws=ws)
+    plan.run()
+    plan.status()
     ref = [host_half(d[3]) for d in descs]
     for m, (W, S, X, Y) in zip(mats, descs):
         check(m, X, Y)
     for _ in range(6):
         for d in descs:
             d[3].fill_(float("nan"))
-        q4.q4_decode_step(layers, 1, P | q4.STEP_WS_CLEAN, ws=ws)
-        torch.cuda.synchronize()
+        plan.run()
+        plan.status()
         for r, d in zip(ref, descs):
             assert np.array_equal(r, host_half(d[3]))

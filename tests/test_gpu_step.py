@@ -107,8 +107,8 @@ def test_independent_lists(mode, shapes):
 def test_range_mode_repeat(shapes):
     """Lists without dependencies (one stretch of row-steps per workgroup, many
     workgroups with none, or hundreds of GEMVs): every row computed once and
-    right, the counters left zero (so STEP_WS_CLEAN calls work), and repeated
-    calls bitwise equal."""
+    right, the counters left zero (so runs of the plan need no clearing), and
+    repeated runs bitwise equal."""
     descs, mats, xs = [], [], []
     for i, (N, K) in enumerate(shapes):
         m, W, S = mat(f"pool/{i}/{N}x{K}", N, K)
@@ -122,70 +122,37 @@ def test_range_mode_repeat(shapes):
     flags = q4.STEP_PERSISTENT
     need = q4.q4_decode_step_workspace_bytes(layers, 1, flags)
     ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")   # garbage
-    q4.q4_decode_step(layers, 1, flags, ws=ws)
-    torch.cuda.synchronize()
+    plan = q4.StepPlan(layers, 1, flags, ws=ws)                         # clears the counters
+    plan.run()
+    plan.status()
     ref = [host_half(d[3]) for d in descs]
     for m, x, y in zip(mats, xs, ref):
         assert_gemv_close(y, m.words(), m.scales(), x)
-    # counters 0..n-1, the exit counter and the spare after it
-    assert not ws[: 4 * (n + 2)].view(torch.int32).cpu().numpy().any()
+    assert counters_zero(ws, n)
     for _ in range(3):
         for d in descs:
             d[3].fill_(float("nan"))
-        q4.q4_decode_step(layers, 1, flags | q4.STEP_WS_CLEAN, ws=ws)
-        torch.cuda.synchronize()
+        plan.run()
+        plan.status()
         for r, d in zip(ref, descs):
             assert np.array_equal(r, host_half(d[3]))
-        assert not ws[: 4 * (n + 2)].view(torch.int32).cpu().numpy().any()
+        assert counters_zero(ws, n)
 
 
-def test_fallback_for_long_rows_and_repeat_determinism():
-    m1, W1, S1 = mat("fb/1", 300, 16384)     # K > 8192: one kernel per descriptor
-    m2, W2, S2 = mat("fb/2", 700, 3072)
-    x1 = synth.activations("fb/x1", 0, 16384)
-    x2 = synth.activations("fb/x2", 0, 3072)
-    y1 = torch.empty(300, dtype=torch.float16, device="cuda")
-    y2 = torch.empty(700, dtype=torch.float16, device="cuda")
-    descs = [(W1, S1, dev_half(x1), y1), (W2, S2, dev_half(x2), y2)]
-    run(descs, 0)
-    assert_gemv_close(host_half(y1), m1.words(), m1.scales(), x1)
-    assert_gemv_close(host_half(y2), m2.words(), m2.scales(), x2)
-    # the persistent kernel on its own, called repeatedly: bitwise the same
-    first = None
-    for _ in range(5):
-        run([descs[1]], q4.STEP_ORDERED)
-        cur = host_half(y2)
-        if first is None:
-            first = cur
-        assert np.array_equal(first, cur)
-
-
-def test_modes_agree_on_the_phi3_layer():
-    shapes = [(9216, 3072), (3072, 3072), (16384, 3072), (3072, 8192)]
-    outs = {}
-    mats = [mat(f"agree/{i}", N, K) for i, (N, K) in enumerate(shapes)]
-    x3 = dev_half(synth.activations("agree/x3", 0, 3072))
-    x8 = dev_half(synth.activations("agree/x8", 0, 8192))
-    for mode, flags in MODES.items():
-        descs = [(W, S, x8 if K == 8192 else x3, torch.empty(N, dtype=torch.float16, device="cuda"))
-                 for (m, W, S), (N, K) in zip(mats, shapes)]
-        run(descs, flags)
-        outs[mode] = [host_half(d[3]) for d in descs]
-    # the persistent kernels use the same lane mapping and arithmetic for these
-    # shapes (32 lanes x 3 groups, 64 x 4): bitwise equal across modes and kernels
-    for m in ("ordered", "auto"):
-        for a, b in zip(outs["hazards"], outs[m]):
-            assert np.array_equal(a, b), m
-    for (m, W, S), y, (N, K) in zip(mats, outs["ordered"], shapes):
-        x = host_half(x8 if K == 8192 else x3)
-        assert_gemv_close(y, m.words(), m.scales(), x)
+def counters_zero(ws, n):
+    """The control block's error word and exit count, and the n completion
+    counters after the block, are zero."""
+    w = ws.view(torch.int32).cpu().numpy()
+    return w[0] == 0 and w[2] == 0 and not w[64:64 + n].any()
 
 
 @pytest.mark.parametrize("flags", [q4.STEP_PERSISTENT, q4.STEP_ORDERED | q4.STEP_PERSISTENT],
                          ids=["hazards", "ordered"])
-def test_workspace_left_clean_and_ws_clean_calls(flags):
-    """The persistent kernel leaves its counters zero, so later calls with the same
-    list may skip clearing them (STEP_WS_CLEAN); results stay bitwise the same."""
+def test_plan_runs_repeat_and_leave_counters_zero(flags):
+    """The persistent kernel leaves its counters zero and advances the hand-over
+    epoch once per launch, so a plan runs again and again on one workspace with
+    nothing cleared in between; results stay bitwise the same, and equal those of
+    the one-call entry point."""
     dims = [3072, 8192, 3072, 6144, 2048, 512, 1024, 256, 3072]
     x = dev_half(synth.activations("wsclean/x", 0, dims[0]))
     descs = []
@@ -198,25 +165,19 @@ def test_workspace_left_clean_and_ws_clean_calls(flags):
     n = len(descs)
     need = q4.q4_decode_step_workspace_bytes(layers, 1, flags)
     ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")   # garbage
-    q4.q4_decode_step(layers, 1, flags, ws=ws)                         # clears, runs
-    torch.cuda.synchronize()
+    q4.q4_decode_step(layers, 1, flags, ws=ws)                          # plans, clears, runs
     ref = [host_half(d[3]) for d in descs]
-    counters = ws[: 4 * (n + 1)].view(torch.int32).cpu().numpy()
-    assert not counters.any()
-    for _ in range(4):
+    assert counters_zero(ws, n)
+    plan = q4.StepPlan(layers, 1, flags, ws=ws)
+    for r in range(5):
         for d in descs:
             d[3].fill_(float("nan"))
-        q4.q4_decode_step(layers, 1, flags | q4.STEP_WS_CLEAN, ws=ws)
-        torch.cuda.synchronize()
-        for r, d in zip(ref, descs):
-            assert np.array_equal(r, host_half(d[3]))
-        assert not ws[: 4 * (n + 1)].view(torch.int32).cpu().numpy().any()
-    # a zero-filled new workspace is clean too
-    ws2 = torch.zeros_like(ws)
-    q4.q4_decode_step(layers, 1, flags | q4.STEP_WS_CLEAN, ws=ws2)
-    torch.cuda.synchronize()
-    for r, d in zip(ref, descs):
-        assert np.array_equal(r, host_half(d[3]))
+        plan.run()
+        plan.status()
+        for a, d in zip(ref, descs):
+            assert np.array_equal(a, host_half(d[3]))
+        assert counters_zero(ws, n)
+        assert int(ws.view(torch.int32)[1]) == r + 1        # the epoch of launch r + 1
 
 
 def _m_chain(prefix, M, dims):
@@ -316,17 +277,39 @@ def test_small_m_workspace_left_clean():
     layers = q4.make_layers(descs)
     need = q4.q4_decode_step_workspace_bytes(layers, M, q4.STEP_PERSISTENT)
     ws = torch.full((need,), 0x33, dtype=torch.uint8, device="cuda")
-    q4.q4_decode_step(layers, M, q4.STEP_PERSISTENT, ws=ws)
-    torch.cuda.synchronize()
+    plan = q4.StepPlan(layers, M, q4.STEP_PERSISTENT, ws=ws)
+    plan.run()
+    plan.status()
     ref = [host_half(d[3]) for d in descs]
     n = len(descs)
-    assert not ws[: 4 * (n + 1)].view(torch.int32).cpu().numpy().any()
+    assert counters_zero(ws, n)
     for _ in range(3):
         for d in descs:
             d[3].fill_(float("nan"))
-        q4.q4_decode_step(layers, M, q4.STEP_PERSISTENT | q4.STEP_WS_CLEAN, ws=ws)
-        torch.cuda.synchronize()
+        plan.run()
+        plan.status()
         for r, d in zip(ref, descs):
             assert np.array_equal(r, host_half(d[3]))
+        assert counters_zero(ws, n)
     for m, (W, S, X, Y) in zip(mats, descs):
         assert_gemv_close(host_half(Y), m.words(), m.scales(), host_half(X))
+
+
+def test_error_word_is_reported_and_cleared():
+    """A nonzero error word in the workspace (as a kernel writes it when a bounded
+    wait runs out: code | (GEMV + 1) << 8) makes q4_step_status fail with
+    Q4_ERR_TIMEOUT naming the wait and the descriptor, and clears the word."""
+    m, W, S = mat("errword/0", 256, 512)
+    x = dev_half(synth.activations("errword/x", 0, 512))
+    descs = [(W, S, x, torch.empty(256, dtype=torch.float16, device="cuda")),
+             (W, S, x, torch.empty(256, dtype=torch.float16, device="cuda"))]
+    plan = q4.StepPlan(q4.make_layers(descs), 1, q4.STEP_PERSISTENT)
+    plan.run()
+    plan.status()                                  # a clean run: no error
+    plan.ws.view(torch.int32)[0] = 2 | (2 << 8)    # counter wait, layers[1]
+    with pytest.raises(q4.Q4Error) as e:
+        plan.status()
+    assert e.value.code == 7 and "layers[1]" in e.value.detail
+    assert "completion counter" in e.value.detail
+    assert int(plan.ws.view(torch.int32)[0]) == 0
+    plan.status()                                  # cleared

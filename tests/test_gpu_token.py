@@ -146,9 +146,9 @@ def wide():
 
 
 @pytest.mark.parametrize("model", ["small", "wide"])
-@pytest.mark.parametrize("flags", [0, q4.TOKENS_EAGER], ids=["graph", "eager"])
+@pytest.mark.parametrize("graph", [True, False], ids=["graph", "eager"])
 @pytest.mark.parametrize("folded", [False, True], ids=["norms", "folded"])
-def test_multi_step_equals_single_steps(request, model, flags, folded):
+def test_multi_step_equals_single_steps(request, model, graph, folded):
     W = request.getfixturevalue(model)
     Wm = W.fmodel if folded else W.model
     steps = 6
@@ -164,15 +164,25 @@ def test_multi_step_equals_single_steps(request, model, flags, folded):
     # the same steps in one call, twice (a graph is replayed again), with eager
     # work and synchronisation in between
     tokens = torch.full((steps + 1,), -1, dtype=torch.int32, device="cuda")
-    for rep in range(3):
-        tokens.fill_(-1)
-        tokens[0] = seq[0]
-        q4.q4_decode_tokens(Wm, tokens, steps, ws=ws, flags=flags)
-        torch.cuda.synchronize()
-        assert tokens.cpu().tolist() == seq, rep
-        junk = torch.randn(1 << 16, device="cuda").sum()        # eager work between replays
-        torch.cuda.synchronize()
-        del junk
+    stream = torch.cuda.Stream()
+    g = q4.TokensGraph(Wm, tokens, ws=ws, stream=stream) if graph else None
+    try:
+        for rep in range(3):
+            tokens.fill_(-1)
+            tokens[0] = seq[0]
+            torch.cuda.synchronize()
+            if graph:
+                g.run(steps, stream=stream)
+            else:
+                q4.q4_decode_tokens(Wm, tokens, steps, ws=ws, stream=stream)
+            torch.cuda.synchronize()
+            assert tokens.cpu().tolist() == seq, rep
+            junk = torch.randn(1 << 16, device="cuda").sum()    # eager work between replays
+            torch.cuda.synchronize()
+            del junk
+    finally:
+        if g is not None:
+            g.close()
     # and the sequence is a chain of argmaxes: recompute the last step by composition
     if not folded:
         lg, t = composed_step(W, seq[-2], check=False)
