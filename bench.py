@@ -675,7 +675,7 @@ def summarize_profiles(d, kernel=KERNEL):
     step_bytes = sum(synth.algorithmic_bytes(P["M"], N, K) for _, N, K in shapes)
     stats = {}
     for r in _csv_rows(os.path.join(d, "stats"), "kernel_stats.csv"):
-        for k in (KERNEL_, "k_zero", "k_zero_m"):
+        for k in (KERNEL_, "k_zero", "k_put"):
             if _is_kernel(r["Name"], k):
                 stats[k] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
                             "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
