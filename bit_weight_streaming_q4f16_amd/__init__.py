@@ -120,6 +120,7 @@ def load():
             "q4_rmsnorm": ([p, p, C.c_float, i64, i64, p, p], i32),
             "q4_add_rmsnorm": ([p, p, p, C.c_float, i64, i64, p, p, p], i32),
             "q4_argmax": ([p, i64, i64, p, p], i32),
+            "q4_gemv_norm": ([p, p, p, p, p, C.c_float, p, p, i64, i64, C.c_uint32, p], i32),
             "q4_gemv_format": ([C.c_uint32, p, p, p, p, p, i64, i64, p], i32),
             "q4_format_weight_bytes": ([C.c_uint32, i64, i64], sz),
             "q4_decode_token_workspace_bytes": ([p], sz),
@@ -413,6 +414,22 @@ def q4_add_rmsnorm(delta, res_in, gamma, eps: float, res_out=None, out=None, str
     _check(load().q4_add_rmsnorm(_ptr(delta), _ptr(res_in), _ptr(gamma), float(eps), M, K,
                                  _ptr(res_out), _ptr(out), _stream(stream)))
     return res_out, out
+
+
+def q4_gemv_norm(words, scales, res_in, gamma, eps: float, delta=None, res_out=None, y=None,
+                 glu: bool = False, stream=None):
+    """y = W . RMSNorm(fp16(res_in + delta)) * gamma with the norm's scalar applied
+    after the product (q4_gemv_norm); glu: W holds gate | up rows and
+    y = fp16(silu(gate) * up)."""
+    torch = _torch()
+    rows, K = words.shape[0], 8 * words.shape[1]
+    N = rows // 2 if glu else rows
+    if y is None:
+        y = torch.empty(N, dtype=torch.float16, device=words.device)
+    _check(load().q4_gemv_norm(_ptr(words), _ptr(scales), _ptr(res_in), _ptr(delta), _ptr(gamma),
+                               float(eps), _ptr(res_out), _ptr(y), N, K, 1 if glu else 0,
+                               _stream(stream)))
+    return y
 
 
 def q4_argmax(x, out=None, stream=None):

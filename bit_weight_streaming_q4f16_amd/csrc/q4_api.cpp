@@ -17,6 +17,9 @@
 
 #include "q4_step_mfma.h"
 #include "q4_formats.h"
+#include "q4_fused.h"
+#include <initializer_list>
+#include <utility>
 
 namespace {
 
@@ -332,6 +335,46 @@ int q4_add_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const uint16_t
   hipError_t e = q4::launch_rmsnorm(delta, res_in, gamma, eps, M, K, res_out, out,
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : device_error(e, "q4_add_rmsnorm");
+}
+
+int q4_gemv_norm(const uint32_t* words, const uint16_t* scales, const uint16_t* res_in,
+                 const uint16_t* delta, const uint16_t* gamma, float eps, uint16_t* res_out,
+                 uint16_t* y, int64_t N, int64_t K, uint32_t glu, q4_stream_t stream) {
+  const char* what = "q4_gemv_norm";
+  if (!words || !scales || !res_in || !gamma || !y)
+    return fail(Q4_ERR_NULL, "%s: NULL pointer (only delta and res_out may be NULL)", what);
+  if (glu > 1) return fail(Q4_ERR_SHAPE, "%s: glu = %u: must be 0 or 1", what, glu);
+  if (int rc = check_shape(glu ? 2 * N : N, K)) return fail(rc, "%s: %s", what, g_error.c_str());
+  if (!(eps >= 0.f)) return fail(Q4_ERR_SHAPE, "%s: eps must be >= 0", what);
+  if (!aligned(words, 16) || !aligned(scales, 2) || !aligned(res_in, 16) || !aligned(gamma, 16) ||
+      (delta && !aligned(delta, 16)) || (res_out && !aligned(res_out, 16)) || !aligned(y, 2))
+    return fail(Q4_ERR_ALIGN, "%s: misaligned pointer", what);
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return fail(Q4_ERR_DEVICE, "%s: no HIP device", what);
+  if ((size_t)(K / 32) * 64 > d->lds_per_block)
+    return fail(Q4_ERR_UNSUPPORTED, "%s: K = %lld: the input does not fit in LDS", what,
+                (long long)K);
+  const int64_t rows = glu ? 2 * N : N, vb = 2 * K;
+  const int64_t wb = rows * K / 2, sb = rows * K / 16, yb = 2 * N;
+  auto any = [&](const void* p, int64_t pb, std::initializer_list<std::pair<const void*, int64_t>> l) {
+    for (auto& q : l)
+      if (q.first && spans_overlap(p, pb, q.first, q.second)) return true;
+    return false;
+  };
+  if (any(y, yb, {{words, wb}, {scales, sb}, {res_in, vb}, {delta, vb}, {gamma, vb}, {res_out, vb}}))
+    return fail(Q4_ERR_SHAPE, "%s: y overlaps another argument", what);
+  if (res_out && any(res_out, vb, {{words, wb}, {scales, sb}, {res_in, vb}, {delta, vb}, {gamma, vb}}))
+    return fail(Q4_ERR_SHAPE, "%s: res_out overlaps an input (it must be a buffer of its own)",
+                what);
+  q4::NormIn nin;
+  nin.delta = delta;
+  nin.res_in = res_in;
+  nin.gamma = gamma;
+  nin.res_out = res_out;
+  nin.eps = eps;
+  hipError_t e = q4::launch_gemv_norm_in(*d, words, scales, nin, y, N, K, glu != 0,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : device_error(e, what);
 }
 
 int q4_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, q4_stream_t stream) {

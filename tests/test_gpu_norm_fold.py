@@ -1,0 +1,121 @@
+"""The folded residual add + RMSNorm + GEMV (q4_gemv_norm, the GEMV of the
+factored-norm decode step) against the oracle's unfolded composition, element by
+element: fp16(res_in + delta) exactly as the oracle rounds it, and every output
+within a bound derived from what differs -- the input rounded to fp16 before the
+norm's scaling instead of after it (one fp16 rounding of each input term on each
+side), the fp32 GEMV, the fp32 norm scalar, and the output rounding."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+import bit_weight_streaming_q4f16_amd as q4
+from gpuhelp import dev_half, dev_words, error_bound, half_f64, host_half, ulp16
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q4.load()
+
+
+def weights_f64(words, scales):
+    codes = oracle.unpack(words).astype(np.float64)
+    return (codes - 7) * np.repeat(half_f64(scales), 32, axis=1)
+
+
+def case(label, rows, K, with_delta):
+    m = synth.Matrix(label, rows, K)
+    w, s = m.words(), m.scales()
+    res = synth.activations(label + "/res", 0, K)
+    delta = synth.to_half_bits(0.5 * synth.normal(label + "/d", 0, 0, K)) if with_delta else None
+    gamma = synth.to_half_bits(1.0 + 0.1 * synth.normal(label + "/g", 0, 0, K))
+    return w, s, res, delta, gamma
+
+
+def folded_bound(w, s, h_bits, gamma_bits, eps, y_ref):
+    """Per-output bound on |y_folded (fp32, before its rounding) - y_unfolded|."""
+    K = h_bits.size
+    h, g = half_f64(h_bits), half_f64(gamma_bits)
+    r = 1.0 / np.sqrt(np.mean(h * h) + eps)
+    a = h * g                                           # exact in fp64
+    v_bits = synth.to_half_bits(a)                      # the folded GEMV's input
+    W = np.abs(weights_f64(w, s))
+    # the two fp16 roundings of each input term: fp16(a) * r against fp16(r a)
+    t_in = W @ (2.0 ** -10 * r * np.abs(a) + 2.0 ** -25 * (1.0 + r))
+    # the folded GEMV's fp32 error on its own input, times r
+    t_gemv = r * error_bound(s, v_bits, "exact")[0]
+    # the fp32 norm scalar: sum of K squares, the mean, the root, the reciprocal, the product
+    t_r = (K + 8) * U * r * (W @ np.abs(half_f64(v_bits)))
+    return t_in + t_gemv + t_r
+
+
+@pytest.mark.parametrize("rows,K,with_delta", [(3000, 3072, True), (257, 544, False),
+                                               (64, 8192, True), (9216, 3072, True)])
+def test_plain_matches_unfolded_oracle(rows, K, with_delta):
+    w, s, res, delta, gamma = case(f"fold/{rows}x{K}", rows, K, with_delta)
+    eps = 1e-5
+    res_out = torch.empty(K, dtype=torch.float16, device="cuda")
+    y = q4.q4_gemv_norm(dev_words(w), dev_half(s), dev_half(res), dev_half(gamma), eps,
+                        delta=dev_half(delta) if delta is not None else None, res_out=res_out)
+    torch.cuda.synchronize()
+    if delta is not None:
+        h_ref, xn = oracle.add_rmsnorm(delta, res, gamma, eps)
+    else:
+        h_ref, xn = res.copy(), oracle.rmsnorm(res, gamma, eps)
+    assert np.array_equal(host_half(res_out), h_ref)          # h rounded once, as the oracle
+    y_ref = oracle.gemv_f64(w, s, xn)                         # the unfolded step
+    B = folded_bound(w, s, h_ref, gamma, np.float32(eps), y_ref)
+    got = half_f64(host_half(y))
+    lim = B + 0.5 * ulp16(np.abs(y_ref) + B)
+    err = np.abs(got - y_ref)
+    assert np.all(err <= lim), (float((err / lim).max()), int(np.argmax(err / lim)))
+    # the bound is a real constraint: inside the GEMV tolerance (it is a worst case,
+    # linear in the terms' magnitudes; the errors measured are far below it)
+    tol = 2e-3 * oracle.vec_norm(xn) * oracle.row_norms(w, s).max()
+    assert lim.max() < tol
+    print(f"folded {rows}x{K}: worst error / bound {float((err / lim).max()):.3f}, "
+          f"bound / tolerance {float(lim.max() / tol):.3f}")
+
+
+@pytest.mark.parametrize("F,K", [(2048, 3072), (100, 1024)])
+def test_glu_matches_unfolded_oracle(F, K):
+    """gate/up rows folded with the glue: y = fp16(silu(fp16(gate)) * fp16(up))."""
+    w, s, res, delta, gamma = case(f"foldglu/{F}x{K}", 2 * F, K, True)
+    eps = 1e-5
+    y = q4.q4_gemv_norm(dev_words(w), dev_half(s), dev_half(res), dev_half(gamma), eps,
+                        delta=dev_half(delta), glu=True)
+    torch.cuda.synchronize()
+    h_ref, xn = oracle.add_rmsnorm(delta, res, gamma, eps)
+    gu_ref = oracle.gemv_f64(w, s, xn)
+    B = folded_bound(w, s, h_ref, gamma, np.float32(eps), gu_ref)
+    # gate and up are rounded to fp16 before the glue: each within B + half an ulp
+    e = B + 0.5 * ulp16(np.abs(gu_ref) + B)
+    g, u = gu_ref[:F], gu_ref[F:]
+    eg, eu = e[:F], e[F:]
+    sg = g / (1.0 + np.exp(-g))
+    want = sg * u
+    # |d silu / dg| <= 1.0999; the glue in fp32 (a few roundings) and its fp16 output
+    lim = (1.1 * np.abs(u) * eg + (np.abs(sg) + 1.1 * eg) * eu + 8 * U * np.abs(want))
+    lim = lim + 0.5 * ulp16(np.abs(want) + lim)
+    got = half_f64(host_half(y))
+    err = np.abs(got - want)
+    assert np.all(err <= lim), (float((err / lim).max()), int(np.argmax(err / lim)))
+
+
+def test_argument_errors():
+    x = torch.zeros(64, dtype=torch.float16, device="cuda")
+    w = torch.zeros(4, 8, dtype=torch.int32, device="cuda")
+    s = torch.zeros(4, 2, dtype=torch.float16, device="cuda")
+    with pytest.raises(q4.Q4Error):        # res_out aliasing res_in
+        q4.q4_gemv_norm(w, s, x, x, 1e-5, res_out=x)
+    with pytest.raises(q4.Q4Error):        # a negative epsilon
+        q4.q4_gemv_norm(w, s, x, x, -1.0)
+    with pytest.raises(q4.Q4Error):        # y overlapping res_in
+        q4.q4_gemv_norm(w, s, x, x, 1e-5, y=x[:4])
