@@ -1,0 +1,108 @@
+// Device-side helpers shared by the GEMV kernels: vector types, bit casts, the
+// x pair order of the nibble decode, DPP / lane-swap team sums, the lane
+// transpose of the MFMA B layout, LDS waits and the buffer cache-policy bits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_g __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8_s __attribute__((ext_vector_type(8)));
+
+// Pointers read from a descriptor table are generic; casting them to the global
+// address space makes the compiler emit global_* (not flat_*) memory
+// instructions, which count only in vmcnt (flat ones also count in lgkmcnt, so
+// every LDS wait would also wait for the weight stream).
+#define Q4_GLOBAL __attribute__((address_space(1)))
+
+// Buffer-instruction cache policy bits and the raw-buffer resource flags.
+constexpr int kCoherent = 1 | 16;        // sc0 | sc1: device-coherent access
+constexpr int kNonTemporal = 2;          // nt: streamed once
+constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
+constexpr int kWaitVm0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt untouched)
+
+template <typename T, typename F>
+__device__ __forceinline__ T bits(F v) {
+  return __builtin_bit_cast(T, v);
+}
+
+__device__ __forceinline__ float half_to_float(uint16_t h) { return (float)bits<_Float16>(h); }
+
+__device__ __forceinline__ uint16_t float_to_half_rne(float v) {
+  return bits<uint16_t>((_Float16)v);
+}
+
+// A block of 8 consecutive x values (one word's worth) reordered into the pairs
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7) in which a word's nibble pairs are decoded.
+__device__ __forceinline__ uint4 pair_order(uint4 v) {
+  uint4 o;
+  o.x = (v.x & 0xFFFFu) | (v.z << 16);
+  o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+  o.z = (v.y & 0xFFFFu) | (v.w << 16);
+  o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+  return o;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return bits<float>(__builtin_amdgcn_update_dpp(0, bits<int>(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned teams of 2^lg lanes (lg in [2, 6], uniform over the wave);
+// every lane of a team gets the total.  No LDS, no barrier.
+__device__ __forceinline__ float team_sum_lg(float v, int lg) {
+  v += dpp<0xB1>(v);                   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp<0x4E>(v);                   // quad_perm [2,3,0,1]: lane ^ 2
+  if (lg >= 3) v += dpp<0x141>(v);     // row_half_mirror: the other quad
+  if (lg >= 4) v += dpp<0x140>(v);     // row_mirror: the other half-row
+  if (lg >= 5) {                       // rows 0<->1 and 2<->3
+    const auto r = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(v), bits<uint32_t>(v),
+                                                    false, false);
+    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
+  }
+  if (lg >= 6) {                       // lanes 0-31 <-> 32-63
+    const auto r = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(v), bits<uint32_t>(v),
+                                                    false, false);
+    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
+  }
+  return v;
+}
+
+// The same for a team size known at compile time.
+template <int LPR>
+__device__ __forceinline__ float team_sum(float v) {
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "team size");
+  return team_sum_lg(v, LPR == 4 ? 2 : LPR == 8 ? 3 : LPR == 16 ? 4 : LPR == 32 ? 5 : 6);
+}
+
+// A 4 x 4 block spread over lanes r, r+16, r+32, r+48: rows {0,1} <-> {2,3}, then
+// rows 0 <-> 1 and 2 <-> 3; afterwards lane row R register t holds what lane row t
+// register R held.
+__device__ __forceinline__ void transpose4(uint32_t (&v)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  v[0] = a[0]; v[2] = a[1]; v[1] = b[0]; v[3] = b[1];
+  auto c = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
+  v[0] = c[0]; v[1] = c[1]; v[2] = d[0]; v[3] = d[1];
+}
+
+// s_waitcnt lgkmcnt(0) only: this wave's LDS operations are complete; its
+// outstanding vector-memory loads are not waited for.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ int lds_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void lds_store(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+}  // namespace q4

@@ -10,38 +10,10 @@
 //     (q - 7) * s summed = s * (sum q x - 7 sum x).
 // The MLX affine format runs on the q4f16_1 GEMV itself (q4_gemv.hip).
 #include "q4_formats.h"
+#include "q4_device.h"
 
 namespace q4 {
 namespace {
-
-template <typename T, typename F>
-__device__ __forceinline__ T bits(F v) {
-  return __builtin_bit_cast(T, v);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return bits<float>(__builtin_amdgcn_update_dpp(0, bits<int>(v), CTRL, 0xF, 0xF, true));
-}
-
-template <int LPR>
-__device__ __forceinline__ float team_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  if constexpr (LPR >= 8) v += dpp<0x141>(v);
-  if constexpr (LPR >= 16) v += dpp<0x140>(v);
-  if constexpr (LPR >= 32) {
-    const auto r = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(v), bits<uint32_t>(v),
-                                                    false, false);
-    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
-  }
-  if constexpr (LPR >= 64) {
-    const auto r = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(v), bits<uint32_t>(v),
-                                                    false, false);
-    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
-  }
-  return v;
-}
 
 enum : int { kQ3 = 1, kQ4F32 = 2 };
 
@@ -153,10 +125,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict_
 // cover the 32 codes as the pairs (i, i+4), (i+1, i+5).
 constexpr uint32_t kQ3MaskA = 0x00070070u, kQ3MaskB = 0x00380380u;
 constexpr uint32_t kQ3ExpA = 0x64005400u, kQ3ExpB = 0x58004800u;
-constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
-constexpr int kNonTemporal = 2;
 
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 // Sum over one group of (2^E + q) * x.  xq: x of the group as four chunks of
 // four pairs, chunk c at xq[c * cstride] holding the pairs (x[8c+p], x[8c+p+4]).

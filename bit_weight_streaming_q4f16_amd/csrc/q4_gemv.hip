@@ -25,37 +25,10 @@
 //    32-weight group, so the per-group scale is applied exactly to its result.
 #include "q4_formats.h"
 #include "q4_fused.h"
+#include "q4_device.h"
 
 namespace q4 {
 namespace {
-
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-
-template <typename T, typename F>
-__device__ __forceinline__ T bits(F v) {
-  return __builtin_bit_cast(T, v);
-}
-
-__device__ __forceinline__ float half_to_float(uint16_t h) {
-  return (float)bits<_Float16>(h);
-}
-
-__device__ __forceinline__ uint16_t float_to_half_rne(float v) {
-  return bits<uint16_t>((_Float16)v);
-}
-
-// A block of 8 consecutive x values (one word's worth) reordered into the pairs
-// (x0,x4) (x1,x5) (x2,x6) (x3,x7) that dequant_word produces.
-__device__ __forceinline__ uint4 pair_order(uint4 v) {
-  uint4 o;
-  o.x = (v.x & 0xFFFFu) | (v.z << 16);
-  o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
-  o.z = (v.y & 0xFFFFu) | (v.w << 16);
-  o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-  return o;
-}
 
 // One word -> four fp16 pairs (q0-7, q4-7) (q1-7, q5-7) (q2-7, q6-7) (q3-7, q7-7),
 // all exact.
@@ -85,32 +58,6 @@ __device__ __forceinline__ float group_dot(uint4 w, const uint4* xs, int gc, int
     b = __builtin_amdgcn_fdot2(q[3], bits<h2_t>(xv.w), b, false);
   }
   return a + b;
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return bits<float>(__builtin_amdgcn_update_dpp(0, bits<int>(v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over aligned teams of LPR lanes; every lane of a team gets the total.
-template <int LPR>
-__device__ __forceinline__ float team_sum(float v) {
-  static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "team size");
-  v += dpp<0xB1>(v);                         // quad_perm [1,0,3,2]: lane ^ 1
-  v += dpp<0x4E>(v);                         // quad_perm [2,3,0,1]: lane ^ 2
-  if constexpr (LPR >= 8) v += dpp<0x141>(v);  // row_half_mirror: the other quad
-  if constexpr (LPR >= 16) v += dpp<0x140>(v); // row_mirror: the other half-row
-  if constexpr (LPR >= 32) {                   // rows 0<->1 and 2<->3
-    const auto r = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(v), bits<uint32_t>(v),
-                                                    false, false);
-    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
-  }
-  if constexpr (LPR >= 64) {                   // lanes 0-31 <-> 32-63
-    const auto r = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(v), bits<uint32_t>(v),
-                                                    false, false);
-    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
-  }
-  return v;
 }
 
 // K slice s of G groups split `splits` ways: [G*s/splits, G*(s+1)/splits).
@@ -286,17 +233,6 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
 // (c, r), which is the B-operand layout of v_mfma_f32_16x16x32_f16 (column = row
 // n, k block = c).  A = X rows (row m = r < M, zero above M), from LDS in the same
 // pair order.  One MFMA per group into a fresh accumulator, then acc += s * D.
-__device__ __forceinline__ void transpose4(uint32_t (&v)[4]) {
-  // rows {0,1} <-> {2,3} for registers (0,2) and (1,3); then rows 0<->1, 2<->3
-  // for (0,1) and (2,3): afterwards row R register t = original row t register R.
-  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
-  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
-  v[0] = a[0]; v[2] = a[1]; v[1] = b[0]; v[3] = b[1];
-  auto c = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
-  auto d = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
-  v[0] = c[0]; v[1] = c[1]; v[2] = d[0]; v[3] = d[1];
-}
-
 __global__ __launch_bounds__(kBlock) void k_gemv_mfma(const uint4* __restrict__ W,
                                                       const uint16_t* __restrict__ S,
                                                       const uint4* __restrict__ X,

@@ -4,11 +4,10 @@
 // the down projection's input).  Eight outputs per thread: one 16-byte load of
 // gate, one of up, one 16-byte store.
 #include "q4_internal.h"
+#include "q4_device.h"
 
 namespace q4 {
 namespace {
-
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 
 __global__ __launch_bounds__(kBlock) void k_silu_mul(const uint4* __restrict__ gu,
                                                      uint4* __restrict__ out,

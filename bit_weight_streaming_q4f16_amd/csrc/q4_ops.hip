@@ -4,16 +4,10 @@
 // Each is one small kernel, one workgroup per row; they move a few KB each, so
 // what they cost is their launch and one memory round trip.
 #include "q4_internal.h"
+#include "q4_device.h"
 
 namespace q4 {
 namespace {
-
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-
-template <typename T, typename F>
-__device__ __forceinline__ T bits(F v) {
-  return __builtin_bit_cast(T, v);
-}
 
 // Sum over the 256 threads of a workgroup (every thread gets the total).
 __device__ __forceinline__ float block_sum(float v, float* red) {

@@ -36,22 +36,11 @@
 #include <cstring>
 
 #include "q4_step.h"
+#include "q4_device.h"
 
 namespace q4 {
 namespace {
 
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-
-template <typename T, typename F>
-__device__ __forceinline__ T bits(F v) {
-  return __builtin_bit_cast(T, v);
-}
-
-// Pointers read from the descriptor table are generic; casting them to the
-// global address space makes the compiler emit global_* (not flat_*) memory
-// instructions, which count only in vmcnt (flat ones also count in lgkmcnt,
-// which would make every LDS wait also wait for the weight stream).
-#define Q4_GLOBAL __attribute__((address_space(1)))
 template <typename T>
 __device__ __forceinline__ const Q4_GLOBAL T* gptr(const T* p) {
   return (const Q4_GLOBAL T*)p;
@@ -60,9 +49,6 @@ template <typename T>
 __device__ __forceinline__ Q4_GLOBAL T* gptr_mut(T* p) {
   return (Q4_GLOBAL T*)p;
 }
-typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_g __attribute__((ext_vector_type(2)));
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 
 // The fields of a descriptor a compute wave needs, read with scalar loads issued
 // as inline assembly.  Read as ordinary loads, they become vector loads (the
@@ -74,7 +60,6 @@ struct CursorDesc {
   const Q4_GLOBAL uint16_t* S;
   int N, G, lg, C, steps, flags, sbase, srem;
 };
-typedef uint32_t u32x8_s __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
   u32x4_g ws;
   u32x8_s rest;        // N, G, lpr_log2 | C << 16, steps, dep, flags, sbase, srem
@@ -102,15 +87,6 @@ __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
   r.sbase = (int)rest[6];
   r.srem = (int)rest[7];
   return r;
-}
-
-__device__ __forceinline__ uint4 pair_order(uint4 v) {
-  uint4 o;
-  o.x = (v.x & 0xFFFFu) | (v.z << 16);
-  o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
-  o.z = (v.y & 0xFFFFu) | (v.w << 16);
-  o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-  return o;
 }
 
 // The nibble-pair masks.  AND-ing a word with 0x000F000F leaves nibbles 0 and 4
@@ -165,47 +141,12 @@ __device__ __forceinline__ float group_dot(uint4 w, const uint4 (&x)[4], const N
 // 2^20: the factor between group_dot's units and the products' (exact in fp32).
 constexpr float kDotUnit = 1048576.f;
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return bits<float>(__builtin_amdgcn_update_dpp(0, bits<int>(v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over aligned teams of 2^lg lanes (lg in [2, 6], uniform).
-__device__ __forceinline__ float team_sum(float v, int lg) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  if (lg >= 3) v += dpp<0x141>(v);
-  if (lg >= 4) v += dpp<0x140>(v);
-  if (lg >= 5) {
-    const auto r = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(v), bits<uint32_t>(v),
-                                                    false, false);
-    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
-  }
-  if (lg >= 6) {
-    const auto r = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(v), bits<uint32_t>(v),
-                                                    false, false);
-    v = bits<float>((uint32_t)r[0]) + bits<float>((uint32_t)r[1]);
-  }
-  return v;
-}
-
-// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt left at their maxima): LDS ops of
-// this wave are complete, outstanding vector-memory loads are not waited for.
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-__device__ __forceinline__ int lds_load(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
 constexpr int kWaves = kStepThreads / 64;   // 16
 constexpr int kSync = 4;                    // sync waves (stage x, copy out y)
 constexpr int kCompute = kWaves - kSync;    // compute waves
 static_assert(kXBufs % kSync == 0, "a GEMV and the one whose x buffer it reuses share an owner");
 constexpr unsigned kSpinLimit = 1u << 24;   // bounded waits (about a second)
 constexpr unsigned kTagSpinLimit = 1u << 18; // polls of tagged pairs (a memory round trip each)
-constexpr int kCoherent = 1 | 16;           // cache policy sc0 | sc1: device-coherent access
-constexpr int kWaitVm0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt untouched)
-constexpr int kNonTemporal = 2;             // cache policy nt: streamed once
 
 struct Shared {
   int x_ready[kXBufs];   // GEMV index whose x sits in buffer b (-1: none yet)
@@ -310,7 +251,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         // per pair (two values and the epoch land together), written through to
         // the coherence point; nothing waits for them here (r0 is even)
         const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-            reinterpret_cast<unsigned char*>(ctl) + d.tag_out, 0, 0x7FFFFFFF, 0x00020000);
+            reinterpret_cast<unsigned char*>(ctl) + d.tag_out, 0, 0x7FFFFFFF, kRsrcFlags);
         for (int q = (r0 >> 1) + lane; 2 * q < r1; q += 64) {
           const uint32_t lo16 = yb[2 * q - r0];
           const uint32_t hi16 = 2 * q + 1 < r1 ? yb[2 * q + 1 - r0] : 0u;
@@ -325,7 +266,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         // device-coherent stores (written through to the coherence point), then
         // wait for them and count this workgroup in: no cache-wide write-back
         const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-            d.Y, 0, 0x7FFFFFFF, 0x00020000);
+            d.Y, 0, 0x7FFFFFFF, kRsrcFlags);
         for (int r = r0 + lane; r < r1; r += 64)
           __builtin_amdgcn_raw_buffer_store_b16(yb[r - r0], ry, 2 * r, 0, kCoherent);
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -381,7 +322,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         }
       }
       const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint4*>(d.X), 0, 0x7FFFFFFF, 0x00020000);
+          const_cast<uint4*>(d.X), 0, 0x7FFFFFFF, kRsrcFlags);
       const Q4_GLOBAL u32x4_g* X = (const Q4_GLOBAL u32x4_g*)d.X;
       const int b = (k - j0) % NX;
       uint4* xb = xbuf + b * 4 * maxG;
@@ -404,7 +345,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           };
           if (tagged) {
             const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-                reinterpret_cast<unsigned char*>(ctl) + d.tag_in, 0, 0x7FFFFFFF, 0x00020000);
+                reinterpret_cast<unsigned char*>(ctl) + d.tag_in, 0, 0x7FFFFFFF, kRsrcFlags);
             unsigned pend = 0;
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -453,7 +394,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           // coherence point); a block is taken once all four carry this call's
           // epoch, and re-read until then
           const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-              reinterpret_cast<unsigned char*>(ctl) + d.tag_in, 0, 0x7FFFFFFF, 0x00020000);
+              reinterpret_cast<unsigned char*>(ctl) + d.tag_in, 0, 0x7FFFFFFF, kRsrcFlags);
           unsigned pend = 0;
 #pragma unroll
           for (int u = 0; u < 8; ++u)
@@ -674,11 +615,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const uint32_t ns = left * 2 < 0xFFFFFFF0ull ? (uint32_t)(left * 2) : 0xFFFFFFF0u;
       const __amdgpu_buffer_rsrc_t bw = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint4*>(live ? (const uint4*)(cu.W + (int64_t)row0 * G) : (const uint4*)W_last),
-          0, (int)nw, 0x00020000);
+          0, (int)nw, kRsrcFlags);
       const __amdgpu_buffer_rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(live ? (const uint16_t*)(cu.S + (int64_t)row0 * G)
                                      : (const uint16_t*)W_last),
-          0, (int)ns, 0x00020000);
+          0, (int)ns, kRsrcFlags);
       // Per-lane slot offsets are fixed per GEMV (the cursor's).  Only this
       // per-lane part of a buffer address is range-checked, so the scalar offset
       // stays 0; lanes past the end of the matrix (or of an empty resource) read
@@ -739,7 +680,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       }
 #pragma unroll
       for (int p = 0; p < B; ++p) {
-        const float r = team_sum(acc[p], lg) * kDotUnit;
+        const float r = team_sum_lg(acc[p], lg) * kDotUnit;
         const int row = U.rrow[p] + (lane >> lg);
         if (li == 0 && row < U.rN[p])
           ybuf[xi * ybuf_rows + (row - U.rr0[p])] = bits<uint16_t>((_Float16)r);
@@ -773,7 +714,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           acc = __builtin_fmaf(pd, (float)bits<_Float16>(U.rs[p][t]), acc);
         }
       }
-      acc = team_sum(acc, lg) * kDotUnit;
+      acc = team_sum_lg(acc, lg) * kDotUnit;
       if (li == 0 && row < U.rN[p])
         ybuf[xi * ybuf_rows + (row - U.rr0[p])] = bits<uint16_t>((_Float16)acc);
     }

@@ -37,22 +37,10 @@
 #include <cstring>
 
 #include "q4_step_mfma.h"
+#include "q4_device.h"
 
 namespace q4 {
 namespace {
-
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_g __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x8_s __attribute__((ext_vector_type(8)));
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-#define Q4_GLOBAL __attribute__((address_space(1)))
-
-template <typename T, typename F>
-__device__ __forceinline__ T bits(F v) {
-  return __builtin_bit_cast(T, v);
-}
 
 constexpr int kWaves = kStepThreads / 64;   // 16
 constexpr int kSync = 4;
@@ -61,42 +49,8 @@ constexpr int kSlots = 8;                   // x_ready slots: GEMVs up to 8 apar
 constexpr int kChunks = 4;                  // chunks (of four groups) per burst
 constexpr int kStage = 2048;                // per compute wave: one staged burst (16 rows x 8 groups)
 constexpr unsigned kSpinLimit = 1u << 24;
-constexpr int kCoherent = 1 | 16;           // sc0 | sc1
-constexpr int kNonTemporal = 2;
-constexpr int kWaitVm0 = 0x0F70;            // s_waitcnt vmcnt(0)
-constexpr int kRsrcFlags = 0x00020000;
 static_assert(kSlots % kSync == 0, "a GEMV and the one whose slot it reuses share an owner");
 
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-__device__ __forceinline__ int lds_load(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void lds_store(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// A block of 8 consecutive x values reordered into the pairs (x0,x4) (x1,x5)
-// (x2,x6) (x3,x7) in which a word's nibble pairs are dequantised.
-__device__ __forceinline__ uint4 pair_order(uint4 v) {
-  uint4 o;
-  o.x = (v.x & 0xFFFFu) | (v.z << 16);
-  o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
-  o.z = (v.y & 0xFFFFu) | (v.w << 16);
-  o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-  return o;
-}
-
-// rows {0,1} <-> {2,3} of a 4 x 4 block spread over lanes r, r+16, r+32, r+48,
-// then rows 0 <-> 1 and 2 <-> 3: afterwards lane row R register t holds what lane
-// row t register R held.
-__device__ __forceinline__ void transpose4(uint32_t (&v)[4]) {
-  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
-  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
-  v[0] = a[0]; v[2] = a[1]; v[1] = b[0]; v[3] = b[1];
-  auto c = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
-  auto d = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
-  v[0] = c[0]; v[1] = c[1]; v[2] = d[0]; v[3] = d[1];
-}
 
 struct Shared {
   int x_ready[kSlots];    // GEMV whose X is staged, per slot (-1: none)
