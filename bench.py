@@ -593,7 +593,50 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
         "ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 1),
         "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
         "tokens": tokens[: min(steps + 1, 9)].cpu().tolist()}
-    del ws, wsf, model, folded
+    del ws, wsf
+    out["whole_token_kernel"] = whole_token_figures(torch, q4, np, stream, folded, tokens,
+                                                    weight_bytes, steps)
+    del model, folded
+    return out
+
+
+def whole_token_figures(torch, q4, np, stream, model, tokens, weight_bytes, steps, reps=10):
+    """The whole-token persistent kernel (q4_tokens_run) on the same model: `steps`
+    tokens per launch, one event pair per launch on the kernel's stream (median,
+    p10, p90 over `reps` launches after warm-up), and one token per launch with a
+    host synchronisation after each.  The error word is checked afterwards."""
+    import ctypes
+    plan = q4.TokensPlan(model, stream=stream)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    tp = ctypes.c_void_p(tokens.data_ptr())
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            assert plan.run_raw(tp, steps, sp) == 0
+        stream.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            assert plan.run_raw(tp, steps, sp) == 0
+            b.record(stream)
+        stream.synchronize()
+        per = np.array([a.elapsed_time(b) / steps for a, b in ev])
+        t0 = time.perf_counter()
+        n1 = 50
+        for _ in range(n1):
+            assert plan.run_raw(tp, 1, sp) == 0
+            stream.synchronize()
+        ms1 = (time.perf_counter() - t0) * 1e3 / n1
+    plan.status(stream)
+    ms = float(np.median(per))
+    out = {"ms_per_token": round(ms, 4), "p10": round(float(np.percentile(per, 10)), 4),
+           "p90": round(float(np.percentile(per, 90)), 4), "tok_s": round(1e3 / ms, 1),
+           "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
+           "pct_of_8tbs": round(100 * weight_bytes / (ms * 1e-3) / 8e12, 1),
+           "tokens_per_launch": steps,
+           "one_token_per_launch_ms": round(ms1, 4),
+           "tokens": tokens[: min(steps + 1, 9)].cpu().tolist()}
+    del plan
     return out
 
 

@@ -129,6 +129,11 @@ def load():
             "q4_tokens_graph_create": ([p, p, p, sz, p, C.POINTER(p)], i32),
             "q4_tokens_graph_run": ([p, i64, p], i32),
             "q4_tokens_graph_destroy": ([p], i32),
+            "q4_tokens_plan_bytes": ([], sz),
+            "q4_tokens_workspace_bytes": ([p], sz),
+            "q4_tokens_plan_init": ([p, p, sz, p, sz, p], i32),
+            "q4_tokens_run": ([p, p, i64, p, p], i32),
+            "q4_tokens_ws_offset": ([p, C.c_uint32, i64], i64),
             "q4_probe_read": ([p, sz, p, i64, p], i32),
             "q4_probe_copy": ([p, p, sz, p], i32),
         }
@@ -522,6 +527,64 @@ class TokensGraph:
         if self.handle:
             _check(load().q4_tokens_graph_destroy(self.handle))
             self.handle = None
+
+
+TOKENS_QK, TOKENS_V, TOKENS_O, TOKENS_H, TOKENS_DOWN, TOKENS_LOGITS = range(6)
+
+
+def q4_tokens_workspace_bytes(model: Model) -> int:
+    return int(load().q4_tokens_workspace_bytes(model.ref()))
+
+
+class TokensPlan:
+    """The whole-token persistent kernel (q4_tokens_plan_init): the plan in host
+    memory, the workspace on the device.  run() enqueues `steps` decode steps
+    (q4_tokens_run), status() checks the error word (q4_step_status), and
+    activation() reads one of the last step's activations back from the
+    workspace (q4_tokens_ws_offset)."""
+
+    def __init__(self, model: Model, ws=None, stream=None):
+        torch = _torch()
+        lib = load()
+        self.model = model
+        self.plan = C.create_string_buffer(int(lib.q4_tokens_plan_bytes()))
+        need = q4_tokens_workspace_bytes(model)
+        if need == 0:
+            _check(lib.q4_tokens_plan_init(model.ref(), self.plan, len(self.plan), None, 0,
+                                           _stream(stream)))
+        self.ws = ws if ws is not None else torch.empty(need, dtype=torch.uint8, device="cuda")
+        _check(lib.q4_tokens_plan_init(model.ref(), self.plan, len(self.plan), _ptr(self.ws),
+                                       self.ws.numel(), _stream(stream)))
+
+    def run(self, tokens, steps: int, logits=None, stream=None):
+        _check(load().q4_tokens_run(self.plan, _ptr(tokens), steps, _ptr(logits),
+                                    _stream(stream)))
+
+    def run_raw(self, tokens_ptr, steps: int, stream_ptr):
+        """q4_tokens_run with ctypes pointers (what the host spends is the C call)."""
+        return load().q4_tokens_run(self.plan, tokens_ptr, steps, None, stream_ptr)
+
+    def status(self, stream=None):
+        q4_step_status(self.ws, stream)
+
+    def offset(self, what: int, block: int = 0) -> int:
+        return int(load().q4_tokens_ws_offset(self.plan, what, block))
+
+    def activation(self, what: int, block: int = 0):
+        """The last step's values of one stage as fp16 bits (numpy uint16): q/k rows,
+        logits, or a block's tagged pairs unpacked (epochs in self.last_epochs)."""
+        import numpy as np
+        off = self.offset(what, block)
+        if off < 0:
+            raise Q4Error(2, f"no activation {what} for block {block}")
+        D, F, V = self.model.D, self.model.F, self.model.V
+        n = {TOKENS_QK: 2 * D, TOKENS_LOGITS: V, TOKENS_V: D, TOKENS_O: D, TOKENS_H: F,
+             TOKENS_DOWN: D}[what]
+        if what in (TOKENS_QK, TOKENS_LOGITS):
+            return self.ws[off: off + 2 * n].cpu().numpy().view(np.uint16).copy()
+        words = self.ws[off: off + 4 * n].cpu().numpy().view(np.uint32).reshape(-1, 2)
+        self.last_epochs = words[:, 1].copy()
+        return words[:, 0].copy().view(np.uint16)[:n]
 
 
 def q4_gemv_format(fmt: int, words, scales, x, K: int, biases=None, y=None, stream=None):

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libq4f16.so")
 SOURCES = ["q4_api.cpp", "q4_plan.cpp", "q4_token.cpp", "q4_noalloc.hip", "q4_gemv.hip", "q4_codec.hip", "q4_glue.hip", "q4_ops.hip", "q4_formats.hip", "q4_step.hip",
-           "q4_step_mfma.hip"]
+           "q4_step_mfma.hip", "q4_tok.hip"]
 ARCH = os.environ.get("Q4_OFFLOAD_ARCH", "gfx950")
 
 

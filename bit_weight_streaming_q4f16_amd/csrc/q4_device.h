@@ -1,6 +1,7 @@
 // Device-side helpers shared by the GEMV kernels: vector types, bit casts, the
 // x pair order of the nibble decode, DPP / lane-swap team sums, the lane
-// transpose of the MFMA B layout, LDS waits and the buffer cache-policy bits.
+// transpose of the MFMA B layout, LDS waits, the buffer cache-policy bits and
+// the subnormal-code group dot product of the persistent kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -104,5 +105,58 @@ __device__ __forceinline__ int lds_load(const int* p) {
 __device__ __forceinline__ void lds_store(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+
+// The nibble-pair masks.  AND-ing a word with 0x000F000F leaves nibbles 0 and 4
+// as the mantissas of two fp16 subnormals, the exact values (q0, q4) * 2^-24;
+// with 0x00F000F0, nibbles 1 and 5 sit one mantissa position higher, (q1, q5) *
+// 2^-20; the same on word >> 8 gives elements 2, 6 and 3, 7.  Each pair is ONE
+// v_and_b32, with no exponent to insert and no offset to remove: the zero point
+// is taken off once per group (see nibble_group_dot).  The masks live in VGPRs.
+struct Nibbles {
+  uint32_t m_lo, m_hi;   // 0x000F000F, 0x00F000F0
+};
+
+__device__ __forceinline__ Nibbles make_nibbles() {
+  Nibbles n{0x000F000Fu, 0x00F000F0u};
+  asm volatile("" : "+v"(n.m_lo), "+v"(n.m_hi));
+  return n;
+}
+
+// One 32-weight group: 2^-20 * sum_k q_k x_k in fp32, from the codes as fp16
+// subnormals (products exact in fp32) and two chains of v_dot2, even and odd
+// positions, joined as 16 * even + odd (exact scaling).  x holds the group's
+// four pair-ordered blocks.  The wanted 2^-20 * sum_k (q_k - 7) x_k is this minus
+// the same function of a word whose codes are all 7 (0x77777777) with the same x,
+// which the sync waves compute once per group when they stage x: both are the
+// same instructions on the same operands, so a group of codes 7 gives exactly
+// zero, and integer codes and x give the exact integer.  The factor 2^20 is
+// applied to the row's sum.
+__device__ __forceinline__ float nibble_group_dot(uint4 w, const uint4 (&x)[4],
+                                                  const Nibbles& nb) {
+  const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
+  // the first product of each chain in the three-operand form: the compiler
+  // would otherwise copy the start value into the accumulator of v_dot2c
+  float a, b;
+  {
+    const uint32_t v = wj[0];
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(a) : "v"(v & nb.m_lo), "v"(x[0].x));
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(b) : "v"(v & nb.m_hi), "v"(x[0].y));
+    const uint32_t v8 = v >> 8;
+    a = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_lo), bits<h2_t>(x[0].z), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_hi), bits<h2_t>(x[0].w), b, false);
+  }
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    const uint32_t v = wj[j], v8 = v >> 8;
+    a = __builtin_amdgcn_fdot2(bits<h2_t>(v & nb.m_lo), bits<h2_t>(x[j].x), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>(v & nb.m_hi), bits<h2_t>(x[j].y), b, false);
+    a = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_lo), bits<h2_t>(x[j].z), a, false);
+    b = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_hi), bits<h2_t>(x[j].w), b, false);
+  }
+  return __builtin_fmaf(a, 16.f, b);
+}
+
+// 2^20: the factor between nibble_group_dot's units and the products' (exact in fp32).
+constexpr float kDotUnit = 1048576.f;
 
 }  // namespace q4

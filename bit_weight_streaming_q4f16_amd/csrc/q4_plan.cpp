@@ -17,6 +17,7 @@
 #include "q4_internal.h"
 #include "q4_step.h"
 #include "q4_step_mfma.h"
+#include "q4_tok.h"
 
 namespace {
 
@@ -306,7 +307,12 @@ int q4_step_status(void* ws, q4_stream_t stream) {
   e = q4::zero_words(ws, 1, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return q4::device_fail(e, "q4_step_status");
-  const unsigned code = word & 0xFFu, gemv = (word >> 8);
+  const unsigned code = word & 0x7Fu, gemv = (word >> 8);
+  if (word & q4::kErrTokenKernel)
+    return q4::api_fail(Q4_ERR_TIMEOUT,
+                        "q4_step_status: %s ran out in the whole-token kernel (error word "
+                        "0x%08x: code %u, stage %d of the step); the tokens and logits of that "
+                        "run are not valid", wait_name(code), word, code, (int)gemv - 1);
   return q4::api_fail(Q4_ERR_TIMEOUT,
                       "q4_step_status: %s ran out (error word 0x%08x: code %u, layers[%d]); "
                       "the outputs of that step are not valid", wait_name(code), word, code,

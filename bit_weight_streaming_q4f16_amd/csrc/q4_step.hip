@@ -89,57 +89,6 @@ __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
   return r;
 }
 
-// The nibble-pair masks.  AND-ing a word with 0x000F000F leaves nibbles 0 and 4
-// as the mantissas of two fp16 subnormals, the exact values (q0, q4) * 2^-24;
-// with 0x00F000F0, nibbles 1 and 5 sit one mantissa position higher, (q1, q5) *
-// 2^-20; the same on word >> 8 gives elements 2, 6 and 3, 7.  Each pair is ONE
-// v_and_b32, with no exponent to insert and no offset to remove: the zero point
-// is taken off once per group (see group_dot).  The masks live in VGPRs.
-struct Nibbles {
-  uint32_t m_lo, m_hi;   // 0x000F000F, 0x00F000F0
-};
-
-__device__ __forceinline__ Nibbles make_nibbles() {
-  Nibbles n{0x000F000Fu, 0x00F000F0u};
-  asm volatile("" : "+v"(n.m_lo), "+v"(n.m_hi));
-  return n;
-}
-
-// One 32-weight group: 2^-20 * sum_k q_k x_k in fp32, from the codes as fp16
-// subnormals (products exact in fp32) and two chains of v_dot2, even and odd
-// positions, joined as 16 * even + odd (exact scaling).  x holds the group's
-// four pair-ordered blocks.  The wanted 2^-20 * sum_k (q_k - 7) x_k is this minus
-// the same function of a word whose codes are all 7 (0x77777777) with the same x,
-// which the sync waves compute once per group when they stage x: both are the
-// same instructions on the same operands, so a group of codes 7 gives exactly
-// zero, and integer codes and x give the exact integer.  The factor 2^20 is
-// applied to the row's sum.
-__device__ __forceinline__ float group_dot(uint4 w, const uint4 (&x)[4], const Nibbles& nb) {
-  const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
-  // the first product of each chain in the three-operand form: the compiler
-  // would otherwise copy the start value into the accumulator of v_dot2c
-  float a, b;
-  {
-    const uint32_t v = wj[0];
-    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(a) : "v"(v & nb.m_lo), "v"(x[0].x));
-    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(b) : "v"(v & nb.m_hi), "v"(x[0].y));
-    const uint32_t v8 = v >> 8;
-    a = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_lo), bits<h2_t>(x[0].z), a, false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_hi), bits<h2_t>(x[0].w), b, false);
-  }
-#pragma unroll
-  for (int j = 1; j < 4; ++j) {
-    const uint32_t v = wj[j], v8 = v >> 8;
-    a = __builtin_amdgcn_fdot2(bits<h2_t>(v & nb.m_lo), bits<h2_t>(x[j].x), a, false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>(v & nb.m_hi), bits<h2_t>(x[j].y), b, false);
-    a = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_lo), bits<h2_t>(x[j].z), a, false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>(v8 & nb.m_hi), bits<h2_t>(x[j].w), b, false);
-  }
-  return __builtin_fmaf(a, 16.f, b);
-}
-
-// 2^20: the factor between group_dot's units and the products' (exact in fp32).
-constexpr float kDotUnit = 1048576.f;
 
 constexpr int kWaves = kStepThreads / 64;   // 16
 constexpr int kSync = 4;                    // sync waves (stage x, copy out y)
@@ -446,7 +395,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         }
       }
       // per group the offset term: the compute waves' chain over codes all 7
-      // with this x (see group_dot), read back from the planes just written
+      // with this x (see nibble_group_dot), read back from the planes just written
       wait_lds();
       {
         const uint4 w7 = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
@@ -454,7 +403,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           uint4 xq[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) xq[q] = xb[q * maxG + g];
-          cb[g] = group_dot(w7, xq, nbs);
+          cb[g] = nibble_group_dot(w7, xq, nbs);
         }
       }
       // groups past G up to the padded count read x = 0 and bias 0, so the
@@ -673,7 +622,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           const float off = cb[lpr * t];
 #pragma unroll
           for (int p = 0; p < B; ++p) {
-            const float pd = group_dot(U.rw[p][t], x, nb) - off;
+            const float pd = nibble_group_dot(U.rw[p][t], x, nb) - off;
             acc[p] = __builtin_fmaf(pd, (float)bits<_Float16>(U.rs[p][t]), acc[p]);
           }
         }
@@ -710,7 +659,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           uint4 x[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
-          const float pd = group_dot(U.rw[p][t], x, nb) - cb[lpr * t];
+          const float pd = nibble_group_dot(U.rw[p][t], x, nb) - cb[lpr * t];
           acc = __builtin_fmaf(pd, (float)bits<_Float16>(U.rs[p][t]), acc);
         }
       }

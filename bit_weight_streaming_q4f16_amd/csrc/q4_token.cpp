@@ -26,6 +26,7 @@
 #include "q4f16.h"
 #include "q4_fused.h"
 #include "q4_internal.h"
+#include "q4_tok.h"
 
 namespace {
 
@@ -337,6 +338,255 @@ int q4_tokens_graph_destroy(q4_tokens_graph* g) {
   hipError_t e = g->exec ? hipGraphExecDestroy(g->exec) : hipSuccess;
   delete g;
   return e == hipSuccess ? q4::api_ok() : device_error(e, "q4_tokens_graph_destroy");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- whole-token persistent kernel
+
+namespace {
+
+constexpr uint32_t kTokMagic = 0x51345431u;    // "Q4T1"
+constexpr uint32_t kTokVersion = 1;
+constexpr int kTokBurstItems = 2;              // items per burst (q4_tok.hip)
+constexpr int64_t kTokMaxStepsPerLaunch = 4096;
+
+// The persistent kernel's plan as it sits in the caller's buffer.
+struct TokPlan {
+  uint32_t magic, version;
+  int32_t device, n_blocks;
+  const void* ws;
+  uint64_t ws_bytes, clear_bytes;
+  uint64_t qk_off, logits_off, tags_off, block_stride;   // workspace layout
+  uint64_t tv_off, to_off, th_off, td_off;               // within a block's tags
+  int64_t D, F, V;
+  q4::TokLaunch launch;
+};
+
+// Workspace layout: control block, stage table, per block the tagged outputs of
+// v (qkv rows 2D..3D), o, the glue (h) and down, then the q/k rows and the logits.
+struct TokLayout {
+  std::vector<q4::TokStage> stages;
+  q4::TokLaunch launch{};
+  size_t clear_bytes = 0, qk_off = 0, logits_off = 0, tags_off = 0, block_stride = 0;
+  size_t tv = 0, to = 0, th = 0, td = 0, bytes = 0;
+};
+
+int tok_lg(int64_t G) {
+  int lg = 2;
+  while ((4 << lg) < G && lg < 6) ++lg;
+  return lg;
+}
+
+// The model's shape limits for the persistent kernel; Q4_OK or a status with the
+// error text set.
+int tok_supported(const char* what, const q4_model& m) {
+  if (m.D > 4096 || m.F > 8192)
+    return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: the whole-token kernel takes D <= 4096 and F "
+                        "<= 8192 (rows of at most 4 groups per lane), got D = %lld, F = %lld",
+                        what, (long long)m.D, (long long)m.F);
+  if (m.V > (1 << 24))
+    return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: vocabulary above 2^24", what);
+  if (m.n_blocks > 4096)
+    return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: more than 4096 blocks", what);
+  return Q4_OK;
+}
+
+TokLayout tok_layout(const q4::DeviceInfo& d, const q4_model& m) {
+  TokLayout L;
+  const int64_t D = m.D, F = m.F, V = m.V, n = m.n_blocks;
+  const int grid = d.cus;
+  size_t off = 256;                                   // control block
+  const size_t table_off = off;
+  off += up256((size_t)(4 * n + 1) * sizeof(q4::TokStage));
+  L.tags_off = off;
+  L.tv = 0;
+  L.to = L.tv + up256((size_t)4 * D);
+  L.th = L.to + up256((size_t)4 * D);
+  L.td = L.th + up256((size_t)4 * F);
+  L.block_stride = L.td + up256((size_t)4 * D);
+  off += (size_t)n * L.block_stride;
+  L.clear_bytes = off;
+  L.qk_off = off;
+  off += up256((size_t)4 * D);
+  L.logits_off = off;
+  off += up256((size_t)2 * V);
+  L.bytes = off;
+  int maxG = 4;
+  auto stage = [&](const q4_weight& w, int64_t nout, int flags, const uint16_t* gamma,
+                   uint16_t* out, int64_t nplain, size_t tag_in, size_t tag_out) {
+    q4::TokStage s{};
+    const int64_t G = w.K / 32;
+    const int lg = tok_lg(G), lpr = 1 << lg;
+    s.W = reinterpret_cast<const uint4*>(w.words);
+    s.S = w.scales;
+    s.gamma = gamma;
+    s.out = out;
+    s.rows = (int)w.N;
+    s.G = (int)G;
+    s.lg = (int16_t)lg;
+    s.C = (int16_t)((G + lpr - 1) / lpr);
+    s.nout = (int)nout;
+    s.flags = flags;
+    s.nplain = (int)nplain;
+    s.tag_in = (int)tag_in;
+    s.tag_out = (int)tag_out;
+    const int opb = q4::tok_outputs_per_burst(kTokBurstItems, lg, (flags & q4::kTokGlu) != 0);
+    s.nburst = (int)((nout + opb - 1) / opb);
+    s.sbase = s.nburst / grid;
+    s.srem = s.nburst % grid;
+    maxG = std::max(maxG, lpr * (int)s.C);
+    L.stages.push_back(s);
+  };
+  auto tags = [&](int64_t b, size_t part) { return L.tags_off + (size_t)b * L.block_stride + part; };
+  for (int64_t b = 0; b < n; ++b) {
+    const q4_block& B = m.blocks[b];
+    stage(B.qkv, 3 * D, b == 0 ? q4::kTokEmbed : q4::kTokNorm, B.attn_norm, nullptr, 2 * D,
+          b == 0 ? 0 : tags(b - 1, L.td), tags(b, L.tv));
+    stage(B.o, D, 0, nullptr, nullptr, 0, tags(b, L.tv), tags(b, L.to));
+    stage(B.gate_up, F, q4::kTokNorm | q4::kTokGlu, B.ffn_norm, nullptr, 0, tags(b, L.to),
+          tags(b, L.th));
+    stage(B.down, D, 0, nullptr, nullptr, 0, tags(b, L.th), tags(b, L.td));
+  }
+  stage(m.lm_head, V, (n == 0 ? q4::kTokEmbed : q4::kTokNorm) | q4::kTokArgmax, m.final_norm,
+        nullptr, V, n == 0 ? 0 : tags(n - 1, L.td), 0);
+  q4::TokLaunch& T = L.launch;
+  T.grid = grid;
+  T.stages = (int)L.stages.size();
+  T.maxG = maxG;
+  T.D = (int)D;
+  T.V = (int)V;
+  T.burst = kTokBurstItems;
+  T.lds_bytes = (uint32_t)q4::tok_lds_bytes(maxG, (int)D);
+  T.eps = m.eps;
+  T.table_off = table_off;
+  T.embed_words = m.embed.words;
+  T.embed_scales = m.embed.scales;
+  return L;
+}
+
+int tok_layout_checked(const char* what, const q4_model* model, TokLayout* out) {
+  if (int rc = check_model(model)) return q4::api_fail(rc, "%s: %s", what, q4_last_error());
+  if (int rc = tok_supported(what, *model)) return rc;
+  const q4::DeviceInfo* d = q4::device_info();
+  if (!d) return q4::api_fail(Q4_ERR_DEVICE, "%s: no HIP device", what);
+  *out = tok_layout(*d, *model);
+  if (out->bytes > (size_t)INT32_MAX)
+    return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: workspace above 2 GiB", what);
+  if (out->launch.lds_bytes > d->lds_per_block)
+    return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: needs %u bytes of LDS, the device has %zu",
+                        what, out->launch.lds_bytes, d->lds_per_block);
+  return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q4_tokens_plan_bytes(void) { return sizeof(TokPlan); }
+
+size_t q4_tokens_workspace_bytes(const q4_model* model) {
+  TokLayout L;
+  if (tok_layout_checked("q4_tokens_workspace_bytes", model, &L)) return 0;
+  return L.bytes;
+}
+
+int q4_tokens_plan_init(const q4_model* model, void* plan, size_t plan_bytes, void* ws,
+                        size_t ws_bytes, q4_stream_t stream) {
+  const char* what = "q4_tokens_plan_init";
+  TokLayout L;
+  if (int rc = tok_layout_checked(what, model, &L)) return rc;
+  if (!plan) return q4::api_fail(Q4_ERR_NULL, "%s: plan is NULL", what);
+  if (plan_bytes < sizeof(TokPlan))
+    return q4::api_fail(Q4_ERR_WORKSPACE, "%s: the plan needs %zu bytes, got %zu", what,
+                        sizeof(TokPlan), plan_bytes);
+  if (reinterpret_cast<uintptr_t>(plan) % 8)
+    return q4::api_fail(Q4_ERR_ALIGN, "%s: plan not 8-byte aligned", what);
+  if (int rc = check_ws(ws, ws_bytes, L.bytes)) return q4::api_fail(rc, "%s: %s", what,
+                                                                    q4_last_error());
+  if (!aligned(ws, 256)) return q4::api_fail(Q4_ERR_ALIGN, "%s: ws not 256-byte aligned", what);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  // the q/k rows and the logits go to the workspace
+  for (q4::TokStage& s : L.stages) {
+    if (s.flags & q4::kTokArgmax) s.out = reinterpret_cast<uint16_t*>(w + L.logits_off);
+    else if (s.nplain) s.out = reinterpret_cast<uint16_t*>(w + L.qk_off);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = q4::tok_prepare(L.launch);
+  if (e == hipSuccess) e = q4::zero_words(ws, L.clear_bytes / 4, s);
+  if (e == hipSuccess)
+    e = q4::write_table(w + L.launch.table_off, L.stages.data(),
+                        L.stages.size() * sizeof(q4::TokStage), s);
+  if (e != hipSuccess) return device_error(e, what);
+  TokPlan p{};
+  p.magic = kTokMagic;
+  p.version = kTokVersion;
+  const q4::DeviceInfo* d = q4::device_info();
+  p.device = d->id;
+  p.n_blocks = (int32_t)model->n_blocks;
+  p.ws = ws;
+  p.ws_bytes = L.bytes;
+  p.clear_bytes = L.clear_bytes;
+  p.qk_off = L.qk_off;
+  p.logits_off = L.logits_off;
+  p.tags_off = L.tags_off;
+  p.block_stride = L.block_stride;
+  p.tv_off = L.tv;
+  p.to_off = L.to;
+  p.th_off = L.th;
+  p.td_off = L.td;
+  p.D = model->D;
+  p.F = model->F;
+  p.V = model->V;
+  p.launch = L.launch;
+  memcpy(plan, &p, sizeof p);
+  return q4::api_ok();
+}
+
+int q4_tokens_run(const void* plan, int32_t* tokens, int64_t steps, uint16_t* logits,
+                  q4_stream_t stream) {
+  const char* what = "q4_tokens_run";
+  if (!plan) return q4::api_fail(Q4_ERR_NULL, "%s: plan is NULL", what);
+  TokPlan p;
+  memcpy(&p, plan, sizeof p);
+  if (p.magic != kTokMagic || p.version != kTokVersion)
+    return q4::api_fail(Q4_ERR_SHAPE, "%s: not a plan made by q4_tokens_plan_init", what);
+  if (!tokens) return q4::api_fail(Q4_ERR_NULL, "%s: tokens is NULL", what);
+  if (!aligned(tokens, 4) || (logits && !aligned(logits, 2)))
+    return q4::api_fail(Q4_ERR_ALIGN, "%s: misaligned tokens or logits", what);
+  if (steps < 0 || steps > INT32_MAX - 1)
+    return q4::api_fail(Q4_ERR_SHAPE, "%s: steps = %lld", what, (long long)steps);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != p.device)
+    return q4::api_fail(Q4_ERR_DEVICE, "%s: the plan is for device %d, the current one is %d",
+                        what, p.device, dev);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  // launches of at most kTokMaxStepsPerLaunch steps (the kernel's counters are
+  // 32-bit); the token array chains them
+  for (int64_t t0 = 0; t0 < steps && e == hipSuccess; t0 += kTokMaxStepsPerLaunch) {
+    const int n = (int)std::min<int64_t>(kTokMaxStepsPerLaunch, steps - t0);
+    e = q4::launch_tokens(p.launch, const_cast<void*>(p.ws), tokens + t0, n, logits, s);
+  }
+  return e == hipSuccess ? q4::api_ok() : device_error(e, what);
+}
+
+int64_t q4_tokens_ws_offset(const void* plan, uint32_t what, int64_t block) {
+  if (!plan) return -1;
+  TokPlan p;
+  memcpy(&p, plan, sizeof p);
+  if (p.magic != kTokMagic || p.version != kTokVersion) return -1;
+  if (what == Q4_TOKENS_QK) return (int64_t)p.qk_off;
+  if (what == Q4_TOKENS_LOGITS) return (int64_t)p.logits_off;
+  if (block < 0 || block >= p.n_blocks) return -1;
+  const uint64_t b = p.tags_off + (uint64_t)block * p.block_stride;
+  switch (what) {
+    case Q4_TOKENS_V: return (int64_t)(b + p.tv_off);
+    case Q4_TOKENS_O: return (int64_t)(b + p.to_off);
+    case Q4_TOKENS_H: return (int64_t)(b + p.th_off);
+    case Q4_TOKENS_DOWN: return (int64_t)(b + p.td_off);
+    default: return -1;
+  }
 }
 
 }  // extern "C"

@@ -270,7 +270,9 @@ Q4_API int q4_step_run(const void* plan, void* ws, size_t ws_bytes, q4_stream_t 
  * and the descriptor (the outputs of the step that ran out are not valid), and
  * the word is cleared.  The workspace's counters are left zero either way (every
  * workgroup of the kernel finishes: the waits are bounded), so later runs start
- * clean.  ws: a workspace set up by q4_step_plan_init. */
+ * clean.  ws: a workspace set up by q4_step_plan_init, or by q4_tokens_plan_init
+ * (the whole-token kernel keeps the same error word; the detail then names the
+ * stage of the step). */
 Q4_API int q4_step_status(void* ws, q4_stream_t stream);
 
 /* q4_decode_step: plan and run a list in one call (Zero TVM documentation,
@@ -496,6 +498,72 @@ Q4_API int q4_tokens_graph_run(q4_tokens_graph* graph, int64_t steps, q4_stream_
  * wait: the caller synchronises the streams the graph was launched on first.
  * NULL is accepted. */
 Q4_API int q4_tokens_graph_destroy(q4_tokens_graph* graph);
+
+/* --------------------------------------------------- whole-token kernel -- */
+/* The decode loop of q4_decode_tokens with every stage of every step in ONE
+ * persistent kernel launch (Zero TVM documentation, "Decode loop"; the
+ * everything-webgpu page's host-side lever of submitting a whole token in one
+ * command, "Multi-step decoding", taken to one kernel for several tokens): per
+ * block qkv, o on the value part, gate/up with the SiLU-multiply, down, then the
+ * LM head and the greedy argmax, the next step's embedding row from that
+ * argmax.  Each workgroup keeps its own copy of the residual stream; the
+ * projections hand their outputs to the next one as epoch-tagged pairs in the
+ * workspace, and the weights of the next projection stream while the current
+ * one waits for its input.  It always computes the factored-norm step
+ * (Q4_MODEL_FACTORED_NORM; model->options is not consulted): results agree with
+ * q4_decode_tokens on that model within fp32 rounding of the dot products (a
+ * different summation order), not bit for bit; the token is the argmax of the
+ * logits it computes (ties to the lowest index, NaN skipped).  Shapes: D <= 4096,
+ * F <= 8192, V <= 2^24, n_blocks <= 4096.  A plan is made once per model and
+ * workspace, then runs launch only. */
+
+/* Bytes of the host plan buffer q4_tokens_plan_init fills (the everything-webgpu
+ * page's multi-step decode, planned once). */
+Q4_API size_t q4_tokens_plan_bytes(void);
+
+/* Workspace bytes of the whole-token kernel for this model (Zero TVM
+ * documentation, "Decode loop": every stage's activations; here the control
+ * block, the stage table, the tagged pairs of every projection, q/k rows and
+ * logits); 0 if the model is invalid or outside the shape limits. */
+Q4_API size_t q4_tokens_workspace_bytes(const q4_model* model);
+
+/* q4_tokens_plan_init: the set-up of the everything-webgpu page's multi-step
+ * decode ("Multi-step decoding") for the whole-token kernel.  Plans the stages
+ * into `plan` (host memory, q4_tokens_plan_bytes(), 8-byte aligned) and
+ * enqueues on `stream` the writes of the stage table and the zeroing of the
+ * control block and tagged pairs in `ws` (device memory,
+ * q4_tokens_workspace_bytes(model), 256-byte aligned).  The plan holds the
+ * model's pointers and ws: they must stay valid and unchanged while it is used.
+ * No allocation, no wait. */
+Q4_API int q4_tokens_plan_init(const q4_model* model, void* plan, size_t plan_bytes, void* ws,
+                               size_t ws_bytes, q4_stream_t stream);
+
+/* q4_tokens_run: `steps` decode steps (Zero TVM documentation, "Decode loop";
+ * everything-webgpu AI.md, "Multi-step decoding"): tokens is DEVICE int32
+ * [steps + 1]; step i reads tokens[i] (i = 0) or the previous step's argmax and
+ * writes tokens[i + 1].  logits: DEVICE fp16 [V] receiving every step's logits
+ * (the last one's remain), or NULL (they stay in the workspace).  One launch per
+ * 4096 steps on `stream`; calls sharing a plan must be ordered on one stream.
+ * No allocation, no wait; q4_step_status(ws, stream) reports a bounded wait
+ * that ran out. */
+Q4_API int q4_tokens_run(const void* plan, int32_t* tokens, int64_t steps, uint16_t* logits,
+                         q4_stream_t stream);
+
+/* q4_tokens_ws_offset: where the last step's activations stay in the workspace
+ * (for inspection and tests of the Zero TVM decode loop's stages): byte offset
+ * of Q4_TOKENS_QK (fp16 [2D]: the q and k rows of the last block's qkv),
+ * Q4_TOKENS_LOGITS (fp16 [V], when run with logits NULL), or for block `block`
+ * the tagged pairs of Q4_TOKENS_V (the value rows of qkv, D values),
+ * Q4_TOKENS_O (D), Q4_TOKENS_H (the SiLU-multiply of gate/up, F) or
+ * Q4_TOKENS_DOWN (D): 8 bytes per two values, {fp16 lo | fp16 hi << 16,
+ * uint32 epoch}.  -1 for an invalid plan, `what` or block. */
+#define Q4_TOKENS_QK 0u
+#define Q4_TOKENS_V 1u
+#define Q4_TOKENS_O 2u
+#define Q4_TOKENS_H 3u
+#define Q4_TOKENS_DOWN 4u
+#define Q4_TOKENS_LOGITS 5u
+Q4_API int64_t q4_tokens_ws_offset(const void* plan, uint32_t what, int64_t block);
 
 /* ------------------------------------------------------ measurement aids -- */
 

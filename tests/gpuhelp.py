@@ -4,6 +4,7 @@ import numpy as np
 import torch
 
 import oracle
+import synth
 
 
 def dev_words(w: np.ndarray) -> torch.Tensor:
@@ -171,3 +172,27 @@ def assert_within_rounding_bound(y_gpu_bits, y_exact64, y_exact16, scales, X, ki
     frac = float(same.mean())
     assert frac >= exact_frac, f"{what}: only {frac:.4f} of outputs exactly rounded"
     return float((err / lim).max()), frac
+
+
+def weights_f64(words, scales):
+    codes = oracle.unpack(words).astype(np.float64)
+    return (codes - 7) * np.repeat(half_f64(scales), 32, axis=1)
+
+
+def folded_bound(w, s, h_bits, gamma_bits, eps, y_ref, kind="exact"):
+    """Per-output bound on |y_folded (fp32, before its rounding) - y_unfolded| for
+    the GEMV of a folded RMSNorm (input fp16(h * gamma), outputs scaled by
+    1 / rms(h)); kind: the GEMV's dequantisation (error_bound)."""
+    K = h_bits.size
+    h, g = half_f64(h_bits), half_f64(gamma_bits)
+    r = 1.0 / np.sqrt(np.mean(h * h) + eps)
+    a = h * g                                           # exact in fp64
+    v_bits = synth.to_half_bits(a)                      # the folded GEMV's input
+    W = np.abs(weights_f64(w, s))
+    # the two fp16 roundings of each input term: fp16(a) * r against fp16(r a)
+    t_in = W @ (2.0 ** -10 * r * np.abs(a) + 2.0 ** -25 * (1.0 + r))
+    # the folded GEMV's fp32 error on its own input, times r
+    t_gemv = r * error_bound(s, v_bits, kind)[0]
+    # the fp32 norm scalar: sum of K squares, the mean, the root, the reciprocal, the product
+    t_r = (K + 8) * _U * r * (W @ np.abs(half_f64(v_bits)))
+    return t_in + t_gemv + t_r

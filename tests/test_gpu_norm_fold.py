@@ -12,7 +12,7 @@ torch = pytest.importorskip("torch")
 import oracle
 import synth
 import bit_weight_streaming_q4f16_amd as q4
-from gpuhelp import dev_half, dev_words, error_bound, half_f64, host_half, ulp16
+from gpuhelp import dev_half, dev_words, folded_bound, half_f64, host_half, ulp16
 
 pytestmark = pytest.mark.gpu
 U = 2.0 ** -24
@@ -25,11 +25,6 @@ def gpu():
     q4.load()
 
 
-def weights_f64(words, scales):
-    codes = oracle.unpack(words).astype(np.float64)
-    return (codes - 7) * np.repeat(half_f64(scales), 32, axis=1)
-
-
 def case(label, rows, K, with_delta):
     m = synth.Matrix(label, rows, K)
     w, s = m.words(), m.scales()
@@ -37,23 +32,6 @@ def case(label, rows, K, with_delta):
     delta = synth.to_half_bits(0.5 * synth.normal(label + "/d", 0, 0, K)) if with_delta else None
     gamma = synth.to_half_bits(1.0 + 0.1 * synth.normal(label + "/g", 0, 0, K))
     return w, s, res, delta, gamma
-
-
-def folded_bound(w, s, h_bits, gamma_bits, eps, y_ref):
-    """Per-output bound on |y_folded (fp32, before its rounding) - y_unfolded|."""
-    K = h_bits.size
-    h, g = half_f64(h_bits), half_f64(gamma_bits)
-    r = 1.0 / np.sqrt(np.mean(h * h) + eps)
-    a = h * g                                           # exact in fp64
-    v_bits = synth.to_half_bits(a)                      # the folded GEMV's input
-    W = np.abs(weights_f64(w, s))
-    # the two fp16 roundings of each input term: fp16(a) * r against fp16(r a)
-    t_in = W @ (2.0 ** -10 * r * np.abs(a) + 2.0 ** -25 * (1.0 + r))
-    # the folded GEMV's fp32 error on its own input, times r
-    t_gemv = r * error_bound(s, v_bits, "exact")[0]
-    # the fp32 norm scalar: sum of K squares, the mean, the root, the reciprocal, the product
-    t_r = (K + 8) * U * r * (W @ np.abs(half_f64(v_bits)))
-    return t_in + t_gemv + t_r
 
 
 @pytest.mark.parametrize("rows,K,with_delta", [(3000, 3072, True), (257, 544, False),

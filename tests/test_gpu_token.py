@@ -13,10 +13,9 @@ import oracle
 import synth
 import bit_weight_streaming_q4f16_amd as q4
 from gpuhelp import assert_gemv_close, dev_half, dev_words, host_half
+from tokhelp import EPS, Weights
 
 pytestmark = pytest.mark.gpu
-
-EPS = 1e-5
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -31,35 +30,6 @@ def within_one_ulp(got, ref):
     r = np.asarray(ref, np.uint16).reshape(-1).view(np.float16).astype(np.float64)
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -14))) - 10)
     assert np.all(np.abs(g - r) <= ulp)
-
-
-class Weights:
-    """Seeded weights of a model with D, F, V and n blocks (host copies kept for
-    the oracle when `host`)."""
-
-    def __init__(self, tag, n, D, F, V, host=True):
-        self.D, self.F, self.V, self.n = D, F, V, n
-        self.mats = {}
-
-        def w(name, N, K, sigma):
-            m = synth.Matrix(f"tok/{tag}/{name}", N, K, sigma=sigma, floor=sigma / 4)
-            self.mats[name] = m if host else None
-            return (m.words_torch("cuda"), dev_half(m.scales()))
-
-        def g(name):
-            v = (1.0 + 0.1 * synth.normal(f"tok/{tag}/{name}", 0, 0, D)).astype(np.float16)
-            return dev_half(v.view(np.uint16))
-        self.embed = w("embed", V, D, 0.05)
-        self.lm_head = w("lm_head", V, D, 2.0 / D)
-        self.final_norm = g("final_norm")
-        self.blocks = [dict(qkv=w(f"{b}/qkv", 3 * D, D, 2.0 / D), o=w(f"{b}/o", D, D, 2.0 / D),
-                            gate_up=w(f"{b}/gate_up", 2 * F, D, 2.0 / D),
-                            down=w(f"{b}/down", D, F, 2.0 / F),
-                            attn_norm=g(f"{b}/attn_norm"), ffn_norm=g(f"{b}/ffn_norm"))
-                       for b in range(n)]
-        self.model = q4.Model(self.embed, self.blocks, self.final_norm, self.lm_head, EPS)
-        self.fmodel = q4.Model(self.embed, self.blocks, self.final_norm, self.lm_head, EPS,
-                               options=q4.MODEL_FACTORED_NORM)
 
 
 def composed_step(W, token, check):
