@@ -82,6 +82,8 @@ def parse():
                     help="run only a plain device copy of BYTES, 3 times (counter calibration)")
     ap.add_argument("--only-m8", action="store_true",
                     help="time only the 2B-class sweep at M=8 (for profiler runs)")
+    ap.add_argument("--only-q3", action="store_true",
+                    help="time only the q3f16_1 and mixed-format Phi-3 sweeps")
     ap.add_argument("--only-tokens", action="store_true",
                     help="time only the Phi-3-shaped decode-token loop (for profiler runs)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -128,6 +130,10 @@ def main():
     stream = torch.cuda.Stream()          # default priority
     if args.copy_probe:
         copy_probe(torch, q4, stream, args.copy_probe)
+        return
+    if args.only_q3:
+        print(json.dumps({"phi3_sweep_q3f16_1": q3_sweep(torch, q4, synth, np, stream)}),
+              flush=True)
         return
     if args.only_tokens:
         descs, meta = build_sweep(torch, q4, synth, np)
@@ -415,6 +421,7 @@ def per_config(torch, q4, synth, np, stream):
     out["formats_qkv_3072x9216_m1"] = fmts
     out["formats_large_m1"] = formats_large(torch, q4, S, stream)
     out["twob_sweep_m8"] = m8_sweep(torch, q4, synth, np, stream)
+    out["phi3_sweep_q3f16_1"] = q3_sweep(torch, q4, synth, np, stream)
     return out
 
 
@@ -510,6 +517,59 @@ def m8_sweep(torch, q4, synth, np, stream, steps=300, warmup=50):
     del descs
     torch.cuda.empty_cache()
     return fig
+
+
+def q3_sweep(torch, q4, synth, np, stream, steps=300, warmup=100):
+    """The Phi-3-shaped sweep with q3f16_1 weights (14 bytes per 32 weights) in the
+    persistent decode-step kernel, and the same list with q3f16_1 and q4f16_1
+    layers alternating: one event pair per step on the kernel's stream, median."""
+    S = synth
+    shapes = S.sweep_shapes("phi3")
+    xs = {}
+    out = {}
+    for name, pick in (("q3f16_1", lambda i: True), ("mixed", lambda i: i % 2 == 0)):
+        descs, nbytes = [], 0
+        for i, (label, N, K) in enumerate(shapes):
+            if K not in xs:
+                h = S.activations(f"phi3/x{K}", 0, K)
+                xs[K] = torch.from_numpy(h.view(np.int16)).cuda().view(torch.float16)
+            q3 = pick(i)
+            y = torch.empty(N, dtype=torch.float16, device="cuda")
+            if q3:
+                words = S.words_torch(label + "/q3words", 0, N * K // 32 * 3).view(N, -1)
+                sc = S.scales_halfnormal(label + "/scales", 0, 0, N * K // 32, 0.01, 1e-3)
+                sc = torch.from_numpy(sc.view(np.int16)).cuda().view(torch.float16)
+                descs.append((words, sc, xs[K], y, 0, q4.FMT_Q3F16_1))
+                nbytes += N * K // 32 * 14 + 2 * K + 2 * N
+            else:
+                m = S.Matrix(label, N, K)
+                sc = torch.from_numpy(m.scales().view(np.int16)).cuda().view(torch.float16)
+                descs.append((m.words_torch("cuda"), sc, xs[K], y, 0, 0))
+                nbytes += S.algorithmic_bytes(1, N, K)
+        plan = q4.StepPlan(q4.make_layers(descs), 1, 0, stream=stream)
+        sp = q4.C.c_void_p(stream.cuda_stream)
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                plan.run_raw(sp)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for a, b in ev:
+                a.record(stream)
+                plan.run_raw(sp)
+                b.record(stream)
+            torch.cuda.synchronize()
+            plan.status(stream)
+        per = np.array([a.elapsed_time(b) for a, b in ev])
+        ms = float(np.median(per))
+        out[name] = _fig(nbytes, ms, gemvs=len(shapes),
+                         q3_layers=sum(1 for i in range(len(shapes)) if pick(i)),
+                         tok_per_s=round(1e3 / ms, 1),
+                         us_p10=round(float(np.percentile(per, 10)) * 1e3, 2),
+                         us_p90=round(float(np.percentile(per, 90)) * 1e3, 2),
+                         statistic="median", kernel="k_step")
+        del descs, plan
+        torch.cuda.empty_cache()
+    return out
 
 
 def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):

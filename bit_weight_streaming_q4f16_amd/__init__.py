@@ -58,7 +58,7 @@ class Layer(C.Structure):
     """q4_layer: one GEMV of a decode step (device pointers and sizes)."""
     _fields_ = [("words", C.c_void_p), ("scales", C.c_void_p), ("x", C.c_void_p),
                 ("y", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64),
-                ("x_op", C.c_uint32), ("reserved", C.c_uint32)]
+                ("x_op", C.c_uint32), ("format", C.c_uint32)]
 
 
 class Weight(C.Structure):
@@ -301,15 +301,19 @@ def q4_gemv_batched_noalloc(words, scales, X, Y=None, stream=None):
 
 
 def make_layers(descs):
-    """descs: iterable of (words, scales, x, y) or (words, scales, x, y, x_op)
-    tensors -> ctypes array of Layer."""
+    """descs: iterable of (words, scales, x, y), (words, scales, x, y, x_op) or
+    (words, scales, x, y, x_op, format) tensors -> ctypes array of Layer.  K
+    follows from the words' row length: 8 per word (q4f16_1) or 32 per three
+    words (format FMT_Q3F16_1)."""
     descs = list(descs)
     arr = (Layer * len(descs))()
     for i, d in enumerate(descs):
         w, s, x, y = d[:4]
         x_op = d[4] if len(d) > 4 else X_PLAIN
-        N, K8 = w.shape
-        arr[i] = Layer(w.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), N, 8 * K8, x_op, 0)
+        fmt = d[5] if len(d) > 5 else 0
+        N, RW = w.shape
+        K = RW * 32 // 3 if fmt == FMT_Q3F16_1 else 8 * RW
+        arr[i] = Layer(w.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, x_op, fmt)
     return arr
 
 

@@ -61,7 +61,7 @@ int check_shape(int64_t N, int64_t K) {
 // x_cols: elements per row of x (K, or 2K when x holds gate | up).
 int check_gemv(const char* what, const uint32_t* words, const uint16_t* scales,
                const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K,
-               int64_t x_cols) {
+               int64_t x_cols, uint32_t format = 0) {
   if (!words) return fail(Q4_ERR_NULL, "%s: words is NULL", what);
   if (!scales) return fail(Q4_ERR_NULL, "%s: scales is NULL", what);
   if (!x) return fail(Q4_ERR_NULL, "%s: x is NULL", what);
@@ -70,8 +70,10 @@ int check_gemv(const char* what, const uint32_t* words, const uint16_t* scales,
     return fail(Q4_ERR_SHAPE, "%s: M = %lld: must be in [1, %d]", what, (long long)M, q4::kMaxM);
   int rc = check_shape(N, K);
   if (rc) return fail(rc, "%s: %s", what, g_error.c_str());
-  if (!aligned(words, 16)) return fail(Q4_ERR_ALIGN, "%s: words %p not 16-byte aligned", what,
-                                       (const void*)words);
+  const bool q3 = format == Q4_FMT_Q3F16_1;
+  if (!aligned(words, q3 ? 4 : 16))
+    return fail(Q4_ERR_ALIGN, "%s: words %p not %d-byte aligned", what, (const void*)words,
+                q3 ? 4 : 16);
   if (!aligned(x, 16)) return fail(Q4_ERR_ALIGN, "%s: x %p not 16-byte aligned", what,
                                    (const void*)x);
   if (!aligned(scales, 2)) return fail(Q4_ERR_ALIGN, "%s: scales %p not 2-byte aligned", what,
@@ -84,7 +86,8 @@ int check_gemv(const char* what, const uint32_t* words, const uint16_t* scales,
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + (uintptr_t)bytes;
     return a0 < y1 && y0 < a1;
   };
-  if (overlaps(words, N * K / 2) || overlaps(scales, N * K / 16) || overlaps(x, 2 * M * x_cols))
+  if (overlaps(words, q3 ? N * K / 32 * 12 : N * K / 2) || overlaps(scales, N * K / 16) ||
+      overlaps(x, 2 * M * x_cols))
     return fail(Q4_ERR_SHAPE, "%s: y overlaps an input", what);
   return Q4_OK;
 }
@@ -199,8 +202,8 @@ namespace q4 {
 
 int gemv_validate(const char* what, const uint32_t* words, const uint16_t* scales,
                   const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K,
-                  int64_t x_cols) {
-  return check_gemv(what, words, scales, x, y, M, N, K, x_cols ? x_cols : K);
+                  int64_t x_cols, uint32_t format) {
+  return check_gemv(what, words, scales, x, y, M, N, K, x_cols ? x_cols : K, format);
 }
 
 int ws_validate(const char* what, void* ws, size_t have, size_t need) {

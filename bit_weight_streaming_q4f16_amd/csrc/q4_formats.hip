@@ -113,50 +113,6 @@ __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict_
   }
 }
 
-// q3f16_1: the codes become fp16 pairs without extracting them one by one.  A
-// 32-bit window of a group's 96-bit value, taken at bit 3i - 4 (one shift or
-// funnel shift), holds code i at bits 4-6, code i+1 at 7-9, code i+4 at 16-18
-// and code i+5 at 19-21.  Masking two of those fields and OR-ing in an exponent
-// chosen per field so that the field's lowest bit has place value 1 gives fp16
-// values 2^E + q exactly (E = 6, 3, 10, 7 for the four fields), one AND-OR per
-// pair; v_dot2_f32_f16 multiplies a pair by the matching x pair.  Per group the
-// sum of (2^E + 3) * x over its codes is staged beside x and subtracted once,
-// which leaves sum (q - 3) * x.  Windows at i = 0, 2, 8, 10, 16, 18, 24, 26
-// cover the 32 codes as the pairs (i, i+4), (i+1, i+5).
-constexpr uint32_t kQ3MaskA = 0x00070070u, kQ3MaskB = 0x00380380u;
-constexpr uint32_t kQ3ExpA = 0x64005400u, kQ3ExpB = 0x58004800u;
-
-
-// Sum over one group of (2^E + q) * x.  xq: x of the group as four chunks of
-// four pairs, chunk c at xq[c * cstride] holding the pairs (x[8c+p], x[8c+p+4]).
-// ma, mb: kQ3MaskA and kQ3MaskB held in registers (an instruction with three
-// operands takes no literal constant, and two literals would split each AND-OR
-// into two instructions).
-__device__ __forceinline__ float q3_group_dot(uint32_t w0, uint32_t w1, uint32_t w2,
-                                              const uint4* xq, int cstride, uint32_t ma,
-                                              uint32_t mb) {
-  const uint32_t v[8] = {w0 << 4,
-                         __builtin_amdgcn_alignbit(w1, w0, 2),
-                         __builtin_amdgcn_alignbit(w1, w0, 20),
-                         __builtin_amdgcn_alignbit(w1, w0, 26),
-                         __builtin_amdgcn_alignbit(w2, w1, 12),
-                         __builtin_amdgcn_alignbit(w2, w1, 18),
-                         w2 >> 4,
-                         w2 >> 10};
-  float a = 0.f, b = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint4 xv = xq[c * cstride];
-    a = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c] & ma) | kQ3ExpA), bits<h2_t>(xv.x), a, false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c] & mb) | kQ3ExpB), bits<h2_t>(xv.y), b, false);
-    a = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c + 1] & ma) | kQ3ExpA), bits<h2_t>(xv.z), a,
-                               false);
-    b = __builtin_amdgcn_fdot2(bits<h2_t>((v[2 * c + 1] & mb) | kQ3ExpB), bits<h2_t>(xv.w), b,
-                               false);
-  }
-  return a + b;
-}
-
 typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 
 // Grid: workgroups striding over rows, a team of LPR lanes per row.  A trip of a

@@ -35,10 +35,11 @@ int api_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)
 int api_ok();
 
 // The argument checks of one GEMV (null pointers, shape, alignment, overlap); x_cols:
-// elements per row of x (0: K).
+// elements per row of x (0: K); format: 0 (q4f16_1) or Q4_FMT_Q3F16_1 (the words'
+// alignment and size).
 int gemv_validate(const char* what, const uint32_t* words, const uint16_t* scales,
                   const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K,
-                  int64_t x_cols = 0);
+                  int64_t x_cols = 0, uint32_t format = 0);
 // The workspace check (NULL, size, 16-byte alignment) when `need` bytes are needed.
 int ws_validate(const char* what, void* ws, size_t have, size_t need);
 // Q4_ERR_DEVICE with the HIP error's text.

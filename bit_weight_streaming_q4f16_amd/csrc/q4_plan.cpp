@@ -16,6 +16,7 @@
 #include "q4f16.h"
 #include "q4_internal.h"
 #include "q4_step.h"
+#include "q4_formats.h"
 #include "q4_step_mfma.h"
 #include "q4_tok.h"
 
@@ -49,7 +50,7 @@ std::vector<q4::StepLayer> to_step_layers(const q4_layer* layers, int64_t n) {
   std::vector<q4::StepLayer> v((size_t)n);
   for (int64_t i = 0; i < n; ++i)
     v[(size_t)i] = q4::StepLayer{layers[i].words, layers[i].scales, layers[i].x, layers[i].y,
-                                 layers[i].N, layers[i].K, layers[i].x_op};
+                                 layers[i].N, layers[i].K, layers[i].x_op, layers[i].format};
   return v;
 }
 
@@ -116,7 +117,8 @@ Choice choose(const q4::DeviceInfo& d, const q4_layer* layers, int64_t n, int64_
   c.plans.resize((size_t)n);
   size_t part = 0, glue = 0;
   for (int64_t i = 0; i < n; ++i) {
-    c.plans[(size_t)i] = q4::plan_auto(d, M, layers[i].N, layers[i].K);
+    // (q3f16_1 layers run as one q3 GEMV kernel, with no split-K partials)
+    if (!layers[i].format) c.plans[(size_t)i] = q4::plan_auto(d, M, layers[i].N, layers[i].K);
     part = std::max(part, c.plans[(size_t)i].ws_bytes);
     if (layers[i].x_op) glue = std::max(glue, (size_t)(2 * M * layers[i].K));
   }
@@ -144,9 +146,15 @@ int validate(const char* what, const q4_layer* layers, int64_t n, int64_t M, uin
     snprintf(w, sizeof w, "%s: layers[%lld]", what, (long long)i);
     if (L.x_op > Q4_X_SILU_MUL)
       return q4::api_fail(Q4_ERR_SHAPE, "%s: x_op = %u: unknown", w, L.x_op);
-    if (L.reserved) return q4::api_fail(Q4_ERR_SHAPE, "%s: reserved = %u: must be 0", w, L.reserved);
+    if (L.format != 0 && L.format != Q4_FMT_Q3F16_1)
+      return q4::api_fail(Q4_ERR_SHAPE, "%s: format = %u: must be 0 (q4f16_1) or "
+                          "Q4_FMT_Q3F16_1", w, L.format);
+    if (L.format && M != 1)
+      return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: q3f16_1 layers run at M = 1 only", w);
+    if (L.format && L.K > 32768)
+      return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: q3f16_1 layers take K <= 32768", w);
     if (int rc = q4::gemv_validate(w, L.words, L.scales, L.x, L.y, M, L.N, L.K,
-                                   L.x_op ? 2 * L.K : L.K))
+                                   L.x_op ? 2 * L.K : L.K, L.format))
       return rc;
   }
   return Q4_OK;
@@ -244,6 +252,10 @@ int run(const char* what, const void* plan, void* ws, size_t ws_bytes, hipStream
       if (L.x_op == Q4_X_SILU_MUL) {
         e = q4::launch_silu_mul(L.x, glue, h.M, L.K, s);
         x = glue;
+      }
+      if (e == hipSuccess && L.format == Q4_FMT_Q3F16_1) {
+        e = q4::launch_gemv_q3(*d, L.words, L.scales, x, L.y, L.N, L.K, -1, s);
+        continue;
       }
       const q4::GemvArgs a{L.words, L.scales, x, L.y, h.M, L.N, L.K};
       if (e == hipSuccess) e = q4::launch_gemv(*d, a, en.plan, base + kCtlBytes, s);

@@ -36,6 +36,7 @@ constexpr int kTagOut = 2;   // y also goes to the workspace as epoch-tagged pai
 constexpr int kTagIn = 4;    // x is read from an earlier descriptor's tagged pairs
 constexpr int kPairs = 8;    // workgroup shares are split in pairs of row-steps (even rows)
 constexpr int kSiluMul = 16; // x is [gate | up]: the input is fp16(silu(gate) * up)
+constexpr int kQ3 = 32;      // q3f16_1 words: 12 bytes per group (W is then a byte address)
 
 // One GEMV as the persistent kernel reads it (device-resident table, 80 bytes).
 struct StepDesc {
@@ -65,6 +66,7 @@ struct StepLayer {
   uint16_t* y;
   int64_t N, K;
   uint32_t x_op;          // Q4_X_PLAIN (x is [M][K]) or Q4_X_SILU_MUL (x is [M][2K])
+  uint32_t format;        // 0: q4f16_1, Q4_FMT_Q3F16_1: q3f16_1 (M = 1 only)
   int64_t x_cols() const { return x_op ? 2 * K : K; }
 };
 

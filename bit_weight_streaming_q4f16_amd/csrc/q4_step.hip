@@ -399,11 +399,14 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       wait_lds();
       {
         const uint4 w7 = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
+        const bool q3 = (d.flags & kQ3) != 0;
         for (int g = lane; g < G; g += 64) {
           uint4 xq[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) xq[q] = xb[q * maxG + g];
-          cb[g] = nibble_group_dot(w7, xq, nbs);
+          // q3f16_1: the same chain over codes all 3 (q3_group_dot)
+          cb[g] = q3 ? q3_group_dot(kQ3Zero0, kQ3Zero1, kQ3Zero2, xq, kQ3MaskA, kQ3MaskB)
+                     : nibble_group_dot(w7, xq, nbs);
         }
       }
       // groups past G up to the padded count read x = 0 and bias 0, so the
@@ -435,6 +438,9 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
 
   // -------------------------------------------------------------- compute waves
   const Nibbles nb = make_nibbles();
+  // the q3f16_1 field masks in registers (q3_group_dot)
+  uint32_t q3ma = kQ3MaskA, q3mb = kQ3MaskB;
+  asm volatile("" : "+v"(q3ma), "+v"(q3mb));
   // Issue cursor.  A workgroup's items of all GEMVs, in list order, form one
   // sequence.  In range mode a wave takes the next B of them from an LDS counter
   // whenever it issues a burst, so waves that get their loads back sooner take
@@ -449,7 +455,9 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     int j, s0, cnt, first;       // GEMV, its first row-step here, its item count, and
                                  // the sequence index of its first item
     int N, G, lg, C, r0;         // its shape, and its first row in this workgroup
+    int q3;                      // q3f16_1 words (12 bytes per group)
     int vo[4];                   // this lane's byte offset of each slot in an item's words
+                                 // (16 bytes per group; q3f16_1 loads take 3/4 of it)
   } cu;
 #pragma unroll
   for (int t = 0; t < 4; ++t) cu.vo[t] = 0;
@@ -463,6 +471,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     cu.G = d.G;
     cu.lg = d.lg;
     cu.C = d.C;
+    cu.q3 = (d.flags & kQ3) != 0;
     cu.j = j;
     cu.s0 = s0;
     cu.cnt = s1 - s0;
@@ -548,7 +557,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   struct Burst {
     uint4 rw[B][4];
     uint16_t rs[B][4];
-    int rj[B], rrow[B], rN[B], rG[B], rlg[B], rC[B], rr0[B];
+    int rj[B], rrow[B], rN[B], rG[B], rlg[B], rC[B], rr0[B], rq[B];
   };
   auto issue = [&](Burst& U, int it0) {   // items it0 + p * stride
 #pragma unroll
@@ -559,11 +568,15 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const int G = live ? cu.G : 1;
       const int C = live ? cu.C : 1;
       const int row0 = live ? (cu.s0 + it0 + p * stride - cu.first) * (64 >> lg) : 0;
+      const bool q3 = live && cu.q3;
       const uint64_t left = live ? (uint64_t)(cu.N - row0) * (uint64_t)G : 0;   // groups
-      const uint32_t nw = left * 16 < 0xFFFFFFF0ull ? (uint32_t)(left * 16) : 0xFFFFFFF0u;
+      const uint64_t gb = q3 ? 12 : 16;                                         // bytes per group
+      const uint32_t nw = left * gb < 0xFFFFFFF0ull ? (uint32_t)(left * gb) : 0xFFFFFFF0u;
       const uint32_t ns = left * 2 < 0xFFFFFFF0ull ? (uint32_t)(left * 2) : 0xFFFFFFF0u;
+      const Q4_GLOBAL uint8_t* wrow =
+          (const Q4_GLOBAL uint8_t*)cu.W + (int64_t)row0 * G * (int64_t)gb;
       const __amdgpu_buffer_rsrc_t bw = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint4*>(live ? (const uint4*)(cu.W + (int64_t)row0 * G) : (const uint4*)W_last),
+          const_cast<uint8_t*>(live ? (const uint8_t*)wrow : (const uint8_t*)W_last),
           0, (int)nw, kRsrcFlags);
       const __amdgpu_buffer_rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(live ? (const uint16_t*)(cu.S + (int64_t)row0 * G)
@@ -573,11 +586,24 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       // per-lane part of a buffer address is range-checked, so the scalar offset
       // stays 0; lanes past the end of the matrix (or of an empty resource) read
       // zeros without a memory access.
+      // (q3f16_1: one 12-byte load per group at 3/4 of the slot's 16-byte offset;
+      // the 2 GiB - 16 of a slot past the row becomes 1.5 GiB - 12, past the
+      // resource unless more than 1.5 GiB of the matrix follow the item)
+      if (q3) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, cu.vo[t], 0, kNonTemporal);
-        U.rw[p][t] = make_uint4(v[0], v[1], v[2], v[3]);
-        U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, cu.vo[t] >> 3, 0, 0);
+        for (int t = 0; t < 4; ++t) {
+          const int wo = (cu.vo[t] >> 1) + (cu.vo[t] >> 2);
+          const u32x3_g v = __builtin_amdgcn_raw_buffer_load_b96(bw, wo, 0, kNonTemporal);
+          U.rw[p][t] = make_uint4(v[0], v[1], v[2], 0u);
+          U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, cu.vo[t] >> 3, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, cu.vo[t], 0, kNonTemporal);
+          U.rw[p][t] = make_uint4(v[0], v[1], v[2], v[3]);
+          U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, cu.vo[t] >> 3, 0, 0);
+        }
       }
       U.rj[p] = live ? cu.j : -1;
       U.rrow[p] = row0;
@@ -586,6 +612,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       U.rlg[p] = lg;
       U.rC[p] = C;
       U.rr0[p] = cu.r0;
+      U.rq[p] = q3;
     }
   };
   // Consume a burst in item order; false once an item past the end is reached.
@@ -622,14 +649,18 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           const float off = cb[lpr * t];
 #pragma unroll
           for (int p = 0; p < B; ++p) {
-            const float pd = nibble_group_dot(U.rw[p][t], x, nb) - off;
+            const uint4 w = U.rw[p][t];
+            const float pd =
+                (U.rq[0] ? q3_group_dot(w.x, w.y, w.z, x, q3ma, q3mb) : nibble_group_dot(w, x, nb)) -
+                off;
             acc[p] = __builtin_fmaf(pd, (float)bits<_Float16>(U.rs[p][t]), acc[p]);
           }
         }
       }
 #pragma unroll
       for (int p = 0; p < B; ++p) {
-        const float r = team_sum_lg(acc[p], lg) * kDotUnit;
+        // q3_group_dot is in the products' own units
+        const float r = team_sum_lg(acc[p], lg) * (U.rq[0] ? 1.f : kDotUnit);
         const int row = U.rrow[p] + (lane >> lg);
         if (li == 0 && row < U.rN[p])
           ybuf[xi * ybuf_rows + (row - U.rr0[p])] = bits<uint16_t>((_Float16)r);
@@ -659,11 +690,14 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           uint4 x[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
-          const float pd = nibble_group_dot(U.rw[p][t], x, nb) - cb[lpr * t];
+          const uint4 w = U.rw[p][t];
+          const float pd =
+              (U.rq[p] ? q3_group_dot(w.x, w.y, w.z, x, q3ma, q3mb) : nibble_group_dot(w, x, nb)) -
+              cb[lpr * t];
           acc = __builtin_fmaf(pd, (float)bits<_Float16>(U.rs[p][t]), acc);
         }
       }
-      acc = team_sum_lg(acc, lg) * kDotUnit;
+      acc = team_sum_lg(acc, lg) * (U.rq[p] ? 1.f : kDotUnit);
       if (li == 0 && row < U.rN[p])
         ybuf[xi * ybuf_rows + (row - U.rr0[p])] = bits<uint16_t>((_Float16)acc);
     }
@@ -771,7 +805,7 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
     s.C = C;
     s.steps = (int)((L.N + rps - 1) / rps);
     s.dep = -1;
-    s.flags = L.x_op ? kSiluMul : 0;
+    s.flags = (L.x_op ? kSiluMul : 0) | (L.format ? kQ3 : 0);
     s.tag_in = s.tag_out = 0;
     s.pad[0] = s.pad[1] = 0;
     s.sbase = s.steps / p.grid;
@@ -881,7 +915,7 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
     std::vector<int64_t> first((size_t)n + 1), cum((size_t)n + 1);   // row-steps, bytes
     for (int64_t k = 0; k < n; ++k) {
       const StepDesc& s = p.desc[(size_t)k];
-      const int64_t step_bytes = (int64_t)(64 >> s.lpr_log2) * s.G * 18;
+      const int64_t step_bytes = (int64_t)(64 >> s.lpr_log2) * s.G * ((s.flags & kQ3) ? 14 : 18);
       first[(size_t)k + 1] = first[(size_t)k] + s.steps;
       cum[(size_t)k + 1] = cum[(size_t)k] + step_bytes * s.steps;
     }
@@ -892,7 +926,7 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
       int64_t k = std::upper_bound(cum.begin(), cum.end(), target) - cum.begin() - 1;
       if (k >= n) k = n - 1;
       const StepDesc& s = p.desc[(size_t)k];
-      const int64_t step_bytes = (int64_t)(64 >> s.lpr_log2) * s.G * 18;
+      const int64_t step_bytes = (int64_t)(64 >> s.lpr_log2) * s.G * ((s.flags & kQ3) ? 14 : 18);
       int64_t st = (target - cum[(size_t)k]) / step_bytes;
       if (st > s.steps) st = s.steps;
       cut[(size_t)w] = w == p.grid ? first[(size_t)n] : first[(size_t)k] + st;

@@ -177,16 +177,20 @@ Q4_API int q4_gemv_batched_noalloc(const uint32_t* words, const uint16_t* scales
 #define Q4_X_SILU_MUL 1u
 
 /* One GEMV of a decode step: y = W h(x) (or Y = W h(X) for M rows), h per x_op.
- * y/Y: fp16 [M][N]. */
+ * y/Y: fp16 [M][N].  format: 0 for q4f16_1 (words [N][K/8], 16-byte aligned), or
+ * Q4_FMT_Q3F16_1 (defined with the format variants below; everything-webgpu AI.md,
+ * "Which quantization to recompile with": words [N][3K/32], 4-byte aligned, a
+ * group's three words one 96-bit value, weight = (q - 3) * s), accepted at M = 1
+ * only (Q4_ERR_UNSUPPORTED otherwise); a list may mix the two. */
 typedef struct q4_layer {
-  const uint32_t* words;   /* [N][K/8]  */
+  const uint32_t* words;   /* [N][K/8] (q4f16_1) or [N][3K/32] (q3f16_1) */
   const uint16_t* scales;  /* [N][K/32] */
   const uint16_t* x;       /* [M][K], or [M][2K] with Q4_X_SILU_MUL */
   uint16_t* y;             /* [M][N]    */
   int64_t N;
   int64_t K;
   uint32_t x_op;           /* Q4_X_PLAIN or Q4_X_SILU_MUL */
-  uint32_t reserved;       /* must be 0 */
+  uint32_t format;         /* 0 (q4f16_1) or Q4_FMT_Q3F16_1 */
 } q4_layer;
 
 /* Run every descriptor as its own kernel launch, in list order on the stream. */

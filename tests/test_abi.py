@@ -104,7 +104,7 @@ def test_layer_struct_matches_header():
     assert C.sizeof(q4.Layer) == 56
     text = open(HEADER).read()
     body = re.search(r"typedef struct q4_layer \{(.*?)\} q4_layer;", text, re.S).group(1)
-    fields = re.findall(r"\b(words|scales|x|y|N|K|x_op|reserved)\s*;", body)
+    fields = re.findall(r"\b(words|scales|x|y|N|K|x_op|format)\s*;", body)
     assert fields == [f[0] for f in q4.Layer._fields_]
     for name, val in (("Q4_X_PLAIN", q4.X_PLAIN), ("Q4_X_SILU_MUL", q4.X_SILU_MUL)):
         m = re.search(r"#define %s (\w+)u" % name, text)
@@ -199,8 +199,14 @@ def test_decode_step_x_op_errors(lib):
     layers[1] = q4.Layer(0x50000, 0x60000, 0x40000, 0x70000, 16, 64, 2, 0)   # unknown x_op
     assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2
     assert "layers[1]" in _err(lib) and "x_op" in _err(lib)
-    layers[1] = q4.Layer(0x50000, 0x60000, 0x40000, 0x70000, 16, 64, 1, 7)   # reserved != 0
-    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2 and "reserved" in _err(lib)
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x40000, 0x70000, 16, 64, 1, 7)   # unknown format
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2 and "format" in _err(lib)
+    # q3f16_1 at M > 1
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x90000, 0xA0000, 16, 64, 0, q4.FMT_Q3F16_1)
+    assert lib.q4_decode_step_flags(layers, 2, 2, 0, None, 0, None) == 6 and "M = 1" in _err(lib)
+    # q3f16_1 words need 4-byte alignment only; 2-byte aligned words fail
+    layers[1] = q4.Layer(0x50002, 0x60000, 0x90000, 0xA0000, 16, 64, 0, q4.FMT_Q3F16_1)
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 3 and "4-byte" in _err(lib)
     # with the glue, x spans 2K: a y inside that span overlaps it
     layers[1] = q4.Layer(0x50000, 0x60000, 0x80000, 0x80000 + 2 * 64 + 16, 16, 64, 1, 0)
     assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2 and "overlap" in _err(lib)
