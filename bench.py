@@ -40,6 +40,7 @@ PEAK_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL = "k_step"
 KERNEL_SOURCES = ["bit_weight_streaming_q4f16_amd/csrc/q4_step.hip",
                   "bit_weight_streaming_q4f16_amd/csrc/q4_step.h",
+                  "bit_weight_streaming_q4f16_amd/csrc/q4_device.h",
                   "bit_weight_streaming_q4f16_amd/csrc/q4_internal.h"]
 PROFILE = os.path.join(ROOT, "profiles", "k_step_phi3_decode_sweep")
 # the kernels with committed counter summaries: the headline step, and the small-M
@@ -51,6 +52,7 @@ PROFILED = {
         profile=os.path.join(ROOT, "profiles", "k_step_mfma_2b_decode_sweep_m8"),
         sources=["bit_weight_streaming_q4f16_amd/csrc/q4_step_mfma.hip",
                  "bit_weight_streaming_q4f16_amd/csrc/q4_step_mfma.h",
+                 "bit_weight_streaming_q4f16_amd/csrc/q4_device.h",
                  "bit_weight_streaming_q4f16_amd/csrc/q4_internal.h"],
         model="2b", M=8,
         title="2B-class decode-step weight sweep, M=8 (113 GEMVs, one launch)"),
@@ -818,7 +820,7 @@ def summarize_profiles(d, kernel=KERNEL):
         fh.write("\n")
     lines = [
         f"# {KERNEL_}: {P['title']}", "",
-        "Commands (run from the repository root; TMPDIR=/tmp):", "",
+        "Commands ($REPO: the repository root; run from /tmp with TMPDIR=/tmp):", "",
         *["    " + c for c in commands.splitlines()], "",
         "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
         "| kernel | calls | avg us | min us | max us | % of GPU time |",
