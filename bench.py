@@ -84,6 +84,8 @@ def parse():
                     help="run only a plain device copy of BYTES, 3 times (counter calibration)")
     ap.add_argument("--only-m8", action="store_true",
                     help="time only the 2B-class sweep at M=8 (for profiler runs)")
+    ap.add_argument("--only-mlp", action="store_true",
+                    help="time only one Phi-3 MLP as two q4_gemv calls (for counter runs)")
     ap.add_argument("--only-q3", action="store_true",
                     help="time only the q3f16_1 and mixed-format Phi-3 sweeps")
     ap.add_argument("--only-tokens", action="store_true",
@@ -132,6 +134,10 @@ def main():
     stream = torch.cuda.Stream()          # default priority
     if args.copy_probe:
         copy_probe(torch, q4, stream, args.copy_probe)
+        return
+    if args.only_mlp:
+        print(json.dumps({"mlp_gate_up_down_m1": mlp_only(torch, q4, synth, np, stream)}),
+              flush=True)
         return
     if args.only_q3:
         print(json.dumps({"phi3_sweep_q3f16_1": q3_sweep(torch, q4, synth, np, stream)}),
@@ -519,6 +525,34 @@ def m8_sweep(torch, q4, synth, np, stream, steps=300, warmup=50):
     del descs
     torch.cuda.empty_cache()
     return fig
+
+
+def mlp_only(torch, q4, synth, np, stream, rounds=4):
+    """One Phi-3-mini MLP at M = 1 (gate_up 3072 -> 16384, then down 8192 -> 3072)
+    as two q4_gemv calls, over 13 weight copies (> 512 MB, so every call streams
+    from HBM), `rounds` passes back to back: the workload of the per-GEMV counter
+    profile.  Returns the mean time per MLP."""
+    S = synth
+    shapes = [("gate_up", 16384, 3072), ("down", 3072, 8192)]
+    xs, descs = {}, []
+    for c in range(13):
+        for role, N, K in shapes:
+            if K not in xs:
+                h = S.activations(f"bench/mlp/x{K}", 0, K)
+                xs[K] = torch.from_numpy(h.view(np.int16)).cuda().view(torch.float16)
+            m = S.Matrix(f"bench/mlp/c{c}/{role}", N, K)
+            sc = torch.from_numpy(m.scales().view(np.int16)).cuda().view(torch.float16)
+            descs.append((m.words_torch("cuda"), sc, xs[K],
+                          torch.empty(N, dtype=torch.float16, device="cuda"), N, K))
+    nb = max(q4.q4_workspace_bytes(1, N, K) for _, N, K in shapes)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    b2 = sum(S.algorithmic_bytes(1, N, K) for _, N, K in shapes)
+
+    def fn(i):
+        W, Sc, x, y, N, K = descs[i % len(descs)]
+        q4.q4_gemv(W, Sc, x, y, ws=ws, stream=stream)
+    ms = _timed(torch, stream, fn, rounds * len(descs)) * 2
+    return _fig(b2, ms, copies=len(descs) // 2, calls=rounds * len(descs))
 
 
 def q3_sweep(torch, q4, synth, np, stream, steps=300, warmup=100):
