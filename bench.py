@@ -258,7 +258,8 @@ def main():
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(np, torch, descs, meta)
         if not args.no_configs:
-            result["per_config"] = per_config(torch, q4, synth, np, stream)
+            result["per_config"] = per_config(torch, q4, synth, np, stream,
+                                              cpu=not args.no_cpu_baseline)
             result["decode_tokens"] = token_figures(torch, q4, synth, np, stream, descs, meta)
     print(json.dumps(result), flush=True)
 
@@ -284,7 +285,7 @@ def _fig(nbytes, ms, **kw):
                 **kw)
 
 
-def per_config(torch, q4, synth, np, stream):
+def per_config(torch, q4, synth, np, stream, cpu=False):
     """The other workloads: a single qkv GEMV and one MLP (gate_up then down), each
     over distinct weight copies totalling > 512 MB so every call streams from HBM,
     timed as back-to-back calls and as one decode-step list; and the 2B-class
@@ -428,7 +429,7 @@ def per_config(torch, q4, synth, np, stream):
         del mk
     out["formats_qkv_3072x9216_m1"] = fmts
     out["formats_large_m1"] = formats_large(torch, q4, S, stream)
-    out["twob_sweep_m8"] = m8_sweep(torch, q4, synth, np, stream)
+    out["twob_sweep_m8"] = m8_sweep(torch, q4, synth, np, stream, cpu=cpu)
     out["phi3_sweep_q3f16_1"] = q3_sweep(torch, q4, synth, np, stream)
     return out
 
@@ -481,10 +482,12 @@ def formats_large(torch, q4, S, stream, N=262144, K=3072, calls=20):
     return out
 
 
-def m8_sweep(torch, q4, synth, np, stream, steps=300, warmup=50):
+def m8_sweep(torch, q4, synth, np, stream, steps=300, warmup=50, cpu=False):
     """The 2B-class sweep at M = 8 (113 GEMVs, eight rows of X each) as one
     q4_decode_step call per step; with the small-M kernel's HBM traffic from its
-    committed counter summary while that kernel is unchanged."""
+    committed counter summary while that kernel is unchanged.  cpu: also the CPU
+    oracle over the whole sweep on every usable core (capped at 16), which checks
+    every output of the last step (the GEMV tolerance per row of X)."""
     S = synth
     shapes = synth.sweep_shapes("2b")
     descs = []
@@ -522,9 +525,44 @@ def m8_sweep(torch, q4, synth, np, stream, steps=300, warmup=50):
                us_p90=round(float(np.percentile(per, 90)) * 1e3, 2), statistic="median",
                kernel="k_step_mfma", traffic=tr,
                traffic_over_algorithmic=None if tr is None else round(tr / b5, 4))
+    if cpu:
+        fig["cpu_oracle"] = cpu_sweep_m8(np, torch, descs, b5)
     del descs
     torch.cuda.empty_cache()
     return fig
+
+
+def cpu_sweep_m8(np, torch, descs, nbytes, max_threads=16):
+    """The fp64 oracle over the M = 8 sweep with its OpenMP row loops, once, and the
+    parity of all its outputs against the GPU's last step."""
+    import oracle
+    model, nproc, usable = host_cpu()
+    threads = max(1, min(usable, max_threads))
+    old = oracle.get_threads()
+    worst, checked, tn = 0.0, 0, 0.0
+    try:
+        oracle.set_threads(threads)
+        for W, Sc, X, Y, N, K in descs:
+            w = W.cpu().numpy().view(np.uint32)
+            s = Sc.view(torch.int16).cpu().numpy().view(np.uint16)
+            x = X.view(torch.int16).cpu().numpy().view(np.uint16).reshape(8, K)
+            y = Y.view(torch.int16).cpu().numpy().view(np.float16).astype(np.float64).reshape(8, N)
+            t0 = time.perf_counter()
+            ref = oracle.gemv_f64(w, s, x)
+            tn += time.perf_counter() - t0
+            rn = oracle.row_norms(w, s).max()
+            for m in range(8):
+                tol = 2e-3 * oracle.vec_norm(x[m]) * rn
+                worst = max(worst, float(np.abs(y[m] - ref[m]).max() / tol))
+            checked += 8 * N
+    finally:
+        oracle.set_threads(old)
+    return {"value": round(nbytes / tn / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_step": round(tn, 3), "host_cpu": model,
+            "sample": "the whole M = 8 sweep (113 GEMVs x 8 rows of X), fp64 plain C oracle "
+                      f"with OpenMP row loops on {threads} threads, once",
+            "parity_all_outputs": {"outputs": checked, "max_error_over_tolerance": round(worst, 4),
+                                   "ok": worst <= 1.0}}
 
 
 def mlp_only(torch, q4, synth, np, stream, rounds=4):
