@@ -216,3 +216,20 @@ def test_shape_limits_and_arguments(small):
         plan.run(tokens, -1)
     assert plan.offset(q4.TOKENS_V, W.n) == -1
     assert plan.offset(9) == -1
+
+
+def test_no_blocks_and_odd_vocabulary():
+    """A model with no blocks (the LM head reads the normalised embedding row
+    itself) and an odd vocabulary (the last logit pair half filled): the logits
+    against the oracle, the token the oracle's argmax, three steps equal to three
+    single launches."""
+    W = Weights("noblk", 0, 256, 512, 999)
+    plan, toks, lg = run_tokens(W, 42)
+    check_step(W, plan, 42, lg)
+    assert toks[1] == int(oracle.argmax(lg.reshape(1, -1))[0])
+    seq = [42]
+    for _ in range(3):
+        _, t, _ = run_tokens(W, seq[-1], plan=plan, logits=False)
+        seq.append(t[1])
+    _, t3, _ = run_tokens(W, 42, steps=3, plan=plan, logits=False)
+    assert t3 == seq
