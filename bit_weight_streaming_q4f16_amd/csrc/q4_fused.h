@@ -13,18 +13,24 @@ namespace q4 {
 // The residual add and RMSNorm feeding a GEMV (RMSNorm as the Zero TVM
 // documentation's decode loop places it), folded into that GEMV: h = res_in +
 // delta (delta may be NULL: h = res_in), written to res_out if that is not NULL
-// (distinct from res_in and delta), and y = RMSNorm(h) . W computed as
-// (W . (h * gamma)) / rms(h).  All fp16 vectors of K values, 16-byte aligned.
+// (distinct from res_in and delta), and y = RMSNorm(h) . W.  Factored (exact ==
+// false): computed as (W . (h * gamma)) / rms(h), so that no reduction precedes
+// the staging; rounds differently from the unfolded step.  Exact: every workgroup
+// forms sum(h^2) first and stages RMSNorm(h) as the RMSNorm kernel rounds it, so y
+// is bitwise the RMSNorm kernel followed by the GEMV.  All fp16 vectors of K
+// values, 16-byte aligned.
 struct NormIn {
   const uint16_t* delta = nullptr;
   const uint16_t* res_in = nullptr;
   const uint16_t* gamma = nullptr;
   uint16_t* res_out = nullptr;
   float eps = 0.f;
+  bool exact = false;
 };
 
 // y[i] for i < N of W [N][K] (glu: W has 2N rows and y[i] = silu_mul_h of rows i
-// and N + i) with the input normalised as above; one K slice.
+// and N + i) with the input normalised as above; one K slice.  hipErrorInvalidValue
+// when the staging does not fit a workgroup's LDS (K / 32 x 64 bytes, x 192 exact).
 hipError_t launch_gemv_norm_in(const DeviceInfo& d, const uint32_t* words,
                                const uint16_t* scales, const NormIn& nin, uint16_t* y,
                                int64_t N, int64_t K, bool glu, hipStream_t s);

@@ -86,7 +86,11 @@ __device__ __forceinline__ int slice_begin(int G, int splits, int s) {
 // reduction precedes the staging: x = h * gamma is staged (h = res_in + delta,
 // rounded to fp16 as the RMSNorm kernel rounds it, and written to res_out by
 // workgroup 0), sum(h^2) is formed alongside, and every output is scaled by
-// 1 / sqrt(sum(h^2) / K + eps) before its rounding.  They need one slice.
+// 1 / sqrt(sum(h^2) / K + eps) before its rounding; with nin.exact they stage
+// RMSNorm(h) itself instead, formed as the RMSNorm kernel forms it (h and gamma
+// parked in LDS beside x while the workgroup sums h^2), and scale nothing, so the
+// outputs are bitwise those of the RMSNorm kernel followed by kPlain or kGlu.
+// They need one slice.
 enum : int { kPlain = 0, kGlu = 1, kAffine = 2, kPlainNorm = 3, kGluNorm = 4, kAffineB = 5 };
 
 // A bf16 bit pattern is the upper half of the fp32 with the same value.
@@ -136,7 +140,33 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
   int n = team;
   if (n < N) issue(n, 0);
   float ss = 0.f;                                 // kNin: this thread's sum of h^2
-  for (int i = threadIdx.x; i < 4 * gc; i += kBlock) {
+  float rs = 1.f;                                 // kNin, factored: 1 / rms of h
+  if (kNin && nin.exact) {
+    // one slice (g0 == 0, gc == G): thread t takes blocks t, t + 256, ... as the
+    // RMSNorm kernel does; h and gamma wait in LDS (each thread's own entries)
+    uint4* const hs = xs + 4 * gc;
+    uint4* const gs = xs + 8 * gc;
+    for (int e = threadIdx.x; e < 4 * gc; e += kBlock) {
+      h8_t v = bits<h8_t>(reinterpret_cast<const uint4*>(nin.res_in)[e]);
+      if (nin.delta) v = v + bits<h8_t>(reinterpret_cast<const uint4*>(nin.delta)[e]);
+      if (nin.res_out && blockIdx.x == 0) reinterpret_cast<uint4*>(nin.res_out)[e] = bits<uint4>(v);
+      gs[e] = reinterpret_cast<const uint4*>(nin.gamma)[e];
+      hs[e] = bits<uint4>(v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float f = (float)v[k];
+        ss = __builtin_fmaf(f, f, ss);
+      }
+    }
+    const float r = rms_scale(block_sum(ss, ssw), G * 32, nin.eps);
+    for (int e = threadIdx.x; e < 4 * gc; e += kBlock) {
+      const h8_t v = bits<h8_t>(hs[e]), gm = bits<h8_t>(gs[e]);
+      h8_t o;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = norm_h(v[k], r, gm[k]);
+      xs[(e & 3) * gc + (e >> 2)] = pair_order(bits<uint4>(o));
+    }
+  } else for (int i = threadIdx.x; i < 4 * gc; i += kBlock) {
     const int g = i >> 2, j = i & 3;
     if constexpr (kNin) {
       const int64_t e = (int64_t)(g0 + g) * 4 + j;   // x[8e .. 8e + 7]
@@ -156,7 +186,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
       xs[j * gc + g] = pair_order(X[(int64_t)(g0 + g) * 4 + j]);
     }
   }
-  if constexpr (kNin) {
+  if (kNin && !nin.exact) {
     ss = team_sum<64>(ss);
     if ((threadIdx.x & 63) == 0) ssw[threadIdx.x >> 6] = ss;
   }
@@ -175,8 +205,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
     }
   }
   __syncthreads();
-  float rs = 1.f;                                 // kNin: 1 / rms of h
-  if constexpr (kNin) {
+  if (kNin && !nin.exact) {
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < kBlock / 64; ++w) tot += ssw[w];
@@ -404,7 +433,8 @@ hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, cons
   const int64_t cap = (int64_t)d.cus * (kNin ? 2 : 8);
   if (blocks > cap) blocks = cap;
   const int64_t gmax = (G + p.splits - 1) / p.splits;
-  const size_t lds = (size_t)gmax * (MODE == kAffine || MODE == kAffineB ? 68 : 64);
+  const size_t lds =
+      (size_t)gmax * (MODE == kAffine || MODE == kAffineB ? 68 : kNin && nin.exact ? 192 : 64);
   const dim3 grid((unsigned)blocks, (unsigned)p.splits);
   if (hipError_t e = allow_lds(k_gemv_m1<LPR, UNR, MODE>, lds)) return e;
   hipLaunchKernelGGL((k_gemv_m1<LPR, UNR, MODE>), grid, dim3(kBlock), lds, s,
@@ -540,7 +570,7 @@ hipError_t launch_gemv_affine(const DeviceInfo& d, const uint32_t* W, const uint
 hipError_t launch_gemv_norm_in(const DeviceInfo& d, const uint32_t* words,
                                const uint16_t* scales, const NormIn& nin, uint16_t* y,
                                int64_t N, int64_t K, bool glu, hipStream_t s) {
-  if (!nin.res_in || !nin.gamma || (size_t)(K / 32) * 64 > d.lds_per_block)
+  if (!nin.res_in || !nin.gamma || (size_t)(K / 32) * (nin.exact ? 192 : 64) > d.lds_per_block)
     return hipErrorInvalidValue;
   const GemvArgs a{words, scales, nullptr, y, 1, N, K};
   const GemvPlan p = plan_splits(d, 1, glu ? 2 * N : N, K, 1);

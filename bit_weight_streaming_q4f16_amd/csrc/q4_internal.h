@@ -100,6 +100,33 @@ __device__ __forceinline__ _Float16 silu_mul_h(_Float16 g, _Float16 u) {
   return (_Float16)p;
 }
 
+// RMSNorm of a row of K values (Zero TVM documentation, "Decode loop"), in the
+// pieces every kernel that forms it shares, so that they all get the same bits:
+// a 256-thread workgroup in which thread t takes the blocks of 8 values t, t + 256,
+// ... and sums their squares with fmaf in index order; block_sum adds the 256
+// partial sums (a butterfly within each wave, then the four waves in order);
+// rms_scale is 1 / sqrt(sum / K + eps); norm_h rounds v * r * gamma to fp32 and
+// then to fp16 (the empty asm keeps the compiler from fusing the product and the
+// conversion into one mixed-precision instruction, which would round once).
+__device__ __forceinline__ float block_sum(float v, float* red) {   // red: 4 floats
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float t = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return t;
+}
+__device__ __forceinline__ float rms_scale(float sum_sq, int K, float eps) {
+  return 1.f / __builtin_sqrtf(sum_sq / (float)K + eps);
+}
+__device__ __forceinline__ _Float16 norm_h(_Float16 v, float r, _Float16 g) {
+  float p = (float)v * r * (float)g;
+  asm volatile("" : "+v"(p));
+  return (_Float16)p;
+}
+
 // out[m][i] = silu_mul_h(gu[m][i], gu[m][H + i]); H % 8 == 0, 16-byte aligned.
 hipError_t launch_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t H,
                            hipStream_t s);

@@ -9,18 +9,6 @@
 namespace q4 {
 namespace {
 
-// Sum over the 256 threads of a workgroup (every thread gets the total).
-__device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  const float t = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  return t;
-}
-
 // One thread per 32-weight group of the chosen row: (q - 7) * s is exact in fp32
 // (a 4-bit integer times an fp16), so each output is rounded once.
 __global__ __launch_bounds__(kBlock) void k_embed_rows(const uint4* __restrict__ words,
@@ -51,9 +39,11 @@ __global__ __launch_bounds__(kBlock) void k_embed_rows(const uint4* __restrict__
   }
 }
 
-// RMSNorm of one row per workgroup, blocks of 8 halves; with `delta`, the row is
-// first res_out = fp16(res_in + delta) (a native fp16 add: rounded once).  The
-// second pass re-reads what this thread read or wrote in the first.
+// RMSNorm of one row per workgroup, blocks of 8 halves, in the pieces of
+// q4_internal.h (the GEMVs that fold the norm in stage the same bits); with
+// `delta`, the row is first res_out = fp16(res_in + delta) (a native fp16 add:
+// rounded once).  The second pass re-reads what this thread read or wrote in the
+// first.
 __global__ __launch_bounds__(kBlock) void k_rmsnorm(const uint4* __restrict__ delta,
                                                     const uint4* res_in,
                                                     const uint4* __restrict__ gamma, float eps,
@@ -77,13 +67,13 @@ __global__ __launch_bounds__(kBlock) void k_rmsnorm(const uint4* __restrict__ de
     }
   }
   const float tot = block_sum(ss, red);
-  const float rs = 1.f / __builtin_sqrtf(tot / (float)(blocks * 8) + eps);
+  const float rs = rms_scale(tot, blocks * 8, eps);
   const uint4* src = delta ? r : x;
   for (int b = threadIdx.x; b < blocks; b += kBlock) {
     const h8_t v = bits<h8_t>(src[b]), g = bits<h8_t>(gamma[b]);
     h8_t o;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (_Float16)((float)v[i] * rs * (float)g[i]);
+    for (int i = 0; i < 8; ++i) o[i] = norm_h(v[i], rs, g[i]);
     out[row * blocks + b] = bits<uint4>(o);
   }
 }

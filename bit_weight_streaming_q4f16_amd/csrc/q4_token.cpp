@@ -1,18 +1,19 @@
 // Decode tokens end to end: the decode loop of the Zero TVM documentation
 // ("Decode loop") over q4f16_1 weights, with attention at a single position.
 //
-// One step is a fixed sequence of kernels: embedding row, RMSNorm, then per block
-// qkv, o (reading the value part of qkv), residual add + RMSNorm, gate/up,
+// One step is a fixed sequence of operations: embedding row, RMSNorm, then per
+// block qkv, o (reading the value part of qkv), residual add + RMSNorm, gate/up,
 // SiLU-multiply, down, residual add + RMSNorm, then the LM head and the argmax.
 // Each projection is one GEMV kernel (one kernel per GEMV is the faster choice
 // for a chain in which every GEMV waits for the one before it).  Where gate/up
-// needs no split-K pass the glue runs inside it (q4_fused.h): six kernels per
-// block instead of seven, with bitwise the same results.  With the model option
-// Q4_MODEL_FACTORED_NORM every residual add + RMSNorm is folded into the GEMV it
-// feeds (q4_fused.h): four kernels per block, results within rounding of the
-// unfolded step, not bitwise.  Every buffer between the kernels lives in the
-// caller's workspace; the residual is updated in place (unfolded) or alternates
-// between two buffers (folded).  A multi-step decode captures one step, with two one-thread kernels
+// needs no split-K pass the glue runs inside it, and every residual add + RMSNorm
+// runs inside the GEMV it feeds (q4_fused.h): four kernels per block instead of
+// seven, with bitwise the same results (the separate norm kernel where a GEMV
+// needs split-K or its staging does not fit LDS).  With the model option
+// Q4_MODEL_FACTORED_NORM the norm is folded in factored form instead: no
+// reduction before the staging, results within rounding of the defined step, not
+// bitwise.  Every buffer between the kernels lives in the caller's workspace; the
+// residual alternates between two buffers.  A multi-step decode captures one step, with two one-thread kernels
 // that take the step's token from and put the next one into the caller's token
 // array at a device-side counter, as a HIP graph and replays it: no host
 // round trip between tokens (the pages' host-side lever is to submit a whole
@@ -58,7 +59,7 @@ Layout layout_for(const q4::DeviceInfo& d, const q4_model& m) {
     return o;
   };
   L.res = take(2 * m.D);
-  L.res2 = take(2 * m.D);      // the factored-norm chain's second residual buffer
+  L.res2 = take(2 * m.D);      // the residual's second buffer (it alternates)
   L.h = take(2 * m.D);
   L.qkv_out = take(2 * 3 * m.D);
   L.attn = take(2 * m.D);
@@ -150,58 +151,55 @@ hipError_t enqueue_step(const q4::DeviceInfo& d, const q4_model& m, const Layout
     if (hipError_t e_ = (call)) return e_;    \
   } while (0)
   Q4_TRY(q4::launch_embed_rows(m.embed.words, m.embed.scales, m.V, m.D, tok_in, 1, res, s));
-  const uint16_t* g0 = m.n_blocks ? m.blocks[0].attn_norm : m.final_norm;
-  if (m.options & Q4_MODEL_FACTORED_NORM) {
-    // every residual add + RMSNorm folded into the GEMV it feeds (q4_fused.h);
-    // the residual alternates between two buffers (its GEMV's workgroups all read
-    // the old one while one of them writes the new one)
-    uint16_t *cur = res, *other = buf(L.res2);
-    q4::NormIn pend;                // the add + norm the next normed GEMV applies
-    pend.gamma = g0;
-    pend.eps = m.eps;
-    auto normed = [&](const q4_weight& w, uint16_t* y, int64_t n_out, bool glu) {
-      q4::NormIn a = pend;
-      a.res_in = cur;
-      a.res_out = pend.delta ? other : nullptr;
-      const hipError_t e = q4::launch_gemv_norm_in(d, w.words, w.scales, a, y, n_out, w.K, glu, s);
-      if (pend.delta) std::swap(cur, other);
-      return e;
-    };
-    for (int64_t b = 0; b < m.n_blocks; ++b) {
-      const q4_block& B = m.blocks[b];
-      const uint16_t* next = b + 1 < m.n_blocks ? m.blocks[b + 1].attn_norm : m.final_norm;
-      Q4_TRY(normed(B.qkv, qkv, 3 * m.D, false));
-      Q4_TRY(gemv(B.o, L.o, qkv + 2 * m.D, attn));
-      pend.delta = attn;
-      pend.gamma = B.ffn_norm;
-      Q4_TRY(normed(B.gate_up, hf, m.F, true));
-      Q4_TRY(gemv(B.down, L.down, hf, dn));
-      pend.delta = dn;
-      pend.gamma = next;
+  // Every residual add + RMSNorm is folded into the GEMV it feeds (q4_fused.h)
+  // where that GEMV runs as one K slice: exact (the default: bitwise the norm
+  // kernel followed by the GEMV) when the staging fits LDS, else as the separate
+  // norm kernel; factored (Q4_MODEL_FACTORED_NORM) always.  The residual
+  // alternates between two buffers (a folded GEMV's workgroups all read the old
+  // one while one of them writes the new one).
+  const bool factored = (m.options & Q4_MODEL_FACTORED_NORM) != 0;
+  const bool exact_fits = (size_t)(m.D / 32) * 192 <= d.lds_per_block;
+  uint16_t *cur = res, *other = buf(L.res2);
+  q4::NormIn pend;                  // the add + norm that the next normed GEMV applies
+  pend.gamma = m.n_blocks ? m.blocks[0].attn_norm : m.final_norm;
+  pend.eps = m.eps;
+  pend.exact = !factored;
+  // y = W . RMSNorm(pending residual); glu: the gate/up GEMV with the glue (y = hf)
+  auto normed = [&](const q4_weight& w, const q4::GemvPlan& p, uint16_t* y, int64_t n_out,
+                    bool glu) {
+    q4::NormIn a = pend;
+    a.res_in = cur;
+    a.res_out = pend.delta ? other : nullptr;
+    hipError_t e;
+    if (factored || (p.splits == 1 && exact_fits)) {
+      e = q4::launch_gemv_norm_in(d, w.words, w.scales, a, y, n_out, w.K, glu, s);
+    } else {
+      e = q4::launch_rmsnorm(a.delta, a.res_in, a.gamma, m.eps, 1, m.D, a.res_out, h, s);
+      if (e == hipSuccess && !glu) e = gemv(w, p, h, y);
+      if (e == hipSuccess && glu && L.fuse)
+        e = q4::launch_gemv_glu(d, w.words, w.scales, h, y, m.F, m.D, p, s);
+      if (e == hipSuccess && glu && !L.fuse) {
+        e = gemv(w, p, h, gu);
+        if (e == hipSuccess) e = q4::launch_silu_mul(gu, y, 1, m.F, s);
+      }
     }
-    Q4_TRY(normed(m.lm_head, lg, m.V, false));
-    Q4_TRY(q4::launch_argmax(lg, 1, m.V, tok_out, s));
-    return hipSuccess;
-  }
-  Q4_TRY(q4::launch_rmsnorm(nullptr, res, g0, m.eps, 1, m.D, nullptr, h, s));
+    if (pend.delta) std::swap(cur, other);
+    return e;
+  };
   for (int64_t b = 0; b < m.n_blocks; ++b) {
     const q4_block& B = m.blocks[b];
     const uint16_t* next = b + 1 < m.n_blocks ? m.blocks[b + 1].attn_norm : m.final_norm;
-    Q4_TRY(gemv(B.qkv, L.qkv, h, qkv));
+    Q4_TRY(normed(B.qkv, L.qkv, qkv, 3 * m.D, false));
     // attention at a single position: its output is the value vector
     Q4_TRY(gemv(B.o, L.o, qkv + 2 * m.D, attn));
-    Q4_TRY(q4::launch_rmsnorm(attn, res, B.ffn_norm, m.eps, 1, m.D, res, h, s));
-    if (L.fuse) {
-      Q4_TRY(q4::launch_gemv_glu(d, B.gate_up.words, B.gate_up.scales, h, hf, m.F, m.D,
-                                 L.gate_up, s));
-    } else {
-      Q4_TRY(gemv(B.gate_up, L.gate_up, h, gu));
-      Q4_TRY(q4::launch_silu_mul(gu, hf, 1, m.F, s));
-    }
+    pend.delta = attn;
+    pend.gamma = B.ffn_norm;
+    Q4_TRY(normed(B.gate_up, L.gate_up, hf, m.F, true));
     Q4_TRY(gemv(B.down, L.down, hf, dn));
-    Q4_TRY(q4::launch_rmsnorm(dn, res, next, m.eps, 1, m.D, res, h, s));
+    pend.delta = dn;
+    pend.gamma = next;
   }
-  Q4_TRY(gemv(m.lm_head, L.lm_head, h, lg));
+  Q4_TRY(normed(m.lm_head, L.lm_head, lg, m.V, false));
   Q4_TRY(q4::launch_argmax(lg, 1, m.V, tok_out, s));
 #undef Q4_TRY
   return hipSuccess;
