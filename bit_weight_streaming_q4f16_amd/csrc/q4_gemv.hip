@@ -138,53 +138,72 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
     }
   };
   int n = team;
+  // kNin (one slice: g0 == 0, gc == G): thread t stages blocks of 8 values t, t +
+  // 256, ... (the RMSNorm kernel's order); its first two blocks' residual, delta and
+  // gamma are requested before the weights, so that they do not queue behind them
+  constexpr int PRE = kNin ? 2 : 1;
+  const uint4* const nres = reinterpret_cast<const uint4*>(nin.res_in);
+  const uint4* const ndel = reinterpret_cast<const uint4*>(nin.delta);
+  const uint4* const ngam = reinterpret_cast<const uint4*>(nin.gamma);
+  uint4 pr[PRE], pd[PRE], pg[PRE];
+  if constexpr (kNin) {
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) {
+      const int e = threadIdx.x + j * kBlock;
+      if (e < 4 * gc) {
+        pr[j] = nres[e];
+        pd[j] = ndel ? ndel[e] : make_uint4(0u, 0u, 0u, 0u);
+        pg[j] = ngam[e];
+      }
+    }
+  }
   if (n < N) issue(n, 0);
   float ss = 0.f;                                 // kNin: this thread's sum of h^2
   float rs = 1.f;                                 // kNin, factored: 1 / rms of h
-  if (kNin && nin.exact) {
-    // one slice (g0 == 0, gc == G): thread t takes blocks t, t + 256, ... as the
-    // RMSNorm kernel does; h and gamma wait in LDS (each thread's own entries)
-    uint4* const hs = xs + 4 * gc;
-    uint4* const gs = xs + 8 * gc;
-    for (int e = threadIdx.x; e < 4 * gc; e += kBlock) {
-      h8_t v = bits<h8_t>(reinterpret_cast<const uint4*>(nin.res_in)[e]);
-      if (nin.delta) v = v + bits<h8_t>(reinterpret_cast<const uint4*>(nin.delta)[e]);
-      if (nin.res_out && blockIdx.x == 0) reinterpret_cast<uint4*>(nin.res_out)[e] = bits<uint4>(v);
-      gs[e] = reinterpret_cast<const uint4*>(nin.gamma)[e];
-      hs[e] = bits<uint4>(v);
+  // exact: h and gamma wait in LDS (each thread's own entries) until the sum of
+  // h^2 is known; factored: h * gamma staged at once
+  uint4* const hs = xs + 4 * gc;
+  uint4* const gs = xs + 8 * gc;
+  auto stage_norm = [&](int e, uint4 r, uint4 dl, uint4 gw) {
+    h8_t v = bits<h8_t>(r);
+    if (ndel) v = v + bits<h8_t>(dl);
+    if (nin.res_out && blockIdx.x == 0) reinterpret_cast<uint4*>(nin.res_out)[e] = bits<uint4>(v);
+    const h8_t gm = bits<h8_t>(gw);
+    h8_t o;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float f = (float)v[k];
-        ss = __builtin_fmaf(f, f, ss);
-      }
+    for (int k = 0; k < 8; ++k) {
+      const float f = (float)v[k];
+      ss = __builtin_fmaf(f, f, ss);
+      o[k] = (_Float16)(f * (float)gm[k]);
     }
-    const float r = rms_scale(block_sum(ss, ssw), G * 32, nin.eps);
-    for (int e = threadIdx.x; e < 4 * gc; e += kBlock) {
-      const h8_t v = bits<h8_t>(hs[e]), gm = bits<h8_t>(gs[e]);
-      h8_t o;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = norm_h(v[k], r, gm[k]);
+    if (nin.exact) {
+      gs[e] = gw;
+      hs[e] = bits<uint4>(v);
+    } else {
       xs[(e & 3) * gc + (e >> 2)] = pair_order(bits<uint4>(o));
     }
-  } else for (int i = threadIdx.x; i < 4 * gc; i += kBlock) {
-    const int g = i >> 2, j = i & 3;
-    if constexpr (kNin) {
-      const int64_t e = (int64_t)(g0 + g) * 4 + j;   // x[8e .. 8e + 7]
-      h8_t v = bits<h8_t>(reinterpret_cast<const uint4*>(nin.res_in)[e]);
-      if (nin.delta) v = v + bits<h8_t>(reinterpret_cast<const uint4*>(nin.delta)[e]);
-      if (nin.res_out && blockIdx.x == 0) reinterpret_cast<uint4*>(nin.res_out)[e] = bits<uint4>(v);
-      const h8_t gm = bits<h8_t>(reinterpret_cast<const uint4*>(nin.gamma)[e]);
-      h8_t o;
+  };
+  if constexpr (kNin) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float f = (float)v[k];
-        ss = __builtin_fmaf(f, f, ss);
-        o[k] = (_Float16)(f * (float)gm[k]);
-      }
-      xs[j * gc + g] = pair_order(bits<uint4>(o));
-    } else {
-      xs[j * gc + g] = pair_order(X[(int64_t)(g0 + g) * 4 + j]);
+    for (int j = 0; j < PRE; ++j) {
+      const int e = threadIdx.x + j * kBlock;
+      if (e < 4 * gc) stage_norm(e, pr[j], pd[j], pg[j]);
     }
+    for (int e = threadIdx.x + PRE * kBlock; e < 4 * gc; e += kBlock)
+      stage_norm(e, nres[e], ndel ? ndel[e] : make_uint4(0u, 0u, 0u, 0u), ngam[e]);
+    if (nin.exact) {
+      const float r = rms_scale(block_sum(ss, ssw), G * 32, nin.eps);
+      for (int e = threadIdx.x; e < 4 * gc; e += kBlock) {
+        const h8_t v = bits<h8_t>(hs[e]), gm = bits<h8_t>(gs[e]);
+        h8_t o;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = norm_h(v[k], r, gm[k]);
+        xs[(e & 3) * gc + (e >> 2)] = pair_order(bits<uint4>(o));
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < 4 * gc; i += kBlock)
+      xs[(i & 3) * gc + (i >> 2)] = pair_order(X[(int64_t)g0 * 4 + i]);
   }
   if (kNin && !nin.exact) {
     ss = team_sum<64>(ss);
