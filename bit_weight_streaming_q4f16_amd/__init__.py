@@ -41,6 +41,8 @@ FMT_AF4_G64_F16 = 4   # the same with fp16 scales and biases (extra variant)
 FMT_LOAD_STAGED = 0x100   # OR-ed into FMT_Q3F16_1: force one way of loading
 FMT_LOAD_DIRECT = 0x200
 MODEL_FACTORED_NORM = 0x1   # q4_model.options: norms folded into the GEMVs they feed
+NORM_GLU = 0x1              # q4_gemv_norm flags
+NORM_EXACT = 0x2
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
           4: "Q4_ERR_WORKSPACE", 5: "Q4_ERR_DEVICE", 6: "Q4_ERR_UNSUPPORTED", 7: "Q4_ERR_TIMEOUT"}
@@ -426,9 +428,10 @@ def q4_add_rmsnorm(delta, res_in, gamma, eps: float, res_out=None, out=None, str
 
 
 def q4_gemv_norm(words, scales, res_in, gamma, eps: float, delta=None, res_out=None, y=None,
-                 glu: bool = False, stream=None):
-    """y = W . RMSNorm(fp16(res_in + delta)) * gamma with the norm's scalar applied
-    after the product (q4_gemv_norm); glu: W holds gate | up rows and
+                 glu: bool = False, exact: bool = False, stream=None):
+    """y = W . RMSNorm(fp16(res_in + delta)) * gamma in one kernel (q4_gemv_norm);
+    exact: the normalised input staged as q4_rmsnorm forms it, else the norm's
+    scalar applied after the product; glu: W holds gate | up rows and
     y = fp16(silu(gate) * up)."""
     torch = _torch()
     rows, K = words.shape[0], 8 * words.shape[1]
@@ -436,7 +439,8 @@ def q4_gemv_norm(words, scales, res_in, gamma, eps: float, delta=None, res_out=N
     if y is None:
         y = torch.empty(N, dtype=torch.float16, device=words.device)
     _check(load().q4_gemv_norm(_ptr(words), _ptr(scales), _ptr(res_in), _ptr(delta), _ptr(gamma),
-                               float(eps), _ptr(res_out), _ptr(y), N, K, 1 if glu else 0,
+                               float(eps), _ptr(res_out), _ptr(y), N, K,
+                               (NORM_GLU if glu else 0) | (NORM_EXACT if exact else 0),
                                _stream(stream)))
     return y
 

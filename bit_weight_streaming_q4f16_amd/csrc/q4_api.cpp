@@ -342,11 +342,13 @@ int q4_add_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const uint16_t
 
 int q4_gemv_norm(const uint32_t* words, const uint16_t* scales, const uint16_t* res_in,
                  const uint16_t* delta, const uint16_t* gamma, float eps, uint16_t* res_out,
-                 uint16_t* y, int64_t N, int64_t K, uint32_t glu, q4_stream_t stream) {
+                 uint16_t* y, int64_t N, int64_t K, uint32_t flags, q4_stream_t stream) {
   const char* what = "q4_gemv_norm";
   if (!words || !scales || !res_in || !gamma || !y)
     return fail(Q4_ERR_NULL, "%s: NULL pointer (only delta and res_out may be NULL)", what);
-  if (glu > 1) return fail(Q4_ERR_SHAPE, "%s: glu = %u: must be 0 or 1", what, glu);
+  if (flags & ~(Q4_NORM_GLU | Q4_NORM_EXACT))
+    return fail(Q4_ERR_SHAPE, "%s: flags = 0x%x: unknown bits", what, flags);
+  const bool glu = (flags & Q4_NORM_GLU) != 0, exact = (flags & Q4_NORM_EXACT) != 0;
   if (int rc = check_shape(glu ? 2 * N : N, K)) return fail(rc, "%s: %s", what, g_error.c_str());
   if (!(eps >= 0.f)) return fail(Q4_ERR_SHAPE, "%s: eps must be >= 0", what);
   if (!aligned(words, 16) || !aligned(scales, 2) || !aligned(res_in, 16) || !aligned(gamma, 16) ||
@@ -354,9 +356,9 @@ int q4_gemv_norm(const uint32_t* words, const uint16_t* scales, const uint16_t* 
     return fail(Q4_ERR_ALIGN, "%s: misaligned pointer", what);
   const q4::DeviceInfo* d = q4::device_info();
   if (!d) return fail(Q4_ERR_DEVICE, "%s: no HIP device", what);
-  if ((size_t)(K / 32) * 64 > d->lds_per_block)
-    return fail(Q4_ERR_UNSUPPORTED, "%s: K = %lld: the input does not fit in LDS", what,
-                (long long)K);
+  if ((size_t)(K / 32) * (exact ? 192 : 64) > d->lds_per_block)
+    return fail(Q4_ERR_UNSUPPORTED, "%s: K = %lld: the %s staging does not fit in LDS", what,
+                (long long)K, exact ? "exact" : "factored");
   const int64_t rows = glu ? 2 * N : N, vb = 2 * K;
   const int64_t wb = rows * K / 2, sb = rows * K / 16, yb = 2 * N;
   auto any = [&](const void* p, int64_t pb, std::initializer_list<std::pair<const void*, int64_t>> l) {
@@ -375,7 +377,8 @@ int q4_gemv_norm(const uint32_t* words, const uint16_t* scales, const uint16_t* 
   nin.gamma = gamma;
   nin.res_out = res_out;
   nin.eps = eps;
-  hipError_t e = q4::launch_gemv_norm_in(*d, words, scales, nin, y, N, K, glu != 0,
+  nin.exact = exact;
+  hipError_t e = q4::launch_gemv_norm_in(*d, words, scales, nin, y, N, K, glu,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : device_error(e, what);
 }

@@ -331,23 +331,32 @@ Q4_API int q4_add_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const u
                           float eps, int64_t M, int64_t K, uint16_t* res_out, uint16_t* out,
                           q4_stream_t stream);
 
-/* q4_gemv_norm: the residual add, RMSNorm and the GEMV it feeds, in one kernel with
- * the norm's scalar applied after the product (Zero TVM documentation, "Decode
- * loop": addNorm followed by the next projection; the GEMV of
- * Q4_MODEL_FACTORED_NORM).  h = fp16(res_in + delta) (rounded once; delta NULL:
- * h = res_in), written to res_out unless that is NULL; the GEMV stages
- * fp16(h * gamma), forms sum(h^2) in fp32 alongside, and scales each fp32 output by
- * 1 / sqrt(sum(h^2) / K + eps) before rounding it.  glu == 0: W is [N][K] and
- * y[n] = fp16(...) for n < N; glu == 1: W is [2N][K] (gate rows, then up rows) and
- * y[i] = fp16(silu(fp16(gate_i)) * fp16(up_i)) for i < N.  It differs from
- * q4_add_rmsnorm followed by q4_gemv by where the normalised input is rounded
- * (there after the scaling, here before it): within the GEMV tolerance plus one
- * fp16 rounding of each input term, not bitwise.  res_in, delta, gamma, res_out:
- * fp16 [K], 16-byte aligned; res_out must not overlap anything else; y must not
- * overlap an input.  K % 32 == 0 and the K values fit in LDS (K <= 81920). */
+/* q4_gemv_norm: the residual add, RMSNorm and the GEMV it feeds, in one kernel
+ * (Zero TVM documentation, "Decode loop": addNorm followed by the next
+ * projection).  h = fp16(res_in + delta) (rounded once; delta NULL: h = res_in),
+ * written to res_out unless that is NULL.  flags:
+ *   Q4_NORM_GLU: W is [2N][K] (gate rows, then up rows) and
+ *     y[i] = fp16(silu(fp16(gate_i)) * fp16(up_i)) for i < N; else W is [N][K] and
+ *     y[n] = fp16(...) for n < N.
+ *   Q4_NORM_EXACT: the GEMV stages RMSNorm(h) * gamma formed as q4_rmsnorm forms
+ *     it (the same sum of squares, order and rounding), so y is bitwise q4_add_rmsnorm
+ *     followed by q4_gemv (and q4_silu_mul) wherever q4_gemv runs as one K slice
+ *     (q4_workspace_bytes(1, rows, K) == 0); K <= 27296 (192 bytes of LDS per 32
+ *     inputs; the decode step's default).
+ *   otherwise (factored; the GEMV of Q4_MODEL_FACTORED_NORM): the GEMV stages
+ *     fp16(h * gamma), forms sum(h^2) in fp32 alongside, and scales each fp32 output
+ *     by 1 / sqrt(sum(h^2) / K + eps) before rounding it: no reduction precedes the
+ *     staging.  It differs from the unfolded step by where the normalised input is
+ *     rounded (there after the scaling, here before it): within the GEMV tolerance
+ *     plus one fp16 rounding of each input term, not bitwise.  K <= 81920.
+ * res_in, delta, gamma, res_out: fp16 [K], 16-byte aligned; res_out must not
+ * overlap anything else; y must not overlap an input.  K % 32 == 0; a K beyond the
+ * limit is Q4_ERR_UNSUPPORTED. */
+#define Q4_NORM_GLU 0x1u
+#define Q4_NORM_EXACT 0x2u
 Q4_API int q4_gemv_norm(const uint32_t* words, const uint16_t* scales, const uint16_t* res_in,
                         const uint16_t* delta, const uint16_t* gamma, float eps,
-                        uint16_t* res_out, uint16_t* y, int64_t N, int64_t K, uint32_t glu,
+                        uint16_t* res_out, uint16_t* y, int64_t N, int64_t K, uint32_t flags,
                         q4_stream_t stream);
 
 /* q4_argmax (Zero TVM documentation, "Decode loop": greedy sampling of the next

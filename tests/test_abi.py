@@ -160,6 +160,18 @@ def test_batched_and_splitk_argument_errors(lib):
     assert lib.q4_workspace_bytes(1, 16, 48) == 0
 
 
+def test_gemv_norm_argument_errors(lib):
+    f = lib.q4_gemv_norm
+    G = P(0x50000)
+    # flags and pointers are checked before any device query: no GPU needed
+    assert f(A, B, X, None, G, 1e-5, None, Y, 16, 64, 4, None) == 2 and "flags" in _err(lib)
+    assert f(A, B, X, None, None, 1e-5, None, Y, 16, 64, 2, None) == 1
+    text = open(HEADER).read()
+    for name, val in (("Q4_NORM_GLU", q4.NORM_GLU), ("Q4_NORM_EXACT", q4.NORM_EXACT)):
+        m = re.search(r"#define %s (\w+)u" % name, text)
+        assert m and int(m.group(1), 0) == val, name
+
+
 def test_noalloc_gemv_argument_errors(lib):
     f = lib.q4_gemv_batched_noalloc
     f.argtypes = [C.c_void_p] * 4 + [C.c_int64] * 3 + [C.c_void_p]

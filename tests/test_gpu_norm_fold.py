@@ -1,9 +1,17 @@
-"""The folded residual add + RMSNorm + GEMV (q4_gemv_norm, the GEMV of the
-factored-norm decode step) against the oracle's unfolded composition, element by
-element: fp16(res_in + delta) exactly as the oracle rounds it, and every output
-within a bound derived from what differs -- the input rounded to fp16 before the
-norm's scaling instead of after it (one fp16 rounding of each input term on each
-side), the fp32 GEMV, the fp32 norm scalar, and the output rounding."""
+"""The folded residual add + RMSNorm + GEMV (q4_gemv_norm).
+
+Factored (the GEMV of the factored-norm decode step): against the oracle's
+unfolded composition, element by element: fp16(res_in + delta) exactly as the
+oracle rounds it, and every output within a bound derived from what differs --
+the input rounded to fp16 before the norm's scaling instead of after it (one fp16
+rounding of each input term on each side), the fp32 GEMV, the fp32 norm scalar,
+and the output rounding.
+
+Exact (the default decode step's GEMVs): bitwise the separate entry points
+(q4_add_rmsnorm, then q4_gemv and q4_silu_mul) wherever q4_gemv runs as one K
+slice, and against the oracle in every case: the residual bitwise, the normalised
+vector within one fp16 ulp, every output within the M = 1 GEMV's rounding bound of
+the exact product of that vector, at least 99 % exactly rounded."""
 import numpy as np
 import pytest
 
@@ -12,7 +20,8 @@ torch = pytest.importorskip("torch")
 import oracle
 import synth
 import bit_weight_streaming_q4f16_amd as q4
-from gpuhelp import dev_half, dev_words, folded_bound, half_f64, host_half, ulp16
+from gpuhelp import (assert_within_rounding_bound, dev_half, dev_words, folded_bound, half_f64,
+                     host_half, ulp16)
 
 pytestmark = pytest.mark.gpu
 U = 2.0 ** -24
@@ -85,6 +94,74 @@ def test_glu_matches_unfolded_oracle(F, K):
     got = half_f64(host_half(y))
     err = np.abs(got - want)
     assert np.all(err <= lim), (float((err / lim).max()), int(np.argmax(err / lim)))
+
+
+def _within_one_ulp(got, ref):
+    g, r = half_f64(np.asarray(got, np.uint16)), half_f64(np.asarray(ref, np.uint16))
+    assert np.all(np.abs(g - r) <= ulp16(np.abs(r)))
+
+
+@pytest.mark.parametrize("rows,K,with_delta,glu", [
+    (9216, 3072, True, False),     # Phi-3 qkv: one K slice, bitwise against q4_gemv
+    (32064, 3072, True, False),    # the LM head
+    (3000, 3072, False, False),    # a ragged row count, no delta
+    (16384, 3072, True, True),     # Phi-3 gate/up with the glue
+    (257, 544, True, False),       # q4_gemv splits K here: oracle bound only
+    (208, 1024, True, True),       # the same with the glue
+    (4096, 8192, True, False),     # a long row: several blocks per thread
+])
+def test_exact_equals_norm_then_gemv(rows, K, with_delta, glu):
+    w, s, res, delta, gamma = case(f"foldx/{rows}x{K}", rows, K, with_delta)
+    eps = 1e-5
+    dw, ds, dres, dg = dev_words(w), dev_half(s), dev_half(res), dev_half(gamma)
+    ddel = dev_half(delta) if delta is not None else None
+    res_out = torch.empty(K, dtype=torch.float16, device="cuda")
+    y = q4.q4_gemv_norm(dw, ds, dres, dg, eps, delta=ddel, res_out=res_out, glu=glu, exact=True)
+    # the separate entry points on the same inputs
+    if ddel is not None:
+        r2, xn = q4.q4_add_rmsnorm(ddel, dres, dg, eps)
+    else:
+        r2, xn = dres.clone(), q4.q4_rmsnorm(dres, dg, eps)
+    full = torch.empty(rows, dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(q4.q4_workspace_bytes(1, rows, K), 16), dtype=torch.uint8, device="cuda")
+    q4.q4_gemv(dw, ds, xn, full, ws=ws)
+    ref_y = q4.q4_silu_mul(full) if glu else full
+    torch.cuda.synchronize()
+    one_slice = q4.q4_workspace_bytes(1, rows, K) == 0
+    h_ref, xn_ref = (oracle.add_rmsnorm(delta, res, gamma, eps) if delta is not None
+                     else (res.copy(), oracle.rmsnorm(res, gamma, eps)))
+    assert np.array_equal(host_half(res_out), h_ref)
+    assert np.array_equal(host_half(r2), h_ref)
+    _within_one_ulp(host_half(xn), xn_ref)
+    if one_slice:
+        assert np.array_equal(host_half(y), host_half(ref_y).reshape(-1)), \
+            "not bitwise the composition"
+    # the GEMV on the normalised vector the kernels staged, against the exact oracle
+    if glu:
+        g16 = host_half(full)
+        y64, y16 = oracle.gemv_exact(w, s, host_half(xn))
+        assert_within_rounding_bound(g16, y64, y16, s, host_half(xn), "exact", exact_frac=0.99,
+                                     what="gate/up")
+        if one_slice:
+            _within_one_ulp(host_half(y), oracle.silu_mul(g16.reshape(1, -1))[0])
+    else:
+        y64, y16 = oracle.gemv_exact(w, s, host_half(xn))
+        assert_within_rounding_bound(host_half(y), y64, y16, s, host_half(xn), "exact",
+                                     exact_frac=0.99, what="exact fold")
+
+
+def test_exact_limit_and_flags():
+    K = 32768                      # 1024 groups: 192 KB of exact staging
+    x = torch.zeros(K, dtype=torch.float16, device="cuda")
+    w = torch.zeros(4, K // 8, dtype=torch.int32, device="cuda")
+    s = torch.zeros(4, K // 32, dtype=torch.float16, device="cuda")
+    with pytest.raises(q4.Q4Error) as e:
+        q4.q4_gemv_norm(w, s, x, x, 1e-5, exact=True)
+    assert e.value.code == 6
+    # the factored form of the same call fits (64 bytes per group) and gives zeros
+    y = q4.q4_gemv_norm(w, s, x, x, 1e-5)
+    torch.cuda.synchronize()
+    assert not bool(torch.any(y != 0))
 
 
 def test_argument_errors():

@@ -96,8 +96,29 @@ def small():
     return Weights("small", 3, 256, 512, 1000)
 
 
-def test_step_matches_composition_and_oracle(small):
-    W = small
+@pytest.fixture(scope="module")
+def mid():
+    """D 1024, FFN 2048, vocabulary 3000: every normed projection needs a split-K
+    pass, so the driver runs each residual add + RMSNorm as its own kernel (and the
+    glue after the gate/up GEMV)."""
+    return Weights("mid", 2, 1024, 2048, 3000)
+
+
+@pytest.fixture(scope="module")
+def mixed():
+    """D 2048, FFN 2048, vocabulary 1000: qkv and gate/up fold their norms, the LM
+    head (split-K) takes the separate norm kernel."""
+    return Weights("mixed", 2, 2048, 2048, 1000)
+
+
+@pytest.mark.parametrize("model", ["small", "mid", "mixed"])
+def test_step_matches_composition_and_oracle(request, model):
+    W = request.getfixturevalue(model)
+    split = lambda N, K: q4.q4_workspace_bytes(1, N, K) > 0
+    if model == "mid":      # the premise: the separate norm kernels run
+        assert split(3 * W.D, W.D) and split(2 * W.F, W.D) and split(W.V, W.D)
+    if model == "mixed":
+        assert not split(3 * W.D, W.D) and not split(2 * W.F, W.D) and split(W.V, W.D)
     lg_ref, t_ref = composed_step(W, 17, check=True)
     tin = torch.tensor([17], dtype=torch.int32, device="cuda")
     tout = torch.full((1,), -1, dtype=torch.int32, device="cuda")
