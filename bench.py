@@ -653,8 +653,9 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
     weights near 0.1 keep them finite): one q4_decode_token per token with a host
     synchronisation after each (one token per host call), and q4_decode_tokens
     with `steps` tokens per host call, kernels enqueued per step or one captured
-    step replayed as a graph; and the graph replay with the norms folded into the
-    GEMVs they feed (Q4_MODEL_FACTORED_NORM)."""
+    step replayed as a graph (every residual add + RMSNorm inside the GEMV it feeds,
+    bitwise the separate kernels); and the graph replay with the norms in factored
+    form (Q4_MODEL_FACTORED_NORM)."""
     D, F, V = 3072, 8192, 32064
     labels = [l for l, _, _ in meta]
     assert len(descs) == 129 and labels[-1].endswith("lm_head"), labels[-1]
@@ -674,7 +675,9 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
     tok_out = torch.empty(1, dtype=torch.int32, device="cuda")
     tokens = torch.zeros(steps + 1, dtype=torch.int32, device="cuda")
     out = {"model": "phi3-mini-shaped, 32 blocks, vocabulary 32064, attention at one position",
-           "weight_bytes_per_token": weight_bytes, "tokens_per_call": steps}
+           "weight_bytes_per_token": weight_bytes, "tokens_per_call": steps,
+           "norms": "each residual add + RMSNorm inside the GEMV it feeds, bitwise the "
+                    "separate kernels (factored: the scalar after the product)"}
     with torch.cuda.stream(stream):
         for _ in range(3):
             q4.q4_decode_token(model, tok_in, tok_out, ws=ws, stream=stream)
@@ -707,7 +710,7 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
         torch.cuda.synchronize()
         graph.close()
     out["tokens"] = tokens[: min(steps + 1, 9)].cpu().tolist()
-    # the same loop with every residual add + RMSNorm folded into the GEMV it feeds
+    # the same loop with the norms in factored form
     folded = q4.Model(embed, blocks, gamma, descs[128][:2], 1e-5,
                       options=q4.MODEL_FACTORED_NORM)
     wsf = torch.empty(q4.q4_decode_token_workspace_bytes(folded), dtype=torch.uint8,
@@ -723,7 +726,7 @@ def token_figures(torch, q4, synth, np, stream, descs, meta, steps=32):
         stream.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / (reps * steps)
         graph.close()
-    out["tokens_per_call_graph_norms_folded"] = {
+    out["tokens_per_call_graph_factored_norms"] = {
         "ms_per_token": round(ms, 4), "tok_s": round(1e3 / ms, 1),
         "gbs": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
         "tokens": tokens[: min(steps + 1, 9)].cpu().tolist()}
