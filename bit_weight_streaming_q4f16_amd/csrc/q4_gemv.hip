@@ -138,26 +138,32 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
     }
   };
   int n = team;
-  // kNin (one slice: g0 == 0, gc == G): thread t stages blocks of 8 values t, t +
-  // 256, ... (the RMSNorm kernel's order); its first two blocks' residual, delta and
-  // gamma are requested before the weights, so that they do not queue behind them
-  constexpr int PRE = kNin ? 2 : 1;
+  // Thread t stages blocks of 8 values t, t + 256, ... (kNin: the RMSNorm kernel's
+  // order; one slice, g0 == 0 and gc == G).  Its first PRE blocks (kNin: residual,
+  // delta and gamma) are loaded before the weights, and both without a branch
+  // (indices clamped, surplus values unused): the compiler counts outstanding loads
+  // in order only through straight-line code, so the staging then waits for its
+  // own loads, not for the weights behind them.
+  constexpr int PRE = kAff ? 0 : kNin ? 2 : 4;
   const uint4* const nres = reinterpret_cast<const uint4*>(nin.res_in);
   const uint4* const ndel = reinterpret_cast<const uint4*>(nin.delta);
   const uint4* const ngam = reinterpret_cast<const uint4*>(nin.gamma);
-  uint4 pr[PRE], pd[PRE], pg[PRE];
-  if constexpr (kNin) {
+  uint4 pr[PRE > 0 ? PRE : 1], pd[PRE > 0 ? PRE : 1], pg[PRE > 0 ? PRE : 1];
 #pragma unroll
-    for (int j = 0; j < PRE; ++j) {
-      const int e = threadIdx.x + j * kBlock;
-      if (e < 4 * gc) {
-        pr[j] = nres[e];
-        pd[j] = ndel ? ndel[e] : make_uint4(0u, 0u, 0u, 0u);
-        pg[j] = ngam[e];
-      }
+  for (int j = 0; j < PRE; ++j) {
+    int e = threadIdx.x + j * kBlock;
+    e = e < 4 * gc ? e : 4 * gc - 1;
+    if constexpr (kNin) {
+      pr[j] = nres[e];
+      pd[j] = (ndel ? ndel : nres)[e];
+      pg[j] = ngam[e];
+    } else {
+      pr[j] = X[(int64_t)g0 * 4 + e];
     }
   }
-  if (n < N) issue(n, 0);
+  __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of the weights
+  issue(n < N ? n : N - 1, 0);   // a team past the last row loads it and never uses it
+  __builtin_amdgcn_sched_barrier(0);
   float ss = 0.f;                                 // kNin: this thread's sum of h^2
   float rs = 1.f;                                 // kNin, factored: 1 / rms of h
   // exact: h and gamma wait in LDS (each thread's own entries) until the sum of
@@ -201,6 +207,17 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
         xs[(e & 3) * gc + (e >> 2)] = pair_order(bits<uint4>(o));
       }
     }
+  } else if constexpr (!kAff) {
+    // unconditional, at the clamped index (a duplicate writes the same value), so
+    // that the early loads stay where they are
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) {
+      int e = threadIdx.x + j * kBlock;
+      e = e < 4 * gc ? e : 4 * gc - 1;
+      xs[(e & 3) * gc + (e >> 2)] = pair_order(pr[j]);
+    }
+    for (int i = threadIdx.x + PRE * kBlock; i < 4 * gc; i += kBlock)
+      xs[(i & 3) * gc + (i >> 2)] = pair_order(X[(int64_t)g0 * 4 + i]);
   } else {
     for (int i = threadIdx.x; i < 4 * gc; i += kBlock)
       xs[(i & 3) * gc + (i >> 2)] = pair_order(X[(int64_t)g0 * 4 + i]);
