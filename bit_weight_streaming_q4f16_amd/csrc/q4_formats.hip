@@ -61,19 +61,53 @@ __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict_
   extern __shared__ float4 xs4[];
   const int G = K / GS;
   float* gsum = reinterpret_cast<float*>(xs4 + K / 4);
-  for (int c = threadIdx.x; c < K / 4; c += kBlock) {   // 4 consecutive x per chunk
-    float4 v;
+  const int lane = threadIdx.x & (LPR - 1);
+  const int team = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) / LPR);
+  const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
+  auto chunk = [&](int c) {   // x[4c .. 4c + 3] as fp32
     if constexpr (F == kQ4F32) {
-      v = static_cast<const float4*>(Xv)[c];
+      return static_cast<const float4*>(Xv)[c];
     } else {
       const uint2 h = static_cast<const uint2*>(Xv)[c];
-      v = make_float4((float)bits<_Float16>((uint16_t)(h.x & 0xFFFFu)),
-                      (float)bits<_Float16>((uint16_t)(h.x >> 16)),
-                      (float)bits<_Float16>((uint16_t)(h.y & 0xFFFFu)),
-                      (float)bits<_Float16>((uint16_t)(h.y >> 16)));
+      return make_float4((float)bits<_Float16>((uint16_t)(h.x & 0xFFFFu)),
+                         (float)bits<_Float16>((uint16_t)(h.x >> 16)),
+                         (float)bits<_Float16>((uint16_t)(h.y & 0xFFFFu)),
+                         (float)bits<_Float16>((uint16_t)(h.y >> 16)));
     }
-    xs4[(c % (GS / 4)) * G + c / (GS / 4)] = v;
+  };
+  // This thread's first PX chunks of x, then the first group of its team's first
+  // row, are loaded before x is staged, without a branch (indices clamped; a
+  // duplicate writes the same value, a group past the end is loaded and unused):
+  // the compiler counts outstanding loads in order only through straight-line
+  // code, so the staging then waits for x, not for the weights behind it.
+  constexpr int PX = 4;
+  float4 xp[PX];
+#pragma unroll
+  for (int j = 0; j < PX; ++j) {
+    const int c = (int)threadIdx.x + j * kBlock;
+    xp[j] = chunk(c < K / 4 ? c : K / 4 - 1);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  const int nf = team < N ? team : N - 1, gf = lane < G ? lane : G - 1;
+  uint32_t wf[NW];
+  {
+    const uint32_t* wp = W + ((int64_t)nf * G + gf) * NW;
+#pragma unroll
+    for (int j = 0; j < NW; j += 4) {
+      const uint4 v = load_nt(reinterpret_cast<const uint4*>(wp + j));
+      wf[j] = v.x; wf[j + 1] = v.y; wf[j + 2] = v.z; wf[j + 3] = v.w;
+    }
+  }
+  const float sf = static_cast<const float*>(Sv)[(int64_t)nf * G + gf];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < PX; ++j) {
+    int c = (int)threadIdx.x + j * kBlock;
+    c = c < K / 4 ? c : K / 4 - 1;
+    xs4[(c % (GS / 4)) * G + c / (GS / 4)] = xp[j];
+  }
+  for (int c = threadIdx.x + PX * kBlock; c < K / 4; c += kBlock)   // 4 consecutive x per chunk
+    xs4[(c % (GS / 4)) * G + c / (GS / 4)] = chunk(c);
   __syncthreads();
   for (int g = threadIdx.x; g < G; g += kBlock) {
     float t = 0.f;
@@ -85,12 +119,14 @@ __global__ __launch_bounds__(kBlock) void k_gemv_fmt(const uint32_t* __restrict_
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & (LPR - 1);
-  const int team = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) / LPR);
-  const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
   for (int n = team; n < N; n += nteams) {
     float acc = 0.f;
-    for (int g = lane; g < G; g += LPR) {
+    int g1 = lane;
+    if (n == team) {            // the group loaded before the staging
+      if (lane < G) acc = __builtin_fmaf(sf, group_qx<F>(wf, xs4, G, lane) - 7.f * gsum[lane], acc);
+      g1 = lane + LPR;
+    }
+    for (int g = g1; g < G; g += LPR) {
       uint32_t w[NW];
       const uint32_t* wp = W + ((int64_t)n * G + g) * NW;
 #pragma unroll
@@ -183,31 +219,55 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q3(const uint32_t* __restrict__
     for (int t = 0; t < 4; ++t)
       f.s[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, (gt + t * LPR + lane) * 2, 0, 0);
   };
-  Trip cur;
-  int n = team, tr = 0;
-  fetch(cur, n, 0);
-  for (int e = threadIdx.x; e < 4 * G; e += kBlock) {   // e: x[8e .. 8e+7]
-    const uint4 v = X[e];
+  // x is loaded before the first trip's weights, and without a branch (indices
+  // clamped, a duplicate writes the same value): the compiler counts outstanding
+  // loads in order only through straight-line code, so the staging then waits for
+  // x, not for the weights behind it.  Thread t stages blocks t and t + 256 of x
+  // and forms the correction of group t from its four blocks.
+  auto pair = [](uint4 v) {
     uint4 o;
     o.x = (v.x & 0xFFFFu) | (v.z << 16);
     o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
     o.z = (v.y & 0xFFFFu) | (v.w << 16);
     o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-    xq[(e & 3) * G + (e >> 2)] = o;
-  }
+    return o;
+  };
   // 2^E + 3 for the codes 8c .. 8c+7 of a chunk
   constexpr float kOff[8] = {67.f, 11.f, 67.f, 11.f, 1027.f, 131.f, 1027.f, 131.f};
-  for (int g = threadIdx.x; g < G; g += kBlock) {
+  auto correction = [&](const uint4 (&v4)[4]) {
     float t = 0.f;
+#pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 v = X[4 * g + c];
-      const uint32_t hw[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t hw[4] = {v4[c].x, v4[c].y, v4[c].z, v4[c].w};
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         t = __builtin_fmaf(kOff[i], (float)bits<_Float16>((uint16_t)(hw[i / 2] >> (16 * (i & 1)))),
                            t);
     }
-    corr[g] = t;
+    return t;
+  };
+  const int e0 = (int)threadIdx.x < 4 * G ? (int)threadIdx.x : 4 * G - 1;
+  const int e1 = (int)threadIdx.x + kBlock < 4 * G ? (int)threadIdx.x + kBlock : 4 * G - 1;
+  const int gx = (int)threadIdx.x < G ? (int)threadIdx.x : G - 1;
+  const uint4 x0 = X[e0], x1 = X[e1];
+  uint4 xg[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) xg[c] = X[4 * gx + c];
+  __builtin_amdgcn_sched_barrier(0);
+  Trip cur;
+  int n = team, tr = 0;
+  fetch(cur, n, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  xq[(e0 & 3) * G + (e0 >> 2)] = pair(x0);
+  xq[(e1 & 3) * G + (e1 >> 2)] = pair(x1);
+  for (int e = threadIdx.x + 2 * kBlock; e < 4 * G; e += kBlock)   // e: x[8e .. 8e+7]
+    xq[(e & 3) * G + (e >> 2)] = pair(X[e]);
+  corr[gx] = correction(xg);
+  for (int g = threadIdx.x + kBlock; g < G; g += kBlock) {
+    uint4 v4[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v4[c] = X[4 * g + c];
+    corr[g] = correction(v4);
   }
   __syncthreads();
 

@@ -144,11 +144,18 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
   // (indices clamped, surplus values unused): the compiler counts outstanding loads
   // in order only through straight-line code, so the staging then waits for its
   // own loads, not for the weights behind them.
-  constexpr int PRE = kAff ? 0 : kNin ? 2 : 4;
+  constexpr int PRE = kNin ? 2 : 4;
   const uint4* const nres = reinterpret_cast<const uint4*>(nin.res_in);
   const uint4* const ndel = reinterpret_cast<const uint4*>(nin.delta);
   const uint4* const ngam = reinterpret_cast<const uint4*>(nin.gamma);
-  uint4 pr[PRE > 0 ? PRE : 1], pd[PRE > 0 ? PRE : 1], pg[PRE > 0 ? PRE : 1];
+  uint4 pr[PRE], pd[PRE], pg[PRE];
+  // kAff: the four blocks of this thread's group (clamped) for the sums of x
+  uint4 px[kAff ? 4 : 1];
+  if constexpr (kAff) {
+    const int g = (int)threadIdx.x < gc ? (int)threadIdx.x : gc - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) px[j] = X[(int64_t)(g0 + g) * 4 + j];
+  }
 #pragma unroll
   for (int j = 0; j < PRE; ++j) {
     int e = threadIdx.x + j * kBlock;
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
         xs[(e & 3) * gc + (e >> 2)] = pair_order(bits<uint4>(o));
       }
     }
-  } else if constexpr (!kAff) {
+  } else {
     // unconditional, at the clamped index (a duplicate writes the same value), so
     // that the early loads stay where they are
 #pragma unroll
@@ -218,9 +225,6 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
     }
     for (int i = threadIdx.x + PRE * kBlock; i < 4 * gc; i += kBlock)
       xs[(i & 3) * gc + (i >> 2)] = pair_order(X[(int64_t)g0 * 4 + i]);
-  } else {
-    for (int i = threadIdx.x; i < 4 * gc; i += kBlock)
-      xs[(i & 3) * gc + (i >> 2)] = pair_order(X[(int64_t)g0 * 4 + i]);
   }
   if (kNin && !nin.exact) {
     ss = team_sum<64>(ss);
@@ -228,16 +232,24 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
   }
   float* const xsum = reinterpret_cast<float*>(xs + 4 * gc);   // kAffine: sum of x per group
   if constexpr (kAff) {
-    for (int g = threadIdx.x; g < gc; g += kBlock) {
+    auto group_sum = [&](const uint4 (&v4)[4]) {
       float t = 0.f;
+#pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint4 v = X[(int64_t)(g0 + g) * 4 + j];
-        const uint32_t hw[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t hw[4] = {v4[j].x, v4[j].y, v4[j].z, v4[j].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           t += half_to_float((uint16_t)(hw[i] & 0xFFFFu)) + half_to_float((uint16_t)(hw[i] >> 16));
       }
-      xsum[g] = t;
+      return t;
+    };
+    // the first group from the early loads (a clamped duplicate writes the same sum)
+    xsum[(int)threadIdx.x < gc ? (int)threadIdx.x : gc - 1] = group_sum(px);
+    for (int g = threadIdx.x + kBlock; g < gc; g += kBlock) {
+      uint4 v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[j] = X[(int64_t)(g0 + g) * 4 + j];
+      xsum[g] = group_sum(v4);
     }
   }
   __syncthreads();
