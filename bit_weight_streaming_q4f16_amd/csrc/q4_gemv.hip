@@ -61,7 +61,7 @@ __device__ __forceinline__ float group_dot(uint4 w, const uint4* xs, int gc, int
 }
 
 // K slice s of G groups split `splits` ways: [G*s/splits, G*(s+1)/splits).
-__device__ __forceinline__ int slice_begin(int G, int splits, int s) {
+__host__ __device__ __forceinline__ int slice_begin(int G, int splits, int s) {
   return (int)((int64_t)G * s / splits);
 }
 
@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
 // (c, r), which is the B-operand layout of v_mfma_f32_16x16x32_f16 (column = row
 // n, k block = c).  A = X rows (row m = r < M, zero above M), from LDS in the same
 // pair order.  One MFMA per group into a fresh accumulator, then acc += s * D.
+template <bool WIDE>
 __global__ __launch_bounds__(kBlock) void k_gemv_mfma(const uint4* __restrict__ W,
                                                       const uint16_t* __restrict__ S,
                                                       const uint4* __restrict__ X,
@@ -322,20 +323,146 @@ __global__ __launch_bounds__(kBlock) void k_gemv_mfma(const uint4* __restrict__ 
   const int g0 = slice_begin(G, splits, split);
   const int gc = slice_begin(G, splits, split + 1) - g0;
   const int pitch = 4 * gc + 1;
-  for (int i = threadIdx.x; i < M * 4 * gc; i += kBlock) {
-    const int m = i / (4 * gc), r = i - m * 4 * gc;
-    xs[m * pitch + r] = pair_order(X[(int64_t)m * G * 4 + (int64_t)g0 * 4 + r]);
-  }
-  __syncthreads();
-
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, c = l >> 4, r = l & 15;
   const bool has_x = r < M;
-  // the eight-group blocks need whole blocks in the slice and 16-byte aligned
-  // scale runs
-  const bool wide = gc % 8 == 0 && g0 % 8 == 0 && G % 8 == 0 &&
-                    (reinterpret_cast<uintptr_t>(S) & 15u) == 0;
   uint32_t* const stage = reinterpret_cast<uint32_t*>(xs + M * pitch) + wave * 512;
   const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const int nx = M * 4 * gc;
+  auto x_at = [&](int i) {   // entry i of X's slice, row-major [M][4 gc]
+    const int m = i / (4 * gc), rr = i - m * 4 * gc;
+    return X[(int64_t)m * G * 4 + (int64_t)g0 * 4 + rr];
+  };
+  auto x_put = [&](int i, uint4 v) {
+    const int m = i / (4 * gc), rr = i - m * 4 * gc;
+    xs[m * pitch + rr] = pair_order(v);
+  };
+
+  if constexpr (WIDE) {
+    // Blocks of eight groups ("chunks"): two loads of 8 rows x 128 contiguous bytes
+    // (lane l: row 8h + l / 8, group l % 8; whole cache lines, where one group per
+    // lane of 16 rows touches 16 half lines), through this wave's stage as word
+    // planes [word][16 rows][8 groups], from which lane (c, r) reads word c of row
+    // r's eight groups as 32 contiguous bytes; the row's eight scales in one load.
+    // Wave w takes chunks 8w, 8w + 32, ... of every tile of 16 rows; every wave has
+    // the same number per tile (CPW; a chunk past the slice is loaded from the
+    // last one and not computed), so all four reach each tile's cross-wave sum
+    // together.  The wave's chunks of all its workgroup's tiles form one sequence,
+    // and the next chunk's loads are issued before a chunk is computed (two
+    // register slots taken in turn).  X's first PX entries per thread and the first
+    // chunk are loaded before X is staged, all without a branch, so the staging
+    // waits for X only.
+    const int CPW = (gc + 31) / 32;
+    const int tstride = gridDim.x * 16;
+    const int tiles = (N - (int)blockIdx.x * 16 + tstride - 1) / tstride;   // >= 1
+    const int total = tiles * CPW;
+    struct Chunk {
+      uint4 raw[2];
+      uint4 sv;
+    };
+    auto issue = [&](Chunk& C, int i) {
+      i = i < total ? i : total - 1;         // past the end: the last chunk again, unused
+      const int n0 = (int)blockIdx.x * 16 + (i / CPW) * tstride;
+      int gb = 8 * wave + 32 * (i % CPW);
+      gb = gb < gc ? gb : gc - 8;
+      const int64_t rows_left = (int64_t)(N - n0);
+      const uint4* wt = W + (int64_t)n0 * G + g0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t row = 8 * h + (l >> 3);
+        C.raw[h] = load_nt(wt + (row < rows_left ? row : rows_left - 1) * G + gb + (l & 7));
+      }
+      const int n = n0 + r < N ? n0 + r : N - 1;
+      C.sv = *reinterpret_cast<const uint4*>(S + (int64_t)n * G + g0 + gb);
+    };
+    constexpr int PX = 8;
+    uint4 xp[PX];
+#pragma unroll
+    for (int j = 0; j < PX; ++j) {
+      const int i = (int)threadIdx.x + j * kBlock;
+      xp[j] = x_at(i < nx ? i : nx - 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    Chunk A, B;
+    issue(A, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < PX; ++j) {   // a clamped duplicate writes the same value
+      const int i = (int)threadIdx.x + j * kBlock;
+      x_put(i < nx ? i : nx - 1, xp[j]);
+    }
+    for (int i = threadIdx.x + PX * kBlock; i < nx; i += kBlock) x_put(i, x_at(i));
+    __syncthreads();
+
+    f4_t acc = zero;
+    auto consume = [&](const Chunk& C, int i) {
+      const int ti = i / CPW, ci = i - ti * CPW;
+      const int n0 = (int)blockIdx.x * 16 + ti * tstride;
+      const int gb = 8 * wave + 32 * ci;
+      if (gb < gc) {
+        // the stage is read by other lanes of the wave: keep its writes and reads
+        // in program order (a wave's LDS operations complete in order)
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          stage[j * 128 + l] = (&C.raw[0].x)[j];
+          stage[j * 128 + 64 + l] = (&C.raw[1].x)[j];
+        }
+        asm volatile("" ::: "memory");
+        const uint4* sp = reinterpret_cast<const uint4*>(stage + c * 128 + r * 8);
+        const uint4 wq0 = sp[0], wq1 = sp[1];
+        asm volatile("" ::: "memory");
+        const uint32_t wc[8] = {wq0.x, wq0.y, wq0.z, wq0.w, wq1.x, wq1.y, wq1.z, wq1.w};
+        const uint32_t sw[4] = {C.sv.x, C.sv.y, C.sv.z, C.sv.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          h2_t q[4];
+          dequant_word(wc[t], q);
+          const h8_t Bq = {q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+          h8_t Ax = {};
+          if (has_x) Ax = bits<h8_t>(xs[r * pitch + 4 * (gb + t) + c]);
+          const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ax, Bq, zero, 0, 0, 0);
+          const float sc = half_to_float((uint16_t)(sw[t >> 1] >> (16 * (t & 1))));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, d[e], acc[e]);
+        }
+      }
+      if (ci == CPW - 1) {
+        // the tile's end: add the four waves' partials in a fixed order
+        if (wave > 0) red[wave - 1][l] = acc;
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+          for (int w = 0; w < 3; ++w) acc += red[w][l];
+          if (n0 + r < N) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int m = 4 * c + e;
+              if (m < M) {
+                if (splits == 1)
+                  Y[(int64_t)m * N + n0 + r] = float_to_half_rne(acc[e]);
+                else
+                  P[((int64_t)split * M + m) * N + n0 + r] = acc[e];
+              }
+            }
+          }
+        }
+        __syncthreads();   // red is reused by the next tile
+        acc = zero;
+      }
+    };
+    for (int i = 0;; i += 2) {
+      issue(B, i + 1);
+      consume(A, i);
+      if (i + 1 >= total) break;
+      issue(A, i + 2);
+      consume(B, i + 1);
+      if (i + 2 >= total) break;
+    }
+    return;
+  }
+
+  for (int i = threadIdx.x; i < nx; i += kBlock) x_put(i, x_at(i));
+  __syncthreads();
   // workgroups loop over tiles of 16 rows, so X is staged once per workgroup, not
   // once per tile
   for (int n0 = blockIdx.x * 16; n0 < N; n0 += gridDim.x * 16) {
@@ -343,51 +470,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_mfma(const uint4* __restrict__ 
     const uint4* wr = W + (int64_t)n * G + g0;
     const uint16_t* sr = S + (int64_t)n * G + g0;
     f4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (wide) {
-      // blocks of eight groups: two loads of 8 rows x 128 contiguous bytes (lane l:
-      // row 8h + l / 8, group l % 8; whole cache lines, where one group per lane of
-      // 16 rows touches 16 half lines), through this wave's stage as word planes
-      // [word][16 rows][8 groups], from which lane (c, r) reads word c of row r's
-      // eight groups as 32 contiguous bytes; the row's eight scales in one load.
-      const uint4* wt = W + (int64_t)n0 * G + g0;
-      const int64_t rows_left = (int64_t)(N - n0);
-      for (int gb = 8 * wave; gb < gc; gb += 32) {
-        uint4 raw[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int64_t row = 8 * h + (l >> 3);
-          raw[h] = load_nt(wt + (row < rows_left ? row : rows_left - 1) * G + gb + (l & 7));
-        }
-        const uint4 sv = *reinterpret_cast<const uint4*>(sr + gb);
-        // the stage is read by other lanes of the wave: keep its writes and reads
-        // in program order (a wave's LDS operations complete in order)
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          stage[j * 128 + l] = (&raw[0].x)[j];
-          stage[j * 128 + 64 + l] = (&raw[1].x)[j];
-        }
-        asm volatile("" ::: "memory");
-        const uint4* sp = reinterpret_cast<const uint4*>(stage + c * 128 + r * 8);
-        const uint4 wq0 = sp[0], wq1 = sp[1];
-        asm volatile("" ::: "memory");
-        const uint32_t wc[8] = {wq0.x, wq0.y, wq0.z, wq0.w, wq1.x, wq1.y, wq1.z, wq1.w};
-        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          h2_t q[4];
-          dequant_word(wc[t], q);
-          const h8_t B = {q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
-          h8_t A = {};
-          if (has_x) A = bits<h8_t>(xs[r * pitch + 4 * (gb + t) + c]);
-          const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, zero, 0, 0, 0);
-          const float sc = half_to_float((uint16_t)(sw[t >> 1] >> (16 * (t & 1))));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(sc, d[e], acc[e]);
-        }
-      }
-    }
-    for (int gb = 4 * wave; !wide && gb < gc; gb += 16) {
+    for (int gb = 4 * wave; gb < gc; gb += 16) {
       const int gl = gb + c < gc ? gb + c : gc - 1;
       const uint4 wv = load_nt(wr + gl);
       float s[4];
@@ -589,8 +672,15 @@ hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p
     const int64_t cap = (int64_t)d.cus * (per_cu < 1 ? 1 : per_cu > 8 ? 8 : per_cu);
     if (tiles * p.splits > cap) tiles = (cap + p.splits - 1) / p.splits;
     const dim3 grid((unsigned)tiles, (unsigned)p.splits);
-    if (hipError_t e2 = allow_lds(k_gemv_mfma, lds)) return e2;
-    hipLaunchKernelGGL(k_gemv_mfma, grid, dim3(kBlock), lds, s,
+    // the eight-group chunks need whole chunks in every slice and 16-byte aligned
+    // scale runs
+    bool wide = G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15u) == 0;
+    for (int sp = 0; wide && sp < p.splits; ++sp)
+      wide = slice_begin((int)G, p.splits, sp) % 8 == 0 &&
+             slice_begin((int)G, p.splits, sp + 1) % 8 == 0;
+    auto kern = wide ? k_gemv_mfma<true> : k_gemv_mfma<false>;
+    if (hipError_t e2 = allow_lds(kern, lds)) return e2;
+    hipLaunchKernelGGL(kern, grid, dim3(kBlock), lds, s,
                        reinterpret_cast<const uint4*>(a.words), a.scales,
                        reinterpret_cast<const uint4*>(a.x), out, part, (int)a.M, (int)a.N,
                        (int)G, p.splits);
