@@ -170,6 +170,14 @@ def test_long_rows(N, K):
     assert_gemv_close(gemv_gpu(w, s, x), w, s, x)
 
 
+@pytest.mark.parametrize("N,K", [(515, 16384), (70, 12320)])
+def test_one_slice_longer_than_the_early_staging_loads(N, K):
+    """One K slice of more than 4 x 256 blocks of x: the staging loads each thread's
+    first four blocks ahead of the weights and the rest in a loop after them."""
+    w, s, x = rand_case(17, N, K, neg=True)
+    assert_gemv_close(gemv_gpu(w, s, x, 1), w, s, x, exact=True)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 13, 32, 64])
 def test_splitk_matches_oracle_and_is_deterministic(splits):
     N, K = 515, 8192
