@@ -558,10 +558,10 @@ hipError_t launch_m1_unr(const GemvArgs& a, const GemvPlan& p, float* part, cons
   // every workgroup stages x once, so a grid of one workgroup per 8 rows re-reads
   // it 6 KB per 14 KB of weights (K = 3072); measured best against 2, 4, 16, 64.
   // The folded-norm modes stage from three vectors (residual, delta, gamma), and
-  // take two per unit (Phi-3-shaped token loop: 0.963 ms at 8, 0.944 at 4,
-  // 0.914 at 2, 1.037 at 1).
+  // take three per unit (Phi-3-shaped token loop, exact norms: 0.847 ms at 2,
+  // 0.828 at 3, 0.860 at 4).
   constexpr bool kNin = MODE == kPlainNorm || MODE == kGluNorm;
-  const int64_t cap = (int64_t)d.cus * (kNin ? 2 : 8);
+  const int64_t cap = (int64_t)d.cus * (kNin ? 3 : 8);
   if (blocks > cap) blocks = cap;
   const int64_t gmax = (G + p.splits - 1) / p.splits;
   const size_t lds =
