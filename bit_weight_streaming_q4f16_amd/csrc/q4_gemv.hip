@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
     for (int e = threadIdx.x + PRE * kBlock; e < 4 * gc; e += kBlock)
       stage_norm(e, nres[e], ndel ? ndel[e] : make_uint4(0u, 0u, 0u, 0u), ngam[e]);
     if (nin.exact) {
-      const float r = rms_scale(block_sum(ss, ssw), G * 32, nin.eps);
+      const float r = rms_scale(block_sum<false>(ss, ssw), G * 32, nin.eps);   // ssw not reused
       for (int e = threadIdx.x; e < 4 * gc; e += kBlock) {
         const h8_t v = bits<h8_t>(hs[e]), gm = bits<h8_t>(gs[e]);
         h8_t o;

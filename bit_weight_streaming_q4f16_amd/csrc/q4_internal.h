@@ -108,6 +108,8 @@ __device__ __forceinline__ _Float16 silu_mul_h(_Float16 g, _Float16 u) {
 // rms_scale is 1 / sqrt(sum / K + eps); norm_h rounds v * r * gamma to fp32 and
 // then to fp16 (the empty asm keeps the compiler from fusing the product and the
 // conversion into one mixed-precision instruction, which would round once).
+// REUSE: a barrier after the read, so that `red` may be written again.
+template <bool REUSE = true>
 __device__ __forceinline__ float block_sum(float v, float* red) {   // red: 4 floats
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -115,7 +117,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {   // red: 4 fl
   if (lane == 0) red[wave] = v;
   __syncthreads();
   const float t = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
+  if (REUSE) __syncthreads();
   return t;
 }
 __device__ __forceinline__ float rms_scale(float sum_sq, int K, float eps) {
