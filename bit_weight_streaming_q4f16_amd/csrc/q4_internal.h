@@ -134,20 +134,18 @@ hipError_t launch_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t
                            hipStream_t s);
 
 // The operations around the GEMVs (q4_ops.hip).  delta == nullptr: plain RMSNorm.
+// A multi-step decode keeps its tokens on the device: with `counter` (M == 1), the
+// embedding row is that of seq[counter[0]] instead of tokens[0], and the argmax,
+// besides out[0], writes seq[counter[0] + 1] and advances counter[0].
 hipError_t launch_embed_rows(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
-                             const int32_t* tokens, int64_t M, uint16_t* out, hipStream_t s);
+                             const int32_t* tokens, int64_t M, uint16_t* out, hipStream_t s,
+                             const int32_t* seq = nullptr, const int32_t* counter = nullptr);
 hipError_t launch_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const uint16_t* gamma,
                           float eps, int64_t M, int64_t K, uint16_t* res_out, uint16_t* out,
                           hipStream_t s);
-hipError_t launch_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, hipStream_t s);
-
-// Device-side token bookkeeping of a multi-step decode (q4_ops.hip):
-// cur[0] = tokens[counter[0]]; tokens[counter[0] + 1] = out[0] and counter[0] += 1;
-// counter[0] = 0.
-hipError_t launch_token_fetch(const int32_t* tokens, const int32_t* counter, int32_t* cur,
-                              hipStream_t s);
-hipError_t launch_token_store(int32_t* tokens, int32_t* counter, const int32_t* out,
-                              hipStream_t s);
+hipError_t launch_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, hipStream_t s,
+                         int32_t* seq = nullptr, int32_t* counter = nullptr);
+// counter[0] = 0 (a kernel, so that a captured graph holds no memset node).
 hipError_t launch_counter_reset(int32_t* counter, hipStream_t s);
 
 // GEMV of a format variant at M = 1 (q4_formats.hip): format 1 q3f16_1, 2 q4f32_1,

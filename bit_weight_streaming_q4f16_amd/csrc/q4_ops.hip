@@ -15,11 +15,13 @@ __global__ __launch_bounds__(kBlock) void k_embed_rows(const uint4* __restrict__
                                                        const uint16_t* __restrict__ scales,
                                                        int64_t N, int G,
                                                        const int32_t* __restrict__ tokens,
-                                                       uint4* __restrict__ out) {
+                                                       uint4* __restrict__ out,
+                                                       const int32_t* __restrict__ seq,
+                                                       const int32_t* __restrict__ counter) {
   const int m = blockIdx.y;
   const int g = blockIdx.x * kBlock + threadIdx.x;
   if (g >= G) return;
-  const int64_t t = tokens[m];
+  const int64_t t = counter ? seq[counter[0]] : tokens[m];
   uint4* o = out + ((int64_t)m * G + g) * 4;
   if (t < 0 || t >= N) {
     const uint4 nan4 = make_uint4(0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u);
@@ -87,7 +89,9 @@ __global__ __launch_bounds__(kBlock) void k_rmsnorm(const uint4* __restrict__ de
 // compares indices.
 constexpr int kArgThreads = 1024;
 __global__ __launch_bounds__(kArgThreads) void k_argmax(const uint16_t* __restrict__ x,
-                                                        int64_t N, int32_t* __restrict__ out) {
+                                                        int64_t N, int32_t* __restrict__ out,
+                                                        int32_t* __restrict__ seq,
+                                                        int32_t* __restrict__ counter) {
   __shared__ float sv[kArgThreads / 64];
   __shared__ int64_t si[kArgThreads / 64];
   const int64_t row = blockIdx.x;
@@ -148,35 +152,19 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax(const uint16_t* __restri
     float v = sv[0];
     int64_t i = si[0];
     for (int w = 1; w < kArgThreads / 64; ++w) take(v, i, sv[w], si[w]);
-    out[row] = (int32_t)(i < 0 ? 0 : i);
+    const int32_t tok = (int32_t)(i < 0 ? 0 : i);
+    out[row] = tok;
+    if (counter) {   // a multi-step decode: the next step's token, one grid of one row
+      const int32_t c = counter[0];
+      seq[c + 1] = tok;
+      counter[0] = c + 1;
+    }
   }
-}
-
-__global__ void k_token_fetch(const int32_t* tokens, const int32_t* counter, int32_t* cur) {
-  cur[0] = tokens[counter[0]];
-}
-
-__global__ void k_token_store(int32_t* tokens, int32_t* counter, const int32_t* out) {
-  const int32_t c = counter[0];
-  tokens[c + 1] = out[0];
-  counter[0] = c + 1;
 }
 
 __global__ void k_counter_reset(int32_t* counter) { counter[0] = 0; }
 
 }  // namespace
-
-hipError_t launch_token_fetch(const int32_t* tokens, const int32_t* counter, int32_t* cur,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(k_token_fetch, dim3(1), dim3(1), 0, s, tokens, counter, cur);
-  return hipGetLastError();
-}
-
-hipError_t launch_token_store(int32_t* tokens, int32_t* counter, const int32_t* out,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(k_token_store, dim3(1), dim3(1), 0, s, tokens, counter, out);
-  return hipGetLastError();
-}
 
 hipError_t launch_counter_reset(int32_t* counter, hipStream_t s) {
   hipLaunchKernelGGL(k_counter_reset, dim3(1), dim3(1), 0, s, counter);
@@ -184,11 +172,13 @@ hipError_t launch_counter_reset(int32_t* counter, hipStream_t s) {
 }
 
 hipError_t launch_embed_rows(const uint32_t* words, const uint16_t* scales, int64_t N, int64_t K,
-                             const int32_t* tokens, int64_t M, uint16_t* out, hipStream_t s) {
+                             const int32_t* tokens, int64_t M, uint16_t* out, hipStream_t s,
+                             const int32_t* seq, const int32_t* counter) {
+  if (counter && M != 1) return hipErrorInvalidValue;
   const int G = (int)(K / 32);
   hipLaunchKernelGGL(k_embed_rows, dim3((G + kBlock - 1) / kBlock, (unsigned)M), dim3(kBlock), 0,
                      s, reinterpret_cast<const uint4*>(words), scales, N, G, tokens,
-                     reinterpret_cast<uint4*>(out));
+                     reinterpret_cast<uint4*>(out), seq, counter);
   return hipGetLastError();
 }
 
@@ -202,8 +192,11 @@ hipError_t launch_rmsnorm(const uint16_t* delta, const uint16_t* res_in, const u
   return hipGetLastError();
 }
 
-hipError_t launch_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax, dim3((unsigned)M), dim3(kArgThreads), 0, s, x, N, out);
+hipError_t launch_argmax(const uint16_t* x, int64_t M, int64_t N, int32_t* out, hipStream_t s,
+                         int32_t* seq, int32_t* counter) {
+  if (counter && M != 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_argmax, dim3((unsigned)M), dim3(kArgThreads), 0, s, x, N, out, seq,
+                     counter);
   return hipGetLastError();
 }
 

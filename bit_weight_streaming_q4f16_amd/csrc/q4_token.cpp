@@ -13,11 +13,12 @@
 // Q4_MODEL_FACTORED_NORM the norm is folded in factored form instead: no
 // reduction before the staging, results within rounding of the defined step, not
 // bitwise.  Every buffer between the kernels lives in the caller's workspace; the
-// residual alternates between two buffers.  A multi-step decode captures one step, with two one-thread kernels
-// that take the step's token from and put the next one into the caller's token
-// array at a device-side counter, as a HIP graph and replays it: no host
-// round trip between tokens (the pages' host-side lever is to submit a whole
-// token in one command; here several tokens go per host call).
+// residual alternates between two buffers.  A multi-step decode keeps its tokens
+// on the device: the embedding kernel takes the step's token from the caller's
+// token array at a device-side counter, and the argmax kernel writes the next one
+// there and advances the counter; one step is captured as a HIP graph and
+// replayed: no host round trip between tokens (the pages' host-side lever is to
+// submit a whole token in one command; here several tokens go per host call).
 #include <string.h>
 
 #include <algorithm>
@@ -137,7 +138,7 @@ int check_ws(void* ws, size_t have, size_t need) {
 // Enqueue one decode step: token tok_in[0] -> tok_out[0] (and the logits).
 hipError_t enqueue_step(const q4::DeviceInfo& d, const q4_model& m, const Layout& L,
                         const int32_t* tok_in, int32_t* tok_out, uint16_t* logits, uint8_t* ws,
-                        hipStream_t s) {
+                        hipStream_t s, int32_t* seq = nullptr, int32_t* counter = nullptr) {
   auto buf = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
   uint16_t *res = buf(L.res), *h = buf(L.h), *qkv = buf(L.qkv_out), *gu = buf(L.gu);
   uint16_t *attn = buf(L.attn), *hf = buf(L.hf), *dn = buf(L.dn);
@@ -150,7 +151,8 @@ hipError_t enqueue_step(const q4::DeviceInfo& d, const q4_model& m, const Layout
   do {                                        \
     if (hipError_t e_ = (call)) return e_;    \
   } while (0)
-  Q4_TRY(q4::launch_embed_rows(m.embed.words, m.embed.scales, m.V, m.D, tok_in, 1, res, s));
+  Q4_TRY(q4::launch_embed_rows(m.embed.words, m.embed.scales, m.V, m.D, tok_in, 1, res, s, seq,
+                               counter));
   // Every residual add + RMSNorm is folded into the GEMV it feeds (q4_fused.h)
   // where that GEMV runs as one K slice: exact (the default: bitwise the norm
   // kernel followed by the GEMV) when the staging fits LDS, else as the separate
@@ -200,7 +202,7 @@ hipError_t enqueue_step(const q4::DeviceInfo& d, const q4_model& m, const Layout
     pend.gamma = next;
   }
   Q4_TRY(normed(m.lm_head, L.lm_head, lg, m.V, false));
-  Q4_TRY(q4::launch_argmax(lg, 1, m.V, tok_out, s));
+  Q4_TRY(q4::launch_argmax(lg, 1, m.V, tok_out, s, seq, counter));
 #undef Q4_TRY
   return hipSuccess;
 }
@@ -268,11 +270,8 @@ int q4_decode_tokens(const q4_model* model, int32_t* tokens, int64_t steps, void
   uint8_t* w = static_cast<uint8_t*>(ws);
   int32_t* tok = reinterpret_cast<int32_t*>(w + L.tok);
   hipError_t e = q4::launch_counter_reset(tok + 2, s);
-  for (int64_t i = 0; i < steps && e == hipSuccess; ++i) {
-    e = q4::launch_token_fetch(tokens, tok + 2, tok, s);
-    if (e == hipSuccess) e = enqueue_step(*d, *model, L, tok, tok + 1, nullptr, w, s);
-    if (e == hipSuccess) e = q4::launch_token_store(tokens, tok + 2, tok + 1, s);
-  }
+  for (int64_t i = 0; i < steps && e == hipSuccess; ++i)
+    e = enqueue_step(*d, *model, L, tok, tok + 1, nullptr, w, s, tokens, tok + 2);
   return e == hipSuccess ? q4::api_ok() : device_error(e, "q4_decode_tokens");
 }
 
@@ -297,9 +296,7 @@ int q4_tokens_graph_create(const q4_model* model, int32_t* tokens, void* ws, siz
   int32_t* tok = reinterpret_cast<int32_t*>(w + L.tok);   // cur, next, counter
   if (hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal))
     return device_error(e, what);
-  hipError_t err = q4::launch_token_fetch(tokens, tok + 2, tok, s);
-  if (err == hipSuccess) err = enqueue_step(*d, *model, L, tok, tok + 1, nullptr, w, s);
-  if (err == hipSuccess) err = q4::launch_token_store(tokens, tok + 2, tok + 1, s);
+  hipError_t err = enqueue_step(*d, *model, L, tok, tok + 1, nullptr, w, s, tokens, tok + 2);
   hipGraph_t graph = nullptr;
   const hipError_t end = hipStreamEndCapture(s, &graph);
   if (err == hipSuccess) err = end;
