@@ -300,8 +300,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const uint4* __restrict__ W,
   }
 }
 
-// ------------------------------------------------------------- M in 2..8 ---
-// A workgroup stages X once and loops over tiles of 16 rows x one K slice (a
+// ------------------------------------------------------------- M in 4..8 ---
+// (2 and 3 rows run on the vector units, k_gemv_mx below.)  A workgroup stages X once and loops over tiles of 16 rows x one K slice (a
 // workgroup per tile staged X once per 16 rows: at M = 8, K = 2048 that was 32 KB
 // of X per 18 KB of weights); its four waves take interleaved chunks of four
 // groups.  In a chunk, lane (c = lane/16, r = lane%16) loads group c of
@@ -516,6 +516,121 @@ __global__ __launch_bounds__(kBlock) void k_gemv_mfma(const uint4* __restrict__ 
   }
 }
 
+// ------------------------------------------------------------- M in 2..3 ---
+// The M = 1 kernel's layout with XM rows of x: a team of LPR lanes per row, lane i
+// taking groups i, i + LPR, ... of the slice (one trip: the launch picks UNR so
+// that a lane's groups fit it), X staged as XM sets of the M = 1 kernel's
+// pair-ordered planes.  Each group's words are decoded once (the exact q - 7
+// pairs) and dotted with every row of X, each row with the M = 1 kernel's own
+// chains, so a row's output equals the M = 1 GEMV of that row when both run as
+// one slice.  Up to three rows this beats the 16-row MFMA tile, which leaves most
+// of its A operand empty (151936 x 2048: 47 -> 43 us at M = 2; 12288 x 2048: 9.6 ->
+// 8.8 us at M = 3); at four, X's LDS reads cost more than the MFMA saves.
+template <int LPR, int UNR, int XM>
+__global__ __launch_bounds__(kBlock) void k_gemv_mx(const uint4* __restrict__ W,
+                                                    const uint16_t* __restrict__ S,
+                                                    const uint4* __restrict__ X,
+                                                    uint16_t* __restrict__ Y,
+                                                    float* __restrict__ P, int N, int G,
+                                                    int splits) {
+  extern __shared__ uint4 xs[];   // [XM][4][gc]
+  const int split = blockIdx.y;
+  const int g0 = slice_begin(G, splits, split);
+  const int gc = slice_begin(G, splits, split + 1) - g0;
+  const int lane = threadIdx.x & (LPR - 1);
+  const int team = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) / LPR);
+  const int nteams = (int)(gridDim.x * (unsigned)(kBlock / LPR));
+  uint4 wv[UNR];
+  uint16_t sv[UNR];
+  auto issue = [&](int n, int t0) {
+    const uint4* wr = W + (int64_t)n * G + g0;
+    const uint16_t* sr = S + (int64_t)n * G + g0;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      int g = t0 + u * LPR + lane;
+      g = g < gc ? g : gc - 1;
+      wv[u] = load_nt(wr + g);
+      sv[u] = sr[g];
+    }
+  };
+  // entry e of X's slice, row-major [XM][4 gc]: block r of row m
+  const int nx = XM * 4 * gc;
+  auto x_at = [&](int e) {
+    const int m = e / (4 * gc), r = e - m * 4 * gc;
+    return X[(int64_t)m * G * 4 + (int64_t)g0 * 4 + r];
+  };
+  auto x_put = [&](int e, uint4 v) {
+    const int m = e / (4 * gc), r = e - m * 4 * gc;
+    xs[m * 4 * gc + (r & 3) * gc + (r >> 2)] = pair_order(v);
+  };
+  // this thread's first PRE entries are loaded before the weights, without a
+  // branch, so that the staging waits for them only (as in the M = 1 kernel)
+  constexpr int PRE = 4;
+  uint4 pr[PRE];
+#pragma unroll
+  for (int j = 0; j < PRE; ++j) {
+    const int e = (int)threadIdx.x + j * kBlock;
+    pr[j] = x_at(e < nx ? e : nx - 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  int n = team;
+  issue(n < N ? n : N - 1, 0);   // a team past the last row loads it and never uses it
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < PRE; ++j) {   // a clamped duplicate writes the same value
+    const int e = (int)threadIdx.x + j * kBlock;
+    x_put(e < nx ? e : nx - 1, pr[j]);
+  }
+  for (int e = threadIdx.x + PRE * kBlock; e < nx; e += kBlock) x_put(e, x_at(e));
+  __syncthreads();
+
+  for (; n < N; n += nteams) {
+    float acc[XM];
+#pragma unroll
+    for (int m = 0; m < XM; ++m) acc[m] = 0.f;
+    for (int t0 = 0; t0 < gc; t0 += LPR * UNR) {
+      if (t0 > 0) issue(n, t0);
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int graw = t0 + u * LPR + lane;
+        const int g = graw < gc ? graw : gc - 1;
+        const uint32_t wj[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+        h2_t q[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dequant_word(wj[j], q[j]);
+        const float sc = half_to_float(sv[u]);
+#pragma unroll
+        for (int m = 0; m < XM; ++m) {
+          const uint4* xm = xs + m * 4 * gc;
+          float a = 0.f, b = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint4 xv = xm[j * gc + g];
+            a = __builtin_amdgcn_fdot2(q[j][0], bits<h2_t>(xv.x), a, false);
+            b = __builtin_amdgcn_fdot2(q[j][1], bits<h2_t>(xv.y), b, false);
+            a = __builtin_amdgcn_fdot2(q[j][2], bits<h2_t>(xv.z), a, false);
+            b = __builtin_amdgcn_fdot2(q[j][3], bits<h2_t>(xv.w), b, false);
+          }
+          const float t = __builtin_fmaf(a + b, sc, acc[m]);
+          acc[m] = graw < gc ? t : acc[m];
+        }
+      }
+    }
+    if (n + nteams < N) issue(n + nteams, 0);
+#pragma unroll
+    for (int m = 0; m < XM; ++m) acc[m] = team_sum<LPR>(acc[m]);
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < XM; ++m) {
+        if (splits == 1)
+          Y[(int64_t)m * N + n] = float_to_half_rne(acc[m]);
+        else
+          P[((int64_t)split * XM + m) * N + n] = acc[m];
+      }
+    }
+  }
+}
+
 // Second pass of split-K: out[i] = fp16(sum over s ascending of P[s*count + i]).
 __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ P,
                                                     uint16_t* __restrict__ Y, int64_t count,
@@ -609,20 +724,67 @@ hipError_t launch_m1_lpr(const GemvArgs& a, const GemvPlan& p, float* part, cons
   }
 }
 
+template <int LPR, int UNR, int XM>
+hipError_t launch_mx_unr(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
+                         hipStream_t s) {
+  const int64_t G = a.K / 32;
+  const int64_t gmax = (G + p.splits - 1) / p.splits;
+  const size_t lds = (size_t)XM * gmax * 64;
+  int64_t blocks = (a.N + kBlock / LPR - 1) / (kBlock / LPR);
+  // workgroups loop over their rows: at most eight per compute unit, fewer when
+  // the LDS of X allows fewer at once
+  int64_t per_cu = (int64_t)(d.lds_per_block / (lds > 0 ? lds : 1));
+  per_cu = per_cu < 1 ? 1 : per_cu > 8 ? 8 : per_cu;
+  if (blocks > (int64_t)d.cus * per_cu) blocks = (int64_t)d.cus * per_cu;
+  const dim3 grid((unsigned)blocks, (unsigned)p.splits);
+  if (hipError_t e = allow_lds(k_gemv_mx<LPR, UNR, XM>, lds)) return e;
+  hipLaunchKernelGGL((k_gemv_mx<LPR, UNR, XM>), grid, dim3(kBlock), lds, s,
+                     reinterpret_cast<const uint4*>(a.words), a.scales,
+                     reinterpret_cast<const uint4*>(a.x), a.y, part, (int)a.N, (int)G, p.splits);
+  return hipGetLastError();
+}
+
+template <int LPR, int XM>
+hipError_t launch_mx(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
+                     hipStream_t s) {
+  const int64_t G = a.K / 32;
+  const int64_t per_lane = ((G + p.splits - 1) / p.splits + LPR - 1) / LPR;
+  switch (per_lane) {
+    case 0: case 1: case 2: return launch_mx_unr<LPR, 2, XM>(a, p, part, d, s);
+    case 3: return launch_mx_unr<LPR, 3, XM>(a, p, part, d, s);
+    case 4: return launch_mx_unr<LPR, 4, XM>(a, p, part, d, s);
+    case 5: return launch_mx_unr<LPR, 5, XM>(a, p, part, d, s);
+    case 6: return launch_mx_unr<LPR, 6, XM>(a, p, part, d, s);
+    default: return launch_mx_unr<LPR, 8, XM>(a, p, part, d, s);
+  }
+}
+
+template <int XM>
+hipError_t launch_mx_lpr(const GemvArgs& a, const GemvPlan& p, float* part, const DeviceInfo& d,
+                         hipStream_t s) {
+  switch (p.lanes_per_row) {
+    case 4: return launch_mx<4, XM>(a, p, part, d, s);
+    case 8: return launch_mx<8, XM>(a, p, part, d, s);
+    case 16: return launch_mx<16, XM>(a, p, part, d, s);
+    case 32: return launch_mx<32, XM>(a, p, part, d, s);
+    default: return launch_mx<64, XM>(a, p, part, d, s);
+  }
+}
+
 }  // namespace
 
 int64_t max_groups_per_slice(const DeviceInfo& d, int64_t M) {
-  // M == 1: 64 bytes of LDS per group.  M > 1: M rows of (4 g + 1) uint4 plus 3 KB
-  // of cross-wave partials and 2 KB of stage per wave.
+  // M <= kMxMax (k_gemv_m1, k_gemv_mx): 64 bytes of LDS per group and row.  More: M
+  // rows of (4 g + 1) uint4 plus 3 KB of cross-wave partials and 2 KB of stage per wave.
   const int64_t lds = (int64_t)d.lds_per_block;
-  if (M <= 1) return lds / 64;
+  if (M <= kMxMax) return lds / (64 * (M < 1 ? 1 : M));
   return ((lds - 3 * 64 * 16 - (kBlock / 64) * 2048) / (16 * M) - 1) / 4;
 }
 
 GemvPlan plan_splits(const DeviceInfo& d, int64_t M, int64_t N, int64_t K, int splits) {
   GemvPlan p;
   p.splits = splits;
-  p.lanes_per_row = M == 1 ? choose_lpr(K / 32) : 64;
+  p.lanes_per_row = M <= kMxMax ? choose_lpr(K / 32) : 64;
   p.ws_bytes = splits > 1 ? (size_t)4 * splits * M * N : 0;
   (void)d;
   return p;
@@ -633,7 +795,7 @@ GemvPlan plan_auto(const DeviceInfo& d, int64_t M, int64_t N, int64_t K) {
   const int64_t gmax = max_groups_per_slice(d, M);
   int64_t splits = (G + gmax - 1) / gmax;       // fit the slice of x in LDS
   int64_t blocks;
-  if (M == 1) {
+  if (M <= kMxMax) {
     const int lpr = choose_lpr(G);
     blocks = (N + kBlock / lpr - 1) / (kBlock / lpr);
   } else {
@@ -642,10 +804,10 @@ GemvPlan plan_auto(const DeviceInfo& d, int64_t M, int64_t N, int64_t K) {
   // too few workgroups to give every compute unit one: split K as well (a
   // workgroup's loads are all in flight at once, so one per unit already
   // streams; a second split-K pass costs more than the rows it would add)
-  const int64_t want = M == 1 ? (int64_t)d.cus : 2 * (int64_t)d.cus;
+  const int64_t want = M <= kMxMax ? (int64_t)d.cus : 2 * (int64_t)d.cus;
   if (blocks * splits < want) {
     int64_t s2 = (want + blocks - 1) / blocks;
-    const int64_t smax = M == 1 ? G / 8 : G / 16;
+    const int64_t smax = M <= kMxMax ? G / 8 : G / 16;
     if (s2 > smax) s2 = smax;
     if (s2 > splits) splits = s2;
   }
@@ -661,6 +823,8 @@ hipError_t launch_gemv(const DeviceInfo& d, const GemvArgs& a, const GemvPlan& p
   hipError_t e;
   if (a.M == 1) {
     e = launch_m1_lpr<kPlain>(a, p, part, d, s);
+  } else if (a.M <= kMxMax) {
+    e = a.M == 2 ? launch_mx_lpr<2>(a, p, part, d, s) : launch_mx_lpr<3>(a, p, part, d, s);
   } else {
     const int64_t G = a.K / 32;
     const int64_t gmax = (G + p.splits - 1) / p.splits;

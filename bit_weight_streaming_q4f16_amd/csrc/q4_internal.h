@@ -62,9 +62,14 @@ struct GemvArgs {
 // Launch plan of one GEMV: how many K slices and which kernel shape.
 struct GemvPlan {
   int splits = 1;                    // K slices (1 = single pass, no workspace)
-  int lanes_per_row = 32;            // M == 1 kernel: lanes cooperating on a row
+  int lanes_per_row = 32;            // M <= kMxMax kernels: lanes cooperating on a row
   size_t ws_bytes = 0;               // fp32 partials when splits > 1
 };
+
+// Input rows up to which a GEMV runs on the vector units (k_gemv_m1, k_gemv_mx);
+// more take the MFMA kernel (at four rows the vector path's LDS reads of X made
+// the 151936 x 2048 GEMV 49 -> 64 us).
+constexpr int64_t kMxMax = 3;
 
 // Largest number of groups one workgroup stages in LDS for M input rows.
 int64_t max_groups_per_slice(const DeviceInfo& d, int64_t M);

@@ -15,7 +15,8 @@ import oracle
 import synth
 import bit_weight_streaming_q4f16_amd as q4
 from conftest import load_golden_cases
-from gpuhelp import (Report, assert_gemv_close, dev_half, dev_words, half_f64, host_half,
+from gpuhelp import (Report, assert_gemv_close, assert_within_rounding_bound, dev_half, dev_words,
+                     half_f64, host_half,
                      host_words)
 
 pytestmark = pytest.mark.gpu
@@ -228,6 +229,23 @@ def test_batched_vs_oracle(M, N, K):
     Y = batched_gpu(w, s, X)
     assert Y.shape == (M, N)
     assert_gemv_close(Y, w, s, X, exact=(N * K <= 100_000))
+
+
+@pytest.mark.parametrize("M", [2, 3])
+@pytest.mark.parametrize("N,K", [(9216, 3072), (20000, 544)])
+def test_batched_vector_rows_equal_single_gemvs(M, N, K):
+    """At two and three rows each row of X runs the single-row GEMV's arithmetic, so
+    where both run as one K slice every row of Y is bitwise that GEMV's output; and
+    every output within the kernel's rounding bound of the exact product (at least
+    99 % exactly rounded)."""
+    assert q4.q4_workspace_bytes(M, N, K) == 0 and q4.q4_workspace_bytes(1, N, K) == 0
+    w, s, X = rand_case(91 + M + N, N, K, M=M, neg=True)
+    Y = batched_gpu(w, s, X)
+    for m in range(M):
+        assert np.array_equal(Y[m], gemv_gpu(w, s, X[m]))
+    y64, y16 = oracle.gemv_exact(w, s, X)
+    assert_within_rounding_bound(Y, y64, y16, s, X, "exact", exact_frac=0.99,
+                                 what=f"M={M} {N}x{K}")
 
 
 @pytest.mark.parametrize("M", [3, 8])
