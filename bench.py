@@ -12,7 +12,8 @@ Prints ONE JSON line (rank 0):
   value = algorithmic bytes per step / time per step, in GB/s;
   roofline = the dominant kernel's algorithmic bytes per launch / its average
              launch duration (HIP events on the stream it runs on) vs 8 TB/s;
-  cpu_baseline = the CPU oracle on this host over one full step (single thread).
+  cpu_baseline = the CPU oracle on this host over one full step (on every usable core up
+                 to the 16-thread share, plus a single-thread figure beside it).
 
 Profiling aids (see profiles/):
   --copy-probe BYTES        run only a plain device copy of BYTES (counter calibration)
