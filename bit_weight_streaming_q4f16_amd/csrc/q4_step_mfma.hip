@@ -48,6 +48,7 @@ constexpr int kCompute = kWaves - kSync;
 constexpr int kSlots = 8;                   // x_ready slots: GEMVs up to 8 apart in flight
 constexpr int kChunks = 4;                  // chunks (of four groups) per burst
 constexpr int kStage = 2048;                // per compute wave: one staged burst (16 rows x 8 groups)
+constexpr int kXRounds = 4;                 // (m, g) pairs of X per lane whose loads are in flight together
 constexpr unsigned kSpinLimit = 1u << 24;
 static_assert(kSlots % kSync == 0, "a GEMV and the one whose slot it reuses share an owner");
 
@@ -57,6 +58,7 @@ struct Shared {
   int local_done[kSlots]; // compute-wave completions per slot (monotonic)
   int fin[kSync];         // highest GEMV each sync wave has finished (copied out)
   int err;
+  int claim;              // range mode: tiles of the workgroup's stretch claimed so far
 };
 
 __device__ __forceinline__ int tile_of(int tbase, int trem, int wg) {
@@ -115,7 +117,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
     sh.local_done[threadIdx.x] = 0;
   }
   if (threadIdx.x < kSync) sh.fin[threadIdx.x] = -1;
-  if (threadIdx.x == 0) sh.err = 0;
+  if (threadIdx.x == 0) {
+    sh.err = 0;
+    sh.claim = 0;
+  }
   __syncthreads();
 
   // This workgroup's share (as in the M = 1 kernel): in range mode the tiles
@@ -233,27 +238,35 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
           __builtin_amdgcn_s_sleep(1);
         }
       }
-      // X rows m < M: lane takes (m, g) pairs
-      const __amdgpu_buffer_rsrc_t rx =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(d.X), 0, 0x7FFFFFFF, kRsrcFlags);
-      const Q4_GLOBAL u32x4_g* X = (const Q4_GLOBAL u32x4_g*)d.X;
+      // X rows m < M: lane takes (m, g) pairs, kXRounds of them per round with
+      // all their loads issued before any is written (one memory round trip per
+      // round, not per pair: the compute waves wait for this at a GEMV's start)
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint4*>(d.X), 0, M * G * 64, kRsrcFlags);
       uint4* xs = reinterpret_cast<uint4*>(lds + d.xoff);
-      for (int e = lane; e < 8 * G; e += 64) {
-        const int g = e >> 3, m = e & 7;
-        if (m < M) {
-          uint4 v[4];
+      for (int e0 = 0; e0 < 8 * G; e0 += 64 * kXRounds) {
+        uint4 v[kXRounds][4];
+#pragma unroll
+        for (int u = 0; u < kXRounds; ++u) {
+          const int e = e0 + 64 * u + lane, g = e >> 3, m = e & 7;
+          const bool ok = e < 8 * G && m < M;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const int i = (m * G + g) * 4 + c;
-            u32x4_g tv;
-            if (coherent)
-              tv = __builtin_amdgcn_raw_buffer_load_b128(rx, 16 * i, 0, kCoherent);
-            else
-              tv = X[i];
-            v[c] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
+            // an entry past X points past the resource: zeros, no access
+            const int off = ok ? ((m * G + g) * 4 + c) * 16 : 0x7FFFFFF0;
+            const u32x4_g tv = coherent
+                                   ? __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, kCoherent)
+                                   : __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+            v[u][c] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
           }
+        }
 #pragma unroll
-          for (int c = 0; c < 4; ++c) xs[(g * 4 + c) * 8 + m] = pair_order(v[c]);
+        for (int u = 0; u < kXRounds; ++u) {
+          const int e = e0 + 64 * u + lane, g = e >> 3, m = e & 7;
+          if (e < 8 * G && m < M) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xs[(g * 4 + c) * 8 + m] = pair_order(v[u][c]);
+          }
         }
       }
       wait_lds();
@@ -286,6 +299,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       int j, t, t_end, row0;     // GEMV, next tile, end tile, first row of the workgroup
       int rows;                  // rows of the workgroup's y buffer for the GEMV
     } cu;
+    // Spread mode deals a GEMV's tiles round-robin (a fixed deal: in a chain every
+    // GEMV waits for its slowest wave, and claiming lets one wave take several
+    // tiles of a short GEMV in a row).  Range mode: a wave claims its next tile of
+    // the workgroup's stretch from an LDS counter when it starts a tile, so a wave
+    // whose loads come back sooner takes more, and the waves run out of tiles
+    // within about one tile of each other.  Either way a wave's tiles come in list
+    // order, so its cursor only moves forward.
     int base = 0;
     auto enter = [&](int j) {
       for (; j <= j1; ++j) {
@@ -307,7 +327,44 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       }
       cu.j = j1 + 1;
     };
-    enter(j0);
+    // range mode: the cursor to tile T of the stretch (T >= the current tile)
+    auto seek = [&](int T) {
+      if (T >= rb) {
+        cu.j = j1 + 1;
+        return;
+      }
+      for (int j = cu.j; j <= j1; ++j) {
+        const TileDesc d = j == cu.j ? cu.d : read_desc(D + j);
+        if (T < d.tbase + (d.N + 15) / 16) {
+          int t0, t1;
+          tile_range(d.tbase, d.trem, d.N, t0, t1);
+          cu.d = d;
+          cu.j = j;
+          cu.t = T - d.tbase;
+          cu.t_end = t1;
+          cu.row0 = t0 * 16;
+          cu.rows = (t1 - t0) * 16;
+          return;
+        }
+      }
+      cu.j = j1 + 1;
+    };
+    const bool claiming = ranges != nullptr;
+    auto claim_next = [&]() {
+      int T = 0;
+      if (lane == 0)
+        T = __hip_atomic_fetch_add(&sh.claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      seek(ra + __builtin_amdgcn_readfirstlane(T));
+    };
+    if (claiming) {
+      cu.j = j0;
+      if (j0 <= j1) {
+        cu.d = read_desc(D + j0);
+        claim_next();
+      }
+    } else {
+      enter(j0);
+    }
     auto wait_x = [&](int j) {
       for (unsigned it = 0; lds_load(&sh.x_ready[(j - j0) % kSlots]) != j; ++it) {
         if (it > kSpinLimit) {
@@ -397,8 +454,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       const int rows = cu.rows;
       const int wrow0 = cu.row0;
       // advance the cursor before the loads are consumed
-      cu.t += kCompute;
-      if (cu.t >= cu.t_end) enter(cu.j + 1);
+      if (claiming) {
+        claim_next();
+      } else {
+        cu.t += kCompute;
+        if (cu.t >= cu.t_end) enter(cu.j + 1);
+      }
 
       f4_t acc = {0.f, 0.f, 0.f, 0.f};
       // Lane (c, r) supplies row r of A (X) and receives rows 4c..4c+3 of D.  Rows
