@@ -166,19 +166,33 @@ __global__ __launch_bounds__(kStepThreads) void k_step_mfma(const MStepDesc* __r
       const int rows = (t1 - t0) * 16, nr = r1 - r0;
       const uint16_t* yb = reinterpret_cast<const uint16_t*>(lds + d.xoff + ybuf_off(M, d.G));
       if (nr > 0) {
-        if (!d.signal) {
-          Q4_GLOBAL uint16_t* Y = (Q4_GLOBAL uint16_t*)d.Y;
-          for (int e = lane; e < M * nr; e += 64) {
-            const int m = e / nr, r = e - m * nr;
-            Y[(int64_t)m * d.N + r0 + r] = yb[m * rows + r];
-          }
-        } else {
-          const __amdgpu_buffer_rsrc_t ry =
-              __builtin_amdgcn_make_buffer_rsrc(d.Y, 0, 0x7FFFFFFF, kRsrcFlags);
-          for (int e = lane; e < M * nr; e += 64) {
-            const int m = e / nr, r = e - m * nr;
-            __builtin_amdgcn_raw_buffer_store_b16(yb[m * rows + r], ry,
-                                                  2 * (m * d.N + r0 + r), 0, kCoherent);
+        // Row by row of Y.  Where every row's run starts 16-byte aligned (Y 16-byte
+        // aligned, N a multiple of 8; r0 is a multiple of 16, so nr is then a
+        // multiple of 8 too) as 16-byte LDS reads and stores; otherwise one value
+        // per lane and store.  (A workgroup's share of a large GEMV is thousands of
+        // values per row of X, copied after its last tile: the step's tail.)
+        const __amdgpu_buffer_rsrc_t ry =
+            __builtin_amdgcn_make_buffer_rsrc(d.Y, 0, 0x7FFFFFFF, kRsrcFlags);
+        const bool vec = (reinterpret_cast<uintptr_t>(d.Y) & 15u) == 0 && d.N % 8 == 0;
+        for (int m = 0; m < M; ++m) {
+          const uint16_t* src = yb + m * rows;
+          const int dst = 2 * (m * d.N + r0);
+          if (vec) {
+            for (int v = lane; v < nr / 8; v += 64) {
+              const uint4 t = *reinterpret_cast<const uint4*>(src + 8 * v);
+              const u32x4_g tv = {t.x, t.y, t.z, t.w};
+              if (d.signal)
+                __builtin_amdgcn_raw_buffer_store_b128(tv, ry, dst + 16 * v, 0, kCoherent);
+              else
+                __builtin_amdgcn_raw_buffer_store_b128(tv, ry, dst + 16 * v, 0, 0);
+            }
+          } else {
+            for (int r = lane; r < nr; r += 64) {
+              if (d.signal)
+                __builtin_amdgcn_raw_buffer_store_b16(src[r], ry, dst + 2 * r, 0, kCoherent);
+              else
+                __builtin_amdgcn_raw_buffer_store_b16(src[r], ry, dst + 2 * r, 0, 0);
+            }
           }
         }
       }
