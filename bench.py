@@ -87,6 +87,8 @@ def parse():
                     help="time only the 2B-class sweep at M=8 (for profiler runs)")
     ap.add_argument("--only-mlp", action="store_true",
                     help="time only one Phi-3 MLP as two q4_gemv calls (for counter runs)")
+    ap.add_argument("--only-affine", action="store_true",
+                    help="time only the affine-format Phi-3 sweeps")
     ap.add_argument("--only-q3", action="store_true",
                     help="time only the q3f16_1 and mixed-format Phi-3 sweeps")
     ap.add_argument("--only-tokens", action="store_true",
@@ -142,6 +144,10 @@ def main():
         return
     if args.only_q3:
         print(json.dumps({"phi3_sweep_q3f16_1": q3_sweep(torch, q4, synth, np, stream)}),
+              flush=True)
+        return
+    if args.only_affine:
+        print(json.dumps({"phi3_sweep_af4g64": affine_sweep(torch, q4, synth, np, stream)}),
               flush=True)
         return
     if args.only_tokens:
@@ -432,6 +438,7 @@ def per_config(torch, q4, synth, np, stream, cpu=False):
     out["formats_large_m1"] = formats_large(torch, q4, S, stream)
     out["twob_sweep_m8"] = m8_sweep(torch, q4, synth, np, stream, cpu=cpu)
     out["phi3_sweep_q3f16_1"] = q3_sweep(torch, q4, synth, np, stream)
+    out["phi3_sweep_af4g64"] = affine_sweep(torch, q4, synth, np, stream)
     return out
 
 
@@ -638,6 +645,59 @@ def q3_sweep(torch, q4, synth, np, stream, steps=300, warmup=100):
         ms = float(np.median(per))
         out[name] = _fig(nbytes, ms, gemvs=len(shapes),
                          q3_layers=sum(1 for i in range(len(shapes)) if pick(i)),
+                         tok_per_s=round(1e3 / ms, 1),
+                         us_p10=round(float(np.percentile(per, 10)) * 1e3, 2),
+                         us_p90=round(float(np.percentile(per, 90)) * 1e3, 2),
+                         statistic="median", kernel="k_step")
+        del descs, plan
+        torch.cuda.empty_cache()
+    return out
+
+
+def affine_sweep(torch, q4, synth, np, stream, steps=300, warmup=100):
+    """The Phi-3-shaped sweep with MLX affine weights (Q4_FMT_AF4_G64: bf16 scale and
+    bias per 64 weights, 18 bytes per 32 like q4f16_1; centred groups, b = -7.5 s +
+    0.1 s N(0, 1)) in the persistent decode-step kernel, and the same list with
+    affine and q4f16_1 layers alternating: one event pair per step, median."""
+    S = synth
+    shapes = S.sweep_shapes("phi3")
+    xs = {}
+    out = {}
+    for name, pick in (("af4g64", lambda i: True), ("mixed", lambda i: i % 2 == 0)):
+        descs, nbytes = [], 0
+        for i, (label, N, K) in enumerate(shapes):
+            if K not in xs:
+                h = S.activations(f"phi3/x{K}", 0, K)
+                xs[K] = torch.from_numpy(h.view(np.int16)).cuda().view(torch.float16)
+            y = torch.empty(N, dtype=torch.float16, device="cuda")
+            if pick(i):
+                words = S.words_torch(label + "/afwords", 0, N * K // 8).view(N, -1)
+                sv = np.abs(0.01 * S.normal(label + "/afs", 0, 0, N * K // 64)) + 1e-3
+                bv = -7.5 * sv + 0.1 * sv * S.normal(label + "/afb", 0, 0, N * K // 64)
+                dev = lambda v: torch.from_numpy(S.to_bf16_bits(v).view(np.int16)).cuda()
+                descs.append((words, dev(sv), xs[K], y, 0, q4.FMT_AF4_G64, dev(bv)))
+            else:
+                m = S.Matrix(label, N, K)
+                sc = torch.from_numpy(m.scales().view(np.int16)).cuda().view(torch.float16)
+                descs.append((m.words_torch("cuda"), sc, xs[K], y, 0, 0))
+            nbytes += S.algorithmic_bytes(1, N, K)      # 18 bytes per 32 weights either way
+        plan = q4.StepPlan(q4.make_layers(descs), 1, 0, stream=stream)
+        sp = q4.C.c_void_p(stream.cuda_stream)
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                plan.run_raw(sp)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for a, b in ev:
+                a.record(stream)
+                plan.run_raw(sp)
+                b.record(stream)
+            torch.cuda.synchronize()
+            plan.status(stream)
+        per = np.array([a.elapsed_time(b) for a, b in ev])
+        ms = float(np.median(per))
+        out[name] = _fig(nbytes, ms, gemvs=len(shapes),
+                         affine_layers=sum(1 for i in range(len(shapes)) if pick(i)),
                          tok_per_s=round(1e3 / ms, 1),
                          us_p10=round(float(np.percentile(per, 10)) * 1e3, 2),
                          us_p90=round(float(np.percentile(per, 90)) * 1e3, 2),

@@ -60,7 +60,7 @@ class Layer(C.Structure):
     """q4_layer: one GEMV of a decode step (device pointers and sizes)."""
     _fields_ = [("words", C.c_void_p), ("scales", C.c_void_p), ("x", C.c_void_p),
                 ("y", C.c_void_p), ("N", C.c_int64), ("K", C.c_int64),
-                ("x_op", C.c_uint32), ("format", C.c_uint32)]
+                ("x_op", C.c_uint32), ("format", C.c_uint32), ("biases", C.c_void_p)]
 
 
 class Weight(C.Structure):
@@ -303,19 +303,22 @@ def q4_gemv_batched_noalloc(words, scales, X, Y=None, stream=None):
 
 
 def make_layers(descs):
-    """descs: iterable of (words, scales, x, y), (words, scales, x, y, x_op) or
-    (words, scales, x, y, x_op, format) tensors -> ctypes array of Layer.  K
-    follows from the words' row length: 8 per word (q4f16_1) or 32 per three
-    words (format FMT_Q3F16_1)."""
+    """descs: iterable of (words, scales, x, y), (words, scales, x, y, x_op),
+    (words, scales, x, y, x_op, format) or (words, scales, x, y, x_op, format,
+    biases) tensors -> ctypes array of Layer.  K follows from the words' row
+    length: 8 per word (q4f16_1, the affine formats) or 32 per three words
+    (format FMT_Q3F16_1).  biases: the affine formats' [N][K/64] tensor."""
     descs = list(descs)
     arr = (Layer * len(descs))()
     for i, d in enumerate(descs):
         w, s, x, y = d[:4]
         x_op = d[4] if len(d) > 4 else X_PLAIN
         fmt = d[5] if len(d) > 5 else 0
+        b = d[6] if len(d) > 6 else None
         N, RW = w.shape
         K = RW * 32 // 3 if fmt == FMT_Q3F16_1 else 8 * RW
-        arr[i] = Layer(w.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, x_op, fmt)
+        arr[i] = Layer(w.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, x_op, fmt,
+                       None if b is None else b.data_ptr())
     return arr
 
 

@@ -61,7 +61,7 @@ int check_shape(int64_t N, int64_t K) {
 // x_cols: elements per row of x (K, or 2K when x holds gate | up).
 int check_gemv(const char* what, const uint32_t* words, const uint16_t* scales,
                const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K,
-               int64_t x_cols, uint32_t format = 0) {
+               int64_t x_cols, uint32_t format = 0, const uint16_t* biases = nullptr) {
   if (!words) return fail(Q4_ERR_NULL, "%s: words is NULL", what);
   if (!scales) return fail(Q4_ERR_NULL, "%s: scales is NULL", what);
   if (!x) return fail(Q4_ERR_NULL, "%s: x is NULL", what);
@@ -86,8 +86,13 @@ int check_gemv(const char* what, const uint32_t* words, const uint16_t* scales,
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + (uintptr_t)bytes;
     return a0 < y1 && y0 < a1;
   };
-  if (overlaps(words, q3 ? N * K / 32 * 12 : N * K / 2) || overlaps(scales, N * K / 16) ||
-      overlaps(x, 2 * M * x_cols))
+  // scales (and the affine biases): 2 bytes per 32 weights, or per 64 (affine)
+  const bool aff = format == Q4_FMT_AF4_G64 || format == Q4_FMT_AF4_G64_F16;
+  const int64_t sbytes = aff ? N * K / 32 : N * K / 16;
+  if (biases && !aligned(biases, 2))
+    return fail(Q4_ERR_ALIGN, "%s: biases %p not 2-byte aligned", what, (const void*)biases);
+  if (overlaps(words, q3 ? N * K / 32 * 12 : N * K / 2) || overlaps(scales, sbytes) ||
+      (biases && overlaps(biases, sbytes)) || overlaps(x, 2 * M * x_cols))
     return fail(Q4_ERR_SHAPE, "%s: y overlaps an input", what);
   return Q4_OK;
 }
@@ -202,8 +207,8 @@ namespace q4 {
 
 int gemv_validate(const char* what, const uint32_t* words, const uint16_t* scales,
                   const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K,
-                  int64_t x_cols, uint32_t format) {
-  return check_gemv(what, words, scales, x, y, M, N, K, x_cols ? x_cols : K, format);
+                  int64_t x_cols, uint32_t format, const uint16_t* biases) {
+  return check_gemv(what, words, scales, x, y, M, N, K, x_cols ? x_cols : K, format, biases);
 }
 
 int ws_validate(const char* what, void* ws, size_t have, size_t need) {

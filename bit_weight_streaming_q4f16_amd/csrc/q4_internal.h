@@ -39,7 +39,8 @@ int api_ok();
 // alignment and size).
 int gemv_validate(const char* what, const uint32_t* words, const uint16_t* scales,
                   const uint16_t* x, const uint16_t* y, int64_t M, int64_t N, int64_t K,
-                  int64_t x_cols = 0, uint32_t format = 0);
+                  int64_t x_cols = 0, uint32_t format = 0,
+                  const uint16_t* biases = nullptr);
 // The workspace check (NULL, size, 16-byte alignment) when `need` bytes are needed.
 int ws_validate(const char* what, void* ws, size_t have, size_t need);
 // Q4_ERR_DEVICE with the HIP error's text.

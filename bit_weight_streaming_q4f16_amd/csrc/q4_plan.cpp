@@ -50,7 +50,8 @@ std::vector<q4::StepLayer> to_step_layers(const q4_layer* layers, int64_t n) {
   std::vector<q4::StepLayer> v((size_t)n);
   for (int64_t i = 0; i < n; ++i)
     v[(size_t)i] = q4::StepLayer{layers[i].words, layers[i].scales, layers[i].x, layers[i].y,
-                                 layers[i].N, layers[i].K, layers[i].x_op, layers[i].format};
+                                 layers[i].N, layers[i].K, layers[i].x_op, layers[i].format,
+                                 layers[i].biases};
   return v;
 }
 
@@ -117,7 +118,7 @@ Choice choose(const q4::DeviceInfo& d, const q4_layer* layers, int64_t n, int64_
   c.plans.resize((size_t)n);
   size_t part = 0, glue = 0;
   for (int64_t i = 0; i < n; ++i) {
-    // (q3f16_1 layers run as one q3 GEMV kernel, with no split-K partials)
+    // (q3f16_1 and affine layers run as one GEMV kernel, with no split-K partials)
     if (!layers[i].format) c.plans[(size_t)i] = q4::plan_auto(d, M, layers[i].N, layers[i].K);
     part = std::max(part, c.plans[(size_t)i].ws_bytes);
     if (layers[i].x_op) glue = std::max(glue, (size_t)(2 * M * layers[i].K));
@@ -146,15 +147,24 @@ int validate(const char* what, const q4_layer* layers, int64_t n, int64_t M, uin
     snprintf(w, sizeof w, "%s: layers[%lld]", what, (long long)i);
     if (L.x_op > Q4_X_SILU_MUL)
       return q4::api_fail(Q4_ERR_SHAPE, "%s: x_op = %u: unknown", w, L.x_op);
-    if (L.format != 0 && L.format != Q4_FMT_Q3F16_1)
-      return q4::api_fail(Q4_ERR_SHAPE, "%s: format = %u: must be 0 (q4f16_1) or "
-                          "Q4_FMT_Q3F16_1", w, L.format);
+    const bool aff = L.format == Q4_FMT_AF4_G64 || L.format == Q4_FMT_AF4_G64_F16;
+    if (L.format != 0 && L.format != Q4_FMT_Q3F16_1 && !aff)
+      return q4::api_fail(Q4_ERR_SHAPE, "%s: format = %u: must be 0 (q4f16_1), "
+                          "Q4_FMT_Q3F16_1, Q4_FMT_AF4_G64 or Q4_FMT_AF4_G64_F16", w, L.format);
     if (L.format && M != 1)
-      return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: q3f16_1 layers run at M = 1 only", w);
+      return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: format %u layers run at M = 1 only", w,
+                          L.format);
     if (L.format && L.K > 32768)
-      return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: q3f16_1 layers take K <= 32768", w);
+      return q4::api_fail(Q4_ERR_UNSUPPORTED, "%s: format %u layers take K <= 32768", w,
+                          L.format);
+    if (aff != (L.biases != nullptr))
+      return q4::api_fail(aff ? Q4_ERR_NULL : Q4_ERR_SHAPE,
+                          "%s: biases must be given for the affine formats only", w);
+    if (aff && L.K % 64)
+      return q4::api_fail(Q4_ERR_SHAPE, "%s: K = %lld: the affine formats take K %% 64 == 0", w,
+                          (long long)L.K);
     if (int rc = q4::gemv_validate(w, L.words, L.scales, L.x, L.y, M, L.N, L.K,
-                                   L.x_op ? 2 * L.K : L.K, L.format))
+                                   L.x_op ? 2 * L.K : L.K, L.format, L.biases))
       return rc;
   }
   return Q4_OK;
@@ -255,6 +265,11 @@ int run(const char* what, const void* plan, void* ws, size_t ws_bytes, hipStream
       }
       if (e == hipSuccess && L.format == Q4_FMT_Q3F16_1) {
         e = q4::launch_gemv_q3(*d, L.words, L.scales, x, L.y, L.N, L.K, -1, s);
+        continue;
+      }
+      if (e == hipSuccess && (L.format == Q4_FMT_AF4_G64 || L.format == Q4_FMT_AF4_G64_F16)) {
+        e = q4::launch_gemv_affine(*d, L.words, L.scales, L.biases, x, L.y, L.N, L.K,
+                                   L.format == Q4_FMT_AF4_G64, s);
         continue;
       }
       const q4::GemvArgs a{L.words, L.scales, x, L.y, h.M, L.N, L.K};

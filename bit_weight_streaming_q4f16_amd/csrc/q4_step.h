@@ -37,6 +37,9 @@ constexpr int kTagIn = 4;    // x is read from an earlier descriptor's tagged pa
 constexpr int kPairs = 8;    // workgroup shares are split in pairs of row-steps (even rows)
 constexpr int kSiluMul = 16; // x is [gate | up]: the input is fp16(silu(gate) * up)
 constexpr int kQ3 = 32;      // q3f16_1 words: 12 bytes per group (W is then a byte address)
+constexpr int kAffine = 64;  // MLX affine: a scale and a bias per two groups (S, Bs [N][G/2]),
+                             // weight = s * q + b; bf16 unless kAffineF16
+constexpr int kAffineF16 = 128;
 
 // One GEMV as the persistent kernel reads it (device-resident table, 80 bytes).
 struct StepDesc {
@@ -55,7 +58,7 @@ struct StepDesc {
                          // grid, the first srem get one more
   int tag_in;            // kTagIn: workspace byte offset of the tagged pairs x is read from
   int tag_out;           // kTagOut: workspace byte offset of this GEMV's tagged pairs
-  int pad[2];
+  const uint16_t* Bs;    // kAffine: biases [N][G/2] (NULL otherwise)
 };
 static_assert(sizeof(StepDesc) == 80, "StepDesc layout");
 
@@ -66,7 +69,8 @@ struct StepLayer {
   uint16_t* y;
   int64_t N, K;
   uint32_t x_op;          // Q4_X_PLAIN (x is [M][K]) or Q4_X_SILU_MUL (x is [M][2K])
-  uint32_t format;        // 0: q4f16_1, Q4_FMT_Q3F16_1: q3f16_1 (M = 1 only)
+  uint32_t format;        // 0: q4f16_1, or Q4_FMT_Q3F16_1, Q4_FMT_AF4_G64(_F16) (M = 1 only)
+  const uint16_t* biases; // the affine formats' biases, NULL otherwise
   int64_t x_cols() const { return x_op ? 2 * K : K; }
 };
 
@@ -85,6 +89,7 @@ struct StepPlan {
   // balanced by weight bytes.  Empty otherwise.
   std::vector<int> ranges;
   size_t lds_bytes = 0;
+  bool affine = false;   // some descriptor is affine (kAffine)
   std::vector<StepDesc> desc;
 };
 
@@ -96,7 +101,8 @@ struct StepLaunch {
   int32_t n, grid, M;
   int32_t nx, maxG, ybuf_rows, stage_off;
   int32_t cross_wg, has_ranges;
-  uint32_t lds_bytes, pad;
+  uint32_t lds_bytes;
+  uint32_t affine;       // k_step: the list holds affine GEMVs (the variant that loads biases)
   uint64_t table_off, ranges_off, table_bytes;
   uint64_t clear_bytes;  // bytes cleared at set-up: control block, counters, tags
   uint64_t ws_bytes;     // total workspace

@@ -35,6 +35,7 @@
 #include <climits>
 #include <cstring>
 
+#include "q4f16.h"
 #include "q4_step.h"
 #include "q4_device.h"
 
@@ -90,6 +91,23 @@ __device__ __forceinline__ CursorDesc read_desc(const StepDesc* d) {
 }
 
 
+// An affine GEMV's bias pointer, read the same way (at GEMV transitions only).
+__device__ __forceinline__ const Q4_GLOBAL uint16_t* read_bias(const StepDesc* d) {
+  u32x2_g b;
+  asm volatile(
+      "s_load_dwordx2 %0, %1, 0x48\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(b)
+      : "s"(d));
+  static_assert(offsetof(StepDesc, Bs) == 72, "bias pointer offset read by the compute waves");
+  return (const Q4_GLOBAL uint16_t*)(((uint64_t)b[1] << 32) | b[0]);
+}
+
+// An affine scale or bias (bf16, or fp16 with kAffineF16) as fp32, exactly.
+__device__ __forceinline__ float affine_value(uint16_t h, bool f16) {
+  return f16 ? (float)bits<_Float16>(h) : bits<float>((uint32_t)h << 16);
+}
+
 constexpr int kWaves = kStepThreads / 64;   // 16
 constexpr int kSync = 4;                    // sync waves (stage x, copy out y)
 constexpr int kCompute = kWaves - kSync;    // compute waves
@@ -116,7 +134,11 @@ __device__ __forceinline__ int wg_step(int sbase, int srem, int wg) {
 //            blocks past a GEMV's own G are zero
 //   cbuf[b]: maxG floats, the offset term of each group (zero past G)
 //   ybuf[b]: ybuf_rows fp16 results of this workgroup's rows
-template <int B, int NX>
+//   sbuf[b]: (AFF) maxG floats, 2^-20 times each group's sum of x (affine GEMVs)
+// AFF: the list holds affine GEMVs (kAffine): every item also loads its biases
+// (from an empty resource for the other formats), so the load count per item stays
+// fixed; lists without them take the variant that never issues those loads.
+template <int B, int NX, bool AFF>
 __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restrict__ D, int n,
                                                        unsigned* __restrict__ ctl, int maxG,
                                                        int ybuf_rows,
@@ -133,6 +155,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   uint4* xbuf = smem;                                                           // [NX][4][maxG]
   float* cbuf = reinterpret_cast<float*>(smem + NX * 4 * maxG);                 // [NX][maxG]
   uint16_t* ybuf = reinterpret_cast<uint16_t*>(cbuf + NX * maxG);              // [NX][rows]
+  float* sbuf = reinterpret_cast<float*>(ybuf + NX * ybuf_rows);                // AFF: [NX][maxG]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wg = blockIdx.x, nwg = gridDim.x;
@@ -399,7 +422,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       wait_lds();
       {
         const uint4 w7 = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
+        const uint4 w1 = make_uint4(0x11111111u, 0x11111111u, 0x11111111u, 0x11111111u);
         const bool q3 = (d.flags & kQ3) != 0;
+        const bool aff = AFF && (d.flags & kAffine) != 0;
+        float* const sb = sbuf + b * maxG;
         for (int g = lane; g < G; g += 64) {
           uint4 xq[4];
 #pragma unroll
@@ -407,6 +433,9 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           // q3f16_1: the same chain over codes all 3 (q3_group_dot)
           cb[g] = q3 ? q3_group_dot(kQ3Zero0, kQ3Zero1, kQ3Zero2, xq, kQ3MaskA, kQ3MaskB)
                      : nibble_group_dot(w7, xq, nbs);
+          // affine: also the chain over codes all 1, 2^-20 times the group's sum of
+          // x, for its (b + 7 s) term
+          if (aff) sb[g] = nibble_group_dot(w1, xq, nbs);
         }
       }
       // groups past G up to the padded count read x = 0 and bias 0, so the
@@ -414,7 +443,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const int Gp = (1 << d.lpr_log2) * d.C;
       for (int i = 4 * G + lane; i < 4 * Gp; i += 64) {
         xb[(i & 3) * maxG + (i >> 2)] = make_uint4(0u, 0u, 0u, 0u);
-        if ((i & 3) == 0) cb[i >> 2] = 0.f;
+        if ((i & 3) == 0) {
+          cb[i >> 2] = 0.f;
+          if (AFF && (d.flags & kAffine)) sbuf[b * maxG + (i >> 2)] = 0.f;
+        }
       }
       wait_lds();
       if (lane == 0) __hip_atomic_store(&sh.x_ready[b], k, __ATOMIC_RELAXED,
@@ -456,6 +488,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
                                  // the sequence index of its first item
     int N, G, lg, C, r0;         // its shape, and its first row in this workgroup
     int q3;                      // q3f16_1 words (12 bytes per group)
+    int aff;                     // affine: 0 none, 1 bf16 scales and biases, 2 fp16
+    const Q4_GLOBAL uint16_t* Bs;   // affine: the biases
     int vo[4];                   // this lane's byte offset of each slot in an item's words
                                  // (16 bytes per group; q3f16_1 loads take 3/4 of it)
   } cu;
@@ -472,6 +506,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
     cu.lg = d.lg;
     cu.C = d.C;
     cu.q3 = (d.flags & kQ3) != 0;
+    cu.aff = !AFF || !(d.flags & kAffine) ? 0 : (d.flags & kAffineF16) ? 2 : 1;
+    cu.Bs = cu.aff ? read_bias(D + j) : nullptr;
     cu.j = j;
     cu.s0 = s0;
     cu.cnt = s1 - s0;
@@ -557,7 +593,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   struct Burst {
     uint4 rw[B][4];
     uint16_t rs[B][4];
-    int rj[B], rrow[B], rN[B], rG[B], rlg[B], rC[B], rr0[B], rq[B];
+    uint16_t rb[B][4];           // affine biases (AFF only)
+    int rj[B], rrow[B], rN[B], rG[B], rlg[B], rC[B], rr0[B], rq[B], ra[B];
   };
   auto issue = [&](Burst& U, int it0) {   // items it0 + p * stride
 #pragma unroll
@@ -569,19 +606,27 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const int C = live ? cu.C : 1;
       const int row0 = live ? (cu.s0 + it0 + p * stride - cu.first) * (64 >> lg) : 0;
       const bool q3 = live && cu.q3;
+      const int aff = live ? cu.aff : 0;
       const uint64_t left = live ? (uint64_t)(cu.N - row0) * (uint64_t)G : 0;   // groups
       const uint64_t gb = q3 ? 12 : 16;                                         // bytes per group
       const uint32_t nw = left * gb < 0xFFFFFFF0ull ? (uint32_t)(left * gb) : 0xFFFFFFF0u;
-      const uint32_t ns = left * 2 < 0xFFFFFFF0ull ? (uint32_t)(left * 2) : 0xFFFFFFF0u;
+      // scales: 2 bytes per group, or (affine) per two groups
+      const uint64_t sb = aff ? left : left * 2;
+      const uint32_t ns = sb < 0xFFFFFFF0ull ? (uint32_t)sb : 0xFFFFFFF0u;
       const Q4_GLOBAL uint8_t* wrow =
           (const Q4_GLOBAL uint8_t*)cu.W + (int64_t)row0 * G * (int64_t)gb;
       const __amdgpu_buffer_rsrc_t bw = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(live ? (const uint8_t*)wrow : (const uint8_t*)W_last),
           0, (int)nw, kRsrcFlags);
       const __amdgpu_buffer_rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(live ? (const uint16_t*)(cu.S + (int64_t)row0 * G)
+          const_cast<uint16_t*>(live ? (const uint16_t*)(cu.S + (int64_t)row0 * (aff ? G / 2 : G))
                                      : (const uint16_t*)W_last),
           0, (int)ns, kRsrcFlags);
+      // affine biases beside the scales; an empty resource for the other formats
+      const __amdgpu_buffer_rsrc_t bb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(aff ? (const uint16_t*)(cu.Bs + (int64_t)row0 * (G / 2))
+                                    : (const uint16_t*)W_last),
+          0, aff ? (int)ns : 0, kRsrcFlags);
       // Per-lane slot offsets are fixed per GEMV (the cursor's).  Only this
       // per-lane part of a buffer address is range-checked, so the scalar offset
       // stays 0; lanes past the end of the matrix (or of an empty resource) read
@@ -596,13 +641,22 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           const u32x3_g v = __builtin_amdgcn_raw_buffer_load_b96(bw, wo, 0, kNonTemporal);
           U.rw[p][t] = make_uint4(v[0], v[1], v[2], 0u);
           U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, cu.vo[t] >> 3, 0, 0);
+          if (AFF) U.rb[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bb, 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, cu.vo[t], 0, kNonTemporal);
           U.rw[p][t] = make_uint4(v[0], v[1], v[2], v[3]);
-          U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, cu.vo[t] >> 3, 0, 0);
+          if (AFF) {
+            // affine: the scale and bias of the slot's pair of groups (slot offset /
+            // 16 is its group; a slot past the row lands past both resources)
+            const int so = aff ? (int)((uint32_t)cu.vo[t] >> 4 & ~1u) : cu.vo[t] >> 3;
+            U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, so, 0, 0);
+            U.rb[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bb, so, 0, 0);
+          } else {
+            U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, cu.vo[t] >> 3, 0, 0);
+          }
         }
       }
       U.rj[p] = live ? cu.j : -1;
@@ -613,6 +667,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       U.rC[p] = C;
       U.rr0[p] = cu.r0;
       U.rq[p] = q3;
+      U.ra[p] = aff;
     }
   };
   // Consume a burst in item order; false once an item past the end is reached.
@@ -634,12 +689,39 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
         for (int t = 0; t < 4; ++t) {
           const bool ok = li + lpr * t < U.rG[0];
 #pragma unroll
-          for (int p = 0; p < B; ++p) U.rs[p][t] = ok ? U.rs[p][t] : (uint16_t)0;
+          for (int p = 0; p < B; ++p) {
+            U.rs[p][t] = ok ? U.rs[p][t] : (uint16_t)0;
+            if (AFF) U.rb[p][t] = ok ? U.rb[p][t] : (uint16_t)0;
+          }
         }
       }
       float acc[B];
 #pragma unroll
       for (int p = 0; p < B; ++p) acc[p] = 0.f;
+      if (AFF && U.ra[0]) {
+        // affine, per group: s * sum((q - 7) x) + (b + 7 s) * sum(x), the first as
+        // the q4f16_1 groups form it (so centred groups cancel before the scaling),
+        // both in the chain's 2^-20 units; 7 s is exact in fp32
+        const bool f16 = U.ra[0] == 2;
+        const float* sb = sbuf + xi * maxG + li;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < U.rC[0]) {
+            uint4 x[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
+            const float off = cb[lpr * t], sx = sb[lpr * t];
+#pragma unroll
+            for (int p = 0; p < B; ++p) {
+              const float pd = nibble_group_dot(U.rw[p][t], x, nb) - off;
+              const float sc = affine_value(U.rs[p][t], f16);
+              acc[p] = __builtin_fmaf(pd, sc, acc[p]);
+              acc[p] = __builtin_fmaf(sx, __builtin_fmaf(7.f, sc, affine_value(U.rb[p][t], f16)),
+                                      acc[p]);
+            }
+          }
+        }
+      } else
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (t < U.rC[0]) {
@@ -681,9 +763,29 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
       const float* cb = cbuf + xi * maxG + li;
       if (U.rC[p] * lpr > U.rG[p]) {      // padded rows: slots past G hold other data
 #pragma unroll
-        for (int t = 0; t < 4; ++t) U.rs[p][t] = li + lpr * t < U.rG[p] ? U.rs[p][t] : (uint16_t)0;
+        for (int t = 0; t < 4; ++t) {
+          U.rs[p][t] = li + lpr * t < U.rG[p] ? U.rs[p][t] : (uint16_t)0;
+          if (AFF) U.rb[p][t] = li + lpr * t < U.rG[p] ? U.rb[p][t] : (uint16_t)0;
+        }
       }
       float acc = 0.f;
+      if (AFF && U.ra[p]) {
+        const bool f16 = U.ra[p] == 2;
+        const float* sb = sbuf + xi * maxG + li;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < U.rC[p]) {
+            uint4 x[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
+            const float pd = nibble_group_dot(U.rw[p][t], x, nb) - cb[lpr * t];
+            const float sc = affine_value(U.rs[p][t], f16);
+            acc = __builtin_fmaf(pd, sc, acc);
+            acc = __builtin_fmaf(sb[lpr * t], __builtin_fmaf(7.f, sc, affine_value(U.rb[p][t], f16)),
+                                 acc);
+          }
+        }
+      } else
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (t < U.rC[p]) {
@@ -805,9 +907,12 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
     s.C = C;
     s.steps = (int)((L.N + rps - 1) / rps);
     s.dep = -1;
-    s.flags = (L.x_op ? kSiluMul : 0) | (L.format ? kQ3 : 0);
+    const bool aff = L.format == Q4_FMT_AF4_G64 || L.format == Q4_FMT_AF4_G64_F16;
+    s.flags = (L.x_op ? kSiluMul : 0) | (L.format == Q4_FMT_Q3F16_1 ? kQ3 : 0) |
+              (aff ? kAffine : 0) | (L.format == Q4_FMT_AF4_G64_F16 ? kAffineF16 : 0);
     s.tag_in = s.tag_out = 0;
-    s.pad[0] = s.pad[1] = 0;
+    s.Bs = aff ? L.biases : nullptr;
+    if (aff) p.affine = true;
     s.sbase = s.steps / p.grid;
     s.srem = s.steps % p.grid;
     if (lpr * C > maxG) maxG = lpr * C;         // padded group count
@@ -906,7 +1011,8 @@ StepPlan plan_step(const DeviceInfo& d, const StepLayer* layers, int64_t n, bool
   p.maxG = maxG;
   const size_t lds_cap = d.lds_per_block - sizeof(int) * 32;
   auto lds_for = [&](int nx, int rows) {
-    return (size_t)nx * ((size_t)4 * maxG * 16 + (size_t)maxG * 4 + (size_t)rows * 2);
+    return (size_t)nx * ((size_t)4 * maxG * 16 + (size_t)maxG * 4 + (size_t)rows * 2 +
+                         (p.affine ? (size_t)maxG * 4 : 0));
   };
   // Range mode: without dependencies, each workgroup streams one contiguous
   // stretch of the row-steps of all GEMVs laid end to end (balanced by weight
@@ -989,6 +1095,7 @@ StepLaunch step_launch_of(const StepPlan& p) {
   L.cross_wg = p.cross_wg;
   L.has_ranges = !p.ranges.empty();
   L.lds_bytes = (uint32_t)p.lds_bytes;
+  L.affine = p.affine ? 1u : 0u;
   L.clear_bytes = p.tag_base + p.tag_bytes;
   L.table_off = (L.clear_bytes + 255) & ~(uint64_t)255;
   L.ranges_off = L.table_off + p.desc.size() * sizeof(StepDesc);
@@ -1006,12 +1113,15 @@ void step_table_bytes(const StepPlan& p, std::vector<uint8_t>* out) {
 }
 
 namespace {
-auto step_kernel(int nx) { return nx == 4 ? k_step<kBurst, 4> : k_step<kBurst, kXBufs>; }
+auto step_kernel(int nx, bool affine) {
+  if (affine) return nx == 4 ? k_step<kBurst, 4, true> : k_step<kBurst, kXBufs, true>;
+  return nx == 4 ? k_step<kBurst, 4, false> : k_step<kBurst, kXBufs, false>;
+}
 }  // namespace
 
 hipError_t step_prepare(const StepLaunch& L) {
   if (L.lds_bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(step_kernel(L.nx)),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(step_kernel(L.nx, L.affine != 0)),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds_bytes);
 }
 
@@ -1020,7 +1130,7 @@ hipError_t launch_step(const StepLaunch& L, void* ws, hipStream_t s) {
   uint8_t* base = static_cast<uint8_t*>(ws);
   const StepDesc* desc = reinterpret_cast<const StepDesc*>(base + L.table_off);
   const int4* rg = L.has_ranges ? reinterpret_cast<const int4*>(base + L.ranges_off) : nullptr;
-  auto kern = step_kernel(L.nx);
+  auto kern = step_kernel(L.nx, L.affine != 0);
   int n = L.n, maxG = L.maxG, yr = L.ybuf_rows;
   // Only waits across workgroups need every workgroup resident at once; without
   // them (no descriptor depends on another) a plain launch does, and it costs
@@ -1038,7 +1148,7 @@ hipError_t launch_step(const StepLaunch& L, void* ws, hipStream_t s) {
 hipError_t step_occupancy(const StepPlan& p, int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
       blocks_per_cu,
-      reinterpret_cast<const void*>(step_kernel(p.nx)), kStepThreads, p.lds_bytes);
+      reinterpret_cast<const void*>(step_kernel(p.nx, p.affine)), kStepThreads, p.lds_bytes);
 }
 
 }  // namespace q4

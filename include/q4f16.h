@@ -177,20 +177,25 @@ Q4_API int q4_gemv_batched_noalloc(const uint32_t* words, const uint16_t* scales
 #define Q4_X_SILU_MUL 1u
 
 /* One GEMV of a decode step: y = W h(x) (or Y = W h(X) for M rows), h per x_op.
- * y/Y: fp16 [M][N].  format: 0 for q4f16_1 (words [N][K/8], 16-byte aligned), or
- * Q4_FMT_Q3F16_1 (defined with the format variants below; everything-webgpu AI.md,
+ * y/Y: fp16 [M][N].  format (the variants are defined below): 0 for q4f16_1
+ * (words [N][K/8], 16-byte aligned); Q4_FMT_Q3F16_1 (everything-webgpu AI.md,
  * "Which quantization to recompile with": words [N][3K/32], 4-byte aligned, a
- * group's three words one 96-bit value, weight = (q - 3) * s), accepted at M = 1
- * only (Q4_ERR_UNSUPPORTED otherwise); a list may mix the two. */
+ * group's three words one 96-bit value, weight = (q - 3) * s); or the MLX affine
+ * format Q4_FMT_AF4_G64 (Splash docs/models.md, "MLX targets": words as q4f16_1,
+ * bf16 scales and biases [N][K/64], weight = s * q + b; K % 64 == 0) or its fp16
+ * variant Q4_FMT_AF4_G64_F16.  Every format but q4f16_1 is accepted at M = 1 only
+ * (Q4_ERR_UNSUPPORTED otherwise); a list may mix them.  biases: the affine
+ * formats' [N][K/64] biases (2-byte aligned), NULL for every other format. */
 typedef struct q4_layer {
-  const uint32_t* words;   /* [N][K/8] (q4f16_1) or [N][3K/32] (q3f16_1) */
-  const uint16_t* scales;  /* [N][K/32] */
+  const uint32_t* words;   /* [N][K/8] (q4f16_1, affine) or [N][3K/32] (q3f16_1) */
+  const uint16_t* scales;  /* [N][K/32], or [N][K/64] (affine) */
   const uint16_t* x;       /* [M][K], or [M][2K] with Q4_X_SILU_MUL */
   uint16_t* y;             /* [M][N]    */
   int64_t N;
   int64_t K;
   uint32_t x_op;           /* Q4_X_PLAIN or Q4_X_SILU_MUL */
-  uint32_t format;         /* 0 (q4f16_1) or Q4_FMT_Q3F16_1 */
+  uint32_t format;         /* 0 (q4f16_1), Q4_FMT_Q3F16_1, Q4_FMT_AF4_G64, Q4_FMT_AF4_G64_F16 */
+  const uint16_t* biases;  /* affine formats: [N][K/64]; NULL otherwise */
 } q4_layer;
 
 /* Run every descriptor as its own kernel launch, in list order on the stream. */

@@ -100,11 +100,11 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_layer_struct_matches_header():
-    # four pointers, two int64, two uint32
-    assert C.sizeof(q4.Layer) == 56
+    # four pointers, two int64, two uint32, the biases pointer
+    assert C.sizeof(q4.Layer) == 64
     text = open(HEADER).read()
     body = re.search(r"typedef struct q4_layer \{(.*?)\} q4_layer;", text, re.S).group(1)
-    fields = re.findall(r"\b(words|scales|x|y|N|K|x_op|format)\s*;", body)
+    fields = re.findall(r"\b(words|scales|x|y|N|K|x_op|format|biases)\s*;", body)
     assert fields == [f[0] for f in q4.Layer._fields_]
     for name, val in (("Q4_X_PLAIN", q4.X_PLAIN), ("Q4_X_SILU_MUL", q4.X_SILU_MUL)):
         m = re.search(r"#define %s (\w+)u" % name, text)
@@ -221,6 +221,28 @@ def test_decode_step_x_op_errors(lib):
     assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 3 and "4-byte" in _err(lib)
     # with the glue, x spans 2K: a y inside that span overlaps it
     layers[1] = q4.Layer(0x50000, 0x60000, 0x80000, 0x80000 + 2 * 64 + 16, 16, 64, 1, 0)
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2 and "overlap" in _err(lib)
+
+
+def test_decode_step_affine_layer_errors(lib):
+    """The affine formats in a layer list: biases required (and only for them), K a
+    multiple of 64, M = 1, 2-byte aligned biases, no overlap of y with the biases."""
+    layers = (q4.Layer * 2)()
+    layers[0] = q4.Layer(0x10000, 0x20000, 0x30000, 0x40000, 16, 128, 0, 0)
+    AF = q4.FMT_AF4_G64
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x30000, 0x70000, 16, 128, 0, AF, None)
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 1 and "biases" in _err(lib)
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x30000, 0x70000, 16, 128, 0, 0, 0x68000)
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2 and "biases" in _err(lib)
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x30000, 0x70000, 16, 96, 0, AF, 0x68000)
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2 and "64" in _err(lib)
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x90000, 0xA0000, 16, 128, 0, AF, 0x68000)
+    assert lib.q4_decode_step_flags(layers, 2, 2, 0, None, 0, None) == 6 and "M = 1" in _err(lib)
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x30000, 0x70000, 16, 128, 0, q4.FMT_AF4_G64_F16,
+                         0x68001)
+    assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 3 and "biases" in _err(lib)
+    # y inside the biases ([16][2] bf16 = 64 bytes from 0x68000)
+    layers[1] = q4.Layer(0x50000, 0x60000, 0x30000, 0x68020, 16, 128, 0, AF, 0x68000)
     assert lib.q4_decode_step_flags(layers, 2, 1, 0, None, 0, None) == 2 and "overlap" in _err(lib)
 
 
