@@ -214,9 +214,11 @@ typedef struct q4_layer {
 
 /* The decode step over a layer list: the GEMVs of layers[0 .. n_layers) in list
  * order, as the Zero TVM decode loop walks the projections of every layer and then
- * the LM head ("Decode loop").  The results are those of calling q4_gemv (M == 1)
- * or q4_gemv_batched (M > 1) on each descriptor in turn, after forming its input
- * per x_op; a descriptor's x may lie in an earlier descriptor's y.
+ * the LM head ("Decode loop").  The results are those of calling q4_gemv (M == 1),
+ * q4_gemv_batched (M > 1) or, for a format variant, q4_gemv_format on each
+ * descriptor in turn, after forming its input per x_op (each within the GEMV
+ * tolerance of the oracle; the kernels differ in rounding order); a descriptor's x
+ * may lie in an earlier descriptor's y.
  *
  * How a list runs: a list whose rows are at most K = 8192 runs as ONE persistent
  * kernel (M == 1; for 2 <= M <= 8 when every K is a multiple of 128, every scales
