@@ -50,6 +50,12 @@ constexpr int kChunks = 4;                  // chunks (of four groups) per burst
 constexpr int kStage = 2048;                // per compute wave: one staged burst (16 rows x 8 groups)
 constexpr int kXRounds = 4;                 // (m, g) pairs of X per lane whose loads are in flight together
 constexpr unsigned kSpinLimit = 1u << 24;
+// Range mode: what a GEMV boundary inside a workgroup's stretch costs, in bytes of
+// weights streamed.  Two neighbouring GEMVs' LDS regions (X, and y until copied
+// out) rarely fit together at M = 8, so the second GEMV's X is staged only once the
+// first is finished and copied out, and the compute waves wait; measured, that is
+// about 19 us, what a compute unit's share of the bandwidth streams of 512 KB.
+constexpr int64_t kBoundaryCost = 512 * 1024;
 static_assert(kSlots % kSync == 0, "a GEMV and the one whose slot it reuses share an owner");
 
 
@@ -742,7 +748,8 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
     return place_in();
   };
   // Range mode (no dependencies): each workgroup takes one contiguous stretch of
-  // the 16-row tiles of all GEMVs laid end to end, balanced by weight bytes.
+  // the 16-row tiles of all GEMVs laid end to end, balanced by weight bytes and
+  // the GEMV boundaries inside each stretch (kBoundaryCost).
   if (!p.cross_wg) {
     std::vector<int64_t> first((size_t)n + 1), cum((size_t)n + 1);
     for (int64_t k = 0; k < n; ++k) {
@@ -752,15 +759,37 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
     }
     const int64_t total = cum[(size_t)n];
     std::vector<int64_t> cut((size_t)p.grid + 1);
-    for (int w = 0; w <= p.grid; ++w) {
-      const int64_t target = (int64_t)(((__int128)total * w) / p.grid);
-      int64_t k = std::upper_bound(cum.begin(), cum.end(), target) - cum.begin() - 1;
-      if (k >= n) k = n - 1;
-      const int64_t tb = 16 * (int64_t)p.desc[(size_t)k].G * 18;
-      int64_t t = (target - cum[(size_t)k]) / tb;
-      if (t > tiles[(size_t)k]) t = tiles[(size_t)k];
-      cut[(size_t)w] = w == p.grid ? first[(size_t)n] : first[(size_t)k] + t;
+    // Stretches of least maximum cost, where a stretch costs its bytes plus
+    // kBoundaryCost for every GEMV it starts after its first one: greedy filling
+    // under a budget, the budget found by bisection.
+    auto fill = [&](int64_t budget, bool keep) {
+      int w = 0;
+      int64_t used = 0;
+      if (keep) cut[0] = 0;
+      for (int64_t k = 0; k < n; ++k) {
+        const int64_t tb = 16 * (int64_t)p.desc[(size_t)k].G * 18;
+        for (int64_t t = 0; t < tiles[(size_t)k]; ++t) {
+          int64_t c = tb + (t == 0 && used > 0 ? kBoundaryCost : 0);
+          if (used + c > budget && used > 0) {
+            if (++w >= p.grid) return false;
+            if (keep) cut[(size_t)w] = first[(size_t)k] + t;
+            used = 0;
+            c = tb;
+          }
+          used += c;
+        }
+      }
+      if (keep)
+        for (int v = w + 1; v <= p.grid; ++v) cut[(size_t)v] = first[(size_t)n];
+      return true;
+    };
+    int64_t lo = (total + p.grid - 1) / p.grid, hi = lo;
+    while (!fill(hi, false)) hi *= 2;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (fill(mid, false)) hi = mid; else lo = mid + 1;
     }
+    fill(hi, true);
     auto gemv_of = [&](int64_t t) {
       return (int)(std::upper_bound(first.begin(), first.end(), t) - first.begin() - 1);
     };
