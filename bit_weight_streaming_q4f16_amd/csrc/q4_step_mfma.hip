@@ -762,21 +762,29 @@ MStepPlan plan_step_mfma(const DeviceInfo& dev, const StepLayer* layers, int64_t
     // Stretches of least maximum cost, where a stretch costs its bytes plus
     // kBoundaryCost for every GEMV it starts after its first one: greedy filling
     // under a budget, the budget found by bisection.
+    // (A GEMV's tiles all cost the same, so a stretch takes them in runs: the
+    // host work is per GEMV and stretch, not per tile.)
     auto fill = [&](int64_t budget, bool keep) {
       int w = 0;
       int64_t used = 0;
       if (keep) cut[0] = 0;
       for (int64_t k = 0; k < n; ++k) {
-        const int64_t tb = 16 * (int64_t)p.desc[(size_t)k].G * 18;
-        for (int64_t t = 0; t < tiles[(size_t)k]; ++t) {
-          int64_t c = tb + (t == 0 && used > 0 ? kBoundaryCost : 0);
-          if (used + c > budget && used > 0) {
+        const int64_t tb = 16 * (int64_t)p.desc[(size_t)k].G * 18, nt = tiles[(size_t)k];
+        for (int64_t t = 0; t < nt;) {
+          const int64_t c = tb + (t == 0 && used > 0 ? kBoundaryCost : 0);
+          if (used + c > budget && used > 0) {   // the next stretch starts at tile t
             if (++w >= p.grid) return false;
             if (keep) cut[(size_t)w] = first[(size_t)k] + t;
             used = 0;
-            c = tb;
+            continue;
           }
-          used += c;
+          used += c;                             // this tile, then all that still fit
+          ++t;
+          const int64_t more = std::min<int64_t>(nt - t, (budget - used) / tb);
+          if (more > 0) {
+            used += more * tb;
+            t += more;
+          }
         }
       }
       if (keep)
