@@ -108,6 +108,16 @@ __device__ __forceinline__ float affine_value(uint16_t h, bool f16) {
   return f16 ? (float)bits<_Float16>(h) : bits<float>((uint32_t)h << 16);
 }
 
+// An affine pair's scale and bias from the two lanes that loaded them (the even
+// lane the scale, the odd lane the bias; neighbours in a row's team).  Every lane
+// of the wave must be active.
+__device__ __forceinline__ void pair_values(uint16_t own, bool f16, float& sc, float& bi) {
+  const uint16_t other = (uint16_t)bits<uint32_t>(dpp<0xB1>(bits<float>((uint32_t)own)));
+  const bool odd = (threadIdx.x & 1) != 0;
+  sc = affine_value(odd ? other : own, f16);
+  bi = affine_value(odd ? own : other, f16);
+}
+
 constexpr int kWaves = kStepThreads / 64;   // 16
 constexpr int kSync = 4;                    // sync waves (stage x, copy out y)
 constexpr int kCompute = kWaves - kSync;    // compute waves
@@ -592,8 +602,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
   // consuming them needs.
   struct Burst {
     uint4 rw[B][4];
-    uint16_t rs[B][4];
-    uint16_t rb[B][4];           // affine biases (AFF only)
+    uint16_t rs[B][4];           // scales; affine: the pair's scale (even lane) or bias (odd)
     int rj[B], rrow[B], rN[B], rG[B], rlg[B], rC[B], rr0[B], rq[B], ra[B];
   };
   auto issue = [&](Burst& U, int it0) {   // items it0 + p * stride
@@ -622,11 +631,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           const_cast<uint16_t*>(live ? (const uint16_t*)(cu.S + (int64_t)row0 * (aff ? G / 2 : G))
                                      : (const uint16_t*)W_last),
           0, (int)ns, kRsrcFlags);
-      // affine biases beside the scales; an empty resource for the other formats
-      const __amdgpu_buffer_rsrc_t bb = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(aff ? (const uint16_t*)(cu.Bs + (int64_t)row0 * (G / 2))
-                                    : (const uint16_t*)W_last),
-          0, aff ? (int)ns : 0, kRsrcFlags);
+      // AFF: the scales (and biases) through per-lane addresses instead; a lane
+      // with nothing to read (a slot past the row, a row past the matrix, an item
+      // past the end) reads 2 bytes at W_last, which nothing consumes
+      const bool row_in = live && row0 + (lane >> lg) < cu.N;
+      const Q4_GLOBAL uint16_t* srow = cu.S + (int64_t)row0 * (aff ? G / 2 : G);
+      const Q4_GLOBAL uint16_t* brow = aff ? cu.Bs + (int64_t)row0 * (G / 2) : srow;
       // Per-lane slot offsets are fixed per GEMV (the cursor's).  Only this
       // per-lane part of a buffer address is range-checked, so the scalar offset
       // stays 0; lanes past the end of the matrix (or of an empty resource) read
@@ -641,7 +651,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           const u32x3_g v = __builtin_amdgcn_raw_buffer_load_b96(bw, wo, 0, kNonTemporal);
           U.rw[p][t] = make_uint4(v[0], v[1], v[2], 0u);
           U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, cu.vo[t] >> 3, 0, 0);
-          if (AFF) U.rb[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bb, 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -649,11 +658,15 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
           const u32x4_g v = __builtin_amdgcn_raw_buffer_load_b128(bw, cu.vo[t], 0, kNonTemporal);
           U.rw[p][t] = make_uint4(v[0], v[1], v[2], v[3]);
           if (AFF) {
-            // affine: the scale and bias of the slot's pair of groups (slot offset /
-            // 16 is its group; a slot past the row lands past both resources)
-            const int so = aff ? (int)((uint32_t)cu.vo[t] >> 4 & ~1u) : cu.vo[t] >> 3;
-            U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, so, 0, 0);
-            U.rb[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bb, so, 0, 0);
+            // one 2-byte load per slot: the group's scale, or (affine) the lane of
+            // the pair's even group takes the pair's scale and the lane of its odd
+            // group (the next lane of the same row) the pair's bias; the two swap
+            // them when the burst is consumed.  Slot offset / 16 is the group.
+            const bool in = row_in && cu.vo[t] != 0x7FFFFFF0;
+            const int el = aff ? cu.vo[t] >> 5 : cu.vo[t] >> 4;
+            const Q4_GLOBAL uint16_t* a =
+                in ? (aff && (lane & 1) ? brow : srow) + el : (const Q4_GLOBAL uint16_t*)W_last;
+            U.rs[p][t] = *a;
           } else {
             U.rs[p][t] = __builtin_amdgcn_raw_buffer_load_b16(bs, cu.vo[t] >> 3, 0, 0);
           }
@@ -691,7 +704,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
 #pragma unroll
           for (int p = 0; p < B; ++p) {
             U.rs[p][t] = ok ? U.rs[p][t] : (uint16_t)0;
-            if (AFF) U.rb[p][t] = ok ? U.rb[p][t] : (uint16_t)0;
           }
         }
       }
@@ -714,10 +726,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
 #pragma unroll
             for (int p = 0; p < B; ++p) {
               const float pd = nibble_group_dot(U.rw[p][t], x, nb) - off;
-              const float sc = affine_value(U.rs[p][t], f16);
+              float sc, bi;
+              pair_values(U.rs[p][t], f16, sc, bi);
               acc[p] = __builtin_fmaf(pd, sc, acc[p]);
-              acc[p] = __builtin_fmaf(sx, __builtin_fmaf(7.f, sc, affine_value(U.rb[p][t], f16)),
-                                      acc[p]);
+              acc[p] = __builtin_fmaf(sx, __builtin_fmaf(7.f, sc, bi), acc[p]);
             }
           }
         }
@@ -765,7 +777,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           U.rs[p][t] = li + lpr * t < U.rG[p] ? U.rs[p][t] : (uint16_t)0;
-          if (AFF) U.rb[p][t] = li + lpr * t < U.rG[p] ? U.rb[p][t] : (uint16_t)0;
         }
       }
       float acc = 0.f;
@@ -779,10 +790,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepDesc* __restric
 #pragma unroll
             for (int q = 0; q < 4; ++q) x[q] = xb[q * maxG + lpr * t];
             const float pd = nibble_group_dot(U.rw[p][t], x, nb) - cb[lpr * t];
-            const float sc = affine_value(U.rs[p][t], f16);
+            float sc, bi;
+            pair_values(U.rs[p][t], f16, sc, bi);
             acc = __builtin_fmaf(pd, sc, acc);
-            acc = __builtin_fmaf(sb[lpr * t], __builtin_fmaf(7.f, sc, affine_value(U.rb[p][t], f16)),
-                                 acc);
+            acc = __builtin_fmaf(sb[lpr * t], __builtin_fmaf(7.f, sc, bi), acc);
           }
         }
       } else
